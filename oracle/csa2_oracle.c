@@ -1,0 +1,481 @@
+/*
+ * csa2_oracle.c -- plain, slow, CPU reference for the CSA2 attention step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and the
+ * cpu_baseline leg of bench.py may load this library.  The product path never
+ * calls it, and it shares no code, header, table or constant with the HIP
+ * library: the two sides meet only at the bytes of the seeded synthetic inputs.
+ *
+ * Sources (cited by page title and section):
+ *   [RN]   "Reading Notes of DeepSeek-V4.1-Flash: Pushing the Limits of KV Cache
+ *          Compression" -- section 3a (attention and its worked example),
+ *          section 3f C2 (CSA2 steps 1-4), 3f C5 (SWA bounded replay).
+ *   [WASTE] "DeepSeek-V4.1-Flash on WASTE" -- "What is new", 1. CSA2 (two KV
+ *          sources in one softmax, attention sink, one 512-wide KV per token).
+ *   [PLLM] PocketLLM "DeepSeek-V4.1-Flash" -- "The op layer" (finite score
+ *          floor: an all-masked row is zeros), "The CSA2 attention layers"
+ *          (window quantized to FP8 over 32 elements; a partial group emits
+ *          nothing), "Correctness and precision" (-1 fills the unused top-k
+ *          slots; ties).
+ *
+ * Arithmetic: every floating-point step of the attention is fp64 over the
+ * exactly decoded bf16 / fp8 inputs.  The indexer score is defined in fp32 by a
+ * canonical sequential FMA chain (the pages do not fix the score precision;
+ * this reading makes selected indices reproducible bit for bit), with an fp64
+ * shadow and a rounding-error bound reported next to it.
+ *
+ * Every function validates its inputs and returns a negative code on refusal
+ * (NaN/Inf input, reserved codes, bad sizes); it never aborts.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_OK 0
+#define ORC_EBADARG (-1)
+#define ORC_ENONFINITE (-2)
+#define ORC_ENOMEM (-3)
+
+enum { ORC_MODE_FULL = 0, ORC_MODE_REINDEX = 1, ORC_MODE_REUSE = 2, ORC_MODE_WINDOW = 3 };
+enum { ORC_KV_BF16 = 0, ORC_KV_FP8 = 1 };
+
+/* ------------------------------------------------------------------------- */
+/* O0: exact decoding of the storage formats                                  */
+/* ------------------------------------------------------------------------- */
+
+/* bfloat16: 1 sign, 8 exponent (bias 127), 7 fraction bits.  Returns -2 for
+ * Inf/NaN, which the oracle refuses. */
+int csa2o_bf16_to_f64(uint16_t b, double *out) {
+  int s = (b >> 15) & 1, e = (b >> 7) & 0xFF, m = b & 0x7F;
+  double v;
+  if (e == 0xFF) return ORC_ENONFINITE;
+  if (e == 0)
+    v = ldexp((double)m, -133); /* 2^(1-127) * m/2^7 */
+  else
+    v = ldexp(1.0 + (double)m / 128.0, e - 127);
+  *out = s ? -v : v;
+  return ORC_OK;
+}
+
+/* FP8 E4M3 ("fn" variant: bias 7, no infinities, S.1111.111 is NaN), as used
+ * for the sliding-window cache ([PLLM] "The CSA2 attention layers"). */
+int csa2o_e4m3_to_f64(uint8_t c, double *out) {
+  int s = (c >> 7) & 1, e = (c >> 3) & 0xF, m = c & 7;
+  double v;
+  if (e == 0xF && m == 7) return ORC_ENONFINITE;
+  if (e == 0)
+    v = ldexp((double)m, -9); /* subnormal: m/8 * 2^(1-7) */
+  else
+    v = ldexp(1.0 + (double)m / 8.0, e - 7);
+  *out = s ? -v : v;
+  return ORC_OK;
+}
+
+/* UE8M0 block scale: an unsigned power of two 2^(e-127); 0xFF is NaN. */
+int csa2o_ue8m0_to_f64(uint8_t e, double *out) {
+  if (e == 0xFF) return ORC_ENONFINITE;
+  *out = ldexp(1.0, (int)e - 127);
+  return ORC_OK;
+}
+
+/* Decode one KV row of d values.  bf16 rows are d uint16; fp8 rows are d codes
+ * followed (in a separate plane) by d/32 UE8M0 scales, one per 32 values. */
+static int decode_row(int kv_dtype, int d, const void *rows, const uint8_t *scales, int64_t r,
+                      double *out) {
+  int i, rc;
+  if (kv_dtype == ORC_KV_BF16) {
+    const uint16_t *p = (const uint16_t *)rows + (size_t)r * (size_t)d;
+    for (i = 0; i < d; ++i)
+      if ((rc = csa2o_bf16_to_f64(p[i], &out[i])) != ORC_OK) return rc;
+    return ORC_OK;
+  }
+  if (kv_dtype == ORC_KV_FP8) {
+    const uint8_t *p = (const uint8_t *)rows + (size_t)r * (size_t)d;
+    const uint8_t *sc = scales + (size_t)r * (size_t)(d / 32);
+    for (i = 0; i < d; ++i) {
+      double code, scale;
+      if ((rc = csa2o_e4m3_to_f64(p[i], &code)) != ORC_OK) return rc;
+      if ((rc = csa2o_ue8m0_to_f64(sc[i / 32], &scale)) != ORC_OK) return rc;
+      out[i] = code * scale; /* exact: a power-of-two scale */
+    }
+    return ORC_OK;
+  }
+  return ORC_EBADARG;
+}
+
+/* ------------------------------------------------------------------------- */
+/* O1: causal reachability ([RN] 3f C2 Step 1: block j covers m consecutive    */
+/* tokens; [PLLM] a partial trailing group emits no entry yet).                */
+/* ------------------------------------------------------------------------- */
+
+/* With 0-based positions, compressed entry j stands for tokens j*m .. j*m+m-1
+ * and exists once its last token is at or before the query position, so the
+ * reachable entries are j < floor((pos+1)/m).  m == 0 (no compressed branch)
+ * and window-only mode reach nothing.  The count is capped by the pool the
+ * caller holds. */
+int64_t csa2o_n_valid(int64_t pos, int32_t m, int32_t mode, int64_t pool_len) {
+  int64_t n;
+  if (pos < 0 || m < 0 || pool_len < 0) return ORC_EBADARG;
+  if (m == 0 || mode == ORC_MODE_WINDOW) return 0;
+  n = (pos + 1) / m;
+  return n < pool_len ? n : pool_len;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Sliding window with the bounded-replay cut ([RN] 3f C2 Step 3: keys         */
+/* t-w < u <= t; 3f C5: a window that would reach before the replay start s    */
+/* begins at s instead).                                                       */
+/* ------------------------------------------------------------------------- */
+int csa2o_window_range(int64_t pos, int32_t w, int64_t replay_start, int64_t *lo, int64_t *count) {
+  int64_t a;
+  if (w < 0 || pos < replay_start) return ORC_EBADARG;
+  a = pos - (int64_t)w + 1;
+  if (a < replay_start) a = replay_start;
+  *lo = a;
+  *count = (w == 0) ? 0 : pos - a + 1;
+  if (w == 0) *lo = pos + 1;
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* O3: indexer scores ([RN] 3f C2 Step 2, lightning-indexer form):             */
+/*   sigma(j) = sum_h w_h * f(q_h . k_j),  f = ReLU (pages) or identity.       */
+/* ------------------------------------------------------------------------- */
+
+/* Canonical fp32 arithmetic for one candidate row `k` (d_i floats):
+ *   per head h: acc = +0.0f; for i = 0..d_i-1: acc = fmaf(q[h][i], k[i], acc)
+ *               f_h = relu ? (acc > 0 ? acc : +0) : acc
+ *   s = +0.0f; for h = 0..h_i-1: s = fmaf(w_h, f_h, s)   (w_h = 1 when absent)
+ *   -0.0 is mapped to +0.0.
+ * The fp64 shadow evaluates the same expression in double, and `bound` is a
+ * Higham-style bound on |s32 - s64|: recursive summation of exact products
+ * errs by at most gamma_n * sum|terms| (gamma_n = n u / (1 - n u), u = 2^-24),
+ * applied per head and once more over the head combination (f is 1-Lipschitz). */
+static void score_one(int h_i, int d_i, const float *q, const float *w, int relu, const float *k,
+                      float *s32, double *s64, double *bound) {
+  const double u = ldexp(1.0, -24);
+  double gam_d = (d_i * u) / (1.0 - d_i * u);
+  double gam_h = (h_i * u) / (1.0 - h_i * u);
+  float s = 0.0f;
+  double t64 = 0.0, err = 0.0, abs_comb = 0.0;
+  int h, i;
+  for (h = 0; h < h_i; ++h) {
+    const float *qh = q + (size_t)h * (size_t)d_i;
+    float acc = 0.0f;
+    double a64 = 0.0, absum = 0.0, f64;
+    float f32, wh = w ? w[h] : 1.0f;
+    for (i = 0; i < d_i; ++i) {
+      acc = fmaf(qh[i], k[i], acc);
+      a64 += (double)qh[i] * (double)k[i];
+      absum += fabs((double)qh[i] * (double)k[i]);
+    }
+    f32 = relu ? (acc > 0.0f ? acc : 0.0f) : acc;
+    f64 = relu ? (a64 > 0.0 ? a64 : 0.0) : a64;
+    s = fmaf(wh, f32, s);
+    t64 += (double)wh * f64;
+    err += fabs((double)wh) * gam_d * absum;
+    abs_comb += fabs((double)wh * (double)f32);
+  }
+  if (s == 0.0f) s = 0.0f; /* -0 -> +0 */
+  *s32 = s;
+  *s64 = t64;
+  *bound = err * (1.0 + gam_h) + gam_h * abs_comb;
+}
+
+/* Scores for n candidates.  cand == NULL: candidate c is pool row c (Full
+ * mode).  Otherwise candidate c is pool row cand[c] (Reindex mode).  keys are
+ * the pool's index keys, row-major [rows, d_i].  Outputs are per candidate. */
+int csa2o_index_scores(int32_t h_i, int32_t d_i, const float *q, const float *w, int32_t relu,
+                       const float *keys, int64_t key_rows, const int32_t *cand, int64_t n,
+                       float *s32, double *s64, double *bound) {
+  int64_t c;
+  int i;
+  if (h_i < 1 || d_i < 1 || n < 0 || !q || !keys || !s32) return ORC_EBADARG;
+  for (i = 0; i < h_i * d_i; ++i)
+    if (!isfinite(q[i])) return ORC_ENONFINITE;
+  if (w)
+    for (i = 0; i < h_i; ++i)
+      if (!isfinite(w[i])) return ORC_ENONFINITE;
+  for (c = 0; c < n; ++c) {
+    int64_t row = cand ? (int64_t)cand[c] : c;
+    const float *k;
+    double d64, b;
+    if (row < 0 || row >= key_rows) return ORC_EBADARG;
+    k = keys + (size_t)row * (size_t)d_i;
+    for (i = 0; i < d_i; ++i)
+      if (!isfinite(k[i])) return ORC_ENONFINITE;
+    score_one(h_i, d_i, q, w, relu, k, &s32[c], &d64, &b);
+    if (s64) s64[c] = d64;
+    if (bound) bound[c] = b;
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* O4: top-K selection ([RN] 3f C2 Step 2: keep the K best; [PLLM]             */
+/* "Correctness and precision": unused slots hold -1).  Order: score           */
+/* descending, then pool index ascending (lowest index wins a tie); +0 and -0  */
+/* compare equal.  Emitted in ascending pool-index order, padded with -1.      */
+/* ------------------------------------------------------------------------- */
+typedef struct {
+  float s;
+  int32_t pos;
+} cand_t;
+
+static int by_score_then_pos(const void *a, const void *b) {
+  const cand_t *x = (const cand_t *)a, *y = (const cand_t *)b;
+  if (x->s > y->s) return -1;
+  if (x->s < y->s) return 1;
+  return (x->pos < y->pos) ? -1 : (x->pos > y->pos);
+}
+static int by_pos(const void *a, const void *b) {
+  const cand_t *x = (const cand_t *)a, *y = (const cand_t *)b;
+  return (x->pos < y->pos) ? -1 : (x->pos > y->pos);
+}
+
+/* scores[c] belongs to pool row pos_of[c] (pos_of == NULL: row c).  Candidates
+ * whose row is at or beyond n_valid are not eligible (Reindex lists may name
+ * rows the query cannot reach yet). */
+int csa2o_topk(const float *scores, const int32_t *pos_of, int64_t n, int64_t n_valid, int32_t k,
+               int32_t *out) {
+  cand_t *c;
+  int64_t i, m = 0, take;
+  if (n < 0 || k < 0 || !out || (n > 0 && !scores)) return ORC_EBADARG;
+  c = (cand_t *)malloc(sizeof(cand_t) * (size_t)(n > 0 ? n : 1));
+  if (!c) return ORC_ENOMEM;
+  for (i = 0; i < n; ++i) {
+    int32_t p = pos_of ? pos_of[i] : (int32_t)i;
+    if (!isfinite(scores[i])) {
+      free(c);
+      return ORC_ENONFINITE;
+    }
+    if (p < 0 || p >= n_valid) continue;
+    c[m].s = scores[i];
+    c[m].pos = p;
+    ++m;
+  }
+  qsort(c, (size_t)m, sizeof(cand_t), by_score_then_pos);
+  take = m < k ? m : k;
+  qsort(c, (size_t)take, sizeof(cand_t), by_pos);
+  for (i = 0; i < k; ++i) out[i] = (i < take) ? c[i].pos : -1;
+  free(c);
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* O6: single softmax over a set of entries ([RN] section 3a):                 */
+/*   o = sum_e alpha_e v_e,  alpha_e = exp(s_e) / sum exp(s_e'),               */
+/*   s_e = scale * <q, k_e>.  Written for separate K and V so the page's       */
+/*   example (k != v) runs through it; CSA2 passes the same rows as both.      */
+/* Attention sink ([WASTE] 1. CSA2): one per-head logit whose exponential      */
+/* joins the denominator only.  No entries and no sink: o = 0, lse = -inf,     */
+/* matching the finite-floor behaviour ([PLLM] "The op layer").                */
+/* ------------------------------------------------------------------------- */
+int csa2o_attend_core(int32_t h, int32_t d, int64_t e, const double *q, const double *kmat,
+                      const double *vmat, const double *sink, double scale, double *out,
+                      double *lse) {
+  double *s;
+  int64_t j;
+  int hh, i;
+  if (h < 1 || d < 1 || e < 0 || !q || !out || (e > 0 && (!kmat || !vmat))) return ORC_EBADARG;
+  s = (double *)malloc(sizeof(double) * (size_t)(e > 0 ? e : 1));
+  if (!s) return ORC_ENOMEM;
+  for (hh = 0; hh < h; ++hh) {
+    const double *qh = q + (size_t)hh * (size_t)d;
+    double *oh = out + (size_t)hh * (size_t)d;
+    double mx = -INFINITY, l = 0.0;
+    for (j = 0; j < e; ++j) {
+      double acc = 0.0;
+      for (i = 0; i < d; ++i) acc += qh[i] * kmat[(size_t)j * (size_t)d + (size_t)i];
+      s[j] = scale * acc;
+      if (s[j] > mx) mx = s[j];
+    }
+    if (sink && sink[hh] > mx) mx = sink[hh];
+    for (i = 0; i < d; ++i) oh[i] = 0.0;
+    if (mx == -INFINITY) { /* nothing to attend to */
+      if (lse) lse[hh] = -INFINITY;
+      continue;
+    }
+    for (j = 0; j < e; ++j) {
+      double p = exp(s[j] - mx);
+      l += p;
+      for (i = 0; i < d; ++i) oh[i] += p * vmat[(size_t)j * (size_t)d + (size_t)i];
+    }
+    if (sink) l += exp(sink[hh] - mx);
+    for (i = 0; i < d; ++i) oh[i] /= l;
+    if (lse) lse[hh] = mx + log(l);
+  }
+  free(s);
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* O5 + O6 + O7 for one query: the entries are the win_len window rows (raw    */
+/* KV) followed by the selected pool rows (compressed KV); one softmax runs    */
+/* over their concatenation ([RN] 3f C2 Step 3; [WASTE] 1. CSA2).  The KV      */
+/* vector is both key and value (one 512-wide KV per token, no separate V).    */
+/* Window rows are win_rows[0 .. win_len-1]; selected entry idx (>= 0) is      */
+/* pool row idx; -1 entries are skipped; other entries are attended as given   */
+/* (duplicates count once per occurrence).                                     */
+/* ------------------------------------------------------------------------- */
+int csa2o_attend_query(int32_t h, int32_t d, int32_t kv_dtype, const uint16_t *q_bf16,
+                       const void *win_rows, const uint8_t *win_scales, int64_t win_len,
+                       const void *pool_rows, const uint8_t *pool_scales, int64_t pool_len,
+                       const int32_t *sel, int32_t n_sel, const float *sink, double scale,
+                       float *out, float *lse) {
+  double *q = NULL, *kv = NULL, *o = NULL, *ls = NULL, *sk = NULL;
+  int64_t e = 0, j;
+  int rc = ORC_OK, i;
+  if (h < 1 || d < 1 || win_len < 0 || n_sel < 0 || !q_bf16 || !out) return ORC_EBADARG;
+  if (kv_dtype == ORC_KV_FP8 && (d % 32) != 0) return ORC_EBADARG;
+  if (win_len > 0 && !win_rows) return ORC_EBADARG;
+  if (!isfinite(scale)) return ORC_ENONFINITE;
+  for (j = 0; j < n_sel; ++j) {
+    if (sel[j] == -1) continue;
+    if (sel[j] < 0 || sel[j] >= pool_len || !pool_rows) return ORC_EBADARG;
+  }
+  q = (double *)malloc(sizeof(double) * (size_t)h * (size_t)d);
+  kv = (double *)malloc(sizeof(double) * (size_t)(win_len + n_sel + 1) * (size_t)d);
+  o = (double *)malloc(sizeof(double) * (size_t)h * (size_t)d);
+  ls = (double *)malloc(sizeof(double) * (size_t)h);
+  if (sink) sk = (double *)malloc(sizeof(double) * (size_t)h);
+  if (!q || !kv || !o || !ls || (sink && !sk)) {
+    rc = ORC_ENOMEM;
+    goto done;
+  }
+  for (i = 0; i < h * d; ++i)
+    if ((rc = csa2o_bf16_to_f64(q_bf16[i], &q[i])) != ORC_OK) goto done;
+  for (j = 0; j < win_len; ++j, ++e)
+    if ((rc = decode_row(kv_dtype, d, win_rows, win_scales, j, kv + (size_t)e * (size_t)d)) != ORC_OK)
+      goto done;
+  for (j = 0; j < n_sel; ++j) {
+    if (sel[j] == -1) continue;
+    if ((rc = decode_row(kv_dtype, d, pool_rows, pool_scales, sel[j], kv + (size_t)e * (size_t)d)) !=
+        ORC_OK)
+      goto done;
+    ++e;
+  }
+  if (sink)
+    for (i = 0; i < h; ++i) {
+      if (!isfinite(sink[i])) {
+        rc = ORC_ENONFINITE;
+        goto done;
+      }
+      sk[i] = sink[i];
+    }
+  if ((rc = csa2o_attend_core(h, d, e, q, kv, kv, sk, scale, o, ls)) != ORC_OK) goto done;
+  for (i = 0; i < h * d; ++i) out[i] = (float)o[i]; /* round to nearest fp32 */
+  if (lse)
+    for (i = 0; i < h; ++i) lse[i] = (float)ls[i];
+done:
+  free(q);
+  free(kv);
+  free(o);
+  free(ls);
+  free(sk);
+  return rc;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Selection for one query (O1-O4): candidates are the reachable pool rows     */
+/* (Full) or the supplied list restricted to reachable rows (Reindex, [RN] 3f  */
+/* C2 Step 4 and C3: a later layer scores only its allowed candidates).        */
+/* Writes k indices; returns the number of scored candidates (>= 0) or a       */
+/* negative error.  scores_out (optional, n floats) receives the fp32 scores   */
+/* of the n scored candidates in candidate order.                              */
+/* ------------------------------------------------------------------------- */
+int64_t csa2o_select_query(int32_t mode, int64_t pos, int32_t m, int64_t pool_len, int32_t h_i,
+                           int32_t d_i, const float *idx_q, const float *idx_w, int32_t relu,
+                           const float *idx_k, const int32_t *cand, int64_t n_cand, int32_t k,
+                           int32_t *out, float *scores_out) {
+  int64_t nv = csa2o_n_valid(pos, m, mode, pool_len), n;
+  float *s;
+  int rc;
+  if (nv < 0) return nv;
+  if (mode != ORC_MODE_FULL && mode != ORC_MODE_REINDEX) return ORC_EBADARG;
+  n = (mode == ORC_MODE_FULL) ? nv : n_cand;
+  if (mode == ORC_MODE_REINDEX && n > 0 && !cand) return ORC_EBADARG;
+  s = (float *)malloc(sizeof(float) * (size_t)(n > 0 ? n : 1));
+  if (!s) return ORC_ENOMEM;
+  if (mode == ORC_MODE_REINDEX) {
+    /* only reachable listed rows are scored; unreachable ones are dropped */
+    int32_t *keep = (int32_t *)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
+    int64_t c, nk = 0;
+    if (!keep) {
+      free(s);
+      return ORC_ENOMEM;
+    }
+    for (c = 0; c < n; ++c)
+      if (cand[c] >= 0 && cand[c] < nv) keep[nk++] = cand[c];
+    rc = csa2o_index_scores(h_i, d_i, idx_q, idx_w, relu, idx_k, pool_len, keep, nk, s, NULL, NULL);
+    if (rc == ORC_OK) rc = csa2o_topk(s, keep, nk, nv, k, out);
+    if (rc == ORC_OK && scores_out) memcpy(scores_out, s, sizeof(float) * (size_t)nk);
+    free(keep);
+    free(s);
+    return rc == ORC_OK ? nk : rc;
+  }
+  rc = csa2o_index_scores(h_i, d_i, idx_q, idx_w, relu, idx_k, pool_len, NULL, n, s, NULL, NULL);
+  if (rc == ORC_OK) rc = csa2o_topk(s, NULL, n, nv, k, out);
+  if (rc == ORC_OK && scores_out) memcpy(scores_out, s, sizeof(float) * (size_t)n);
+  free(s);
+  return rc == ORC_OK ? n : rc;
+}
+
+/* ------------------------------------------------------------------------- */
+/* A batch of independent decode queries, each through the steps above in the */
+/* pages' order: reachability -> (Full/Reindex) scores and top-K -> one        */
+/* softmax over window rows and selected rows.  Reuse queries read their       */
+/* selection from sel_io; Full/Reindex queries write theirs there.  Window     */
+/* queries attend to their window only.  Layout per query b:                   */
+/*   q [b][h][d] bf16;  window rows win_rows[win_row0[b] ..][d];               */
+/*   pool rows / index keys start at pool_row0[b] and span pool_len[b] rows;   */
+/*   idx_q [b][h_i][d_i];  idx_w [b][h_i] (or NULL);                           */
+/*   Reindex lists cand_idx[cand_off[b] .. cand_off[b+1]) (pool-relative).     */
+/* Queries run in parallel (OpenMP) -- they share nothing.                     */
+/* ------------------------------------------------------------------------- */
+int csa2o_decode_batch(int32_t nb, int32_t h, int32_t d, int32_t k, int32_t h_i, int32_t d_i,
+                       int32_t relu, int32_t kv_dtype, double scale, const int64_t *pos,
+                       const int32_t *mode, const int32_t *ratio, const int64_t *win_row0,
+                       const int32_t *win_len, const int64_t *pool_row0, const int32_t *pool_len,
+                       const int64_t *cand_off, const int32_t *cand_idx, const uint16_t *q,
+                       const void *win_rows, const uint8_t *win_scales, const void *pool_rows,
+                       const uint8_t *pool_scales, const float *idx_q, const float *idx_w,
+                       const float *idx_k, const float *sink, int32_t *sel_io, float *out,
+                       float *lse) {
+  int32_t b;
+  int err = ORC_OK;
+  size_t rb = (kv_dtype == ORC_KV_FP8) ? (size_t)d : 2 * (size_t)d; /* bytes per KV row */
+#pragma omp parallel for schedule(dynamic, 1)
+  for (b = 0; b < nb; ++b) {
+    int rc = ORC_OK;
+    int32_t *sel = sel_io + (size_t)b * (size_t)k;
+    const uint8_t *wr = (const uint8_t *)win_rows + (size_t)win_row0[b] * rb;
+    const uint8_t *ws = win_scales ? win_scales + (size_t)win_row0[b] * (size_t)(d / 32) : NULL;
+    const uint8_t *pr = (const uint8_t *)pool_rows + (size_t)pool_row0[b] * rb;
+    const uint8_t *ps = pool_scales ? pool_scales + (size_t)pool_row0[b] * (size_t)(d / 32) : NULL;
+    int32_t nsel = k;
+    if (mode[b] == ORC_MODE_FULL || mode[b] == ORC_MODE_REINDEX) {
+      const int32_t *cl = (mode[b] == ORC_MODE_REINDEX) ? cand_idx + cand_off[b] : NULL;
+      int64_t nc = (mode[b] == ORC_MODE_REINDEX) ? cand_off[b + 1] - cand_off[b] : 0;
+      int64_t r = csa2o_select_query(mode[b], pos[b], ratio[b], pool_len[b], h_i, d_i,
+                                     idx_q + (size_t)b * (size_t)(h_i * d_i),
+                                     idx_w ? idx_w + (size_t)b * (size_t)h_i : NULL, relu,
+                                     idx_k + (size_t)pool_row0[b] * (size_t)d_i, cl, nc, k, sel, NULL);
+      if (r < 0) rc = (int)r;
+    } else if (mode[b] == ORC_MODE_WINDOW) {
+      nsel = 0;
+    } else if (mode[b] != ORC_MODE_REUSE) {
+      rc = ORC_EBADARG;
+    }
+    if (rc == ORC_OK)
+      rc = csa2o_attend_query(h, d, kv_dtype, q + (size_t)b * (size_t)(h * d), wr, ws, win_len[b], pr,
+                              ps, pool_len[b], sel, nsel, sink, scale,
+                              out + (size_t)b * (size_t)(h * d), lse ? lse + (size_t)b * (size_t)h : NULL);
+    if (rc != ORC_OK) {
+#pragma omp critical
+      err = rc;
+    }
+  }
+  return err;
+}

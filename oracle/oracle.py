@@ -1,0 +1,235 @@
+"""ctypes front end of the CPU oracle (liboracle.so, built from csa2_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py``; never by the product path.
+
+Every function here is marshalling: the arithmetic lives in csa2_oracle.c,
+which follows the pages step by step (see the comments there).  The per-query
+composition (``decode_query`` / ``prefill_query``) strings the C steps together
+in the pages' order: reachability -> scores -> top-K -> one softmax over the
+window rows and the selected compressed rows.
+"""
+import ctypes as C
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liboracle.so")
+
+MODE_FULL, MODE_REINDEX, MODE_REUSE, MODE_WINDOW = 0, 1, 2, 3
+KV_BF16, KV_FP8 = 0, 1
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            from . import build
+            build.build()
+        L = C.CDLL(LIB_PATH)
+        P = C.c_void_p
+        i32, i64, dbl = C.c_int32, C.c_int64, C.c_double
+        L.csa2o_bf16_to_f64.argtypes = [C.c_uint16, C.POINTER(dbl)]
+        L.csa2o_e4m3_to_f64.argtypes = [C.c_uint8, C.POINTER(dbl)]
+        L.csa2o_ue8m0_to_f64.argtypes = [C.c_uint8, C.POINTER(dbl)]
+        for f in (L.csa2o_bf16_to_f64, L.csa2o_e4m3_to_f64, L.csa2o_ue8m0_to_f64):
+            f.restype = C.c_int
+        L.csa2o_n_valid.argtypes = [i64, i32, i32, i64]
+        L.csa2o_n_valid.restype = i64
+        L.csa2o_window_range.argtypes = [i64, i32, i64, C.POINTER(i64), C.POINTER(i64)]
+        L.csa2o_window_range.restype = C.c_int
+        L.csa2o_index_scores.argtypes = [i32, i32, P, P, i32, P, i64, P, i64, P, P, P]
+        L.csa2o_index_scores.restype = C.c_int
+        L.csa2o_topk.argtypes = [P, P, i64, i64, i32, P]
+        L.csa2o_topk.restype = C.c_int
+        L.csa2o_attend_core.argtypes = [i32, i32, i64, P, P, P, P, dbl, P, P]
+        L.csa2o_attend_core.restype = C.c_int
+        L.csa2o_attend_query.argtypes = [i32, i32, i32, P, P, P, i64, P, P, i64, P, i32, P, dbl, P, P]
+        L.csa2o_attend_query.restype = C.c_int
+        L.csa2o_select_query.argtypes = [i32, i64, i32, i64, i32, i32, P, P, i32, P, P, i64, i32, P, P]
+        L.csa2o_select_query.restype = i64
+        L.csa2o_decode_batch.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, dbl,
+                                         P, P, P, P, P, P, P, P, P,
+                                         P, P, P, P, P, P, P, P, P, P, P, P]
+        L.csa2o_decode_batch.restype = C.c_int
+        _lib = L
+    return _lib
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _check(rc):
+    if rc < 0:
+        raise OracleError(f"oracle refused the input (code {rc})")
+    return rc
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+# --- O0 decoders --------------------------------------------------------------
+
+def bf16_to_f64(code):
+    out = C.c_double()
+    _check(lib().csa2o_bf16_to_f64(int(code), C.byref(out)))
+    return out.value
+
+
+def e4m3_to_f64(code):
+    out = C.c_double()
+    _check(lib().csa2o_e4m3_to_f64(int(code), C.byref(out)))
+    return out.value
+
+
+def ue8m0_to_f64(code):
+    out = C.c_double()
+    _check(lib().csa2o_ue8m0_to_f64(int(code), C.byref(out)))
+    return out.value
+
+
+# --- O1 / window ------------------------------------------------------------
+
+def n_valid(pos, ratio, mode, pool_len):
+    return _check(lib().csa2o_n_valid(int(pos), int(ratio), int(mode), int(pool_len)))
+
+
+def window_range(pos, w, replay_start):
+    lo, cnt = C.c_int64(), C.c_int64()
+    _check(lib().csa2o_window_range(int(pos), int(w), int(replay_start), C.byref(lo), C.byref(cnt)))
+    return lo.value, cnt.value
+
+
+# --- O3 / O4 ----------------------------------------------------------------
+
+def index_scores(q, keys, w=None, relu=False, cand=None, n=None):
+    """q [H_I, D_I] f32; keys [rows, D_I] f32.  Returns (s32, s64, bound)."""
+    q = _c(q, np.float32)
+    keys = _c(keys, np.float32)
+    w = _c(w, np.float32)
+    h_i, d_i = q.shape
+    cand = _c(cand, np.int32)
+    if n is None:
+        n = keys.shape[0] if cand is None else cand.shape[0]
+    s32 = np.empty(n, np.float32)
+    s64 = np.empty(n, np.float64)
+    bnd = np.empty(n, np.float64)
+    _check(lib().csa2o_index_scores(h_i, d_i, _ptr(q), _ptr(w), int(bool(relu)), _ptr(keys),
+                                    keys.shape[0], _ptr(cand), n, _ptr(s32), _ptr(s64), _ptr(bnd)))
+    return s32, s64, bnd
+
+
+def topk(scores, k, n_valid_=None, pos_of=None):
+    scores = _c(scores, np.float32)
+    pos_of = _c(pos_of, np.int32)
+    n = scores.shape[0]
+    if n_valid_ is None:
+        n_valid_ = n if pos_of is None else (int(pos_of.max()) + 1 if n else 0)
+    out = np.empty(k, np.int32)
+    _check(lib().csa2o_topk(_ptr(scores), _ptr(pos_of), n, int(n_valid_), int(k), _ptr(out)))
+    return out
+
+
+# --- O6 ----------------------------------------------------------------------
+
+def attend_core(q, kmat, vmat, sink=None, scale=1.0):
+    """fp64 single softmax: q [H, D], kmat/vmat [E, D].  Returns (out [H, D], lse [H])."""
+    q = _c(q, np.float64)
+    h, d = q.shape
+    kmat = _c(kmat, np.float64).reshape(-1, d)
+    vmat = _c(vmat, np.float64).reshape(-1, d)
+    sink = _c(sink, np.float64)
+    out = np.empty((h, d), np.float64)
+    lse = np.empty(h, np.float64)
+    _check(lib().csa2o_attend_core(h, d, kmat.shape[0], _ptr(q), _ptr(kmat), _ptr(vmat), _ptr(sink),
+                                   float(scale), _ptr(out), _ptr(lse)))
+    return out, lse
+
+
+def attend_query(q_bf16, win_rows, pool_rows, sel, kv_dtype=KV_BF16, win_scales=None,
+                 pool_scales=None, sink=None, scale=1.0):
+    """One query's two-source attention.
+
+    q_bf16 [H, D] uint16; win_rows [win_len, D] (uint16 bf16, or uint8 e4m3 with
+    win_scales [win_len, D/32] uint8); pool_rows likewise; sel int32 list of
+    pool rows (-1 skipped).  Returns (out f32 [H, D], lse f32 [H]).
+    """
+    q = _c(q_bf16, np.uint16)
+    h, d = q.shape
+    rdt = np.uint16 if kv_dtype == KV_BF16 else np.uint8
+    win_rows = np.zeros((0, d), rdt) if win_rows is None else _c(win_rows, rdt).reshape(-1, d)
+    pool_rows = np.zeros((0, d), rdt) if pool_rows is None else _c(pool_rows, rdt).reshape(-1, d)
+    win_scales = _c(win_scales, np.uint8)
+    pool_scales = _c(pool_scales, np.uint8)
+    sel = np.zeros(0, np.int32) if sel is None else _c(sel, np.int32)
+    sink = _c(sink, np.float32)
+    out = np.empty((h, d), np.float32)
+    lse = np.empty(h, np.float32)
+    _check(lib().csa2o_attend_query(h, d, kv_dtype, _ptr(q), _ptr(win_rows), _ptr(win_scales),
+                                    win_rows.shape[0], _ptr(pool_rows), _ptr(pool_scales),
+                                    pool_rows.shape[0], _ptr(sel), sel.shape[0], _ptr(sink),
+                                    float(scale), _ptr(out), _ptr(lse)))
+    return out, lse
+
+
+def select_query(mode, pos, ratio, pool_len, idx_q, idx_k, k, idx_w=None, relu=False, cand=None):
+    """Reachability + scores + top-K for one Full/Reindex query.  Returns int32 [k]."""
+    idx_q = _c(idx_q, np.float32)
+    h_i, d_i = idx_q.shape
+    idx_k = _c(idx_k, np.float32)
+    idx_w = _c(idx_w, np.float32)
+    cand = _c(cand, np.int32)
+    out = np.empty(k, np.int32)
+    _check(lib().csa2o_select_query(int(mode), int(pos), int(ratio), int(pool_len), h_i, d_i,
+                                    _ptr(idx_q), _ptr(idx_w), int(bool(relu)), _ptr(idx_k), _ptr(cand),
+                                    0 if cand is None else cand.shape[0], int(k), _ptr(out), None))
+    return out
+
+
+def decode_batch(inp, queries=None, sink=None, scale=1.0):
+    """Run the oracle over a decode batch described like the HIP library's
+    batch (see sparse_long_context_amd.synth): dict of numpy arrays.  ``queries``
+    restricts the run to a subset (indices into the batch).  Returns
+    (sel int32 [n, K], out f32 [n, H, D], lse f32 [n, H])."""
+    d = inp["dims"]
+    qs = np.arange(inp["B"]) if queries is None else np.asarray(queries)
+    n = len(qs)
+    H, D, K, HI, DI = d["n_heads"], d["head_dim"], d["index_topk"], d["index_heads"], d["index_dim"]
+    kvd = d["kv_dtype"]
+    take = lambda name: np.ascontiguousarray(inp[name][qs])  # noqa: E731
+    pos, mode, ratio = take("pos").astype(np.int64), take("mode").astype(np.int32), take("ratio").astype(np.int32)
+    win_row0, win_len = take("win_row0").astype(np.int64), take("win_len").astype(np.int32)
+    pool_row0, pool_len = take("pool_row0").astype(np.int64), take("pool_len").astype(np.int32)
+    q = take("q")
+    idx_q = take("idx_q")
+    idx_w = None if inp.get("idx_w") is None else take("idx_w")
+    sel = np.full((n, K), -1, np.int32)
+    if inp.get("sel_in") is not None:
+        sel[:] = take("sel_in")
+    cand_off = cand_idx = None
+    if inp.get("cand_off") is not None:
+        offs = inp["cand_off"]
+        parts = [inp["cand_idx"][offs[b]:offs[b + 1]] for b in qs]
+        cand_off = np.zeros(n + 1, np.int64)
+        cand_off[1:] = np.cumsum([len(p) for p in parts])
+        cand_idx = np.ascontiguousarray(np.concatenate(parts) if parts else np.zeros(0), np.int32)
+    out = np.empty((n, H, D), np.float32)
+    lse = np.empty((n, H), np.float32)
+    sink = _c(sink, np.float32)
+    rc = lib().csa2o_decode_batch(
+        n, H, D, K, HI, DI, int(d["index_relu"]), kvd, float(scale),
+        _ptr(pos), _ptr(mode), _ptr(ratio), _ptr(win_row0), _ptr(win_len), _ptr(pool_row0), _ptr(pool_len),
+        _ptr(cand_off), _ptr(cand_idx), _ptr(q), _ptr(inp["win_kv"]), _ptr(inp.get("win_scale")),
+        _ptr(inp["comp_kv"]), _ptr(inp.get("comp_scale")), _ptr(idx_q), _ptr(idx_w), _ptr(inp["idx_k"]),
+        _ptr(sink), _ptr(sel), _ptr(out), _ptr(lse))
+    _check(rc)
+    return sel, out, lse

@@ -1,0 +1,53 @@
+"""Build the native libraries of the package in-tree.
+
+* ``libcsa2.so``        -- the HIP library behind include/csa2.h (hipcc, gfx950).
+* ``libcsa2_synth.so``  -- the seeded synthetic-input generator (gcc).
+"""
+import glob
+import os
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+HIP_LIB = os.path.join(PKG, "libcsa2.so")
+SYNTH_LIB = os.path.join(PKG, "libcsa2_synth.so")
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+
+
+def build_synth(verbose: bool = False) -> str:
+    src = os.path.join(PKG, "synth_c", "csa2_synth.c")
+    _run(["gcc", "-O2", "-std=c99", "-D_DEFAULT_SOURCE", "-ffp-contract=off", "-fopenmp", "-fPIC",
+          "-shared", "-Wall", "-Wextra", "-o", SYNTH_LIB + ".tmp", src, "-lm"], verbose)
+    os.replace(SYNTH_LIB + ".tmp", SYNTH_LIB)
+    return SYNTH_LIB
+
+
+def build_hip(verbose: bool = False) -> str:
+    srcs = sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
+    if not srcs:
+        raise RuntimeError("no HIP sources under csrc/")
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+           # packed-fp32 instructions are kept out of every kernel
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Wall", "-Wno-unused-result",
+           "-I", os.path.join(ROOT, "include"),
+           "-o", HIP_LIB + ".tmp"] + srcs
+    _run(cmd, verbose)
+    os.replace(HIP_LIB + ".tmp", HIP_LIB)
+    return HIP_LIB
+
+
+def build_all(verbose: bool = False):
+    return build_synth(verbose), build_hip(verbose)
+
+
+if __name__ == "__main__":
+    build_all(verbose=True)

@@ -1,0 +1,395 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Every test here runs on the CPU.  None of them re-types the oracle's formulas:
+they check it against the pages' worked examples (tests/golden/), closed forms,
+library routines (torch / numpy) for the special cases that reduce to them,
+exact rational arithmetic, and brute force on small inputs.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from sparse_long_context_amd import synth
+
+GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def to_bf16_bits(x):
+    """float values -> bf16 bit patterns via torch's own conversion (RNE)."""
+    t = torch.tensor(np.asarray(x, np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+# --------------------------------------------------------------------------
+# codecs: exhaustive against library decoders
+# --------------------------------------------------------------------------
+
+def test_bf16_decode_exhaustive():
+    codes = np.arange(65536, dtype=np.uint32)
+    ref = (codes << 16).view(np.float32).astype(np.float64)
+    for c in range(65536):
+        e = (c >> 7) & 0xFF
+        if e == 0xFF:
+            with pytest.raises(O.OracleError):
+                O.bf16_to_f64(c)
+        else:
+            v = O.bf16_to_f64(c)
+            assert v == ref[c] and math.copysign(1, v) == math.copysign(1, ref[c]), c
+
+
+def test_e4m3_decode_exhaustive():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for c in range(256):
+        if np.isnan(ref[c]):
+            with pytest.raises(O.OracleError):
+                O.e4m3_to_f64(c)
+        else:
+            v = O.e4m3_to_f64(c)
+            assert v == ref[c] and math.copysign(1, v) == math.copysign(1, ref[c]), c
+    # the format's fixed points: max 448, smallest subnormal 2^-9
+    assert O.e4m3_to_f64(0x7E) == 448.0 and O.e4m3_to_f64(0x01) == 2.0 ** -9
+
+
+def test_ue8m0_decode_exhaustive():
+    for e in range(255):
+        assert O.ue8m0_to_f64(e) == math.ldexp(1.0, e - 127)
+    with pytest.raises(O.OracleError):
+        O.ue8m0_to_f64(255)
+
+
+# --------------------------------------------------------------------------
+# reachability and windows
+# --------------------------------------------------------------------------
+
+def brute_reachable(pos, m, pool_len):
+    """Count blocks j (tokens j*m .. j*m+m-1) whose last token is <= pos."""
+    if m == 0:
+        return 0
+    return sum(1 for j in range(pool_len) if j * m + m - 1 <= pos)
+
+
+@pytest.mark.parametrize("pos,m,pool", [(4095, 4, 1024), (65535, 4, 16384), (126976, 8, 16384),
+                                        (131071, 8, 16384), (0, 4, 10), (2, 4, 10), (3, 4, 10),
+                                        (7, 1, 5), (100, 3, 1000), (1048575, 64, 16384), (5, 0, 10)])
+def test_n_valid_brute_force(pos, m, pool):
+    assert O.n_valid(pos, m, O.MODE_FULL, pool) == brute_reachable(pos, m, pool)
+    assert O.n_valid(pos, m, O.MODE_WINDOW, pool) == 0
+
+
+def test_n_valid_workload_values():
+    # the values the workloads rely on (closed-form from the block rule)
+    assert O.n_valid(4095, 4, 0, 1024) == 1024
+    assert O.n_valid(65535, 4, 0, 16384) == 16384
+    assert O.n_valid(1048575, 64, 0, 16384) == 16384
+    nv = [O.n_valid(p, 8, 0, 16384) for p in range(126976, 131072)]
+    assert nv[0] == 15872 and nv[-1] == 16384 and abs(np.mean(nv) - 16127.625) < 1e-9
+
+
+def test_replay_window_example():
+    g = gold("replay_window_example.json")
+    lo, cnt = O.window_range(g["query"], g["window"], g["replay_start"])
+    assert [lo, lo + cnt - 1] == g["keys_with_cut"] and cnt == g["count_with_cut"]
+    lo, cnt = O.window_range(g["query"], g["window"], 0)
+    assert [lo, lo + cnt - 1] == g["keys_without_cut"] and cnt == g["count_without_cut"]
+    # the same windows by brute force over t-w < u <= t, u >= s
+    for s in (0, 1000, 1040, 1050):
+        us = [u for u in range(0, 1051) if 1050 - 128 < u <= 1050 and u >= s]
+        lo, cnt = O.window_range(1050, 128, s)
+        assert (lo, cnt) == (us[0], len(us))
+
+
+# --------------------------------------------------------------------------
+# indexer scores and top-K
+# --------------------------------------------------------------------------
+
+def test_indexer_example_relu():
+    g = gold("indexer_example.json")
+    q = np.array([g["q"]], np.float32)
+    keys = np.array(g["keys"], np.float32)
+    s32, s64, _ = O.index_scores(q, keys, relu=g["relu"])
+    assert list(s32) == g["scores"] and list(s64) == g["scores"]
+    assert list(O.topk(s32, 1)) == g["top1"]
+    # tie between entries 1 and 2 (both score 0): the lower index wins
+    assert list(O.topk(s32, 2)) == [0, 1]
+    # without ReLU the second dot is -1 and the tie disappears
+    s32n, _, _ = O.index_scores(q, keys, relu=False)
+    assert list(s32n) == [2.0, -1.0, 0.0]
+    assert list(O.topk(s32n, 2)) == [0, 2]
+
+
+def f32_round(x: Fraction) -> Fraction:
+    """Exact round-to-nearest-even of a rational to binary32 (no overflow)."""
+    if x == 0:
+        return Fraction(0)
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -126)
+    quantum = Fraction(2) ** (e - 23)
+    r = round(a / quantum) * quantum  # Fraction.__round__ is half-to-even
+    return r if x > 0 else -r
+
+
+def exact_fma_chain(q, k):
+    acc = Fraction(0)
+    for a, b in zip(q, k):
+        acc = f32_round(Fraction(float(a)) * Fraction(float(b)) + acc)
+    return acc
+
+
+def test_canonical_score_bit_exact_against_rational_fma():
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((1, 128)).astype(np.float32)
+    keys = rng.standard_normal((60, 128)).astype(np.float32)
+    keys[5] = 0.0
+    keys[6] = -keys[6]
+    s32, s64, bnd = O.index_scores(q, keys)
+    for j in range(keys.shape[0]):
+        ref = np.float32(float(exact_fma_chain(q[0], keys[j])))
+        if ref == 0:
+            ref = np.float32(0.0)
+        assert s32[j].tobytes() == ref.tobytes(), j
+        # fp64 shadow is the exact dot to within double rounding, and the fp32
+        # value lies inside the reported bound
+        exact = sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(q[0], keys[j]))
+        assert abs(s64[j] - float(exact)) <= 1e-12 * max(1.0, abs(float(exact)))
+        assert abs(float(s32[j]) - float(exact)) <= bnd[j]
+
+
+def test_multihead_relu_weighted_score_rational():
+    rng = np.random.default_rng(11)
+    hi = 4
+    q = rng.standard_normal((hi, 16)).astype(np.float32)
+    w = rng.standard_normal(hi).astype(np.float32)
+    keys = rng.standard_normal((20, 16)).astype(np.float32)
+    s32, _, _ = O.index_scores(q, keys, w=w, relu=True)
+    for j in range(keys.shape[0]):
+        s = Fraction(0)
+        for h in range(hi):
+            a = exact_fma_chain(q[h], keys[j])
+            f = a if a > 0 else Fraction(0)
+            s = f32_round(Fraction(float(w[h])) * f + s)
+        ref = np.float32(float(s))
+        assert s32[j] == ref, j
+
+
+def brute_topk(scores, k, pos=None):
+    scores = np.asarray(scores, np.float32)
+    pos = np.arange(len(scores)) if pos is None else np.asarray(pos)
+    order = np.lexsort((pos, -scores.astype(np.float64)))
+    take = np.sort(pos[order[:k]])
+    out = np.full(k, -1, np.int32)
+    out[:len(take)] = take
+    return out
+
+
+@pytest.mark.parametrize("n,k", [(0, 8), (5, 8), (8, 8), (9, 8), (1000, 512), (4096, 512), (700, 1)])
+def test_topk_brute_force_with_ties(n, k):
+    rng = np.random.default_rng(n * 31 + k)
+    s = rng.integers(-20, 20, size=n).astype(np.float32) / 4  # many exact ties
+    if n:
+        s[rng.integers(0, n, size=max(1, n // 10))] = -0.0
+        s[rng.integers(0, n, size=max(1, n // 10))] = 0.0
+    assert np.array_equal(O.topk(s, k), brute_topk(s, k))
+
+
+def test_topk_all_equal_and_duplicate_rows():
+    s = np.full(2000, 1.5, np.float32)
+    assert np.array_equal(O.topk(s, 512), np.arange(512, dtype=np.int32))
+    # duplicated key rows give identical scores; the lowest indices win
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((1, 128)).astype(np.float32)
+    keys = rng.standard_normal((600, 128)).astype(np.float32)
+    keys[300:] = keys[:300]
+    s32, _, _ = O.index_scores(q, keys)
+    sel = O.topk(s32, 512)
+    assert np.array_equal(sel, brute_topk(s32, 512))
+    best = int(np.argmax(s32[:300]))
+    assert best in sel and best + 300 in sel
+
+
+def test_topk_respects_reachability_and_reindex_lists():
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((1, 128)).astype(np.float32)
+    keys = rng.standard_normal((400, 128)).astype(np.float32)
+    # Full: only the first n_valid rows are candidates (pos 799, ratio 4 -> 200)
+    sel = O.select_query(O.MODE_FULL, 799, 4, 400, q, keys, 64)
+    s32, _, _ = O.index_scores(q, keys[:200])
+    assert np.array_equal(sel, brute_topk(s32, 64))
+    # Reindex: a list that also names unreachable rows; those are dropped
+    cand = np.sort(rng.choice(400, size=150, replace=False)).astype(np.int32)
+    sel = O.select_query(O.MODE_REINDEX, 799, 4, 400, q, keys, 64, cand=cand)
+    keep = cand[cand < 200]
+    s32k, _, _ = O.index_scores(q, keys, cand=keep)
+    assert np.array_equal(sel, brute_topk(s32k, 64, keep))
+
+
+# --------------------------------------------------------------------------
+# the single softmax
+# --------------------------------------------------------------------------
+
+def test_attention_worked_example():
+    g = gold("attention_example.json")
+    k = np.array([[0.0], [math.log(3.0)]])
+    v = np.array(g["v"], np.float64)
+    out, lse = O.attend_core(np.array([g["q"]]), k, v)
+    assert abs(out[0, 0] - g["o"][0]) < 1e-12
+    # weights (0.25, 0.75) <=> lse = ln(1 + 3)
+    assert abs(lse[0] - math.log(4.0)) < 1e-12
+    assert abs(math.exp(0.0 - lse[0]) - g["weights"][0]) < 1e-12
+
+
+def test_worked_example_embedded_as_two_source_bf16_query():
+    """The page's example with K = V: query e0, window row A = (0, 10, 0...),
+    compressed row B = (ln 3, 20, 0...) -- A in the window, B selected from the pool."""
+    H, D = 2, 64
+    q = np.zeros((H, D), np.float32)
+    q[:, 0] = 1.0
+    A = np.zeros(D, np.float32)
+    A[1] = 10.0
+    B = np.zeros(D, np.float32)
+    B[0], B[1] = math.log(3.0), 20.0
+    pool = np.zeros((5, D), np.float32)
+    pool[3] = B
+    out, lse = O.attend_query(to_bf16_bits(q), to_bf16_bits(A[None]), to_bf16_bits(pool),
+                              np.array([3, -1, -1], np.int32))
+    b = 1.1015625  # ln 3 rounded to bf16
+    assert float(torch.tensor(math.log(3.0)).to(torch.bfloat16)) == b
+    w = math.exp(b) / (1.0 + math.exp(b))
+    assert abs(out[0, 1] - (10 + 10 * w)) < 2e-6 and abs(out[1, 1] - (10 + 10 * w)) < 2e-6
+    assert abs(out[0, 0] - b * w) < 1e-6
+    assert abs(lse[0] - math.log(1 + math.exp(b))) < 1e-6
+
+
+def sdpa64(q, kv, scale):
+    t = torch.nn.functional.scaled_dot_product_attention(
+        torch.tensor(q)[None], torch.tensor(kv)[None], torch.tensor(kv)[None], scale=scale)
+    return t[0].numpy()
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.37])
+def test_dense_equivalence_when_topk_covers_everything(scale):
+    """K >= n_valid: the step is dense attention over window rows + all reachable pool rows."""
+    rng = np.random.default_rng(21)
+    H, D, W, P = 8, 64, 16, 40
+    q = to_bf16_bits(rng.standard_normal((H, D)) / 8)
+    win = to_bf16_bits(rng.standard_normal((W, D)))
+    pool = to_bf16_bits(rng.standard_normal((P, D)))
+    keys = rng.standard_normal((P, 16)).astype(np.float32)
+    iq = rng.standard_normal((1, 16)).astype(np.float32)
+    sel = O.select_query(O.MODE_FULL, 4 * 30 - 1, 4, P, iq, keys, 64)  # 30 reachable rows
+    assert np.array_equal(sel[:30], np.arange(30)) and (sel[30:] == -1).all()
+    out, _ = O.attend_query(q, win, pool, sel, scale=scale)
+    f = lambda a: synth.bf16_bits_to_f32(a).astype(np.float64)  # noqa: E731
+    ref = sdpa64(f(q), np.concatenate([f(win), f(pool[:30])]), scale)
+    assert np.abs(out - ref).max() < 1e-6 * np.abs(ref).max()
+
+
+def test_permutation_invariance_and_lse_merge():
+    rng = np.random.default_rng(9)
+    H, D, W, P = 4, 32, 12, 50
+    q = to_bf16_bits(rng.standard_normal((H, D)) / 4)
+    win = to_bf16_bits(rng.standard_normal((W, D)))
+    pool = to_bf16_bits(rng.standard_normal((P, D)))
+    sel = np.array([3, 7, 11, 20, 21, 40, -1, -1], np.int32)
+    out, lse = O.attend_query(q, win, pool, sel)
+    out2, lse2 = O.attend_query(q, win, pool, rng.permutation(sel))
+    assert np.abs(out - out2).max() < 1e-6 and np.abs(lse - lse2).max() < 1e-6
+    # split the entries into the two sources and merge by log-sum-exp
+    ow, lw = O.attend_query(q, win, pool, None)
+    op, lp = O.attend_query(q, None, pool, sel)
+    m = np.maximum(lw, lp)
+    a, b = np.exp(lw - m), np.exp(lp - m)
+    merged = (a[:, None] * ow + b[:, None] * op) / (a + b)[:, None]
+    assert np.abs(merged - out).max() < 1e-6
+    assert np.abs(m + np.log(a + b) - lse).max() < 1e-5
+
+
+def test_all_masked_row_is_zero_not_nan():
+    H, D = 4, 32
+    q = to_bf16_bits(np.ones((H, D)))
+    pool = to_bf16_bits(np.ones((3, D)))
+    out, lse = O.attend_query(q, None, pool, np.full(8, -1, np.int32))
+    assert (out == 0).all() and np.isneginf(lse).all()
+    out, lse = O.attend_query(q, None, None, None)
+    assert (out == 0).all() and np.isneginf(lse).all()
+
+
+def test_sink_closed_form():
+    rng = np.random.default_rng(4)
+    H, D = 4, 32
+    q = to_bf16_bits(rng.standard_normal((H, D)) / 4)
+    win = to_bf16_bits(rng.standard_normal((9, D)))
+    sink = rng.standard_normal(H).astype(np.float32)
+    out, lse = O.attend_query(q, win, None, None)
+    outs, lses = O.attend_query(q, win, None, None, sink=sink)
+    L = np.exp(lse.astype(np.float64))
+    factor = L / (L + np.exp(sink.astype(np.float64)))
+    assert np.abs(outs - out * factor[:, None]).max() < 1e-6
+    assert np.abs(lses - np.logaddexp(lse, sink)).max() < 1e-5
+
+
+def test_fp8_rows_equal_their_exact_bf16_images():
+    """fp8 E4M3 x 2^k values are exact in bf16; the oracle's fp8 path must equal
+    its bf16 path on those images (decoded here with torch's own e4m3)."""
+    H, D = 4, 64
+    codes, scales = synth.normal_fp8(13, 99, 20, D)
+    q = synth.normal_bf16(13, 98, (H, D), scale=0.125)
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64)
+    vals = vals * torch.pow(2.0, torch.from_numpy(scales.astype(np.float64) - 127)).repeat_interleave(32, 1)
+    img = vals.to(torch.bfloat16)
+    assert (img.to(torch.float64) == vals).all()
+    img = img.view(torch.int16).numpy().view(np.uint16)
+    sel = np.array([12, 3, -1, 19], np.int32)
+    a = O.attend_query(q, codes[:8], codes, sel, kv_dtype=O.KV_FP8, win_scales=scales[:8],
+                       pool_scales=scales)
+    b = O.attend_query(q, img[:8], img, sel)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_oracle_refuses_nonfinite_input():
+    q = np.full((1, 8), 0x7FC0, np.uint16)  # bf16 NaN
+    with pytest.raises(O.OracleError):
+        O.attend_query(q, np.zeros((1, 8), np.uint16), None, None)
+    with pytest.raises(O.OracleError):
+        O.index_scores(np.array([[np.inf]], np.float32), np.ones((2, 1), np.float32))
+
+
+def test_budget_accounting_matches_the_page():
+    g = gold("budget_example.json")
+    assert g["topk"] + g["window"] == g["entries_per_query"]
+    # one query attends 640 entries with 64 heads x 512 dims: QK^T and PV MACs
+    mac_per_layer = 2 * 64 * g["entries_per_query"] * 512
+    total = g["layers"] * mac_per_layer
+    assert abs(total - g["attention_score_mac_per_token"]) / total < g["rounding"]
+
+
+def test_reachability_boundary_is_exclusive():
+    """Row n_valid itself (the block still being filled) is never selectable,
+    even with the best score -- directly in top-K and through a Reindex list."""
+    s = np.array([0.0, 1.0, 9.0, 2.0], np.float32)
+    pos_of = np.array([0, 1, 2, 3], np.int32)
+    assert list(O.topk(s, 2, n_valid_=2, pos_of=pos_of)) == [0, 1]
+    assert list(O.topk(s, 2, n_valid_=3, pos_of=pos_of)) == [1, 2]
+    keys = np.zeros((8, 4), np.float32)
+    keys[:, 0] = np.arange(8)  # score grows with the row
+    q = np.array([[1.0, 0, 0, 0]], np.float32)
+    # pos 11, ratio 4 -> rows 0..2 reachable; row 3 is the partial block
+    sel = O.select_query(O.MODE_REINDEX, 11, 4, 8, q, keys, 2, cand=np.array([1, 2, 3, 7], np.int32))
+    assert list(sel) == [1, 2]
+    sel = O.select_query(O.MODE_FULL, 11, 4, 8, q, keys, 2)
+    assert list(sel) == [1, 2]
