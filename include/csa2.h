@@ -1,0 +1,205 @@
+/*
+ * csa2.h -- C ABI of the CSA2 compressed-sparse-attention step on MI355X (gfx950).
+ *
+ * What the step computes (one query token):
+ *   1. Reachability: compressed entry j stands for the m tokens j*m .. j*m+m-1
+ *      and can be read once its last token is at or before the query position
+ *      ("Reading Notes of DeepSeek-V4.1-Flash", section 3f C2 Step 1; PocketLLM
+ *      "DeepSeek-V4.1-Flash", "The CSA2 attention layers": a partial group emits
+ *      nothing).  n_valid = min(pool_len, floor((pos + 1) / m)); m = 0 -> 0.
+ *   2. Index scores: sigma(j) = sum_h w_h * f(q^I_h . k^I_j), f = ReLU or identity
+ *      (Reading Notes, 3f C2 Step 2, lightning-indexer form).
+ *   3. Top-K: keep the K best candidates (same section), lowest index winning a
+ *      tie; unused slots hold -1 (PocketLLM page, "Correctness and precision").
+ *   4. Attention: the query's H heads attend in ONE softmax over the
+ *      concatenation of its sliding window of raw KV rows and the selected
+ *      compressed rows; each KV row is both key and value (one 512-wide KV per
+ *      token shared by all heads: "DeepSeek-V4.1-Flash on WASTE", What is new,
+ *      1. CSA2; Reading Notes, 3f C2 Step 3).  An optional per-head sink logit
+ *      joins the denominator only (WASTE page, same section).  A query with no
+ *      entry returns zeros (PocketLLM page, "The op layer": finite score floor).
+ *   Modes (Reading Notes, 3f C2 Step 4): FULL scores every reachable entry;
+ *   REINDEX scores a supplied candidate list (3f C3: a later layer searches
+ *   only its pool); REUSE takes a supplied selection; WINDOW has no
+ *   compressed branch (compress ratio 0).
+ *
+ * Numerics.  Index scores are fp32 with a fixed evaluation order, so selections
+ * are reproducible bit for bit: per head acc = +0, acc = fmaf(q[i], k[i], acc)
+ * for i = 0 .. D_I-1 in order; f applied; s = +0, s = fmaf(w_h, f_h, s) for
+ * h = 0 .. H_I-1 in order (w_h = 1 when no weights are given); -0 becomes +0.
+ * Attention multiplies bf16 operands on the matrix cores with fp32
+ * accumulation and an fp32 online softmax; the probabilities are rounded to
+ * bf16 for the second product.  FP8 KV (E4M3, one UE8M0 scale per 32 values)
+ * is widened to bf16 exactly before use.
+ *
+ * Conventions common to every entry point:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller; nothing is
+ *     retained after the call returns.  Base pointers are 16-byte aligned.
+ *   - Calls only enqueue work on `stream` and never synchronize.
+ *   - The library is stateless and allocates no device memory; scratch comes
+ *     from a caller-provided workspace sized by the *_workspace_size calls.
+ *   - Host-visible arguments are validated before anything is launched; on an
+ *     error nothing is launched and no output is touched.  A failed launch
+ *     returns CSA2_ERR_HIP and csa2_last_hip_error() gives its hipError_t.
+ *   - Device-side values (positions, lengths, indices) are preconditions; every
+ *     kernel clamps its reads to the rows the descriptors describe, so a bad
+ *     index yields a wrong answer, never an access outside the described rows.
+ *   - Supported geometry: n_heads 64, head_dim 512, index_dim 128,
+ *     1 <= index_heads <= 64, 1 <= index_topk <= 512, 0 <= window <= 128.
+ *     Others return CSA2_ERR_UNSUPPORTED.
+ *
+ * Layouts (row-major, rows contiguous):
+ *   q        bf16  [B][64][512]
+ *   idx_q    f32   [B][H_I][128];  idx_w f32 [B][H_I] or NULL (unit weights)
+ *   idx_k    f32   [rows][128]     (same row numbering as comp_kv)
+ *   win_kv / comp_kv: bf16 [rows][512], or fp8 codes uint8 [rows][512] with
+ *            scales uint8 [rows][16] (UE8M0, value = code * 2^(s-127))
+ *   topk_idx int32 [B][K]: pool-relative row numbers, ascending, -1 padded
+ *   out      f32   [B][64][512];   lse f32 [B][64] (natural log) or NULL
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA2_ABI_VERSION 1
+
+typedef enum {
+  CSA2_OK = 0,
+  CSA2_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad enum, ... */
+  CSA2_ERR_UNSUPPORTED = 2, /* geometry this build does not implement */
+  CSA2_ERR_WORKSPACE = 3,   /* workspace missing or too small */
+  CSA2_ERR_HIP = 4          /* a kernel launch failed; see csa2_last_hip_error */
+} csa2_status;
+
+typedef enum { CSA2_KV_BF16 = 0, CSA2_KV_FP8_E4M3_UE8M0_32 = 1 } csa2_kv_dtype;
+
+typedef enum {
+  CSA2_MODE_FULL = 0,    /* score every reachable compressed entry, select top-K */
+  CSA2_MODE_REINDEX = 1, /* score a supplied candidate list, select top-K */
+  CSA2_MODE_REUSE = 2,   /* attend a supplied selection */
+  CSA2_MODE_WINDOW = 3   /* window rows only */
+} csa2_mode;
+
+typedef struct csa2_dims {
+  int32_t n_heads;     /* H, query heads (64) */
+  int32_t head_dim;    /* D, dims per head and per KV row (512) */
+  int32_t window;      /* W, window rows per query, at most (prefill: the window size) */
+  int32_t index_topk;  /* K, selected compressed entries per query */
+  int32_t index_dim;   /* D_I (128) */
+  int32_t index_heads; /* H_I */
+  int32_t index_relu;  /* 0: f = identity, 1: f = ReLU */
+  int32_t kv_dtype;    /* csa2_kv_dtype, for both KV sources */
+  float softmax_scale; /* multiplies q.k before the softmax (1 when folded into q) */
+} csa2_dims;
+
+/* Per-query descriptors of a decode batch: DEVICE arrays of length B (cand_off: B+1). */
+typedef struct csa2_batch {
+  const int64_t *pos;            /* absolute position of the query token */
+  const int32_t *mode;           /* csa2_mode */
+  const int32_t *compress_ratio; /* m; 0 = no compressed branch */
+  const int64_t *win_row0;       /* first window row of the query in win_kv */
+  const int32_t *win_len;        /* its number of window rows, 0 .. W (order free) */
+  const int64_t *pool_row0;      /* first row of the query's pool in comp_kv / idx_k */
+  const int32_t *pool_len;       /* rows in that pool */
+  const int64_t *cand_off;       /* REINDEX: list of query b is cand_idx[cand_off[b] .. cand_off[b+1]) */
+  const int32_t *cand_idx;       /*   pool-relative rows, strictly ascending; NULL if no REINDEX query */
+  int32_t max_candidates;        /* HOST value: candidates considered per FULL/REINDEX query are
+                                    capped at this (use the largest pool_len / list length) */
+} csa2_batch;
+
+/* One prefill chunk: T consecutive queries of one sequence (host values). */
+typedef struct csa2_prefill_desc {
+  int64_t pos0;           /* position of the first query; query t sits at pos0 + t */
+  int32_t n_queries;      /* T */
+  int32_t mode;           /* csa2_mode, the same for the whole chunk */
+  int32_t compress_ratio; /* m */
+  int32_t pool_len;       /* rows of comp_kv / idx_k (the sequence's whole pool) */
+  int64_t win_pos0;       /* win_kv row r holds position win_pos0 + r.  It is also the replay
+                             start: a window never reaches before it (Reading Notes, 3f C5,
+                             SWA bounded replay).  Query at p reads rows
+                             [max(win_pos0, p - W + 1), p] - win_pos0.  Needs win_pos0 <= pos0. */
+  const int64_t *cand_off; /* REINDEX (device, T+1) / NULL */
+  const int32_t *cand_idx;
+  int32_t max_candidates;  /* REINDEX: cap on list length per query (host); ignored otherwise */
+} csa2_prefill_desc;
+
+int csa2_abi_version(void);
+const char *csa2_status_str(csa2_status s);
+/* hipError_t of the last CSA2_ERR_HIP returned on this thread (0 if none). */
+int32_t csa2_last_hip_error(void);
+
+/* Workspace bytes csa2_decode needs for B queries with at most max_candidates
+ * candidates each (also enough for csa2_attend's split-K partials). */
+csa2_status csa2_workspace_size(const csa2_dims *dims, int32_t B, int32_t max_candidates,
+                                size_t *bytes);
+
+/* Steps 1-2 for every FULL / REINDEX query b of the batch (other queries are
+ * skipped): scores[b * score_stride + j] for candidate j < n_cand(b), where
+ * n_cand = min(n_valid, max_candidates) (FULL: candidate j is pool row j) or
+ * min(list length, max_candidates) (REINDEX: candidate j is the j-th list row).
+ * A listed row outside [0, n_valid) scores -inf.  Other slots are not written.
+ * Requires score_stride >= max_candidates. */
+csa2_status csa2_index_scores(const csa2_dims *dims, int32_t B, const csa2_batch *batch,
+                              const float *idx_q, const float *idx_w, const float *idx_k,
+                              float *scores, int64_t score_stride, hipStream_t stream);
+
+/* Step 3 for every FULL / REINDEX query: from the scores of csa2_index_scores,
+ * write the first min(K, eligible) candidates under (score descending, row
+ * ascending) to topk_idx[b][*] in ascending row order, padded with -1.
+ * Eligible: candidate row in [0, n_valid).  Scores must be finite or -inf; +0
+ * and -0 tie.  Rows of REUSE / WINDOW queries are not written. */
+csa2_status csa2_topk(const csa2_dims *dims, int32_t B, const csa2_batch *batch, const float *scores,
+                      int64_t score_stride, int32_t *topk_idx, hipStream_t stream);
+
+/* Step 4 for every query: FULL / REINDEX / REUSE queries attend their window
+ * rows plus the pool rows named in topk_idx[b] (-1 skipped; duplicates count
+ * per occurrence; rows outside [0, pool_len) skipped); WINDOW queries attend
+ * their window rows only (topk_idx may be NULL if every query is WINDOW).
+ * win_kv may be NULL (no query then has window rows) and comp_kv may be NULL
+ * (no query then has compressed rows); fp8 scale planes are required exactly
+ * when their KV source is given.
+ * sink: f32 [64] or NULL.  With a workspace of csa2_workspace_size bytes the
+ * entries of a query may be split over several workgroups and merged; with
+ * workspace == NULL and workspace_bytes == 0 every query runs unsplit. */
+csa2_status csa2_attend(const csa2_dims *dims, int32_t B, const csa2_batch *batch, const void *q,
+                        const void *win_kv, const uint8_t *win_scale, const void *comp_kv,
+                        const uint8_t *comp_scale, const int32_t *topk_idx, const float *sink,
+                        float *out, float *lse, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/* The whole step for a decode batch of independent queries with per-query
+ * modes: scores + top-K for FULL / REINDEX queries (their topk_idx rows are
+ * written), then attention for all (REUSE rows of topk_idx are read). */
+csa2_status csa2_decode(const csa2_dims *dims, int32_t B, const csa2_batch *batch, const void *q,
+                        const float *idx_q, const float *idx_w, const float *idx_k,
+                        const void *win_kv, const uint8_t *win_scale, const void *comp_kv,
+                        const uint8_t *comp_scale, int32_t *topk_idx, const float *sink,
+                        float *out, float *lse, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/* Workspace bytes for csa2_prefill on this chunk. */
+csa2_status csa2_prefill_workspace_size(const csa2_dims *dims, const csa2_prefill_desc *desc,
+                                        size_t *bytes);
+
+/* The whole step for one prefill chunk (T queries of one sequence sharing its
+ * window rows, pool and index keys).  Per query t at p = pos0 + t: window rows
+ * as in csa2_prefill_desc; reachability, scores and top-K as for decode; q,
+ * idx_q, topk_idx, out and lse are indexed by t. */
+csa2_status csa2_prefill(const csa2_dims *dims, const csa2_prefill_desc *desc, const void *q,
+                         const float *idx_q, const float *idx_w, const float *idx_k,
+                         const void *win_kv, const uint8_t *win_scale, const void *comp_kv,
+                         const uint8_t *comp_scale, int32_t *topk_idx, const float *sink,
+                         float *out, float *lse, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA2_H */

@@ -1,0 +1,381 @@
+// Two-source single-softmax attention (Reading Notes of DeepSeek-V4.1-Flash,
+// section 3f C2 Step 3; "DeepSeek-V4.1-Flash on WASTE", What is new, 1. CSA2):
+// each query's 64 heads attend, in ONE softmax, over its window rows followed
+// by its selected compressed rows.  Every KV row (512 dims) serves all heads
+// as both key and value.  An optional per-head sink logit joins only the
+// denominator; a query with no entry yields zeros (PocketLLM page, "The op
+// layer").
+//
+// Workgroup = one (query, split) pair, 4 waves; wave w owns heads 16w..16w+15.
+// Entries are processed in chunks of 32 rows staged in LDS (double buffered;
+// the next chunk's global loads are in flight while the current one is used):
+//   S^T (32 entries x 16 heads) = K (32 x 512) * Q^T      v_mfma_f32_16x16x32_bf16
+//   online softmax per head in fp32 (exp2 domain)
+//   O^T (512 dims x 16 heads) += V^T (512 x 32) * P^T       same MFMA
+// Putting the entries on the M side of the first product leaves each lane's
+// probabilities (head = lane % 16, 8 entries) exactly where the second
+// product's B operand needs them, so P never leaves registers.  V^T fragments
+// come straight out of the row-major LDS tile with the gfx950 transposing LDS
+// read (ds_read_b64_tr_b16).  Rows are XOR-swizzled in 16-byte units so both
+// the row reads of the first product and the transposed reads of the second
+// spread over all LDS banks.
+//
+// FP8 rows (E4M3 with one UE8M0 scale per 32 values) are widened to bf16 while
+// staging; the conversion is exact (4 significant bits times a power of two).
+#include "csa2_internal.h"
+
+namespace csa2 {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int kChunk = 32;                         // entries per staged chunk
+constexpr int kRowBytes = kDim * 2;                // one bf16 row in LDS
+constexpr int kBufBytes = kChunk * kRowBytes;      // 32 KiB per buffer
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct AttendArgs {
+  const int64_t* pos;
+  const int32_t* mode;
+  const int64_t* win_row0;
+  const int32_t* win_len;
+  const int64_t* pool_row0;
+  const int32_t* pool_len;
+  const uint16_t* q;
+  const uint8_t* win_kv;
+  const uint8_t* win_scale;
+  const uint8_t* comp_kv;
+  const uint8_t* comp_scale;
+  const int32_t* topk;
+  const float* sink;
+  float* out;
+  float* lse;
+  float* part_o;   // [B][S][64][512] unnormalised partial outputs (split only)
+  float* part_ml;  // [B][S][64][2]   running max (log2 units) and sum
+  int32_t K;
+  int32_t W;
+  int32_t n_split;
+  float scale_log2;  // softmax_scale * log2(e)
+};
+
+// 16-byte unit u of LDS row r lives at unit u ^ f(r); f is a bijection on 0..15
+// with f(r) = f(r + 16), chosen so 16 consecutive rows at one unit, and 8 rows x
+// 2 adjacent units, each land on distinct bank groups.
+__device__ __forceinline__ int swz_unit(int r, int u) { return u ^ (((r << 1) + (r >> 3)) & 15); }
+__device__ __forceinline__ int lds_off(int r, int byte) {
+  return r * kRowBytes + (swz_unit(r, byte >> 4) << 4) + (byte & 15);
+}
+
+// Widen 8 E4M3 codes (two dwords) times 2^e to 8 bf16 (exact).
+__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 codes, int e) {
+  float f[8];
+  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(codes.x, false);
+  const auto bq = __builtin_amdgcn_cvt_pk_f32_fp8(codes.x, true);
+  const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(codes.y, false);
+  const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(codes.y, true);
+  f[0] = a[0], f[1] = a[1], f[2] = bq[0], f[3] = bq[1], f[4] = c[0], f[5] = c[1], f[6] = d[0], f[7] = d[1];
+  uint32_t h[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) h[i] = __float_as_uint(__builtin_ldexpf(f[i], e)) >> 16;
+  return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+}
+
+template <int KV>
+__global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kBufBytes];  // 2 chunk buffers
+  __shared__ int64_t ent_s[kMaxEntries];  // >= 0: window row; < 0: -(pool row) - 1
+  __shared__ uint32_t wcnt_s[4];
+
+  const int b = blockIdx.x / a.n_split;
+  const int sp = blockIdx.x % a.n_split;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int g = lane >> 4, l16 = lane & 15;
+
+  // ---- entry list: window rows, then the selected pool rows in list order ----
+  int wl = a.win_kv ? a.win_len[b] : 0;  // no window rows without a window source
+  wl = wl < 0 ? 0 : (wl > a.W ? a.W : wl);
+  const int64_t w0 = a.win_row0[b];
+  for (int e = t; e < wl; e += 256) ent_s[e] = w0 + e;
+  const int md = a.mode[b];
+  uint32_t nsel = 0;
+  if (md != CSA2_MODE_WINDOW && a.topk != nullptr && a.comp_kv != nullptr) {
+    const int32_t plen = a.pool_len[b];
+    const int64_t p0 = a.pool_row0[b];
+    const int32_t* lst = a.topk + (int64_t)b * a.K;
+    for (int r0 = 0; r0 < a.K; r0 += 256) {
+      const int i = r0 + t;
+      int32_t idx = (i < a.K) ? lst[i] : -1;
+      const bool ok = idx >= 0 && idx < plen;
+      const uint64_t m = __ballot(ok);
+      if (lane == 0) wcnt_s[wv] = __popcll(m);
+      __syncthreads();
+      uint32_t before = nsel, tot = 0;
+      for (int w = 0; w < 4; ++w) {
+        if (w < wv) before += wcnt_s[w];
+        tot += wcnt_s[w];
+      }
+      before += __popcll(m & ((1ull << lane) - 1ull));
+      if (ok) ent_s[wl + before] = -(p0 + idx) - 1;
+      nsel += tot;
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+  const int E = wl + (int)nsel;
+  const int nch = (E + kChunk - 1) / kChunk;
+  const int cps = (nch + a.n_split - 1) / a.n_split;
+  const int cbeg = sp * cps;
+  const int cend = (cbeg + cps < nch) ? cbeg + cps : nch;
+
+  // ---- this wave's 16 heads of q, as the B operand (dims x heads) ----
+  const int head = wv * 16 + l16;
+  bf16x8 qf[16];
+  {
+    const uint16_t* qp = a.q + ((int64_t)b * kHeads + head) * kDim + g * 8;
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qp + kk * 32);
+      qf[kk] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  f32x4 acc[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -__builtin_inff(), l_run = 0.f;
+
+  // ---- staging: 32 rows per chunk, one row per wave instruction ----
+  constexpr int kPieces = 8;  // 16-byte LDS pieces per thread per chunk
+  uint4 stage[kPieces];
+  auto fetch = [&](int c) {
+#pragma unroll
+    for (int it = 0; it < kPieces; ++it) {
+      const int p = it * 256 + t;
+      const int er = p >> 6, u = p & 63;
+      const int e = c * kChunk + er;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (e < E) {
+        const int64_t ev = ent_s[e];
+        const bool pool = ev < 0;
+        const int64_t row = pool ? (-ev - 1) : ev;
+        if (KV == CSA2_KV_BF16) {
+          const uint8_t* base = pool ? a.comp_kv : a.win_kv;
+          v = *reinterpret_cast<const uint4*>(base + row * kRowBytes + u * 16);
+        } else {
+          const uint8_t* base = pool ? a.comp_kv : a.win_kv;
+          const uint8_t* sc = pool ? a.comp_scale : a.win_scale;
+          const uint2 codes = *reinterpret_cast<const uint2*>(base + row * kDim + u * 8);
+          const int ex = (int)sc[row * (kDim / kScaleBlock) + (u >> 2)] - 127;
+          v = fp8x8_to_bf16x8(codes, ex);
+        }
+      }
+      stage[it] = v;
+    }
+  };
+  auto stash = [&](int buf) {
+    uint8_t* base = smem + buf * kBufBytes;
+#pragma unroll
+    for (int it = 0; it < kPieces; ++it) {
+      const int p = it * 256 + t;
+      *reinterpret_cast<uint4*>(base + lds_off(p >> 6, (p & 63) * 16)) = stage[it];
+    }
+  };
+
+  if (cbeg < cend) {
+    fetch(cbeg);
+    stash(0);
+  }
+  __syncthreads();
+
+  for (int c = cbeg; c < cend; ++c) {
+    const int buf = (c - cbeg) & 1;
+    if (c + 1 < cend) fetch(c + 1);
+    const uint8_t* base = smem + buf * kBufBytes;
+
+    // S^T = K Q^T: rows 0-15 and 16-31 of the chunk
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      const uint4 k0 = *reinterpret_cast<const uint4*>(base + lds_off(l16, kk * 64 + g * 16));
+      const uint4 k1 = *reinterpret_cast<const uint4*>(base + lds_off(16 + l16, kk * 64 + g * 16));
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k0), qf[kk], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k1), qf[kk], s1, 0, 0, 0);
+    }
+    // lane holds head `head`, entries c*32 + 4g + i and c*32 + 16 + 4g + i
+    float sv[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e0 = c * kChunk + 4 * g + i, e1 = e0 + 16;
+      sv[i] = (e0 < E) ? s0[i] * a.scale_log2 : -__builtin_inff();
+      sv[4 + i] = (e1 < E) ? s1[i] * a.scale_log2 : -__builtin_inff();
+    }
+    float cmax = sv[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) cmax = fmaxf(cmax, sv[i]);
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+    const float m_new = fmaxf(m_run, cmax);
+    float alpha = 1.f, pv[8], rs = 0.f;
+    if (m_new == -__builtin_inff()) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pv[i] = 0.f;
+    } else {
+      alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_new);
+        rs += pv[i];
+      }
+    }
+    rs += __shfl_xor(rs, 16);
+    rs += __shfl_xor(rs, 32);
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+    bf16x8 pb;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pb[i] = (__bf16)pv[i];
+
+    // O^T += V^T P^T, 32 tiles of 16 dims
+    const int tj = (lane >> 2) & 3, tc = lane & 3;
+    const int r_lo = 4 * g + tj, r_hi = 16 + 4 * g + tj;
+#pragma unroll
+    for (int tt = 0; tt < 32; ++tt) {
+      const int byte = tt * 32 + tc * 8;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)((__attribute__((address_space(3))) uint8_t*)(base + lds_off(r_lo, byte))));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)((__attribute__((address_space(3))) uint8_t*)(base + lds_off(r_hi, byte))));
+      typedef short s16x8 __attribute__((ext_vector_type(8)));
+      const s16x8 v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      acc[tt] *= alpha;
+      acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v8), pb, acc[tt], 0, 0, 0);
+    }
+
+    if (c + 1 < cend) stash(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds O^T[16*tt + 4g + i][head] ----
+  if (a.n_split == 1) {
+    float M = m_run, L = l_run, f;
+    if (a.sink) {
+      const float s2 = a.sink[head] * kLog2e;
+      const float M2 = fmaxf(M, s2);
+      L = L * __builtin_amdgcn_exp2f(M - M2) + __builtin_amdgcn_exp2f(s2 - M2);
+      f = __builtin_amdgcn_exp2f(M - M2) / L;
+      M = M2;
+    } else {
+      f = (L > 0.f) ? 1.f / L : 0.f;
+    }
+    float* op = a.out + ((int64_t)b * kHeads + head) * kDim + 4 * g;
+#pragma unroll
+    for (int tt = 0; tt < 32; ++tt) {
+      const f32x4 v = acc[tt] * f;
+      *reinterpret_cast<float4*>(op + tt * 16) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+    if (a.lse && g == 0) a.lse[(int64_t)b * kHeads + head] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -__builtin_inff();
+  } else {
+    const int64_t slot = ((int64_t)b * a.n_split + sp) * kHeads + head;
+    float* op = a.part_o + slot * kDim + 4 * g;
+#pragma unroll
+    for (int tt = 0; tt < 32; ++tt)
+      *reinterpret_cast<float4*>(op + tt * 16) = make_float4(acc[tt][0], acc[tt][1], acc[tt][2], acc[tt][3]);
+    if (g == 0) {
+      a.part_ml[slot * 2] = m_run;
+      a.part_ml[slot * 2 + 1] = l_run;
+    }
+  }
+}
+
+// Merge the split partials of one (query, head): log-sum-exp weights.
+__global__ __launch_bounds__(128) void attend_combine(int32_t n_split, const float* __restrict__ part_o,
+                                                     const float* __restrict__ part_ml,
+                                                     const float* __restrict__ sink, float* __restrict__ out,
+                                                     float* __restrict__ lse) {
+  const int b = blockIdx.x / kHeads, h = blockIdx.x % kHeads;
+  const int t = threadIdx.x;
+  const int64_t slot0 = (int64_t)b * n_split * kHeads + h;
+  float M = -__builtin_inff();
+  for (int s = 0; s < n_split; ++s) M = fmaxf(M, part_ml[(slot0 + (int64_t)s * kHeads) * 2]);
+  float s2 = -__builtin_inff();
+  if (sink) {
+    s2 = sink[h] * kLog2e;
+    M = fmaxf(M, s2);
+  }
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  float L = 0.f;
+  if (M != -__builtin_inff()) {
+    for (int s = 0; s < n_split; ++s) {
+      const int64_t slot = slot0 + (int64_t)s * kHeads;
+      const float ms = part_ml[slot * 2];
+      if (ms == -__builtin_inff()) continue;
+      const float w = __builtin_amdgcn_exp2f(ms - M);
+      L += w * part_ml[slot * 2 + 1];
+      const float4 v = *reinterpret_cast<const float4*>(part_o + slot * kDim + t * 4);
+      o.x += w * v.x, o.y += w * v.y, o.z += w * v.z, o.w += w * v.w;
+    }
+    if (sink) L += __builtin_amdgcn_exp2f(s2 - M);
+  }
+  const float f = (L > 0.f) ? 1.f / L : 0.f;
+  *reinterpret_cast<float4*>(out + ((int64_t)b * kHeads + h) * kDim + t * 4) =
+      make_float4(o.x * f, o.y * f, o.z * f, o.w * f);
+  if (lse && t == 0) lse[(int64_t)b * kHeads + h] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -__builtin_inff();
+}
+
+}  // namespace
+
+int attend_split_for(int32_t B) {
+  // aim for >= 256 workgroups (one per CU) when the batch alone gives fewer
+  int s = (B > 0) ? (256 + B - 1) / B : 1;
+  return s < 1 ? 1 : (s > 4 ? 4 : s);
+}
+
+size_t attend_partial_floats(int32_t B, int n_split) {
+  if (n_split <= 1) return 0;
+  return (size_t)B * n_split * kHeads * (kDim + 2);
+}
+
+hipError_t launch_attend(const csa2_dims& d, int32_t B, const csa2_batch& bt, const void* q,
+                         const void* win_kv, const uint8_t* win_scale, const void* comp_kv,
+                         const uint8_t* comp_scale, const int32_t* topk_idx, const float* sink,
+                         float* out, float* lse, int n_split, float* partial, hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  if (n_split < 1) n_split = 1;
+  AttendArgs a;
+  a.pos = bt.pos;
+  a.mode = bt.mode;
+  a.win_row0 = bt.win_row0;
+  a.win_len = bt.win_len;
+  a.pool_row0 = bt.pool_row0;
+  a.pool_len = bt.pool_len;
+  a.q = static_cast<const uint16_t*>(q);
+  a.win_kv = static_cast<const uint8_t*>(win_kv);
+  a.win_scale = win_scale;
+  a.comp_kv = static_cast<const uint8_t*>(comp_kv);
+  a.comp_scale = comp_scale;
+  a.topk = topk_idx;
+  a.sink = sink;
+  a.out = out;
+  a.lse = lse;
+  a.part_o = partial;
+  a.part_ml = partial ? partial + (size_t)B * n_split * kHeads * kDim : nullptr;
+  a.K = d.index_topk;
+  a.W = d.window;
+  a.n_split = n_split;
+  a.scale_log2 = d.softmax_scale * kLog2e;
+  if (d.kv_dtype == CSA2_KV_BF16)
+    hipLaunchKernelGGL(attend_kernel<CSA2_KV_BF16>, dim3(B * n_split), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(attend_kernel<CSA2_KV_FP8_E4M3_UE8M0_32>, dim3(B * n_split), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || n_split == 1) return e;
+  hipLaunchKernelGGL(attend_combine, dim3(B * kHeads), dim3(128), 0, s, n_split, a.part_o, a.part_ml, sink,
+                     out, lse);
+  return hipGetLastError();
+}
+
+}  // namespace csa2

@@ -1,0 +1,292 @@
+// C-ABI entry points of libcsa2 (declared in include/csa2.h): host-side
+// validation, workspace carving and kernel launches.  Nothing here allocates,
+// synchronizes or keeps a pointer.
+#include <math.h>
+#include <string.h>
+
+#include "csa2_internal.h"
+
+using namespace csa2;
+
+namespace {
+
+thread_local int32_t g_last_hip = 0;
+
+csa2_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return CSA2_OK;
+  g_last_hip = (int32_t)e;
+  return CSA2_ERR_HIP;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+csa2_status check_dims(const csa2_dims* d) {
+  if (!d) return CSA2_ERR_INVALID_ARG;
+  if (d->kv_dtype != CSA2_KV_BF16 && d->kv_dtype != CSA2_KV_FP8_E4M3_UE8M0_32) return CSA2_ERR_INVALID_ARG;
+  if (d->index_relu != 0 && d->index_relu != 1) return CSA2_ERR_INVALID_ARG;
+  if (!isfinite(d->softmax_scale)) return CSA2_ERR_INVALID_ARG;
+  if (d->window < 0 || d->index_topk < 1 || d->index_heads < 1) return CSA2_ERR_INVALID_ARG;
+  if (d->n_heads != kHeads || d->head_dim != kDim || d->index_dim != kIndexDim) return CSA2_ERR_UNSUPPORTED;
+  if (d->window > kMaxWindow || d->index_topk > kMaxTopK || d->index_heads > 64) return CSA2_ERR_UNSUPPORTED;
+  return CSA2_OK;
+}
+
+csa2_status check_batch(const csa2_batch* bt, int32_t B) {
+  if (!bt || B < 0) return CSA2_ERR_INVALID_ARG;
+  if (B == 0) return CSA2_OK;
+  if (!bt->pos || !bt->mode || !bt->compress_ratio || !bt->win_row0 || !bt->win_len || !bt->pool_row0 ||
+      !bt->pool_len)
+    return CSA2_ERR_INVALID_ARG;
+  if (bt->max_candidates < 0) return CSA2_ERR_INVALID_ARG;
+  if ((bt->cand_off == nullptr) != (bt->cand_idx == nullptr)) return CSA2_ERR_INVALID_ARG;
+  return CSA2_OK;
+}
+
+size_t score_stride_for(int32_t max_cand) { return align_up((size_t)max_cand * sizeof(float)) / sizeof(float); }
+
+size_t decode_ws_bytes(int32_t B, int32_t max_cand) {
+  size_t s = align_up((size_t)B * score_stride_for(max_cand) * sizeof(float));
+  s += align_up(attend_partial_floats(B, attend_split_for(B)) * sizeof(float));
+  return s;
+}
+
+// Per-query prefill descriptors live at the front of the prefill workspace.
+struct PrefillMeta {
+  int64_t* pos;
+  int32_t* mode;
+  int32_t* ratio;
+  int64_t* win_row0;
+  int32_t* win_len;
+  int64_t* pool_row0;
+  int32_t* pool_len;
+};
+size_t prefill_meta_bytes(int32_t T) { return 3 * align_up((size_t)T * 8) + 4 * align_up((size_t)T * 4); }
+PrefillMeta carve_meta(uint8_t* p, int32_t T) {
+  PrefillMeta m;
+  const size_t a8 = align_up((size_t)T * 8), a4 = align_up((size_t)T * 4);
+  m.pos = (int64_t*)p, p += a8;
+  m.win_row0 = (int64_t*)p, p += a8;
+  m.pool_row0 = (int64_t*)p, p += a8;
+  m.mode = (int32_t*)p, p += a4;
+  m.ratio = (int32_t*)p, p += a4;
+  m.win_len = (int32_t*)p, p += a4;
+  m.pool_len = (int32_t*)p;
+  return m;
+}
+int32_t prefill_max_cand(const csa2_prefill_desc* p) {
+  if (p->mode == CSA2_MODE_FULL) return p->pool_len;
+  if (p->mode == CSA2_MODE_REINDEX) return p->max_candidates;
+  return 0;
+}
+
+csa2_status check_prefill(const csa2_dims* d, const csa2_prefill_desc* p) {
+  csa2_status st = check_dims(d);
+  if (st != CSA2_OK) return st;
+  if (!p || p->n_queries < 0 || p->pos0 < 0 || p->compress_ratio < 0 || p->pool_len < 0) return CSA2_ERR_INVALID_ARG;
+  if (p->mode < CSA2_MODE_FULL || p->mode > CSA2_MODE_WINDOW) return CSA2_ERR_INVALID_ARG;
+  if (p->win_pos0 < 0 || p->win_pos0 > p->pos0) return CSA2_ERR_INVALID_ARG;
+  if (p->mode == CSA2_MODE_REINDEX && (!p->cand_off || !p->cand_idx || p->max_candidates < 0))
+    return CSA2_ERR_INVALID_ARG;
+  return CSA2_OK;
+}
+
+}  // namespace
+
+// ---- prefill descriptors ----------------------------------------------------
+namespace csa2 {
+namespace {
+__global__ void prefill_meta_kernel(csa2_prefill_desc p, int32_t W, PrefillMeta m) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= p.n_queries) return;
+  const int64_t pos = p.pos0 + t;
+  int64_t lo = pos - W + 1;
+  if (lo < p.win_pos0) lo = p.win_pos0;
+  m.pos[t] = pos;
+  m.mode[t] = p.mode;
+  m.ratio[t] = p.compress_ratio;
+  m.win_row0[t] = lo - p.win_pos0;
+  m.win_len[t] = W > 0 ? (int32_t)(pos - lo + 1) : 0;
+  m.pool_row0[t] = 0;
+  m.pool_len[t] = p.pool_len;
+}
+}  // namespace
+}  // namespace csa2
+
+extern "C" {
+
+int csa2_abi_version(void) { return CSA2_ABI_VERSION; }
+
+const char* csa2_status_str(csa2_status s) {
+  switch (s) {
+    case CSA2_OK: return "ok";
+    case CSA2_ERR_INVALID_ARG: return "invalid argument";
+    case CSA2_ERR_UNSUPPORTED: return "unsupported geometry";
+    case CSA2_ERR_WORKSPACE: return "workspace missing or too small";
+    case CSA2_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t csa2_last_hip_error(void) { return g_last_hip; }
+
+csa2_status csa2_workspace_size(const csa2_dims* dims, int32_t B, int32_t max_candidates, size_t* bytes) {
+  csa2_status st = check_dims(dims);
+  if (st != CSA2_OK) return st;
+  if (!bytes || B < 0 || max_candidates < 0) return CSA2_ERR_INVALID_ARG;
+  *bytes = decode_ws_bytes(B, max_candidates);
+  return CSA2_OK;
+}
+
+csa2_status csa2_index_scores(const csa2_dims* dims, int32_t B, const csa2_batch* batch, const float* idx_q,
+                              const float* idx_w, const float* idx_k, float* scores, int64_t score_stride,
+                              hipStream_t stream) {
+  csa2_status st = check_dims(dims);
+  if (st == CSA2_OK) st = check_batch(batch, B);
+  if (st != CSA2_OK) return st;
+  if (B == 0 || batch->max_candidates == 0) return CSA2_OK;
+  if (!idx_q || !idx_k || !scores || score_stride < batch->max_candidates) return CSA2_ERR_INVALID_ARG;
+  return hip_status(launch_index_scores(*dims, B, *batch, idx_q, idx_w, idx_k, scores, score_stride, stream));
+}
+
+csa2_status csa2_topk(const csa2_dims* dims, int32_t B, const csa2_batch* batch, const float* scores,
+                      int64_t score_stride, int32_t* topk_idx, hipStream_t stream) {
+  csa2_status st = check_dims(dims);
+  if (st == CSA2_OK) st = check_batch(batch, B);
+  if (st != CSA2_OK) return st;
+  if (B == 0) return CSA2_OK;
+  if (!topk_idx || (batch->max_candidates > 0 && !scores) || score_stride < batch->max_candidates)
+    return CSA2_ERR_INVALID_ARG;
+  return hip_status(launch_topk(*dims, B, *batch, scores, score_stride, topk_idx, stream));
+}
+
+static csa2_status attend_common(const csa2_dims* dims, int32_t B, const csa2_batch* batch, const void* q,
+                                 const void* win_kv, const uint8_t* win_scale, const void* comp_kv,
+                                 const uint8_t* comp_scale, const int32_t* topk_idx, const float* sink,
+                                 float* out, float* lse, float* partial, int n_split, hipStream_t stream) {
+  return hip_status(launch_attend(*dims, B, *batch, q, win_kv, win_scale, comp_kv, comp_scale, topk_idx, sink,
+                                  out, lse, n_split, partial, stream));
+}
+
+static csa2_status check_attend_ptrs(const csa2_dims* dims, const void* q, const void* win_kv,
+                                     const uint8_t* win_scale, const void* comp_kv, const uint8_t* comp_scale,
+                                     float* out) {
+  if (!q || !out) return CSA2_ERR_INVALID_ARG;
+  if (dims->kv_dtype == CSA2_KV_FP8_E4M3_UE8M0_32 && ((win_kv && !win_scale) || (comp_kv && !comp_scale)))
+    return CSA2_ERR_INVALID_ARG;
+  return CSA2_OK;
+}
+
+csa2_status csa2_attend(const csa2_dims* dims, int32_t B, const csa2_batch* batch, const void* q,
+                        const void* win_kv, const uint8_t* win_scale, const void* comp_kv,
+                        const uint8_t* comp_scale, const int32_t* topk_idx, const float* sink, float* out,
+                        float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  csa2_status st = check_dims(dims);
+  if (st == CSA2_OK) st = check_batch(batch, B);
+  if (st == CSA2_OK && B > 0) st = check_attend_ptrs(dims, q, win_kv, win_scale, comp_kv, comp_scale, out);
+  if (st != CSA2_OK) return st;
+  if (B == 0) return CSA2_OK;
+  int n_split = 1;
+  float* partial = nullptr;
+  if (workspace != nullptr || workspace_bytes != 0) {
+    const int sp = attend_split_for(B);
+    const size_t need = align_up(attend_partial_floats(B, sp) * sizeof(float));
+    if (!workspace || workspace_bytes < need) return CSA2_ERR_WORKSPACE;
+    n_split = sp;
+    partial = static_cast<float*>(workspace);
+  }
+  return attend_common(dims, B, batch, q, win_kv, win_scale, comp_kv, comp_scale, topk_idx, sink, out, lse, partial,
+                       n_split, stream);
+}
+
+csa2_status csa2_decode(const csa2_dims* dims, int32_t B, const csa2_batch* batch, const void* q,
+                        const float* idx_q, const float* idx_w, const float* idx_k, const void* win_kv,
+                        const uint8_t* win_scale, const void* comp_kv, const uint8_t* comp_scale,
+                        int32_t* topk_idx, const float* sink, float* out, float* lse, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  csa2_status st = check_dims(dims);
+  if (st == CSA2_OK) st = check_batch(batch, B);
+  if (st == CSA2_OK && B > 0) st = check_attend_ptrs(dims, q, win_kv, win_scale, comp_kv, comp_scale, out);
+  if (st != CSA2_OK) return st;
+  if (B == 0) return CSA2_OK;
+  if (!topk_idx || (batch->max_candidates > 0 && (!idx_q || !idx_k))) return CSA2_ERR_INVALID_ARG;
+  const size_t need = decode_ws_bytes(B, batch->max_candidates);
+  if (!workspace || workspace_bytes < need) return CSA2_ERR_WORKSPACE;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const int64_t stride = (int64_t)score_stride_for(batch->max_candidates);
+  float* scores = reinterpret_cast<float*>(ws);
+  ws += align_up((size_t)B * stride * sizeof(float));
+  const int sp = attend_split_for(B);
+  float* partial = sp > 1 ? reinterpret_cast<float*>(ws) : nullptr;
+
+  if (batch->max_candidates > 0) {
+    if ((st = hip_status(launch_index_scores(*dims, B, *batch, idx_q, idx_w, idx_k, scores, stride, stream))) != CSA2_OK)
+      return st;
+    if ((st = hip_status(launch_topk(*dims, B, *batch, scores, stride, topk_idx, stream))) != CSA2_OK) return st;
+  }
+  return attend_common(dims, B, batch, q, win_kv, win_scale, comp_kv, comp_scale, topk_idx, sink, out, lse, partial, sp,
+                       stream);
+}
+
+csa2_status csa2_prefill_workspace_size(const csa2_dims* dims, const csa2_prefill_desc* desc, size_t* bytes) {
+  csa2_status st = check_prefill(dims, desc);
+  if (st != CSA2_OK) return st;
+  if (!bytes) return CSA2_ERR_INVALID_ARG;
+  const int32_t T = desc->n_queries;
+  *bytes = prefill_meta_bytes(T) + decode_ws_bytes(T, prefill_max_cand(desc));
+  return CSA2_OK;
+}
+
+csa2_status csa2_prefill(const csa2_dims* dims, const csa2_prefill_desc* desc, const void* q, const float* idx_q,
+                         const float* idx_w, const float* idx_k, const void* win_kv, const uint8_t* win_scale,
+                         const void* comp_kv, const uint8_t* comp_scale, int32_t* topk_idx, const float* sink,
+                         float* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  csa2_status st = check_prefill(dims, desc);
+  if (st != CSA2_OK) return st;
+  const int32_t T = desc->n_queries;
+  if (T == 0) return CSA2_OK;
+  if ((st = check_attend_ptrs(dims, q, win_kv, win_scale, comp_kv, comp_scale, out)) != CSA2_OK) return st;
+  const int32_t max_cand = prefill_max_cand(desc);
+  const bool selects = desc->mode == CSA2_MODE_FULL || desc->mode == CSA2_MODE_REINDEX;
+  if (desc->mode != CSA2_MODE_WINDOW && !topk_idx) return CSA2_ERR_INVALID_ARG;
+  if (selects && max_cand > 0 && (!idx_q || !idx_k)) return CSA2_ERR_INVALID_ARG;
+  size_t need = prefill_meta_bytes(T) + decode_ws_bytes(T, max_cand);
+  if (!workspace || workspace_bytes < need) return CSA2_ERR_WORKSPACE;
+
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  PrefillMeta m = carve_meta(ws, T);
+  ws += prefill_meta_bytes(T);
+  const int64_t stride = (int64_t)score_stride_for(max_cand);
+  float* scores = reinterpret_cast<float*>(ws);
+  ws += align_up((size_t)T * stride * sizeof(float));
+  const int sp = attend_split_for(T);
+  float* partial = sp > 1 ? reinterpret_cast<float*>(ws) : nullptr;
+
+  hipLaunchKernelGGL(prefill_meta_kernel, dim3((T + 255) / 256), dim3(256), 0, stream, *desc, dims->window, m);
+  if ((st = hip_status(hipGetLastError())) != CSA2_OK) return st;
+  csa2_batch bt;
+  bt.pos = m.pos;
+  bt.mode = m.mode;
+  bt.compress_ratio = m.ratio;
+  bt.win_row0 = m.win_row0;
+  bt.win_len = m.win_len;
+  bt.pool_row0 = m.pool_row0;
+  bt.pool_len = m.pool_len;
+  bt.cand_off = desc->mode == CSA2_MODE_REINDEX ? desc->cand_off : nullptr;
+  bt.cand_idx = desc->mode == CSA2_MODE_REINDEX ? desc->cand_idx : nullptr;
+  bt.max_candidates = max_cand;
+
+  if (selects && max_cand > 0) {
+    if (desc->mode == CSA2_MODE_FULL && dims->index_heads == 1)
+      st = hip_status(launch_index_scores_prefill(*dims, T, m.pos, desc->mode, desc->compress_ratio, desc->pool_len,
+                                                  idx_q, idx_w, idx_k, scores, stride, stream));
+    else
+      st = hip_status(launch_index_scores(*dims, T, bt, idx_q, idx_w, idx_k, scores, stride, stream));
+    if (st != CSA2_OK) return st;
+    if ((st = hip_status(launch_topk(*dims, T, bt, scores, stride, topk_idx, stream))) != CSA2_OK) return st;
+  }
+  return attend_common(dims, T, &bt, q, win_kv, win_scale, comp_kv, comp_scale,
+                       desc->mode == CSA2_MODE_WINDOW ? nullptr : topk_idx, sink, out, lse, partial, sp, stream);
+}
+
+}  // extern "C"

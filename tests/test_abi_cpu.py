@@ -1,0 +1,129 @@
+"""Host-side checks of the C-ABI library: it loads, exports every entry point
+include/csa2.h declares, and rejects bad arguments before launching anything.
+No call here reaches a kernel launch."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from sparse_long_context_amd import csa2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "csa2.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa2_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_documented_entry_points():
+    names = declared_functions()
+    for n in ["csa2_index_scores", "csa2_topk", "csa2_attend", "csa2_decode", "csa2_prefill",
+              "csa2_workspace_size", "csa2_prefill_workspace_size", "csa2_status_str", "csa2_abi_version",
+              "csa2_last_hip_error"]:
+        assert n in names, n
+
+
+def test_library_exports_every_declared_symbol():
+    L = csa2.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    assert set(declared_functions()) == set(csa2.EXPORTS)
+    assert csa2.csa2_abi_version() == 1
+    assert csa2.status_str(0) == "ok"
+
+
+def dims(**kw):
+    d = dict(n_heads=64, head_dim=512, window=128, index_topk=512, index_dim=128, index_heads=1,
+             index_relu=0, kv_dtype=0, softmax_scale=1.0)
+    d.update(kw)
+    return csa2.Dims.from_dict(d)
+
+
+FAKE = 0x1000  # never dereferenced: validation fails before any launch
+
+
+def batch(**kw):
+    b = csa2.Batch(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 16)
+    for k, v in kw.items():
+        setattr(b, k, v)
+    return b
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_heads=32), csa2.CSA2_ERR_UNSUPPORTED),
+    (dict(head_dim=256), csa2.CSA2_ERR_UNSUPPORTED),
+    (dict(index_dim=64), csa2.CSA2_ERR_UNSUPPORTED),
+    (dict(index_topk=513), csa2.CSA2_ERR_UNSUPPORTED),
+    (dict(window=129), csa2.CSA2_ERR_UNSUPPORTED),
+    (dict(index_heads=65), csa2.CSA2_ERR_UNSUPPORTED),
+    (dict(index_topk=0), csa2.CSA2_ERR_INVALID_ARG),
+    (dict(window=-1), csa2.CSA2_ERR_INVALID_ARG),
+    (dict(kv_dtype=2), csa2.CSA2_ERR_INVALID_ARG),
+    (dict(index_relu=2), csa2.CSA2_ERR_INVALID_ARG),
+    (dict(softmax_scale=float("nan")), csa2.CSA2_ERR_INVALID_ARG),
+])
+def test_bad_dims_rejected_everywhere(kw, status):
+    d = dims(**kw)
+    with pytest.raises(csa2.Csa2Error) as e:
+        csa2.csa2_workspace_size(d, 4, 100)
+    assert e.value.status == status
+    with pytest.raises(csa2.Csa2Error) as e:
+        csa2.csa2_decode(d, 4, batch(), FAKE, FAKE, None, FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, None,
+                         FAKE, 1 << 30, stream=0)
+    assert e.value.status == status
+
+
+def test_bad_arguments_rejected_before_launch():
+    d = dims()
+    E = csa2.Csa2Error
+    with pytest.raises(E) as e:  # negative batch
+        csa2.csa2_index_scores(d, -1, batch(), FAKE, None, FAKE, FAKE, 16, stream=0)
+    assert e.value.status == csa2.CSA2_ERR_INVALID_ARG
+    with pytest.raises(E) as e:  # missing descriptor array
+        csa2.csa2_topk(d, 2, batch(pos=None), FAKE, 16, FAKE, stream=0)
+    assert e.value.status == csa2.CSA2_ERR_INVALID_ARG
+    with pytest.raises(E) as e:  # stride below the candidate bound
+        csa2.csa2_index_scores(d, 2, batch(), FAKE, None, FAKE, FAKE, 15, stream=0)
+    assert e.value.status == csa2.CSA2_ERR_INVALID_ARG
+    with pytest.raises(E) as e:  # list offsets without a list
+        csa2.csa2_topk(d, 2, batch(cand_off=FAKE), FAKE, 16, FAKE, stream=0)
+    assert e.value.status == csa2.CSA2_ERR_INVALID_ARG
+    with pytest.raises(E) as e:  # fp8 without scale planes
+        csa2.csa2_attend(dims(kv_dtype=1), 2, batch(), FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, None, None,
+                         0, stream=0)
+    assert e.value.status == csa2.CSA2_ERR_INVALID_ARG
+    with pytest.raises(E) as e:  # no output
+        csa2.csa2_attend(d, 2, batch(), FAKE, FAKE, None, FAKE, None, FAKE, None, None, None, None, 0, stream=0)
+    assert e.value.status == csa2.CSA2_ERR_INVALID_ARG
+    with pytest.raises(E) as e:  # workspace too small
+        csa2.csa2_decode(d, 2, batch(), FAKE, FAKE, None, FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, None,
+                         FAKE, 16, stream=0)
+    assert e.value.status == csa2.CSA2_ERR_WORKSPACE
+    with pytest.raises(E) as e:  # attend: workspace given but too small
+        csa2.csa2_attend(d, 2, batch(), FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 16, stream=0)
+    assert e.value.status == csa2.CSA2_ERR_WORKSPACE
+
+
+def test_prefill_descriptor_validation():
+    d = dims()
+    desc = csa2.PrefillDesc(1000, 10, csa2.MODE_FULL, 4, 250, 900, None, None, 0)
+    assert csa2.csa2_prefill_workspace_size(d, desc) > 0
+    for bad in [dict(win_pos0=1001), dict(n_queries=-1), dict(mode=7), dict(compress_ratio=-2),
+                dict(mode=csa2.MODE_REINDEX)]:
+        dd = csa2.PrefillDesc(1000, 10, csa2.MODE_FULL, 4, 250, 900, None, None, 0)
+        for k, v in bad.items():
+            setattr(dd, k, v)
+        with pytest.raises(csa2.Csa2Error) as e:
+            csa2.csa2_prefill_workspace_size(d, dd)
+        assert e.value.status == csa2.CSA2_ERR_INVALID_ARG
+
+
+def test_zero_sized_calls_are_noops():
+    d = dims()
+    csa2.csa2_index_scores(d, 0, batch(), None, None, None, None, 0, stream=0)
+    csa2.csa2_topk(d, 0, batch(), None, 0, None, stream=0)
+    csa2.csa2_attend(d, 0, batch(), None, None, None, None, None, None, None, None, None, None, 0, stream=0)
+    assert csa2.csa2_workspace_size(d, 0, 0) >= 0

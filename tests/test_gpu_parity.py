@@ -1,0 +1,313 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Selected indices must match bit for bit; outputs must agree per query to a
+normwise relative error max|o - o_ref| / max|o_ref| <= 1e-2 (bf16 KV) or 3e-2
+(fp8 KV).  Stages are also checked in isolation by feeding each one the
+oracle's intermediates.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import oracle as O  # noqa: E402
+from sparse_long_context_amd import csa2, synth  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+TOL = {synth.KV_BF16: 1e-2, synth.KV_FP8: 3e-2}
+LSE_TOL = 2e-3
+
+
+def say(*a):
+    print("[gpu-parity]", *a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    csa2.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def normwise(a, ref):
+    m = float(np.abs(ref).max())
+    if m == 0.0:
+        return 0.0 if float(np.abs(a).max()) == 0.0 else float("inf")
+    return float(np.abs(a - ref).max()) / m
+
+
+def run_decode(inp, sink=None):
+    w = csa2.DecodeWorkload(inp, sink=sink)
+    w.decode()
+    torch.cuda.synchronize()
+    return w, w.topk.cpu().numpy(), w.out.cpu().numpy(), w.lse.cpu().numpy()
+
+
+def compare(inp, sel_g, out_g, lse_g, queries=None, sink=None, scale=1.0):
+    qs = np.arange(inp["B"]) if queries is None else np.asarray(queries)
+    sel_o, out_o, lse_o = O.decode_batch(inp, qs, sink=sink, scale=scale)
+    tol = TOL[inp["dims"]["kv_dtype"]]
+    worst = 0.0
+    for i, b in enumerate(qs):
+        if inp["mode"][b] in (synth.MODE_FULL, synth.MODE_REINDEX):
+            assert np.array_equal(sel_g[b], sel_o[i]), f"query {b}: selection differs"
+        err = normwise(out_g[b], out_o[i])
+        worst = max(worst, err)
+        assert err <= tol, f"query {b}: normwise error {err:.3e} > {tol}"
+        fin = np.isfinite(lse_o[i])
+        assert np.array_equal(fin, np.isfinite(lse_g[b])), f"query {b}: lse finiteness"
+        assert np.abs(lse_g[b][fin] - lse_o[i][fin]).max(initial=0.0) <= LSE_TOL, f"query {b}: lse"
+    return worst
+
+
+def small_dims(**kw):
+    d = synth.default_dims()
+    d.update(kw)
+    return d
+
+
+# ---------------------------------------------------------------------------
+# stages in isolation
+# ---------------------------------------------------------------------------
+
+def test_index_scores_bit_exact_full_and_reindex():
+    ctx = [4096 + 4 * 37, 999, 64 * 1024 + 4, 3, 20000]
+    modes = [0, 1, 0, 0, 1]
+    inp = synth.decode_batch(11, ctx, modes, [4] * 5, dims=small_dims())
+    synth.add_reindex_lists(inp, 11, frac=0.4)
+    say("index scores: B=5 ragged pools", list(inp["pool_len"]))
+    w = csa2.DecodeWorkload(inp)
+    stride = w.max_cand + 3
+    scores = torch.full((w.B, stride), float("nan"), device="cuda")
+    csa2.csa2_index_scores(w.dims, w.B, w.batch, w.idx_q, w.idx_w, w.idx_k, scores, stride)
+    torch.cuda.synchronize()
+    sg = scores.cpu().numpy()
+    for b in range(w.B):
+        p0, pl = int(inp["pool_row0"][b]), int(inp["pool_len"][b])
+        keys = inp["idx_k"][p0:p0 + pl]
+        nv = O.n_valid(inp["pos"][b], 4, modes[b], pl)
+        if modes[b] == 0:
+            ref, _, _ = O.index_scores(inp["idx_q"][b], keys, n=nv)
+            got = sg[b, :nv]
+        else:
+            lst = inp["cand_idx"][inp["cand_off"][b]:inp["cand_off"][b + 1]]
+            ref, _, _ = O.index_scores(inp["idx_q"][b], keys, cand=lst)
+            ref = np.where(lst < nv, ref, -np.inf).astype(np.float32)
+            got = sg[b, :len(lst)]
+        assert got.tobytes() == ref.tobytes(), f"query {b}"
+        # slots past the candidate count are not written
+        n = nv if modes[b] == 0 else len(got)
+        assert np.isnan(sg[b, n:]).all()
+
+
+@pytest.mark.parametrize("n,k", [(100, 512), (512, 512), (513, 512), (3000, 512), (16384, 512), (40000, 512),
+                                 (65536, 512), (5000, 1), (5000, 37)])
+def test_topk_from_oracle_scores_with_ties(n, k):
+    rng = np.random.default_rng(n + k)
+    B = 3
+    s = (rng.integers(-64, 64, size=(B, n)) / 8).astype(np.float32)  # heavy ties
+    s[0] = rng.standard_normal(n).astype(np.float32)
+    s[2, rng.integers(0, n, size=n // 3)] = -0.0
+    s[2, rng.integers(0, n, size=n // 3)] = 0.0
+    dims = synth.default_dims(index_topk=k)
+    inp = dict(B=B, pos=np.full(B, n - 1, np.int64), mode=np.zeros(B, np.int32), ratio=np.ones(B, np.int32),
+               win_row0=np.zeros(B, np.int64), win_len=np.zeros(B, np.int32), pool_row0=np.zeros(B, np.int64),
+               pool_len=np.full(B, n, np.int32))
+    dev = {kk: torch.from_numpy(v).cuda() for kk, v in inp.items() if kk != "B"}
+    bt = csa2.Batch(*(dev[x].data_ptr() for x in ["pos", "mode", "ratio", "win_row0", "win_len", "pool_row0",
+                                                   "pool_len"]), None, None, n)
+    sc = torch.from_numpy(s).cuda()
+    out = torch.full((B, k), -7, dtype=torch.int32, device="cuda")
+    say(f"topk n={n} k={k}")
+    csa2.csa2_topk(csa2.Dims.from_dict(dims), B, bt, sc, n, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for b in range(B):
+        assert np.array_equal(got[b], O.topk(s[b], k)), f"row {b}"
+
+
+def test_attend_reuse_lists_with_padding_and_duplicates():
+    ctx = [30000, 2000, 500, 128 * 4 + 8]
+    inp = synth.decode_batch(12, ctx, [synth.MODE_REUSE] * 4, [4] * 4, dims=small_dims())
+    sel = inp["sel_in"]
+    sel[1, 100:200] = -1                 # holes in the middle
+    sel[2, :] = -1                       # nothing selected: window only
+    sel[3, 5:10] = sel[3, 0]             # duplicates count per occurrence
+    inp["win_len"][2] = 0                # ... and no window either: zeros
+    say("attend reuse: holes, empty, duplicates")
+    _, sg, og, lg = run_decode(inp)
+    compare(inp, sg, og, lg)
+    assert (og[2] == 0).all() and np.isneginf(lg[2]).all()
+
+
+# ---------------------------------------------------------------------------
+# whole decode step, small shapes (several tiles + ragged tails)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kv", [synth.KV_BF16, synth.KV_FP8])
+def test_decode_full_ragged(kv):
+    ctx = [1000, 4096 + 4 * 300 + 3, 70001, 4 * 513, 2, 12345, 4 * 512 + 3]
+    inp = synth.decode_batch(13 + kv, ctx, [synth.MODE_FULL] * len(ctx), [4] * len(ctx),
+                             dims=small_dims(kv_dtype=kv))
+    say("decode full ragged kv", kv, "pools", list(inp["pool_len"]))
+    _, sg, og, lg = run_decode(inp)
+    worst = compare(inp, sg, og, lg)
+    say(f"  worst normwise error {worst:.2e}")
+    # a query whose position precedes its first block end has no compressed entry
+    assert (sg[4] == -1).all()
+
+
+def test_decode_mixed_modes_sink_scale():
+    ctx = [9000, 9000, 9000, 9000, 300, 50000, 77, 20000]
+    modes = [0, 1, 2, 3, 0, 1, 3, 2]
+    ratios = [4, 4, 4, 0, 4, 4, 0, 4]
+    dims = small_dims(softmax_scale=0.8)
+    inp = synth.decode_batch(14, ctx, modes, ratios, dims=dims)
+    synth.add_reindex_lists(inp, 14, frac=0.3)
+    sink = synth.normal_f32(14, 77, (64,))
+    say("decode mixed modes + sink + scale 0.8")
+    _, sg, og, lg = run_decode(inp, sink=sink)
+    compare(inp, sg, og, lg, sink=sink, scale=0.8)
+
+
+@pytest.mark.parametrize("k,w", [(1, 16), (7, 0), (100, 128), (512, 1)])
+def test_decode_small_topk_and_window(k, w):
+    ctx = [5000, 130, 64 * 40]
+    dims = small_dims(index_topk=k, window=w)
+    inp = synth.decode_batch(15, ctx, [0] * 3, [4] * 3, dims=dims)
+    say(f"decode k={k} window={w}")
+    _, sg, og, lg = run_decode(inp)
+    compare(inp, sg, og, lg)
+
+
+def test_attend_split_matches_unsplit():
+    inp = synth.decode_batch(16, [20000] * 3, [0] * 3, [4] * 3, dims=small_dims())
+    w = csa2.DecodeWorkload(inp)
+    w.decode()
+    out_split = w.out.clone()
+    out_one = torch.empty_like(w.out)
+    lse_one = torch.empty_like(w.lse)
+    csa2.csa2_attend(w.dims, w.B, w.batch, w.q, w.win_kv, None, w.comp_kv, None, w.topk, None, out_one, lse_one,
+                     None, 0)
+    torch.cuda.synchronize()
+    a, b = out_split.cpu().numpy(), out_one.cpu().numpy()
+    # the two differ only by where the probabilities are rounded to bf16 (each
+    # split rounds relative to its own running maximum); both must meet the bar
+    assert w.B * 4 <= 256 and not np.array_equal(a, b)
+    compare(inp, w.topk.cpu().numpy(), a, w.lse.cpu().numpy())
+    compare(inp, w.topk.cpu().numpy(), b, lse_one.cpu().numpy())
+
+
+def test_decode_is_deterministic():
+    inp = synth.decode_batch(17, [60000, 8000], [0, 0], [4, 4], dims=small_dims())
+    w = csa2.DecodeWorkload(inp)
+    w.decode()
+    o1, s1, l1 = w.out.clone(), w.topk.clone(), w.lse.clone()
+    w.decode()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, w.out) and torch.equal(s1, w.topk) and torch.equal(l1, w.lse)
+
+
+# ---------------------------------------------------------------------------
+# prefill (one sequence, queries sharing window rows, pool and keys)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kv", [synth.KV_BF16, synth.KV_FP8])
+def test_prefill_small_with_replay_cut(kv):
+    pos0, T, m = 6000, 300, 8
+    pf = synth.prefill_chunk(18 + kv, T, pos0, m, (pos0 + T) // m, dims=small_dims(kv_dtype=kv),
+                             win_pos0=pos0 - 40)
+    say("prefill T=300 kv", kv)
+    w = csa2.PrefillWorkload(pf)
+    w.prefill()
+    torch.cuda.synchronize()
+    inp = synth.prefill_as_batch(pf)
+    assert inp["win_len"][0] == 41 and inp["win_len"][-1] == 128
+    compare(inp, w.topk.cpu().numpy(), w.out.cpu().numpy(), w.lse.cpu().numpy())
+
+
+@pytest.mark.parametrize("mode", [synth.MODE_REUSE, synth.MODE_WINDOW, synth.MODE_REINDEX])
+def test_prefill_other_modes(mode):
+    pos0, T, m = 3000, 130, 4
+    pool = (pos0 + T) // m
+    pf = synth.prefill_chunk(19, T, pos0, m, pool, dims=small_dims(), mode=mode)
+    if mode == synth.MODE_REUSE:
+        sel = np.full((T, 512), -1, np.int32)
+        for t in range(T):
+            s = synth.sample_distinct(19, 1000 + t, (pos0 + t + 1) // m, 300)
+            sel[t, :len(s)] = s
+        pf["sel_in"] = sel
+    if mode == synth.MODE_REINDEX:
+        offs = np.zeros(T + 1, np.int64)
+        parts = []
+        for t in range(T):
+            s = synth.sample_distinct(19, 2000 + t, pool, 700)
+            parts.append(s)
+            offs[t + 1] = offs[t] + len(s)
+        pf["cand_off"], pf["cand_idx"] = offs, np.concatenate(parts).astype(np.int32)
+    say("prefill mode", mode)
+    w = csa2.PrefillWorkload(pf)
+    w.prefill()
+    torch.cuda.synchronize()
+    inp = synth.prefill_as_batch(pf)
+    compare(inp, w.topk.cpu().numpy(), w.out.cpu().numpy(), w.lse.cpu().numpy())
+
+
+# ---------------------------------------------------------------------------
+# the five workloads at full size, sampled against the oracle
+# ---------------------------------------------------------------------------
+
+def test_config0_tiny():
+    inp = synth.config(0)
+    say("config tiny")
+    _, sg, og, lg = run_decode(inp)
+    compare(inp, sg, og, lg)
+    assert (sg[0] >= 0).all()  # 1,024 reachable, 512 selected
+
+
+@pytest.mark.parametrize("idx,samples", [(1, [0, 17, 63]), (3, [0, 100, 255]), (4, None)])
+def test_full_size_decode_configs(idx, samples):
+    say(f"building config {idx}")
+    inp = synth.config(idx)
+    say(f"config {idx}: B={inp['B']} running")
+    w, sg, og, lg = run_decode(inp)
+    del w
+    torch.cuda.empty_cache()
+    if samples is None:  # mixed batch: one query of each mode plus the longest and shortest
+        lens = inp["pool_len"]
+        full = np.nonzero(inp["mode"] == 0)[0]
+        samples = sorted({0, 1, 2, int(full[np.argmax(lens[full])]), int(full[np.argmin(lens[full])])})
+    say(f"config {idx}: oracle on queries {samples}")
+    worst = compare(inp, sg, og, lg, samples)
+    say(f"config {idx}: worst normwise error {worst:.2e}")
+    # properties over every query: selections ascending, -1 padded, in range
+    for b in range(inp["B"]):
+        if inp["mode"][b] in (0, 1):
+            s = sg[b]
+            v = s[s >= 0]
+            assert (np.diff(v) > 0).all() and (s[len(v):] == -1).all()
+            assert len(v) == min(512, O.n_valid(inp["pos"][b], inp["ratio"][b], 0, inp["pool_len"][b]))
+    assert np.isfinite(og).all()
+
+
+def test_full_size_prefill_config():
+    say("building config 2 (prefill)")
+    pf = synth.config(2)
+    w = csa2.PrefillWorkload(pf)
+    say("config 2 running")
+    w.prefill()
+    torch.cuda.synchronize()
+    sg, og, lg = w.topk.cpu().numpy(), w.out.cpu().numpy(), w.lse.cpu().numpy()
+    del w
+    torch.cuda.empty_cache()
+    samples = [0, 1, 127, 128, 2047, 4095]
+    inp = synth.prefill_as_batch(pf)
+    say(f"config 2: oracle on queries {samples}")
+    compare(inp, sg, og, lg, samples)
+    assert np.isfinite(og).all()
+    assert (sg >= 0).all()  # at least 15,872 reachable everywhere, so every slot is filled
