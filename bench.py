@@ -1,0 +1,193 @@
+"""Throughput of the CSA2 attention step on one MI355X.
+
+One step = one csa2_decode call over the whole batch: indexer scores for every
+query over its reachable compressed entries, per-query top-512, and the
+64-head single-softmax attention over 128 window rows + 512 selected rows.
+Default workload: 64 independent decode queries at context 65,536 with
+compress ratio 4 (16,384 candidates each), bf16 KV, fp32 indexer keys; inputs
+are seeded synthetic N(0, 1) data, resident in HBM before timing starts.
+
+Prints ONE JSON line.  Besides the contract fields it carries
+  roofline:     the dominant kernel (the indexer scan) against HBM bandwidth,
+                its duration measured here with HIP events on the launch stream;
+  cpu_baseline: the CPU oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "CSA2 attended queries/sec (64h×512, 128+512 keys) + % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+INDEX_KEY_BYTES = 128 * 4    # one fp32 index key row per scanned candidate
+INDEX_Q_BYTES = 128 * 4      # one fp32 indexer query per query
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILE_DIR, "index_scores_decode_64x16384_traffic.json")
+INDEX_SRC = os.path.join(ROOT, "sparse_long_context_amd", "csrc", "index_scores.hip")
+
+
+def source_digest(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def workload_desc(inp):
+    d = inp["dims"]
+    kv = "bf16" if d["kv_dtype"] == 0 else "fp8 e4m3 + ue8m0/32"
+    return {
+        "workload": (f"decode, {inp['B']} queries, context {int(inp['pos'][0]) + 1}, compress ratio "
+                     f"{int(inp['ratio'][0])} -> {int(inp['pool_len'][0])} candidates each, window "
+                     f"{d['window']}, top-{d['index_topk']}, {d['n_heads']} heads x {d['head_dim']}, {kv} KV, "
+                     f"fp32 indexer dim {d['index_dim']}"),
+        "queries_per_step": int(inp["B"]),
+        "candidates_per_query": int(inp["pool_len"][0]),
+        "window": d["window"], "index_topk": d["index_topk"], "kv": kv,
+    }
+
+
+def traffic_from_profile():
+    """HBM bytes per launch of the indexer kernel from committed rocprofv3 PMC
+    counters, if they were taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != source_digest(INDEX_SRC):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, min_seconds=10.0, max_seconds=30.0):
+    """Oracle over whole passes of the batch until at least min_seconds."""
+    from oracle import oracle as O
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    n = 0
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        O.decode_batch(inp)
+        n += inp["B"]
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or el >= max_seconds:
+            break
+    return {"value": n / el, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"{passes} passes over the {inp['B']}-query batch ({n} queries, {el:.1f} s, fp64 oracle, "
+                      f"OpenMP over queries)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=1, help="decode workload index (1, 3 or 4)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); the decode batch "
+              "shards by sequence with no exchange, so N GPUs would each run this same step on their own "
+              "queries.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_long_context_amd import csa2, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.config not in (1, 3, 4):
+        print("bench.py times the decode workloads 1, 3 or 4", file=sys.stderr)
+        sys.exit(2)
+    print(f"[bench] generating workload {args.config}", file=sys.stderr, flush=True)
+    inp = synth.config(args.config)
+    w = csa2.DecodeWorkload(inp)
+    stream = torch.cuda.current_stream()
+    B = w.B
+
+    for _ in range(args.warmup):
+        w.decode()
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        w.decode()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    value = B * args.steps / wall
+
+    # per-kernel durations: the same three launches issued stage by stage, with
+    # HIP events between them on the launch stream
+    stride = w.max_cand
+    scores = torch.empty((B, stride), dtype=torch.float32, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    acc = [0.0, 0.0, 0.0]
+    sp_ws = csa2.csa2_workspace_size(w.dims, B, 0)
+    attend_ws = torch.empty(max(sp_ws, 1), dtype=torch.uint8, device="cuda")
+    for it in range(args.warmup + args.steps):
+        ev[0].record(stream)
+        csa2.csa2_index_scores(w.dims, B, w.batch, w.idx_q, w.idx_w, w.idx_k, scores, stride)
+        ev[1].record(stream)
+        csa2.csa2_topk(w.dims, B, w.batch, scores, stride, w.topk)
+        ev[2].record(stream)
+        csa2.csa2_attend(w.dims, B, w.batch, w.q, w.win_kv, w.win_scale, w.comp_kv, w.comp_scale, w.topk, w.sink,
+                         w.out, w.lse, attend_ws, sp_ws)
+        ev[3].record(stream)
+        torch.cuda.synchronize()
+        if it >= args.warmup:
+            for k in range(3):
+                acc[k] += ev[k].elapsed_time(ev[k + 1])
+    stage_us = [1000.0 * a / args.steps for a in acc]
+
+    n_cand = int(sum(min(int(p), (int(pos) + 1) // int(r)) for p, pos, r, m in
+                     zip(inp["pool_len"], inp["pos"], inp["ratio"], inp["mode"]) if m == 0 and r > 0))
+    n_full = int((inp["mode"] == 0).sum())
+    idx_bytes = n_cand * INDEX_KEY_BYTES + n_full * INDEX_Q_BYTES
+    achieved = idx_bytes / (stage_us[0] * 1e-6) / 1e9
+    traffic = traffic_from_profile() if args.config == 1 else None
+    roofline = {"bound": "hbm", "kernel": "index_scores_decode", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "algorithmic_bytes_per_launch": idx_bytes,
+                "avg_launch_us": round(stage_us[0], 2)}
+    # the attention contraction on its own: 2 x (64 x entries x 512) MACs per query
+    ent = 0
+    for b in range(B):
+        nv = min(int(inp["pool_len"][b]), (int(inp["pos"][b]) + 1) // max(int(inp["ratio"][b]), 1))
+        sel = min(512, nv) if inp["mode"][b] in (0, 1) else (int((inp["sel_in"][b] >= 0).sum())
+                                                            if inp["mode"][b] == 2 else 0)
+        ent += int(inp["win_len"][b]) + sel
+    attn_flops = 4.0 * 64 * 512 * ent
+    attend_tflops = attn_flops / (stage_us[2] * 1e-6) / 1e12
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": workload_desc(inp),
+        "roofline": roofline,
+        "stages_us": {"index_scores": round(stage_us[0], 2), "topk": round(stage_us[1], 2),
+                      "attend": round(stage_us[2], 2)},
+        "attend_mfma": {"achieved": round(attend_tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(attend_tflops / BF16_PEAK_TFLOPS, 4)},
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
