@@ -7,8 +7,10 @@
 // layer").
 //
 // Workgroup = one (query, split) pair, 4 waves; wave w owns heads 16w..16w+15.
-// Entries are processed in chunks of 32 rows staged in LDS (double buffered;
-// the next chunk's global loads are in flight while the current one is used):
+// Entries are processed in chunks of 32 rows staged in LDS: bf16 rows travel
+// by DMA (global_load_lds) through a 4-deep ring, so three chunks are in
+// flight while one is consumed; fp8 rows are widened in registers and double
+// buffered.  Per chunk:
 //   S^T (32 entries x 16 heads) = K (32 x 512) * Q^T      v_mfma_f32_16x16x32_bf16
 //   online softmax per head in fp32 (exp2 domain)
 //   O^T (512 dims x 16 heads) += V^T (512 x 32) * P^T       same MFMA
@@ -37,6 +39,7 @@ constexpr int kRowBytes = kDim * 2;                // one bf16 row in LDS
 constexpr int kBufBytes = kChunk * kRowBytes;      // 32 KiB per buffer
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazy = 8.0f;  // log2 headroom before the running max is raised
 
 struct AttendArgs {
   const int64_t* pos;
@@ -84,9 +87,9 @@ __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 codes, int e) {
   return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
 }
 
-template <int KV>
+template <int KV, int NBUF>
 __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kBufBytes];  // 2 chunk buffers
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NBUF * kBufBytes];  // chunk ring
   __shared__ int64_t ent_s[kMaxEntries];  // >= 0: window row; < 0: -(pool row) - 1
   __shared__ uint32_t wcnt_s[4];
 
@@ -148,54 +151,8 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
   for (int i = 0; i < 32; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -__builtin_inff(), l_run = 0.f;
 
-  // ---- staging: 32 rows per chunk, one row per wave instruction ----
-  constexpr int kPieces = 8;  // 16-byte LDS pieces per thread per chunk
-  uint4 stage[kPieces];
-  auto fetch = [&](int c) {
-#pragma unroll
-    for (int it = 0; it < kPieces; ++it) {
-      const int p = it * 256 + t;
-      const int er = p >> 6, u = p & 63;
-      const int e = c * kChunk + er;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (e < E) {
-        const int64_t ev = ent_s[e];
-        const bool pool = ev < 0;
-        const int64_t row = pool ? (-ev - 1) : ev;
-        if (KV == CSA2_KV_BF16) {
-          const uint8_t* base = pool ? a.comp_kv : a.win_kv;
-          v = *reinterpret_cast<const uint4*>(base + row * kRowBytes + u * 16);
-        } else {
-          const uint8_t* base = pool ? a.comp_kv : a.win_kv;
-          const uint8_t* sc = pool ? a.comp_scale : a.win_scale;
-          const uint2 codes = *reinterpret_cast<const uint2*>(base + row * kDim + u * 8);
-          const int ex = (int)sc[row * (kDim / kScaleBlock) + (u >> 2)] - 127;
-          v = fp8x8_to_bf16x8(codes, ex);
-        }
-      }
-      stage[it] = v;
-    }
-  };
-  auto stash = [&](int buf) {
-    uint8_t* base = smem + buf * kBufBytes;
-#pragma unroll
-    for (int it = 0; it < kPieces; ++it) {
-      const int p = it * 256 + t;
-      *reinterpret_cast<uint4*>(base + lds_off(p >> 6, (p & 63) * 16)) = stage[it];
-    }
-  };
-
-  if (cbeg < cend) {
-    fetch(cbeg);
-    stash(0);
-  }
-  __syncthreads();
-
-  for (int c = cbeg; c < cend; ++c) {
-    const int buf = (c - cbeg) & 1;
-    if (c + 1 < cend) fetch(c + 1);
-    const uint8_t* base = smem + buf * kBufBytes;
-
+  // ---- one chunk of 32 staged rows: S^T, online softmax, O^T update ----
+  auto consume = [&](const uint8_t* base, int c) {
     // S^T = K Q^T: rows 0-15 and 16-31 of the chunk
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -218,26 +175,31 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     for (int i = 1; i < 8; ++i) cmax = fmaxf(cmax, sv[i]);
     cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
     cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-    const float m_new = fmaxf(m_run, cmax);
-    float alpha = 1.f, pv[8], rs = 0.f;
-    if (m_new == -__builtin_inff()) {
+    // The running reference moves only when a chunk's maximum exceeds it by
+    // more than 2^kLazy: until then probabilities stay below 2^kLazy (no
+    // overflow risk in fp32 or bf16) and the accumulators need no rescale.
+    const bool raise = cmax > m_run + kLazy;  // false while both are -inf
+    float alpha = 1.f;
+    if (raise) {
+      alpha = __builtin_amdgcn_exp2f(m_run - cmax);
+      m_run = cmax;
+    }
+    float pv[8], rs = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pv[i] = 0.f;
-    } else {
-      alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_new);
-        rs += pv[i];
-      }
+    for (int i = 0; i < 8; ++i) {
+      pv[i] = (m_run == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(sv[i] - m_run);
+      rs += pv[i];
     }
     rs += __shfl_xor(rs, 16);
     rs += __shfl_xor(rs, 32);
     l_run = l_run * alpha + rs;
-    m_run = m_new;
     bf16x8 pb;
 #pragma unroll
     for (int i = 0; i < 8; ++i) pb[i] = (__bf16)pv[i];
+    if (__ballot(raise)) {  // wave-uniform: rescale only when some head moved
+#pragma unroll
+      for (int tt = 0; tt < 32; ++tt) acc[tt] *= alpha;
+    }
 
     // O^T += V^T P^T, 32 tiles of 16 dims
     const int tj = (lane >> 2) & 3, tc = lane & 3;
@@ -251,12 +213,94 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
           (lds_s16x4*)((__attribute__((address_space(3))) uint8_t*)(base + lds_off(r_hi, byte))));
       typedef short s16x8 __attribute__((ext_vector_type(8)));
       const s16x8 v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      acc[tt] *= alpha;
       acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v8), pb, acc[tt], 0, 0, 0);
     }
+  };
 
-    if (c + 1 < cend) stash(buf ^ 1);
+  if constexpr (KV == CSA2_KV_BF16) {
+    // ---- bf16 rows go HBM -> LDS by DMA through an NBUF-deep ring ----
+    // Wave w moves rows 8w .. 8w+7 of a chunk, one 1 KiB row per instruction;
+    // lane l fetches the 16-byte unit that belongs at LDS unit l of the row.
+    // Rows past the last entry repeat a real row (their probabilities are 0),
+    // so every instruction is whole and each chunk is exactly 8 per wave.
+    auto issue = [&](int c) {
+      uint8_t* slot = smem + (c % NBUF) * kBufBytes;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int er = wv * 8 + k;
+        int e = c * kChunk + er;
+        if (e >= E) e = 0;
+        const int64_t ev = ent_s[e];
+        const bool pool = ev < 0;
+        const int64_t row = pool ? (-ev - 1) : ev;
+        const uint8_t* src = (pool ? a.comp_kv : a.win_kv) + row * kRowBytes + swz_unit(er, lane) * 16;
+        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                         (void __attribute__((address_space(3)))*)(slot + er * kRowBytes), 16,
+                                         0, 0);
+      }
+    };
+    int issued = 0;
+    const int total = cend - cbeg;
+    for (; issued < total && issued < NBUF; ++issued) issue(cbeg + issued);
+    for (int i = 0; i < total; ++i) {
+      const int younger = issued - i - 1;  // chunks issued after this one, still allowed in flight
+      if (younger >= 3)
+        asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+      else if (younger == 2)
+        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      else if (younger == 1)
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      consume(smem + ((cbeg + i) % NBUF) * kBufBytes, cbeg + i);
+      __syncthreads();
+      if (issued < total) issue(cbeg + issued++);
+    }
+  } else {
+    // ---- fp8 rows: widened to bf16 in registers, double-buffered in LDS ----
+    constexpr int kPieces = 8;  // 16-byte LDS pieces per thread per chunk
+    uint4 stage[kPieces];
+    auto fetch = [&](int c) {
+#pragma unroll
+      for (int it = 0; it < kPieces; ++it) {
+        const int p = it * 256 + t;
+        const int er = p >> 6, u = p & 63;
+        const int e = c * kChunk + er;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (e < E) {
+          const int64_t ev = ent_s[e];
+          const bool pool = ev < 0;
+          const int64_t row = pool ? (-ev - 1) : ev;
+          const uint8_t* base = pool ? a.comp_kv : a.win_kv;
+          const uint8_t* sc = pool ? a.comp_scale : a.win_scale;
+          const uint2 codes = *reinterpret_cast<const uint2*>(base + row * kDim + u * 8);
+          const int ex = (int)sc[row * (kDim / kScaleBlock) + (u >> 2)] - 127;
+          v = fp8x8_to_bf16x8(codes, ex);
+        }
+        stage[it] = v;
+      }
+    };
+    auto stash = [&](int buf) {
+      uint8_t* base = smem + buf * kBufBytes;
+#pragma unroll
+      for (int it = 0; it < kPieces; ++it) {
+        const int p = it * 256 + t;
+        *reinterpret_cast<uint4*>(base + lds_off(p >> 6, (p & 63) * 16)) = stage[it];
+      }
+    };
+    if (cbeg < cend) {
+      fetch(cbeg);
+      stash(0);
+    }
     __syncthreads();
+    for (int c = cbeg; c < cend; ++c) {
+      const int buf = (c - cbeg) & 1;
+      if (c + 1 < cend) fetch(c + 1);
+      consume(smem + buf * kBufBytes, c);
+      if (c + 1 < cend) stash(buf ^ 1);
+      __syncthreads();
+    }
   }
 
   // ---- epilogue: lane holds O^T[16*tt + 4g + i][head] ----
@@ -368,9 +412,9 @@ hipError_t launch_attend(const csa2_dims& d, int32_t B, const csa2_batch& bt, co
   a.n_split = n_split;
   a.scale_log2 = d.softmax_scale * kLog2e;
   if (d.kv_dtype == CSA2_KV_BF16)
-    hipLaunchKernelGGL(attend_kernel<CSA2_KV_BF16>, dim3(B * n_split), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attend_kernel<CSA2_KV_BF16, 4>), dim3(B * n_split), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(attend_kernel<CSA2_KV_FP8_E4M3_UE8M0_32>, dim3(B * n_split), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attend_kernel<CSA2_KV_FP8_E4M3_UE8M0_32, 2>), dim3(B * n_split), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_split == 1) return e;
   hipLaunchKernelGGL(attend_combine, dim3(B * kHeads), dim3(128), 0, s, n_split, a.part_o, a.part_ml, sink,

@@ -8,10 +8,10 @@
 // leaves every sum unchanged (0 * finite adds an exact zero).
 //
 // Two kernels:
-//  * decode: one workgroup per (query, 256 candidates).  The key rows are the
-//    only large stream (512 B per candidate); they are staged through LDS in
-//    four 32-float slabs with fully coalesced 128-byte row segments, the next
-//    slab prefetched into registers while the current one is consumed.
+//  * decode: one workgroup per (query, 32 candidates).  The key rows are the
+//    only large stream (512 B per candidate); 256 threads load them with
+//    coalesced 16-byte loads into LDS, then each of 32 lanes runs one
+//    candidate's FMA chain out of LDS.
 //  * prefill: one sequence, many queries sharing the key rows, so the keys are
 //    reused across queries: a register-tiled product of 128 queries x 128
 //    candidates per workgroup (8 x 8 outputs per thread), each output's FMA
@@ -21,10 +21,6 @@
 namespace csa2 {
 namespace {
 
-constexpr int kTile = 256;       // candidates per decode workgroup (one per thread)
-constexpr int kSlab = 32;        // floats per staged key slab
-constexpr int kSlabPad = 36;     // LDS row stride (floats): 16-byte aligned, conflict-free reads
-constexpr int kSlabs = kIndexDim / kSlab;
 
 __device__ __forceinline__ float finish_score(const float* acc, const float* w, int hp, int relu) {
   float s = 0.0f;
@@ -36,18 +32,30 @@ __device__ __forceinline__ float finish_score(const float* acc, const float* w, 
   return s == 0.0f ? 0.0f : s;
 }
 
+// 256 threads move the 32 key rows of a workgroup (16 KiB, contiguous for
+// FULL queries) with plain coalesced 16-byte loads, four per thread, into an
+// XOR-swizzled LDS tile; then 32 lanes each run one candidate's FMA chain out
+// of LDS.  Tiny workgroups keep many loads in flight per CU, which is what
+// reaches the HBM read ceiling here.
+constexpr int kRows = 32;                          // candidates per workgroup
+constexpr int kThreads = 256;
+constexpr int kUnits = kIndexDim / 4;              // 32 units of 16 B per key row
+constexpr int kPieces = kRows * kUnits / kThreads; // 4 loads per thread
+
+__device__ __forceinline__ int key_unit_swz(int r, int u) { return u ^ (r & 15); }
+
 template <int HP>
-__global__ __launch_bounds__(kTile) void index_scores_decode(
+__global__ __launch_bounds__(kThreads) void index_scores_decode(
     int32_t hi, int32_t relu, int32_t max_cand, const int64_t* __restrict__ pos,
     const int32_t* __restrict__ mode, const int32_t* __restrict__ ratio,
     const int64_t* __restrict__ pool_row0, const int32_t* __restrict__ pool_len,
     const int64_t* __restrict__ cand_off, const int32_t* __restrict__ cand_idx,
     const float* __restrict__ idx_q, const float* __restrict__ idx_w, const float* __restrict__ idx_k,
     float* __restrict__ scores, int64_t stride) {
-  __shared__ float q_s[HP][kIndexDim];
+  __shared__ __attribute__((aligned(16))) float k_s[kRows * kIndexDim];
+  __shared__ __attribute__((aligned(16))) float q_s[HP][kIndexDim];
   __shared__ float w_s[HP];
-  __shared__ __attribute__((aligned(16))) float k_s[kTile][kSlabPad];
-  __shared__ int64_t row_s[kTile];
+  __shared__ int64_t row_s[kRows];
 
   const int b = blockIdx.y;
   const int t = threadIdx.x;
@@ -56,75 +64,62 @@ __global__ __launch_bounds__(kTile) void index_scores_decode(
   const int64_t nv = n_valid_of(pos[b], ratio[b], md, pool_len[b]);
   int64_t n = (md == CSA2_MODE_FULL) ? nv : (cand_off[b + 1] - cand_off[b]);
   if (n > max_cand) n = max_cand;
-  const int64_t j0 = (int64_t)blockIdx.x * kTile;
+  const int64_t j0 = (int64_t)blockIdx.x * kRows;
   if (j0 >= n) return;
 
-  // query vectors and weights of this query (heads padded with zeros)
-  for (int x = t; x < HP * kIndexDim; x += kTile) {
+  if (t < kRows) {  // candidate rows (pool-relative), -1 when there is none
+    const int64_t j = j0 + t;
+    int64_t r = -1;
+    if (j < n) {
+      const int64_t rr = (md == CSA2_MODE_FULL) ? j : (int64_t)cand_idx[cand_off[b] + j];
+      if (rr >= 0 && rr < nv) r = rr;
+    }
+    row_s[t] = r;
+  }
+  for (int x = t; x < HP * kIndexDim; x += kThreads) {
     const int h = x / kIndexDim, i = x % kIndexDim;
     q_s[h][i] = (h < hi) ? idx_q[((int64_t)b * hi + h) * kIndexDim + i] : 0.0f;
   }
   if (t < HP) w_s[t] = (t < hi) ? (idx_w ? idx_w[(int64_t)b * hi + t] : 1.0f) : 0.0f;
-
-  // this thread's candidate: global key row, or -1 when it has none
-  const int64_t j = j0 + t;
-  int64_t row = -1;
-  if (j < n) {
-    int64_t r = (md == CSA2_MODE_FULL) ? j : (int64_t)cand_idx[cand_off[b] + j];
-    if (r >= 0 && r < nv) row = pool_row0[b] + r;
-  }
-  row_s[t] = row;
   __syncthreads();
 
-  // slab loader: 256 rows x 8 float4 pieces, 8 pieces per thread, 8 lanes per row
-  float4 pf[8];
-  auto fetch = [&](int s) {
+  const float* kbase = idx_k + pool_row0[b] * kIndexDim;
+  float4 v[kPieces];
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int p = it * kTile + t;
-      const int c = p >> 3, part = p & 7;
-      const int64_t r = row_s[c];
-      pf[it] = (r >= 0) ? *reinterpret_cast<const float4*>(idx_k + r * kIndexDim + s * kSlab + part * 4)
-                        : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  };
-  auto stash = [&]() {
+  for (int it = 0; it < kPieces; ++it) {
+    const int p = it * kThreads + t, r = p / kUnits, u = p % kUnits;
+    const int64_t rr = row_s[r];
+    v[it] = (rr >= 0) ? *reinterpret_cast<const float4*>(kbase + rr * kIndexDim + u * 4)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int p = it * kTile + t;
-      *reinterpret_cast<float4*>(&k_s[p >> 3][(p & 7) * 4]) = pf[it];
-    }
-  };
-
-  float acc[HP];
+  for (int it = 0; it < kPieces; ++it) {
+    const int p = it * kThreads + t, r = p / kUnits, u = p % kUnits;
+    *reinterpret_cast<float4*>(&k_s[r * kIndexDim + key_unit_swz(r, u) * 4]) = v[it];
+  }
+  __syncthreads();
+  if (t >= kRows) return;
+  const int64_t j = j0 + t;
+  if (j >= n) return;
+  float sc = -__builtin_inff();
+  if (row_s[t] >= 0) {
+    float acc[HP];
 #pragma unroll
-  for (int h = 0; h < HP; ++h) acc[h] = 0.0f;
-
-  fetch(0);
-#pragma unroll 1
-  for (int s = 0; s < kSlabs; ++s) {
-    stash();
-    __syncthreads();
-    if (s + 1 < kSlabs) fetch(s + 1);
+    for (int h = 0; h < HP; ++h) acc[h] = 0.0f;
 #pragma unroll
-    for (int i4 = 0; i4 < kSlab / 4; ++i4) {
-      const float4 k4 = *reinterpret_cast<const float4*>(&k_s[t][i4 * 4]);
+    for (int u = 0; u < kUnits; ++u) {
+      const float4 k4 = *reinterpret_cast<const float4*>(&k_s[t * kIndexDim + key_unit_swz(t, u) * 4]);
       const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = s * kSlab + i4 * 4 + u;
+      for (int e = 0; e < 4; ++e) {
+        const int i = u * 4 + e;
 #pragma unroll
-        for (int h = 0; h < HP; ++h) acc[h] = __builtin_fmaf(q_s[h][i], kv[u], acc[h]);
+        for (int h = 0; h < HP; ++h) acc[h] = __builtin_fmaf(q_s[h][i], kv[e], acc[h]);
       }
     }
-    __syncthreads();
+    sc = finish_score(acc, w_s, HP, relu);
   }
-
-  if (j < n) {
-    float sc = -__builtin_inff();
-    if (row >= 0) sc = finish_score(acc, w_s, HP, relu);
-    scores[(int64_t)b * stride + j] = sc;
-  }
+  scores[(int64_t)b * stride + j] = sc;
 }
 
 // ---- prefill: queries x candidates, register tiled -------------------------
@@ -214,19 +209,19 @@ hipError_t launch_index_scores(const csa2_dims& d, int32_t B, const csa2_batch& 
                                const float* idx_w, const float* idx_k, float* scores, int64_t stride,
                                hipStream_t s) {
   if (B == 0 || bt.max_candidates == 0) return hipSuccess;
-  dim3 grid((bt.max_candidates + kTile - 1) / kTile, B);
+  dim3 grid((bt.max_candidates + kRows - 1) / kRows, B);
   const int hi = d.index_heads;
 #define CSA2_IDX_ARGS                                                                                 \
   hi, d.index_relu, bt.max_candidates, bt.pos, bt.mode, bt.compress_ratio, bt.pool_row0, bt.pool_len, \
       bt.cand_off, bt.cand_idx, idx_q, idx_w, idx_k, scores, stride
   if (hi <= 1)
-    hipLaunchKernelGGL(index_scores_decode<1>, grid, dim3(kTile), 0, s, CSA2_IDX_ARGS);
+    hipLaunchKernelGGL(index_scores_decode<1>, grid, dim3(kThreads), 0, s, CSA2_IDX_ARGS);
   else if (hi <= 4)
-    hipLaunchKernelGGL(index_scores_decode<4>, grid, dim3(kTile), 0, s, CSA2_IDX_ARGS);
+    hipLaunchKernelGGL(index_scores_decode<4>, grid, dim3(kThreads), 0, s, CSA2_IDX_ARGS);
   else if (hi <= 16)
-    hipLaunchKernelGGL(index_scores_decode<16>, grid, dim3(kTile), 0, s, CSA2_IDX_ARGS);
+    hipLaunchKernelGGL(index_scores_decode<16>, grid, dim3(kThreads), 0, s, CSA2_IDX_ARGS);
   else
-    hipLaunchKernelGGL(index_scores_decode<64>, grid, dim3(kTile), 0, s, CSA2_IDX_ARGS);
+    hipLaunchKernelGGL(index_scores_decode<64>, grid, dim3(kThreads), 0, s, CSA2_IDX_ARGS);
 #undef CSA2_IDX_ARGS
   return hipGetLastError();
 }

@@ -106,7 +106,7 @@ def test_index_scores_bit_exact_full_and_reindex():
 
 
 @pytest.mark.parametrize("n,k", [(100, 512), (512, 512), (513, 512), (3000, 512), (16384, 512), (40000, 512),
-                                 (65536, 512), (5000, 1), (5000, 37)])
+                                 (65536, 512), (65537, 512), (100003, 300), (5000, 1), (5000, 37), (1027, 512)])
 def test_topk_from_oracle_scores_with_ties(n, k):
     rng = np.random.default_rng(n + k)
     B = 3
