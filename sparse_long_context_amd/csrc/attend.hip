@@ -7,10 +7,9 @@
 // layer").
 //
 // Workgroup = one (query, split) pair, 4 waves; wave w owns heads 16w..16w+15.
-// Entries are processed in chunks of 32 rows staged in LDS: bf16 rows travel
-// by DMA (global_load_lds) through a 4-deep ring, so three chunks are in
-// flight while one is consumed; fp8 rows are widened in registers and double
-// buffered.  Per chunk:
+// Entries are processed in chunks of 32 rows staged in LDS (double buffered);
+// their global loads are issued two chunks ahead into registers, and fp8 rows
+// are widened to bf16 on the way into LDS.  Per chunk:
 //   S^T (32 entries x 16 heads) = K (32 x 512) * Q^T      v_mfma_f32_16x16x32_bf16
 //   online softmax per head in fp32 (exp2 domain)
 //   O^T (512 dims x 16 heads) += V^T (512 x 32) * P^T       same MFMA
@@ -65,31 +64,32 @@ struct AttendArgs {
   float scale_log2;  // softmax_scale * log2(e)
 };
 
-// 16-byte unit u of LDS row r lives at unit u ^ f(r); f is a bijection on 0..15
-// with f(r) = f(r + 16), chosen so 16 consecutive rows at one unit, and 8 rows x
-// 2 adjacent units, each land on distinct bank groups.
-__device__ __forceinline__ int swz_unit(int r, int u) { return u ^ (((r << 1) + (r >> 3)) & 15); }
+// 16-byte unit u of LDS row r lives at unit u ^ f(r), where f swaps the two
+// 2-bit halves of r mod 16 (so f(r) = f(r + 16)).  Sixteen consecutive rows at
+// one unit (the row reads of the first product), and four aligned rows x four
+// aligned units (the transposing reads of the second), both land on 16
+// distinct bank groups.
+__device__ __forceinline__ int swz_unit(int r, int u) { return u ^ (((r & 3) << 2) | ((r >> 2) & 3)); }
 __device__ __forceinline__ int lds_off(int r, int byte) {
   return r * kRowBytes + (swz_unit(r, byte >> 4) << 4) + (byte & 15);
 }
 
-// Widen 8 E4M3 codes (two dwords) times 2^e to 8 bf16 (exact).
-__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 codes, int e) {
-  float f[8];
-  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(codes.x, false);
-  const auto bq = __builtin_amdgcn_cvt_pk_f32_fp8(codes.x, true);
-  const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(codes.y, false);
-  const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(codes.y, true);
-  f[0] = a[0], f[1] = a[1], f[2] = bq[0], f[3] = bq[1], f[4] = c[0], f[5] = c[1], f[6] = d[0], f[7] = d[1];
-  uint32_t h[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) h[i] = __float_as_uint(__builtin_ldexpf(f[i], e)) >> 16;
-  return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+// Widen 8 E4M3 codes (two dwords) times 2^(e - 127) to 8 bf16 with the gfx950
+// scaled conversion; exact, since each product has at most 4 significant bits.
+__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 codes, uint32_t e) {
+  const float scale = __uint_as_float(e << 23);  // 2^(e-127); e in 1..254 for the stored scales
+  const auto a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.x, scale, false);
+  const auto a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.x, scale, true);
+  const auto a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.y, scale, false);
+  const auto a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.y, scale, true);
+  return make_uint4(__builtin_bit_cast(uint32_t, a0), __builtin_bit_cast(uint32_t, a1),
+                    __builtin_bit_cast(uint32_t, a2), __builtin_bit_cast(uint32_t, a3));
 }
 
-template <int KV, int NBUF>
+template <int KV>
 __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[NBUF * kBufBytes];  // chunk ring
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kBufBytes];  // double buffer
+  __shared__ __attribute__((aligned(16))) uint8_t q_s[kHeads * kRowBytes];  // the query, 64 KiB
   __shared__ int64_t ent_s[kMaxEntries];  // >= 0: window row; < 0: -(pool row) - 1
   __shared__ uint32_t wcnt_s[4];
 
@@ -134,15 +134,17 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
   const int cbeg = sp * cps;
   const int cend = (cbeg + cps < nch) ? cbeg + cps : nch;
 
-  // ---- this wave's 16 heads of q, as the B operand (dims x heads) ----
+  // ---- the query's 64 heads x 512 dims go to LDS once (1 KiB row per head,
+  // same swizzle as the KV rows); fragments are read per chunk as the B
+  // operand (dims x heads) ----
   const int head = wv * 16 + l16;
-  bf16x8 qf[16];
   {
-    const uint16_t* qp = a.q + ((int64_t)b * kHeads + head) * kDim + g * 8;
+    const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.q + (int64_t)b * kHeads * kDim);
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      const uint4 v = *reinterpret_cast<const uint4*>(qp + kk * 32);
-      qf[kk] = __builtin_bit_cast(bf16x8, v);
+    for (int it = 0; it < kHeads * kRowBytes / 16 / 256; ++it) {
+      const int p = it * 256 + t;
+      *reinterpret_cast<uint4*>(q_s + lds_off(p >> 6, (p & 63) * 16)) =
+          *reinterpret_cast<const uint4*>(qsrc + (size_t)p * 16);
     }
   }
 
@@ -151,16 +153,32 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
   for (int i = 0; i < 32; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -__builtin_inff(), l_run = 0.f;
 
+  // ---- per-lane LDS offsets.  The swizzle only touches the low four bits of
+  // a row's 16-byte unit index, so each fragment address is one of a few
+  // per-lane bases plus a compile-time offset (and rows r, r+16 share f). ----
+  const int tj = (lane >> 2) & 3, tc = lane & 3;
+  const int r_lo = 4 * g + tj;
+  uint32_t qo[4], vo[8];
+#pragma unroll
+  for (int bq = 0; bq < 4; ++bq) qo[bq] = l16 * kRowBytes + (swz_unit(l16, 4 * bq + g) << 4);
+#pragma unroll
+  for (int bt = 0; bt < 8; ++bt) vo[bt] = r_lo * kRowBytes + (swz_unit(r_lo, 2 * bt + (tc >> 1)) << 4) + 8 * (tc & 1);
+
   // ---- one chunk of 32 staged rows: S^T, online softmax, O^T update ----
   auto consume = [&](const uint8_t* base, int c) {
-    // S^T = K Q^T: rows 0-15 and 16-31 of the chunk
+    // S^T = K Q^T: rows 0-15 and 16-31 of the chunk (K fragment kk = 4a + bq
+    // sits at qo[bq] + 256 a, its second-half twin 16 rows further)
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) {
-      const uint4 k0 = *reinterpret_cast<const uint4*>(base + lds_off(l16, kk * 64 + g * 16));
-      const uint4 k1 = *reinterpret_cast<const uint4*>(base + lds_off(16 + l16, kk * 64 + g * 16));
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k0), qf[kk], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k1), qf[kk], s1, 0, 0, 0);
+      const uint8_t* pk = base + qo[kk & 3] + 256 * (kk >> 2);
+      const uint4 k0 = *reinterpret_cast<const uint4*>(pk);
+      const uint4 k1 = *reinterpret_cast<const uint4*>(pk + 16 * kRowBytes);
+      // head rows 16w + l16 share the K rows' swizzle offsets (f(r + 16) = f(r))
+      const bf16x8 qk = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(q_s + wv * 16 * kRowBytes + qo[kk & 3] + 256 * (kk >> 2)));
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k0), qk, s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k1), qk, s1, 0, 0, 0);
+      if ((kk & 3) == 3) asm volatile("" ::: "memory");  // bound the fragment reads in flight
     }
     // lane holds head `head`, entries c*32 + 4g + i and c*32 + 16 + 4g + i
     float sv[8];
@@ -201,106 +219,89 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
       for (int tt = 0; tt < 32; ++tt) acc[tt] *= alpha;
     }
 
-    // O^T += V^T P^T, 32 tiles of 16 dims
-    const int tj = (lane >> 2) & 3, tc = lane & 3;
-    const int r_lo = 4 * g + tj, r_hi = 16 + 4 * g + tj;
+    // O^T += V^T P^T, 32 tiles of 16 dims (tile tt = 8a + bt reads rows
+    // 4g + tj and 16 + 4g + tj at vo[bt] + 256 a)
 #pragma unroll
     for (int tt = 0; tt < 32; ++tt) {
-      const int byte = tt * 32 + tc * 8;
+      const uint8_t* pv_lo = base + vo[tt & 7] + 256 * (tt >> 3);
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)((__attribute__((address_space(3))) uint8_t*)(base + lds_off(r_lo, byte))));
+          (lds_s16x4*)((__attribute__((address_space(3))) uint8_t*)(pv_lo)));
       const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)((__attribute__((address_space(3))) uint8_t*)(base + lds_off(r_hi, byte))));
+          (lds_s16x4*)((__attribute__((address_space(3))) uint8_t*)(pv_lo + 16 * kRowBytes)));
       typedef short s16x8 __attribute__((ext_vector_type(8)));
       const s16x8 v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v8), pb, acc[tt], 0, 0, 0);
+      if ((tt & 3) == 3) asm volatile("" ::: "memory");
     }
   };
 
-  if constexpr (KV == CSA2_KV_BF16) {
-    // ---- bf16 rows go HBM -> LDS by DMA through an NBUF-deep ring ----
-    // Wave w moves rows 8w .. 8w+7 of a chunk, one 1 KiB row per instruction;
-    // lane l fetches the 16-byte unit that belongs at LDS unit l of the row.
-    // Rows past the last entry repeat a real row (their probabilities are 0),
-    // so every instruction is whole and each chunk is exactly 8 per wave.
-    auto issue = [&](int c) {
-      uint8_t* slot = smem + (c % NBUF) * kBufBytes;
+  // ---- staging: chunk c's rows travel HBM -> registers -> LDS.  Two register
+  // sets alternate, so while chunk c is consumed the loads of chunks c+1 and
+  // c+2 are in flight; LDS is double buffered.  Row `er` of a chunk is moved by
+  // one wave instruction (64 lanes x 16 bytes of bf16 = one 1 KiB row).  Rows
+  // past the last entry repeat a real row (their probabilities are 0). ----
+  constexpr int kPieces = kBufBytes / 16 / 256;  // 8 LDS units per thread per chunk
+  struct Stage {
+    uint4 v[KV == CSA2_KV_BF16 ? kPieces : 1];
+    uint2 code[KV == CSA2_KV_BF16 ? 1 : kPieces];
+    uint32_t sc[KV == CSA2_KV_BF16 ? 1 : kPieces];
+  };
+  auto fetch = [&](int c, Stage& st) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int er = wv * 8 + k;
-        int e = c * kChunk + er;
-        if (e >= E) e = 0;
-        const int64_t ev = ent_s[e];
-        const bool pool = ev < 0;
-        const int64_t row = pool ? (-ev - 1) : ev;
-        const uint8_t* src = (pool ? a.comp_kv : a.win_kv) + row * kRowBytes + swz_unit(er, lane) * 16;
-        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
-                                         (void __attribute__((address_space(3)))*)(slot + er * kRowBytes), 16,
-                                         0, 0);
+    for (int it = 0; it < kPieces; ++it) {
+      const int p = it * 256 + t;
+      const int er = p >> 6, u = p & 63;
+      int e = c * kChunk + er;
+      if (e >= E) e = 0;
+      const int64_t ev = ent_s[e];
+      const bool pool = ev < 0;
+      const int64_t row = pool ? (-ev - 1) : ev;
+      if constexpr (KV == CSA2_KV_BF16) {
+        st.v[it] = *reinterpret_cast<const uint4*>((pool ? a.comp_kv : a.win_kv) + row * kRowBytes + u * 16);
+      } else {
+        st.code[it] = *reinterpret_cast<const uint2*>((pool ? a.comp_kv : a.win_kv) + row * kDim + u * 8);
+        st.sc[it] = (pool ? a.comp_scale : a.win_scale)[row * (kDim / kScaleBlock) + (u >> 2)];
       }
-    };
-    int issued = 0;
-    const int total = cend - cbeg;
-    for (; issued < total && issued < NBUF; ++issued) issue(cbeg + issued);
-    for (int i = 0; i < total; ++i) {
-      const int younger = issued - i - 1;  // chunks issued after this one, still allowed in flight
-      if (younger >= 3)
-        asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
-      else if (younger == 2)
-        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-      else if (younger == 1)
-        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      consume(smem + ((cbeg + i) % NBUF) * kBufBytes, cbeg + i);
-      __syncthreads();
-      if (issued < total) issue(cbeg + issued++);
     }
-  } else {
-    // ---- fp8 rows: widened to bf16 in registers, double-buffered in LDS ----
-    constexpr int kPieces = 8;  // 16-byte LDS pieces per thread per chunk
-    uint4 stage[kPieces];
-    auto fetch = [&](int c) {
+  };
+  auto stash = [&](int buf, const Stage& st) {
+    uint8_t* base = smem + buf * kBufBytes;
 #pragma unroll
-      for (int it = 0; it < kPieces; ++it) {
-        const int p = it * 256 + t;
-        const int er = p >> 6, u = p & 63;
-        const int e = c * kChunk + er;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (e < E) {
-          const int64_t ev = ent_s[e];
-          const bool pool = ev < 0;
-          const int64_t row = pool ? (-ev - 1) : ev;
-          const uint8_t* base = pool ? a.comp_kv : a.win_kv;
-          const uint8_t* sc = pool ? a.comp_scale : a.win_scale;
-          const uint2 codes = *reinterpret_cast<const uint2*>(base + row * kDim + u * 8);
-          const int ex = (int)sc[row * (kDim / kScaleBlock) + (u >> 2)] - 127;
-          v = fp8x8_to_bf16x8(codes, ex);
-        }
-        stage[it] = v;
+    for (int it = 0; it < kPieces; ++it) {
+      const int p = it * 256 + t;
+      uint4 v;
+      if constexpr (KV == CSA2_KV_BF16) {
+        v = st.v[it];
+      } else {
+        v = fp8x8_to_bf16x8(st.code[it], st.sc[it]);
       }
-    };
-    auto stash = [&](int buf) {
-      uint8_t* base = smem + buf * kBufBytes;
-#pragma unroll
-      for (int it = 0; it < kPieces; ++it) {
-        const int p = it * 256 + t;
-        *reinterpret_cast<uint4*>(base + lds_off(p >> 6, (p & 63) * 16)) = stage[it];
-      }
-    };
-    if (cbeg < cend) {
-      fetch(cbeg);
-      stash(0);
+      *reinterpret_cast<uint4*>(base + lds_off(p >> 6, (p & 63) * 16)) = v;
+    }
+  };
+  Stage s0, s1;
+  if (cbeg < cend) {
+    fetch(cbeg, s0);
+    if (cbeg + 1 < cend) fetch(cbeg + 1, s1);
+    stash(0, s0);
+    if (cbeg + 2 < cend) fetch(cbeg + 2, s0);
+  }
+  __syncthreads();
+  // iteration c consumes LDS buffer (c - cbeg) & 1; the register set holding
+  // chunk c+1 is stashed into the other buffer, then refilled with chunk c+3
+  for (int c = cbeg; c < cend; c += 2) {
+    consume(smem, c);
+    if (c + 1 < cend) {
+      stash(1, s1);
+      if (c + 3 < cend) fetch(c + 3, s1);
     }
     __syncthreads();
-    for (int c = cbeg; c < cend; ++c) {
-      const int buf = (c - cbeg) & 1;
-      if (c + 1 < cend) fetch(c + 1);
-      consume(smem + buf * kBufBytes, c);
-      if (c + 1 < cend) stash(buf ^ 1);
-      __syncthreads();
+    if (c + 1 >= cend) break;
+    consume(smem + kBufBytes, c + 1);
+    if (c + 2 < cend) {
+      stash(0, s0);
+      if (c + 4 < cend) fetch(c + 4, s0);
     }
+    __syncthreads();
   }
 
   // ---- epilogue: lane holds O^T[16*tt + 4g + i][head] ----
@@ -412,9 +413,9 @@ hipError_t launch_attend(const csa2_dims& d, int32_t B, const csa2_batch& bt, co
   a.n_split = n_split;
   a.scale_log2 = d.softmax_scale * kLog2e;
   if (d.kv_dtype == CSA2_KV_BF16)
-    hipLaunchKernelGGL((attend_kernel<CSA2_KV_BF16, 4>), dim3(B * n_split), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attend_kernel<CSA2_KV_BF16>), dim3(B * n_split), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((attend_kernel<CSA2_KV_FP8_E4M3_UE8M0_32, 2>), dim3(B * n_split), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attend_kernel<CSA2_KV_FP8_E4M3_UE8M0_32>), dim3(B * n_split), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_split == 1) return e;
   hipLaunchKernelGGL(attend_combine, dim3(B * kHeads), dim3(128), 0, s, n_split, a.part_o, a.part_ml, sink,
