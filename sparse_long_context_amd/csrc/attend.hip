@@ -6,23 +6,26 @@
 // denominator; a query with no entry yields zeros (PocketLLM page, "The op
 // layer").
 //
-// Workgroup = one (query, split) pair, 4 waves; wave w owns heads 16w..16w+15.
-// Entries are processed in chunks of 32 rows staged in LDS (double buffered);
-// their global loads are issued two chunks ahead into registers, and fp8 rows
-// are widened to bf16 on the way into LDS.  Per chunk:
-//   S^T (32 entries x 16 heads) = K (32 x 512) * Q^T      v_mfma_f32_16x16x32_bf16
-//   online softmax per head in fp32 (exp2 domain)
-//   O^T (512 dims x 16 heads) += V^T (512 x 32) * P^T       same MFMA
+// Workgroup = one (query, split) pair, 8 waves, two per SIMD so one wave's
+// latency (LDS, softmax, barriers) hides behind another's matrix work.  Wave w
+// owns heads 16(w%4) .. +15 and half h = w/4 of the 512 dims: it contracts its
+// dim half of q.k, the two halves add their partial scores through LDS (a + b
+// is the same sum in both waves), and it accumulates its dim half of the
+// output.  Entries are processed in chunks of 32 rows staged in LDS (double
+// buffered); their global loads are issued two chunks ahead into registers,
+// and fp8 rows are widened to bf16 on the way into LDS.  Per chunk and wave:
+//   S^T (32 entries x 16 heads) = K (32 x 256) * Q^T (256 x 16)   v_mfma_f32_16x16x32_bf16
+//   + the partner half's partial, online softmax in fp32 (exp2 domain)
+//   O^T (256 dims x 16 heads) += V^T (256 x 32) * P^T (32 x 16)     same MFMA
 // Putting the entries on the M side of the first product leaves each lane's
 // probabilities (head = lane % 16, 8 entries) exactly where the second
-// product's B operand needs them, so P never leaves registers.  V^T fragments
-// come straight out of the row-major LDS tile with the gfx950 transposing LDS
-// read (ds_read_b64_tr_b16).  Rows are XOR-swizzled in 16-byte units so both
-// the row reads of the first product and the transposed reads of the second
-// spread over all LDS banks.
+// product's B operand needs them.  V^T fragments come straight out of the
+// row-major LDS tile with the gfx950 transposing LDS read (ds_read_b64_tr_b16).
+// Rows are XOR-swizzled in 16-byte units so the row reads of the first product
+// and the transposed reads of the second both spread over all LDS banks.
 //
 // FP8 rows (E4M3 with one UE8M0 scale per 32 values) are widened to bf16 while
-// staging; the conversion is exact (4 significant bits times a power of two).
+// staging, exactly (each product has at most 4 significant bits).
 #include "csa2_internal.h"
 
 namespace csa2 {
@@ -68,7 +71,8 @@ struct AttendArgs {
 // 2-bit halves of r mod 16 (so f(r) = f(r + 16)).  Sixteen consecutive rows at
 // one unit (the row reads of the first product), and four aligned rows x four
 // aligned units (the transposing reads of the second), both land on 16
-// distinct bank groups.
+// distinct bank groups.  f touches only the low four bits of a unit index, so
+// every fragment address is a per-lane base plus a compile-time offset.
 __device__ __forceinline__ int swz_unit(int r, int u) { return u ^ (((r & 3) << 2) | ((r >> 2) & 3)); }
 __device__ __forceinline__ int lds_off(int r, int byte) {
   return r * kRowBytes + (swz_unit(r, byte >> 4) << 4) + (byte & 15);
@@ -86,39 +90,45 @@ __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 codes, uint32_t e) {
                     __builtin_bit_cast(uint32_t, a2), __builtin_bit_cast(uint32_t, a3));
 }
 
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kPieces = kBufBytes / 16 / kThreads;  // 16-byte LDS units per thread per chunk (4)
+
 template <int KV>
-__global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
+__global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kBufBytes];  // double buffer
-  __shared__ __attribute__((aligned(16))) uint8_t q_s[kHeads * kRowBytes];  // the query, 64 KiB
+  __shared__ __attribute__((aligned(16))) float xs_s[kWaves][8][64];     // partial scores
   __shared__ int64_t ent_s[kMaxEntries];  // >= 0: window row; < 0: -(pool row) - 1
-  __shared__ uint32_t wcnt_s[4];
+  __shared__ uint32_t wcnt_s[kWaves];
 
   const int b = blockIdx.x / a.n_split;
   const int sp = blockIdx.x % a.n_split;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int hg = wv & 3, dh = wv >> 2;  // head group, dim half
   const int g = lane >> 4, l16 = lane & 15;
 
   // ---- entry list: window rows, then the selected pool rows in list order ----
   int wl = a.win_kv ? a.win_len[b] : 0;  // no window rows without a window source
   wl = wl < 0 ? 0 : (wl > a.W ? a.W : wl);
   const int64_t w0 = a.win_row0[b];
-  for (int e = t; e < wl; e += 256) ent_s[e] = w0 + e;
+  for (int e = t; e < wl; e += kThreads) ent_s[e] = w0 + e;
   const int md = a.mode[b];
   uint32_t nsel = 0;
   if (md != CSA2_MODE_WINDOW && a.topk != nullptr && a.comp_kv != nullptr) {
     const int32_t plen = a.pool_len[b];
     const int64_t p0 = a.pool_row0[b];
     const int32_t* lst = a.topk + (int64_t)b * a.K;
-    for (int r0 = 0; r0 < a.K; r0 += 256) {
+    for (int r0 = 0; r0 < a.K; r0 += kThreads) {
       const int i = r0 + t;
-      int32_t idx = (i < a.K) ? lst[i] : -1;
-      const bool ok = idx >= 0 && idx < plen;
+      const int32_t idx = (i < a.K) ? lst[i] : -1;
+      const bool ok = (idx >= 0) & (idx < plen);
       const uint64_t m = __ballot(ok);
       if (lane == 0) wcnt_s[wv] = __popcll(m);
       __syncthreads();
       uint32_t before = nsel, tot = 0;
-      for (int w = 0; w < 4; ++w) {
-        if (w < wv) before += wcnt_s[w];
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        before += (w < wv) ? wcnt_s[w] : 0u;
         tot += wcnt_s[w];
       }
       before += __popcll(m & ((1ull << lane) - 1ull));
@@ -134,59 +144,57 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
   const int cbeg = sp * cps;
   const int cend = (cbeg + cps < nch) ? cbeg + cps : nch;
 
-  // ---- the query's 64 heads x 512 dims go to LDS once (1 KiB row per head,
-  // same swizzle as the KV rows); fragments are read per chunk as the B
-  // operand (dims x heads) ----
-  const int head = wv * 16 + l16;
+  // ---- q fragments of this wave's 16 heads and dim half (B operand, dims x heads) ----
+  const int head = hg * 16 + l16;
+  bf16x8 qf[8];
   {
-    const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.q + (int64_t)b * kHeads * kDim);
+    const uint16_t* qp = a.q + ((int64_t)b * kHeads + head) * kDim + dh * 256 + g * 8;
 #pragma unroll
-    for (int it = 0; it < kHeads * kRowBytes / 16 / 256; ++it) {
-      const int p = it * 256 + t;
-      *reinterpret_cast<uint4*>(q_s + lds_off(p >> 6, (p & 63) * 16)) =
-          *reinterpret_cast<const uint4*>(qsrc + (size_t)p * 16);
-    }
+    for (int kk = 0; kk < 8; ++kk) qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + kk * 32));
   }
 
-  f32x4 acc[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -__builtin_inff(), l_run = 0.f;
-
-  // ---- per-lane LDS offsets.  The swizzle only touches the low four bits of
-  // a row's 16-byte unit index, so each fragment address is one of a few
-  // per-lane bases plus a compile-time offset (and rows r, r+16 share f). ----
+  // ---- per-lane LDS bases: K fragment kk = 4a + bq of row l16 sits at
+  // qo[bq] + 512 dh + 256 a; V^T tile tt = 8a + bt of rows 4g + tj at
+  // vo[bt] + 512 dh + 256 a; rows r + 16 are 16 KiB further on ----
   const int tj = (lane >> 2) & 3, tc = lane & 3;
   const int r_lo = 4 * g + tj;
   uint32_t qo[4], vo[8];
 #pragma unroll
-  for (int bq = 0; bq < 4; ++bq) qo[bq] = l16 * kRowBytes + (swz_unit(l16, 4 * bq + g) << 4);
+  for (int bq = 0; bq < 4; ++bq) qo[bq] = l16 * kRowBytes + dh * 512 + (swz_unit(l16, 4 * bq + g) << 4);
 #pragma unroll
-  for (int bt = 0; bt < 8; ++bt) vo[bt] = r_lo * kRowBytes + (swz_unit(r_lo, 2 * bt + (tc >> 1)) << 4) + 8 * (tc & 1);
+  for (int bt = 0; bt < 8; ++bt)
+    vo[bt] = r_lo * kRowBytes + dh * 512 + (swz_unit(r_lo, 2 * bt + (tc >> 1)) << 4) + 8 * (tc & 1);
 
-  // ---- one chunk of 32 staged rows: S^T, online softmax, O^T update ----
+  f32x4 acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -__builtin_inff(), l_run = 0.f;
+
+  // ---- one chunk of 32 staged rows ----
   auto consume = [&](const uint8_t* base, int c) {
-    // S^T = K Q^T: rows 0-15 and 16-31 of the chunk (K fragment kk = 4a + bq
-    // sits at qo[bq] + 256 a, its second-half twin 16 rows further)
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
+    for (int kk = 0; kk < 8; ++kk) {
       const uint8_t* pk = base + qo[kk & 3] + 256 * (kk >> 2);
       const uint4 k0 = *reinterpret_cast<const uint4*>(pk);
       const uint4 k1 = *reinterpret_cast<const uint4*>(pk + 16 * kRowBytes);
-      // head rows 16w + l16 share the K rows' swizzle offsets (f(r + 16) = f(r))
-      const bf16x8 qk = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(q_s + wv * 16 * kRowBytes + qo[kk & 3] + 256 * (kk >> 2)));
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k0), qk, s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k1), qk, s1, 0, 0, 0);
-      if ((kk & 3) == 3) asm volatile("" ::: "memory");  // bound the fragment reads in flight
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k0), qf[kk], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k1), qf[kk], s1, 0, 0, 0);
     }
-    // lane holds head `head`, entries c*32 + 4g + i and c*32 + 16 + 4g + i
+    // add the partner half's partial scores (same sum, same order of the two terms)
+    float* mine = &xs_s[wv][0][0];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mine[i * 64 + lane] = s0[i], mine[(4 + i) * 64 + lane] = s1[i];
+    __syncthreads();
+    const float* other = &xs_s[wv ^ 4][0][0];
     float sv[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      const float t0 = (dh == 0) ? s0[i] + other[i * 64 + lane] : other[i * 64 + lane] + s0[i];
+      const float t1 = (dh == 0) ? s1[i] + other[(4 + i) * 64 + lane] : other[(4 + i) * 64 + lane] + s1[i];
       const int e0 = c * kChunk + 4 * g + i, e1 = e0 + 16;
-      sv[i] = (e0 < E) ? s0[i] * a.scale_log2 : -__builtin_inff();
-      sv[4 + i] = (e1 < E) ? s1[i] * a.scale_log2 : -__builtin_inff();
+      sv[i] = (e0 < E) ? t0 * a.scale_log2 : -__builtin_inff();
+      sv[4 + i] = (e1 < E) ? t1 * a.scale_log2 : -__builtin_inff();
     }
     float cmax = sv[0];
 #pragma unroll
@@ -202,27 +210,25 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
       alpha = __builtin_amdgcn_exp2f(m_run - cmax);
       m_run = cmax;
     }
-    float pv[8], rs = 0.f;
+    const bool live = m_run != -__builtin_inff();
+    float rs = 0.f;
+    bf16x8 pb;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      pv[i] = (m_run == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(sv[i] - m_run);
-      rs += pv[i];
+      const float pv = live ? __builtin_amdgcn_exp2f(sv[i] - m_run) : 0.f;
+      rs += pv;
+      pb[i] = (__bf16)pv;
     }
     rs += __shfl_xor(rs, 16);
     rs += __shfl_xor(rs, 32);
     l_run = l_run * alpha + rs;
-    bf16x8 pb;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) pb[i] = (__bf16)pv[i];
     if (__ballot(raise)) {  // wave-uniform: rescale only when some head moved
 #pragma unroll
-      for (int tt = 0; tt < 32; ++tt) acc[tt] *= alpha;
+      for (int tt = 0; tt < 16; ++tt) acc[tt] *= alpha;
     }
-
-    // O^T += V^T P^T, 32 tiles of 16 dims (tile tt = 8a + bt reads rows
-    // 4g + tj and 16 + 4g + tj at vo[bt] + 256 a)
+    // O^T (this wave's 256 dims x 16 heads) += V^T P^T, 16 tiles of 16 dims
 #pragma unroll
-    for (int tt = 0; tt < 32; ++tt) {
+    for (int tt = 0; tt < 16; ++tt) {
       const uint8_t* pv_lo = base + vo[tt & 7] + 256 * (tt >> 3);
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_s16x4*)((__attribute__((address_space(3))) uint8_t*)(pv_lo)));
@@ -231,16 +237,13 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
       typedef short s16x8 __attribute__((ext_vector_type(8)));
       const s16x8 v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v8), pb, acc[tt], 0, 0, 0);
-      if ((tt & 3) == 3) asm volatile("" ::: "memory");
     }
   };
 
   // ---- staging: chunk c's rows travel HBM -> registers -> LDS.  Two register
   // sets alternate, so while chunk c is consumed the loads of chunks c+1 and
-  // c+2 are in flight; LDS is double buffered.  Row `er` of a chunk is moved by
-  // one wave instruction (64 lanes x 16 bytes of bf16 = one 1 KiB row).  Rows
-  // past the last entry repeat a real row (their probabilities are 0). ----
-  constexpr int kPieces = kBufBytes / 16 / 256;  // 8 LDS units per thread per chunk
+  // c+2 are in flight; LDS is double buffered.  A wave instruction moves half a
+  // 1 KiB bf16 row; rows past the last entry repeat a real row (probability 0).
   struct Stage {
     uint4 v[KV == CSA2_KV_BF16 ? kPieces : 1];
     uint2 code[KV == CSA2_KV_BF16 ? 1 : kPieces];
@@ -249,7 +252,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
   auto fetch = [&](int c, Stage& st) {
 #pragma unroll
     for (int it = 0; it < kPieces; ++it) {
-      const int p = it * 256 + t;
+      const int p = it * kThreads + t;
       const int er = p >> 6, u = p & 63;
       int e = c * kChunk + er;
       if (e >= E) e = 0;
@@ -268,7 +271,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     uint8_t* base = smem + buf * kBufBytes;
 #pragma unroll
     for (int it = 0; it < kPieces; ++it) {
-      const int p = it * 256 + t;
+      const int p = it * kThreads + t;
       uint4 v;
       if constexpr (KV == CSA2_KV_BF16) {
         v = st.v[it];
@@ -278,33 +281,34 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
       *reinterpret_cast<uint4*>(base + lds_off(p >> 6, (p & 63) * 16)) = v;
     }
   };
-  Stage s0, s1;
+  Stage st0, st1;
   if (cbeg < cend) {
-    fetch(cbeg, s0);
-    if (cbeg + 1 < cend) fetch(cbeg + 1, s1);
-    stash(0, s0);
-    if (cbeg + 2 < cend) fetch(cbeg + 2, s0);
+    fetch(cbeg, st0);
+    if (cbeg + 1 < cend) fetch(cbeg + 1, st1);
+    stash(0, st0);
+    if (cbeg + 2 < cend) fetch(cbeg + 2, st0);
   }
   __syncthreads();
-  // iteration c consumes LDS buffer (c - cbeg) & 1; the register set holding
-  // chunk c+1 is stashed into the other buffer, then refilled with chunk c+3
+  // chunk c lives in LDS buffer (c - cbeg) & 1; after consuming it, the
+  // register set holding chunk c+1 goes to the other buffer and is refilled
+  // with chunk c+3
   for (int c = cbeg; c < cend; c += 2) {
     consume(smem, c);
     if (c + 1 < cend) {
-      stash(1, s1);
-      if (c + 3 < cend) fetch(c + 3, s1);
+      stash(1, st1);
+      if (c + 3 < cend) fetch(c + 3, st1);
     }
     __syncthreads();
     if (c + 1 >= cend) break;
     consume(smem + kBufBytes, c + 1);
     if (c + 2 < cend) {
-      stash(0, s0);
-      if (c + 4 < cend) fetch(c + 4, s0);
+      stash(0, st0);
+      if (c + 4 < cend) fetch(c + 4, st0);
     }
     __syncthreads();
   }
 
-  // ---- epilogue: lane holds O^T[16*tt + 4g + i][head] ----
+  // ---- epilogue: lane holds O^T[256 dh + 16 tt + 4g + i][head] ----
   if (a.n_split == 1) {
     float M = m_run, L = l_run, f;
     if (a.sink) {
@@ -316,20 +320,21 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     } else {
       f = (L > 0.f) ? 1.f / L : 0.f;
     }
-    float* op = a.out + ((int64_t)b * kHeads + head) * kDim + 4 * g;
+    float* op = a.out + ((int64_t)b * kHeads + head) * kDim + dh * 256 + 4 * g;
 #pragma unroll
-    for (int tt = 0; tt < 32; ++tt) {
+    for (int tt = 0; tt < 16; ++tt) {
       const f32x4 v = acc[tt] * f;
       *reinterpret_cast<float4*>(op + tt * 16) = make_float4(v[0], v[1], v[2], v[3]);
     }
-    if (a.lse && g == 0) a.lse[(int64_t)b * kHeads + head] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -__builtin_inff();
+    if (a.lse && g == 0 && dh == 0)
+      a.lse[(int64_t)b * kHeads + head] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -__builtin_inff();
   } else {
     const int64_t slot = ((int64_t)b * a.n_split + sp) * kHeads + head;
-    float* op = a.part_o + slot * kDim + 4 * g;
+    float* op = a.part_o + slot * kDim + dh * 256 + 4 * g;
 #pragma unroll
-    for (int tt = 0; tt < 32; ++tt)
+    for (int tt = 0; tt < 16; ++tt)
       *reinterpret_cast<float4*>(op + tt * 16) = make_float4(acc[tt][0], acc[tt][1], acc[tt][2], acc[tt][3]);
-    if (g == 0) {
+    if (g == 0 && dh == 0) {
       a.part_ml[slot * 2] = m_run;
       a.part_ml[slot * 2 + 1] = l_run;
     }
@@ -413,9 +418,9 @@ hipError_t launch_attend(const csa2_dims& d, int32_t B, const csa2_batch& bt, co
   a.n_split = n_split;
   a.scale_log2 = d.softmax_scale * kLog2e;
   if (d.kv_dtype == CSA2_KV_BF16)
-    hipLaunchKernelGGL((attend_kernel<CSA2_KV_BF16>), dim3(B * n_split), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attend_kernel<CSA2_KV_BF16>), dim3(B * n_split), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((attend_kernel<CSA2_KV_FP8_E4M3_UE8M0_32>), dim3(B * n_split), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attend_kernel<CSA2_KV_FP8_E4M3_UE8M0_32>), dim3(B * n_split), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_split == 1) return e;
   hipLaunchKernelGGL(attend_combine, dim3(B * kHeads), dim3(128), 0, s, n_split, a.part_o, a.part_ml, sink,
