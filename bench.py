@@ -30,6 +30,7 @@ INDEX_Q_BYTES = 128 * 4      # one fp32 indexer query per query
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILE_DIR, "index_scores_decode_64x16384_traffic.json")
 INDEX_SRC = os.path.join(ROOT, "sparse_long_context_amd", "csrc", "index_scores.hip")
+COPY_PROBE_BYTES = 512 << 20
 
 
 def source_digest(path):
@@ -64,6 +65,48 @@ def traffic_from_profile():
     return rec.get("hbm_bytes_per_launch")
 
 
+def summarize_traffic(fetch_csv, write_csv):
+    """Per-launch HBM bytes of the indexer from rocprofv3 counter CSVs.
+
+    FETCH_SIZE and WRITE_SIZE are in KiB per dispatch.  Each is scaled by what
+    the counter reads for a plain streaming kernel of COPY_PROBE_BYTES (a sum
+    that reads exactly that many bytes, a fill that writes them), so the result
+    is in true bytes."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    out = {}
+    for path, counter in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
+        v = per_kernel(path, counter)
+        idx = [x for k, xs in v.items() if "index_scores_decode" in k for x in xs]
+        # the probe's streaming kernel for this counter: the sum reads, the fill writes
+        probe = "reduce_kernel" if counter == "FETCH_SIZE" else "FillFunctor"
+        cpy = [x for k, xs in v.items() if probe in k for x in xs if x * 1024 > 0.25 * COPY_PROBE_BYTES]
+        if not idx or not cpy:
+            raise SystemExit(f"{path}: no indexer or copy dispatches with {counter}")
+        scale = COPY_PROBE_BYTES / (1024.0 * (sum(cpy) / len(cpy)))
+        out[counter] = {"kib_per_launch": sum(idx) / len(idx), "copy_kib": sum(cpy) / len(cpy), "scale": scale,
+                        "bytes_per_launch": scale * 1024.0 * sum(idx) / len(idx), "launches": len(idx)}
+    rec = {"kernel": "index_scores_decode", "workload": "decode, 64 queries x 16,384 candidates",
+           "kernel_source_sha256_16": source_digest(INDEX_SRC),
+           "hbm_bytes_per_launch": round(out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"]),
+           "fetch": out["FETCH_SIZE"], "write": out["WRITE_SIZE"],
+           "commands": ["rocprofv3 --pmc FETCH_SIZE -d <dir> -o fetch --output-format csv -- python3 bench.py "
+                        "--no-cpu-baseline --copy-probe --steps 3 --warmup 1",
+                        "rocprofv3 --pmc WRITE_SIZE -d <dir> -o write --output-format csv -- python3 bench.py "
+                        "--no-cpu-baseline --copy-probe --steps 3 --warmup 1"]}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
 def cpu_baseline(inp, min_seconds=10.0, max_seconds=30.0):
     """Oracle over whole passes of the batch until at least min_seconds."""
     from oracle import oracle as O
@@ -90,7 +133,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1, help="decode workload index (1, 3 or 4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain %d MiB fill and sum (for scaling rocprofv3 byte counters)" % (COPY_PROBE_BYTES >> 20))
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of 'bench.py --copy-probe' "
+                         "into the indexer's HBM bytes per launch, and exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        summarize_traffic(*args.traffic_from)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); the decode batch "
               "shards by sequence with no exchange, so N GPUs would each run this same step on their own "
@@ -128,28 +179,39 @@ def main():
     ms_step = ev0.elapsed_time(ev1) / args.steps
     value = B * args.steps / wall
 
-    # per-kernel durations: the same three launches issued stage by stage, with
-    # HIP events between them on the launch stream
+    # per-kernel durations: each of the three stage entry points launched
+    # `steps` times back to back between two HIP events on the launch stream
+    # (the same kernels and launch shapes csa2_decode issues)
     stride = w.max_cand
     scores = torch.empty((B, stride), dtype=torch.float32, device="cuda")
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    acc = [0.0, 0.0, 0.0]
     sp_ws = csa2.csa2_workspace_size(w.dims, B, 0)
     attend_ws = torch.empty(max(sp_ws, 1), dtype=torch.uint8, device="cuda")
-    for it in range(args.warmup + args.steps):
-        ev[0].record(stream)
-        csa2.csa2_index_scores(w.dims, B, w.batch, w.idx_q, w.idx_w, w.idx_k, scores, stride)
-        ev[1].record(stream)
-        csa2.csa2_topk(w.dims, B, w.batch, scores, stride, w.topk)
-        ev[2].record(stream)
-        csa2.csa2_attend(w.dims, B, w.batch, w.q, w.win_kv, w.win_scale, w.comp_kv, w.comp_scale, w.topk, w.sink,
-                         w.out, w.lse, attend_ws, sp_ws)
-        ev[3].record(stream)
+    stages = [
+        lambda: csa2.csa2_index_scores(w.dims, B, w.batch, w.idx_q, w.idx_w, w.idx_k, scores, stride),
+        lambda: csa2.csa2_topk(w.dims, B, w.batch, scores, stride, w.topk),
+        lambda: csa2.csa2_attend(w.dims, B, w.batch, w.q, w.win_kv, w.win_scale, w.comp_kv, w.comp_scale, w.topk,
+                                 w.sink, w.out, w.lse, attend_ws, sp_ws),
+    ]
+    stage_us = []
+    for fn in stages:
+        for _ in range(args.warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        if it >= args.warmup:
-            for k in range(3):
-                acc[k] += ev[k].elapsed_time(ev[k + 1])
-    stage_us = [1000.0 * a / args.steps for a in acc]
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        stage_us.append(1000.0 * e0.elapsed_time(e1) / args.steps)
+    if args.copy_probe:
+        # plain streaming kernels of known size, for scaling the HBM byte
+        # counters: a fill writes COPY_PROBE_BYTES, a sum reads them
+        src = torch.empty(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
+        for _ in range(3):
+            src.fill_(1.0)
+            float(src.sum())
+        torch.cuda.synchronize()
 
     n_cand = int(sum(min(int(p), (int(pos) + 1) // int(r)) for p, pos, r, m in
                      zip(inp["pool_len"], inp["pos"], inp["ratio"], inp["mode"]) if m == 0 and r > 0))
