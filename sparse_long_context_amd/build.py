@@ -37,6 +37,9 @@ def build_hip(verbose: bool = False) -> str:
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            # packed-fp32 instructions are kept out of every kernel
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # matrix-core accumulators in ordinary VGPRs, so the register
+           # allocator can use the accumulation registers for staged rows
+           "-mllvm", "-amdgpu-mfma-vgpr-form",
            "-Wall", "-Wno-unused-result",
            "-I", os.path.join(ROOT, "include"),
            "-o", HIP_LIB + ".tmp"] + srcs

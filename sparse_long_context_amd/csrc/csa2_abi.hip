@@ -45,9 +45,17 @@ csa2_status check_batch(const csa2_batch* bt, int32_t B) {
 
 size_t score_stride_for(int32_t max_cand) { return align_up((size_t)max_cand * sizeof(float)) / sizeof(float); }
 
-size_t decode_ws_bytes(int32_t B, int32_t max_cand) {
+// Batches of up to this many queries attend with four head-group workgroups
+// per query (every workgroup streams all of its query's rows, sharing them
+// through the XCD's L2); larger ones with one workgroup per (query, entry
+// split) holding all 64 heads, where each row crosses into one CU only once.
+constexpr int32_t kHeadGroupMaxBatch = 64;
+bool use_head_groups(int32_t B) { return B <= kHeadGroupMaxBatch; }
+
+// Scores, then the split partials of the attention when its kernel uses them.
+size_t decode_ws_bytes(int32_t B, int32_t max_cand, bool split_partials) {
   size_t s = align_up((size_t)B * score_stride_for(max_cand) * sizeof(float));
-  s += align_up(attend_partial_floats(B, attend_split_for(B)) * sizeof(float));
+  if (split_partials) s += align_up(attend_partial_floats(B, attend_split_for(B)) * sizeof(float));
   return s;
 }
 
@@ -134,7 +142,7 @@ csa2_status csa2_workspace_size(const csa2_dims* dims, int32_t B, int32_t max_ca
   csa2_status st = check_dims(dims);
   if (st != CSA2_OK) return st;
   if (!bytes || B < 0 || max_candidates < 0) return CSA2_ERR_INVALID_ARG;
-  *bytes = decode_ws_bytes(B, max_candidates);
+  *bytes = decode_ws_bytes(B, max_candidates, !use_head_groups(B));
   return CSA2_OK;
 }
 
@@ -186,15 +194,16 @@ csa2_status csa2_attend(const csa2_dims* dims, int32_t B, const csa2_batch* batc
   if (st == CSA2_OK && B > 0) st = check_attend_ptrs(dims, q, win_kv, win_scale, comp_kv, comp_scale, out);
   if (st != CSA2_OK) return st;
   if (B == 0) return CSA2_OK;
-  int n_split = 1;
-  float* partial = nullptr;
-  if (workspace != nullptr || workspace_bytes != 0) {
-    const int sp = attend_split_for(B);
-    const size_t need = align_up(attend_partial_floats(B, sp) * sizeof(float));
-    if (!workspace || workspace_bytes < need) return CSA2_ERR_WORKSPACE;
-    n_split = sp;
-    partial = static_cast<float*>(workspace);
-  }
+  if (use_head_groups(B))
+    return hip_status(launch_attend_hg(*dims, B, *batch, q, win_kv, win_scale, comp_kv, comp_scale, topk_idx, sink,
+                                       out, lse, stream));
+  if (workspace == nullptr && workspace_bytes == 0)
+    return attend_common(dims, B, batch, q, win_kv, win_scale, comp_kv, comp_scale, topk_idx, sink, out, lse, nullptr,
+                         1, stream);
+  const int n_split = attend_split_for(B);
+  const size_t need = align_up(attend_partial_floats(B, n_split) * sizeof(float));
+  if (!workspace || workspace_bytes < need) return CSA2_ERR_WORKSPACE;
+  float* partial = n_split > 1 ? static_cast<float*>(workspace) : nullptr;
   return attend_common(dims, B, batch, q, win_kv, win_scale, comp_kv, comp_scale, topk_idx, sink, out, lse, partial,
                        n_split, stream);
 }
@@ -210,20 +219,24 @@ csa2_status csa2_decode(const csa2_dims* dims, int32_t B, const csa2_batch* batc
   if (st != CSA2_OK) return st;
   if (B == 0) return CSA2_OK;
   if (!topk_idx || (batch->max_candidates > 0 && (!idx_q || !idx_k))) return CSA2_ERR_INVALID_ARG;
-  const size_t need = decode_ws_bytes(B, batch->max_candidates);
-  if (!workspace || workspace_bytes < need) return CSA2_ERR_WORKSPACE;
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const bool hg = use_head_groups(B);
+  const size_t need = decode_ws_bytes(B, batch->max_candidates, !hg);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return CSA2_ERR_WORKSPACE;
   const int64_t stride = (int64_t)score_stride_for(batch->max_candidates);
-  float* scores = reinterpret_cast<float*>(ws);
-  ws += align_up((size_t)B * stride * sizeof(float));
-  const int sp = attend_split_for(B);
-  float* partial = sp > 1 ? reinterpret_cast<float*>(ws) : nullptr;
+  float* scores = static_cast<float*>(workspace);
+  const int sp = hg ? 1 : attend_split_for(B);
+  float* partial = sp > 1 ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                                     align_up((size_t)B * stride * sizeof(float)))
+                          : nullptr;
 
   if (batch->max_candidates > 0) {
     if ((st = hip_status(launch_index_scores(*dims, B, *batch, idx_q, idx_w, idx_k, scores, stride, stream))) != CSA2_OK)
       return st;
     if ((st = hip_status(launch_topk(*dims, B, *batch, scores, stride, topk_idx, stream))) != CSA2_OK) return st;
   }
+  if (hg)
+    return hip_status(launch_attend_hg(*dims, B, *batch, q, win_kv, win_scale, comp_kv, comp_scale, topk_idx, sink,
+                                       out, lse, stream));
   return attend_common(dims, B, batch, q, win_kv, win_scale, comp_kv, comp_scale, topk_idx, sink, out, lse, partial, sp,
                        stream);
 }
@@ -233,7 +246,7 @@ csa2_status csa2_prefill_workspace_size(const csa2_dims* dims, const csa2_prefil
   if (st != CSA2_OK) return st;
   if (!bytes) return CSA2_ERR_INVALID_ARG;
   const int32_t T = desc->n_queries;
-  *bytes = prefill_meta_bytes(T) + decode_ws_bytes(T, prefill_max_cand(desc));
+  *bytes = prefill_meta_bytes(T) + decode_ws_bytes(T, prefill_max_cand(desc), true);
   return CSA2_OK;
 }
 
@@ -250,7 +263,7 @@ csa2_status csa2_prefill(const csa2_dims* dims, const csa2_prefill_desc* desc, c
   const bool selects = desc->mode == CSA2_MODE_FULL || desc->mode == CSA2_MODE_REINDEX;
   if (desc->mode != CSA2_MODE_WINDOW && !topk_idx) return CSA2_ERR_INVALID_ARG;
   if (selects && max_cand > 0 && (!idx_q || !idx_k)) return CSA2_ERR_INVALID_ARG;
-  size_t need = prefill_meta_bytes(T) + decode_ws_bytes(T, max_cand);
+  size_t need = prefill_meta_bytes(T) + decode_ws_bytes(T, max_cand, true);
   if (!workspace || workspace_bytes < need) return CSA2_ERR_WORKSPACE;
 
   uint8_t* ws = static_cast<uint8_t*>(workspace);

@@ -43,6 +43,11 @@ hipError_t launch_attend(const csa2_dims& d, int32_t B, const csa2_batch& bt, co
                          const uint8_t* comp_scale, const int32_t* topk_idx, const float* sink,
                          float* out, float* lse, int n_split, float* partial, hipStream_t s);
 size_t attend_partial_floats(int32_t B, int n_split);
+// Decode-shaped batches: four workgroups per query (16 heads each), no workspace.
+hipError_t launch_attend_hg(const csa2_dims& d, int32_t B, const csa2_batch& bt, const void* q,
+                            const void* win_kv, const uint8_t* win_scale, const void* comp_kv,
+                            const uint8_t* comp_scale, const int32_t* topk_idx, const float* sink, float* out,
+                            float* lse, hipStream_t s);
 int attend_split_for(int32_t B);
 
 // Per-query descriptors of a prefill chunk, written into workspace arrays.

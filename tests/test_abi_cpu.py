@@ -103,7 +103,7 @@ def test_bad_arguments_rejected_before_launch():
                          FAKE, 16, stream=0)
     assert e.value.status == csa2.CSA2_ERR_WORKSPACE
     with pytest.raises(E) as e:  # attend: workspace given but too small
-        csa2.csa2_attend(d, 2, batch(), FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 16, stream=0)
+        csa2.csa2_attend(d, 100, batch(), FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 16, stream=0)
     assert e.value.status == csa2.CSA2_ERR_WORKSPACE
 
 
