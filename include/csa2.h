@@ -136,7 +136,8 @@ const char *csa2_status_str(csa2_status s);
 int32_t csa2_last_hip_error(void);
 
 /* Workspace bytes csa2_decode needs for B queries with at most max_candidates
- * candidates each (also enough for csa2_attend's split-K partials). */
+ * candidates each (scores, plus attention split partials when B > 64).  With
+ * max_candidates = 0 it is the workspace csa2_attend can use to split entries. */
 csa2_status csa2_workspace_size(const csa2_dims *dims, int32_t B, int32_t max_candidates,
                                 size_t *bytes);
 
@@ -165,8 +166,11 @@ csa2_status csa2_topk(const csa2_dims *dims, int32_t B, const csa2_batch *batch,
  * win_kv may be NULL (no query then has window rows) and comp_kv may be NULL
  * (no query then has compressed rows); fp8 scale planes are required exactly
  * when their KV source is given.
- * sink: f32 [64] or NULL.  With a workspace of csa2_workspace_size bytes the
- * entries of a query may be split over several workgroups and merged; with
+ * sink: f32 [64] or NULL.
+ * Batches of B <= 64 queries run four workgroups of 16 heads per query and
+ * ignore the workspace.  Larger batches run one workgroup of all 64 heads per
+ * query; with a workspace of csa2_workspace_size(dims, B, 0) bytes the entries
+ * of a query may be split over several such workgroups and merged, with
  * workspace == NULL and workspace_bytes == 0 every query runs unsplit. */
 csa2_status csa2_attend(const csa2_dims *dims, int32_t B, const csa2_batch *batch, const void *q,
                         const void *win_kv, const uint8_t *win_scale, const void *comp_kv,
