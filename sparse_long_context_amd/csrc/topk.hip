@@ -30,6 +30,7 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxKpt = 16;              // keys per thread held in registers
+static_assert(kMaxKpt == 16, "a thread's marks are read as one 16-bit run of a 32-bit word");
 constexpr int kRegKeys = kThreads * kMaxKpt;
 constexpr int kBins = 4096;
 
@@ -41,42 +42,53 @@ __device__ __forceinline__ uint32_t order_key(float s) {
 
 __device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (1ull << lane) - 1ull; }
 
-// Block-wide exclusive suffix sum (sum over threads with a larger id).
+// Inclusive prefix sum over the 64 lanes of a wave: shifts within each row of
+// 16 lanes, then the last lane of a row is broadcast into the rows above it
+// (DPP row_shr:1,2,4,8, row_bcast:15, row_bcast:31).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  int x = (int)v;
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);
+  return (uint32_t)x;
+}
+
+// Block-wide exclusive suffix sum (sum over threads with a larger id).  Every
+// call site passes a barrier before red_s is written again.
 __device__ __forceinline__ uint32_t block_suffix_excl(uint32_t v, uint32_t* red_s, int lane, int wv) {
-  uint32_t inc = v;
+  const uint32_t inc = wave_incl_scan(v);
+  if (lane == 63) red_s[wv] = inc;
+  __syncthreads();
+  uint32_t higher = 0, total = 0;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t x = __shfl_down(inc, o);
-    if (lane + o < 64) inc += x;
+  for (int w = 0; w < kWaves; ++w) {
+    const uint32_t c = red_s[w];
+    higher += (w > wv) ? c : 0u;
+    total += (w == wv) ? c : 0u;
   }
-  if (lane == 0) red_s[wv] = inc;
-  __syncthreads();
-  uint32_t higher = 0;
-  for (int w = wv + 1; w < kWaves; ++w) higher += red_s[w];
-  __syncthreads();
-  return higher + inc - v;
+  // within the wave: lanes above this one hold (wave total - inclusive prefix)
+  return higher + (total - inc);
 }
 
 // Block-wide exclusive prefix sums of two values (sum over threads with a
-// smaller id); also returns the totals.
+// smaller id); also returns the totals.  Every call site passes a barrier
+// before red_s is written again.
 __device__ __forceinline__ void block_prefix2(uint32_t a, uint32_t b, uint32_t* red_s, int lane, int wv,
                                               uint32_t& pa, uint32_t& pb, uint32_t& ta, uint32_t& tb) {
-  uint32_t ia = a, ib = b;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t xa = __shfl_up(ia, o), xb = __shfl_up(ib, o);
-    if (lane >= o) ia += xa, ib += xb;
-  }
+  const uint32_t ia = wave_incl_scan(a), ib = wave_incl_scan(b);
   if (lane == 63) red_s[wv] = ia, red_s[kWaves + wv] = ib;
   __syncthreads();
   uint32_t la = 0, lb = 0;
   ta = 0, tb = 0;
+#pragma unroll
   for (int w = 0; w < kWaves; ++w) {
     const uint32_t ca = red_s[w], cb = red_s[kWaves + w];
     if (w < wv) la += ca, lb += cb;
     ta += ca, tb += cb;
   }
-  __syncthreads();
   pa = la + ia - a;
   pb = lb + ib - b;
 }
@@ -266,17 +278,46 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
   bool ranked = true;  // boundary bucket resolved by direct ranking
   uint32_t thr = 0, take_eq = 0;
   if (!take_all) {
+    // gather the boundary bucket: a wave-wide prefix of the per-thread counts
+    // and one LDS atomic per wave place every key
+    uint32_t nb = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxKpt; ++j) nb += (k[j] != 0u) & ((k[j] >> 20) == bucket);
+    const uint32_t nb_incl = wave_incl_scan(nb);
+    uint32_t wbase = 0;
+    if (lane == 63 && nb_incl != 0u) wbase = atomicAdd(&bcount_s, nb_incl);
+    uint32_t slot = (uint32_t)__builtin_amdgcn_readlane((int)wbase, 63) + nb_incl - nb;
 #pragma unroll
     for (int j = 0; j < kMaxKpt; ++j) {
       if (k[j] != 0u && (k[j] >> 20) == bucket) {
-        const uint32_t slot = atomicAdd(&bcount_s, 1u);
         if (slot < (uint32_t)kRankCap) bk_s[slot] = ((uint64_t)k[j] << 32) | (uint32_t)~(uint32_t)(i0 + j);
+        ++slot;
       }
     }
     __syncthreads();
     const uint32_t m = bcount_s;
     ranked = m <= (uint32_t)kRankCap;
-    if (ranked) {
+    if (ranked && m <= (uint32_t)(kThreads / 4)) {
+      // four threads per key, each comparing against every fourth key
+      const uint32_t key = (uint32_t)t >> 2, part = (uint32_t)t & 3u;
+      const uint64_t me = bk_s[key < m ? key : 0u];
+      uint32_t r = 0;
+      uint32_t q = part;
+      for (; q + 28 < m; q += 32) {
+        uint64_t o[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) o[u] = bk_s[q + 4 * u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) r += (uint32_t)(o[u] > me);
+      }
+      for (; q < m; q += 4) r += (uint32_t)(bk_s[q] > me);
+      // sum the quad (DPP quad_perm [1,0,3,2] then [2,3,0,1])
+      r += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)r, 0xB1, 0xf, 0xf, false);
+      r += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)r, 0x4E, 0xf, 0xf, false);
+      const uint32_t mi = ~(uint32_t)me;
+      if (key < m && part == 0u && r < quota) atomicOr(&mark_s[mi >> 5], 1u << (mi & 31));
+      __syncthreads();
+    } else if (ranked) {
       if ((uint32_t)t < m) {
         // (key desc, index asc) is the unsigned order of key << 32 | ~index
         const uint64_t me = bk_s[t];
@@ -309,11 +350,11 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
     // chosen: eligible (take_all), above the boundary bucket, or a marked bucket key
     bool sel[kMaxKpt];
     uint32_t cnt = 0;
+    const uint32_t mword = mark_s[i0 >> 5] >> (i0 & 31);  // this thread's 16 indices share one word
 #pragma unroll
     for (int j = 0; j < kMaxKpt; ++j) {
       const uint32_t hb = k[j] >> 20;
-      const int i = i0 + j;
-      const uint32_t marked = (mark_s[i >> 5] >> (i & 31)) & 1u;
+      const uint32_t marked = (mword >> j) & 1u;
       sel[j] = take_all ? (k[j] != 0u) : ((hb > bucket) | ((hb == bucket) & (k[j] != 0u) & (marked != 0u)));
       cnt += sel[j];
     }
