@@ -15,8 +15,13 @@
  *   [PLLM] PocketLLM "DeepSeek-V4.1-Flash" -- "The op layer" (finite score
  *          floor: an all-masked row is zeros), "The CSA2 attention layers"
  *          (window quantized to FP8 over 32 elements; a partial group emits
- *          nothing), "Correctness and precision" (-1 fills the unused top-k
- *          slots; ties).
+ *          nothing; compressed KV to FP4 with E4M3 scales over 16, indexer
+ *          keys to FP4 with E8M0 scales over 32), "Correctness and precision"
+ *          (-1 fills the unused top-k slots; ties), the FP4 quantizer notes
+ *          (scale e4m3(amax / 6) with an amax floor of 6 * 2^-9; E8M0 scale
+ *          2^round(log2(amax / 6)); round-to-even FP4 ties).
+ *   [RN] 3f C4 (FP4 main KV cache: E2M1 grid, s = amax / 6 per 16 channels,
+ *          codes round_E2M1(x / s), decode s * c; its worked example).
  *
  * Arithmetic: every floating-point step of the attention is fp64 over the
  * exactly decoded bf16 / fp8 inputs.  The indexer score is defined in fp32 by a
@@ -38,7 +43,8 @@
 #define ORC_ENOMEM (-3)
 
 enum { ORC_MODE_FULL = 0, ORC_MODE_REINDEX = 1, ORC_MODE_REUSE = 2, ORC_MODE_WINDOW = 3 };
-enum { ORC_KV_BF16 = 0, ORC_KV_FP8 = 1 };
+enum { ORC_KV_BF16 = 0, ORC_KV_FP8 = 1, ORC_KV_FP4 = 2 };
+enum { ORC_IDXK_F32 = 0, ORC_IDXK_MXFP4 = 1 };
 
 /* ------------------------------------------------------------------------- */
 /* O0: exact decoding of the storage formats                                  */
@@ -79,6 +85,155 @@ int csa2o_ue8m0_to_f64(uint8_t e, double *out) {
   return ORC_OK;
 }
 
+/* FP4 E2M1: 1 sign, 2 exponent (bias 1), 1 mantissa bit; magnitudes
+ * 0, 0.5, 1, 1.5, 2, 3, 4, 6 ([RN] 3f C4).  `nib` is the low 4 bits. */
+int csa2o_e2m1_to_f64(uint8_t nib, double *out) {
+  int s = (nib >> 3) & 1, e = (nib >> 1) & 3, m = nib & 1;
+  double v = (e == 0) ? 0.5 * (double)m : ldexp(1.0 + 0.5 * (double)m, e - 1);
+  *out = s ? -v : v;
+  return ORC_OK;
+}
+
+/* Nearest E2M1 code to v, ties to the code with an even mantissa bit
+ * ([PLLM] round-to-even FP4 ties); magnitudes above 6 are nearest to 6, so
+ * they saturate there.  A zero magnitude is emitted as +0 (code 0). */
+uint8_t csa2o_e2m1_encode(double v) {
+  const double a = fabs(v);
+  int best = 0, c;
+  double bd = a;
+  for (c = 1; c < 8; ++c) {
+    double g, dist;
+    csa2o_e2m1_to_f64((uint8_t)c, &g);
+    dist = fabs(a - g);
+    if (dist < bd || (dist == bd && (c & 1) == 0)) {
+      bd = dist;
+      best = c;
+    }
+  }
+  return (uint8_t)((v < 0.0 && best != 0) ? (best | 8) : best);
+}
+
+/* Round a finite fp32 value to FP8 E4M3 (the "fn" variant), nearest-even,
+ * saturating at +-448.  Written from the format: 3 fraction bits, exponent
+ * bias 7, subnormal quantum 2^-9. */
+int csa2o_f32_to_e4m3(float v, uint8_t *out) {
+  double a = fabs((double)v), q, r;
+  int e, ef;
+  uint8_t sign = (v < 0.0f) ? 0x80 : 0x00;
+  if (!isfinite(v)) return ORC_ENONFINITE;
+  if (a >= 448.0) {
+    *out = sign | 0x7E;
+    return ORC_OK;
+  }
+  if (a < ldexp(1.0, -6)) {
+    q = ldexp(1.0, -9); /* subnormal spacing */
+  } else {
+    frexp(a, &e);       /* a = f * 2^e, f in [0.5, 1) */
+    q = ldexp(1.0, e - 1 - 3);
+  }
+  r = a / q; /* exact: q is a power of two */
+  {
+    double fl = floor(r), fr = r - fl;
+    if (fr > 0.5 || (fr == 0.5 && fmod(fl, 2.0) != 0.0)) fl += 1.0;
+    r = fl * q;
+  }
+  if (r >= 448.0) r = 448.0;
+  if (r == 0.0) {
+    *out = sign;
+    return ORC_OK;
+  }
+  if (r < ldexp(1.0, -6)) {
+    *out = sign | (uint8_t)(r / ldexp(1.0, -9));
+    return ORC_OK;
+  }
+  frexp(r, &e);
+  ef = e - 1 + 7;
+  *out = sign | (uint8_t)(ef << 3) | (uint8_t)((ldexp(r, -(e - 1)) - 1.0) * 8.0);
+  return ORC_OK;
+}
+
+/* [RN] 3f C4 / [PLLM] FP4 quantizer of the main KV: per block of 16 values,
+ * amax = max |x| (floored at 6 * 2^-9 so every scale is nonzero), the scale is
+ * e4m3(amax / 6) with the division done in fp32, and each code is
+ * round_E2M1(x / s) against that stored scale, the quotient taken in fp32.
+ * Codes are packed two per byte, element 2i in the low nibble.  n must be a
+ * multiple of 16; codes gets n/2 bytes, scales n/16 bytes. */
+int csa2o_quant_fp4kv(const float *x, int64_t n, uint8_t *codes, uint8_t *scales) {
+  int64_t b, i;
+  if (n < 0 || (n % 16) != 0 || !x || !codes || !scales) return ORC_EBADARG;
+  for (b = 0; b < n / 16; ++b) {
+    const float *xb = x + 16 * b;
+    float amax = 0.0f, s32, s;
+    double sd;
+    int rc;
+    for (i = 0; i < 16; ++i) {
+      if (!isfinite(xb[i])) return ORC_ENONFINITE;
+      if (fabsf(xb[i]) > amax) amax = fabsf(xb[i]);
+    }
+    if (amax < 6.0f * 0.001953125f) amax = 6.0f * 0.001953125f;
+    s32 = amax / 6.0f;
+    if ((rc = csa2o_f32_to_e4m3(s32, &scales[b])) != ORC_OK) return rc;
+    csa2o_e4m3_to_f64(scales[b], &sd);
+    s = (float)sd; /* exact */
+    for (i = 0; i < 16; i += 2) {
+      const float q0 = xb[i] / s, q1 = xb[i + 1] / s;
+      codes[8 * b + i / 2] = (uint8_t)(csa2o_e2m1_encode((double)q0) | (csa2o_e2m1_encode((double)q1) << 4));
+    }
+  }
+  return ORC_OK;
+}
+
+/* [PLLM] MXFP4 quantizer of the indexer keys: per block of 32 values the
+ * scale is 2^e with e = round(log2(amax / 6)) (amax / 6 taken in fp32), stored
+ * as the E8M0 byte e + 127 and clamped to 1..254 (an all-zero block gets
+ * 2^-126).  log2 of y = m 2^k (m in [1, 2)) rounds up exactly when m > sqrt 2,
+ * i.e. m * m > 2, which is decided exactly in double; no tie is possible.
+ * Codes are round_E2M1(x / 2^e), the quotient exact.  Packing as above;
+ * codes gets n/2 bytes, scales n/32 bytes. */
+int csa2o_quant_mxfp4(const float *x, int64_t n, uint8_t *codes, uint8_t *scales) {
+  int64_t b, i;
+  if (n < 0 || (n % 32) != 0 || !x || !codes || !scales) return ORC_EBADARG;
+  for (b = 0; b < n / 32; ++b) {
+    const float *xb = x + 32 * b;
+    float amax = 0.0f, y;
+    int e, k;
+    for (i = 0; i < 32; ++i) {
+      if (!isfinite(xb[i])) return ORC_ENONFINITE;
+      if (fabsf(xb[i]) > amax) amax = fabsf(xb[i]);
+    }
+    y = amax / 6.0f;
+    if (y == 0.0f) {
+      e = -126;
+    } else {
+      double m = frexp((double)y, &k) * 2.0; /* y = m 2^(k-1), m in [1, 2) */
+      e = (k - 1) + ((m * m > 2.0) ? 1 : 0);
+    }
+    if (e < -126) e = -126;
+    if (e > 127) e = 127;
+    scales[b] = (uint8_t)(e + 127);
+    for (i = 0; i < 32; i += 2) {
+      const double q0 = ldexp((double)xb[i], -e), q1 = ldexp((double)xb[i + 1], -e);
+      codes[16 * b + i / 2] = (uint8_t)(csa2o_e2m1_encode(q0) | (csa2o_e2m1_encode(q1) << 4));
+    }
+  }
+  return ORC_OK;
+}
+
+/* Decode n MXFP4 values (codes n/2 bytes, scales n/32 E8M0 bytes) to fp32;
+ * exact (at most 2 significant bits times a power of two). */
+int csa2o_dequant_mxfp4(const uint8_t *codes, const uint8_t *scales, int64_t n, float *out) {
+  int64_t i;
+  int rc;
+  if (n < 0 || (n % 32) != 0 || !codes || !scales || !out) return ORC_EBADARG;
+  for (i = 0; i < n; ++i) {
+    double c, s;
+    csa2o_e2m1_to_f64((uint8_t)((codes[i / 2] >> (4 * (i & 1))) & 15), &c);
+    if ((rc = csa2o_ue8m0_to_f64(scales[i / 32], &s)) != ORC_OK) return rc;
+    out[i] = (float)(c * s);
+  }
+  return ORC_OK;
+}
+
 /* Decode one KV row of d values.  bf16 rows are d uint16; fp8 rows are d codes
  * followed (in a separate plane) by d/32 UE8M0 scales, one per 32 values. */
 static int decode_row(int kv_dtype, int d, const void *rows, const uint8_t *scales, int64_t r,
@@ -98,6 +253,18 @@ static int decode_row(int kv_dtype, int d, const void *rows, const uint8_t *scal
       if ((rc = csa2o_e4m3_to_f64(p[i], &code)) != ORC_OK) return rc;
       if ((rc = csa2o_ue8m0_to_f64(sc[i / 32], &scale)) != ORC_OK) return rc;
       out[i] = code * scale; /* exact: a power-of-two scale */
+    }
+    return ORC_OK;
+  }
+  if (kv_dtype == ORC_KV_FP4) {
+    /* FP4: d/2 bytes of E2M1 codes (element 2i low nibble) and d/16 E4M3 scales */
+    const uint8_t *p = (const uint8_t *)rows + (size_t)r * (size_t)(d / 2);
+    const uint8_t *sc = scales + (size_t)r * (size_t)(d / 16);
+    for (i = 0; i < d; ++i) {
+      double code, scale;
+      csa2o_e2m1_to_f64((uint8_t)((p[i / 2] >> (4 * (i & 1))) & 15), &code);
+      if ((rc = csa2o_e4m3_to_f64(sc[i / 16], &scale)) != ORC_OK) return rc;
+      out[i] = code * scale; /* exact in double */
     }
     return ORC_OK;
   }
@@ -329,6 +496,7 @@ int csa2o_attend_query(int32_t h, int32_t d, int32_t kv_dtype, const uint16_t *q
   int rc = ORC_OK, i;
   if (h < 1 || d < 1 || win_len < 0 || n_sel < 0 || !q_bf16 || !out) return ORC_EBADARG;
   if (kv_dtype == ORC_KV_FP8 && (d % 32) != 0) return ORC_EBADARG;
+  if (kv_dtype == ORC_KV_FP4 && (d % 16) != 0) return ORC_EBADARG;
   if (win_len > 0 && !win_rows) return ORC_EBADARG;
   if (!isfinite(scale)) return ORC_ENONFINITE;
   for (j = 0; j < n_sel; ++j) {
@@ -432,6 +600,10 @@ int64_t csa2o_select_query(int32_t mode, int64_t pos, int32_t m, int64_t pool_le
 /*   pool rows / index keys start at pool_row0[b] and span pool_len[b] rows;   */
 /*   idx_q [b][h_i][d_i];  idx_w [b][h_i] (or NULL);                           */
 /*   Reindex lists cand_idx[cand_off[b] .. cand_off[b+1]) (pool-relative).     */
+/* Index keys are fp32 [rows][d_i] (idx_kdtype 0) or MXFP4 (idx_kdtype 1:     */
+/* codes [rows][d_i/2], E8M0 scales [rows][d_i/32]), decoded exactly to fp32   */
+/* before the canonical score.  KV rows are bf16, fp8 (+ UE8M0 per 32) or FP4   */
+/* (d/2 code bytes + E4M3 per 16).                                             */
 /* Queries run in parallel (OpenMP) -- they share nothing.                     */
 /* ------------------------------------------------------------------------- */
 int csa2o_decode_batch(int32_t nb, int32_t h, int32_t d, int32_t k, int32_t h_i, int32_t d_i,
@@ -441,27 +613,49 @@ int csa2o_decode_batch(int32_t nb, int32_t h, int32_t d, int32_t k, int32_t h_i,
                        const int64_t *cand_off, const int32_t *cand_idx, const uint16_t *q,
                        const void *win_rows, const uint8_t *win_scales, const void *pool_rows,
                        const uint8_t *pool_scales, const float *idx_q, const float *idx_w,
-                       const float *idx_k, const float *sink, int32_t *sel_io, float *out,
-                       float *lse) {
+                       int32_t idx_kdtype, const void *idx_k, const uint8_t *idx_k_scales,
+                       const float *sink, int32_t *sel_io, float *out, float *lse) {
   int32_t b;
   int err = ORC_OK;
-  size_t rb = (kv_dtype == ORC_KV_FP8) ? (size_t)d : 2 * (size_t)d; /* bytes per KV row */
+  /* bytes per KV row and scale bytes per row */
+  size_t rb = (kv_dtype == ORC_KV_FP8) ? (size_t)d : (kv_dtype == ORC_KV_FP4) ? (size_t)d / 2 : 2 * (size_t)d;
+  size_t sb = (kv_dtype == ORC_KV_FP8) ? (size_t)d / 32 : (kv_dtype == ORC_KV_FP4) ? (size_t)d / 16 : 0;
+  if (idx_kdtype != ORC_IDXK_F32 && idx_kdtype != ORC_IDXK_MXFP4) return ORC_EBADARG;
+  if (idx_kdtype == ORC_IDXK_MXFP4 && ((d_i % 32) != 0 || !idx_k_scales)) return ORC_EBADARG;
 #pragma omp parallel for schedule(dynamic, 1)
   for (b = 0; b < nb; ++b) {
     int rc = ORC_OK;
     int32_t *sel = sel_io + (size_t)b * (size_t)k;
     const uint8_t *wr = (const uint8_t *)win_rows + (size_t)win_row0[b] * rb;
-    const uint8_t *ws = win_scales ? win_scales + (size_t)win_row0[b] * (size_t)(d / 32) : NULL;
+    const uint8_t *ws = win_scales ? win_scales + (size_t)win_row0[b] * sb : NULL;
     const uint8_t *pr = (const uint8_t *)pool_rows + (size_t)pool_row0[b] * rb;
-    const uint8_t *ps = pool_scales ? pool_scales + (size_t)pool_row0[b] * (size_t)(d / 32) : NULL;
+    const uint8_t *ps = pool_scales ? pool_scales + (size_t)pool_row0[b] * sb : NULL;
     int32_t nsel = k;
     if (mode[b] == ORC_MODE_FULL || mode[b] == ORC_MODE_REINDEX) {
       const int32_t *cl = (mode[b] == ORC_MODE_REINDEX) ? cand_idx + cand_off[b] : NULL;
       int64_t nc = (mode[b] == ORC_MODE_REINDEX) ? cand_off[b + 1] - cand_off[b] : 0;
-      int64_t r = csa2o_select_query(mode[b], pos[b], ratio[b], pool_len[b], h_i, d_i,
-                                     idx_q + (size_t)b * (size_t)(h_i * d_i),
-                                     idx_w ? idx_w + (size_t)b * (size_t)h_i : NULL, relu,
-                                     idx_k + (size_t)pool_row0[b] * (size_t)d_i, cl, nc, k, sel, NULL);
+      const float *keys = NULL;
+      float *dec = NULL;
+      int64_t r;
+      if (idx_kdtype == ORC_IDXK_F32) {
+        keys = (const float *)idx_k + (size_t)pool_row0[b] * (size_t)d_i;
+      } else {
+        dec = (float *)malloc(sizeof(float) * (size_t)(pool_len[b] > 0 ? pool_len[b] : 1) * (size_t)d_i);
+        if (!dec) {
+          rc = ORC_ENOMEM;
+        } else {
+          rc = csa2o_dequant_mxfp4((const uint8_t *)idx_k + (size_t)pool_row0[b] * (size_t)(d_i / 2),
+                                   idx_k_scales + (size_t)pool_row0[b] * (size_t)(d_i / 32),
+                                   (int64_t)pool_len[b] * d_i, dec);
+          keys = dec;
+        }
+      }
+      r = (rc == ORC_OK)
+              ? csa2o_select_query(mode[b], pos[b], ratio[b], pool_len[b], h_i, d_i,
+                                   idx_q + (size_t)b * (size_t)(h_i * d_i),
+                                   idx_w ? idx_w + (size_t)b * (size_t)h_i : NULL, relu, keys, cl, nc, k, sel, NULL)
+              : rc;
+      free(dec);
       if (r < 0) rc = (int)r;
     } else if (mode[b] == ORC_MODE_WINDOW) {
       nsel = 0;

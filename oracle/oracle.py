@@ -18,7 +18,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liboracle.so")
 
 MODE_FULL, MODE_REINDEX, MODE_REUSE, MODE_WINDOW = 0, 1, 2, 3
-KV_BF16, KV_FP8 = 0, 1
+KV_BF16, KV_FP8, KV_FP4 = 0, 1, 2
+IDXK_F32, IDXK_MXFP4 = 0, 1
 
 _lib = None
 
@@ -37,6 +38,17 @@ def lib():
         L.csa2o_ue8m0_to_f64.argtypes = [C.c_uint8, C.POINTER(dbl)]
         for f in (L.csa2o_bf16_to_f64, L.csa2o_e4m3_to_f64, L.csa2o_ue8m0_to_f64):
             f.restype = C.c_int
+        L.csa2o_e2m1_to_f64.argtypes = [C.c_uint8, C.POINTER(dbl)]
+        L.csa2o_e2m1_to_f64.restype = C.c_int
+        L.csa2o_e2m1_encode.argtypes = [dbl]
+        L.csa2o_e2m1_encode.restype = C.c_uint8
+        L.csa2o_f32_to_e4m3.argtypes = [C.c_float, C.POINTER(C.c_uint8)]
+        L.csa2o_f32_to_e4m3.restype = C.c_int
+        for f in (L.csa2o_quant_fp4kv, L.csa2o_quant_mxfp4):
+            f.argtypes = [P, i64, P, P]
+            f.restype = C.c_int
+        L.csa2o_dequant_mxfp4.argtypes = [P, P, i64, P]
+        L.csa2o_dequant_mxfp4.restype = C.c_int
         L.csa2o_n_valid.argtypes = [i64, i32, i32, i64]
         L.csa2o_n_valid.restype = i64
         L.csa2o_window_range.argtypes = [i64, i32, i64, C.POINTER(i64), C.POINTER(i64)]
@@ -53,7 +65,7 @@ def lib():
         L.csa2o_select_query.restype = i64
         L.csa2o_decode_batch.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, dbl,
                                          P, P, P, P, P, P, P, P, P,
-                                         P, P, P, P, P, P, P, P, P, P, P, P]
+                                         P, P, P, P, P, P, P, i32, P, P, P, P, P, P]
         L.csa2o_decode_batch.restype = C.c_int
         _lib = L
     return _lib
@@ -95,6 +107,53 @@ def ue8m0_to_f64(code):
     out = C.c_double()
     _check(lib().csa2o_ue8m0_to_f64(int(code), C.byref(out)))
     return out.value
+
+
+def e2m1_to_f64(code):
+    out = C.c_double()
+    _check(lib().csa2o_e2m1_to_f64(int(code) & 15, C.byref(out)))
+    return out.value
+
+
+def e2m1_encode(v):
+    """Nearest E2M1 code (4 bits) to v, ties to even, saturating at 6."""
+    return int(lib().csa2o_e2m1_encode(float(v)))
+
+
+def f32_to_e4m3(v):
+    out = C.c_uint8()
+    _check(lib().csa2o_f32_to_e4m3(float(np.float32(v)), C.byref(out)))
+    return int(out.value)
+
+
+def quant_fp4kv(x):
+    """FP4 main-KV quantizer over the last axis (a multiple of 16): returns
+    (codes uint8 [..., n/2], E4M3 scales uint8 [..., n/16])."""
+    x = np.ascontiguousarray(x, np.float32)
+    n = x.shape[-1]
+    codes = np.empty(x.shape[:-1] + (n // 2,), np.uint8)
+    scales = np.empty(x.shape[:-1] + (n // 16,), np.uint8)
+    _check(lib().csa2o_quant_fp4kv(_ptr(x), x.size, _ptr(codes), _ptr(scales)))
+    return codes, scales
+
+
+def quant_mxfp4(x):
+    """MXFP4 quantizer over the last axis (a multiple of 32): returns
+    (codes uint8 [..., n/2], E8M0 scales uint8 [..., n/32])."""
+    x = np.ascontiguousarray(x, np.float32)
+    n = x.shape[-1]
+    codes = np.empty(x.shape[:-1] + (n // 2,), np.uint8)
+    scales = np.empty(x.shape[:-1] + (n // 32,), np.uint8)
+    _check(lib().csa2o_quant_mxfp4(_ptr(x), x.size, _ptr(codes), _ptr(scales)))
+    return codes, scales
+
+
+def dequant_mxfp4(codes, scales):
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    out = np.empty(codes.shape[:-1] + (codes.shape[-1] * 2,), np.float32)
+    _check(lib().csa2o_dequant_mxfp4(_ptr(codes), _ptr(scales), out.size, _ptr(out)))
+    return out
 
 
 # --- O1 / window ------------------------------------------------------------
@@ -160,14 +219,16 @@ def attend_query(q_bf16, win_rows, pool_rows, sel, kv_dtype=KV_BF16, win_scales=
     """One query's two-source attention.
 
     q_bf16 [H, D] uint16; win_rows [win_len, D] (uint16 bf16, or uint8 e4m3 with
-    win_scales [win_len, D/32] uint8); pool_rows likewise; sel int32 list of
+    win_scales [win_len, D/32] uint8, or uint8 [win_len, D/2] FP4 codes with
+    win_scales [win_len, D/16] E4M3); pool_rows likewise; sel int32 list of
     pool rows (-1 skipped).  Returns (out f32 [H, D], lse f32 [H]).
     """
     q = _c(q_bf16, np.uint16)
     h, d = q.shape
     rdt = np.uint16 if kv_dtype == KV_BF16 else np.uint8
-    win_rows = np.zeros((0, d), rdt) if win_rows is None else _c(win_rows, rdt).reshape(-1, d)
-    pool_rows = np.zeros((0, d), rdt) if pool_rows is None else _c(pool_rows, rdt).reshape(-1, d)
+    w = d // 2 if kv_dtype == KV_FP4 else d
+    win_rows = np.zeros((0, w), rdt) if win_rows is None else _c(win_rows, rdt).reshape(-1, w)
+    pool_rows = np.zeros((0, w), rdt) if pool_rows is None else _c(pool_rows, rdt).reshape(-1, w)
     win_scales = _c(win_scales, np.uint8)
     pool_scales = _c(pool_scales, np.uint8)
     sel = np.zeros(0, np.int32) if sel is None else _c(sel, np.int32)
@@ -229,7 +290,8 @@ def decode_batch(inp, queries=None, sink=None, scale=1.0):
         n, H, D, K, HI, DI, int(d["index_relu"]), kvd, float(scale),
         _ptr(pos), _ptr(mode), _ptr(ratio), _ptr(win_row0), _ptr(win_len), _ptr(pool_row0), _ptr(pool_len),
         _ptr(cand_off), _ptr(cand_idx), _ptr(q), _ptr(inp["win_kv"]), _ptr(inp.get("win_scale")),
-        _ptr(inp["comp_kv"]), _ptr(inp.get("comp_scale")), _ptr(idx_q), _ptr(idx_w), _ptr(inp["idx_k"]),
+        _ptr(inp["comp_kv"]), _ptr(inp.get("comp_scale")), _ptr(idx_q), _ptr(idx_w),
+        int(d.get("index_key_dtype", IDXK_F32)), _ptr(inp["idx_k"]), _ptr(inp.get("idx_k_scale")),
         _ptr(sink), _ptr(sel), _ptr(out), _ptr(lse))
     _check(rc)
     return sel, out, lse

@@ -393,3 +393,161 @@ def test_reachability_boundary_is_exclusive():
     assert list(sel) == [1, 2]
     sel = O.select_query(O.MODE_FULL, 11, 4, 8, q, keys, 2)
     assert list(sel) == [1, 2]
+
+
+# ---------------------------------------------------------------------------
+# FP4 storage formats ([RN] 3f C4; PocketLLM "The CSA2 attention layers" and
+# its FP4 quantizer notes)
+# ---------------------------------------------------------------------------
+
+def _grid():
+    return gold("fp4_example.json")["grid"]
+
+
+def _nearest_code(v):
+    """Brute force: the E2M1 code whose value is nearest v, ties to the code
+    with an even mantissa bit, magnitudes beyond 6 clamp to 6, zero as +0."""
+    g = _grid()
+    a = min(abs(v), 6.0)
+    best = min(range(8), key=lambda c: (abs(a - g[c]), c & 1))
+    return best | 8 if (v < 0 and best != 0) else best
+
+
+def test_e2m1_grid_is_the_pages_grid():
+    g = _grid()
+    for c in range(16):
+        want = g[c & 7] * (-1.0 if c & 8 else 1.0)
+        assert O.e2m1_to_f64(c) == want
+
+
+def test_fp4_worked_example():
+    ex = gold("fp4_example.json")
+    s = ex["s"]
+    for x, r, code, xh in zip(ex["x"], ex["x_over_s"], ex["codes"], ex["x_hat"]):
+        assert abs(x / s - r) < 1e-12
+        c = O.e2m1_encode(x / s)
+        assert O.e2m1_to_f64(c) == code
+        assert abs(s * O.e2m1_to_f64(c) - xh) < 1e-12
+    # storage: 16 four-bit codes and one 8-bit scale per 16 numbers
+    assert (16 * 4 + 8) / 16 == ex["bits_per_number"]
+
+
+def test_e2m1_encode_brute_force_with_ties():
+    g = _grid()
+    vals = [0.0, -0.0, 6.5, -7.0, 100.0]
+    vals += [s * (g[i] + g[i + 1]) / 2 for i in range(7) for s in (1, -1)]  # every midpoint
+    vals += [s * x for x in g for s in (1, -1)]
+    rng = np.random.default_rng(5)
+    vals += list(rng.uniform(-8, 8, 2000))
+    for v in vals:
+        assert O.e2m1_encode(v) == _nearest_code(v), v
+
+
+def test_e4m3_encode_matches_torch():
+    rng = np.random.default_rng(6)
+    x = np.concatenate([rng.uniform(-448, 448, 4000), rng.uniform(-0.02, 0.02, 2000),
+                        np.ldexp(rng.integers(0, 16, 200).astype(np.float64), -10),  # around the subnormals
+                        [0.0, 448.0, -448.0, 2.0 ** -9, 2.0 ** -10, 3 * 2.0 ** -11]]).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([O.f32_to_e4m3(v) for v in x], np.uint8)
+    assert np.array_equal(got, want)
+    assert O.f32_to_e4m3(1000.0) == 0x7E and O.f32_to_e4m3(-1000.0) == 0xFE  # saturates
+
+
+def _e4m3_value(byte):
+    return float(torch.tensor([byte], dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64))
+
+
+def test_fp4kv_quantizer_follows_the_rule():
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal((40, 64)) * rng.uniform(0.01, 30, (40, 1))).astype(np.float32)
+    x[3, 16:32] = 0.0                     # an all-zero block
+    x[5, :16] = np.float32(1e-4)          # below the amax floor
+    codes, scales = O.quant_fp4kv(x)
+    assert codes.shape == (40, 32) and scales.shape == (40, 4)
+    for r in range(40):
+        for b in range(4):
+            blk = x[r, 16 * b:16 * b + 16]
+            amax = max(float(np.abs(blk).max()), 6 * 2.0 ** -9)
+            s_byte = int(torch.tensor(np.float32(np.float32(amax) / np.float32(6.0))).to(torch.float8_e4m3fn)
+                         .view(torch.uint8))
+            assert scales[r, b] == s_byte
+            s = np.float32(_e4m3_value(s_byte))
+            for i in range(16):
+                nib = (codes[r, 8 * b + i // 2] >> (4 * (i % 2))) & 15   # element 2i in the low nibble
+                assert nib == _nearest_code(float(np.float32(blk[i]) / s)), (r, b, i)
+    assert scales[3, 1] == 0x01 and not codes[3, 8:16].any()   # zero block: scale 2^-9, codes 0
+
+
+def test_fp4kv_round_trip_error_bound():
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((64, 512)).astype(np.float32)
+    codes, scales = O.quant_fp4kv(x)
+    lut = np.array(_grid() + [-v for v in _grid()])
+    nib = np.stack([codes & 15, codes >> 4], -1).reshape(64, 512)
+    sc = np.array([_e4m3_value(b) for b in range(256) if b not in (0x7F, 0xFF)] + [0, 0])
+    s = np.repeat(np.array([[_e4m3_value(int(b)) for b in row] for row in scales]), 16, axis=1)
+    xh = lut[nib] * s
+    # no block saturates here (e4m3 rounding of amax/6 is far from 6/5.5), so the
+    # error is at most half the largest grid gap (2 between 4 and 6) times s
+    assert np.all(np.abs(xh - x) <= s * 1.0 + 1e-12)
+    assert sc.size  # lookup built from torch's e4m3, independent of the oracle
+
+
+def test_mxfp4_quantizer_follows_the_rule():
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal((30, 128)) * rng.uniform(1e-3, 50, (30, 1))).astype(np.float32)
+    x[2, 32:64] = 0.0
+    codes, scales = O.quant_mxfp4(x)
+    assert codes.shape == (30, 64) and scales.shape == (30, 4)
+    for r in range(30):
+        for b in range(4):
+            blk = x[r, 32 * b:32 * b + 32]
+            y = np.float32(np.abs(blk).max()) / np.float32(6.0)
+            e = -126 if y == 0 else int(np.rint(np.log2(np.float64(y))))
+            e = min(max(e, -126), 127)
+            assert scales[r, b] == e + 127
+            for i in range(32):
+                nib = (codes[r, 16 * b + i // 2] >> (4 * (i % 2))) & 15
+                assert nib == _nearest_code(float(blk[i]) * 2.0 ** -e), (r, b, i)
+    dec = O.dequant_mxfp4(codes, scales)
+    lut = np.array(_grid() + [-v for v in _grid()])
+    nib = np.stack([codes & 15, codes >> 4], -1).reshape(30, 128)
+    assert np.array_equal(dec, (lut[nib] * np.exp2(np.repeat(scales.astype(np.float64) - 127, 32, 1)))
+                          .astype(np.float32))
+
+
+def test_fp4_rows_equal_their_exact_bf16_images():
+    """FP4 codes times E4M3 scales are exact in bf16; the oracle's FP4 path must
+    equal its bf16 path on those images (decoded here from the page's grid and
+    torch's e4m3)."""
+    H, D = 4, 64
+    vals = synth.normal_f32(21, 97, (20, D))
+    codes, scales = O.quant_fp4kv(vals)
+    lut = np.array(_grid() + [-v for v in _grid()])
+    nib = np.stack([codes & 15, codes >> 4], -1).reshape(20, D)
+    s = np.repeat(np.array([[_e4m3_value(int(b)) for b in row] for row in scales]), 16, axis=1)
+    dec = torch.from_numpy(lut[nib] * s)
+    img = dec.to(torch.bfloat16)
+    assert (img.to(torch.float64) == dec).all()
+    img = img.view(torch.int16).numpy().view(np.uint16)
+    q = synth.normal_bf16(21, 96, (H, D), scale=0.125)
+    sel = np.array([12, 3, -1, 19], np.int32)
+    a = O.attend_query(q, codes[:8], codes, sel, kv_dtype=O.KV_FP4, win_scales=scales[:8], pool_scales=scales)
+    b = O.attend_query(q, img[:8], img, sel)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_mxfp4_index_keys_equal_their_decoded_fp32_keys():
+    """A batch whose index keys are MXFP4 selects and attends exactly as the same
+    batch with those keys decoded (page grid x 2^(e-127)) to fp32."""
+    inp = synth.decode_batch(22, [3000, 1500], [synth.MODE_FULL] * 2, [4, 4],
+                             dims=synth.default_dims(index_topk=64))
+    codes, scales = O.quant_mxfp4(inp["idx_k"])
+    lut = np.array(_grid() + [-v for v in _grid()])
+    nib = np.stack([codes & 15, codes >> 4], -1).reshape(inp["idx_k"].shape)
+    dec = (lut[nib] * np.exp2(np.repeat(scales.astype(np.float64) - 127, 32, 1))).astype(np.float32)
+    mx = dict(inp, idx_k=codes, idx_k_scale=scales, dims=dict(inp["dims"], index_key_dtype=O.IDXK_MXFP4))
+    f32 = dict(inp, idx_k=dec)
+    a, b = O.decode_batch(mx), O.decode_batch(f32)
+    assert all(np.array_equal(u, v) for u, v in zip(a, b))
