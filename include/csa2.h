@@ -30,7 +30,10 @@
  * Attention multiplies bf16 operands on the matrix cores with fp32
  * accumulation and an fp32 online softmax; the probabilities are rounded to
  * bf16 for the second product.  FP8 KV (E4M3, one UE8M0 scale per 32 values)
- * is widened to bf16 exactly before use.
+ * and FP4 KV (E2M1, one E4M3 scale per 16 values: Reading Notes, 3f C4) are
+ * widened to bf16 exactly before use; MXFP4 index keys (E2M1, one E8M0 scale
+ * per 32: PocketLLM page, "The CSA2 attention layers") are widened to fp32
+ * exactly before the fixed-order score.
  *
  * Conventions common to every entry point:
  *   - Every tensor pointer is a DEVICE pointer owned by the caller; nothing is
@@ -51,9 +54,15 @@
  * Layouts (row-major, rows contiguous):
  *   q        bf16  [B][64][512]
  *   idx_q    f32   [B][H_I][128];  idx_w f32 [B][H_I] or NULL (unit weights)
- *   idx_k    f32   [rows][128]     (same row numbering as comp_kv)
+ *   idx_k    f32   [rows][128]     (same row numbering as comp_kv), or MXFP4:
+ *            codes uint8 [rows][64] with idx_k_scale uint8 [rows][4]
+ *            (E8M0, value = code * 2^(s-127), one scale per 32 values)
  *   win_kv / comp_kv: bf16 [rows][512], or fp8 codes uint8 [rows][512] with
- *            scales uint8 [rows][16] (UE8M0, value = code * 2^(s-127))
+ *            scales uint8 [rows][16] (UE8M0, value = code * 2^(s-127)), or FP4
+ *            codes uint8 [rows][256] with scales uint8 [rows][32] (E4M3,
+ *            value = code * scale, one scale per 16 values)
+ *   FP4 codes: E2M1 (0, +-0.5, +-1, +-1.5, +-2, +-3, +-4, +-6), two per byte,
+ *            element 2i in the low nibble.
  *   topk_idx int32 [B][K]: pool-relative row numbers, ascending, -1 padded
  *   out      f32   [B][64][512];   lse f32 [B][64] (natural log) or NULL
  */
@@ -68,7 +77,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 1
+#define CSA2_ABI_VERSION 2
 
 typedef enum {
   CSA2_OK = 0,
@@ -78,7 +87,16 @@ typedef enum {
   CSA2_ERR_HIP = 4          /* a kernel launch failed; see csa2_last_hip_error */
 } csa2_status;
 
-typedef enum { CSA2_KV_BF16 = 0, CSA2_KV_FP8_E4M3_UE8M0_32 = 1 } csa2_kv_dtype;
+typedef enum {
+  CSA2_KV_BF16 = 0,
+  CSA2_KV_FP8_E4M3_UE8M0_32 = 1, /* sliding-window format of the pages' model */
+  CSA2_KV_FP4_E2M1_E4M3_16 = 2   /* main (compressed) KV format, Reading Notes 3f C4 */
+} csa2_kv_dtype;
+
+typedef enum {
+  CSA2_IDXK_F32 = 0,  /* fp32 keys */
+  CSA2_IDXK_MXFP4 = 1 /* E2M1 codes + E8M0 scale per 32 */
+} csa2_index_key_dtype;
 
 typedef enum {
   CSA2_MODE_FULL = 0,    /* score every reachable compressed entry, select top-K */
@@ -97,6 +115,7 @@ typedef struct csa2_dims {
   int32_t index_relu;  /* 0: f = identity, 1: f = ReLU */
   int32_t kv_dtype;    /* csa2_kv_dtype, for both KV sources */
   float softmax_scale; /* multiplies q.k before the softmax (1 when folded into q) */
+  int32_t index_key_dtype; /* csa2_index_key_dtype of idx_k */
 } csa2_dims;
 
 /* Per-query descriptors of a decode batch: DEVICE arrays of length B (cand_off: B+1). */
@@ -146,10 +165,13 @@ csa2_status csa2_workspace_size(const csa2_dims *dims, int32_t B, int32_t max_ca
  * n_cand = min(n_valid, max_candidates) (FULL: candidate j is pool row j) or
  * min(list length, max_candidates) (REINDEX: candidate j is the j-th list row).
  * A listed row outside [0, n_valid) scores -inf.  Other slots are not written.
- * Requires score_stride >= max_candidates. */
+ * Requires score_stride >= max_candidates.  idx_k is f32 keys, or MXFP4 codes
+ * with their scale plane idx_k_scale (dims->index_key_dtype; idx_k_scale is
+ * ignored for f32 keys). */
 csa2_status csa2_index_scores(const csa2_dims *dims, int32_t B, const csa2_batch *batch,
-                              const float *idx_q, const float *idx_w, const float *idx_k,
-                              float *scores, int64_t score_stride, hipStream_t stream);
+                              const float *idx_q, const float *idx_w, const void *idx_k,
+                              const uint8_t *idx_k_scale, float *scores, int64_t score_stride,
+                              hipStream_t stream);
 
 /* Step 3 for every FULL / REINDEX query: from the scores of csa2_index_scores,
  * write the first min(K, eligible) candidates under (score descending, row
@@ -164,8 +186,8 @@ csa2_status csa2_topk(const csa2_dims *dims, int32_t B, const csa2_batch *batch,
  * per occurrence; rows outside [0, pool_len) skipped); WINDOW queries attend
  * their window rows only (topk_idx may be NULL if every query is WINDOW).
  * win_kv may be NULL (no query then has window rows) and comp_kv may be NULL
- * (no query then has compressed rows); fp8 scale planes are required exactly
- * when their KV source is given.
+ * (no query then has compressed rows); the scale planes of fp8 / FP4 KV are
+ * required exactly when their KV source is given.
  * sink: f32 [64] or NULL.
  * Batches of B <= 64 queries run four workgroups of 16 heads per query and
  * ignore the workspace.  Larger batches run one workgroup of all 64 heads per
@@ -182,8 +204,8 @@ csa2_status csa2_attend(const csa2_dims *dims, int32_t B, const csa2_batch *batc
  * modes: scores + top-K for FULL / REINDEX queries (their topk_idx rows are
  * written), then attention for all (REUSE rows of topk_idx are read). */
 csa2_status csa2_decode(const csa2_dims *dims, int32_t B, const csa2_batch *batch, const void *q,
-                        const float *idx_q, const float *idx_w, const float *idx_k,
-                        const void *win_kv, const uint8_t *win_scale, const void *comp_kv,
+                        const float *idx_q, const float *idx_w, const void *idx_k,
+                        const uint8_t *idx_k_scale, const void *win_kv, const uint8_t *win_scale, const void *comp_kv,
                         const uint8_t *comp_scale, int32_t *topk_idx, const float *sink,
                         float *out, float *lse, void *workspace, size_t workspace_bytes,
                         hipStream_t stream);
@@ -197,11 +219,31 @@ csa2_status csa2_prefill_workspace_size(const csa2_dims *dims, const csa2_prefil
  * as in csa2_prefill_desc; reachability, scores and top-K as for decode; q,
  * idx_q, topk_idx, out and lse are indexed by t. */
 csa2_status csa2_prefill(const csa2_dims *dims, const csa2_prefill_desc *desc, const void *q,
-                         const float *idx_q, const float *idx_w, const float *idx_k,
-                         const void *win_kv, const uint8_t *win_scale, const void *comp_kv,
+                         const float *idx_q, const float *idx_w, const void *idx_k,
+                         const uint8_t *idx_k_scale, const void *win_kv, const uint8_t *win_scale, const void *comp_kv,
                          const uint8_t *comp_scale, int32_t *topk_idx, const float *sink,
                          float *out, float *lse, void *workspace, size_t workspace_bytes,
                          hipStream_t stream);
+
+/* The cache writer's quantizers (Reading Notes, 3f C4; PocketLLM page, "The
+ * CSA2 attention layers" and its FP4 quantizer notes).  Both read n_rows rows
+ * of d fp32 values (device) and write codes uint8 [n_rows][d/2] (element 2i in
+ * the low nibble) and scales.  Codes round to the nearest E2M1 value, ties to
+ * the even code, saturating at 6; a zero is stored as +0.
+ *
+ * FP4 main KV, one E4M3 scale per 16 values (d a multiple of 16; scales
+ * [n_rows][d/16]): amax = max |x| over the block, at least 6 * 2^-9; scale =
+ * e4m3(amax / 6) (the quotient in fp32, nearest-even, saturating at 448);
+ * code = E2M1(x / scale), the quotient in fp32. */
+csa2_status csa2_quantize_fp4_kv(int64_t n_rows, int32_t d, const float *src, uint8_t *codes,
+                                 uint8_t *scales, hipStream_t stream);
+
+/* MXFP4 index keys, one E8M0 scale per 32 values (d a multiple of 32; scales
+ * [n_rows][d/32]): scale = 2^e with e = round(log2(amax / 6)) (amax / 6 in
+ * fp32; e clamped to -126 .. 127, an all-zero block gets -126), stored as
+ * e + 127; code = E2M1(x / 2^e). */
+csa2_status csa2_quantize_mxfp4(int64_t n_rows, int32_t d, const float *src, uint8_t *codes,
+                                uint8_t *scales, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(PKG, "libcsa2.so")
 
 CSA2_OK, CSA2_ERR_INVALID_ARG, CSA2_ERR_UNSUPPORTED, CSA2_ERR_WORKSPACE, CSA2_ERR_HIP = range(5)
 MODE_FULL, MODE_REINDEX, MODE_REUSE, MODE_WINDOW = range(4)
-KV_BF16, KV_FP8 = 0, 1
+KV_BF16, KV_FP8, KV_FP4 = 0, 1, 2
+IDXK_F32, IDXK_MXFP4 = 0, 1
 
 
 class Csa2Error(RuntimeError):
@@ -28,11 +29,12 @@ class Csa2Error(RuntimeError):
 class Dims(C.Structure):
     _fields_ = [("n_heads", C.c_int32), ("head_dim", C.c_int32), ("window", C.c_int32),
                 ("index_topk", C.c_int32), ("index_dim", C.c_int32), ("index_heads", C.c_int32),
-                ("index_relu", C.c_int32), ("kv_dtype", C.c_int32), ("softmax_scale", C.c_float)]
+                ("index_relu", C.c_int32), ("kv_dtype", C.c_int32), ("softmax_scale", C.c_float),
+                ("index_key_dtype", C.c_int32)]
 
     @classmethod
     def from_dict(cls, d):
-        return cls(**{k: d[k] for k, _ in cls._fields_})
+        return cls(**{k: d.get(k, 0) for k, _ in cls._fields_})
 
 
 class Batch(C.Structure):
@@ -51,7 +53,7 @@ class PrefillDesc(C.Structure):
 _lib = None
 EXPORTS = ["csa2_abi_version", "csa2_status_str", "csa2_last_hip_error", "csa2_workspace_size",
            "csa2_index_scores", "csa2_topk", "csa2_attend", "csa2_decode", "csa2_prefill_workspace_size",
-           "csa2_prefill"]
+           "csa2_prefill", "csa2_quantize_fp4_kv", "csa2_quantize_mxfp4"]
 
 
 def lib():
@@ -66,12 +68,14 @@ def lib():
         L.csa2_status_str.restype = C.c_char_p
         L.csa2_last_hip_error.restype = i32
         L.csa2_workspace_size.argtypes = [P, i32, i32, C.POINTER(sz)]
-        L.csa2_index_scores.argtypes = [P, i32, P, P, P, P, P, i64, P]
+        L.csa2_index_scores.argtypes = [P, i32, P, P, P, P, P, P, i64, P]
         L.csa2_topk.argtypes = [P, i32, P, P, i64, P, P]
         L.csa2_attend.argtypes = [P, i32, P, P, P, P, P, P, P, P, P, P, P, sz, P]
-        L.csa2_decode.argtypes = [P, i32, P, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]
+        L.csa2_decode.argtypes = [P, i32, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]
         L.csa2_prefill_workspace_size.argtypes = [P, P, C.POINTER(sz)]
-        L.csa2_prefill.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]
+        L.csa2_prefill.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]
+        L.csa2_quantize_fp4_kv.argtypes = [i64, i32, P, P, P, P]
+        L.csa2_quantize_mxfp4.argtypes = [i64, i32, P, P, P, P]
         for name in EXPORTS[3:]:
             getattr(L, name).restype = C.c_int
         _lib = L
@@ -118,9 +122,9 @@ def csa2_workspace_size(dims, B, max_candidates):
     return out.value
 
 
-def csa2_index_scores(dims, B, batch, idx_q, idx_w, idx_k, scores, score_stride, stream=None):
+def csa2_index_scores(dims, B, batch, idx_q, idx_w, idx_k, scores, score_stride, stream=None, idx_k_scale=None):
     _ok(lib().csa2_index_scores(C.byref(dims), B, C.byref(batch), _p(idx_q), _p(idx_w), _p(idx_k),
-                                _p(scores), score_stride, _stream(stream)), "csa2_index_scores")
+                                _p(idx_k_scale), _p(scores), score_stride, _stream(stream)), "csa2_index_scores")
 
 
 def csa2_topk(dims, B, batch, scores, score_stride, topk_idx, stream=None):
@@ -136,8 +140,9 @@ def csa2_attend(dims, B, batch, q, win_kv, win_scale, comp_kv, comp_scale, topk_
 
 
 def csa2_decode(dims, B, batch, q, idx_q, idx_w, idx_k, win_kv, win_scale, comp_kv, comp_scale, topk_idx, sink,
-                out, lse, workspace, workspace_bytes, stream=None):
-    _ok(lib().csa2_decode(C.byref(dims), B, C.byref(batch), _p(q), _p(idx_q), _p(idx_w), _p(idx_k), _p(win_kv),
+                out, lse, workspace, workspace_bytes, stream=None, idx_k_scale=None):
+    _ok(lib().csa2_decode(C.byref(dims), B, C.byref(batch), _p(q), _p(idx_q), _p(idx_w), _p(idx_k),
+                          _p(idx_k_scale), _p(win_kv),
                           _p(win_scale), _p(comp_kv), _p(comp_scale), _p(topk_idx), _p(sink), _p(out), _p(lse),
                           _p(workspace), workspace_bytes, _stream(stream)), "csa2_decode")
 
@@ -150,10 +155,21 @@ def csa2_prefill_workspace_size(dims, desc):
 
 
 def csa2_prefill(dims, desc, q, idx_q, idx_w, idx_k, win_kv, win_scale, comp_kv, comp_scale, topk_idx, sink,
-                 out, lse, workspace, workspace_bytes, stream=None):
-    _ok(lib().csa2_prefill(C.byref(dims), C.byref(desc), _p(q), _p(idx_q), _p(idx_w), _p(idx_k), _p(win_kv),
+                 out, lse, workspace, workspace_bytes, stream=None, idx_k_scale=None):
+    _ok(lib().csa2_prefill(C.byref(dims), C.byref(desc), _p(q), _p(idx_q), _p(idx_w), _p(idx_k),
+                           _p(idx_k_scale), _p(win_kv),
                            _p(win_scale), _p(comp_kv), _p(comp_scale), _p(topk_idx), _p(sink), _p(out), _p(lse),
                            _p(workspace), workspace_bytes, _stream(stream)), "csa2_prefill")
+
+
+def csa2_quantize_fp4_kv(n_rows, d, src, codes, scales, stream=None):
+    _ok(lib().csa2_quantize_fp4_kv(n_rows, d, _p(src), _p(codes), _p(scales), _stream(stream)),
+        "csa2_quantize_fp4_kv")
+
+
+def csa2_quantize_mxfp4(n_rows, d, src, codes, scales, stream=None):
+    _ok(lib().csa2_quantize_mxfp4(n_rows, d, _p(src), _p(codes), _p(scales), _stream(stream)),
+        "csa2_quantize_mxfp4")
 
 
 # ---- device-resident workloads (torch used for memory only) -------------------
@@ -183,7 +199,7 @@ class DecodeWorkload:
         self.cand_off, self.cand_idx = d("cand_off"), d("cand_idx")
         self.q, self.win_kv, self.win_scale = d("q"), d("win_kv"), d("win_scale")
         self.comp_kv, self.comp_scale = d("comp_kv"), d("comp_scale")
-        self.idx_q, self.idx_w, self.idx_k = d("idx_q"), d("idx_w"), d("idx_k")
+        self.idx_q, self.idx_w, self.idx_k, self.idx_k_scale = d("idx_q"), d("idx_w"), d("idx_k"), d("idx_k_scale")
         self.sink = None if sink is None else _dev(np.asarray(sink, np.float32), device)
         K, H, D = inp["dims"]["index_topk"], inp["dims"]["n_heads"], inp["dims"]["head_dim"]
         if inp.get("cand_off") is not None:
@@ -204,7 +220,7 @@ class DecodeWorkload:
     def decode(self, stream=None):
         csa2_decode(self.dims, self.B, self.batch, self.q, self.idx_q, self.idx_w, self.idx_k, self.win_kv,
                     self.win_scale, self.comp_kv, self.comp_scale, self.topk, self.sink, self.out, self.lse,
-                    self.ws, self.ws_bytes, stream)
+                    self.ws, self.ws_bytes, stream, idx_k_scale=self.idx_k_scale)
 
 
 class PrefillWorkload:
@@ -218,7 +234,7 @@ class PrefillWorkload:
         d = lambda k: _dev(pf.get(k), device)  # noqa: E731
         self.q, self.win_kv, self.win_scale = d("q"), d("win_kv"), d("win_scale")
         self.comp_kv, self.comp_scale = d("comp_kv"), d("comp_scale")
-        self.idx_q, self.idx_w, self.idx_k = d("idx_q"), d("idx_w"), d("idx_k")
+        self.idx_q, self.idx_w, self.idx_k, self.idx_k_scale = d("idx_q"), d("idx_w"), d("idx_k"), d("idx_k_scale")
         self.cand_off, self.cand_idx = d("cand_off"), d("cand_idx")
         self.sink = None if sink is None else _dev(np.asarray(sink, np.float32), device)
         K, H, D = pf["dims"]["index_topk"], pf["dims"]["n_heads"], pf["dims"]["head_dim"]
@@ -237,4 +253,4 @@ class PrefillWorkload:
     def prefill(self, stream=None):
         csa2_prefill(self.dims, self.desc, self.q, self.idx_q, self.idx_w, self.idx_k, self.win_kv, self.win_scale,
                      self.comp_kv, self.comp_scale, self.topk, self.sink, self.out, self.lse, self.ws, self.ws_bytes,
-                     stream)
+                     stream, idx_k_scale=self.idx_k_scale)

@@ -24,8 +24,9 @@
 // Rows are XOR-swizzled in 16-byte units so the row reads of the first product
 // and the transposed reads of the second both spread over all LDS banks.
 //
-// FP8 rows (E4M3 with one UE8M0 scale per 32 values) are widened to bf16 while
-// staging, exactly (each product has at most 4 significant bits).
+// FP8 rows (E4M3 with one UE8M0 scale per 32 values) and FP4 rows (E2M1 with
+// one E4M3 scale per 16 values) are widened to bf16 while staging, exactly
+// (each product has at most 4 and 6 significant bits).
 #include "csa2_internal.h"
 
 namespace csa2 {
@@ -246,7 +247,8 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
   // 1 KiB bf16 row; rows past the last entry repeat a real row (probability 0).
   struct Stage {
     uint4 v[KV == CSA2_KV_BF16 ? kPieces : 1];
-    uint2 code[KV == CSA2_KV_BF16 ? 1 : kPieces];
+    uint2 code[KV == CSA2_KV_FP8_E4M3_UE8M0_32 ? kPieces : 1];
+    uint32_t c4[KV == CSA2_KV_FP4_E2M1_E4M3_16 ? kPieces : 1];
     uint32_t sc[KV == CSA2_KV_BF16 ? 1 : kPieces];
   };
   auto fetch = [&](int c, Stage& st) {
@@ -261,9 +263,12 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
       const int64_t row = pool ? (-ev - 1) : ev;
       if constexpr (KV == CSA2_KV_BF16) {
         st.v[it] = *reinterpret_cast<const uint4*>((pool ? a.comp_kv : a.win_kv) + row * kRowBytes + u * 16);
-      } else {
+      } else if constexpr (KV == CSA2_KV_FP8_E4M3_UE8M0_32) {
         st.code[it] = *reinterpret_cast<const uint2*>((pool ? a.comp_kv : a.win_kv) + row * kDim + u * 8);
         st.sc[it] = (pool ? a.comp_scale : a.win_scale)[row * (kDim / kScaleBlock) + (u >> 2)];
+      } else {  // FP4: 8 codes (4 bytes) and the E4M3 scale of their 16-value block
+        st.c4[it] = *reinterpret_cast<const uint32_t*>((pool ? a.comp_kv : a.win_kv) + row * (kDim / 2) + u * 4);
+        st.sc[it] = (pool ? a.comp_scale : a.win_scale)[row * (kDim / 16) + (u >> 1)];
       }
     }
   };
@@ -275,8 +280,10 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
       uint4 v;
       if constexpr (KV == CSA2_KV_BF16) {
         v = st.v[it];
-      } else {
+      } else if constexpr (KV == CSA2_KV_FP8_E4M3_UE8M0_32) {
         v = fp8x8_to_bf16x8(st.code[it], st.sc[it]);
+      } else {
+        v = fp4x8_e4m3_to_bf16x8(st.c4[it], st.sc[it]);
       }
       *reinterpret_cast<uint4*>(base + lds_off(p >> 6, (p & 63) * 16)) = v;
     }
@@ -419,8 +426,10 @@ hipError_t launch_attend(const csa2_dims& d, int32_t B, const csa2_batch& bt, co
   a.scale_log2 = d.softmax_scale * kLog2e;
   if (d.kv_dtype == CSA2_KV_BF16)
     hipLaunchKernelGGL((attend_kernel<CSA2_KV_BF16>), dim3(B * n_split), dim3(kThreads), 0, s, a);
-  else
+  else if (d.kv_dtype == CSA2_KV_FP8_E4M3_UE8M0_32)
     hipLaunchKernelGGL((attend_kernel<CSA2_KV_FP8_E4M3_UE8M0_32>), dim3(B * n_split), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((attend_kernel<CSA2_KV_FP4_E2M1_E4M3_16>), dim3(B * n_split), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_split == 1) return e;
   hipLaunchKernelGGL(attend_combine, dim3(B * kHeads), dim3(128), 0, s, n_split, a.part_o, a.part_ml, sink,

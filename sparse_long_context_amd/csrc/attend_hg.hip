@@ -23,8 +23,13 @@
 // end the four waves' (max, sum, O) are merged with log-sum-exp weights
 // through LDS and the workgroup writes its 16 heads of the final output.
 //
-// FP8 rows (E4M3 with one UE8M0 scale per 32 values) are widened exactly to
-// bf16 before the first product (each value has at most 4 significant bits).
+// FP8 rows (E4M3 with one UE8M0 scale per 32 values) and FP4 rows (E2M1 with
+// one E4M3 scale per 16 values, Reading Notes 3f C4) are widened exactly to
+// bf16 before the first product (at most 4 and 6 significant bits).  FP4 rows
+// are loaded 32 dims (16 bytes) per lane at a time, so k-step s = 4a + b of
+// lane group g covers dims 128a + 32g + 8b .. +7 instead of 32s + 8g .. +7;
+// q is read in the same order, and each piece still lands in its natural LDS
+// place for the second product.
 #include "csa2_internal.h"
 
 namespace csa2 {
@@ -102,6 +107,11 @@ struct Rows<CSA2_KV_FP8_E4M3_UE8M0_32> {
   uint2 code[2][16];
   uint4 sc[2];  // the row's 16 scale bytes, one per 32 dims = one per k-step
 };
+template <>
+struct Rows<CSA2_KV_FP4_E2M1_E4M3_16> {
+  uint4 code[2][4];  // [tile][a]: codes of dims 128a + 32g .. +31
+  uint32_t sw[2][4]; // [tile][a]: scale bytes 8a + 4(g/2) .. +3 (this lane's two are 8a + 2g, +1)
+};
 
 template <int KV>
 __global__ __launch_bounds__(kThr) void attend_hg_kernel(HgArgs a) {
@@ -172,7 +182,8 @@ __global__ __launch_bounds__(kThr) void attend_hg_kernel(HgArgs a) {
   const int r_lo = 4 * g + tj;
   uint32_t wo[4], vo[8];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) wo[j] = l16 * kRowB + (swz(l16, 4 * j + g) << 4);
+  for (int j = 0; j < 4; ++j)
+    wo[j] = l16 * kRowB + (swz(l16, (KV == CSA2_KV_FP4_E2M1_E4M3_16) ? (4 * g + j) : (4 * j + g)) << 4);
 #pragma unroll
   for (int j = 0; j < 8; ++j) vo[j] = r_lo * kRowB + (swz(r_lo, 2 * j + (tc >> 1)) << 4) + 8 * (tc & 1);
 
@@ -193,21 +204,34 @@ __global__ __launch_bounds__(kThr) void attend_hg_kernel(HgArgs a) {
         const uint8_t* rp = (pool ? a.comp_kv : a.win_kv) + row * kRowB + 16 * g;
 #pragma unroll
         for (int s = 0; s < 16; ++s) st.v[tl][s] = *reinterpret_cast<const uint4*>(rp + 64 * s);
-      } else {
+      } else if constexpr (KV == CSA2_KV_FP8_E4M3_UE8M0_32) {
         const uint8_t* rp = (pool ? a.comp_kv : a.win_kv) + row * kDim + 8 * g;
 #pragma unroll
         for (int s = 0; s < 16; ++s) st.code[tl][s] = *reinterpret_cast<const uint2*>(rp + 32 * s);
         st.sc[tl] = *reinterpret_cast<const uint4*>((pool ? a.comp_scale : a.win_scale) +
                                                     row * (kDim / kScaleBlock));
+      } else {
+        const uint8_t* rp = (pool ? a.comp_kv : a.win_kv) + row * (kDim / 2) + 16 * g;
+        const uint8_t* sp = (pool ? a.comp_scale : a.win_scale) + row * (kDim / 16) + 4 * (g >> 1);
+#pragma unroll
+        for (int aa = 0; aa < 4; ++aa) {
+          st.code[tl][aa] = *reinterpret_cast<const uint4*>(rp + 64 * aa);
+          st.sw[tl][aa] = *reinterpret_cast<const uint32_t*>(sp + 8 * aa);
+        }
       }
     }
   };
   auto piece = [&](const Rows<KV>& st, int tl, int s) -> uint4 {
     if constexpr (KV == CSA2_KV_BF16) {
       return st.v[tl][s];
-    } else {
+    } else if constexpr (KV == CSA2_KV_FP8_E4M3_UE8M0_32) {
       const uint32_t w = (s < 4) ? st.sc[tl].x : (s < 8) ? st.sc[tl].y : (s < 12) ? st.sc[tl].z : st.sc[tl].w;
       return fp8x8_to_bf16x8(st.code[tl][s], (w >> (8 * (s & 3))) & 0xffu);
+    } else {
+      const int aa = s >> 2, bb = s & 3;
+      const uint4 c = st.code[tl][aa];
+      const uint32_t w = (bb == 0) ? c.x : (bb == 1) ? c.y : (bb == 2) ? c.z : c.w;
+      return fp4x8_e4m3_to_bf16x8(w, (st.sw[tl][aa] >> (16 * (g & 1) + 8 * (bb >> 1))) & 0xffu);
     }
   };
 
@@ -380,8 +404,10 @@ hipError_t launch_attend_hg(const csa2_dims& d, int32_t B, const csa2_batch& bt,
   const dim3 grid((unsigned)(32 * ((B + 7) / 8)));
   if (d.kv_dtype == CSA2_KV_BF16)
     hipLaunchKernelGGL((attend_hg_kernel<CSA2_KV_BF16>), grid, dim3(kThr), 0, s, a);
-  else
+  else if (d.kv_dtype == CSA2_KV_FP8_E4M3_UE8M0_32)
     hipLaunchKernelGGL((attend_hg_kernel<CSA2_KV_FP8_E4M3_UE8M0_32>), grid, dim3(kThr), 0, s, a);
+  else
+    hipLaunchKernelGGL((attend_hg_kernel<CSA2_KV_FP4_E2M1_E4M3_16>), grid, dim3(kThr), 0, s, a);
   return hipGetLastError();
 }
 

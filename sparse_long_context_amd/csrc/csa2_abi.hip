@@ -23,13 +23,22 @@ size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 csa2_status check_dims(const csa2_dims* d) {
   if (!d) return CSA2_ERR_INVALID_ARG;
-  if (d->kv_dtype != CSA2_KV_BF16 && d->kv_dtype != CSA2_KV_FP8_E4M3_UE8M0_32) return CSA2_ERR_INVALID_ARG;
+  if (d->kv_dtype != CSA2_KV_BF16 && d->kv_dtype != CSA2_KV_FP8_E4M3_UE8M0_32 &&
+      d->kv_dtype != CSA2_KV_FP4_E2M1_E4M3_16)
+    return CSA2_ERR_INVALID_ARG;
+  if (d->index_key_dtype != CSA2_IDXK_F32 && d->index_key_dtype != CSA2_IDXK_MXFP4) return CSA2_ERR_INVALID_ARG;
   if (d->index_relu != 0 && d->index_relu != 1) return CSA2_ERR_INVALID_ARG;
   if (!isfinite(d->softmax_scale)) return CSA2_ERR_INVALID_ARG;
   if (d->window < 0 || d->index_topk < 1 || d->index_heads < 1) return CSA2_ERR_INVALID_ARG;
   if (d->n_heads != kHeads || d->head_dim != kDim || d->index_dim != kIndexDim) return CSA2_ERR_UNSUPPORTED;
-  if (d->window > kMaxWindow || d->index_topk > kMaxTopK || d->index_heads > 64) return CSA2_ERR_UNSUPPORTED;
+  if (d->window > kMaxWindow || d->index_topk > kMaxTopK || d->index_heads > kMaxIndexHeads)
+    return CSA2_ERR_UNSUPPORTED;
   return CSA2_OK;
+}
+
+// Index keys need their scale plane exactly when they are MXFP4.
+bool index_keys_ok(const csa2_dims* d, const void* idx_k, const uint8_t* idx_k_scale) {
+  return idx_k && (d->index_key_dtype != CSA2_IDXK_MXFP4 || idx_k_scale);
 }
 
 csa2_status check_batch(const csa2_batch* bt, int32_t B) {
@@ -147,14 +156,16 @@ csa2_status csa2_workspace_size(const csa2_dims* dims, int32_t B, int32_t max_ca
 }
 
 csa2_status csa2_index_scores(const csa2_dims* dims, int32_t B, const csa2_batch* batch, const float* idx_q,
-                              const float* idx_w, const float* idx_k, float* scores, int64_t score_stride,
-                              hipStream_t stream) {
+                              const float* idx_w, const void* idx_k, const uint8_t* idx_k_scale, float* scores,
+                              int64_t score_stride, hipStream_t stream) {
   csa2_status st = check_dims(dims);
   if (st == CSA2_OK) st = check_batch(batch, B);
   if (st != CSA2_OK) return st;
   if (B == 0 || batch->max_candidates == 0) return CSA2_OK;
-  if (!idx_q || !idx_k || !scores || score_stride < batch->max_candidates) return CSA2_ERR_INVALID_ARG;
-  return hip_status(launch_index_scores(*dims, B, *batch, idx_q, idx_w, idx_k, scores, score_stride, stream));
+  if (!idx_q || !index_keys_ok(dims, idx_k, idx_k_scale) || !scores || score_stride < batch->max_candidates)
+    return CSA2_ERR_INVALID_ARG;
+  return hip_status(
+      launch_index_scores(*dims, B, *batch, idx_q, idx_w, idx_k, idx_k_scale, scores, score_stride, stream));
 }
 
 csa2_status csa2_topk(const csa2_dims* dims, int32_t B, const csa2_batch* batch, const float* scores,
@@ -180,7 +191,7 @@ static csa2_status check_attend_ptrs(const csa2_dims* dims, const void* q, const
                                      const uint8_t* win_scale, const void* comp_kv, const uint8_t* comp_scale,
                                      float* out) {
   if (!q || !out) return CSA2_ERR_INVALID_ARG;
-  if (dims->kv_dtype == CSA2_KV_FP8_E4M3_UE8M0_32 && ((win_kv && !win_scale) || (comp_kv && !comp_scale)))
+  if (dims->kv_dtype != CSA2_KV_BF16 && ((win_kv && !win_scale) || (comp_kv && !comp_scale)))
     return CSA2_ERR_INVALID_ARG;
   return CSA2_OK;
 }
@@ -209,7 +220,8 @@ csa2_status csa2_attend(const csa2_dims* dims, int32_t B, const csa2_batch* batc
 }
 
 csa2_status csa2_decode(const csa2_dims* dims, int32_t B, const csa2_batch* batch, const void* q,
-                        const float* idx_q, const float* idx_w, const float* idx_k, const void* win_kv,
+                        const float* idx_q, const float* idx_w, const void* idx_k, const uint8_t* idx_k_scale,
+                        const void* win_kv,
                         const uint8_t* win_scale, const void* comp_kv, const uint8_t* comp_scale,
                         int32_t* topk_idx, const float* sink, float* out, float* lse, void* workspace,
                         size_t workspace_bytes, hipStream_t stream) {
@@ -218,7 +230,8 @@ csa2_status csa2_decode(const csa2_dims* dims, int32_t B, const csa2_batch* batc
   if (st == CSA2_OK && B > 0) st = check_attend_ptrs(dims, q, win_kv, win_scale, comp_kv, comp_scale, out);
   if (st != CSA2_OK) return st;
   if (B == 0) return CSA2_OK;
-  if (!topk_idx || (batch->max_candidates > 0 && (!idx_q || !idx_k))) return CSA2_ERR_INVALID_ARG;
+  if (!topk_idx || (batch->max_candidates > 0 && (!idx_q || !index_keys_ok(dims, idx_k, idx_k_scale))))
+    return CSA2_ERR_INVALID_ARG;
   const bool hg = use_head_groups(B);
   const size_t need = decode_ws_bytes(B, batch->max_candidates, !hg);
   if (need > 0 && (!workspace || workspace_bytes < need)) return CSA2_ERR_WORKSPACE;
@@ -230,7 +243,8 @@ csa2_status csa2_decode(const csa2_dims* dims, int32_t B, const csa2_batch* batc
                           : nullptr;
 
   if (batch->max_candidates > 0) {
-    if ((st = hip_status(launch_index_scores(*dims, B, *batch, idx_q, idx_w, idx_k, scores, stride, stream))) != CSA2_OK)
+    if ((st = hip_status(launch_index_scores(*dims, B, *batch, idx_q, idx_w, idx_k, idx_k_scale, scores, stride,
+                                             stream))) != CSA2_OK)
       return st;
     if ((st = hip_status(launch_topk(*dims, B, *batch, scores, stride, topk_idx, stream))) != CSA2_OK) return st;
   }
@@ -251,7 +265,8 @@ csa2_status csa2_prefill_workspace_size(const csa2_dims* dims, const csa2_prefil
 }
 
 csa2_status csa2_prefill(const csa2_dims* dims, const csa2_prefill_desc* desc, const void* q, const float* idx_q,
-                         const float* idx_w, const float* idx_k, const void* win_kv, const uint8_t* win_scale,
+                         const float* idx_w, const void* idx_k, const uint8_t* idx_k_scale, const void* win_kv,
+                         const uint8_t* win_scale,
                          const void* comp_kv, const uint8_t* comp_scale, int32_t* topk_idx, const float* sink,
                          float* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   csa2_status st = check_prefill(dims, desc);
@@ -262,7 +277,7 @@ csa2_status csa2_prefill(const csa2_dims* dims, const csa2_prefill_desc* desc, c
   const int32_t max_cand = prefill_max_cand(desc);
   const bool selects = desc->mode == CSA2_MODE_FULL || desc->mode == CSA2_MODE_REINDEX;
   if (desc->mode != CSA2_MODE_WINDOW && !topk_idx) return CSA2_ERR_INVALID_ARG;
-  if (selects && max_cand > 0 && (!idx_q || !idx_k)) return CSA2_ERR_INVALID_ARG;
+  if (selects && max_cand > 0 && (!idx_q || !index_keys_ok(dims, idx_k, idx_k_scale))) return CSA2_ERR_INVALID_ARG;
   size_t need = prefill_meta_bytes(T) + decode_ws_bytes(T, max_cand, true);
   if (!workspace || workspace_bytes < need) return CSA2_ERR_WORKSPACE;
 
@@ -290,16 +305,33 @@ csa2_status csa2_prefill(const csa2_dims* dims, const csa2_prefill_desc* desc, c
   bt.max_candidates = max_cand;
 
   if (selects && max_cand > 0) {
-    if (desc->mode == CSA2_MODE_FULL && dims->index_heads == 1)
+    if (desc->mode == CSA2_MODE_FULL && dims->index_heads == 1 && dims->index_key_dtype == CSA2_IDXK_F32)
       st = hip_status(launch_index_scores_prefill(*dims, T, m.pos, desc->mode, desc->compress_ratio, desc->pool_len,
-                                                  idx_q, idx_w, idx_k, scores, stride, stream));
+                                                  idx_q, idx_w, static_cast<const float*>(idx_k), scores, stride,
+                                                  stream));
     else
-      st = hip_status(launch_index_scores(*dims, T, bt, idx_q, idx_w, idx_k, scores, stride, stream));
+      st = hip_status(launch_index_scores(*dims, T, bt, idx_q, idx_w, idx_k, idx_k_scale, scores, stride, stream));
     if (st != CSA2_OK) return st;
     if ((st = hip_status(launch_topk(*dims, T, bt, scores, stride, topk_idx, stream))) != CSA2_OK) return st;
   }
   return attend_common(dims, T, &bt, q, win_kv, win_scale, comp_kv, comp_scale,
                        desc->mode == CSA2_MODE_WINDOW ? nullptr : topk_idx, sink, out, lse, partial, sp, stream);
+}
+
+csa2_status csa2_quantize_fp4_kv(int64_t n_rows, int32_t d, const float* src, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t stream) {
+  if (n_rows < 0 || d <= 0 || (d % 16) != 0) return CSA2_ERR_INVALID_ARG;
+  if (n_rows == 0) return CSA2_OK;
+  if (!src || !codes || !scales) return CSA2_ERR_INVALID_ARG;
+  return hip_status(launch_quantize_fp4_kv(n_rows, d, src, codes, scales, stream));
+}
+
+csa2_status csa2_quantize_mxfp4(int64_t n_rows, int32_t d, const float* src, uint8_t* codes, uint8_t* scales,
+                                hipStream_t stream) {
+  if (n_rows < 0 || d <= 0 || (d % 32) != 0) return CSA2_ERR_INVALID_ARG;
+  if (n_rows == 0) return CSA2_OK;
+  if (!src || !codes || !scales) return CSA2_ERR_INVALID_ARG;
+  return hip_status(launch_quantize_mxfp4(n_rows, d, src, codes, scales, stream));
 }
 
 }  // extern "C"

@@ -11,6 +11,7 @@ namespace csa2 {
 constexpr int kHeads = 64;      // query heads sharing one KV row
 constexpr int kDim = 512;       // dims per head and per KV row
 constexpr int kIndexDim = 128;  // indexer key / query width
+constexpr int kMaxIndexHeads = 64;
 constexpr int kMaxTopK = 512;
 constexpr int kMaxWindow = 128;
 constexpr int kMaxEntries = kMaxWindow + kMaxTopK;  // 640 rows attended per query at most
@@ -24,12 +25,39 @@ __device__ __forceinline__ int64_t n_valid_of(int64_t pos, int32_t m, int32_t mo
   return n < pool_len ? n : (int64_t)pool_len;
 }
 
+// Eight E2M1 codes (a 32-bit word, element 0 in the low nibble) -> their exact
+// fp32 values, with the gfx950 scaled conversion at scale 1.
+__device__ __forceinline__ void fp4x8_to_f32x8(uint32_t w, float* out) {
+  const auto a0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const auto a1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  const auto a2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  const auto a3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  out[0] = a0[0], out[1] = a0[1], out[2] = a1[0], out[3] = a1[1];
+  out[4] = a2[0], out[5] = a2[1], out[6] = a3[0], out[7] = a3[1];
+}
+
+// Eight E2M1 codes times one E4M3 scale byte -> eight bf16 (a uint4), exact:
+// each product has at most 6 significant bits.
+__device__ __forceinline__ uint4 fp4x8_e4m3_to_bf16x8(uint32_t w, uint32_t scale_byte) {
+  float v[8];
+  fp4x8_to_f32x8(w, v);
+  const float s = __builtin_amdgcn_cvt_f32_fp8((int)scale_byte, 0);
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const __bf16 lo = (__bf16)(v[2 * i] * s), hi = (__bf16)(v[2 * i + 1] * s);
+    o[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 // ---- launchers (each returns the launch's hipError_t) ----------------------
 
 // Decode-shaped scores: one workgroup per (query, tile of candidates).
+// idx_k: f32 keys, or MXFP4 codes with their E8M0 scale plane (d.index_key_dtype).
 hipError_t launch_index_scores(const csa2_dims& d, int32_t B, const csa2_batch& bt, const float* idx_q,
-                               const float* idx_w, const float* idx_k, float* scores, int64_t stride,
-                               hipStream_t s);
+                               const float* idx_w, const void* idx_k, const uint8_t* idx_k_scale,
+                               float* scores, int64_t stride, hipStream_t s);
 // Prefill-shaped scores (one sequence): register-tiled queries x candidates.
 hipError_t launch_index_scores_prefill(const csa2_dims& d, int32_t T, const int64_t* pos, int32_t mode,
                                        int32_t ratio, int32_t pool_len, const float* idx_q,
@@ -49,6 +77,12 @@ hipError_t launch_attend_hg(const csa2_dims& d, int32_t B, const csa2_batch& bt,
                             const uint8_t* comp_scale, const int32_t* topk_idx, const float* sink, float* out,
                             float* lse, hipStream_t s);
 int attend_split_for(int32_t B);
+
+// The cache writer's quantizers (one thread per scale block).
+hipError_t launch_quantize_fp4_kv(int64_t n_rows, int32_t d, const float* src, uint8_t* codes, uint8_t* scales,
+                                  hipStream_t s);
+hipError_t launch_quantize_mxfp4(int64_t n_rows, int32_t d, const float* src, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t s);
 
 // Per-query descriptors of a prefill chunk, written into workspace arrays.
 hipError_t launch_prefill_meta(const csa2_prefill_desc& p, int32_t window, int64_t* pos, int32_t* mode,

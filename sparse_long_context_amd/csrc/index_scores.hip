@@ -12,6 +12,12 @@
 //    only large stream (512 B per candidate); 256 threads load them with
 //    coalesced 16-byte loads into LDS, then each of 32 lanes runs one
 //    candidate's FMA chain out of LDS.
+//  * decode with MXFP4 keys (E2M1 codes + one E8M0 scale per 32, 68 B per
+//    candidate; PocketLLM "DeepSeek-V4.1-Flash", "The CSA2 attention layers"):
+//    one workgroup per (query, 256 candidates); the code rows come in with
+//    coalesced 16-byte loads through LDS, and each thread widens its own row to
+//    fp32 exactly and runs its FMA chain, so the score is the one fp32 keys
+//    holding the decoded values would give.
 //  * prefill: one sequence, many queries sharing the key rows, so the keys are
 //    reused across queries: a register-tiled product of 128 queries x 128
 //    candidates per workgroup (8 x 8 outputs per thread), each output's FMA
@@ -122,6 +128,102 @@ __global__ __launch_bounds__(kThreads) void index_scores_decode(
   scores[(int64_t)b * stride + j] = sc;
 }
 
+// ---- decode, MXFP4 keys ------------------------------------------------------
+constexpr int kMxRows = 256;                  // candidates per workgroup, one per thread
+constexpr int kMxRowB = kIndexDim / 2;        // 64 code bytes per key row
+constexpr int kMxScales = kIndexDim / 32;     // 4 E8M0 scales per key row
+static_assert(kMxScales == 4, "a key row's scales are read as one 32-bit word");
+
+// 16-byte unit u of code row r sits at unit u ^ ((r >> 2) & 3): sixteen lanes
+// reading the same unit of their own rows then cover all 64 banks.
+__device__ __forceinline__ int mx_unit_swz(int r, int u) { return u ^ ((r >> 2) & 3); }
+
+__global__ __launch_bounds__(kThreads) void index_scores_decode_mx(
+    int32_t hi, int32_t relu, int32_t max_cand, const int64_t* __restrict__ pos,
+    const int32_t* __restrict__ mode, const int32_t* __restrict__ ratio,
+    const int64_t* __restrict__ pool_row0, const int32_t* __restrict__ pool_len,
+    const int64_t* __restrict__ cand_off, const int32_t* __restrict__ cand_idx,
+    const float* __restrict__ idx_q, const float* __restrict__ idx_w, const uint8_t* __restrict__ kcodes,
+    const uint8_t* __restrict__ kscales, float* __restrict__ scores, int64_t stride) {
+  __shared__ __attribute__((aligned(16))) uint8_t c_s[kMxRows * kMxRowB];
+  __shared__ __attribute__((aligned(16))) float q_s[kMaxIndexHeads][kIndexDim];
+  __shared__ float w_s[kMaxIndexHeads];
+  __shared__ int64_t row_s[kMxRows];
+
+  const int b = blockIdx.y;
+  const int t = threadIdx.x;
+  const int md = mode[b];
+  if (md != CSA2_MODE_FULL && md != CSA2_MODE_REINDEX) return;
+  const int64_t nv = n_valid_of(pos[b], ratio[b], md, pool_len[b]);
+  int64_t n = (md == CSA2_MODE_FULL) ? nv : (cand_off[b + 1] - cand_off[b]);
+  if (n > max_cand) n = max_cand;
+  const int64_t j0 = (int64_t)blockIdx.x * kMxRows;
+  if (j0 >= n) return;
+
+  const int64_t j = j0 + t;
+  int64_t my_row = -1;  // this thread's candidate row (pool-relative), -1 when there is none
+  if (j < n) {
+    const int64_t rr = (md == CSA2_MODE_FULL) ? j : (int64_t)cand_idx[cand_off[b] + j];
+    if (rr >= 0 && rr < nv) my_row = rr;
+  }
+  row_s[t] = my_row;
+  for (int x = t; x < hi * kIndexDim; x += kThreads) q_s[x / kIndexDim][x % kIndexDim] = idx_q[(int64_t)b * hi * kIndexDim + x];
+  if (t < hi) w_s[t] = idx_w ? idx_w[(int64_t)b * hi + t] : 1.0f;
+  const int64_t prow0 = pool_row0[b];
+  const uint32_t sc4 = (my_row >= 0) ? *reinterpret_cast<const uint32_t*>(kscales + (prow0 + my_row) * kMxScales)
+                                     : 0u;
+  __syncthreads();
+
+  // code rows: four threads per 64-byte row, 64 rows per pass
+  uint4 v[4];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int r = it * 64 + (t >> 2), u = t & 3;
+    const int64_t rr = row_s[r];
+    v[it] = (rr >= 0) ? *reinterpret_cast<const uint4*>(kcodes + (prow0 + rr) * kMxRowB + u * 16)
+                      : make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int r = it * 64 + (t >> 2), u = t & 3;
+    *reinterpret_cast<uint4*>(&c_s[r * kMxRowB + mx_unit_swz(r, u) * 16]) = v[it];
+  }
+  __syncthreads();
+  if (j >= n) return;
+  float sc = -__builtin_inff();
+  if (my_row >= 0) {
+    // widen the row: unit u holds dims 32u .. 32u+31, the block of scale byte u
+    float k[kIndexDim];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint4 c = *reinterpret_cast<const uint4*>(&c_s[t * kMxRowB + mx_unit_swz(t, u) * 16]);
+      const uint32_t e = (sc4 >> (8 * u)) & 0xffu;
+      // 2^(e-127) as fp32 (e = 0 is the subnormal 2^-127); products are exact
+      const float scale = e ? __uint_as_float(e << 23) : __uint_as_float(0x00400000u);
+      const uint32_t wds[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd) {
+        float kv[8];
+        fp4x8_to_f32x8(wds[wd], kv);
+#pragma unroll
+        for (int e2 = 0; e2 < 8; ++e2) k[32 * u + 8 * wd + e2] = kv[e2] * scale;
+      }
+    }
+    // heads in order, each folded into the score as soon as its chain ends
+    float s = 0.0f;
+#pragma unroll 1
+    for (int h = 0; h < hi; ++h) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int i = 0; i < kIndexDim; ++i) acc = __builtin_fmaf(q_s[h][i], k[i], acc);
+      if (relu) acc = acc > 0.0f ? acc : 0.0f;
+      s = __builtin_fmaf(w_s[h], acc, s);
+    }
+    sc = (s == 0.0f) ? 0.0f : s;
+  }
+  scores[(int64_t)b * stride + j] = sc;
+}
+
 // ---- prefill: queries x candidates, register tiled -------------------------
 constexpr int kPQ = 128;  // queries per workgroup
 constexpr int kPC = 128;  // candidates per workgroup
@@ -206,11 +308,20 @@ __global__ __launch_bounds__(256) void index_scores_prefill(
 }  // namespace
 
 hipError_t launch_index_scores(const csa2_dims& d, int32_t B, const csa2_batch& bt, const float* idx_q,
-                               const float* idx_w, const float* idx_k, float* scores, int64_t stride,
-                               hipStream_t s) {
+                               const float* idx_w, const void* idx_k_v, const uint8_t* idx_k_scale,
+                               float* scores, int64_t stride, hipStream_t s) {
   if (B == 0 || bt.max_candidates == 0) return hipSuccess;
-  dim3 grid((bt.max_candidates + kRows - 1) / kRows, B);
   const int hi = d.index_heads;
+  if (d.index_key_dtype == CSA2_IDXK_MXFP4) {
+    dim3 grid((bt.max_candidates + kMxRows - 1) / kMxRows, B);
+    const uint8_t* kc = static_cast<const uint8_t*>(idx_k_v);
+    hipLaunchKernelGGL(index_scores_decode_mx, grid, dim3(kThreads), 0, s, hi, d.index_relu, bt.max_candidates,
+                       bt.pos, bt.mode, bt.compress_ratio, bt.pool_row0, bt.pool_len, bt.cand_off, bt.cand_idx,
+                       idx_q, idx_w, kc, idx_k_scale, scores, stride);
+    return hipGetLastError();
+  }
+  const float* idx_k = static_cast<const float*>(idx_k_v);
+  dim3 grid((bt.max_candidates + kRows - 1) / kRows, B);
 #define CSA2_IDX_ARGS                                                                                 \
   hi, d.index_relu, bt.max_candidates, bt.pos, bt.mode, bt.compress_ratio, bt.pool_row0, bt.pool_len, \
       bt.cand_off, bt.cand_idx, idx_q, idx_w, idx_k, scores, stride

@@ -38,7 +38,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 SYNTH_LIB = os.path.join(PKG, "libcsa2_synth.so")
 
 MODE_FULL, MODE_REINDEX, MODE_REUSE, MODE_WINDOW = 0, 1, 2, 3
-KV_BF16, KV_FP8 = 0, 1
+KV_BF16, KV_FP8, KV_FP4 = 0, 1, 2
+IDXK_F32, IDXK_MXFP4 = 0, 1
 
 # streams: one per tensor kind
 S_Q, S_WIN, S_POOL, S_IDXQ, S_IDXK, S_CTX, S_REUSE, S_CAND = 1, 2, 3, 4, 5, 6, 7, 8

@@ -15,14 +15,14 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def declared_functions():
     src = open(os.path.join(ROOT, "include", "csa2.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(csa2_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(csa2_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_declares_the_documented_entry_points():
     names = declared_functions()
     for n in ["csa2_index_scores", "csa2_topk", "csa2_attend", "csa2_decode", "csa2_prefill",
               "csa2_workspace_size", "csa2_prefill_workspace_size", "csa2_status_str", "csa2_abi_version",
-              "csa2_last_hip_error"]:
+              "csa2_last_hip_error", "csa2_quantize_fp4_kv", "csa2_quantize_mxfp4"]:
         assert n in names, n
 
 
@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     for n in declared_functions():
         assert hasattr(L, n), n
     assert set(declared_functions()) == set(csa2.EXPORTS)
-    assert csa2.csa2_abi_version() == 1
+    assert csa2.csa2_abi_version() == 2
     assert csa2.status_str(0) == "ok"
 
 
@@ -61,7 +61,8 @@ def batch(**kw):
     (dict(index_heads=65), csa2.CSA2_ERR_UNSUPPORTED),
     (dict(index_topk=0), csa2.CSA2_ERR_INVALID_ARG),
     (dict(window=-1), csa2.CSA2_ERR_INVALID_ARG),
-    (dict(kv_dtype=2), csa2.CSA2_ERR_INVALID_ARG),
+    (dict(kv_dtype=3), csa2.CSA2_ERR_INVALID_ARG),
+    (dict(index_key_dtype=2), csa2.CSA2_ERR_INVALID_ARG),
     (dict(index_relu=2), csa2.CSA2_ERR_INVALID_ARG),
     (dict(softmax_scale=float("nan")), csa2.CSA2_ERR_INVALID_ARG),
 ])
@@ -127,3 +128,28 @@ def test_zero_sized_calls_are_noops():
     csa2.csa2_topk(d, 0, batch(), None, 0, None, stream=0)
     csa2.csa2_attend(d, 0, batch(), None, None, None, None, None, None, None, None, None, None, 0, stream=0)
     assert csa2.csa2_workspace_size(d, 0, 0) >= 0
+
+
+def test_storage_format_arguments_are_validated():
+    E = csa2.Csa2Error
+    for kw in (dict(kv_dtype=3), dict(kv_dtype=-1), dict(index_key_dtype=2)):
+        with pytest.raises(E) as e:
+            csa2.csa2_workspace_size(dims(**kw), 4, 100)
+        assert e.value.status == csa2.CSA2_ERR_INVALID_ARG
+    # MXFP4 keys without their scale plane
+    with pytest.raises(E) as e:
+        csa2.csa2_index_scores(dims(index_key_dtype=1), 2, batch(), FAKE, None, FAKE, FAKE, 16, stream=0)
+    assert e.value.status == csa2.CSA2_ERR_INVALID_ARG
+    # FP4 KV without its scale plane
+    with pytest.raises(E) as e:
+        csa2.csa2_attend(dims(kv_dtype=2), 2, batch(), FAKE, FAKE, None, None, None, FAKE, None, FAKE, None,
+                         None, 0, stream=0)
+    assert e.value.status == csa2.CSA2_ERR_INVALID_ARG
+    # quantizers: block multiples, null pointers, negative sizes; zero rows is a no-op
+    for fn, bad_d in ((csa2.csa2_quantize_fp4_kv, 24), (csa2.csa2_quantize_mxfp4, 48)):
+        for args in ((4, bad_d, FAKE, FAKE, FAKE), (4, 0, FAKE, FAKE, FAKE), (-1, 64, FAKE, FAKE, FAKE),
+                     (4, 64, None, FAKE, FAKE), (4, 64, FAKE, None, FAKE), (4, 64, FAKE, FAKE, None)):
+            with pytest.raises(E) as e:
+                fn(*args, stream=0)
+            assert e.value.status == csa2.CSA2_ERR_INVALID_ARG, (fn, args)
+        fn(0, 64, None, None, None, stream=0)

@@ -1,0 +1,191 @@
+"""GPU parity of the FP4 storage formats: FP4 main KV (E2M1 codes, one E4M3
+scale per 16 values) and MXFP4 index keys (E2M1 codes, one E8M0 scale per 32).
+
+The FP4 bytes every comparison uses are written by the oracle's quantizer from
+fp32 values (the bf16 rows of the seeded workloads, widened), so both paths read
+identical inputs.  The HIP quantizers are checked separately, byte for byte,
+against the oracle's.  FP4 values are exact in bf16, so the attention meets
+the bf16 bar (normwise 1e-2); index scores over the decoded keys, and hence
+the selections, match bit for bit.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import oracle as O  # noqa: E402
+from sparse_long_context_amd import csa2, synth  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+LSE_TOL = 2e-3
+
+
+def say(*a):
+    print("[gpu-fp4]", *a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    csa2.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def normwise(a, ref):
+    m = float(np.abs(ref).max())
+    if m == 0.0:
+        return 0.0 if float(np.abs(a).max()) == 0.0 else float("inf")
+    return float(np.abs(a - ref).max()) / m
+
+
+def with_fp4_kv(inp):
+    """The batch with its bf16 KV rows re-stored as FP4 (oracle quantizer)."""
+    out = dict(inp, dims=dict(inp["dims"], kv_dtype=synth.KV_FP4))
+    for src, sc in (("win_kv", "win_scale"), ("comp_kv", "comp_scale")):
+        codes, scales = O.quant_fp4kv(synth.bf16_bits_to_f32(inp[src]))
+        out[src], out[sc] = codes, scales
+    return out
+
+
+def with_mxfp4_keys(inp):
+    codes, scales = O.quant_mxfp4(inp["idx_k"])
+    return dict(inp, idx_k=codes, idx_k_scale=scales, dims=dict(inp["dims"], index_key_dtype=synth.IDXK_MXFP4))
+
+
+def compare(inp, sel_g, out_g, lse_g, queries=None):
+    qs = np.arange(inp["B"]) if queries is None else np.asarray(queries)
+    sel_o, out_o, lse_o = O.decode_batch(inp, qs)
+    worst = 0.0
+    for i, b in enumerate(qs):
+        if inp["mode"][b] in (synth.MODE_FULL, synth.MODE_REINDEX):
+            assert np.array_equal(sel_g[b], sel_o[i]), f"query {b}: selection differs"
+        err = normwise(out_g[b], out_o[i])
+        worst = max(worst, err)
+        assert err <= TOL, f"query {b}: normwise error {err:.3e}"
+        fin = np.isfinite(lse_o[i])
+        assert np.array_equal(fin, np.isfinite(lse_g[b]))
+        assert np.abs(lse_g[b][fin] - lse_o[i][fin]).max(initial=0.0) <= LSE_TOL
+    return worst
+
+
+def run_decode(inp):
+    w = csa2.DecodeWorkload(inp)
+    w.decode()
+    torch.cuda.synchronize()
+    return w.topk.cpu().numpy(), w.out.cpu().numpy(), w.lse.cpu().numpy()
+
+
+def small_dims(**kw):
+    d = synth.default_dims()
+    d.update(kw)
+    return d
+
+
+def test_quantizers_match_the_oracle_byte_for_byte():
+    rng = np.random.default_rng(31)
+    kv = (rng.standard_normal((777, 512)) * np.exp(rng.uniform(-7, 7, (777, 1)))).astype(np.float32)
+    kv[5, 32:48] = 0.0                                   # all-zero block: scale 2^-9
+    kv[6] *= 1e4                                         # amax / 6 above 448: saturating scale and codes
+    s = np.float32(0.375)                                # exact E4M3; amax 6 s gives exactly this scale
+    mids = np.array([6, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.25, -0.75, -1.25, -1.75, -2.5, -3.5, -5.0, 0.5],
+                    np.float32)
+    kv[7, :16] = mids * s                                # every E2M1 rounding tie, both signs
+    keys = (rng.standard_normal((999, 128)) * np.exp(rng.uniform(-20, 20, (999, 1)))).astype(np.float32)
+    keys[3, 32:64] = 0.0
+    mids32 = np.concatenate([mids, mids[::-1]])
+    keys[4, :32] = mids32 * np.float32(2.0 ** -3)        # amax / 6 = 2^-3 exactly: ties at the E8M0 scale
+    for name, x, fn, oq, blk in (("fp4 kv", kv, csa2.csa2_quantize_fp4_kv, O.quant_fp4kv, 16),
+                                 ("mxfp4", keys, csa2.csa2_quantize_mxfp4, O.quant_mxfp4, 32)):
+        say(f"quantizer {name}: {x.shape}")
+        src = torch.from_numpy(x).cuda()
+        codes = torch.empty((x.shape[0], x.shape[1] // 2), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((x.shape[0], x.shape[1] // blk), dtype=torch.uint8, device="cuda")
+        fn(x.shape[0], x.shape[1], src, codes, scales)
+        torch.cuda.synchronize()
+        c_o, s_o = oq(x)
+        assert np.array_equal(scales.cpu().numpy(), s_o), name
+        assert np.array_equal(codes.cpu().numpy(), c_o), name
+
+
+def test_decode_fp4_kv_and_mxfp4_keys():
+    ctx = [1000, 4096 + 4 * 300 + 3, 70001, 4 * 513, 2, 12345]
+    inp = synth.decode_batch(32, ctx, [synth.MODE_FULL] * len(ctx), [4] * len(ctx), dims=small_dims())
+    inp = with_mxfp4_keys(with_fp4_kv(inp))
+    say("decode FP4 KV + MXFP4 keys, B =", inp["B"])
+    sg, og, lg = run_decode(inp)
+    say(f"  worst normwise error {compare(inp, sg, og, lg):.2e}")
+
+
+def test_decode_fp4_kv_all_heads_kernel():
+    # more than 64 queries: the all-heads kernel, entries split over workgroups
+    ctx = [20000] * 3 + [300] * 63
+    inp = synth.decode_batch(33, ctx, [0] * 3 + [3] * 63, [4] * 3 + [0] * 63, dims=small_dims())
+    inp = with_fp4_kv(inp)
+    say("decode FP4 KV, B =", inp["B"])
+    sg, og, lg = run_decode(inp)
+    compare(inp, sg, og, lg, queries=[0, 1, 2, 3, 65])
+
+
+def test_decode_mxfp4_keys_reindex_and_heads():
+    ctx = [9000, 9000, 9000, 300, 50000, 20000]
+    modes = [0, 1, 2, 0, 1, 1]
+    dims = small_dims(index_heads=3, index_relu=1)
+    inp = synth.decode_batch(34, ctx, modes, [4] * len(ctx), dims=dims)
+    synth.add_reindex_lists(inp, 34, frac=0.3)
+    inp = with_mxfp4_keys(inp)
+    say("decode MXFP4 keys, 3 ReLU index heads, Reindex lists")
+    sg, og, lg = run_decode(inp)
+    compare(inp, sg, og, lg)
+
+
+def test_prefill_fp4_kv_and_mxfp4_keys():
+    pos0, T, m = 6000, 300, 8
+    pf = synth.prefill_chunk(35, T, pos0, m, (pos0 + T) // m, dims=small_dims(), win_pos0=pos0 - 40)
+    pf = with_mxfp4_keys(with_fp4_kv(pf))
+    say("prefill T=300 FP4 KV + MXFP4 keys")
+    w = csa2.PrefillWorkload(pf)
+    w.prefill()
+    torch.cuda.synchronize()
+    inp = synth.prefill_as_batch(pf)
+    compare(inp, w.topk.cpu().numpy(), w.out.cpu().numpy(), w.lse.cpu().numpy(), queries=[0, 1, 40, 41, 150, 299])
+
+
+def test_full_size_decode_fp4():
+    """The 64-query, 16,384-candidate decode workload with its KV rows in FP4 and
+    its index keys in MXFP4: the HIP quantizers reproduce the oracle's bytes at
+    full size, and sampled queries match the oracle."""
+    say("building config 1")
+    inp = synth.config(1)
+    for src, fn, blk, nb in (("comp_kv", csa2.csa2_quantize_fp4_kv, 16, 512), ("idx_k", csa2.csa2_quantize_mxfp4, 32, 128)):
+        x = synth.bf16_bits_to_f32(inp[src]) if src == "comp_kv" else inp[src]
+        rows = x.shape[0]
+        say(f"quantizing {src} on the GPU: {rows} rows")
+        xs = torch.from_numpy(np.ascontiguousarray(x)).cuda()
+        codes = torch.empty((rows, nb // 2), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((rows, nb // blk), dtype=torch.uint8, device="cuda")
+        fn(rows, nb, xs, codes, scales)
+        torch.cuda.synchronize()
+        c_g, s_g = codes.cpu().numpy(), scales.cpu().numpy()
+        del xs, codes, scales
+        torch.cuda.empty_cache()
+        c_o, s_o = (O.quant_fp4kv if src == "comp_kv" else O.quant_mxfp4)(x)
+        assert np.array_equal(s_g, s_o) and np.array_equal(c_g, c_o), src
+        del c_g, s_g, c_o, s_o
+    inp = with_mxfp4_keys(with_fp4_kv(inp))
+    say("config 1 in FP4 / MXFP4: running")
+    sg, og, lg = run_decode(inp)
+    torch.cuda.empty_cache()
+    samples = [0, 31, 63]
+    say(f"oracle on queries {samples}")
+    worst = compare(inp, sg, og, lg, samples)
+    say(f"  worst normwise error {worst:.2e}")
+    for b in range(inp["B"]):
+        v = sg[b][sg[b] >= 0]
+        assert len(v) == 512 and (np.diff(v) > 0).all()
+    assert np.isfinite(og).all()
