@@ -26,6 +26,7 @@ METRIC = "CSA2 attended queries/sec (64h×512, 128+512 keys) + % of HBM/MFMA roo
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
 INDEX_KEY_BYTES = 128 * 4    # one fp32 index key row per scanned candidate
+MXFP4_KEY_BYTES = 64 + 4     # one MXFP4 index key row: 64 code bytes + 4 E8M0 scales
 INDEX_Q_BYTES = 128 * 4      # one fp32 indexer query per query
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILE_DIR, "index_scores_decode_64x16384_traffic.json")
@@ -38,17 +39,20 @@ def source_digest(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def workload_desc(inp):
+def workload_desc(inp, storage="native"):
     d = inp["dims"]
     kv = "bf16" if d["kv_dtype"] == 0 else "fp8 e4m3 + ue8m0/32"
+    keys = "fp32"
+    if storage == "fp4":
+        kv, keys = "fp4 e2m1 + e4m3/16", "mxfp4 (e2m1 + e8m0/32)"
     return {
         "workload": (f"decode, {inp['B']} queries, context {int(inp['pos'][0]) + 1}, compress ratio "
                      f"{int(inp['ratio'][0])} -> {int(inp['pool_len'][0])} candidates each, window "
                      f"{d['window']}, top-{d['index_topk']}, {d['n_heads']} heads x {d['head_dim']}, {kv} KV, "
-                     f"fp32 indexer dim {d['index_dim']}"),
+                     f"{keys} indexer keys dim {d['index_dim']}"),
         "queries_per_step": int(inp["B"]),
         "candidates_per_query": int(inp["pool_len"][0]),
-        "window": d["window"], "index_topk": d["index_topk"], "kv": kv,
+        "window": d["window"], "index_topk": d["index_topk"], "kv": kv, "index_keys": keys,
     }
 
 
@@ -132,6 +136,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1, help="decode workload index (1, 3 or 4)")
+    ap.add_argument("--storage", choices=("native", "fp4"), default="native",
+                    help="fp4: the same workload with its KV rows re-stored as FP4 (E4M3 scale per 16) and its index "
+                         "keys as MXFP4, quantized on the GPU by the library's own quantizers before timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain %d MiB fill and sum (for scaling rocprofv3 byte counters)" % (COPY_PROBE_BYTES >> 20))
@@ -162,6 +169,28 @@ def main():
     w = csa2.DecodeWorkload(inp)
     stream = torch.cuda.current_stream()
     B = w.B
+    if args.storage == "fp4":
+        if inp["dims"]["kv_dtype"] != 0:
+            print("--storage fp4 re-stores bf16 workloads (1 or 4)", file=sys.stderr)
+            sys.exit(2)
+        print("[bench] re-storing KV as FP4 and index keys as MXFP4 on the GPU", file=sys.stderr, flush=True)
+        for name, scname in (("win_kv", "win_scale"), ("comp_kv", "comp_scale")):
+            src = getattr(w, name).view(torch.bfloat16).float()
+            rows = src.shape[0]
+            codes = torch.empty((rows, 256), dtype=torch.uint8, device="cuda")
+            scales = torch.empty((rows, 32), dtype=torch.uint8, device="cuda")
+            csa2.csa2_quantize_fp4_kv(rows, 512, src, codes, scales)
+            setattr(w, name, codes)
+            setattr(w, scname, scales)
+            del src
+        rows = w.idx_k.shape[0]
+        kc = torch.empty((rows, 64), dtype=torch.uint8, device="cuda")
+        ks = torch.empty((rows, 4), dtype=torch.uint8, device="cuda")
+        csa2.csa2_quantize_mxfp4(rows, 128, w.idx_k, kc, ks)
+        w.idx_k, w.idx_k_scale = kc, ks
+        w.dims.kv_dtype, w.dims.index_key_dtype = 2, 1
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
 
     for _ in range(args.warmup):
         w.decode()
@@ -185,7 +214,8 @@ def main():
     stride = w.max_cand
     scores = torch.empty((B, stride), dtype=torch.float32, device="cuda")
     stages = [
-        lambda: csa2.csa2_index_scores(w.dims, B, w.batch, w.idx_q, w.idx_w, w.idx_k, scores, stride),
+        lambda: csa2.csa2_index_scores(w.dims, B, w.batch, w.idx_q, w.idx_w, w.idx_k, scores, stride,
+                                       idx_k_scale=w.idx_k_scale),
         lambda: csa2.csa2_topk(w.dims, B, w.batch, scores, stride, w.topk),
         lambda: csa2.csa2_attend(w.dims, B, w.batch, w.q, w.win_kv, w.win_scale, w.comp_kv, w.comp_scale, w.topk,
                                  w.sink, w.out, w.lse, None, 0),
@@ -214,10 +244,11 @@ def main():
     n_cand = int(sum(min(int(p), (int(pos) + 1) // int(r)) for p, pos, r, m in
                      zip(inp["pool_len"], inp["pos"], inp["ratio"], inp["mode"]) if m == 0 and r > 0))
     n_full = int((inp["mode"] == 0).sum())
-    idx_bytes = n_cand * INDEX_KEY_BYTES + n_full * INDEX_Q_BYTES
+    key_bytes = MXFP4_KEY_BYTES if args.storage == "fp4" else INDEX_KEY_BYTES
+    idx_bytes = n_cand * key_bytes + n_full * INDEX_Q_BYTES
     achieved = idx_bytes / (stage_us[0] * 1e-6) / 1e9
-    traffic = traffic_from_profile() if args.config == 1 else None
-    roofline = {"bound": "hbm", "kernel": "index_scores_decode", "achieved": round(achieved, 1),
+    traffic = traffic_from_profile() if (args.config == 1 and args.storage == "native") else None
+    roofline = {"bound": "hbm", "kernel": "index_scores_decode" if args.storage == "native" else "index_scores_decode_mx", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "algorithmic_bytes_per_launch": idx_bytes,
                 "avg_launch_us": round(stage_us[0], 2)}
@@ -235,7 +266,7 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": workload_desc(inp),
+        "config": workload_desc(inp, args.storage),
         "roofline": roofline,
         "stages_us": {"index_scores": round(stage_us[0], 2), "topk": round(stage_us[1], 2),
                       "attend": round(stage_us[2], 2)},
@@ -243,7 +274,7 @@ def main():
                         "frac": round(attend_tflops / BF16_PEAK_TFLOPS, 4)},
         "gpu": torch.cuda.get_device_name(0),
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.storage == "native":
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(line), flush=True)

@@ -14,7 +14,7 @@
 //    candidate's FMA chain out of LDS.
 //  * decode with MXFP4 keys (E2M1 codes + one E8M0 scale per 32, 68 B per
 //    candidate; PocketLLM "DeepSeek-V4.1-Flash", "The CSA2 attention layers"):
-//    one workgroup per (query, 256 candidates); the code rows come in with
+//    one workgroup (one wave) per (query, 64 candidates); the code rows come in with
 //    coalesced 16-byte loads through LDS, and each thread widens its own row to
 //    fp32 exactly and runs its FMA chain, so the score is the one fp32 keys
 //    holding the decoded values would give.
@@ -129,7 +129,8 @@ __global__ __launch_bounds__(kThreads) void index_scores_decode(
 }
 
 // ---- decode, MXFP4 keys ------------------------------------------------------
-constexpr int kMxRows = 256;                  // candidates per workgroup, one per thread
+constexpr int kMxRows = 64;                   // candidates per workgroup (one wave), one per thread
+constexpr int kMxThreads = kMxRows;
 constexpr int kMxRowB = kIndexDim / 2;        // 64 code bytes per key row
 constexpr int kMxScales = kIndexDim / 32;     // 4 E8M0 scales per key row
 static_assert(kMxScales == 4, "a key row's scales are read as one 32-bit word");
@@ -138,7 +139,11 @@ static_assert(kMxScales == 4, "a key row's scales are read as one 32-bit word");
 // reading the same unit of their own rows then cover all 64 banks.
 __device__ __forceinline__ int mx_unit_swz(int r, int u) { return u ^ ((r >> 2) & 3); }
 
-__global__ __launch_bounds__(kThreads) void index_scores_decode_mx(
+// ONE: a single index head (the workloads' form): q takes 512 B of LDS and each
+// row is widened eight values at a time into its FMA chain, which keeps the
+// footprint small enough for many workgroups per CU (more loads in flight).
+template <bool ONE>
+__global__ __launch_bounds__(kMxThreads) void index_scores_decode_mx(
     int32_t hi, int32_t relu, int32_t max_cand, const int64_t* __restrict__ pos,
     const int32_t* __restrict__ mode, const int32_t* __restrict__ ratio,
     const int64_t* __restrict__ pool_row0, const int32_t* __restrict__ pool_len,
@@ -146,52 +151,74 @@ __global__ __launch_bounds__(kThreads) void index_scores_decode_mx(
     const float* __restrict__ idx_q, const float* __restrict__ idx_w, const uint8_t* __restrict__ kcodes,
     const uint8_t* __restrict__ kscales, float* __restrict__ scores, int64_t stride) {
   __shared__ __attribute__((aligned(16))) uint8_t c_s[kMxRows * kMxRowB];
-  __shared__ __attribute__((aligned(16))) float q_s[kMaxIndexHeads][kIndexDim];
-  __shared__ float w_s[kMaxIndexHeads];
-  __shared__ int64_t row_s[kMxRows];
-
+  __shared__ __attribute__((aligned(16))) float q_s[ONE ? 1 : kMaxIndexHeads][kIndexDim];
+  __shared__ float w_s[ONE ? 1 : kMaxIndexHeads];
   const int b = blockIdx.y;
   const int t = threadIdx.x;
   const int md = mode[b];
   if (md != CSA2_MODE_FULL && md != CSA2_MODE_REINDEX) return;
+  if (ONE) hi = 1;
   const int64_t nv = n_valid_of(pos[b], ratio[b], md, pool_len[b]);
   int64_t n = (md == CSA2_MODE_FULL) ? nv : (cand_off[b + 1] - cand_off[b]);
   if (n > max_cand) n = max_cand;
   const int64_t j0 = (int64_t)blockIdx.x * kMxRows;
   if (j0 >= n) return;
 
+  // candidate c of this workgroup -> its pool row, -1 when there is none
+  const int64_t coff = (md == CSA2_MODE_REINDEX) ? cand_off[b] : 0;
+  auto row_of = [&](int c) -> int64_t {
+    const int64_t jj = j0 + c;
+    if (jj >= n) return -1;
+    const int64_t rr = (md == CSA2_MODE_FULL) ? jj : (int64_t)cand_idx[coff + jj];
+    return (rr >= 0 && rr < nv) ? rr : -1;
+  };
   const int64_t j = j0 + t;
-  int64_t my_row = -1;  // this thread's candidate row (pool-relative), -1 when there is none
-  if (j < n) {
-    const int64_t rr = (md == CSA2_MODE_FULL) ? j : (int64_t)cand_idx[cand_off[b] + j];
-    if (rr >= 0 && rr < nv) my_row = rr;
-  }
-  row_s[t] = my_row;
-  for (int x = t; x < hi * kIndexDim; x += kThreads) q_s[x / kIndexDim][x % kIndexDim] = idx_q[(int64_t)b * hi * kIndexDim + x];
-  if (t < hi) w_s[t] = idx_w ? idx_w[(int64_t)b * hi + t] : 1.0f;
+  const int64_t my_row = row_of(t);
   const int64_t prow0 = pool_row0[b];
-  const uint32_t sc4 = (my_row >= 0) ? *reinterpret_cast<const uint32_t*>(kscales + (prow0 + my_row) * kMxScales)
-                                     : 0u;
-  __syncthreads();
-
-  // code rows: four threads per 64-byte row, 64 rows per pass
+  // every global load of the workgroup is issued before its one barrier: the
+  // code rows (four threads per 64-byte row, a quarter of the rows per pass),
+  // this thread's four scale bytes, and q
   uint4 v[4];
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
-    const int r = it * 64 + (t >> 2), u = t & 3;
-    const int64_t rr = row_s[r];
+    const int r = it * (kMxRows / 4) + (t >> 2), u = t & 3;
+    const int64_t rr = row_of(r);
     v[it] = (rr >= 0) ? *reinterpret_cast<const uint4*>(kcodes + (prow0 + rr) * kMxRowB + u * 16)
                       : make_uint4(0u, 0u, 0u, 0u);
   }
+  const uint32_t sc4 = (my_row >= 0) ? *reinterpret_cast<const uint32_t*>(kscales + (prow0 + my_row) * kMxScales)
+                                     : 0u;
+  for (int x = t; x < hi * kIndexDim; x += kMxThreads)
+    q_s[x / kIndexDim][x % kIndexDim] = idx_q[(int64_t)b * hi * kIndexDim + x];
+  if (t < hi) w_s[t] = idx_w ? idx_w[(int64_t)b * hi + t] : 1.0f;
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
-    const int r = it * 64 + (t >> 2), u = t & 3;
+    const int r = it * (kMxRows / 4) + (t >> 2), u = t & 3;
     *reinterpret_cast<uint4*>(&c_s[r * kMxRowB + mx_unit_swz(r, u) * 16]) = v[it];
   }
   __syncthreads();
   if (j >= n) return;
   float sc = -__builtin_inff();
-  if (my_row >= 0) {
+  if (ONE && my_row >= 0) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {  // unit u = dims 32u .. 32u+31 = scale block u
+      const uint4 c = *reinterpret_cast<const uint4*>(&c_s[t * kMxRowB + mx_unit_swz(t, u) * 16]);
+      const uint32_t e = (sc4 >> (8 * u)) & 0xffu;
+      const float scale = e ? __uint_as_float(e << 23) : __uint_as_float(0x00400000u);
+      const uint32_t wds[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd) {
+        float kv[8];
+        fp4x8_to_f32x8(wds[wd], kv);
+#pragma unroll
+        for (int e2 = 0; e2 < 8; ++e2) acc = __builtin_fmaf(q_s[0][32 * u + 8 * wd + e2], kv[e2] * scale, acc);
+      }
+    }
+    if (relu) acc = acc > 0.0f ? acc : 0.0f;
+    const float s = __builtin_fmaf(w_s[0], acc, 0.0f);
+    sc = (s == 0.0f) ? 0.0f : s;
+  } else if (!ONE && my_row >= 0) {
     // widen the row: unit u holds dims 32u .. 32u+31, the block of scale byte u
     float k[kIndexDim];
 #pragma unroll
@@ -315,9 +342,14 @@ hipError_t launch_index_scores(const csa2_dims& d, int32_t B, const csa2_batch& 
   if (d.index_key_dtype == CSA2_IDXK_MXFP4) {
     dim3 grid((bt.max_candidates + kMxRows - 1) / kMxRows, B);
     const uint8_t* kc = static_cast<const uint8_t*>(idx_k_v);
-    hipLaunchKernelGGL(index_scores_decode_mx, grid, dim3(kThreads), 0, s, hi, d.index_relu, bt.max_candidates,
-                       bt.pos, bt.mode, bt.compress_ratio, bt.pool_row0, bt.pool_len, bt.cand_off, bt.cand_idx,
-                       idx_q, idx_w, kc, idx_k_scale, scores, stride);
+    if (hi == 1)
+      hipLaunchKernelGGL(index_scores_decode_mx<true>, grid, dim3(kMxThreads), 0, s, hi, d.index_relu,
+                         bt.max_candidates, bt.pos, bt.mode, bt.compress_ratio, bt.pool_row0, bt.pool_len,
+                         bt.cand_off, bt.cand_idx, idx_q, idx_w, kc, idx_k_scale, scores, stride);
+    else
+      hipLaunchKernelGGL(index_scores_decode_mx<false>, grid, dim3(kMxThreads), 0, s, hi, d.index_relu,
+                         bt.max_candidates, bt.pos, bt.mode, bt.compress_ratio, bt.pool_row0, bt.pool_len,
+                         bt.cand_off, bt.cand_idx, idx_q, idx_w, kc, idx_k_scale, scores, stride);
     return hipGetLastError();
   }
   const float* idx_k = static_cast<const float*>(idx_k_v);
