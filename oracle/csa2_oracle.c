@@ -478,6 +478,66 @@ int csa2o_attend_core(int32_t h, int32_t d, int64_t e, const double *q, const do
 }
 
 /* ------------------------------------------------------------------------- */
+/* Hierarchical candidate pool ([RN] 3f C3; [PLLM] "The CSA2 attention         */
+/* layers", select_candidate_blocks): the Full layer's scores over the n       */
+/* reachable entries are grouped into blocks of bs consecutive entries; a      */
+/* block scores its best member; the pool is the top_blocks best blocks under  */
+/* (block score descending, block index ascending), except that a block still  */
+/* being filled (the last one, when n is not a multiple of bs) is always in    */
+/* and takes one of the top_blocks places.  Output: the reachable entries of   */
+/* the chosen blocks in ascending order, then -1 up to top_blocks * bs.        */
+/* ------------------------------------------------------------------------- */
+typedef struct {
+  float s;
+  int64_t blk;
+} blk_t;
+
+static int by_block_score(const void *a, const void *b) {
+  const blk_t *x = (const blk_t *)a, *y = (const blk_t *)b;
+  if (x->s > y->s) return -1;
+  if (x->s < y->s) return 1;
+  return (x->blk < y->blk) ? -1 : (x->blk > y->blk);
+}
+
+static int by_block_index(const void *a, const void *b) {
+  const blk_t *x = (const blk_t *)a, *y = (const blk_t *)b;
+  return (x->blk < y->blk) ? -1 : (x->blk > y->blk);
+}
+
+int csa2o_candidate_pool(const float *scores, int64_t n, int32_t bs, int32_t top_blocks, int32_t *out) {
+  int64_t nblk, b, i, take, o = 0, nsort;
+  int pinned;
+  blk_t *v;
+  if (n < 0 || bs < 1 || top_blocks < 1 || (n > 0 && !scores) || !out) return ORC_EBADARG;
+  for (i = 0; i < n; ++i)
+    if (isnan(scores[i])) return ORC_ENONFINITE;
+  nblk = (n + bs - 1) / bs;
+  pinned = (n % bs) != 0;
+  v = (blk_t *)malloc(sizeof(blk_t) * (size_t)(nblk > 0 ? nblk : 1));
+  if (!v) return ORC_ENOMEM;
+  for (b = 0; b < nblk; ++b) {
+    float m = -INFINITY;
+    for (i = b * bs; i < (b + 1) * bs && i < n; ++i)
+      if (scores[i] > m) m = scores[i];
+    v[b].s = m;
+    v[b].blk = b;
+  }
+  /* rank every block but the pinned one; the pinned block is the last */
+  nsort = pinned ? nblk - 1 : nblk;
+  qsort(v, (size_t)nsort, sizeof(blk_t), by_block_score);
+  take = (int64_t)top_blocks - (pinned ? 1 : 0);
+  if (take > nsort) take = nsort;
+  if (take < 0) take = 0;
+  if (pinned) v[take++] = v[nsort]; /* the pinned block: last, never sorted */
+  qsort(v, (size_t)take, sizeof(blk_t), by_block_index);
+  for (b = 0; b < take; ++b)
+    for (i = v[b].blk * bs; i < (v[b].blk + 1) * bs && i < n; ++i) out[o++] = (int32_t)i;
+  while (o < (int64_t)top_blocks * bs) out[o++] = -1;
+  free(v);
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------- */
 /* O5 + O6 + O7 for one query: the entries are the win_len window rows (raw    */
 /* KV) followed by the selected pool rows (compressed KV); one softmax runs    */
 /* over their concatenation ([RN] 3f C2 Step 3; [WASTE] 1. CSA2).  The KV      */

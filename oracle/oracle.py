@@ -49,6 +49,8 @@ def lib():
             f.restype = C.c_int
         L.csa2o_dequant_mxfp4.argtypes = [P, P, i64, P]
         L.csa2o_dequant_mxfp4.restype = C.c_int
+        L.csa2o_candidate_pool.argtypes = [P, i64, i32, i32, P]
+        L.csa2o_candidate_pool.restype = C.c_int
         L.csa2o_n_valid.argtypes = [i64, i32, i32, i64]
         L.csa2o_n_valid.restype = i64
         L.csa2o_window_range.argtypes = [i64, i32, i64, C.POINTER(i64), C.POINTER(i64)]
@@ -253,6 +255,15 @@ def select_query(mode, pos, ratio, pool_len, idx_q, idx_k, k, idx_w=None, relu=F
     _check(lib().csa2o_select_query(int(mode), int(pos), int(ratio), int(pool_len), h_i, d_i,
                                     _ptr(idx_q), _ptr(idx_w), int(bool(relu)), _ptr(idx_k), _ptr(cand),
                                     0 if cand is None else cand.shape[0], int(k), _ptr(out), None))
+    return out
+
+
+def candidate_pool(scores, block_size=8, top_blocks=2048):
+    """Hierarchical candidate pool of one query from its Full-layer scores over
+    its reachable entries: int32 [top_blocks * block_size], ascending, -1 padded."""
+    s = _c(scores, np.float32)
+    out = np.empty(top_blocks * block_size, np.int32)
+    _check(lib().csa2o_candidate_pool(_ptr(s), s.size, int(block_size), int(top_blocks), _ptr(out)))
     return out
 
 

@@ -551,3 +551,69 @@ def test_mxfp4_index_keys_equal_their_decoded_fp32_keys():
     f32 = dict(inp, idx_k=dec)
     a, b = O.decode_batch(mx), O.decode_batch(f32)
     assert all(np.array_equal(u, v) for u, v in zip(a, b))
+
+
+# ---------------------------------------------------------------------------
+# Hierarchical candidate pool ([RN] 3f C3; PocketLLM page, the candidate
+# source layer's select_candidate_blocks and its pinned filling block)
+# ---------------------------------------------------------------------------
+
+def _pool_brute(scores, bs, top):
+    """Brute force: try every set of `top` blocks that contains the filling
+    block (if any) and keep the one whose sorted (score desc, index asc) key
+    list is lexicographically best; small inputs only."""
+    import itertools
+    n = len(scores)
+    nblk = -(-n // bs)
+    best = [max(scores[b * bs:(b + 1) * bs]) for b in range(nblk)]
+    filling = nblk - 1 if n % bs else None
+    others = [b for b in range(nblk) if b != filling]
+    want = min(top - (filling is not None), len(others))
+    chosen = None
+    for comb in itertools.combinations(others, want):
+        key = sorted(((-best[b], b) for b in comb))
+        if chosen is None or key < chosen[0]:
+            chosen = (key, comb)
+    blocks = sorted(list(chosen[1]) + ([filling] if filling is not None else []))
+    pos = [i for b in blocks for i in range(b * bs, min((b + 1) * bs, n))]
+    return pos + [-1] * (top * bs - len(pos))
+
+
+@pytest.mark.parametrize("n,bs,top", [(37, 4, 3), (40, 4, 3), (9, 8, 1), (23, 2, 5), (5, 8, 2), (0, 8, 2)])
+def test_candidate_pool_brute_force(n, bs, top):
+    rng = np.random.default_rng(n * 31 + bs)
+    for trial in range(20):
+        scores = rng.integers(-3, 4, n).astype(np.float32)  # many ties
+        got = O.candidate_pool(scores, bs, top)
+        assert list(got) == _pool_brute(list(scores), bs, top), (trial, scores)
+
+
+def test_candidate_pool_keeps_the_filling_block():
+    # 5 full blocks of 8 and a filling block of 3 whose best score is the lowest of all
+    scores = np.full(43, 1.0, np.float32)
+    scores[40:] = -5.0
+    scores[3] = 9.0
+    got = O.candidate_pool(scores, 8, 2)
+    assert list(got[:8]) == list(range(0, 8))          # the best full block
+    assert list(got[8:11]) == [40, 41, 42]             # the filling block, pinned
+    assert (got[11:] == -1).all()
+    # a full newest block gets no such favour
+    got = O.candidate_pool(scores[:40], 8, 2)
+    assert list(got) == list(range(0, 16))             # ties among full blocks go to the lower index
+
+
+def test_candidate_pool_size_bound_and_saving():
+    # the page's numbers: at most 2,048 blocks of 8 = 16,384 candidates, so at
+    # N = 10^6 a deeper indexer scores 61x fewer entries than a full scan
+    rng = np.random.default_rng(3)
+    scores = rng.standard_normal(100_003).astype(np.float32)
+    got = O.candidate_pool(scores, 8, 2048)
+    v = got[got >= 0]
+    assert len(got) == 16_384 and len(v) == 16_384 - 5 and (np.diff(v) > 0).all()
+    assert round(1e6 / 16_384) == 61
+    # every chosen full block beats every unchosen one
+    blocks = set(v // 8)
+    best = scores[: 100_000].reshape(-1, 8).max(1)
+    chosen_min = min(best[b] for b in blocks if b < 12_500)
+    unchosen_max = max(best[b] for b in range(12_500) if b not in blocks)
+    assert chosen_min >= unchosen_max
