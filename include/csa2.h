@@ -128,7 +128,8 @@ typedef struct csa2_batch {
   const int64_t *pool_row0;      /* first row of the query's pool in comp_kv / idx_k */
   const int32_t *pool_len;       /* rows in that pool */
   const int64_t *cand_off;       /* REINDEX: list of query b is cand_idx[cand_off[b] .. cand_off[b+1]) */
-  const int32_t *cand_idx;       /*   pool-relative rows, strictly ascending; NULL if no REINDEX query */
+  const int32_t *cand_idx;       /*   pool-relative rows, strictly ascending, optionally followed by -1
+                                    padding (never eligible); NULL if no REINDEX query */
   int32_t max_candidates;        /* HOST value: candidates considered per FULL/REINDEX query are
                                     capped at this (use the largest pool_len / list length) */
 } csa2_batch;
@@ -224,6 +225,26 @@ csa2_status csa2_prefill(const csa2_dims *dims, const csa2_prefill_desc *desc, c
                          const uint8_t *comp_scale, int32_t *topk_idx, const float *sink,
                          float *out, float *lse, void *workspace, size_t workspace_bytes,
                          hipStream_t stream);
+
+/* Hierarchical candidate pool (Reading Notes, 3f C3; PocketLLM page, "The
+ * CSA2 attention layers"): from the scores csa2_index_scores wrote for the
+ * FULL queries of a batch (the candidate source layer), each query's reachable
+ * entries are grouped into blocks of block_size consecutive entries; a block
+ * scores its best member; the pool is the top_blocks best blocks under (block
+ * score descending, block index ascending), except that a block still being
+ * filled (the last block, when the entry count n = min(n_valid,
+ * max_candidates) is not a multiple of block_size) is always in the pool and
+ * takes one of its places.  Output, ready to be a REINDEX batch's lists:
+ * cand_off int64 [B+1] = b * top_blocks * block_size, and cand_idx int32
+ * [B][top_blocks * block_size]: the pool's entries in ascending order, then
+ * -1 (a query that is not FULL gets only -1).  Scores must not be NaN.
+ * 1 <= block_size <= 64, 1 <= top_blocks <= 65536; workspace from
+ * csa2_candidate_pool_workspace_size. */
+csa2_status csa2_candidate_pool_workspace_size(int32_t B, int32_t max_candidates, int32_t block_size,
+                                               int32_t top_blocks, size_t *bytes);
+csa2_status csa2_candidate_pool(int32_t B, const csa2_batch *batch, const float *scores, int64_t score_stride,
+                                int32_t block_size, int32_t top_blocks, int64_t *cand_off, int32_t *cand_idx,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* The cache writer's quantizers (Reading Notes, 3f C4; PocketLLM page, "The
  * CSA2 attention layers" and its FP4 quantizer notes).  Both read n_rows rows

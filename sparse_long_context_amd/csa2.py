@@ -53,7 +53,8 @@ class PrefillDesc(C.Structure):
 _lib = None
 EXPORTS = ["csa2_abi_version", "csa2_status_str", "csa2_last_hip_error", "csa2_workspace_size",
            "csa2_index_scores", "csa2_topk", "csa2_attend", "csa2_decode", "csa2_prefill_workspace_size",
-           "csa2_prefill", "csa2_quantize_fp4_kv", "csa2_quantize_mxfp4"]
+           "csa2_prefill", "csa2_quantize_fp4_kv", "csa2_quantize_mxfp4", "csa2_candidate_pool_workspace_size",
+           "csa2_candidate_pool"]
 
 
 def lib():
@@ -75,6 +76,8 @@ def lib():
         L.csa2_prefill_workspace_size.argtypes = [P, P, C.POINTER(sz)]
         L.csa2_prefill.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]
         L.csa2_quantize_fp4_kv.argtypes = [i64, i32, P, P, P, P]
+        L.csa2_candidate_pool_workspace_size.argtypes = [i32, i32, i32, i32, C.POINTER(sz)]
+        L.csa2_candidate_pool.argtypes = [i32, P, P, i64, i32, i32, P, P, P, sz, P]
         L.csa2_quantize_mxfp4.argtypes = [i64, i32, P, P, P, P]
         for name in EXPORTS[3:]:
             getattr(L, name).restype = C.c_int
@@ -170,6 +173,19 @@ def csa2_quantize_fp4_kv(n_rows, d, src, codes, scales, stream=None):
 def csa2_quantize_mxfp4(n_rows, d, src, codes, scales, stream=None):
     _ok(lib().csa2_quantize_mxfp4(n_rows, d, _p(src), _p(codes), _p(scales), _stream(stream)),
         "csa2_quantize_mxfp4")
+
+
+def csa2_candidate_pool_workspace_size(B, max_candidates, block_size, top_blocks):
+    out = C.c_size_t()
+    _ok(lib().csa2_candidate_pool_workspace_size(B, max_candidates, block_size, top_blocks, C.byref(out)),
+        "csa2_candidate_pool_workspace_size")
+    return out.value
+
+
+def csa2_candidate_pool(B, batch, scores, score_stride, block_size, top_blocks, cand_off, cand_idx, workspace,
+                        workspace_bytes, stream=None):
+    _ok(lib().csa2_candidate_pool(B, C.byref(batch), _p(scores), score_stride, block_size, top_blocks, _p(cand_off),
+                                  _p(cand_idx), _p(workspace), workspace_bytes, _stream(stream)), "csa2_candidate_pool")
 
 
 # ---- device-resident workloads (torch used for memory only) -------------------

@@ -318,6 +318,36 @@ csa2_status csa2_prefill(const csa2_dims* dims, const csa2_prefill_desc* desc, c
                        desc->mode == CSA2_MODE_WINDOW ? nullptr : topk_idx, sink, out, lse, partial, sp, stream);
 }
 
+static csa2_status check_pool_args(int32_t B, int32_t max_cand, int32_t bs, int32_t top_blocks) {
+  if (B < 0 || max_cand < 0 || bs < 1 || bs > 64 || top_blocks < 1 || top_blocks > 65536)
+    return CSA2_ERR_INVALID_ARG;
+  return CSA2_OK;
+}
+
+csa2_status csa2_candidate_pool_workspace_size(int32_t B, int32_t max_candidates, int32_t block_size,
+                                               int32_t top_blocks, size_t* bytes) {
+  csa2_status st = check_pool_args(B, max_candidates, block_size, top_blocks);
+  if (st != CSA2_OK) return st;
+  if (!bytes) return CSA2_ERR_INVALID_ARG;
+  *bytes = candidate_pool_ws_bytes(B, max_candidates, block_size, top_blocks);
+  return CSA2_OK;
+}
+
+csa2_status csa2_candidate_pool(int32_t B, const csa2_batch* batch, const float* scores, int64_t score_stride,
+                                int32_t block_size, int32_t top_blocks, int64_t* cand_off, int32_t* cand_idx,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  csa2_status st = check_batch(batch, B);
+  if (st != CSA2_OK) return st;
+  if ((st = check_pool_args(B, batch ? batch->max_candidates : 0, block_size, top_blocks)) != CSA2_OK) return st;
+  if (B == 0) return CSA2_OK;
+  if (!cand_off || !cand_idx || (batch->max_candidates > 0 && !scores) || score_stride < batch->max_candidates)
+    return CSA2_ERR_INVALID_ARG;
+  const size_t need = candidate_pool_ws_bytes(B, batch->max_candidates, block_size, top_blocks);
+  if (!workspace || workspace_bytes < need) return CSA2_ERR_WORKSPACE;
+  return hip_status(launch_candidate_pool(B, *batch, scores, score_stride, block_size, top_blocks, cand_off, cand_idx,
+                                          workspace, stream));
+}
+
 csa2_status csa2_quantize_fp4_kv(int64_t n_rows, int32_t d, const float* src, uint8_t* codes, uint8_t* scales,
                                  hipStream_t stream) {
   if (n_rows < 0 || d <= 0 || (d % 16) != 0) return CSA2_ERR_INVALID_ARG;

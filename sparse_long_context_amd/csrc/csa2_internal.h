@@ -65,6 +65,14 @@ hipError_t launch_index_scores_prefill(const csa2_dims& d, int32_t T, const int6
                                        int64_t stride, hipStream_t s);
 hipError_t launch_topk(const csa2_dims& d, int32_t B, const csa2_batch& bt, const float* scores,
                        int64_t stride, int32_t* topk_idx, hipStream_t s);
+// The same selection with an explicit K (any K >= 1).
+hipError_t launch_topk_k(int32_t K, int32_t B, const csa2_batch& bt, const float* scores, int64_t stride,
+                         int32_t* topk_idx, hipStream_t s);
+// Hierarchical candidate pool of FULL queries (workspace: candidate_pool_ws_bytes).
+size_t candidate_pool_ws_bytes(int32_t B, int32_t max_cand, int32_t block_size, int32_t top_blocks);
+hipError_t launch_candidate_pool(int32_t B, const csa2_batch& bt, const float* scores, int64_t stride,
+                                 int32_t block_size, int32_t top_blocks, int64_t* cand_off, int32_t* cand_idx,
+                                 void* ws, hipStream_t s);
 // n_split > 1 needs `partial` (see attend_partial_floats).
 hipError_t launch_attend(const csa2_dims& d, int32_t B, const csa2_batch& bt, const void* q,
                          const void* win_kv, const uint8_t* win_scale, const void* comp_kv,

@@ -397,13 +397,17 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
 
 }  // namespace
 
+hipError_t launch_topk_k(int32_t K, int32_t B, const csa2_batch& bt, const float* scores, int64_t stride,
+                         int32_t* topk_idx, hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_kernel, dim3(B), dim3(kThreads), 0, s, K, bt.max_candidates, bt.pos, bt.mode,
+                     bt.compress_ratio, bt.pool_len, bt.cand_off, bt.cand_idx, scores, stride, topk_idx);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk(const csa2_dims& d, int32_t B, const csa2_batch& bt, const float* scores,
                        int64_t stride, int32_t* topk_idx, hipStream_t s) {
-  if (B == 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_kernel, dim3(B), dim3(kThreads), 0, s, d.index_topk, bt.max_candidates, bt.pos,
-                     bt.mode, bt.compress_ratio, bt.pool_len, bt.cand_off, bt.cand_idx, scores, stride,
-                     topk_idx);
-  return hipGetLastError();
+  return launch_topk_k(d.index_topk, B, bt, scores, stride, topk_idx, s);
 }
 
 }  // namespace csa2

@@ -153,3 +153,21 @@ def test_storage_format_arguments_are_validated():
                 fn(*args, stream=0)
             assert e.value.status == csa2.CSA2_ERR_INVALID_ARG, (fn, args)
         fn(0, 64, None, None, None, stream=0)
+
+
+def test_candidate_pool_arguments_are_validated():
+    E = csa2.Csa2Error
+    for args in ((4, 100, 0, 8), (4, 100, 65, 8), (4, 100, 8, 0), (4, 100, 8, 65537), (-1, 100, 8, 8), (4, -1, 8, 8)):
+        with pytest.raises(E) as e:
+            csa2.csa2_candidate_pool_workspace_size(*args)
+        assert e.value.status == csa2.CSA2_ERR_INVALID_ARG, args
+    assert csa2.csa2_candidate_pool_workspace_size(4, 100, 8, 16) > 0
+    with pytest.raises(E) as e:  # no output lists
+        csa2.csa2_candidate_pool(2, batch(), FAKE, 16, 8, 16, None, FAKE, FAKE, 1 << 20, stream=0)
+    assert e.value.status == csa2.CSA2_ERR_INVALID_ARG
+    with pytest.raises(E) as e:  # stride below max_candidates
+        csa2.csa2_candidate_pool(2, batch(), FAKE, 15, 8, 16, FAKE, FAKE, FAKE, 1 << 20, stream=0)
+    assert e.value.status == csa2.CSA2_ERR_INVALID_ARG
+    with pytest.raises(E) as e:  # workspace too small
+        csa2.csa2_candidate_pool(2, batch(), FAKE, 16, 8, 16, FAKE, FAKE, FAKE, 16, stream=0)
+    assert e.value.status == csa2.CSA2_ERR_WORKSPACE
