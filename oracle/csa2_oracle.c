@@ -478,6 +478,81 @@ int csa2o_attend_core(int32_t h, int32_t d, int64_t e, const double *q, const do
 }
 
 /* ------------------------------------------------------------------------- */
+/* Compressor ([RN] 3f C2 Step 1: each block of m consecutive tokens becomes   */
+/* one entry, sum_u softmax_u(g_u) (.) c_u, the softmax over the block's tokens */
+/* taken per channel; [PLLM] "The compressor": pooled in fp32, then RMS-normed; */
+/* at ratio 1 there is no gate).  c and g are [n_groups * m][d] (g unused when  */
+/* m == 1); out[j] = RMSNorm(pooled_j) = pooled / sqrt(mean(pooled^2) + eps)   */
+/* (.) w, computed in double and rounded to fp32.                               */
+/* ------------------------------------------------------------------------- */
+int csa2o_compress(int64_t n_groups, int32_t m, int32_t d, const float *c, const float *g, const float *w,
+                   double eps, float *out) {
+  int64_t j;
+  int i, u;
+  double *pooled;
+  if (n_groups < 0 || m < 1 || d < 1 || eps < 0.0 || (n_groups > 0 && (!c || !w || !out || (m > 1 && !g))))
+    return ORC_EBADARG;
+  pooled = (double *)malloc(sizeof(double) * (size_t)d);
+  if (!pooled) return ORC_ENOMEM;
+  for (j = 0; j < n_groups; ++j) {
+    double ss = 0.0, r;
+    for (i = 0; i < d; ++i) {
+      if (m == 1) {
+        pooled[i] = (double)c[(size_t)j * (size_t)d + (size_t)i];
+      } else {
+        double mx = -INFINITY, z = 0.0, acc = 0.0;
+        for (u = 0; u < m; ++u) {
+          const double gu = (double)g[((size_t)j * (size_t)m + (size_t)u) * (size_t)d + (size_t)i];
+          if (gu > mx) mx = gu;
+        }
+        for (u = 0; u < m; ++u) {
+          const size_t at = ((size_t)j * (size_t)m + (size_t)u) * (size_t)d + (size_t)i;
+          const double e = exp((double)g[at] - mx);
+          z += e;
+          acc += e * (double)c[at];
+        }
+        pooled[i] = acc / z;
+      }
+      if (!isfinite(pooled[i])) {
+        free(pooled);
+        return ORC_ENONFINITE;
+      }
+      ss += pooled[i] * pooled[i];
+    }
+    r = 1.0 / sqrt(ss / (double)d + eps);
+    for (i = 0; i < d; ++i) out[(size_t)j * (size_t)d + (size_t)i] = (float)(pooled[i] * r * (double)w[i]);
+  }
+  free(pooled);
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Output de-rotation ([WASTE] "What is new", 1. CSA2: the rope dims of the    */
+/* attention output are rotated by the conjugate of the query's rotation).     */
+/* Each head's dims rope_off + 2i, rope_off + 2i + 1 (i < rope_dims / 2) form  */
+/* a pair rotated by -pos * inv_freq[i]:                                        */
+/*   (x, y) -> (x cos a + y sin a, -x sin a + y cos a),  a = pos * inv_freq[i]. */
+/* The frequency table is the caller's (plain RoPE or a YaRN-scaled schedule). */
+/* out [n_heads][d] is rotated in place (double arithmetic, rounded to fp32).  */
+/* ------------------------------------------------------------------------- */
+int csa2o_derotate(int32_t n_heads, int32_t d, int32_t rope_off, int32_t rope_dims, const double *inv_freq,
+                   int64_t pos, float *out) {
+  int h, i;
+  if (n_heads < 1 || d < 1 || rope_off < 0 || rope_dims < 0 || (rope_dims % 2) != 0 || rope_off + rope_dims > d ||
+      (rope_dims > 0 && !inv_freq) || !out)
+    return ORC_EBADARG;
+  for (h = 0; h < n_heads; ++h)
+    for (i = 0; i < rope_dims / 2; ++i) {
+      float *p = out + (size_t)h * (size_t)d + (size_t)rope_off + 2 * (size_t)i;
+      const double a = (double)pos * inv_freq[i];
+      const double x = p[0], y = p[1], cs = cos(a), sn = sin(a);
+      p[0] = (float)(x * cs + y * sn);
+      p[1] = (float)(-x * sn + y * cs);
+    }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------- */
 /* Hierarchical candidate pool ([RN] 3f C3; [PLLM] "The CSA2 attention         */
 /* layers", select_candidate_blocks): the Full layer's scores over the n       */
 /* reachable entries are grouped into blocks of bs consecutive entries; a      */

@@ -49,6 +49,10 @@ def lib():
             f.restype = C.c_int
         L.csa2o_dequant_mxfp4.argtypes = [P, P, i64, P]
         L.csa2o_dequant_mxfp4.restype = C.c_int
+        L.csa2o_compress.argtypes = [i64, i32, i32, P, P, P, dbl, P]
+        L.csa2o_compress.restype = C.c_int
+        L.csa2o_derotate.argtypes = [i32, i32, i32, i32, P, i64, P]
+        L.csa2o_derotate.restype = C.c_int
         L.csa2o_candidate_pool.argtypes = [P, i64, i32, i32, P]
         L.csa2o_candidate_pool.restype = C.c_int
         L.csa2o_n_valid.argtypes = [i64, i32, i32, i64]
@@ -256,6 +260,27 @@ def select_query(mode, pos, ratio, pool_len, idx_q, idx_k, k, idx_w=None, relu=F
                                     _ptr(idx_q), _ptr(idx_w), int(bool(relu)), _ptr(idx_k), _ptr(cand),
                                     0 if cand is None else cand.shape[0], int(k), _ptr(out), None))
     return out
+
+
+def compress(c, g, w, m, eps=1e-20):
+    """Compressor over n_groups * m tokens: c, g f32 [n_groups * m, d] (g None
+    for m == 1), w f32 [d] -> f32 [n_groups, d]."""
+    c = _c(c, np.float32)
+    g = _c(g, np.float32)
+    w = _c(w, np.float32)
+    d = c.shape[-1]
+    n = c.shape[0] // m
+    out = np.empty((n, d), np.float32)
+    _check(lib().csa2o_compress(n, int(m), d, _ptr(c), _ptr(g), _ptr(w), float(eps), _ptr(out)))
+    return out
+
+
+def derotate(out_h_d, pos, inv_freq, rope_off=448, rope_dims=64):
+    """De-rotate one query's output [H, D] (copy returned)."""
+    o = np.array(out_h_d, np.float32, copy=True, order="C")
+    f = _c(inv_freq, np.float64)
+    _check(lib().csa2o_derotate(o.shape[0], o.shape[1], int(rope_off), int(rope_dims), _ptr(f), int(pos), _ptr(o)))
+    return o
 
 
 def candidate_pool(scores, block_size=8, top_blocks=2048):

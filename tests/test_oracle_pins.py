@@ -617,3 +617,65 @@ def test_candidate_pool_size_bound_and_saving():
     chosen_min = min(best[b] for b in blocks if b < 12_500)
     unchosen_max = max(best[b] for b in range(12_500) if b not in blocks)
     assert chosen_min >= unchosen_max
+
+
+# ---------------------------------------------------------------------------
+# Compressor ([RN] 3f C2 Step 1) and output de-rotation (WASTE page, 1. CSA2)
+# ---------------------------------------------------------------------------
+
+def _rms(x, w, eps):
+    x = np.asarray(x, np.float64)
+    return x / np.sqrt(np.mean(x * x) + eps) * w
+
+
+def test_compressor_worked_example():
+    ex = gold("compress_example.json")
+    c = np.array(ex["c"], np.float32)
+    # one weight per token: equal gate logits across channels, softmax (0.75, 0.25)
+    g = np.log(np.array(ex["weights"], np.float64))[:, None].repeat(2, 1).astype(np.float32)
+    out = O.compress(c, g, np.ones(2, np.float32), ex["m"], eps=0.0)
+    assert np.allclose(out[0], _rms(ex["pooled"], 1.0, 0.0), rtol=1e-6)
+
+
+def test_compressor_closed_forms():
+    rng = np.random.default_rng(11)
+    d, m = 64, 4
+    c = rng.standard_normal((3 * m, d)).astype(np.float32)
+    w = rng.uniform(0.5, 2, d).astype(np.float32)
+    # equal gates: the mean of the group, then RMSNorm
+    out = O.compress(c, np.zeros_like(c), w, m, eps=1e-6)
+    for j in range(3):
+        assert np.allclose(out[j], _rms(c[j * m:(j + 1) * m].astype(np.float64).mean(0), w, 1e-6), rtol=1e-6, atol=1e-7)
+    # one dominant gate per channel selects that token's channel value
+    g = np.full_like(c, -60.0)
+    pick = rng.integers(0, m, d)
+    for i in range(d):
+        g[pick[i], i] = 60.0
+    out = O.compress(c[:m], g[:m], w, m, eps=1e-6)
+    assert np.allclose(out[0], _rms(c[pick, np.arange(d)], w, 1e-6), rtol=1e-5)
+    # ratio 1: no gate, just the norm; and tokens permuted within a group change nothing
+    assert np.allclose(O.compress(c, None, w, 1, eps=1e-6), np.stack([_rms(x, w, 1e-6) for x in c]), rtol=1e-6, atol=1e-7)
+    gg = rng.standard_normal(c.shape).astype(np.float32)
+    perm = np.concatenate([rng.permutation(m) + j * m for j in range(3)])
+    assert np.allclose(O.compress(c, gg, w, m), O.compress(c[perm], gg[perm], w, m), rtol=1e-6, atol=1e-7)
+
+
+def test_derotation_undoes_the_rotation():
+    rng = np.random.default_rng(12)
+    H, D, off, rd = 4, 512, 448, 64
+    inv = 160000.0 ** (-np.arange(rd // 2) * 2.0 / rd)
+    o = rng.standard_normal((H, D)).astype(np.float32)
+    pos = 123_457
+    # rotate forward here (numpy's own cos/sin), then the oracle de-rotates
+    a = pos * inv
+    x, y = o[:, off::2].astype(np.float64), o[:, off + 1::2].astype(np.float64)
+    fwd = o.astype(np.float64).copy()
+    fwd[:, off::2] = x * np.cos(a) - y * np.sin(a)
+    fwd[:, off + 1::2] = x * np.sin(a) + y * np.cos(a)
+    back = O.derotate(fwd.astype(np.float32), pos, inv, off, rd)
+    assert np.allclose(back, o, atol=2e-6)
+    assert np.array_equal(back[:, :off], o[:, :off])              # other dims untouched
+    assert np.array_equal(O.derotate(o, 0, inv, off, rd), o)       # position 0: identity
+    # a quarter turn maps (x, y) to (y, -x)
+    q = O.derotate(o, 1, np.full(rd // 2, np.pi / 2), off, rd)
+    assert np.allclose(q[:, off::2], o[:, off + 1::2], atol=1e-6) and np.allclose(q[:, off + 1::2], -o[:, off::2], atol=1e-6)
