@@ -246,6 +246,26 @@ csa2_status csa2_candidate_pool(int32_t B, const csa2_batch *batch, const float 
                                 int32_t block_size, int32_t top_blocks, int64_t *cand_off, int32_t *cand_idx,
                                 void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Compressor (Reading Notes, 3f C2 Step 1; PocketLLM page, "The compressor"):
+ * n_groups groups of m consecutive tokens each become one latent.  c and g are
+ * f32 [n_groups * m][d] (the tokens' latents and gate logits; g is ignored and
+ * may be NULL when m == 1); per channel i of group j
+ *   pooled = sum_u softmax_u(g[jm+u][i]) * c[jm+u][i],
+ * then out[j] = pooled / sqrt(mean_i pooled^2 + eps) * norm_w (RMSNorm), f32
+ * [n_groups][d].  fp32 arithmetic.  1 <= d <= 1024, m >= 1, eps >= 0. */
+csa2_status csa2_compress(int64_t n_groups, int32_t m, int32_t d, const float *c, const float *g,
+                          const float *norm_w, float eps, float *out, hipStream_t stream);
+
+/* Output de-rotation ("DeepSeek-V4.1-Flash on WASTE", What is new, 1. CSA2):
+ * for each query b and head, the pairs of dims (rope_offset + 2i, +2i+1),
+ * i < rope_dims / 2, of out [B][64][512] are rotated in place by
+ * -pos[b] * inv_freq[i]:  (x, y) -> (x cos a + y sin a, -x sin a + y cos a).
+ * inv_freq: f64 [rope_dims / 2] (device), the caller's frequency schedule
+ * (plain RoPE theta^(-2i/rope_dims), or a YaRN-scaled one).  pos: device int64
+ * [B].  Angles, sines and cosines in fp64.  rope_dims even, at most 128. */
+csa2_status csa2_derotate(const csa2_dims *dims, int32_t B, const int64_t *pos, int32_t rope_offset,
+                          int32_t rope_dims, const double *inv_freq, float *out, hipStream_t stream);
+
 /* The cache writer's quantizers (Reading Notes, 3f C4; PocketLLM page, "The
  * CSA2 attention layers" and its FP4 quantizer notes).  Both read n_rows rows
  * of d fp32 values (device) and write codes uint8 [n_rows][d/2] (element 2i in

@@ -54,7 +54,7 @@ _lib = None
 EXPORTS = ["csa2_abi_version", "csa2_status_str", "csa2_last_hip_error", "csa2_workspace_size",
            "csa2_index_scores", "csa2_topk", "csa2_attend", "csa2_decode", "csa2_prefill_workspace_size",
            "csa2_prefill", "csa2_quantize_fp4_kv", "csa2_quantize_mxfp4", "csa2_candidate_pool_workspace_size",
-           "csa2_candidate_pool"]
+           "csa2_candidate_pool", "csa2_compress", "csa2_derotate"]
 
 
 def lib():
@@ -78,6 +78,8 @@ def lib():
         L.csa2_quantize_fp4_kv.argtypes = [i64, i32, P, P, P, P]
         L.csa2_candidate_pool_workspace_size.argtypes = [i32, i32, i32, i32, C.POINTER(sz)]
         L.csa2_candidate_pool.argtypes = [i32, P, P, i64, i32, i32, P, P, P, sz, P]
+        L.csa2_compress.argtypes = [i64, i32, i32, P, P, P, C.c_float, P, P]
+        L.csa2_derotate.argtypes = [P, i32, P, i32, i32, P, P, P]
         L.csa2_quantize_mxfp4.argtypes = [i64, i32, P, P, P, P]
         for name in EXPORTS[3:]:
             getattr(L, name).restype = C.c_int
@@ -186,6 +188,16 @@ def csa2_candidate_pool(B, batch, scores, score_stride, block_size, top_blocks, 
                         workspace_bytes, stream=None):
     _ok(lib().csa2_candidate_pool(B, C.byref(batch), _p(scores), score_stride, block_size, top_blocks, _p(cand_off),
                                   _p(cand_idx), _p(workspace), workspace_bytes, _stream(stream)), "csa2_candidate_pool")
+
+
+def csa2_compress(n_groups, m, d, c, g, norm_w, eps, out, stream=None):
+    _ok(lib().csa2_compress(n_groups, m, d, _p(c), _p(g), _p(norm_w), float(eps), _p(out), _stream(stream)),
+        "csa2_compress")
+
+
+def csa2_derotate(dims, B, pos, rope_offset, rope_dims, inv_freq, out, stream=None):
+    _ok(lib().csa2_derotate(C.byref(dims), B, _p(pos), rope_offset, rope_dims, _p(inv_freq), _p(out),
+                            _stream(stream)), "csa2_derotate")
 
 
 # ---- device-resident workloads (torch used for memory only) -------------------

@@ -348,6 +348,27 @@ csa2_status csa2_candidate_pool(int32_t B, const csa2_batch* batch, const float*
                                           workspace, stream));
 }
 
+csa2_status csa2_compress(int64_t n_groups, int32_t m, int32_t d, const float* c, const float* g,
+                          const float* norm_w, float eps, float* out, hipStream_t stream) {
+  if (n_groups < 0 || m < 1 || d < 1 || d > kMaxCompressDim || !(eps >= 0.0f) || !isfinite(eps))
+    return CSA2_ERR_INVALID_ARG;
+  if (n_groups == 0) return CSA2_OK;
+  if (!c || !norm_w || !out || (m > 1 && !g)) return CSA2_ERR_INVALID_ARG;
+  return hip_status(launch_compress(n_groups, m, d, c, g, norm_w, eps, out, stream));
+}
+
+csa2_status csa2_derotate(const csa2_dims* dims, int32_t B, const int64_t* pos, int32_t rope_offset,
+                          int32_t rope_dims, const double* inv_freq, float* out, hipStream_t stream) {
+  csa2_status st = check_dims(dims);
+  if (st != CSA2_OK) return st;
+  if (B < 0 || rope_offset < 0 || rope_dims < 0 || (rope_dims % 2) != 0 || rope_dims > kMaxRopeDims ||
+      rope_offset + rope_dims > kDim)
+    return CSA2_ERR_INVALID_ARG;
+  if (B == 0 || rope_dims == 0) return CSA2_OK;
+  if (!pos || !inv_freq || !out) return CSA2_ERR_INVALID_ARG;
+  return hip_status(launch_derotate(B, pos, rope_offset, rope_dims, inv_freq, out, stream));
+}
+
 csa2_status csa2_quantize_fp4_kv(int64_t n_rows, int32_t d, const float* src, uint8_t* codes, uint8_t* scales,
                                  hipStream_t stream) {
   if (n_rows < 0 || d <= 0 || (d % 16) != 0) return CSA2_ERR_INVALID_ARG;

@@ -12,6 +12,8 @@ constexpr int kHeads = 64;      // query heads sharing one KV row
 constexpr int kDim = 512;       // dims per head and per KV row
 constexpr int kIndexDim = 128;  // indexer key / query width
 constexpr int kMaxIndexHeads = 64;
+constexpr int kMaxCompressDim = 1024;  // widest latent the compressor pools
+constexpr int kMaxRopeDims = 128;      // widest rope part the de-rotation turns
 constexpr int kMaxTopK = 512;
 constexpr int kMaxWindow = 128;
 constexpr int kMaxEntries = kMaxWindow + kMaxTopK;  // 640 rows attended per query at most
@@ -91,6 +93,12 @@ hipError_t launch_quantize_fp4_kv(int64_t n_rows, int32_t d, const float* src, u
                                   hipStream_t s);
 hipError_t launch_quantize_mxfp4(int64_t n_rows, int32_t d, const float* src, uint8_t* codes, uint8_t* scales,
                                  hipStream_t s);
+
+// Compressor (one workgroup per group) and output de-rotation (one per query).
+hipError_t launch_compress(int64_t n_groups, int32_t m, int32_t d, const float* c, const float* g, const float* w,
+                           float eps, float* out, hipStream_t s);
+hipError_t launch_derotate(int32_t B, const int64_t* pos, int32_t rope_off, int32_t rope_dims,
+                           const double* inv_freq, float* out, hipStream_t s);
 
 // Per-query descriptors of a prefill chunk, written into workspace arrays.
 hipError_t launch_prefill_meta(const csa2_prefill_desc& p, int32_t window, int64_t* pos, int32_t* mode,

@@ -171,3 +171,27 @@ def test_candidate_pool_arguments_are_validated():
     with pytest.raises(E) as e:  # workspace too small
         csa2.csa2_candidate_pool(2, batch(), FAKE, 16, 8, 16, FAKE, FAKE, FAKE, 16, stream=0)
     assert e.value.status == csa2.CSA2_ERR_WORKSPACE
+
+
+def test_compress_and_derotate_arguments_are_validated():
+    E = csa2.Csa2Error
+    for args in ((4, 0, 512), (4, 2, 0), (4, 2, 1025), (-1, 2, 512)):
+        with pytest.raises(E) as e:
+            csa2.csa2_compress(*args, FAKE, FAKE, FAKE, 1e-6, FAKE, stream=0)
+        assert e.value.status == csa2.CSA2_ERR_INVALID_ARG, args
+    for bad in ((FAKE, None, FAKE, FAKE), (None, FAKE, FAKE, FAKE), (FAKE, FAKE, None, FAKE), (FAKE, FAKE, FAKE, None)):
+        with pytest.raises(E) as e:
+            csa2.csa2_compress(4, 2, 512, bad[0], bad[1], bad[2], 1e-6, bad[3], stream=0)
+        assert e.value.status == csa2.CSA2_ERR_INVALID_ARG
+    with pytest.raises(E) as e:
+        csa2.csa2_compress(4, 2, 512, FAKE, FAKE, FAKE, -1.0, FAKE, stream=0)
+    assert e.value.status == csa2.CSA2_ERR_INVALID_ARG
+    csa2.csa2_compress(0, 2, 512, None, None, None, 1e-6, None, stream=0)
+    d = dims()
+    for args in ((2, 448, 63), (2, 449, 64), (2, 0, 130), (2, -1, 64), (-1, 448, 64)):
+        with pytest.raises(E) as e:
+            csa2.csa2_derotate(d, args[0], FAKE, args[1], args[2], FAKE, FAKE, stream=0)
+        assert e.value.status == csa2.CSA2_ERR_INVALID_ARG, args
+    with pytest.raises(E) as e:
+        csa2.csa2_derotate(d, 2, None, 448, 64, FAKE, FAKE, stream=0)
+    assert e.value.status == csa2.CSA2_ERR_INVALID_ARG

@@ -1,0 +1,66 @@
+"""GPU parity of the compressor (Reading Notes of DeepSeek-V4.1-Flash, 3f C2
+Step 1) and of the output de-rotation ("DeepSeek-V4.1-Flash on WASTE", 1.
+CSA2) against the oracle.
+
+Compressor: fp32 on the GPU against fp64 in the oracle; per group the
+normwise error max|o - o_ref| / max|o_ref| must stay below 1e-5 (a fast exp
+with a few ulps of error, sums of at most m terms and one reciprocal square
+root, all well below that).  De-rotation: fp64 angles and rotation on both
+sides, so the outputs agree to within one fp32 rounding (2e-7 relative).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import oracle as O  # noqa: E402
+from sparse_long_context_amd import csa2, synth  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[gpu-epilogue]", *a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    csa2.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("m,d,n", [(1, 512, 300), (2, 512, 1000), (4, 512, 257), (128, 512, 9), (3, 96, 50)])
+def test_compressor_matches_oracle(m, d, n):
+    c = synth.normal_f32(51, 1, (n * m, d), scale=2.0)
+    g = synth.normal_f32(51, 2, (n * m, d), scale=3.0)
+    w = synth.normal_f32(51, 3, (d,))
+    say(f"compress m={m} d={d} groups={n}")
+    ct, gt, wt = (torch.from_numpy(x).cuda() for x in (c, g, w))
+    out = torch.empty((n, d), dtype=torch.float32, device="cuda")
+    csa2.csa2_compress(n, m, d, ct, gt, wt, 1e-20, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    want = O.compress(c, g if m > 1 else None, w, m, eps=1e-20)
+    err = np.abs(got - want).max(1) / np.abs(want).max(1)
+    assert err.max() <= 1e-5, err.max()
+
+
+def test_derotation_matches_oracle():
+    B = 7
+    pos = np.array([0, 1, 127, 65_535, 131_071, 1_000_000 - 1, 4_000_000], np.int64)
+    out = synth.normal_f32(52, 1, (B, 64, 512))
+    inv = 160000.0 ** (-np.arange(32) * 2.0 / 64)
+    ot = torch.from_numpy(out).cuda()
+    dims = csa2.Dims.from_dict(synth.default_dims())
+    csa2.csa2_derotate(dims, B, torch.from_numpy(pos).cuda(), 448, 64, torch.from_numpy(inv).cuda(), ot)
+    torch.cuda.synchronize()
+    got = ot.cpu().numpy()
+    for b in range(B):
+        want = O.derotate(out[b], pos[b], inv, 448, 64)
+        assert np.abs(got[b] - want).max() <= 2e-7 * np.abs(want).max()
+        assert np.array_equal(got[b][:, :448], out[b][:, :448])
