@@ -211,7 +211,7 @@ def main():
     # per-kernel durations: each of the three stage entry points launched
     # `steps` times back to back between two HIP events on the launch stream
     # (the same kernels and launch shapes csa2_decode issues)
-    stride = w.max_cand
+    stride = (w.max_cand + 63) // 64 * 64  # the row stride csa2_decode uses for its own score buffer
     scores = torch.empty((B, stride), dtype=torch.float32, device="cuda")
     stages = [
         lambda: csa2.csa2_index_scores(w.dims, B, w.batch, w.idx_q, w.idx_w, w.idx_k, scores, stride,

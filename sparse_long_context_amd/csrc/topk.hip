@@ -5,33 +5,35 @@
 // Order: score descending, then row ascending (the lowest row wins a tie); +0
 // and -0 tie.  Output: the chosen rows in ascending order, then -1s.
 //
-// One workgroup (1024 threads, 16 waves) per query.  Scores map to
-// order-preserving 32-bit keys; ineligible slots get key 0, below every finite
-// score and -inf.  Up to 16,384 candidates the keys live in registers (thread t
-// holds the contiguous run [t*kpt, t*kpt+kpt)), and the selection is:
-//  1. one LDS histogram of the top 12 key bits and a block-wide suffix scan
+// One workgroup of NT threads per query.  Scores map to order-preserving
+// 32-bit keys; ineligible slots get key 0, below every finite score and -inf.
+// The list is read in segments of NT * KPT keys, thread t holding the
+// contiguous run [t*KPT, t*KPT+KPT) of a segment in registers; a list of one
+// segment stays in registers throughout, a longer one is re-read from the
+// score buffer (just written, so from cache) in each pass:
+//  1. an LDS histogram of the top 12 key bits and a block-wide suffix scan
 //     find the bucket that holds the K-th best key and how many keys lie above
 //     it (and the eligible total: at most K eligible means take them all);
 //  2. the keys of that bucket (typically 1-2 % of them) are gathered into LDS
-//     and ranked exactly against each other under (key desc, row asc); the
-//     bucket keys ranked below the remaining quota are marked in an LDS bitmap;
-//  3. compaction: a key is chosen if its bucket lies above the boundary bucket
-//     or it is marked; one block-wide prefix over threads (= index order) of
-//     the per-thread counts places every chosen row.
-// When the boundary bucket is too large to rank (heavy ties), or the list is
-// longer than 16,384, a three-digit radix select (bits 31-20, 19-8, 7-0) finds
-// the exact K-th key instead, with the keys re-read from the score buffer for
-// long lists.
+//     with their indices and ranked exactly against each other under
+//     (key desc, index asc); the one ranked at the remaining quota is the K-th
+//     key overall, (th, idx_lim);
+//  3. compaction: a key is chosen iff key > th, or key == th and its index is
+//     <= idx_lim; a block-wide prefix over threads (= index order) of the
+//     per-thread counts, carried across segments, places every chosen row.
+// When the boundary bucket is too large to rank (heavy ties), a radix select
+// over the two remaining digits (bits 19-8, 7-0) finds the K-th key value and
+// a prefix over the keys equal to it finds its index.
+//
+// Two shapes are built: 1,024 threads x 16 keys (few queries: the lowest
+// latency per query) and 512 x 32 for batches of many queries (a prefill
+// chunk): two independent workgroups per CU, so one workgroup's barriers and
+// LDS round trips hide behind the other's.
 #include "csa2_internal.h"
 
 namespace csa2 {
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / 64;
-constexpr int kMaxKpt = 16;              // keys per thread held in registers
-static_assert(kMaxKpt == 16, "a thread's marks are read as one 16-bit run of a 32-bit word");
-constexpr int kRegKeys = kThreads * kMaxKpt;
 constexpr int kBins = 4096;
 
 __device__ __forceinline__ uint32_t order_key(float s) {
@@ -39,8 +41,6 @@ __device__ __forceinline__ uint32_t order_key(float s) {
   if (u == 0x80000000u) u = 0u;  // -0 ties with +0
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-
-__device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (1ull << lane) - 1ull; }
 
 // Inclusive prefix sum over the 64 lanes of a wave: shifts within each row of
 // 16 lanes, then the last lane of a row is broadcast into the rows above it
@@ -58,6 +58,7 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
 
 // Block-wide exclusive suffix sum (sum over threads with a larger id).  Every
 // call site passes a barrier before red_s is written again.
+template <int kWaves>
 __device__ __forceinline__ uint32_t block_suffix_excl(uint32_t v, uint32_t* red_s, int lane, int wv) {
   const uint32_t inc = wave_incl_scan(v);
   if (lane == 63) red_s[wv] = inc;
@@ -76,6 +77,7 @@ __device__ __forceinline__ uint32_t block_suffix_excl(uint32_t v, uint32_t* red_
 // Block-wide exclusive prefix sums of two values (sum over threads with a
 // smaller id); also returns the totals.  Every call site passes a barrier
 // before red_s is written again.
+template <int kWaves>
 __device__ __forceinline__ void block_prefix2(uint32_t a, uint32_t b, uint32_t* red_s, int lane, int wv,
                                               uint32_t& pa, uint32_t& pb, uint32_t& ta, uint32_t& tb) {
   const uint32_t ia = wave_incl_scan(a), ib = wave_incl_scan(b);
@@ -94,14 +96,15 @@ __device__ __forceinline__ void block_prefix2(uint32_t a, uint32_t b, uint32_t* 
 }
 
 constexpr int kRankCap = 1024;  // boundary-bucket keys ranked directly
-constexpr int kMaxBpt = kBins / kThreads;  // histogram buckets owned per thread (>= 1)
 
 // Find the bucket of an nb-bucket histogram that holds the krem-th largest
 // key: each thread owns a run of consecutive buckets, a block-wide suffix scan
 // gives the count above each run.  pick_s[0] = bucket, pick_s[1] = keys above
 // it, pick_s[2] = all keys counted.  Contains barriers; call uniformly.
+template <int kThreads>
 __device__ __forceinline__ void find_bucket(const uint32_t* hist_s, int nb, uint32_t krem, uint32_t* red_s,
                                             uint32_t* pick_s, int t, int lane, int wv) {
+  constexpr int kMaxBpt = kBins / kThreads;  // histogram buckets owned per thread (>= 1)
   const int bpt = (nb + kThreads - 1) / kThreads;
   uint32_t c[kMaxBpt], tot = 0;
 #pragma unroll
@@ -110,7 +113,7 @@ __device__ __forceinline__ void find_bucket(const uint32_t* hist_s, int nb, uint
     c[u] = (u < bpt && bkt < nb) ? hist_s[bkt] : 0u;
     tot += c[u];
   }
-  uint32_t above = block_suffix_excl(tot, red_s, lane, wv);
+  uint32_t above = block_suffix_excl<kThreads / 64>(tot, red_s, lane, wv);
   if (t == 0) pick_s[2] = above + tot;
 #pragma unroll
   for (int u = kMaxBpt - 1; u >= 0; --u) {
@@ -128,7 +131,7 @@ __device__ __forceinline__ void find_bucket(const uint32_t* hist_s, int nb, uint
 // known prefix; `count_keys(shift, nb, prefix, pmask)` adds the keys matching
 // the prefix into hist_s.  Returns the K-th key and the quota left among keys
 // equal to it.
-template <typename CountFn>
+template <int kThreads, typename CountFn>
 __device__ __forceinline__ void radix_finish(int d0, uint32_t prefix, uint32_t pmask, uint32_t krem,
                                              uint32_t* hist_s, uint32_t* red_s, uint32_t* pick_s, int t,
                                              int lane, int wv, CountFn count_keys, uint32_t& thr,
@@ -142,7 +145,7 @@ __device__ __forceinline__ void radix_finish(int d0, uint32_t prefix, uint32_t p
     __syncthreads();
     count_keys(shift, dm, prefix, pmask);
     __syncthreads();
-    find_bucket(hist_s, nb, krem, red_s, pick_s, t, lane, wv);
+    find_bucket<kThreads>(hist_s, nb, krem, red_s, pick_s, t, lane, wv);
     __syncthreads();
     krem -= pick_s[1];
     prefix |= pick_s[0] << shift;
@@ -153,16 +156,20 @@ __device__ __forceinline__ void radix_finish(int d0, uint32_t prefix, uint32_t p
   take_eq = krem;
 }
 
+template <int kThreads, int kKpt>
 __global__ __launch_bounds__(kThreads) void topk_kernel(
     int32_t K, int32_t max_cand, const int64_t* __restrict__ pos, const int32_t* __restrict__ mode,
     const int32_t* __restrict__ ratio, const int32_t* __restrict__ pool_len,
     const int64_t* __restrict__ cand_off, const int32_t* __restrict__ cand_idx,
     const float* __restrict__ scores, int64_t stride, int32_t* __restrict__ topk_idx) {
+  constexpr int kWaves = kThreads / 64;
+  constexpr int kSeg = kThreads * kKpt;  // keys per segment (one key register set)
+  static_assert(kKpt % 4 == 0, "keys are loaded four at a time");
   __shared__ __attribute__((aligned(16))) uint32_t hist_s[kBins];
   __shared__ uint32_t red_s[2 * kWaves];
   __shared__ uint32_t pick_s[4];
-  __shared__ uint64_t bk_s[kRankCap];           // boundary-bucket (key << 32 | ~index)
-  __shared__ uint32_t mark_s[kRegKeys / 32];    // chosen boundary-bucket keys, by index
+  __shared__ uint64_t bk_s[kRankCap];  // boundary-bucket (key << 32 | ~index)
+  __shared__ uint64_t thr_s;
   __shared__ uint32_t bcount_s;
 
   const int b = blockIdx.x;
@@ -177,231 +184,229 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
   const int32_t* lst = (md == CSA2_MODE_REINDEX) ? cand_idx + cand_off[b] : nullptr;
   const float* sc = scores + (int64_t)b * stride;
   int32_t* out = topk_idx + (int64_t)b * K;
-
-  auto row_of = [&](int i) -> int32_t { return lst ? lst[i] : i; };
-  auto key_global = [&](int i) -> uint32_t {
-    const int32_t r = row_of(i);
-    return (r >= 0 && r < nv) ? order_key(sc[i]) : 0u;
-  };
+  const bool sc_aligned = (reinterpret_cast<uintptr_t>(sc) & 15u) == 0;
   auto pad = [&](uint32_t chosen) {
     if (chosen > (uint32_t)K) chosen = K;
     for (int x = (int)chosen + t; x < K; x += kThreads) out[x] = -1;
   };
 
-  if (n > kRegKeys) {
-    // ---- long lists: full radix select, keys re-read from the score buffer ----
-    uint32_t my_elig = 0;
-    for (int i = t; i < n; i += kThreads) my_elig += (key_global(i) != 0u);
-    const uint32_t incl = block_suffix_excl(my_elig, red_s, lane, wv) + my_elig;
-    if (t == 0) pick_s[2] = incl;
-    __syncthreads();
-    const uint32_t total = pick_s[2];
-    __syncthreads();
-    uint32_t thr = 0, take_eq = 0;
-    if (total > (uint32_t)K)
-      radix_finish(0, 0u, 0u, (uint32_t)K, hist_s, red_s, pick_s, t, lane, wv,
-                   [&](int shift, uint32_t dm, uint32_t prefix, uint32_t pmask) {
-                     for (int i = t; i < n; i += kThreads) {
-                       const uint32_t kk = key_global(i);
-                       if (kk != 0u && (kk & pmask) == prefix) atomicAdd(&hist_s[(kk >> shift) & dm], 1u);
-                     }
-                   },
-                   thr, take_eq);
-    const bool has_eq = thr != 0u;
-    const int seg = ((n + kWaves - 1) / kWaves + 63) & ~63;
-    const int s0 = wv * seg, s1 = (s0 + seg < n) ? s0 + seg : n;
-    uint32_t cnt_gt = 0, cnt_eq = 0;
-    for (int q0 = s0; q0 < s1; q0 += 64) {
-      const int i = q0 + lane;
-      const uint32_t kk = (i < s1) ? key_global(i) : 0u;
-      cnt_gt += __popcll(__ballot(i < s1 && kk > thr));
-      cnt_eq += __popcll(__ballot(i < s1 && has_eq && kk == thr));
-    }
-    uint32_t gt_run, eq_run, gt_tot, eq_tot;
-    block_prefix2(lane == 0 ? cnt_gt : 0u, lane == 0 ? cnt_eq : 0u, red_s, lane, wv, gt_run, eq_run, gt_tot,
-                  eq_tot);
-    gt_run = __shfl(gt_run, 0);
-    eq_run = __shfl(eq_run, 0);
-    for (int q0 = s0; q0 < s1; q0 += 64) {
-      const int i = q0 + lane;
-      const uint32_t kk = (i < s1) ? key_global(i) : 0u;
-      const bool gt = i < s1 && kk > thr;
-      const bool eq = i < s1 && has_eq && kk == thr;
-      const uint64_t bg = __ballot(gt), be = __ballot(eq);
-      const uint32_t gtb = gt_run + __popcll(bg & lanemask_lt(lane));
-      const uint32_t eqb = eq_run + __popcll(be & lanemask_lt(lane));
-      if (gt || (eq && eqb < take_eq)) {
-        const uint32_t p = gtb + (eqb < take_eq ? eqb : take_eq);
-        if (p < (uint32_t)K) out[p] = row_of(i);
-      }
-      gt_run += __popcll(bg);
-      eq_run += __popcll(be);
-    }
-    pad(gt_tot + (eq_tot < take_eq ? eq_tot : take_eq));
-    return;
-  }
-
-  // ---- keys in registers ----
-  constexpr int kpt = kMaxKpt;
-  const int i0 = t * kpt;
-  const bool vec_ok = !lst && ((reinterpret_cast<uintptr_t>(sc) & 15u) == 0);
-  uint32_t k[kMaxKpt];
+  // Thread t holds keys s*kSeg + t*kKpt + j, j < kKpt, of segment s.  Bounds
+  // are tested as j < nrem with j a constant, so no per-key index stays live.
+  const int nseg = (n + kSeg - 1) / kSeg;
+  uint32_t k[kKpt];
+  auto load_seg = [&](int s) __attribute__((always_inline)) {
+    const int base = s * kSeg + t * kKpt;
+    const int nrem = n - base;
+    const float* sp = sc + base;
+    if (nrem >= kKpt && sc_aligned) {
+      const float4* p4 = reinterpret_cast<const float4*>(sp);
 #pragma unroll
-  for (int j4 = 0; j4 < kMaxKpt / 4; ++j4) {
-    const int i = i0 + 4 * j4;
-    if (4 * j4 < kpt && i + 3 < n && vec_ok) {
-      const float4 s4 = *reinterpret_cast<const float4*>(sc + i);
-      k[4 * j4 + 0] = order_key(s4.x);
-      k[4 * j4 + 1] = order_key(s4.y);
-      k[4 * j4 + 2] = order_key(s4.z);
-      k[4 * j4 + 3] = order_key(s4.w);
+      for (int j4 = 0; j4 < kKpt / 4; ++j4) {
+        const float4 s4 = p4[j4];
+        k[4 * j4 + 0] = order_key(s4.x);
+        k[4 * j4 + 1] = order_key(s4.y);
+        k[4 * j4 + 2] = order_key(s4.z);
+        k[4 * j4 + 3] = order_key(s4.w);
+      }
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) k[4 * j4 + e] = (4 * j4 < kpt && i + e < n) ? key_global(i + e) : 0u;
+      for (int j = 0; j < kKpt; ++j) k[j] = (j < nrem) ? order_key(sp[j]) : 0u;
     }
-  }
+    if (lst) {  // REINDEX rows outside the reachable range are ineligible
+      const int32_t* lp = lst + base;
+#pragma unroll
+      for (int j = 0; j < kKpt; ++j) {
+        if (j < nrem) {
+          const int32_t r = lp[j];
+          if (r < 0 || r >= nv) k[j] = 0u;
+        }
+      }
+    }
+  };
+  // one segment: its keys stay in registers through every pass
+  if (nseg == 1) load_seg(0);
+  auto seg_keys = [&](int s) __attribute__((always_inline)) {
+    if (nseg > 1) load_seg(s);
+  };
+
+  // ---- pass 1: histogram of the top 12 key bits ----
   for (int x = t; x < kBins; x += kThreads) hist_s[x] = 0u;
-  for (int x = t; x < kRegKeys / 32; x += kThreads) mark_s[x] = 0u;
   if (t == 0) bcount_s = 0u;
   __syncthreads();
+  for (int s = 0; s < nseg; ++s) {
+    seg_keys(s);
 #pragma unroll
-  for (int j = 0; j < kMaxKpt; ++j)
-    if (k[j] != 0u) atomicAdd(&hist_s[k[j] >> 20], 1u);
+    for (int j = 0; j < kKpt; ++j)
+      if (k[j] != 0u) atomicAdd(&hist_s[k[j] >> 20], 1u);
+  }
   __syncthreads();
-  find_bucket(hist_s, kBins, (uint32_t)K, red_s, pick_s, t, lane, wv);  // pick_s[2]: eligible total
+  find_bucket<kThreads>(hist_s, kBins, (uint32_t)K, red_s, pick_s, t, lane, wv);  // pick_s[2]: eligible total
   __syncthreads();
   const uint32_t total = pick_s[2];
   const bool take_all = total <= (uint32_t)K;
-  const uint32_t bucket = take_all ? 0u : pick_s[0];
-  const uint32_t quota = take_all ? 0u : (uint32_t)K - pick_s[1];
 
-  bool ranked = true;  // boundary bucket resolved by direct ranking
-  uint32_t thr = 0, take_eq = 0;
+  // The chosen keys are exactly those with (key << 32 | ~index) >= that of
+  // the K-th best key; with the K-th key as (th, idx_lim) a key is chosen iff
+  // key > th, or key == th and index <= idx_lim.
+  uint32_t th = 1u;              // take_all: every eligible key (key >= 1)
+  int32_t idx_lim = 0x7fffffff;
   if (!take_all) {
-    // gather the boundary bucket: a wave-wide prefix of the per-thread counts
-    // and one LDS atomic per wave place every key
-    uint32_t nb = 0;
+    const uint32_t bucket = pick_s[0];
+    const uint32_t quota = (uint32_t)K - pick_s[1];  // 1 .. keys in the bucket
+    const uint32_t lo = bucket << 20;
+    // ---- pass 2: gather the boundary bucket (a wave-wide prefix of the
+    // per-thread counts and one LDS atomic per wave place every key) ----
+    for (int s = 0; s < nseg; ++s) {
+      seg_keys(s);
+      uint32_t nb = 0;
 #pragma unroll
-    for (int j = 0; j < kMaxKpt; ++j) nb += (k[j] != 0u) & ((k[j] >> 20) == bucket);
-    const uint32_t nb_incl = wave_incl_scan(nb);
-    uint32_t wbase = 0;
-    if (lane == 63 && nb_incl != 0u) wbase = atomicAdd(&bcount_s, nb_incl);
-    uint32_t slot = (uint32_t)__builtin_amdgcn_readlane((int)wbase, 63) + nb_incl - nb;
+      for (int j = 0; j < kKpt; ++j) nb += (k[j] != 0u) & ((k[j] - lo) < (1u << 20));
+      const uint32_t nb_incl = wave_incl_scan(nb);
+      uint32_t wbase = 0;
+      if (lane == 63 && nb_incl != 0u) wbase = atomicAdd(&bcount_s, nb_incl);
+      uint32_t slot = (uint32_t)__builtin_amdgcn_readlane((int)wbase, 63) + nb_incl - nb;
+      const uint32_t gbase = (uint32_t)(s * kSeg + t * kKpt);
+      if (nb != 0u) {
 #pragma unroll
-    for (int j = 0; j < kMaxKpt; ++j) {
-      if (k[j] != 0u && (k[j] >> 20) == bucket) {
-        if (slot < (uint32_t)kRankCap) bk_s[slot] = ((uint64_t)k[j] << 32) | (uint32_t)~(uint32_t)(i0 + j);
-        ++slot;
+        for (int j = 0; j < kKpt; ++j) {
+          if (k[j] != 0u && (k[j] - lo) < (1u << 20)) {
+            if (slot < (uint32_t)kRankCap) bk_s[slot] = ((uint64_t)k[j] << 32) | (uint32_t)~(gbase + j);
+            ++slot;
+          }
+        }
       }
     }
     __syncthreads();
     const uint32_t m = bcount_s;
-    ranked = m <= (uint32_t)kRankCap;
-    if (ranked && m <= (uint32_t)(kThreads / 4)) {
-      // four threads per key, each comparing against every fourth key
-      const uint32_t key = (uint32_t)t >> 2, part = (uint32_t)t & 3u;
-      const uint64_t me = bk_s[key < m ? key : 0u];
-      uint32_t r = 0;
-      uint32_t q = part;
-      for (; q + 28 < m; q += 32) {
-        uint64_t o[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) o[u] = bk_s[q + 4 * u];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) r += (uint32_t)(o[u] > me);
-      }
-      for (; q < m; q += 4) r += (uint32_t)(bk_s[q] > me);
-      // sum the quad (DPP quad_perm [1,0,3,2] then [2,3,0,1])
-      r += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)r, 0xB1, 0xf, 0xf, false);
-      r += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)r, 0x4E, 0xf, 0xf, false);
-      const uint32_t mi = ~(uint32_t)me;
-      if (key < m && part == 0u && r < quota) atomicOr(&mark_s[mi >> 5], 1u << (mi & 31));
-      __syncthreads();
-    } else if (ranked) {
-      if ((uint32_t)t < m) {
-        // (key desc, index asc) is the unsigned order of key << 32 | ~index
-        const uint64_t me = bk_s[t];
+    if (m <= (uint32_t)kRankCap) {
+      // rank the bucket's keys against each other; the one ranked quota-1
+      // is the K-th key overall
+      if (m <= (uint32_t)(kThreads / 4)) {
+        // four threads per key, each comparing against every fourth key
+        const uint32_t key = (uint32_t)t >> 2, part = (uint32_t)t & 3u;
+        const uint64_t me = bk_s[key < m ? key : 0u];
         uint32_t r = 0;
-        uint32_t q = 0;
-        for (; q + 8 <= m; q += 8) {  // eight independent LDS reads in flight
+        uint32_t q = part;
+        for (; q + 28 < m; q += 32) {
           uint64_t o[8];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) o[u] = bk_s[q + u];
+          for (int u = 0; u < 8; ++u) o[u] = bk_s[q + 4 * u];
 #pragma unroll
           for (int u = 0; u < 8; ++u) r += (uint32_t)(o[u] > me);
         }
-        for (; q < m; ++q) r += (uint32_t)(bk_s[q] > me);
-        const uint32_t mi = ~(uint32_t)me;
-        if (r < quota) atomicOr(&mark_s[mi >> 5], 1u << (mi & 31));
+        for (; q < m; q += 4) r += (uint32_t)(bk_s[q] > me);
+        // sum the quad (DPP quad_perm [1,0,3,2] then [2,3,0,1])
+        r += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)r, 0xB1, 0xf, 0xf, false);
+        r += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)r, 0x4E, 0xf, 0xf, false);
+        if (key < m && part == 0u && r == quota - 1u) thr_s = me;
+      } else {
+        // one thread per key, several keys per thread past kThreads
+        for (uint32_t key = (uint32_t)t; key < m; key += kThreads) {
+          // (key desc, index asc) is the unsigned order of key << 32 | ~index
+          const uint64_t me = bk_s[key];
+          uint32_t r = 0;
+          uint32_t q = 0;
+          for (; q + 8 <= m; q += 8) {  // eight independent LDS reads in flight
+            uint64_t o[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) o[u] = bk_s[q + u];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) r += (uint32_t)(o[u] > me);
+          }
+          for (; q < m; ++q) r += (uint32_t)(bk_s[q] > me);
+          if (r == quota - 1u) thr_s = me;
+        }
       }
-      __syncthreads();
     } else {
-      radix_finish(1, bucket << 20, 0xFFF00000u, quota, hist_s, red_s, pick_s, t, lane, wv,
-                   [&](int shift, uint32_t dm, uint32_t prefix, uint32_t pmask) {
+      // heavy ties: radix select gives the K-th key value and how many keys
+      // equal to it are taken (lowest indices first); the last of those,
+      // found by a prefix over the keys in index order, is the K-th key.
+      // This rare path re-reads the keys, so the register copy need not
+      // stay live through it.
+      uint32_t thr = 0, take_eq = 0;
+      radix_finish<kThreads>(1, lo, 0xFFF00000u, quota, hist_s, red_s, pick_s, t, lane, wv,
+                             [&](int shift, uint32_t dm, uint32_t prefix, uint32_t pmask) __attribute__((always_inline)) {
+                               for (int s = 0; s < nseg; ++s) {
+                                 load_seg(s);
 #pragma unroll
-                     for (int j = 0; j < kMaxKpt; ++j)
-                       if (k[j] != 0u && (k[j] & pmask) == prefix) atomicAdd(&hist_s[(k[j] >> shift) & dm], 1u);
-                   },
-                   thr, take_eq);
-    }
-  }
-
-  if (ranked) {
-    // chosen: eligible (take_all), above the boundary bucket, or a marked bucket key
-    bool sel[kMaxKpt];
-    uint32_t cnt = 0;
-    const uint32_t mword = mark_s[i0 >> 5] >> (i0 & 31);  // this thread's 16 indices share one word
+                                 for (int j = 0; j < kKpt; ++j)
+                                   if (k[j] != 0u && (k[j] & pmask) == prefix)
+                                     atomicAdd(&hist_s[(k[j] >> shift) & dm], 1u);
+                               }
+                             },
+                             thr, take_eq);
+      uint32_t carry = 0;
+      for (int s = 0; s < nseg; ++s) {
+        load_seg(s);
+        uint32_t ce = 0;
 #pragma unroll
-    for (int j = 0; j < kMaxKpt; ++j) {
-      const uint32_t hb = k[j] >> 20;
-      const uint32_t marked = (mword >> j) & 1u;
-      sel[j] = take_all ? (k[j] != 0u) : ((hb > bucket) | ((hb == bucket) & (k[j] != 0u) & (marked != 0u)));
-      cnt += sel[j];
-    }
-    uint32_t before, unused, tot_sel, unused2;
-    block_prefix2(cnt, 0u, red_s, lane, wv, before, unused, tot_sel, unused2);
+        for (int j = 0; j < kKpt; ++j) ce += (k[j] == thr);
+        uint32_t before, unused, tot_eq, unused2;
+        block_prefix2<kWaves>(ce, 0u, red_s, lane, wv, before, unused, tot_eq, unused2);
+        before += carry;
+        if (before < take_eq && take_eq <= before + ce) {
+          const uint32_t gbase = (uint32_t)(s * kSeg + t * kKpt);
 #pragma unroll
-    for (int j = 0; j < kMaxKpt; ++j) {
-      if (sel[j]) {
-        if (before < (uint32_t)K) out[before] = row_of(i0 + j);
-        ++before;
+          for (int j = 0; j < kKpt; ++j) {
+            if (k[j] == thr) {
+              if (++before == take_eq) thr_s = ((uint64_t)thr << 32) | (uint32_t)~(gbase + j);
+            }
+          }
+        }
+        carry += tot_eq;
+        __syncthreads();
       }
     }
-    pad(tot_sel);
-    return;
+    __syncthreads();
+    const uint64_t kth = thr_s;
+    th = (uint32_t)(kth >> 32);
+    idx_lim = (int32_t)~(uint32_t)kth;
   }
 
-  // boundary bucket too large to rank: keys above the radix threshold, then the
-  // lowest-index keys equal to it
-  uint32_t cg = 0, ce = 0;
+  // ---- pass 3: compaction in index order (a block-wide prefix of the
+  // per-thread counts, carried from segment to segment) ----
+  uint32_t carry = 0;
+  for (int s = 0; s < nseg; ++s) {
+    seg_keys(s);
+    const int base = s * kSeg + t * kKpt;
+    const int jl = idx_lim - base;  // key j of this thread may equal th iff j <= jl
+    auto chosen = [&](int j) __attribute__((always_inline)) -> bool { return (k[j] > th) | ((k[j] == th) & (j <= jl)); };
+    uint32_t cnt = 0;
 #pragma unroll
-  for (int j = 0; j < kMaxKpt; ++j) {
-    cg += (k[j] > thr);
-    ce += (k[j] == thr);
-  }
-  uint32_t gtb, eqb, gt_tot, eq_tot;
-  block_prefix2(cg, ce, red_s, lane, wv, gtb, eqb, gt_tot, eq_tot);
+    for (int j = 0; j < kKpt; ++j) cnt += chosen(j);
+    uint32_t before, unused, tot_sel, unused2;
+    block_prefix2<kWaves>(cnt, 0u, red_s, lane, wv, before, unused, tot_sel, unused2);
+    before += carry;
+    if (cnt != 0u) {
+      const int32_t* lp = lst ? lst + base : nullptr;
 #pragma unroll
-  for (int j = 0; j < kMaxKpt; ++j) {
-    const bool gt = k[j] > thr;
-    const bool eq = k[j] == thr;
-    if (gt || (eq && eqb < take_eq)) {
-      const uint32_t p = gtb + (eqb < take_eq ? eqb : take_eq);
-      if (p < (uint32_t)K) out[p] = row_of(i0 + j);
+      for (int j = 0; j < kKpt; ++j) {
+        if (chosen(j)) {
+          if (before < (uint32_t)K) out[before] = lp ? lp[j] : base + j;
+          ++before;
+        }
+      }
     }
-    gtb += gt;
-    eqb += eq;
+    carry += tot_sel;
+    __syncthreads();
   }
-  pad(gt_tot + (eq_tot < take_eq ? eq_tot : take_eq));
+  pad(carry);
 }
 
 }  // namespace
 
+// Batches of at least this many queries take the 512-thread shape.
+constexpr int32_t kManyQueries = 512;
+
 hipError_t launch_topk_k(int32_t K, int32_t B, const csa2_batch& bt, const float* scores, int64_t stride,
                          int32_t* topk_idx, hipStream_t s) {
   if (B == 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_kernel, dim3(B), dim3(kThreads), 0, s, K, bt.max_candidates, bt.pos, bt.mode,
-                     bt.compress_ratio, bt.pool_len, bt.cand_off, bt.cand_idx, scores, stride, topk_idx);
+  if (B >= kManyQueries)
+    hipLaunchKernelGGL((topk_kernel<512, 32>), dim3(B), dim3(512), 0, s, K, bt.max_candidates, bt.pos, bt.mode,
+                       bt.compress_ratio, bt.pool_len, bt.cand_off, bt.cand_idx, scores, stride, topk_idx);
+  else
+    hipLaunchKernelGGL((topk_kernel<1024, 16>), dim3(B), dim3(1024), 0, s, K, bt.max_candidates, bt.pos, bt.mode,
+                       bt.compress_ratio, bt.pool_len, bt.cand_off, bt.cand_idx, scores, stride, topk_idx);
   return hipGetLastError();
 }
 

@@ -131,6 +131,33 @@ def test_topk_from_oracle_scores_with_ties(n, k):
         assert np.array_equal(got[b], O.topk(s[b], k)), f"row {b}"
 
 
+@pytest.mark.parametrize("B,n,k", [(520, 20000, 512), (512, 16384, 512), (600, 700, 512), (530, 40000, 100)])
+def test_topk_many_queries_with_ties(B, n, k):
+    # a batch of many queries takes the top-K kernel's many-queries shape;
+    # lists longer than one register segment are re-read per pass
+    rng = np.random.default_rng(B * 7 + n)
+    s = (rng.standard_normal((B, n)) * 11.0).astype(np.float32)
+    s[1::5] = (rng.integers(-64, 64, size=s[1::5].shape) / 8).astype(np.float32)  # heavy ties
+    s[2::5] = 3.0                                                                  # all equal
+    lens = rng.integers(1, n + 1, size=B).astype(np.int32)
+    lens[:4] = [n, 0, k, k + 1]
+    dims = synth.default_dims(index_topk=k)
+    inp = dict(pos=lens.astype(np.int64) - 1, mode=np.zeros(B, np.int32), ratio=np.ones(B, np.int32),
+               win_row0=np.zeros(B, np.int64), win_len=np.zeros(B, np.int32), pool_row0=np.zeros(B, np.int64),
+               pool_len=np.full(B, n, np.int32))
+    dev = {kk: torch.from_numpy(v).cuda() for kk, v in inp.items()}
+    bt = csa2.Batch(*(dev[x].data_ptr() for x in ["pos", "mode", "ratio", "win_row0", "win_len", "pool_row0",
+                                                   "pool_len"]), None, None, n)
+    sc = torch.from_numpy(s).cuda()
+    out = torch.full((B, k), -7, dtype=torch.int32, device="cuda")
+    say(f"topk many queries B={B} n={n} k={k}")
+    csa2.csa2_topk(csa2.Dims.from_dict(dims), B, bt, sc, n, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for b in range(B):
+        assert np.array_equal(got[b], O.topk(s[b, :lens[b]], k)), f"row {b} (n={lens[b]})"
+
+
 def test_attend_reuse_lists_with_padding_and_duplicates():
     ctx = [30000, 2000, 500, 128 * 4 + 8]
     inp = synth.decode_batch(12, ctx, [synth.MODE_REUSE] * 4, [4] * 4, dims=small_dims())
