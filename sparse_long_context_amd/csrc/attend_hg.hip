@@ -129,49 +129,32 @@ __global__ __launch_bounds__(kThr) void attend_hg_kernel(HgArgs a) {
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int g = lane >> 4, l16 = lane & 15;
 
-  // ---- this group's 16 q rows into LDS (read back as the B operand: dims x heads) ----
+  // ---- prologue: every global load it needs is issued before the first
+  // wait -- this group's 16 q rows, the selection list, and (when it lies in
+  // the window) the rows of the wave's first chunk ----
+  constexpr int kQPieces = kGroupHeads * (kRowB / 16) / kThr;  // 16-byte q pieces per thread (4)
+  constexpr int kListPer = kMaxTopK / kThr;                    // list entries per thread (2)
+  uint4 qv[kQPieces];
 #pragma unroll
-  for (int it = 0; it < kGroupHeads * (kRowB / 16) / kThr; ++it) {
+  for (int it = 0; it < kQPieces; ++it) {
     const int p = t + kThr * it;
     const int h = p >> 6, u = p & 63;
-    const uint4 v = *reinterpret_cast<const uint4*>(a.q + ((int64_t)b * kHeads + hg * kGroupHeads + h) * kDim + 8 * u);
-    *reinterpret_cast<uint4*>(q_s + h * kRowB + (swz(h, u) << 4)) = v;
+    qv[it] = *reinterpret_cast<const uint4*>(a.q + ((int64_t)b * kHeads + hg * kGroupHeads + h) * kDim + 8 * u);
   }
-
-  // ---- entry list: window rows, then the selected pool rows in list order ----
   int wl = a.win_kv ? a.win_len[b] : 0;
   wl = wl < 0 ? 0 : (wl > a.W ? a.W : wl);
   const int64_t w0 = a.win_row0[b];
-  for (int e = t; e < wl; e += kThr) ent_s[e] = w0 + e;
   const int md = a.mode[b];
-  uint32_t nsel = 0;
-  if (md != CSA2_MODE_WINDOW && a.topk != nullptr && a.comp_kv != nullptr) {
-    const int32_t plen = a.pool_len[b];
-    const int64_t p0 = a.pool_row0[b];
+  const bool has_list = md != CSA2_MODE_WINDOW && a.topk != nullptr && a.comp_kv != nullptr;
+  int32_t idxv[kListPer];
+  {
     const int32_t* lst = a.topk + (int64_t)b * a.K;
-    for (int r0 = 0; r0 < a.K; r0 += kThr) {
-      const int k = r0 + t;
-      const int32_t idx = (k < a.K) ? lst[k] : -1;
-      const bool ok = (idx >= 0) & (idx < plen);
-      const uint64_t m = __ballot(ok);
-      if (lane == 0) wcnt_s[wv] = __popcll(m);
-      __syncthreads();
-      uint32_t before = nsel, tot = 0;
 #pragma unroll
-      for (int w = 0; w < kWv; ++w) {
-        before += (w < wv) ? wcnt_s[w] : 0u;
-        tot += wcnt_s[w];
-      }
-      before += __popcll(m & ((1ull << lane) - 1ull));
-      if (ok) ent_s[wl + before] = -(p0 + idx) - 1;
-      nsel += tot;
-      __syncthreads();
+    for (int r = 0; r < kListPer; ++r) {
+      const int k = r * kThr + t;
+      idxv[r] = (has_list && k < a.K) ? lst[k] : -1;
     }
   }
-  __syncthreads();
-  const int E = wl + (int)nsel;
-  const int nch = (E + kCh - 1) / kCh;
-
   // ---- per-lane LDS offsets inside this wave's region ----
   // row-major write of k-step s of tile tl: wo[s & 3] + 256 (s >> 2) + 16 KiB tl
   // (the same offsets, in q_s, give this lane's q fragment of k-step s);
@@ -192,12 +175,16 @@ __global__ __launch_bounds__(kThr) void attend_hg_kernel(HgArgs a) {
   for (int T = 0; T < 32; ++T) acc[T] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -__builtin_inff(), l_run = 0.f;
 
+  // entry e -> its row: window rows first (known without the list), then the
+  // selected pool rows as ent_s holds them (-(row) - 1).  E counts the entries
+  // known so far: the window's until the list is in.
+  int E = wl;
   auto fetch = [&](int c, Rows<KV>& st) {
 #pragma unroll
     for (int tl = 0; tl < 2; ++tl) {
       int e = c * kCh + 16 * tl + l16;
       if (e >= E) e = 0;  // rows past the end repeat a real row; their probability is 0
-      const int64_t ev = ent_s[e];
+      const int64_t ev = (e < wl) ? w0 + e : ent_s[e];
       const bool pool = ev < 0;
       const int64_t row = pool ? (-ev - 1) : ev;
       if constexpr (KV == CSA2_KV_BF16) {
@@ -312,14 +299,54 @@ __global__ __launch_bounds__(kThr) void attend_hg_kernel(HgArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   };
 
+  Rows<KV> sa, sb;
+  // the wave's first chunk, when it lies in the window, goes out now
+  const bool early = (wv + 1) * kCh <= wl;
+  if (early) fetch(wv, sa);
+
+  // ---- q rows into LDS (read back as the B operand: dims x heads) ----
+#pragma unroll
+  for (int it = 0; it < kQPieces; ++it) {
+    const int p = t + kThr * it;
+    const int h = p >> 6, u = p & 63;
+    *reinterpret_cast<uint4*>(q_s + h * kRowB + (swz(h, u) << 4)) = qv[it];
+  }
+  // ---- the selected pool rows, in list order, after the window rows ----
+  uint32_t nsel = 0;
+  if (has_list) {
+    const int32_t plen = a.pool_len[b];
+    const int64_t p0 = a.pool_row0[b];
+#pragma unroll
+    for (int r = 0; r < kListPer; ++r) {
+      if (r * kThr >= a.K) break;  // uniform
+      const int32_t idx = idxv[r];
+      const bool ok = (idx >= 0) & (idx < plen);
+      const uint64_t m = __ballot(ok);
+      if (lane == 0) wcnt_s[wv] = __popcll(m);
+      __syncthreads();
+      uint32_t before = nsel, tot = 0;
+#pragma unroll
+      for (int w = 0; w < kWv; ++w) {
+        before += (w < wv) ? wcnt_s[w] : 0u;
+        tot += wcnt_s[w];
+      }
+      before += __popcll(m & ((1ull << lane) - 1ull));
+      if (ok) ent_s[wl + before] = -(p0 + idx) - 1;
+      nsel += tot;
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+  E = wl + (int)nsel;
+  const int nch = (E + kCh - 1) / kCh;
+
   // wave wv takes chunks wv, wv + 4, ... (nw of them); two register sets
   // alternate.  Inside the loop every refill is issued, even past the last
   // chunk (its rows then repeat entry 0), so each wait for a set's rows
   // leaves the other set's loads in flight.
   const int nw = (nch > wv) ? (nch - wv + kWv - 1) / kWv : 0;
   if (nw > 0) {
-    Rows<KV> sa, sb;
-    fetch(wv, sa);
+    if (!early) fetch(wv, sa);
     fetch(wv + kWv, sb);
     int k = 0;
 #pragma clang loop unroll(disable)

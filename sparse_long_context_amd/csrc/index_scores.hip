@@ -64,8 +64,11 @@ __device__ __forceinline__ uint4 load_stream(const uint8_t* p) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// With one or a few index heads: eight waves per SIMD (at most 64 VGPRs), so
+// eight workgroups per CU keep 128 KiB of key rows in flight, where the
+// register use the compiler picks by itself (80) allows six.
 template <int HP>
-__global__ __launch_bounds__(kThreads) void index_scores_decode(
+__global__ __launch_bounds__(kThreads, HP <= 4 ? 8 : 1) void index_scores_decode(
     int32_t hi, int32_t relu, int32_t max_cand, const int64_t* __restrict__ pos,
     const int32_t* __restrict__ mode, const int32_t* __restrict__ ratio,
     const int64_t* __restrict__ pool_row0, const int32_t* __restrict__ pool_len,

@@ -231,6 +231,27 @@ def test_attend_kernels_agree_with_oracle():
     compare(many, v.topk.cpu().numpy(), v.out.cpu().numpy(), v.lse.cpu().numpy(), queries=[0, 1, 2, 5, 65])
 
 
+@pytest.mark.parametrize("kv", [synth.KV_BF16, synth.KV_FP8])
+def test_decode_many_queries_all_heads_kernel(kv):
+    # 300 queries: one workgroup of all 64 heads per query, no entry split;
+    # entry counts from 0 to 640 (partial last chunks), all four modes, a sink
+    rng = np.random.default_rng(20 + kv)
+    B = 300
+    ctx = rng.integers(1, 12000, size=B)
+    ctx[:6] = [1, 3, 4 * 33, 4 * 512 + 7, 60000, 9000]
+    modes = np.array([0, 1, 2, 3] * (B // 4), np.int32)
+    modes[:6] = [0, 0, 0, 0, 0, 3]
+    ratios = np.where(modes == 3, 0, 4).astype(np.int32)
+    dims = small_dims(kv_dtype=kv, softmax_scale=0.9)
+    inp = synth.decode_batch(20 + kv, list(ctx), list(modes), list(ratios), dims=dims)
+    synth.add_reindex_lists(inp, 20 + kv, frac=0.3)
+    inp["win_len"][7] = 0
+    sink = synth.normal_f32(20, 78, (64,))
+    say(f"decode B={B} all-heads kernel kv {kv}")
+    _, sg, og, lg = run_decode(inp, sink=sink)
+    compare(inp, sg, og, lg, queries=[0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 150, 299], sink=sink, scale=0.9)
+
+
 def test_decode_is_deterministic():
     inp = synth.decode_batch(17, [60000, 8000], [0, 0], [4, 4], dims=small_dims())
     w = csa2.DecodeWorkload(inp)
