@@ -364,7 +364,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
   }
 
   // ---- pass 3: compaction in index order (a block-wide prefix of the
-  // per-thread counts, carried from segment to segment) ----
+  // per-thread counts, carried from segment to segment).  With K up to the
+  // histogram's size the chosen rows are placed in the (now free) histogram
+  // first and written out with one coalesced pass, -1 padded ----
+  const bool staged = K <= kBins;
   uint32_t carry = 0;
   for (int s = 0; s < nseg; ++s) {
     seg_keys(s);
@@ -382,7 +385,11 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
 #pragma unroll
       for (int j = 0; j < kKpt; ++j) {
         if (chosen(j)) {
-          if (before < (uint32_t)K) out[before] = lp ? lp[j] : base + j;
+          if (before < (uint32_t)K) {
+            const int32_t row = lp ? lp[j] : base + j;
+            if (staged) hist_s[before] = (uint32_t)row;
+            else out[before] = row;
+          }
           ++before;
         }
       }
@@ -390,7 +397,12 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
     carry += tot_sel;
     __syncthreads();
   }
-  pad(carry);
+  if (staged) {
+    const uint32_t n_out = carry < (uint32_t)K ? carry : (uint32_t)K;
+    for (int x = t; x < K; x += kThreads) out[x] = (uint32_t)x < n_out ? (int32_t)hist_s[x] : -1;
+  } else {
+    pad(carry);
+  }
 }
 
 }  // namespace
