@@ -3,9 +3,11 @@
 * ``libcsa2.so``        -- the HIP library behind include/csa2.h (hipcc, gfx950).
 * ``libcsa2_synth.so``  -- the seeded synthetic-input generator (gcc).
 """
+import concurrent.futures as cf
 import glob
 import os
 import subprocess
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -14,7 +16,6 @@ ARCH = "gfx950"
 
 HIP_LIB = os.path.join(PKG, "libcsa2.so")
 SYNTH_LIB = os.path.join(PKG, "libcsa2_synth.so")
-
 
 def _run(cmd, verbose):
     if verbose:
@@ -30,20 +31,29 @@ def build_synth(verbose: bool = False) -> str:
     return SYNTH_LIB
 
 
+def _hip_flags(src):
+    flags = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+             # packed-fp32 instructions are kept out of every kernel
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             # matrix-core accumulators in ordinary VGPRs, so the register
+             # allocator can use the accumulation registers for staged rows
+             "-mllvm", "-amdgpu-mfma-vgpr-form",
+             "-Wall", "-Wno-unused-result", "-I", os.path.join(ROOT, "include")]
+    return flags
+
+
 def build_hip(verbose: bool = False) -> str:
     srcs = sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
     if not srcs:
         raise RuntimeError("no HIP sources under csrc/")
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           # packed-fp32 instructions are kept out of every kernel
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           # matrix-core accumulators in ordinary VGPRs, so the register
-           # allocator can use the accumulation registers for staged rows
-           "-mllvm", "-amdgpu-mfma-vgpr-form",
-           "-Wall", "-Wno-unused-result",
-           "-I", os.path.join(ROOT, "include"),
-           "-o", HIP_LIB + ".tmp"] + srcs
-    _run(cmd, verbose)
+    with tempfile.TemporaryDirectory(prefix="csa2_build_") as tmp:
+        objs = [os.path.join(tmp, os.path.basename(s) + ".o") for s in srcs]
+        jobs = min(len(srcs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1)))
+        with cf.ThreadPoolExecutor(max_workers=max(jobs, 1)) as ex:
+            futs = [ex.submit(_run, [HIPCC] + _hip_flags(s) + ["-c", s, "-o", o], verbose) for s, o in zip(srcs, objs)]
+            for f in futs:
+                f.result()
+        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", HIP_LIB + ".tmp"] + objs, verbose)
     os.replace(HIP_LIB + ".tmp", HIP_LIB)
     return HIP_LIB
 
