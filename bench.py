@@ -130,12 +130,100 @@ def cpu_baseline(inp, min_seconds=10.0, max_seconds=30.0):
                       f"OpenMP over queries)"}
 
 
+def bench_prefill(args):
+    """The prefill chunk (4,096 queries of one sequence at positions
+    126,976..131,071, compress ratio 8): one step = one csa2_prefill call."""
+    import torch
+    from sparse_long_context_amd import csa2, synth
+    print("[bench] generating the prefill chunk", file=sys.stderr, flush=True)
+    pf = synth.config(2)
+    w = csa2.PrefillWorkload(pf)
+    stream = torch.cuda.current_stream()
+    T = w.T
+    for _ in range(args.warmup):
+        w.prefill()
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        w.prefill()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    # the attention on its own (the dominant kernel): the same batch through
+    # csa2_attend, launched back to back between two HIP events
+    inp = synth.prefill_as_batch(pf)
+    dw = csa2.DecodeWorkload(inp)
+    dw.topk.copy_(w.topk)
+    attend = lambda: csa2.csa2_attend(dw.dims, T, dw.batch, dw.q, dw.win_kv, dw.win_scale, dw.comp_kv,  # noqa: E731
+                                      dw.comp_scale, dw.topk, None, dw.out, dw.lse, None, 0)
+    for _ in range(args.warmup):
+        attend()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        attend()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    attn_us = 1000.0 * e0.elapsed_time(e1) / args.steps
+    ent = int(inp["win_len"].sum()) + T * pf["dims"]["index_topk"]
+    attn_flops = 4.0 * 64 * 512 * ent
+    achieved = attn_flops / (attn_us * 1e-6) / 1e12
+    d = pf["dims"]
+    line = {
+        "metric": METRIC, "value": round(T * args.steps / wall, 1), "unit": "queries/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": (f"prefill chunk, {T} queries at positions {int(pf['pos0'])}..{int(pf['pos0']) + T - 1}, "
+                                f"compress ratio {int(pf['ratio'])} -> {int(pf['pool_len'])} pool rows, window "
+                                f"{d['window']}, top-{d['index_topk']}, {d['n_heads']} heads x {d['head_dim']}, bf16 KV, "
+                                f"fp32 indexer keys dim {d['index_dim']}"),
+                   "queries_per_step": T, "pool_rows": int(pf["pool_len"]), "window": d["window"],
+                   "index_topk": d["index_topk"], "kv": "bf16", "index_keys": "fp32"},
+        "roofline": {"bound": "mfma", "kernel": "attend_mq_kernel", "achieved": round(achieved, 1),
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "algorithmic_flops_per_launch": attn_flops, "avg_launch_us": round(attn_us, 2)},
+        "stages_us": {"attend": round(attn_us, 2)},
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline_prefill(pf, inp)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_prefill(pf, inp, min_seconds=10.0):
+    """Oracle over groups of 64 consecutive prefill queries (scores against
+    the shared pool, top-512, attention) until at least min_seconds."""
+    import numpy as np
+    from oracle import oracle as O
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    n = 0
+    t0 = time.perf_counter()
+    start = 0
+    while True:
+        qs = np.arange(start, start + 64) % pf["T"]
+        O.decode_batch(inp, qs)
+        n += len(qs)
+        start += 64
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    return {"value": n / el, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of the chunk's queries in groups of 64 ({el:.1f} s, fp64 oracle, OpenMP over queries)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=1, help="decode workload index (1, 3 or 4)")
+    ap.add_argument("--config", type=int, default=1,
+                    help="workload index: decode 1, 3 or 4, or 2 (the 4,096-query prefill chunk)")
     ap.add_argument("--storage", choices=("native", "fp4"), default="native",
                     help="fp4: the same workload with its KV rows re-stored as FP4 (E4M3 scale per 16) and its index "
                          "keys as MXFP4, quantized on the GPU by the library's own quantizers before timing")
@@ -161,9 +249,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    if args.config not in (1, 3, 4):
-        print("bench.py times the decode workloads 1, 3 or 4", file=sys.stderr)
+    if args.config not in (1, 2, 3, 4):
+        print("bench.py times the workloads 1, 2, 3 or 4", file=sys.stderr)
         sys.exit(2)
+    if args.config == 2:
+        if args.storage != "native":
+            print("--storage fp4 re-stores decode workloads only", file=sys.stderr)
+            sys.exit(2)
+        bench_prefill(args)
+        return
     print(f"[bench] generating workload {args.config}", file=sys.stderr, flush=True)
     inp = synth.config(args.config)
     w = csa2.DecodeWorkload(inp)

@@ -271,7 +271,7 @@ constexpr int kPQ = 128;  // queries per workgroup
 constexpr int kPC = 128;  // candidates per workgroup
 constexpr int kPK = 16;   // k slab
 
-__global__ __launch_bounds__(256) void index_scores_prefill(
+__global__ __launch_bounds__(256, 4) void index_scores_prefill(
     int32_t T, const int64_t* __restrict__ pos, int32_t md, int32_t ratio, int32_t pool_len,
     const float* __restrict__ idx_q, const float* __restrict__ idx_w, int32_t relu,
     const float* __restrict__ idx_k, float* __restrict__ scores, int64_t stride) {
@@ -291,28 +291,41 @@ __global__ __launch_bounds__(256) void index_scores_prefill(
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[a][c] = 0.0f;
 
-  // loaders: 128 rows x 16 floats per slab = 512 float4, two per thread
-  for (int s = 0; s < kIndexDim / kPK; ++s) {
+  // loaders: 128 rows x 16 floats per slab = 512 float4, two per thread; the
+  // next slab's loads are issued before the current slab's products
+  float4 vq[2], vk[2];
+  auto load = [&](int s) __attribute__((always_inline)) {
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
       const int p = it * 256 + t;
       const int r = p >> 2, part = p & 3;
-      const int qq = q0 + r;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (qq < T) v = *reinterpret_cast<const float4*>(idx_q + (int64_t)qq * kIndexDim + s * kPK + part * 4);
-      qs[part * 4 + 0][r] = v.x;
-      qs[part * 4 + 1][r] = v.y;
-      qs[part * 4 + 2][r] = v.z;
-      qs[part * 4 + 3][r] = v.w;
-      const int cc = c0 + r;
-      float4 kv = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (cc < nmax) kv = *reinterpret_cast<const float4*>(idx_k + (int64_t)cc * kIndexDim + s * kPK + part * 4);
-      ks[part * 4 + 0][r] = kv.x;
-      ks[part * 4 + 1][r] = kv.y;
-      ks[part * 4 + 2][r] = kv.z;
-      ks[part * 4 + 3][r] = kv.w;
+      const int qq = q0 + r, cc = c0 + r;
+      vq[it] = (qq < T) ? *reinterpret_cast<const float4*>(idx_q + (int64_t)qq * kIndexDim + s * kPK + part * 4)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+      vk[it] = (cc < nmax) ? *reinterpret_cast<const float4*>(idx_k + (int64_t)cc * kIndexDim + s * kPK + part * 4)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+  };
+  auto stage = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int p = it * 256 + t;
+      const int r = p >> 2, part = p & 3;
+      qs[part * 4 + 0][r] = vq[it].x;
+      qs[part * 4 + 1][r] = vq[it].y;
+      qs[part * 4 + 2][r] = vq[it].z;
+      qs[part * 4 + 3][r] = vq[it].w;
+      ks[part * 4 + 0][r] = vk[it].x;
+      ks[part * 4 + 1][r] = vk[it].y;
+      ks[part * 4 + 2][r] = vk[it].z;
+      ks[part * 4 + 3][r] = vk[it].w;
+    }
+  };
+  load(0);
+  for (int s = 0; s < kIndexDim / kPK; ++s) {
+    stage();
     __syncthreads();
+    if (s + 1 < kIndexDim / kPK) load(s + 1);
 #pragma unroll
     for (int k = 0; k < kPK; ++k) {
       const float4 qa = *reinterpret_cast<const float4*>(&qs[k][tq * 8]);
