@@ -172,6 +172,25 @@ def test_attend_reuse_lists_with_padding_and_duplicates():
     assert (og[2] == 0).all() and np.isneginf(lg[2]).all()
 
 
+def test_attend_reuse_lists_many_queries():
+    # the same list shapes through the all-heads kernels (260 queries: one
+    # workgroup per query, no entry split), bf16 and fp8
+    for kv in (synth.KV_BF16, synth.KV_FP8):
+        B = 260
+        ctx = [30000, 2000, 500, 128 * 4 + 8] * (B // 4)
+        inp = synth.decode_batch(40 + kv, ctx, [synth.MODE_REUSE] * B, [4] * B, dims=small_dims(kv_dtype=kv))
+        sel = inp["sel_in"]
+        sel[1, 100:200] = -1                 # holes in the middle
+        sel[2, :] = -1                       # nothing selected: window only
+        sel[3, 5:10] = sel[3, 0]             # duplicates count per occurrence
+        sel[5, 511] = sel[5, 0]
+        inp["win_len"][2] = 0                # ... and no window either: zeros
+        say(f"attend reuse many queries kv {kv}")
+        _, sg, og, lg = run_decode(inp)
+        compare(inp, sg, og, lg, queries=[0, 1, 2, 3, 5, 259])
+        assert (og[2] == 0).all() and np.isneginf(lg[2]).all()
+
+
 # ---------------------------------------------------------------------------
 # whole decode step, small shapes (several tiles + ragged tails)
 # ---------------------------------------------------------------------------
