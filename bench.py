@@ -10,7 +10,11 @@ are seeded synthetic N(0, 1) data, resident in HBM before timing starts.
 Prints ONE JSON line.  Besides the contract fields it carries
   roofline:     the dominant kernel (the indexer scan) against HBM bandwidth,
                 its duration measured here with HIP events on the launch stream;
-  cpu_baseline: the CPU oracle timed on a bounded sample of the same workload.
+  cpu_baseline: the CPU oracle timed on a bounded sample of the same workload;
+  step_us:      medians of per-step HIP-event times, warm (back to back) and
+                cold (a 1 GiB fill before each step evicts the last-level cache).
+--config 2 times the 4,096-query prefill chunk instead (one csa2_prefill per
+step; the roofline is then the attention's against the bf16 MFMA peak).
 """
 import argparse
 import hashlib
@@ -92,7 +96,9 @@ def summarize_traffic(fetch_csv, write_csv):
         idx = [x for k, xs in v.items() if "index_scores_decode" in k for x in xs]
         # the probe's streaming kernel for this counter: the sum reads, the fill writes
         probe = "reduce_kernel" if counter == "FETCH_SIZE" else "FillFunctor"
-        cpy = [x for k, xs in v.items() if probe in k for x in xs if x * 1024 > 0.25 * COPY_PROBE_BYTES]
+        # (the cold-step flush is a 1 GiB fill: twice the probe, so it is not taken)
+        cpy = [x for k, xs in v.items() if probe in k for x in xs
+               if 0.75 * COPY_PROBE_BYTES < x * 1024 < 1.5 * COPY_PROBE_BYTES]
         if not idx or not cpy:
             raise SystemExit(f"{path}: no indexer or copy dispatches with {counter}")
         scale = COPY_PROBE_BYTES / (1024.0 * (sum(cpy) / len(cpy)))
@@ -128,6 +134,29 @@ def cpu_baseline(inp, min_seconds=10.0, max_seconds=30.0):
     return {"value": n / el, "unit": "queries/s", "cores": threads, "kind": "oracle",
             "sample": f"{passes} passes over the {inp['B']}-query batch ({n} queries, {el:.1f} s, fp64 oracle, "
                       f"OpenMP over queries)"}
+
+
+def step_medians(torch, fn, steps, stream):
+    """Median of per-step HIP-event times of fn (microseconds): warm, back to
+    back with no flush; cold, with a 1 GiB fill before each step, which evicts
+    the last-level cache (256 MB) so every input comes from HBM again."""
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    out = {}
+    for mode in ("warm", "cold"):
+        ts = []
+        for _ in range(steps):
+            if mode == "cold":
+                flush.fill_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(1000.0 * e0.elapsed_time(e1))
+        ts.sort()
+        out[mode + "_median_us"] = round(ts[len(ts) // 2], 2)
+    del flush
+    return out
 
 
 def bench_prefill(args):
@@ -170,6 +199,7 @@ def bench_prefill(args):
     e1.record(stream)
     torch.cuda.synchronize()
     attn_us = 1000.0 * e0.elapsed_time(e1) / args.steps
+    step_us = step_medians(torch, w.prefill, min(args.steps, 20), stream)
     ent = int(inp["win_len"].sum()) + T * pf["dims"]["index_topk"]
     attn_flops = 4.0 * 64 * 512 * ent
     achieved = attn_flops / (attn_us * 1e-6) / 1e12
@@ -188,6 +218,7 @@ def bench_prefill(args):
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                      "traffic": None, "algorithmic_flops_per_launch": attn_flops, "avg_launch_us": round(attn_us, 2)},
         "stages_us": {"attend": round(attn_us, 2)},
+        "step_us": step_us,
         "gpu": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu_baseline:
@@ -326,6 +357,7 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         stage_us.append(1000.0 * e0.elapsed_time(e1) / args.steps)
+    step_us = step_medians(torch, w.decode, args.steps, stream)
     if args.copy_probe:
         # plain streaming kernels of known size, for scaling the HBM byte
         # counters: a fill writes COPY_PROBE_BYTES, a sum reads them
@@ -366,6 +398,7 @@ def main():
                       "attend": round(stage_us[2], 2)},
         "attend_mfma": {"achieved": round(attend_tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(attend_tflops / BF16_PEAK_TFLOPS, 4)},
+        "step_us": step_us,
         "gpu": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu_baseline and args.storage == "native":
