@@ -432,8 +432,12 @@ hipError_t launch_attend(const csa2_dims& d, int32_t B, const csa2_batch& bt, co
     hipLaunchKernelGGL((attend_kernel<CSA2_KV_FP4_E2M1_E4M3_16>), dim3(B * n_split), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_split == 1) return e;
-  hipLaunchKernelGGL(attend_combine, dim3(B * kHeads), dim3(128), 0, s, n_split, a.part_o, a.part_ml, sink,
-                     out, lse);
+  return launch_attend_combine(B, n_split, a.part_o, a.part_ml, sink, out, lse, s);
+}
+
+hipError_t launch_attend_combine(int32_t B, int n_split, const float* part_o, const float* part_ml, const float* sink,
+                                 float* out, float* lse, hipStream_t s) {
+  hipLaunchKernelGGL(attend_combine, dim3(B * kHeads), dim3(128), 0, s, n_split, part_o, part_ml, sink, out, lse);
   return hipGetLastError();
 }
 

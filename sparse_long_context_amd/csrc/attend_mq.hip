@@ -67,6 +67,9 @@ struct MqArgs {
   const float* sink;
   float* out;
   float* lse;
+  float* part_o;   // [B][S][64][512] unnormalised partial outputs (entry splits only)
+  float* part_ml;  // [B][S][64][2]   running max (log2 units) and sum
+  int32_t n_split;
   int32_t B;
   int32_t K;
   int32_t W;
@@ -89,11 +92,13 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
   __shared__ int64_t ent_s[kMaxEntries];  // >= 0: window row; < 0: -(pool row) - 1
   __shared__ uint32_t wcnt_s[kWv];
 
-  // contiguous runs of queries per XCD: workgroup i -> XCD i % 8, slot i / 8
+  // contiguous runs of (query, split) pairs per XCD: workgroup i -> XCD
+  // i % 8, slot i / 8
   const int nwg = (int)gridDim.x;
   const int xcd = (int)blockIdx.x & 7, wslot = (int)blockIdx.x >> 3;
   const int per = nwg >> 3, rem = nwg & 7;
-  const int b = xcd * per + (xcd < rem ? xcd : rem) + wslot;
+  const int item = xcd * per + (xcd < rem ? xcd : rem) + wslot;
+  const int b = item / a.n_split, sp = item % a.n_split;
   if (b >= a.B) return;  // whole workgroup, before any barrier
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int g = lane >> 4, l16 = lane & 15;
@@ -140,7 +145,12 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
   }
   __syncthreads();
   const int E = wl + (int)nsel;
-  const int nch = (E + kCh - 1) / kCh;
+  // this workgroup's chunks: [c_beg, c_beg + nch) of the query's
+  const int nch_all = (E + kCh - 1) / kCh;
+  const int cps = (nch_all + a.n_split - 1) / a.n_split;
+  const int c_beg = sp * cps;
+  const int c_end = c_beg + cps < nch_all ? c_beg + cps : nch_all;
+  const int nch = c_end > c_beg ? c_end - c_beg : 0;  // local chunk c is the query's c_beg + c
 
   // ---- gather of chunk c into its slot: this wave's 8 rows, one DMA each;
   // rows past the last entry repeat entry 0 (their probability is 0).  Lane
@@ -148,7 +158,7 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
   // then take each row from that lane, so no LDS round trip sits between
   // them ----
   auto entry_for = [&](int c) __attribute__((always_inline)) -> int64_t {
-    int e = c * kCh + kRowsPerWave * wv + (lane & (kRowsPerWave - 1));
+    int e = (c_beg + c) * kCh + kRowsPerWave * wv + (lane & (kRowsPerWave - 1));
     if (e >= E) e = 0;
     return ent_s[e];
   };
@@ -241,7 +251,7 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const float s2 = dh ? o4[i][k] + sa[et][ht][k] : sa[et][ht][k] + o4[i][k];
-        const int e = c * kCh + 16 * et + 4 * g + k;
+        const int e = (c_beg + c) * kCh + 16 * et + 4 * g + k;
         sv[ht][4 * et + k] = (e < E) ? s2 * a.scale_log2 : -__builtin_inff();
       }
     }
@@ -322,7 +332,21 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
     const int head = 32 * hh + 16 * ht + l16;
-    float M = m_run[ht], L = head_sum(l_run[ht]), f;
+    const float lsum = head_sum(l_run[ht]);
+    if (a.n_split > 1) {  // unnormalised partials, merged by attend_combine
+      const int64_t pslot = ((int64_t)b * a.n_split + sp) * kHeads + head;
+      float* op = a.part_o + pslot * kDim + 256 * dh + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < 16; ++dt)
+        *reinterpret_cast<float4*>(op + 16 * dt) =
+            make_float4(acc[dt][ht][0], acc[dt][ht][1], acc[dt][ht][2], acc[dt][ht][3]);
+      if (g == 0 && dh == 0) {
+        a.part_ml[pslot * 2] = m_run[ht];
+        a.part_ml[pslot * 2 + 1] = lsum;
+      }
+      continue;
+    }
+    float M = m_run[ht], L = lsum, f;
     if (a.sink) {
       const float s2 = a.sink[head] * kLog2e;
       const float M2 = fmaxf(M, s2);
@@ -347,7 +371,7 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
 
 hipError_t launch_attend_mq(const csa2_dims& d, int32_t B, const csa2_batch& bt, const void* q,
                             const void* win_kv, const void* comp_kv, const int32_t* topk_idx, const float* sink,
-                            float* out, float* lse, hipStream_t s) {
+                            float* out, float* lse, int n_split, float* partial, hipStream_t s) {
   if (B == 0) return hipSuccess;
   MqArgs a;
   a.mode = bt.mode;
@@ -362,12 +386,18 @@ hipError_t launch_attend_mq(const csa2_dims& d, int32_t B, const csa2_batch& bt,
   a.sink = sink;
   a.out = out;
   a.lse = lse;
+  if (n_split < 1) n_split = 1;
+  a.n_split = n_split;
+  a.part_o = partial;
+  a.part_ml = partial ? partial + (size_t)B * n_split * kHeads * kDim : nullptr;
   a.B = B;
   a.K = d.index_topk;
   a.W = d.window;
   a.scale_log2 = d.softmax_scale * kLog2e;
-  hipLaunchKernelGGL(attend_mq_kernel, dim3((unsigned)B), dim3(kThr), 0, s, a);
-  return hipGetLastError();
+  hipLaunchKernelGGL(attend_mq_kernel, dim3((unsigned)(B * n_split)), dim3(kThr), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || n_split == 1) return e;
+  return launch_attend_combine(B, n_split, a.part_o, a.part_ml, sink, out, lse, s);
 }
 
 }  // namespace csa2

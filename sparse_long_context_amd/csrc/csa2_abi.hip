@@ -179,16 +179,17 @@ csa2_status csa2_topk(const csa2_dims* dims, int32_t B, const csa2_batch* batch,
   return hip_status(launch_topk(*dims, B, *batch, scores, score_stride, topk_idx, stream));
 }
 
-// Batches past the head-group size: with bf16 KV and one workgroup per query,
-// the all-heads kernel whose rows reach LDS by DMA; otherwise (fp8 / FP4 rows,
-// or entry splits for batches smaller than the CU count) the all-heads kernel
-// that stages rows through registers.
+// Batches past the head-group size: with bf16 KV the all-heads kernel whose
+// rows reach LDS by DMA; with fp8 / FP4 rows the all-heads kernel that stages
+// rows through registers (both split a query's entries over several
+// workgroups when the batch has fewer queries than CUs and a workspace).
 static csa2_status attend_common(const csa2_dims* dims, int32_t B, const csa2_batch* batch, const void* q,
                                  const void* win_kv, const uint8_t* win_scale, const void* comp_kv,
                                  const uint8_t* comp_scale, const int32_t* topk_idx, const float* sink,
                                  float* out, float* lse, float* partial, int n_split, hipStream_t stream) {
-  if (n_split <= 1 && dims->kv_dtype == CSA2_KV_BF16)
-    return hip_status(launch_attend_mq(*dims, B, *batch, q, win_kv, comp_kv, topk_idx, sink, out, lse, stream));
+  if (dims->kv_dtype == CSA2_KV_BF16)
+    return hip_status(
+        launch_attend_mq(*dims, B, *batch, q, win_kv, comp_kv, topk_idx, sink, out, lse, n_split, partial, stream));
   return hip_status(launch_attend(*dims, B, *batch, q, win_kv, win_scale, comp_kv, comp_scale, topk_idx, sink,
                                   out, lse, n_split, partial, stream));
 }

@@ -87,10 +87,14 @@ hipError_t launch_attend_hg(const csa2_dims& d, int32_t B, const csa2_batch& bt,
                             const uint8_t* comp_scale, const int32_t* topk_idx, const float* sink, float* out,
                             float* lse, hipStream_t s);
 int attend_split_for(int32_t B);
-// bf16 KV, one workgroup of four waves per query, rows gathered into LDS by DMA.
+// bf16 KV, one workgroup of four waves per (query, entry split), rows
+// gathered into LDS by DMA; n_split > 1 needs `partial` (attend_partial_floats).
 hipError_t launch_attend_mq(const csa2_dims& d, int32_t B, const csa2_batch& bt, const void* q,
                             const void* win_kv, const void* comp_kv, const int32_t* topk_idx, const float* sink,
-                            float* out, float* lse, hipStream_t s);
+                            float* out, float* lse, int n_split, float* partial, hipStream_t s);
+// Log-sum-exp merge of split partials into out / lse.
+hipError_t launch_attend_combine(int32_t B, int n_split, const float* part_o, const float* part_ml, const float* sink,
+                                 float* out, float* lse, hipStream_t s);
 
 // The cache writer's quantizers (one thread per scale block).
 hipError_t launch_quantize_fp4_kv(int64_t n_rows, int32_t d, const float* src, uint8_t* codes, uint8_t* scales,
