@@ -6,6 +6,9 @@
 // denominator; a query with no entry yields zeros (PocketLLM page, "The op
 // layer").
 //
+// This kernel serves batches of more than 64 queries whose rows are stored
+// narrower than bf16 (fp8, FP4); bf16 rows go to the DMA-ring kernel.
+//
 // Workgroup = one (query, split) pair, 8 waves, two per SIMD so one wave's
 // latency (LDS, softmax, barriers) hides behind another's matrix work.  Wave w
 // owns heads 16(w%4) .. +15 and half h = w/4 of the 512 dims: it contracts its
@@ -246,10 +249,9 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
   // c+2 are in flight; LDS is double buffered.  A wave instruction moves half a
   // 1 KiB bf16 row; rows past the last entry repeat a real row (probability 0).
   struct Stage {
-    uint4 v[KV == CSA2_KV_BF16 ? kPieces : 1];
     uint2 code[KV == CSA2_KV_FP8_E4M3_UE8M0_32 ? kPieces : 1];
     uint32_t c4[KV == CSA2_KV_FP4_E2M1_E4M3_16 ? kPieces : 1];
-    uint32_t sc[KV == CSA2_KV_BF16 ? 1 : kPieces];
+    uint32_t sc[kPieces];
   };
   auto fetch = [&](int c, Stage& st) {
 #pragma unroll
@@ -261,9 +263,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
       const int64_t ev = ent_s[e];
       const bool pool = ev < 0;
       const int64_t row = pool ? (-ev - 1) : ev;
-      if constexpr (KV == CSA2_KV_BF16) {
-        st.v[it] = *reinterpret_cast<const uint4*>((pool ? a.comp_kv : a.win_kv) + row * kRowBytes + u * 16);
-      } else if constexpr (KV == CSA2_KV_FP8_E4M3_UE8M0_32) {
+      if constexpr (KV == CSA2_KV_FP8_E4M3_UE8M0_32) {
         st.code[it] = *reinterpret_cast<const uint2*>((pool ? a.comp_kv : a.win_kv) + row * kDim + u * 8);
         st.sc[it] = (pool ? a.comp_scale : a.win_scale)[row * (kDim / kScaleBlock) + (u >> 2)];
       } else {  // FP4: 8 codes (4 bytes) and the E4M3 scale of their 16-value block
@@ -278,9 +278,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
     for (int it = 0; it < kPieces; ++it) {
       const int p = it * kThreads + t;
       uint4 v;
-      if constexpr (KV == CSA2_KV_BF16) {
-        v = st.v[it];
-      } else if constexpr (KV == CSA2_KV_FP8_E4M3_UE8M0_32) {
+      if constexpr (KV == CSA2_KV_FP8_E4M3_UE8M0_32) {
         v = fp8x8_to_bf16x8(st.code[it], st.sc[it]);
       } else {
         v = fp4x8_e4m3_to_bf16x8(st.c4[it], st.sc[it]);
@@ -424,9 +422,8 @@ hipError_t launch_attend(const csa2_dims& d, int32_t B, const csa2_batch& bt, co
   a.W = d.window;
   a.n_split = n_split;
   a.scale_log2 = d.softmax_scale * kLog2e;
-  if (d.kv_dtype == CSA2_KV_BF16)
-    hipLaunchKernelGGL((attend_kernel<CSA2_KV_BF16>), dim3(B * n_split), dim3(kThreads), 0, s, a);
-  else if (d.kv_dtype == CSA2_KV_FP8_E4M3_UE8M0_32)
+  if (d.kv_dtype == CSA2_KV_BF16) return hipErrorInvalidValue;  // the DMA-ring kernel's
+  if (d.kv_dtype == CSA2_KV_FP8_E4M3_UE8M0_32)
     hipLaunchKernelGGL((attend_kernel<CSA2_KV_FP8_E4M3_UE8M0_32>), dim3(B * n_split), dim3(kThreads), 0, s, a);
   else
     hipLaunchKernelGGL((attend_kernel<CSA2_KV_FP4_E2M1_E4M3_16>), dim3(B * n_split), dim3(kThreads), 0, s, a);
