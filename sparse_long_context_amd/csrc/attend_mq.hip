@@ -1,6 +1,6 @@
 // Two-source single-softmax attention for batches of many queries with bf16
 // KV (a prefill chunk, or a decode batch of a few hundred queries), one
-// workgroup of four waves per query (Reading Notes of DeepSeek-V4.1-Flash,
+// workgroup of eight waves per query (Reading Notes of DeepSeek-V4.1-Flash,
 // section 3f C2 Step 3; "DeepSeek-V4.1-Flash on WASTE", What is new, 1. CSA2):
 // the query's 64 heads attend, in ONE softmax, over its window rows followed
 // by its selected compressed rows; every KV row is both key and value; an
@@ -8,24 +8,28 @@
 // entry gives zeros (PocketLLM page, "The op layer").
 //
 // Rows reach LDS by DMA (global_load_lds_dwordx4: lane l's 16 bytes land at
-// the instruction's LDS base + 16 l), into a ring of four 32-row slots, so
-// three chunks are in flight without holding a register.  Each of the four
-// waves gathers 8 rows of a chunk, one whole 1 KiB row per instruction; lane
-// l fetches 16-byte unit l ^ f(r) of row r, which leaves the slot XOR-swizzled.
+// the instruction's LDS base + 16 l), into a ring of four 32-row slots, one
+// whole 1 KiB row per instruction, lane l fetching 16-byte unit l ^ f(r) of
+// row r, which leaves the slot XOR-swizzled.
 //
-// Wave w = hh + 2 dh (one per SIMD) owns heads 32 hh .. +31 and dims
-// 256 dh .. +255.  Per chunk of 32 entries:
-//   S^T (32 entries x 32 heads) = K (32 x 256) * Q^T (256 x 32)
-//       K fragments read from the slot, Q^T held in registers for the query;
-//   the two dim halves' partial scores are added through LDS (in the same
-//   order in both waves, so both hold the same scores), online softmax in
-//   fp32 (exp2 domain, lazily raised reference);
-//   O^T (256 dims x 32 heads) += V^T (256 x 32) * P^T (32 x 32)
-//       V^T read transposed (ds_read_b64_tr_b16) from the same slot.
-// All products are v_mfma_f32_16x16x32_bf16 with their accumulators in the
-// accumulation registers.  Per entry a CU moves 1 KiB into LDS, reads 2 KiB
-// of K and 2 KiB of V^T out of it and exchanges 256 B of partial scores; the
-// K and V^T of each dim half are read by the two head halves.
+// Wave w runs on SIMD w mod 4, two waves per SIMD, and the waves split the
+// two products by role so that every SIMD carries the same matrix work:
+//   waves 0, 1, 4, 5 (scores; two each on SIMDs 0, 1): scorer h holds Q^T of
+//     heads 16 h .. +15 for all 512 dims and per chunk of 32 entries computes
+//       S^T (32 entries x 16 heads) = K (32 x 512) * Q^T (512 x 16),
+//     runs the online softmax of its heads in fp32 (exp2 domain, lazily
+//     raised reference) and leaves P (bf16) and the heads' rescale factors
+//     in LDS; while one scorer of a SIMD is in its softmax the other keeps
+//     the matrix core busy;
+//   waves 2, 3, 6, 7 (values; two each on SIMDs 2, 3): value wave v holds
+//     O^T of dims 128 v .. +127 for all 64 heads and, one chunk behind, adds
+//       O^T (128 dims x 64 heads) += V^T (128 x 32) * P^T (32 x 64),
+//     V^T read transposed out of the slot (ds_read_b64_tr_b16); it also
+//     gathers 8 rows of every chunk.
+// All products are v_mfma_f32_16x16x32_bf16.  Per entry the CU reads K out of
+// LDS four times and V^T once, and no partial scores cross waves.  One
+// barrier per chunk: chunk c's scores and chunk c - 1's values run between
+// two barriers, while chunks c + 1 and c + 2 are in flight.
 //
 // Workgroup i runs on XCD i mod 8 (round-robin dispatch); queries are handed
 // out so each XCD takes a contiguous run, which keeps the window rows that
@@ -40,16 +44,16 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) const void global_cvoid;
 
-constexpr int kWv = 4;
+constexpr int kWv = 8;
 constexpr int kThr = 64 * kWv;
 constexpr int kCh = 32;                 // entries per chunk
 constexpr int kRowB = kDim * 2;         // one bf16 row
 constexpr int kSlotB = kCh * kRowB;     // 32 KiB per ring slot
 constexpr int kSlots = 4;               // chunk c lives in slot c % 4
-constexpr int kRowsPerWave = kCh / kWv; // rows of a chunk each wave gathers
+constexpr int kRowsPerValuer = kCh / 4; // rows of a chunk each value wave gathers
+constexpr int kPRowB = 80;              // one head's 32 probabilities (64 B), padded
+constexpr int kPBufB = kHeads * kPRowB;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;  // log2 headroom before the running max is raised
@@ -76,11 +80,28 @@ struct MqArgs {
   float scale_log2;  // softmax_scale * log2(e)
 };
 
-// 16-byte unit u of a slot row r sits at unit u ^ f(r), f swapping the two
-// 2-bit halves of r mod 16: sixteen rows at one unit (the K fragment reads)
-// and four aligned rows x four aligned units (the transposing reads) both
-// spread over all 16 bank groups; f touches only the low four bits of u.
-__device__ __forceinline__ int swz(int r, int u) { return u ^ (((r & 3) << 2) | ((r >> 2) & 3)); }
+// 16-byte unit u of slot row r sits at unit u ^ f(r), f(r) = 2 (r mod 4) +
+// (r / 4 mod 2) + 8 (r / 8 mod 2) < 16.  Sixteen consecutive rows at one unit
+// (the K fragments) take sixteen different units, any aligned eight of them
+// eight different units mod 8; four aligned rows x two adjacent units (the
+// transposing reads) take eight different units mod 8.  So both access
+// patterns spread over all LDS banks whether a cycle serves 128 or 256 bytes.
+__device__ __forceinline__ int swz(int r, int u) {
+  return u ^ ((2 * (r & 3)) | ((r >> 2) & 1) | (r & 8));
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)p;
+}
+
+// One 16-byte-per-lane DMA from global memory into LDS: lane l's bytes land
+// at lds + 16 l.  Issued as inline assembly so that the compiler, which
+// cannot tell ring slots apart, does not wait for every DMA in flight before
+// each LDS read; the kernel orders the DMAs itself (a vmcnt wait, then a
+// barrier, before a slot is read).
+__device__ __forceinline__ void dma_row16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+}
 
 // s_waitcnt with only the vector-memory count constrained (expcnt and lgkmcnt
 // at their maxima): vmcnt in bits 3:0 and 15:14.
@@ -88,7 +109,10 @@ __device__ __forceinline__ int swz(int r, int u) { return u ^ (((r & 3) << 2) | 
 
 __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[kSlots * kSlotB];
-  __shared__ __attribute__((aligned(16))) f32x4 xs[kWv][4][64];  // partial scores, one chunk at a time
+  __shared__ __attribute__((aligned(16))) uint8_t pbuf[2][kPBufB];  // P of chunk c in pbuf[c % 2]
+  __shared__ float alpha_s[2][kHeads];  // rescale factor of each head, valid where flag_s is set
+  __shared__ __attribute__((aligned(16))) uint32_t flag_s[2][4];  // [chunk % 2][head tile]: the tile's references moved
+  __shared__ float fin_s[kHeads];       // output factor of each head
   __shared__ int64_t ent_s[kMaxEntries];  // >= 0: window row; < 0: -(pool row) - 1
   __shared__ uint32_t wcnt_s[kWv];
 
@@ -100,18 +124,11 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
   const int item = xcd * per + (xcd < rem ? xcd : rem) + wslot;
   const int b = item / a.n_split, sp = item % a.n_split;
   if (b >= a.B) return;  // whole workgroup, before any barrier
-  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform role
+  const bool scorer = (wv & 2) == 0;
+  const int hq = (wv & 1) + 2 * (wv >> 2);  // scorer: head tile; value wave: dim quarter
   const int g = lane >> 4, l16 = lane & 15;
-  const int hh = wv & 1, dh = wv >> 1;
-
-  // ---- Q^T fragments: head 32 hh + 16 ht + l16, dims 256 dh + 32 s + 8 g .. +7 ----
-  bf16x8 qf[2][8];
-#pragma unroll
-  for (int ht = 0; ht < 2; ++ht) {
-    const uint16_t* qp = a.q + ((int64_t)b * kHeads + 32 * hh + 16 * ht + l16) * kDim + 256 * dh + 8 * g;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) qf[ht][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 32 * s));
-  }
 
   // ---- entry list: window rows, then the selected pool rows in list order ----
   int wl = a.win_kv ? a.win_len[b] : 0;
@@ -144,7 +161,7 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
     }
   }
   __syncthreads();
-  const int E = wl + (int)nsel;
+  const int E = __builtin_amdgcn_readfirstlane(wl + (int)nsel);  // uniform: the loops run on scalars
   // this workgroup's chunks: [c_beg, c_beg + nch) of the query's
   const int nch_all = (E + kCh - 1) / kCh;
   const int cps = (nch_all + a.n_split - 1) / a.n_split;
@@ -152,51 +169,27 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
   const int c_end = c_beg + cps < nch_all ? c_beg + cps : nch_all;
   const int nch = c_end > c_beg ? c_end - c_beg : 0;  // local chunk c is the query's c_beg + c
 
-  // ---- gather of chunk c into its slot: this wave's 8 rows, one DMA each;
-  // rows past the last entry repeat entry 0 (their probability is 0).  Lane
-  // i < 8 looks up the entry of row i ahead of time (entry_for); the DMAs
-  // then take each row from that lane, so no LDS round trip sits between
-  // them ----
-  auto entry_for = [&](int c) __attribute__((always_inline)) -> int64_t {
-    int e = (c_beg + c) * kCh + kRowsPerWave * wv + (lane & (kRowsPerWave - 1));
-    if (e >= E) e = 0;
-    return ent_s[e];
-  };
-  auto gather = [&](int c, int64_t evl) __attribute__((always_inline)) {
-    uint8_t* slot = ring + (c % kSlots) * kSlotB;
-    const uint32_t lo = (uint32_t)evl, hi = (uint32_t)((uint64_t)evl >> 32);
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) {
-      const int r = kRowsPerWave * wv + i;
-      const int64_t ev = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, i) << 32) |
-                                   (uint32_t)__builtin_amdgcn_readlane((int)lo, i));
-      const uint8_t* src = (ev < 0) ? a.comp_kv + (-ev - 1) * kRowB : a.win_kv + ev * kRowB;
-      __builtin_amdgcn_global_load_lds((global_cvoid*)(src + (swz(r, lane) << 4)),
-                                       (lds_void*)(slot + r * kRowB), 16, 0, 0);
-    }
-  };
-
-  // ---- per-lane LDS offsets within a slot ----
-  // K fragment (entry tile et, k-step s): row 16 et + l16, unit 32 dh + 4 s + g
-  //   -> ko[s & 3] + 256 (s >> 2) (+16 KiB for et = 1);
-  // V^T of dim tile dt (16 dims), rows 4 g + tj (+16): vo[dt & 7] + 256 (dt >> 3) (+16 KiB)
+  // Per-lane LDS offsets within a slot, for 16 x 16 x 32 fragments (lane (g,
+  // l16) holds row l16 of a 16-row tile and 8 consecutive values of its
+  // k-range):
+  //   K of k-step s (dims 32 s + 8 g ..), entry tile et: row 16 et + l16,
+  //     unit 4 s + g -> ko[s % 4] + 256 (s / 4) + 16 KiB et;
+  //   V^T of dim tile dt (dims 128 v + 16 dt ..), rows 4 g + tj (+16), the
+  //     transposing read's 8-byte piece -> vo[dt] (+16 KiB).
   const int tj = (lane >> 2) & 3, tc = lane & 3;
   const int r_lo = 4 * g + tj;
   uint32_t ko[4], vo[8];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) ko[j] = l16 * kRowB + 512 * dh + (swz(l16, 4 * j + g) << 4);
+  for (int j = 0; j < 4; ++j) ko[j] = l16 * kRowB + (swz(l16, 4 * j + g) << 4);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) vo[j] = r_lo * kRowB + 512 * dh + (swz(r_lo, 2 * j + (tc >> 1)) << 4) + 8 * (tc & 1);
+  for (int j = 0; j < 8; ++j) vo[j] = r_lo * kRowB + 256 * hq + (swz(r_lo, 2 * j + (tc >> 1)) << 4) + 8 * (tc & 1);
 
-  f32x4 acc[16][2];  // O^T tiles: [dim tile][head tile]
-#pragma unroll
-  for (int dt = 0; dt < 16; ++dt) acc[dt][0] = acc[dt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // running reference (log2 units) of the lane's two heads, the same in the
-  // four lanes of a head; the sums are this lane's share (reduced at the end)
-  float m_run[2] = {-__builtin_inff(), -__builtin_inff()}, l_run[2] = {0.f, 0.f};
-
-  // maximum / sum over the four lanes of a head (lanes l16 + 16 g): swap with
-  // the lane 32 away, then with the lane 16 away (gfx950 permlane swaps)
+  // ---- scorer state: the running reference (log2 units) of the lane's
+  // head, the same in its four lanes l16 + 16 g; the sum is this lane's
+  // share (reduced at the end) ----
+  float m_run = -__builtin_inff(), l_run = 0.f;
+  // maximum / sum over the four lanes of a head: swap with the lane 32 away,
+  // then with the lane 16 away (gfx950 permlane swaps)
   auto head_max = [&](float x) __attribute__((always_inline)) -> float {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -210,143 +203,170 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
     return __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
   };
 
-  // Chunk c: QK from slot c % 4, partial-score exchange (two barriers: one
-  // after the writes, one after the reads, so one buffer serves every chunk),
-  // the gather of chunk c + 3 into the slot chunk c - 1 used (every wave has
-  // finished with it by the first barrier), softmax, PV from slot c % 4.
-  // Chunk c + 1 must have landed before the second barrier: each wave waits
-  // for its own DMAs of c + 1 (issued two chunks earlier; those of c + 2 stay
-  // in flight).
-  auto step = [&](int c) __attribute__((always_inline)) {
+  // Scores and softmax of chunk c (scorers): P into pbuf[c % 2], the
+  // rescale factors into alpha_s / flag_s of the same parity.  Lane (g, l16)
+  // ends with head 16 hq + l16 and entries 4 g .. +3 of both entry tiles,
+  // exactly its group of the head's P row (see the value waves' P^T).
+  auto score = [&](int c, const bf16x8* qf) __attribute__((always_inline)) {
     const uint8_t* slot = ring + (c % kSlots) * kSlotB;
-    const int64_t ev_next = entry_for(c + 3);  // its LDS latency hides behind QK
-    f32x4 sa[2][2];  // [entry tile][head tile]
+    f32x4 sa[2][2] = {};  // [entry tile][k-step parity]
+    constexpr int kAhead = 8;  // K fragments in flight
+    bf16x8 kf[kAhead];
+    // read i: k-step i / 2, entry tile i % 2
+    auto kread = [&](int i) __attribute__((always_inline)) -> bf16x8 {
+      const int s = i >> 1, et = i & 1;
+      return *reinterpret_cast<const bf16x8*>(slot + ko[s & 3] + 256 * (s >> 2) + 16 * kRowB * et);
+    };
 #pragma unroll
-    for (int et = 0; et < 2; ++et) sa[et][0] = sa[et][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < kAhead; ++i) kf[i] = kread(i);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const uint32_t o = ko[s & 3] + 256 * (s >> 2);
-      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(slot + o);
-      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(slot + o + 16 * kRowB);
-      sa[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[0][s], sa[0][0], 0, 0, 0);
-      sa[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[1][s], sa[0][1], 0, 0, 0);
-      sa[1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[0][s], sa[1][0], 0, 0, 0);
-      sa[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[1][s], sa[1][1], 0, 0, 0);
+    for (int i = 0; i < 32; ++i) {
+      const bf16x8 k = kf[i % kAhead];
+      if (i + kAhead < 32) kf[i % kAhead] = kread(i + kAhead);
+      const int s = i >> 1, et = i & 1;
+      sa[et][s & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k, qf[s], sa[et][s & 1], 0, 0, 0);
     }
+    // keep kAhead fragment reads in flight ahead of the products (LDS reads:
+    // mask 0x100, matrix ops: 0x008)
+    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xs[wv][i][lane] = sa[i >> 1][i & 1];
-    __syncthreads();
-    f32x4 o4[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o4[i] = xs[wv ^ 2][i][lane];
-    if (c + 2 < nch) CSA2_WAIT_VMCNT(kRowsPerWave); else CSA2_WAIT_VMCNT(0);
-    __syncthreads();
-    if (c + 3 < nch) gather(c + 3, ev_next);
+    for (int i = 0; i < 32 - kAhead; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
 
-    // full scores: the dim-0 half's partial plus the dim-1 half's, in that order
-    float sv[2][8];  // [head tile][entry 4 g + k, then 16 + 4 g + k]
+    float sv[8];  // entry 16 (i / 4) + 4 g + i % 4
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int et = i >> 1, ht = i & 1;
+    for (int i = 0; i < 8; ++i) sv[i] = (sa[i >> 2][0][i & 3] + sa[i >> 2][1][i & 3]) * a.scale_log2;
+    if ((c_beg + c + 1) * kCh > E) {  // the query's last chunk: rows past E score -inf
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float s2 = dh ? o4[i][k] + sa[et][ht][k] : sa[et][ht][k] + o4[i][k];
-        const int e = (c_beg + c) * kCh + 16 * et + 4 * g + k;
-        sv[ht][4 * et + k] = (e < E) ? s2 * a.scale_log2 : -__builtin_inff();
-      }
+      for (int i = 0; i < 8; ++i)
+        if ((c_beg + c) * kCh + 16 * (i >> 2) + 4 * g + (i & 3) >= E) sv[i] = -__builtin_inff();
     }
+    float lm = sv[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) lm = fmaxf(lm, sv[i]);
     // The reference of a head moves only when one of its scores exceeds it by
-    // more than 2^kLazy, so probabilities stay below 2^kLazy.  Each lane tests
-    // its own scores; only when some lane would move does the wave reduce the
-    // chunk maxima over each head's four lanes and rescale.
-    float lm[2];
-#pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
-      lm[ht] = sv[ht][0];
-#pragma unroll
-      for (int k = 1; k < 8; ++k) lm[ht] = fmaxf(lm[ht], sv[ht][k]);
-    }
-    if (__ballot((lm[0] > m_run[0] + kLazy) || (lm[1] > m_run[1] + kLazy))) {
-      float alpha[2];
-#pragma unroll
-      for (int ht = 0; ht < 2; ++ht) {
-        const float cmax = head_max(lm[ht]);
-        alpha[ht] = 1.f;
-        if (cmax > m_run[ht] + kLazy) {  // false while both are -inf
-          alpha[ht] = __builtin_amdgcn_exp2f(m_run[ht] - cmax);
-          m_run[ht] = cmax;
-        }
-        l_run[ht] *= alpha[ht];
+    // more than 2^kLazy, so probabilities stay below 2^kLazy.  Only when some
+    // lane would move does the wave take the chunk maxima over each head's
+    // four lanes and rescale.
+    uint32_t moved = 0;
+    if (__ballot(lm > m_run + kLazy)) {
+      const float cmax = head_max(lm);
+      float alpha = 1.f;
+      if (cmax > m_run + kLazy) {  // false while both are -inf
+        alpha = __builtin_amdgcn_exp2f(m_run - cmax);
+        m_run = cmax;
       }
-#pragma unroll
-      for (int dt = 0; dt < 16; ++dt) acc[dt][0] *= alpha[0], acc[dt][1] *= alpha[1];
+      l_run *= alpha;
+      if (g == 0) alpha_s[c & 1][16 * hq + l16] = alpha;
+      moved = 1;
     }
+    if (lane == 0) flag_s[c & 1][hq] = moved;
     // every chunk holds at least one entry, so after the first the references
     // are finite
-    bf16x8 pb[2];
+    bf16x8 pb;
+    float rs = 0.f;
 #pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
-      float rs = 0.f;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float pv = __builtin_amdgcn_exp2f(sv[ht][k] - m_run[ht]);
-        rs += pv;
-        pb[ht][k] = (__bf16)pv;
-      }
-      l_run[ht] += rs;
+    for (int i = 0; i < 8; ++i) {
+      const float pv = __builtin_amdgcn_exp2f(sv[i] - m_run);
+      rs += pv;
+      pb[i] = (__bf16)pv;
     }
+    l_run += rs;
+    *reinterpret_cast<bf16x8*>(pbuf[c & 1] + (16 * hq + l16) * kPRowB + 16 * g) = pb;
+  };
 
-    // O^T += V^T P^T over 16 dim tiles; transposed reads run two tiles ahead
+  // value waves: O^T tiles [dim tile][head tile]; lane holds
+  // O^T[128 v + 16 dt + 4 g + k][16 ht + l16]
+  f32x4 acc[8][4];
+  // Values of chunk c (value waves).  P^T operand of head tile ht: lane (g,
+  // l16) takes head 16 ht + l16, entries 4 g .. +3 and 16 + 4 g .. +3 (entry
+  // group g of the head's P row), matching the V^T rows of the transposed
+  // reads.
+  auto values = [&](int c) __attribute__((always_inline)) {
+    const uint8_t* slot = ring + (c % kSlots) * kSlotB;
+    const uint4 fl = *reinterpret_cast<const uint4*>(flag_s[c & 1]);
+    if (__builtin_amdgcn_readfirstlane(fl.x | fl.y | fl.z | fl.w)) {
+      const uint32_t f4[4] = {fl.x, fl.y, fl.z, fl.w};
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) {
+        const float al = f4[ht] ? alpha_s[c & 1][16 * ht + l16] : 1.f;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) acc[dt][ht] *= al;
+      }
+    }
+    bf16x8 pt[4];
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+      pt[ht] = *reinterpret_cast<const bf16x8*>(pbuf[c & 1] + (16 * ht + l16) * kPRowB + 16 * g);
     auto vread = [&](int dt, s16x4& lo, s16x4& hi) __attribute__((always_inline)) {
-      const uint8_t* p = slot + vo[dt & 7] + 256 * (dt >> 3);
+      const uint8_t* p = slot + vo[dt];
       lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((__attribute__((address_space(3))) uint8_t*)(p)));
       hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_s16x4*)((__attribute__((address_space(3))) uint8_t*)(p + 16 * kRowB)));
     };
-    s16x4 vl[2], vh[2];
+    s16x4 vl[3], vh[3];
     vread(0, vl[0], vh[0]);
     vread(1, vl[1], vh[1]);
+    vread(2, vl[2], vh[2]);
 #pragma unroll
-    for (int dt = 0; dt < 16; ++dt) {
-      const s16x8 v8 = {vl[dt & 1][0], vl[dt & 1][1], vl[dt & 1][2], vl[dt & 1][3],
-                        vh[dt & 1][0], vh[dt & 1][1], vh[dt & 1][2], vh[dt & 1][3]};
-      if (dt + 2 < 16) vread(dt + 2, vl[dt & 1], vh[dt & 1]);
-      acc[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v8), pb[0], acc[dt][0], 0, 0, 0);
-      acc[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v8), pb[1], acc[dt][1], 0, 0, 0);
+    for (int dt = 0; dt < 8; ++dt) {
+      const int u = dt % 3;
+      const s16x8 v8 = {vl[u][0], vl[u][1], vl[u][2], vl[u][3], vh[u][0], vh[u][1], vh[u][2], vh[u][3]};
+      if (dt + 3 < 8) vread(dt + 3, vl[u], vh[u]);
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht)
+        acc[dt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v8), pt[ht], acc[dt][ht], 0, 0, 0);
+    }
+    // P^T and three V^T tiles ahead, then each tile's four products followed
+    // by the reads of the tile three ahead
+    __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
+#pragma unroll
+    for (int dt = 0; dt < 5; ++dt) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
+  };
+
+  // ---- gather of chunk c into its slot (value waves): this wave's 8 rows,
+  // one DMA each; rows past the last entry repeat entry 0 (their probability
+  // is 0).  Lane i < 8 looks up the entry of row i a chunk ahead
+  // (entry_for); the DMAs then take each row from that lane ----
+  auto entry_for = [&](int c) __attribute__((always_inline)) -> int64_t {
+    int e = (c_beg + c) * kCh + kRowsPerValuer * hq + (lane & (kRowsPerValuer - 1));
+    if (e >= E) e = 0;
+    return ent_s[e];
+  };
+  auto gather = [&](int c, int64_t evl) __attribute__((always_inline)) {
+    uint8_t* slot = ring + (c % kSlots) * kSlotB;
+    const uint32_t lo = (uint32_t)evl, hi = (uint32_t)((uint64_t)evl >> 32);
+#pragma unroll
+    for (int i = 0; i < kRowsPerValuer; ++i) {
+      const int r = kRowsPerValuer * hq + i;
+      const int64_t ev = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, i) << 32) |
+                                   (uint32_t)__builtin_amdgcn_readlane((int)lo, i));
+      const uint8_t* src = (ev < 0) ? a.comp_kv + (-ev - 1) * kRowB : a.win_kv + ev * kRowB;
+      dma_row16(src + (swz(r, lane) << 4), lds_addr(slot + r * kRowB));
     }
   };
 
-  if (nch > 0) {
-    // chunks 0, 1, 2 in flight; chunk 0 landed everywhere before the first step
-#pragma unroll
-    for (int c = 0; c < 3; ++c)
-      if (c < nch) gather(c, entry_for(c));
-    if (nch > 2) CSA2_WAIT_VMCNT(2 * kRowsPerWave);
-    else CSA2_WAIT_VMCNT(0);
-    __syncthreads();
-#pragma clang loop unroll(disable)
-    for (int c = 0; c < nch; ++c) step(c);
-  }
-
-  // ---- epilogue: lane holds O^T[256 dh + 16 dt + 4 g + k][32 hh + 16 ht + l16] ----
-#pragma unroll
-  for (int ht = 0; ht < 2; ++ht) {
-    const int head = 32 * hh + 16 * ht + l16;
-    const float lsum = head_sum(l_run[ht]);
+  // scorer: the factor that turns a head's sum into its output, and its
+  // lse (or, for entry splits, the partial max and sum)
+  auto finish = [&]() __attribute__((always_inline)) {
+    const float lsum = head_sum(l_run);
+    if (g != 0) return;
+    const int head = 16 * hq + l16;
     if (a.n_split > 1) {  // unnormalised partials, merged by attend_combine
       const int64_t pslot = ((int64_t)b * a.n_split + sp) * kHeads + head;
-      float* op = a.part_o + pslot * kDim + 256 * dh + 4 * g;
-#pragma unroll
-      for (int dt = 0; dt < 16; ++dt)
-        *reinterpret_cast<float4*>(op + 16 * dt) =
-            make_float4(acc[dt][ht][0], acc[dt][ht][1], acc[dt][ht][2], acc[dt][ht][3]);
-      if (g == 0 && dh == 0) {
-        a.part_ml[pslot * 2] = m_run[ht];
-        a.part_ml[pslot * 2 + 1] = lsum;
-      }
-      continue;
+      a.part_ml[pslot * 2] = m_run;
+      a.part_ml[pslot * 2 + 1] = lsum;
+      fin_s[head] = 1.f;
+      return;
     }
-    float M = m_run[ht], L = lsum, f;
+    float M = m_run, L = lsum, f;
     if (a.sink) {
       const float s2 = a.sink[head] * kLog2e;
       const float M2 = fmaxf(M, s2);
@@ -356,14 +376,86 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
     } else {
       f = (L > 0.f) ? 1.f / L : 0.f;
     }
-    float* op = a.out + ((int64_t)b * kHeads + head) * kDim + 256 * dh + 4 * g;
+    fin_s[head] = f;
+    if (a.lse) a.lse[(int64_t)b * kHeads + head] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -__builtin_inff();
+  };
+
+  // Iteration c: the gather of chunk c + 2 (into the slot chunk c - 2 used,
+  // released by the previous barrier), scores of chunk c, values of chunk
+  // c - 1; chunk c + 1 must have landed before the barrier (the value waves
+  // wait for their DMAs, issued an iteration earlier).  The roles run
+  // separate copies of the loop (the branch is wave-uniform) with the same
+  // barriers, so the scorers' Q^T and the value waves' accumulators never
+  // share a live range.
+  if (scorer) {
+    // Q^T fragments of head 16 hq + l16, dims 32 s + 8 g .. +7, held in this
+    // branch only.  The Q rows of the query's heads reach ring slots 2 and 3
+    // by DMA (head 16 hq + j at row 16 (hq % 2) + j of slot 2 + hq / 2) while
+    // the first two chunks are gathered (slots 2 and 3 take no chunk before
+    // the first barrier), and the fragments come out of LDS like the K
+    // fragments, so no global load of the compiler's is pending in the loop
+    // (it would make the compiler wait for every DMA there).
+    bf16x8 qf[16];
+    if (nch > 0) {
+      const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.q + ((int64_t)b * kHeads + 16 * hq) * kDim);
+      uint8_t* qs = ring + (2 + (hq >> 1)) * kSlotB + 16 * (hq & 1) * kRowB;
+#pragma unroll 4
+      for (int r = 0; r < 16; ++r) dma_row16(qsrc + r * kRowB + (swz(r, lane) << 4), lds_addr(qs + r * kRowB));
+      CSA2_WAIT_VMCNT(0);
+      asm volatile("" ::: "memory");  // the Q reads stay behind the wait
 #pragma unroll
-    for (int dt = 0; dt < 16; ++dt) {
+      for (int s = 0; s < 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qs + ko[s & 3] + 256 * (s >> 2));
+      __syncthreads();
+    }
+#pragma clang loop unroll(disable)
+    for (int c = 0; c < nch; ++c) {
+      score(c, qf);
+      __syncthreads();
+    }
+    finish();
+  } else {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) acc[dt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (nch > 0) {
+      int64_t ev_next = 0;
+      gather(0, entry_for(0));
+      if (nch > 1) gather(1, entry_for(1));
+      if (nch > 2) ev_next = entry_for(2);
+      if (nch > 1) CSA2_WAIT_VMCNT(kRowsPerValuer);
+      else CSA2_WAIT_VMCNT(0);
+      __syncthreads();
+#pragma clang loop unroll(disable)
+      for (int c = 0; c < nch; ++c) {
+        if (c + 2 < nch) {
+          gather(c + 2, ev_next);
+          if (c + 3 < nch) ev_next = entry_for(c + 3);
+        }
+        if (c > 0) values(c - 1);
+        if (c + 2 < nch) CSA2_WAIT_VMCNT(kRowsPerValuer);
+        else CSA2_WAIT_VMCNT(0);
+        __syncthreads();
+      }
+      values(nch - 1);
+    }
+  }
+  __syncthreads();
+  if (scorer) return;
+
+  // ---- value waves write O: lane holds O^T[128 v + 16 dt + 4 g + k][16 ht + l16] ----
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) {
+    const int head = 16 * ht + l16;
+    const float f = fin_s[head];
+    float* op = (a.n_split > 1 ? a.part_o + (((int64_t)b * a.n_split + sp) * kHeads + head) * kDim
+                               : a.out + ((int64_t)b * kHeads + head) * kDim) +
+                128 * hq + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
       const f32x4 v = acc[dt][ht] * f;
       *reinterpret_cast<float4*>(op + 16 * dt) = make_float4(v[0], v[1], v[2], v[3]);
     }
-    if (a.lse && g == 0 && dh == 0)
-      a.lse[(int64_t)b * kHeads + head] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -__builtin_inff();
   }
 }
 
