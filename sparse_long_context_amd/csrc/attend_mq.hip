@@ -45,7 +45,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int kWv = 8;
+constexpr int kWv = 12;
 constexpr int kThr = 64 * kWv;
 constexpr int kCh = 32;                 // entries per chunk
 constexpr int kRowB = kDim * 2;         // one bf16 row
@@ -126,8 +126,9 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
   if (b >= a.B) return;  // whole workgroup, before any barrier
   const int t = threadIdx.x, lane = t & 63;
   const int wv = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform role
-  const bool scorer = (wv & 2) == 0;
-  const int hq = (wv & 1) + 2 * (wv >> 2);  // scorer: head tile; value wave: dim quarter
+  const bool scorer = wv < 8 && (wv & 2) == 0;
+  const bool gatherer = wv >= 8;
+  const int hq = gatherer ? wv - 8 : (wv & 1) + 2 * (wv >> 2);  // scorer: head tile; value wave: dim quarter; gatherer: row group
   const int g = lane >> 4, l16 = lane & 15;
 
   // ---- entry list: window rows, then the selected pool rows in list order ----
@@ -413,11 +414,7 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
       __syncthreads();
     }
     finish();
-  } else {
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-      for (int ht = 0; ht < 4; ++ht) acc[dt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+  } else if (gatherer) {
     if (nch > 0) {
       int64_t ev_next = 0;
       gather(0, entry_for(0));
@@ -431,17 +428,30 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
         if (c + 2 < nch) {
           gather(c + 2, ev_next);
           if (c + 3 < nch) ev_next = entry_for(c + 3);
+          CSA2_WAIT_VMCNT(kRowsPerValuer);
+        } else {
+          CSA2_WAIT_VMCNT(0);
         }
+        __syncthreads();
+      }
+    }
+  } else {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) acc[dt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (nch > 0) {
+      __syncthreads();
+#pragma clang loop unroll(disable)
+      for (int c = 0; c < nch; ++c) {
         if (c > 0) values(c - 1);
-        if (c + 2 < nch) CSA2_WAIT_VMCNT(kRowsPerValuer);
-        else CSA2_WAIT_VMCNT(0);
         __syncthreads();
       }
       values(nch - 1);
     }
   }
   __syncthreads();
-  if (scorer) return;
+  if (scorer || gatherer) return;
 
   // ---- value waves write O: lane holds O^T[128 v + 16 dt + 4 g + k][16 ht + l16] ----
 #pragma unroll
