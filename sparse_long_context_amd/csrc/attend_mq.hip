@@ -34,6 +34,8 @@
 // Workgroup i runs on XCD i mod 8 (round-robin dispatch); queries are handed
 // out so each XCD takes a contiguous run, which keeps the window rows that
 // consecutive prefill queries share (127 of 128) in that XCD's L2.
+#include <type_traits>
+
 #include "csa2_internal.h"
 
 namespace csa2 {
@@ -57,6 +59,7 @@ constexpr int kPBufB = kHeads * kPRowB;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;  // log2 headroom before the running max is raised
+constexpr int kScorer = 0, kValuer = 1, kGatherer = 2;  // wave roles
 
 struct MqArgs {
   const int32_t* mode;
@@ -100,7 +103,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // each LDS read; the kernel orders the DMAs itself (a vmcnt wait, then a
 // barrier, before a slot is read).
 __device__ __forceinline__ void dma_row16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+  uint32_t m0_saved;  // the compiler treats m0 as reserved: keep its value
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(m0_saved)
+      : "v"(src), "s"(lds)
+      : "memory");
 }
 
 // s_waitcnt with only the vector-memory count constrained (expcnt and lgkmcnt
@@ -116,35 +124,57 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
   __shared__ int64_t ent_s[kMaxEntries];  // >= 0: window row; < 0: -(pool row) - 1
   __shared__ uint32_t wcnt_s[kWv];
 
-  // contiguous runs of (query, split) pairs per XCD: workgroup i -> XCD
-  // i % 8, slot i / 8
+  const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // wave-uniform role
+  const int role = wv >= 8 ? kGatherer : ((wv & 2) == 0 ? kScorer : kValuer);
+  const int hq = role == kGatherer ? wv - 8 : (wv & 1) + 2 * (wv >> 2);  // scorer: head tile; value wave: dim quarter; gatherer: row group
+  constexpr int kListThr = 8 * 64;
+
+  // The workgroups stay resident and take (query, split) items in turn: the
+  // items form contiguous runs per XCD (workgroup i runs on XCD i % 8), and
+  // the M workgroups of an XCD take every M-th item of its run, so each
+  // XCD's CUs work on neighbouring queries at any time.  One item's output
+  // stores drain while the next item is prepared.
+  const int n_items = a.B * a.n_split;
   const int nwg = (int)gridDim.x;
-  const int xcd = (int)blockIdx.x & 7, wslot = (int)blockIdx.x >> 3;
-  const int per = nwg >> 3, rem = nwg & 7;
-  const int item = xcd * per + (xcd < rem ? xcd : rem) + wslot;
+  const int xcd = (int)blockIdx.x & 7;
+  const int m_xcd = (nwg - xcd + 7) >> 3;
+  const int run_len = n_items / 8 + (xcd < n_items % 8 ? 1 : 0);
+  const int run0 = xcd * (n_items / 8) + (xcd < n_items % 8 ? xcd : n_items % 8);
+  // One copy of the item loop per role (the role is a template constant in
+  // each), so no role's registers stay live through another role's code;
+  // the copies pass the same barriers.
+  auto run = [&](auto role_c) __attribute__((always_inline)) {
+  constexpr int R = decltype(role_c)::value;
+  constexpr bool scorer = R == kScorer, gatherer = R == kGatherer, valuer = R == kValuer;
+#pragma clang loop unroll(disable)
+  for (int k_item = (int)blockIdx.x >> 3; k_item < run_len; k_item += m_xcd) {
+  const int item = run0 + k_item;
   const int b = item / a.n_split, sp = item % a.n_split;
-  if (b >= a.B) return;  // whole workgroup, before any barrier
-  const int t = threadIdx.x, lane = t & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform role
-  const bool scorer = wv < 8 && (wv & 2) == 0;
-  const bool gatherer = wv >= 8;
-  const int hq = gatherer ? wv - 8 : (wv & 1) + 2 * (wv >> 2);  // scorer: head tile; value wave: dim quarter; gatherer: row group
+  // The lane index is re-derived opaquely for every item, so the per-lane
+  // offsets of all three roles are not hoisted out of the item loop (they
+  // would stay live through every role's code).
+  int lane = (int)threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
   const int g = lane >> 4, l16 = lane & 15;
+  // thread index among the eight waves that are not value waves (they build
+  // the entry lists, so the value waves' output stores never delay a wait)
+  const int tl = (wv < 2 ? wv : (wv < 6 ? wv - 2 : wv - 4)) * 64 + lane;
 
   // ---- entry list: window rows, then the selected pool rows in list order ----
   int wl = a.win_kv ? a.win_len[b] : 0;
   wl = wl < 0 ? 0 : (wl > a.W ? a.W : wl);
   const int64_t w0 = a.win_row0[b];
-  for (int e = t; e < wl; e += kThr) ent_s[e] = w0 + e;
+  if (!valuer)
+    for (int e = tl; e < wl; e += kListThr) ent_s[e] = w0 + e;
   const int md = a.mode[b];
   uint32_t nsel = 0;
   if (md != CSA2_MODE_WINDOW && a.topk != nullptr && a.comp_kv != nullptr) {
     const int32_t plen = a.pool_len[b];
     const int64_t p0 = a.pool_row0[b];
     const int32_t* lst = a.topk + (int64_t)b * a.K;
-    for (int r0 = 0; r0 < a.K; r0 += kThr) {
-      const int k = r0 + t;
-      const int32_t idx = (k < a.K) ? lst[k] : -1;
+    for (int r0 = 0; r0 < a.K; r0 += kListThr) {
+      const int k = r0 + tl;
+      const int32_t idx = (!valuer && k < a.K) ? lst[k] : -1;
       const bool ok = (idx >= 0) & (idx < plen);
       const uint64_t m = __ballot(ok);
       if (lane == 0) wcnt_s[wv] = __popcll(m);
@@ -388,7 +418,7 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
   // separate copies of the loop (the branch is wave-uniform) with the same
   // barriers, so the scorers' Q^T and the value waves' accumulators never
   // share a live range.
-  if (scorer) {
+  if constexpr (scorer) {
     // Q^T fragments of head 16 hq + l16, dims 32 s + 8 g .. +7, held in this
     // branch only.  The Q rows of the query's heads reach ring slots 2 and 3
     // by DMA (head 16 hq + j at row 16 (hq % 2) + j of slot 2 + hq / 2) while
@@ -414,7 +444,7 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
       __syncthreads();
     }
     finish();
-  } else if (gatherer) {
+  } else if constexpr (gatherer) {
     if (nch > 0) {
       int64_t ev_next = 0;
       gather(0, entry_for(0));
@@ -451,8 +481,7 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
     }
   }
   __syncthreads();
-  if (scorer || gatherer) return;
-
+  if constexpr (valuer) {
   // ---- value waves write O: lane holds O^T[128 v + 16 dt + 4 g + k][16 ht + l16] ----
 #pragma unroll
   for (int ht = 0; ht < 4; ++ht) {
@@ -467,6 +496,12 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
       *reinterpret_cast<float4*>(op + 16 * dt) = make_float4(v[0], v[1], v[2], v[3]);
     }
   }
+  }
+  }  // items
+  };
+  if (role == kScorer) run(std::integral_constant<int, kScorer>{});
+  else if (role == kGatherer) run(std::integral_constant<int, kGatherer>{});
+  else run(std::integral_constant<int, kValuer>{});
 }
 
 }  // namespace
@@ -496,7 +531,15 @@ hipError_t launch_attend_mq(const csa2_dims& d, int32_t B, const csa2_batch& bt,
   a.K = d.index_topk;
   a.W = d.window;
   a.scale_log2 = d.softmax_scale * kLog2e;
-  hipLaunchKernelGGL(attend_mq_kernel, dim3((unsigned)(B * n_split)), dim3(kThr), 0, s, a);
+  // one resident workgroup per CU (its LDS rules out a second), each taking
+  // items in turn
+  int dev = 0, n_cu = 0;
+  hipError_t e0 = hipGetDevice(&dev);
+  if (e0 == hipSuccess) e0 = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e0 != hipSuccess) return e0;
+  const int64_t n_items = (int64_t)B * n_split;
+  const int grid = (int)(n_items < n_cu ? n_items : (n_cu > 0 ? n_cu : 1));
+  hipLaunchKernelGGL(attend_mq_kernel, dim3((unsigned)grid), dim3(kThr), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_split == 1) return e;
   return launch_attend_combine(B, n_split, a.part_o, a.part_ml, sink, out, lse, s);
