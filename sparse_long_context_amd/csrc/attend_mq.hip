@@ -146,8 +146,32 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
   auto run = [&](auto role_c) __attribute__((always_inline)) {
   constexpr int R = decltype(role_c)::value;
   constexpr bool scorer = R == kScorer, gatherer = R == kGatherer, valuer = R == kValuer;
+  // An item's metadata and selection list are loaded one item ahead (thread
+  // tl of the list builders holds list entry tl; K <= 512), so their latency
+  // hides under the previous item's chunks.
+  struct Pf {
+    int32_t wl, md, plen, idx;
+    int64_t w0, p0;
+  };
+  auto prefetch = [&](int item_, int tl_) __attribute__((always_inline)) -> Pf {
+    const int bb = item_ / a.n_split;
+    Pf p;
+    p.wl = a.win_kv ? a.win_len[bb] : 0;
+    p.w0 = a.win_row0[bb];
+    p.md = a.mode[bb];
+    p.plen = a.pool_len[bb];
+    p.p0 = a.pool_row0[bb];
+    p.idx = (!valuer && a.topk != nullptr && tl_ < a.K) ? a.topk[(int64_t)bb * a.K + tl_] : -1;
+    return p;
+  };
+  const int k_first = (int)blockIdx.x >> 3;
+  Pf pf = {};
+  if (k_first < run_len) {
+    int lane0 = (int)threadIdx.x & 63;
+    pf = prefetch(run0 + k_first, (wv < 2 ? wv : (wv < 6 ? wv - 2 : wv - 4)) * 64 + lane0);
+  }
 #pragma clang loop unroll(disable)
-  for (int k_item = (int)blockIdx.x >> 3; k_item < run_len; k_item += m_xcd) {
+  for (int k_item = k_first; k_item < run_len; k_item += m_xcd) {
   const int item = run0 + k_item;
   const int b = item / a.n_split, sp = item % a.n_split;
   // The lane index is re-derived opaquely for every item, so the per-lane
@@ -159,22 +183,28 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
   // thread index among the eight waves that are not value waves (they build
   // the entry lists, so the value waves' output stores never delay a wait)
   const int tl = (wv < 2 ? wv : (wv < 6 ? wv - 2 : wv - 4)) * 64 + lane;
+  const Pf cur = pf;
+  if (k_item + m_xcd < run_len) pf = prefetch(item + m_xcd, tl);
+  // The scalar loads of the prefetch must have returned before a chunk loop
+  // starts: while one is outstanding the compiler can only wait for all LDS
+  // reads at once (lgkmcnt(0)).
+  auto settle = [&]() __attribute__((always_inline)) {
+    asm volatile("" ::"s"(pf.wl), "s"(pf.md), "s"(pf.plen), "s"(pf.w0), "s"(pf.p0));
+  };
 
   // ---- entry list: window rows, then the selected pool rows in list order ----
-  int wl = a.win_kv ? a.win_len[b] : 0;
+  int wl = cur.wl;
   wl = wl < 0 ? 0 : (wl > a.W ? a.W : wl);
-  const int64_t w0 = a.win_row0[b];
+  const int64_t w0 = cur.w0;
   if (!valuer)
     for (int e = tl; e < wl; e += kListThr) ent_s[e] = w0 + e;
-  const int md = a.mode[b];
+  const int md = cur.md;
   uint32_t nsel = 0;
   if (md != CSA2_MODE_WINDOW && a.topk != nullptr && a.comp_kv != nullptr) {
-    const int32_t plen = a.pool_len[b];
-    const int64_t p0 = a.pool_row0[b];
-    const int32_t* lst = a.topk + (int64_t)b * a.K;
-    for (int r0 = 0; r0 < a.K; r0 += kListThr) {
-      const int k = r0 + tl;
-      const int32_t idx = (!valuer && k < a.K) ? lst[k] : -1;
+    const int32_t plen = cur.plen;
+    const int64_t p0 = cur.p0;
+    {
+      const int32_t idx = cur.idx;
       const bool ok = (idx >= 0) & (idx < plen);
       const uint64_t m = __ballot(ok);
       if (lane == 0) wcnt_s[wv] = __popcll(m);
@@ -206,14 +236,16 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
   //   K of k-step s (dims 32 s + 8 g ..), entry tile et: row 16 et + l16,
   //     unit 4 s + g -> ko[s % 4] + 256 (s / 4) + 16 KiB et;
   //   V^T of dim tile dt (dims 128 v + 16 dt ..), rows 4 g + tj (+16), the
-  //     transposing read's 8-byte piece -> vo[dt] (+16 KiB).
+  //     transposing read's 8-byte piece -> vo0 + 32 (dt ^ vf) (+16 KiB), since
+  //     (2 dt + b) ^ f(r) = 2 (dt ^ f(r) / 2) + (b ^ f(r) % 2).
   const int tj = (lane >> 2) & 3, tc = lane & 3;
   const int r_lo = 4 * g + tj;
-  uint32_t ko[4], vo[8];
+  uint32_t ko[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) ko[j] = l16 * kRowB + (swz(l16, 4 * j + g) << 4);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) vo[j] = r_lo * kRowB + 256 * hq + (swz(r_lo, 2 * j + (tc >> 1)) << 4) + 8 * (tc & 1);
+  const int vf_full = swz(r_lo, 0);
+  const int vf = vf_full >> 1;
+  const uint32_t vo0 = r_lo * kRowB + 256 * hq + 16 * ((tc >> 1) ^ (vf_full & 1)) + 8 * (tc & 1);
 
   // ---- scorer state: the running reference (log2 units) of the lane's
   // head, the same in its four lanes l16 + 16 g; the sum is this lane's
@@ -332,34 +364,38 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht)
       pt[ht] = *reinterpret_cast<const bf16x8*>(pbuf[c & 1] + (16 * ht + l16) * kPRowB + 16 * g);
+    // re-derived opaquely per chunk so the eight tile offsets are not kept
+    // in registers through the loop (the accumulators need them)
+    uint32_t vbase = vo0;
+    int vfx = vf;
+    asm volatile("" : "+v"(vbase), "+v"(vfx));
     auto vread = [&](int dt, s16x4& lo, s16x4& hi) __attribute__((always_inline)) {
-      const uint8_t* p = slot + vo[dt];
+      const uint8_t* p = slot + vbase + 32 * (dt ^ vfx);
       lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((__attribute__((address_space(3))) uint8_t*)(p)));
       hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_s16x4*)((__attribute__((address_space(3))) uint8_t*)(p + 16 * kRowB)));
     };
-    s16x4 vl[3], vh[3];
+    s16x4 vl[2], vh[2];
     vread(0, vl[0], vh[0]);
     vread(1, vl[1], vh[1]);
-    vread(2, vl[2], vh[2]);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const int u = dt % 3;
+      const int u = dt % 2;
       const s16x8 v8 = {vl[u][0], vl[u][1], vl[u][2], vl[u][3], vh[u][0], vh[u][1], vh[u][2], vh[u][3]};
-      if (dt + 3 < 8) vread(dt + 3, vl[u], vh[u]);
+      if (dt + 2 < 8) vread(dt + 2, vl[u], vh[u]);
 #pragma unroll
       for (int ht = 0; ht < 4; ++ht)
         acc[dt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v8), pt[ht], acc[dt][ht], 0, 0, 0);
     }
-    // P^T and three V^T tiles ahead, then each tile's four products followed
-    // by the reads of the tile three ahead
-    __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
+    // P^T and two V^T tiles ahead, then each tile's four products followed
+    // by the reads of the tile two ahead
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-    for (int dt = 0; dt < 5; ++dt) {
+    for (int dt = 0; dt < 6; ++dt) {
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   };
 
   // ---- gather of chunk c into its slot (value waves): this wave's 8 rows,
@@ -438,6 +474,7 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
       for (int s = 0; s < 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qs + ko[s & 3] + 256 * (s >> 2));
       __syncthreads();
     }
+    settle();
 #pragma clang loop unroll(disable)
     for (int c = 0; c < nch; ++c) {
       score(c, qf);
@@ -453,6 +490,7 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
       if (nch > 1) CSA2_WAIT_VMCNT(kRowsPerValuer);
       else CSA2_WAIT_VMCNT(0);
       __syncthreads();
+      settle();
 #pragma clang loop unroll(disable)
       for (int c = 0; c < nch; ++c) {
         if (c + 2 < nch) {
@@ -472,6 +510,7 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
       for (int ht = 0; ht < 4; ++ht) acc[dt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (nch > 0) {
       __syncthreads();
+      settle();
 #pragma clang loop unroll(disable)
       for (int c = 0; c < nch; ++c) {
         if (c > 0) values(c - 1);
