@@ -83,14 +83,17 @@ struct MqArgs {
   float scale_log2;  // softmax_scale * log2(e)
 };
 
-// 16-byte unit u of slot row r sits at unit u ^ f(r), f(r) = 2 (r mod 4) +
-// (r / 4 mod 2) + 8 (r / 8 mod 2) < 16.  Sixteen consecutive rows at one unit
-// (the K fragments) take sixteen different units, any aligned eight of them
-// eight different units mod 8; four aligned rows x two adjacent units (the
-// transposing reads) take eight different units mod 8.  So both access
-// patterns spread over all LDS banks whether a cycle serves 128 or 256 bytes.
+// 16-byte unit u of slot row r sits at unit u ^ f(r), with f(r) =
+// 2 (r mod 4) + (r / 4 mod 2) + 8 ((r / 4 xor r / 8) mod 2) < 16.
+//   K fragments (row r = 16-row tile row, one unit): rows 0..15 take sixteen
+//     different units, rows 0..7 and 8..15 eight different units mod 8;
+//   transposing reads (rows 4 g + 0..3, units 2 j and 2 j + 1, 8 bytes per
+//     lane): one group of four rows takes eight different units mod 8, and
+//     the groups g = 0, 1 (and 2, 3) differ in bit 3.
+// So both patterns spread over all LDS banks whether a cycle serves 128 or
+// 256 bytes.
 __device__ __forceinline__ int swz(int r, int u) {
-  return u ^ ((2 * (r & 3)) | ((r >> 2) & 1) | (r & 8));
+  return u ^ ((2 * (r & 3)) | ((r >> 2) & 1) | ((((r >> 2) ^ (r >> 3)) & 1) << 3));
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
