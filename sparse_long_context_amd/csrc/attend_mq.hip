@@ -125,38 +125,42 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t flag_s[2][4];  // [chunk % 2][head tile]: the tile's references moved
   __shared__ float fin_s[kHeads];       // output factor of each head
   __shared__ int64_t ent_s[kMaxEntries];  // >= 0: window row; < 0: -(pool row) - 1
-  __shared__ uint32_t wcnt_s[kWv];
+  __shared__ int32_t item_e_s[2];       // entry count of the item, by item parity
 
   const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // wave-uniform role
   const int role = wv >= 8 ? kGatherer : ((wv & 2) == 0 ? kScorer : kValuer);
   const int hq = role == kGatherer ? wv - 8 : (wv & 1) + 2 * (wv >> 2);  // scorer: head tile; value wave: dim quarter; gatherer: row group
-  constexpr int kListThr = 8 * 64;
 
   // The workgroups stay resident and take (query, split) items in turn: the
   // items form contiguous runs per XCD (workgroup i runs on XCD i % 8), and
   // the M workgroups of an XCD take every M-th item of its run, so each
-  // XCD's CUs work on neighbouring queries at any time.  One item's output
-  // stores drain while the next item is prepared.
+  // XCD's CUs work on neighbouring queries at any time.
   const int n_items = a.B * a.n_split;
   const int nwg = (int)gridDim.x;
   const int xcd = (int)blockIdx.x & 7;
   const int m_xcd = (nwg - xcd + 7) >> 3;
   const int run_len = n_items / 8 + (xcd < n_items % 8 ? 1 : 0);
   const int run0 = xcd * (n_items / 8) + (xcd < n_items % 8 ? xcd : n_items % 8);
+  const int k_first = (int)blockIdx.x >> 3;
   // One copy of the item loop per role (the role is a template constant in
   // each), so no role's registers stay live through another role's code;
-  // the copies pass the same barriers.
+  // the copies pass the same barriers: per item one after the first rows
+  // have landed, one per chunk, one at the end.
   auto run = [&](auto role_c) __attribute__((always_inline)) {
   constexpr int R = decltype(role_c)::value;
   constexpr bool scorer = R == kScorer, gatherer = R == kGatherer, valuer = R == kValuer;
-  // An item's metadata and selection list are loaded one item ahead (thread
-  // tl of the list builders holds list entry tl; K <= 512), so their latency
-  // hides under the previous item's chunks.
+  // ---- entry lists (gather waves): an item's metadata and selection list
+  // are loaded one item ahead into the gather waves' registers (lane l holds
+  // list entries 64 r + l), and each gather wave compacts the list into
+  // ent_s itself (the four write the same values), so a list needs no
+  // barrier of its own and the value waves' output stores of the previous
+  // item drain while the first rows of the next are on their way ----
   struct Pf {
-    int32_t wl, md, plen, idx;
+    int32_t wl, md, plen;
     int64_t w0, p0;
+    int32_t idx[8];
   };
-  auto prefetch = [&](int item_, int tl_) __attribute__((always_inline)) -> Pf {
+  auto prefetch = [&](int item_, int lane_) __attribute__((always_inline)) -> Pf {
     const int bb = item_ / a.n_split;
     Pf p;
     p.wl = a.win_kv ? a.win_len[bb] : 0;
@@ -164,74 +168,66 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
     p.md = a.mode[bb];
     p.plen = a.pool_len[bb];
     p.p0 = a.pool_row0[bb];
-    p.idx = (!valuer && a.topk != nullptr && tl_ < a.K) ? a.topk[(int64_t)bb * a.K + tl_] : -1;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int k = 64 * r + lane_;
+      p.idx[r] = (a.topk != nullptr && k < a.K) ? a.topk[(int64_t)bb * a.K + k] : -1;
+    }
     return p;
   };
-  const int k_first = (int)blockIdx.x >> 3;
   Pf pf = {};
-  if (k_first < run_len) {
-    int lane0 = (int)threadIdx.x & 63;
-    pf = prefetch(run0 + k_first, (wv < 2 ? wv : (wv < 6 ? wv - 2 : wv - 4)) * 64 + lane0);
-  }
+  if constexpr (gatherer)
+    if (k_first < run_len) pf = prefetch(run0 + k_first, (int)threadIdx.x & 63);
+  // value waves: O^T tiles [dim tile][head tile]; lane holds
+  // O^T[128 v + 16 dt + 4 g + k][16 ht + l16]; the output of item
+  // (prev_b, prev_sp) waits in them until the next item starts
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) acc[dt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int prev_b = -1, prev_sp = 0;
+  auto write_out = [&](int b_, int sp_) __attribute__((always_inline)) {
+    // lane offset re-derived here, so no output address stays live through
+    // the loops
+    int lane_ = (int)threadIdx.x & 63;
+    asm volatile("" : "+v"(lane_));
+    const int g_ = lane_ >> 4, l16_ = lane_ & 15;
+    float* obase = a.n_split > 1 ? a.part_o + ((int64_t)b_ * a.n_split + sp_) * kHeads * kDim
+                                 : a.out + (int64_t)b_ * kHeads * kDim;
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) {
+      const int head = 16 * ht + l16_;
+      const float f = fin_s[head];
+      float* op = obase + head * kDim + 128 * hq + 4 * g_;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const f32x4 v = acc[dt][ht] * f;
+        *reinterpret_cast<float4*>(op + 16 * dt) = make_float4(v[0], v[1], v[2], v[3]);
+        acc[dt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
+  int par = 0;  // item parity (item_e_s)
 #pragma clang loop unroll(disable)
   for (int k_item = k_first; k_item < run_len; k_item += m_xcd) {
   const int item = run0 + k_item;
   const int b = item / a.n_split, sp = item % a.n_split;
   // The lane index is re-derived opaquely for every item, so the per-lane
-  // offsets of all three roles are not hoisted out of the item loop (they
-  // would stay live through every role's code).
+  // offsets are not hoisted out of the item loop.
   int lane = (int)threadIdx.x & 63;
   asm volatile("" : "+v"(lane));
   const int g = lane >> 4, l16 = lane & 15;
-  // thread index among the eight waves that are not value waves (they build
-  // the entry lists, so the value waves' output stores never delay a wait)
-  const int tl = (wv < 2 ? wv : (wv < 6 ? wv - 2 : wv - 4)) * 64 + lane;
-  const Pf cur = pf;
-  if (k_item + m_xcd < run_len) pf = prefetch(item + m_xcd, tl);
-  // The scalar loads of the prefetch must have returned before a chunk loop
-  // starts: while one is outstanding the compiler can only wait for all LDS
-  // reads at once (lgkmcnt(0)).
-  auto settle = [&]() __attribute__((always_inline)) {
-    asm volatile("" ::"s"(pf.wl), "s"(pf.md), "s"(pf.plen), "s"(pf.w0), "s"(pf.p0));
+  // the item's entries and its chunks [c_beg, c_beg + nch) of the query's
+  int E = 0, c_beg = 0, nch = 0;
+  auto set_entries = [&](int E_) __attribute__((always_inline)) {
+    E = __builtin_amdgcn_readfirstlane(E_);  // uniform: the loops run on scalars
+    const int nch_all = (E + kCh - 1) / kCh;
+    const int cps = (nch_all + a.n_split - 1) / a.n_split;
+    c_beg = sp * cps;
+    const int c_end = c_beg + cps < nch_all ? c_beg + cps : nch_all;
+    nch = c_end > c_beg ? c_end - c_beg : 0;  // local chunk c is the query's c_beg + c
   };
-
-  // ---- entry list: window rows, then the selected pool rows in list order ----
-  int wl = cur.wl;
-  wl = wl < 0 ? 0 : (wl > a.W ? a.W : wl);
-  const int64_t w0 = cur.w0;
-  if (!valuer)
-    for (int e = tl; e < wl; e += kListThr) ent_s[e] = w0 + e;
-  const int md = cur.md;
-  uint32_t nsel = 0;
-  if (md != CSA2_MODE_WINDOW && a.topk != nullptr && a.comp_kv != nullptr) {
-    const int32_t plen = cur.plen;
-    const int64_t p0 = cur.p0;
-    {
-      const int32_t idx = cur.idx;
-      const bool ok = (idx >= 0) & (idx < plen);
-      const uint64_t m = __ballot(ok);
-      if (lane == 0) wcnt_s[wv] = __popcll(m);
-      __syncthreads();
-      uint32_t before = nsel, tot = 0;
-#pragma unroll
-      for (int w = 0; w < kWv; ++w) {
-        before += (w < wv) ? wcnt_s[w] : 0u;
-        tot += wcnt_s[w];
-      }
-      before += __popcll(m & ((1ull << lane) - 1ull));
-      if (ok) ent_s[wl + before] = -(p0 + idx) - 1;
-      nsel += tot;
-      __syncthreads();
-    }
-  }
-  __syncthreads();
-  const int E = __builtin_amdgcn_readfirstlane(wl + (int)nsel);  // uniform: the loops run on scalars
-  // this workgroup's chunks: [c_beg, c_beg + nch) of the query's
-  const int nch_all = (E + kCh - 1) / kCh;
-  const int cps = (nch_all + a.n_split - 1) / a.n_split;
-  const int c_beg = sp * cps;
-  const int c_end = c_beg + cps < nch_all ? c_beg + cps : nch_all;
-  const int nch = c_end > c_beg ? c_end - c_beg : 0;  // local chunk c is the query's c_beg + c
 
   // Per-lane LDS offsets within a slot, for 16 x 16 x 32 fragments (lane (g,
   // l16) holds row l16 of a 16-row tile and 8 consecutive values of its
@@ -344,9 +340,6 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
     *reinterpret_cast<bf16x8*>(pbuf[c & 1] + (16 * hq + l16) * kPRowB + 16 * g) = pb;
   };
 
-  // value waves: O^T tiles [dim tile][head tile]; lane holds
-  // O^T[128 v + 16 dt + 4 g + k][16 ht + l16]
-  f32x4 acc[8][4];
   // Values of chunk c (value waves).  P^T operand of head tile ht: lane (g,
   // l16) takes head 16 ht + l16, entries 4 g .. +3 and 16 + 4 g .. +3 (entry
   // group g of the head's P row), matching the V^T rows of the transposed
@@ -450,23 +443,58 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
     if (a.lse) a.lse[(int64_t)b * kHeads + head] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -__builtin_inff();
   };
 
-  // Iteration c: the gather of chunk c + 2 (into the slot chunk c - 2 used,
-  // released by the previous barrier), scores of chunk c, values of chunk
-  // c - 1; chunk c + 1 must have landed before the barrier (the value waves
-  // wait for their DMAs, issued an iteration earlier).  The roles run
-  // separate copies of the loop (the branch is wave-uniform) with the same
-  // barriers, so the scorers' Q^T and the value waves' accumulators never
-  // share a live range.
-  if constexpr (scorer) {
-    // Q^T fragments of head 16 hq + l16, dims 32 s + 8 g .. +7, held in this
-    // branch only.  The Q rows of the query's heads reach ring slots 2 and 3
-    // by DMA (head 16 hq + j at row 16 (hq % 2) + j of slot 2 + hq / 2) while
-    // the first two chunks are gathered (slots 2 and 3 take no chunk before
-    // the first barrier), and the fragments come out of LDS like the K
-    // fragments, so no global load of the compiler's is pending in the loop
-    // (it would make the compiler wait for every DMA there).
+  if constexpr (gatherer) {
+    // ---- this item's list, then its first two chunks ----
+    const Pf cur = pf;
+    int wl = cur.wl;
+    wl = wl < 0 ? 0 : (wl > a.W ? a.W : wl);
+    for (int e = lane; e < wl; e += 64) ent_s[e] = cur.w0 + e;
+    int nsel = 0;
+    if (cur.md != CSA2_MODE_WINDOW && a.topk != nullptr && a.comp_kv != nullptr) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const bool ok = (cur.idx[r] >= 0) & (cur.idx[r] < cur.plen);
+        const uint64_t m = __ballot(ok);
+        if (ok) ent_s[wl + nsel + __popcll(m & ((1ull << lane) - 1ull))] = -(cur.p0 + cur.idx[r]) - 1;
+        nsel += __popcll(m);
+      }
+    }
+    set_entries(wl + nsel);
+    if (hq == 0 && lane == 0) item_e_s[par] = E;
+    // the next item's list loads go out before this item's first rows, so
+    // the wait for those covers them
+    if (k_item + m_xcd < run_len) pf = prefetch(item + m_xcd, lane);
+    int64_t ev_next = 0;
+    if (nch > 0) gather(0, entry_for(0));
+    if (nch > 1) gather(1, entry_for(1));
+    if (nch > 2) ev_next = entry_for(2);
+    if (nch > 1) CSA2_WAIT_VMCNT(kRowsPerValuer);
+    else CSA2_WAIT_VMCNT(0);
+    __syncthreads();
+    // the next item's scalar loads have returned before the chunk loop (while
+    // one is outstanding the compiler can only wait for all LDS reads at once)
+    asm volatile("" ::"s"(pf.wl), "s"(pf.md), "s"(pf.plen), "s"(pf.w0), "s"(pf.p0));
+#pragma clang loop unroll(disable)
+    for (int c = 0; c < nch; ++c) {
+      if (c + 2 < nch) {
+        gather(c + 2, ev_next);
+        if (c + 3 < nch) ev_next = entry_for(c + 3);
+        CSA2_WAIT_VMCNT(kRowsPerValuer);
+      } else {
+        CSA2_WAIT_VMCNT(0);
+      }
+      __syncthreads();
+    }
+  } else if constexpr (scorer) {
+    // Q^T fragments of head 16 hq + l16, dims 32 s + 8 g .. +7.  The Q rows
+    // of the query's heads reach ring slots 2 and 3 by DMA (head 16 hq + j at
+    // row 16 (hq % 2) + j of slot 2 + hq / 2) while the first two chunks are
+    // gathered (slots 2 and 3 take no chunk before the first barrier), and
+    // the fragments come out of LDS like the K fragments, so no global load
+    // of the compiler's is pending in the loop (it would make the compiler
+    // wait for every DMA there).
     bf16x8 qf[16];
-    if (nch > 0) {
+    {
       const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.q + ((int64_t)b * kHeads + 16 * hq) * kDim);
       uint8_t* qs = ring + (2 + (hq >> 1)) * kSlotB + 16 * (hq & 1) * kRowB;
 #pragma unroll 4
@@ -475,71 +503,35 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
       asm volatile("" ::: "memory");  // the Q reads stay behind the wait
 #pragma unroll
       for (int s = 0; s < 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qs + ko[s & 3] + 256 * (s >> 2));
-      __syncthreads();
     }
-    settle();
+    __syncthreads();
+    set_entries(item_e_s[par]);
 #pragma clang loop unroll(disable)
     for (int c = 0; c < nch; ++c) {
       score(c, qf);
       __syncthreads();
     }
     finish();
-  } else if constexpr (gatherer) {
-    if (nch > 0) {
-      int64_t ev_next = 0;
-      gather(0, entry_for(0));
-      if (nch > 1) gather(1, entry_for(1));
-      if (nch > 2) ev_next = entry_for(2);
-      if (nch > 1) CSA2_WAIT_VMCNT(kRowsPerValuer);
-      else CSA2_WAIT_VMCNT(0);
-      __syncthreads();
-      settle();
-#pragma clang loop unroll(disable)
-      for (int c = 0; c < nch; ++c) {
-        if (c + 2 < nch) {
-          gather(c + 2, ev_next);
-          if (c + 3 < nch) ev_next = entry_for(c + 3);
-          CSA2_WAIT_VMCNT(kRowsPerValuer);
-        } else {
-          CSA2_WAIT_VMCNT(0);
-        }
-        __syncthreads();
-      }
-    }
   } else {
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-      for (int ht = 0; ht < 4; ++ht) acc[dt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (nch > 0) {
-      __syncthreads();
-      settle();
+    // the previous item's output (its factors are in fin_s since the last
+    // barrier) drains while the first rows of this one are gathered
+    if (prev_b >= 0) write_out(prev_b, prev_sp);
+    __syncthreads();
+    set_entries(item_e_s[par]);
 #pragma clang loop unroll(disable)
-      for (int c = 0; c < nch; ++c) {
-        if (c > 0) values(c - 1);
-        __syncthreads();
-      }
-      values(nch - 1);
+    for (int c = 0; c < nch; ++c) {
+      if (c > 0) values(c - 1);
+      __syncthreads();
     }
+    if (nch > 0) values(nch - 1);
+    prev_b = b;
+    prev_sp = sp;
   }
   __syncthreads();
-  if constexpr (valuer) {
-  // ---- value waves write O: lane holds O^T[128 v + 16 dt + 4 g + k][16 ht + l16] ----
-#pragma unroll
-  for (int ht = 0; ht < 4; ++ht) {
-    const int head = 16 * ht + l16;
-    const float f = fin_s[head];
-    float* op = (a.n_split > 1 ? a.part_o + (((int64_t)b * a.n_split + sp) * kHeads + head) * kDim
-                               : a.out + ((int64_t)b * kHeads + head) * kDim) +
-                128 * hq + 4 * g;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const f32x4 v = acc[dt][ht] * f;
-      *reinterpret_cast<float4*>(op + 16 * dt) = make_float4(v[0], v[1], v[2], v[3]);
-    }
-  }
-  }
+  par ^= 1;
   }  // items
+  if constexpr (valuer)
+    if (prev_b >= 0) write_out(prev_b, prev_sp);
   };
   if (role == kScorer) run(std::integral_constant<int, kScorer>{});
   else if (role == kGatherer) run(std::integral_constant<int, kGatherer>{});
