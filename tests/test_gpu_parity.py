@@ -271,6 +271,53 @@ def test_decode_many_queries_all_heads_kernel(kv):
     compare(inp, sg, og, lg, queries=[0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 150, 299], sink=sink, scale=0.9)
 
 
+def test_attend_resident_many_items():
+    # 1,100 queries over the 256 resident workgroups (four or five items each,
+    # one workgroup per CU): ragged entry counts, all four modes, queries with
+    # no entry at all (zero output, -inf lse) between full ones, REINDEX lists
+    # with holes; sampled at the start, middle and end of the item runs
+    rng = np.random.default_rng(31)
+    B = 1100
+    ctx = rng.integers(1, 9000, size=B)
+    modes = rng.integers(0, 4, size=B).astype(np.int32)
+    ratios = np.where(modes == 3, 0, 4).astype(np.int32)
+    dims = small_dims()
+    inp = synth.decode_batch(31, list(ctx), list(modes), list(ratios), dims=dims)
+    synth.add_reindex_lists(inp, 31, frac=0.3)
+    empty = [5, 6, 546, 1099]
+    for b in empty:  # window-only with an empty window: no entries
+        inp["mode"][b] = synth.MODE_WINDOW
+        inp["ratio"][b] = 0
+        inp["win_len"][b] = 0
+        inp["pool_len"][b] = 0
+    say(f"decode B={B} resident all-heads kernel, {len(empty)} empty queries")
+    _, sg, og, lg = run_decode(inp)
+    for b in empty:
+        assert not og[b].any() and np.all(np.isneginf(lg[b])), f"query {b}: empty query output"
+    qs = sorted(set([0, 1, 2, 3, 4, 7, 8, 255, 256, 257, 511, 547, 548, 700, 1023, 1024, 1097, 1098]))
+    compare(inp, sg, og, lg, queries=qs)
+
+
+def test_attend_entry_splits_with_empty_splits():
+    # 70 queries: each split over four items (280 items on 256 resident
+    # workgroups); queries with fewer chunks than splits leave whole items
+    # without entries, whose partials the merge must ignore
+    rng = np.random.default_rng(32)
+    B = 70
+    ctx = rng.integers(1, 30000, size=B)
+    ctx[:4] = [1, 2, 4 * 40, 4 * 100]  # 0, 0, 40, 100 selectable rows
+    modes = np.zeros(B, np.int32)
+    modes[4:10] = synth.MODE_WINDOW
+    ratios = np.where(modes == 3, 0, 4).astype(np.int32)
+    inp = synth.decode_batch(32, list(ctx), list(modes), list(ratios), dims=small_dims())
+    inp["win_len"][1] = 0
+    inp["win_len"][4] = 17
+    say(f"decode B={B} all-heads kernel over entry splits")
+    w, sg, og, lg = run_decode(inp)
+    assert csa2.csa2_workspace_size(w.dims, w.B, 0) > 0
+    compare(inp, sg, og, lg, queries=[0, 1, 2, 3, 4, 5, 11, 35, 69])
+
+
 def test_decode_is_deterministic():
     inp = synth.decode_batch(17, [60000, 8000], [0, 0], [4, 4], dims=small_dims())
     w = csa2.DecodeWorkload(inp)
