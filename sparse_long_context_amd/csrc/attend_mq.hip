@@ -1,19 +1,20 @@
 // Two-source single-softmax attention for batches of many queries with bf16
-// KV (a prefill chunk, or a decode batch of a few hundred queries), one
-// workgroup of eight waves per query (Reading Notes of DeepSeek-V4.1-Flash,
-// section 3f C2 Step 3; "DeepSeek-V4.1-Flash on WASTE", What is new, 1. CSA2):
-// the query's 64 heads attend, in ONE softmax, over its window rows followed
-// by its selected compressed rows; every KV row is both key and value; an
-// optional per-head sink logit joins only the denominator; a query with no
-// entry gives zeros (PocketLLM page, "The op layer").
+// KV (a prefill chunk, or a decode batch of a few hundred queries): one
+// resident workgroup of twelve waves per CU takes (query, entry split)
+// items in turn (Reading Notes of DeepSeek-V4.1-Flash, section 3f C2 Step 3;
+// "DeepSeek-V4.1-Flash on WASTE", What is new, 1. CSA2): the query's 64
+// heads attend, in ONE softmax, over its window rows followed by its
+// selected compressed rows; every KV row is both key and value; an optional
+// per-head sink logit joins only the denominator; a query with no entry
+// gives zeros (PocketLLM page, "The op layer").
 //
 // Rows reach LDS by DMA (global_load_lds_dwordx4: lane l's 16 bytes land at
 // the instruction's LDS base + 16 l), into a ring of four 32-row slots, one
 // whole 1 KiB row per instruction, lane l fetching 16-byte unit l ^ f(r) of
 // row r, which leaves the slot XOR-swizzled.
 //
-// Wave w runs on SIMD w mod 4, two waves per SIMD, and the waves split the
-// two products by role so that every SIMD carries the same matrix work:
+// Wave w runs on SIMD w mod 4, three waves per SIMD, and the waves split the
+// work by role so that every SIMD carries the same matrix work:
 //   waves 0, 1, 4, 5 (scores; two each on SIMDs 0, 1): scorer h holds Q^T of
 //     heads 16 h .. +15 for all 512 dims and per chunk of 32 entries computes
 //       S^T (32 entries x 16 heads) = K (32 x 512) * Q^T (512 x 16),
@@ -24,14 +25,15 @@
 //   waves 2, 3, 6, 7 (values; two each on SIMDs 2, 3): value wave v holds
 //     O^T of dims 128 v .. +127 for all 64 heads and, one chunk behind, adds
 //       O^T (128 dims x 64 heads) += V^T (128 x 32) * P^T (32 x 64),
-//     V^T read transposed out of the slot (ds_read_b64_tr_b16); it also
-//     gathers 8 rows of every chunk.
+//     V^T read transposed out of the slot (ds_read_b64_tr_b16);
+//   waves 8 .. 11 (gathers, one per SIMD): build each item's entry list and
+//     issue the row DMAs, 8 rows of every chunk each, two chunks ahead.
 // All products are v_mfma_f32_16x16x32_bf16.  Per entry the CU reads K out of
 // LDS four times and V^T once, and no partial scores cross waves.  One
 // barrier per chunk: chunk c's scores and chunk c - 1's values run between
 // two barriers, while chunks c + 1 and c + 2 are in flight.
 //
-// Workgroup i runs on XCD i mod 8 (round-robin dispatch); queries are handed
+// Workgroup i runs on XCD i mod 8 (round-robin dispatch); items are handed
 // out so each XCD takes a contiguous run, which keeps the window rows that
 // consecutive prefill queries share (127 of 128) in that XCD's L2.
 #include <type_traits>
@@ -178,6 +180,24 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
   Pf pf = {};
   if constexpr (gatherer)
     if (k_first < run_len) pf = prefetch(run0 + k_first, (int)threadIdx.x & 63);
+  // scorers: Q^T fragments of head 16 h + l16, dims 32 s + 8 g .. +7, loaded
+  // from global memory one item ahead (after the last scores of the item
+  // before), so they arrive while that item's output leaves
+  bf16x8 qf[16];
+  auto load_q = [&](int item_) __attribute__((always_inline)) {
+    int lane_ = (int)threadIdx.x & 63;
+    asm volatile("" : "+v"(lane_));
+    const uint16_t* qp = a.q + ((int64_t)(item_ / a.n_split) * kHeads + 16 * hq + (lane_ & 15)) * kDim + 8 * (lane_ >> 4);
+#pragma unroll
+    for (int s = 0; s < 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qp + 32 * s);
+  };
+  // the sink logit of the scorer lane's head (log2 units), read once, so that
+  // no global load of finish() waits behind the next item's Q loads
+  float sink_l2 = 0.f;
+  if constexpr (scorer) {
+    if (a.sink) sink_l2 = a.sink[16 * hq + ((int)threadIdx.x & 15)] * kLog2e;
+    if (k_first < run_len) load_q(run0 + k_first);
+  }
   // value waves: O^T tiles [dim tile][head tile]; lane holds
   // O^T[128 v + 16 dt + 4 g + k][16 ht + l16]; the output of item
   // (prev_b, prev_sp) waits in them until the next item starts
@@ -187,25 +207,65 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) acc[dt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
   int prev_b = -1, prev_sp = 0;
-  auto write_out = [&](int b_, int sp_) __attribute__((always_inline)) {
-    // lane offset re-derived here, so no output address stays live through
-    // the loops
+  // The output of item (prev_b, prev_sp) leaves in two rounds through ring
+  // slots 2 and 3 (free between the end of an item and the first barrier of
+  // the next): round r stages heads 32 r .. +31 as fp32 rows [32][512] (16-
+  // byte unit u of row h at u ^ (h % 16), so neither the writes nor the
+  // reads conflict), then value wave v stores rows 8 v .. +7 of it, each
+  // instruction 1 KiB at consecutive addresses.  Stored straight from the
+  // accumulator layout, each instruction would cover sixteen 64-byte pieces
+  // 2 KiB apart, which drain several times slower and hold up the next
+  // item's loads behind them.  The lane index is re-derived opaquely, so no
+  // output address stays live through the loops.
+  auto stage_out = [&](auto r_c) __attribute__((always_inline)) {
+    constexpr int r = decltype(r_c)::value;
     int lane_ = (int)threadIdx.x & 63;
     asm volatile("" : "+v"(lane_));
     const int g_ = lane_ >> 4, l16_ = lane_ & 15;
-    float* obase = a.n_split > 1 ? a.part_o + ((int64_t)b_ * a.n_split + sp_) * kHeads * kDim
-                                 : a.out + (int64_t)b_ * kHeads * kDim;
+    uint8_t* st = ring + 2 * kSlotB;
 #pragma unroll
-    for (int ht = 0; ht < 4; ++ht) {
-      const int head = 16 * ht + l16_;
-      const float f = fin_s[head];
-      float* op = obase + head * kDim + 128 * hq + 4 * g_;
+    for (int t = 0; t < 2; ++t) {
+      const int ht = 2 * r + t;
+      const float f = fin_s[16 * ht + l16_];
+      uint8_t* row = st + (16 * t + l16_) * (kDim * 4);
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const f32x4 v = acc[dt][ht] * f;
-        *reinterpret_cast<float4*>(op + 16 * dt) = make_float4(v[0], v[1], v[2], v[3]);
+        const int u = 32 * hq + 4 * dt + g_;  // dims 128 v + 16 dt + 4 g ..
+        *reinterpret_cast<f32x4*>(row + ((u ^ l16_) << 4)) = acc[dt][ht] * f;
         acc[dt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
+    }
+  };
+  auto store_out = [&](auto r_c, int b_, int sp_) __attribute__((always_inline)) {
+    constexpr int r = decltype(r_c)::value;
+    int lane_ = (int)threadIdx.x & 63;
+    asm volatile("" : "+v"(lane_));
+    float* obase = (a.n_split > 1 ? a.part_o + ((int64_t)b_ * a.n_split + sp_) * kHeads * kDim
+                                  : a.out + (int64_t)b_ * kHeads * kDim) +
+                   (32 * r + 8 * hq) * kDim + 4 * lane_;
+    const uint8_t* st = ring + 2 * kSlotB + 8 * hq * (kDim * 4);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int h = 8 * hq + (i >> 1);  // staged row
+      const int u = 64 * (i & 1) + lane_;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(st + (i >> 1) * (kDim * 4) + ((u ^ (h & 15)) << 4));
+      *reinterpret_cast<f32x4*>(obase + (i >> 1) * kDim + 256 * (i & 1)) = v;
+    }
+  };
+  // three barriers in every role: stage, store, stage, store
+  auto flush_out = [&]() __attribute__((always_inline)) {
+    if constexpr (valuer) {
+      if (prev_b >= 0) stage_out(std::integral_constant<int, 0>{});
+      __syncthreads();
+      if (prev_b >= 0) store_out(std::integral_constant<int, 0>{}, prev_b, prev_sp);
+      __syncthreads();
+      if (prev_b >= 0) stage_out(std::integral_constant<int, 1>{});
+      __syncthreads();
+      if (prev_b >= 0) store_out(std::integral_constant<int, 1>{}, prev_b, prev_sp);
+    } else {
+      __syncthreads();
+      __syncthreads();
+      __syncthreads();
     }
   };
   int par = 0;  // item parity (item_e_s)
@@ -431,7 +491,7 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
     }
     float M = m_run, L = lsum, f;
     if (a.sink) {
-      const float s2 = a.sink[head] * kLog2e;
+      const float s2 = sink_l2;
       const float M2 = fmaxf(M, s2);
       L = L * __builtin_amdgcn_exp2f(M - M2) + __builtin_amdgcn_exp2f(s2 - M2);
       f = __builtin_amdgcn_exp2f(M - M2) / L;
@@ -468,12 +528,10 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
     if (nch > 0) gather(0, entry_for(0));
     if (nch > 1) gather(1, entry_for(1));
     if (nch > 2) ev_next = entry_for(2);
+    flush_out();
     if (nch > 1) CSA2_WAIT_VMCNT(kRowsPerValuer);
     else CSA2_WAIT_VMCNT(0);
     __syncthreads();
-    // the next item's scalar loads have returned before the chunk loop (while
-    // one is outstanding the compiler can only wait for all LDS reads at once)
-    asm volatile("" ::"s"(pf.wl), "s"(pf.md), "s"(pf.plen), "s"(pf.w0), "s"(pf.p0));
 #pragma clang loop unroll(disable)
     for (int c = 0; c < nch; ++c) {
       if (c + 2 < nch) {
@@ -486,24 +544,7 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
       __syncthreads();
     }
   } else if constexpr (scorer) {
-    // Q^T fragments of head 16 hq + l16, dims 32 s + 8 g .. +7.  The Q rows
-    // of the query's heads reach ring slots 2 and 3 by DMA (head 16 hq + j at
-    // row 16 (hq % 2) + j of slot 2 + hq / 2) while the first two chunks are
-    // gathered (slots 2 and 3 take no chunk before the first barrier), and
-    // the fragments come out of LDS like the K fragments, so no global load
-    // of the compiler's is pending in the loop (it would make the compiler
-    // wait for every DMA there).
-    bf16x8 qf[16];
-    {
-      const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.q + ((int64_t)b * kHeads + 16 * hq) * kDim);
-      uint8_t* qs = ring + (2 + (hq >> 1)) * kSlotB + 16 * (hq & 1) * kRowB;
-#pragma unroll 4
-      for (int r = 0; r < 16; ++r) dma_row16(qsrc + r * kRowB + (swz(r, lane) << 4), lds_addr(qs + r * kRowB));
-      CSA2_WAIT_VMCNT(0);
-      asm volatile("" ::: "memory");  // the Q reads stay behind the wait
-#pragma unroll
-      for (int s = 0; s < 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qs + ko[s & 3] + 256 * (s >> 2));
-    }
+    flush_out();
     __syncthreads();
     set_entries(item_e_s[par]);
 #pragma clang loop unroll(disable)
@@ -511,11 +552,12 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
       score(c, qf);
       __syncthreads();
     }
+    if (k_item + m_xcd < run_len) load_q(item + m_xcd);
     finish();
   } else {
     // the previous item's output (its factors are in fin_s since the last
-    // barrier) drains while the first rows of this one are gathered
-    if (prev_b >= 0) write_out(prev_b, prev_sp);
+    // barrier) leaves while the first rows of this one are gathered
+    flush_out();
     __syncthreads();
     set_entries(item_e_s[par]);
 #pragma clang loop unroll(disable)
@@ -530,8 +572,7 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
   __syncthreads();
   par ^= 1;
   }  // items
-  if constexpr (valuer)
-    if (prev_b >= 0) write_out(prev_b, prev_sp);
+  flush_out();  // the last item's output
   };
   if (role == kScorer) run(std::integral_constant<int, kScorer>{});
   else if (role == kGatherer) run(std::integral_constant<int, kGatherer>{});
