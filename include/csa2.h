@@ -190,11 +190,12 @@ csa2_status csa2_topk(const csa2_dims *dims, int32_t B, const csa2_batch *batch,
  * (no query then has compressed rows); the scale planes of fp8 / FP4 KV are
  * required exactly when their KV source is given.
  * sink: f32 [64] or NULL.
- * Batches of B <= 64 queries run four workgroups of 16 heads per query and
- * ignore the workspace.  Larger batches run one workgroup of all 64 heads per
- * query; with a workspace of csa2_workspace_size(dims, B, 0) bytes the entries
- * of a query may be split over several such workgroups and merged, with
- * workspace == NULL and workspace_bytes == 0 every query runs unsplit. */
+ * With fp8 / FP4 KV, batches of B <= 64 queries run four workgroups of 16
+ * heads per query and ignore the workspace.  Larger batches, and bf16 KV at
+ * every B, run workgroups of all 64 heads; with a workspace of
+ * csa2_workspace_size(dims, B, 0) bytes the entries of a query may be split
+ * over several such workgroups and merged, with workspace == NULL and
+ * workspace_bytes == 0 every query runs unsplit. */
 csa2_status csa2_attend(const csa2_dims *dims, int32_t B, const csa2_batch *batch, const void *q,
                         const void *win_kv, const uint8_t *win_scale, const void *comp_kv,
                         const uint8_t *comp_scale, const int32_t *topk_idx, const float *sink,

@@ -54,12 +54,17 @@ csa2_status check_batch(const csa2_batch* bt, int32_t B) {
 
 size_t score_stride_for(int32_t max_cand) { return align_up((size_t)max_cand * sizeof(float)) / sizeof(float); }
 
-// Batches of up to this many queries attend with four head-group workgroups
-// per query (every workgroup streams all of its query's rows, sharing them
-// through the XCD's L2); larger ones with one workgroup per (query, entry
-// split) holding all 64 heads, where each row crosses into one CU only once.
+// With fp8 / FP4 KV, batches of up to this many queries attend with four
+// head-group workgroups per query (every workgroup streams all of its query's
+// rows, sharing them through the XCD's L2); larger ones, and bf16 KV at any
+// batch size, with workgroups of all 64 heads taking (query, entry split)
+// items, where each row crosses into one CU only once (for 64 bf16 queries
+// split four ways the all-heads kernel measured 27 against the head groups'
+// 31 us).
 constexpr int32_t kHeadGroupMaxBatch = 64;
-bool use_head_groups(int32_t B) { return B <= kHeadGroupMaxBatch; }
+bool use_head_groups(const csa2_dims& d, int32_t B) {
+  return B <= kHeadGroupMaxBatch && d.kv_dtype != CSA2_KV_BF16;
+}
 
 // Scores, then the split partials of the attention when its kernel uses them.
 size_t decode_ws_bytes(int32_t B, int32_t max_cand, bool split_partials) {
@@ -151,7 +156,7 @@ csa2_status csa2_workspace_size(const csa2_dims* dims, int32_t B, int32_t max_ca
   csa2_status st = check_dims(dims);
   if (st != CSA2_OK) return st;
   if (!bytes || B < 0 || max_candidates < 0) return CSA2_ERR_INVALID_ARG;
-  *bytes = decode_ws_bytes(B, max_candidates, !use_head_groups(B));
+  *bytes = decode_ws_bytes(B, max_candidates, !use_head_groups(*dims, B));
   return CSA2_OK;
 }
 
@@ -212,7 +217,7 @@ csa2_status csa2_attend(const csa2_dims* dims, int32_t B, const csa2_batch* batc
   if (st == CSA2_OK && B > 0) st = check_attend_ptrs(dims, q, win_kv, win_scale, comp_kv, comp_scale, out);
   if (st != CSA2_OK) return st;
   if (B == 0) return CSA2_OK;
-  if (use_head_groups(B))
+  if (use_head_groups(*dims, B))
     return hip_status(launch_attend_hg(*dims, B, *batch, q, win_kv, win_scale, comp_kv, comp_scale, topk_idx, sink,
                                        out, lse, stream));
   if (workspace == nullptr && workspace_bytes == 0)
@@ -239,7 +244,7 @@ csa2_status csa2_decode(const csa2_dims* dims, int32_t B, const csa2_batch* batc
   if (B == 0) return CSA2_OK;
   if (!topk_idx || (batch->max_candidates > 0 && (!idx_q || !index_keys_ok(dims, idx_k, idx_k_scale))))
     return CSA2_ERR_INVALID_ARG;
-  const bool hg = use_head_groups(B);
+  const bool hg = use_head_groups(*dims, B);
   const size_t need = decode_ws_bytes(B, batch->max_candidates, !hg);
   if (need > 0 && (!workspace || workspace_bytes < need)) return CSA2_ERR_WORKSPACE;
   const int64_t stride = (int64_t)score_stride_for(batch->max_candidates);

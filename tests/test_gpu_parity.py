@@ -232,15 +232,19 @@ def test_decode_small_topk_and_window(k, w):
 
 
 def test_attend_kernels_agree_with_oracle():
-    # A batch of at most 64 queries attends with four head-group workgroups per
-    # query; a larger one with workgroups of all 64 heads over entry splits.
-    # Three Full queries go through the first, then three more (with 63
-    # window-only queries, 66 in all) through the second; both meet the bar.
-    few = synth.decode_batch(16, [20000] * 3, [0] * 3, [4] * 3, dims=small_dims())
-    w = csa2.DecodeWorkload(few)
-    w.decode()
-    torch.cuda.synchronize()
-    compare(few, w.topk.cpu().numpy(), w.out.cpu().numpy(), w.lse.cpu().numpy())
+    # With fp8 KV a batch of at most 64 queries attends with four head-group
+    # workgroups per query; bf16 batches of any size, and larger fp8 ones,
+    # with workgroups of all 64 heads over entry splits.  Three Full queries
+    # go through the head groups (fp8) and the all-heads kernel (bf16), then
+    # three more (with 63 window-only queries, 66 in all) through the
+    # all-heads kernel; all meet the bar.
+    for kv in (synth.KV_FP8, synth.KV_BF16):
+        few = synth.decode_batch(16, [20000] * 3, [0] * 3, [4] * 3, dims=small_dims(kv_dtype=kv))
+        w = csa2.DecodeWorkload(few)
+        w.decode()
+        torch.cuda.synchronize()
+        assert (csa2.csa2_workspace_size(w.dims, w.B, 0) > 0) == (kv == synth.KV_BF16)
+        compare(few, w.topk.cpu().numpy(), w.out.cpu().numpy(), w.lse.cpu().numpy())
     many = synth.decode_batch(16, [20000] * 3 + [300] * 63, [0] * 3 + [3] * 63, [4] * 3 + [0] * 63,
                               dims=small_dims())
     v = csa2.DecodeWorkload(many)
