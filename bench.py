@@ -343,7 +343,7 @@ def main():
                                        idx_k_scale=w.idx_k_scale),
         lambda: csa2.csa2_topk(w.dims, B, w.batch, scores, stride, w.topk),
         lambda: csa2.csa2_attend(w.dims, B, w.batch, w.q, w.win_kv, w.win_scale, w.comp_kv, w.comp_scale, w.topk,
-                                 w.sink, w.out, w.lse, None, 0),
+                                 w.sink, w.out, w.lse, w.ws, w.ws_bytes),
     ]
     stage_us = []
     for fn in stages:

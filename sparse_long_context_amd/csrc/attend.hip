@@ -346,7 +346,9 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
   }
 }
 
-// Merge the split partials of one (query, head): log-sum-exp weights.
+// Merge the split partials of one (query, head): log-sum-exp weights.  All
+// of a thread's loads (every split's max, sum and four output values) are
+// issued before the first is used, so the merge costs one memory round trip.
 __global__ __launch_bounds__(128) void attend_combine(int32_t n_split, const float* __restrict__ part_o,
                                                      const float* __restrict__ part_ml,
                                                      const float* __restrict__ sink, float* __restrict__ out,
@@ -354,8 +356,23 @@ __global__ __launch_bounds__(128) void attend_combine(int32_t n_split, const flo
   const int b = blockIdx.x / kHeads, h = blockIdx.x % kHeads;
   const int t = threadIdx.x;
   const int64_t slot0 = (int64_t)b * n_split * kHeads + h;
+  float ms[kMaxSplit], ls[kMaxSplit];
+  float4 v[kMaxSplit];
+#pragma unroll
+  for (int s = 0; s < kMaxSplit; ++s) {
+    ms[s] = -__builtin_inff();
+    ls[s] = 0.f;
+    v[s] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (s < n_split) {
+      const int64_t slot = slot0 + (int64_t)s * kHeads;
+      ms[s] = part_ml[slot * 2];
+      ls[s] = part_ml[slot * 2 + 1];
+      v[s] = *reinterpret_cast<const float4*>(part_o + slot * kDim + t * 4);
+    }
+  }
   float M = -__builtin_inff();
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, part_ml[(slot0 + (int64_t)s * kHeads) * 2]);
+#pragma unroll
+  for (int s = 0; s < kMaxSplit; ++s) M = fmaxf(M, ms[s]);
   float s2 = -__builtin_inff();
   if (sink) {
     s2 = sink[h] * kLog2e;
@@ -364,14 +381,12 @@ __global__ __launch_bounds__(128) void attend_combine(int32_t n_split, const flo
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   float L = 0.f;
   if (M != -__builtin_inff()) {
-    for (int s = 0; s < n_split; ++s) {
-      const int64_t slot = slot0 + (int64_t)s * kHeads;
-      const float ms = part_ml[slot * 2];
-      if (ms == -__builtin_inff()) continue;
-      const float w = __builtin_amdgcn_exp2f(ms - M);
-      L += w * part_ml[slot * 2 + 1];
-      const float4 v = *reinterpret_cast<const float4*>(part_o + slot * kDim + t * 4);
-      o.x += w * v.x, o.y += w * v.y, o.z += w * v.z, o.w += w * v.w;
+#pragma unroll
+    for (int s = 0; s < kMaxSplit; ++s) {
+      if (ms[s] == -__builtin_inff()) continue;  // an empty split (or none)
+      const float w = __builtin_amdgcn_exp2f(ms[s] - M);
+      L += w * ls[s];
+      o.x += w * v[s].x, o.y += w * v[s].y, o.z += w * v[s].z, o.w += w * v[s].w;
     }
     if (sink) L += __builtin_amdgcn_exp2f(s2 - M);
   }
@@ -386,7 +401,7 @@ __global__ __launch_bounds__(128) void attend_combine(int32_t n_split, const flo
 int attend_split_for(int32_t B) {
   // aim for >= 256 workgroups (one per CU) when the batch alone gives fewer
   int s = (B > 0) ? (256 + B - 1) / B : 1;
-  return s < 1 ? 1 : (s > 4 ? 4 : s);
+  return s < 1 ? 1 : (s > kMaxSplit ? kMaxSplit : s);
 }
 
 size_t attend_partial_floats(int32_t B, int n_split) {
@@ -398,6 +413,7 @@ hipError_t launch_attend(const csa2_dims& d, int32_t B, const csa2_batch& bt, co
                          const void* win_kv, const uint8_t* win_scale, const void* comp_kv,
                          const uint8_t* comp_scale, const int32_t* topk_idx, const float* sink,
                          float* out, float* lse, int n_split, float* partial, hipStream_t s) {
+  if (n_split > kMaxSplit) return hipErrorInvalidValue;
   if (B == 0) return hipSuccess;
   if (n_split < 1) n_split = 1;
   AttendArgs a;
@@ -434,6 +450,7 @@ hipError_t launch_attend(const csa2_dims& d, int32_t B, const csa2_batch& bt, co
 
 hipError_t launch_attend_combine(int32_t B, int n_split, const float* part_o, const float* part_ml, const float* sink,
                                  float* out, float* lse, hipStream_t s) {
+  if (n_split < 1 || n_split > kMaxSplit) return hipErrorInvalidValue;
   hipLaunchKernelGGL(attend_combine, dim3(B * kHeads), dim3(128), 0, s, n_split, part_o, part_ml, sink, out, lse);
   return hipGetLastError();
 }

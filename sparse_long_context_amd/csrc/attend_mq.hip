@@ -585,6 +585,7 @@ hipError_t launch_attend_mq(const csa2_dims& d, int32_t B, const csa2_batch& bt,
                             const void* win_kv, const void* comp_kv, const int32_t* topk_idx, const float* sink,
                             float* out, float* lse, int n_split, float* partial, hipStream_t s) {
   if (B == 0) return hipSuccess;
+  if (n_split > kMaxSplit) return hipErrorInvalidValue;
   MqArgs a;
   a.mode = bt.mode;
   a.win_row0 = bt.win_row0;

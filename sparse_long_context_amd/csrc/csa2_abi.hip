@@ -57,19 +57,31 @@ size_t score_stride_for(int32_t max_cand) { return align_up((size_t)max_cand * s
 // With fp8 / FP4 KV, batches of up to this many queries attend with four
 // head-group workgroups per query (every workgroup streams all of its query's
 // rows, sharing them through the XCD's L2); larger ones, and bf16 KV at any
-// batch size, with workgroups of all 64 heads taking (query, entry split)
-// items, where each row crosses into one CU only once (for 64 bf16 queries
-// split four ways the all-heads kernel measured 27 against the head groups'
-// 31 us).
+// batch size, with workgroups of all 64 heads, where each row crosses into
+// one CU only once (64 bf16 queries: 25.5 against the head groups' 31 us).
 constexpr int32_t kHeadGroupMaxBatch = 64;
 bool use_head_groups(const csa2_dims& d, int32_t B) {
   return B <= kHeadGroupMaxBatch && d.kv_dtype != CSA2_KV_BF16;
 }
 
+// Entry splits of the attention when a workspace is given (1: none).  The
+// bf16 all-heads kernel splits only batches below 64 queries: from there on
+// the merge of the partials costs more than the CUs the splits bring in
+// (64 queries: 26.5 us split four ways, 25.5 unsplit; 128 queries: 30.4
+// split two ways, 26.9 unsplit).
+constexpr int32_t kMqSplitBelow = 64;
+int all_heads_splits(const csa2_dims& d, int32_t B) {
+  if (d.kv_dtype == CSA2_KV_BF16 && B >= kMqSplitBelow) return 1;
+  return attend_split_for(B);
+}
+// the same for the decode and attention entry points, which send small fp8 /
+// FP4 batches to the head groups (never split)
+int attend_splits(const csa2_dims& d, int32_t B) { return use_head_groups(d, B) ? 1 : all_heads_splits(d, B); }
+
 // Scores, then the split partials of the attention when its kernel uses them.
-size_t decode_ws_bytes(int32_t B, int32_t max_cand, bool split_partials) {
+size_t decode_ws_bytes(int32_t B, int32_t max_cand, int n_split) {
   size_t s = align_up((size_t)B * score_stride_for(max_cand) * sizeof(float));
-  if (split_partials) s += align_up(attend_partial_floats(B, attend_split_for(B)) * sizeof(float));
+  s += align_up(attend_partial_floats(B, n_split) * sizeof(float));
   return s;
 }
 
@@ -156,7 +168,7 @@ csa2_status csa2_workspace_size(const csa2_dims* dims, int32_t B, int32_t max_ca
   csa2_status st = check_dims(dims);
   if (st != CSA2_OK) return st;
   if (!bytes || B < 0 || max_candidates < 0) return CSA2_ERR_INVALID_ARG;
-  *bytes = decode_ws_bytes(B, max_candidates, !use_head_groups(*dims, B));
+  *bytes = decode_ws_bytes(B, max_candidates, attend_splits(*dims, B));
   return CSA2_OK;
 }
 
@@ -223,7 +235,7 @@ csa2_status csa2_attend(const csa2_dims* dims, int32_t B, const csa2_batch* batc
   if (workspace == nullptr && workspace_bytes == 0)
     return attend_common(dims, B, batch, q, win_kv, win_scale, comp_kv, comp_scale, topk_idx, sink, out, lse, nullptr,
                          1, stream);
-  const int n_split = attend_split_for(B);
+  const int n_split = attend_splits(*dims, B);
   const size_t need = align_up(attend_partial_floats(B, n_split) * sizeof(float));
   if (!workspace || workspace_bytes < need) return CSA2_ERR_WORKSPACE;
   float* partial = n_split > 1 ? static_cast<float*>(workspace) : nullptr;
@@ -245,11 +257,11 @@ csa2_status csa2_decode(const csa2_dims* dims, int32_t B, const csa2_batch* batc
   if (!topk_idx || (batch->max_candidates > 0 && (!idx_q || !index_keys_ok(dims, idx_k, idx_k_scale))))
     return CSA2_ERR_INVALID_ARG;
   const bool hg = use_head_groups(*dims, B);
-  const size_t need = decode_ws_bytes(B, batch->max_candidates, !hg);
+  const size_t need = decode_ws_bytes(B, batch->max_candidates, attend_splits(*dims, B));
   if (need > 0 && (!workspace || workspace_bytes < need)) return CSA2_ERR_WORKSPACE;
   const int64_t stride = (int64_t)score_stride_for(batch->max_candidates);
   float* scores = static_cast<float*>(workspace);
-  const int sp = hg ? 1 : attend_split_for(B);
+  const int sp = attend_splits(*dims, B);
   float* partial = sp > 1 ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
                                                      align_up((size_t)B * stride * sizeof(float)))
                           : nullptr;
@@ -272,7 +284,7 @@ csa2_status csa2_prefill_workspace_size(const csa2_dims* dims, const csa2_prefil
   if (st != CSA2_OK) return st;
   if (!bytes) return CSA2_ERR_INVALID_ARG;
   const int32_t T = desc->n_queries;
-  *bytes = prefill_meta_bytes(T) + decode_ws_bytes(T, prefill_max_cand(desc), true);
+  *bytes = prefill_meta_bytes(T) + decode_ws_bytes(T, prefill_max_cand(desc), all_heads_splits(*dims, T));
   return CSA2_OK;
 }
 
@@ -290,7 +302,7 @@ csa2_status csa2_prefill(const csa2_dims* dims, const csa2_prefill_desc* desc, c
   const bool selects = desc->mode == CSA2_MODE_FULL || desc->mode == CSA2_MODE_REINDEX;
   if (desc->mode != CSA2_MODE_WINDOW && !topk_idx) return CSA2_ERR_INVALID_ARG;
   if (selects && max_cand > 0 && (!idx_q || !index_keys_ok(dims, idx_k, idx_k_scale))) return CSA2_ERR_INVALID_ARG;
-  size_t need = prefill_meta_bytes(T) + decode_ws_bytes(T, max_cand, true);
+  size_t need = prefill_meta_bytes(T) + decode_ws_bytes(T, max_cand, all_heads_splits(*dims, T));
   if (!workspace || workspace_bytes < need) return CSA2_ERR_WORKSPACE;
 
   uint8_t* ws = static_cast<uint8_t*>(workspace);
@@ -299,7 +311,7 @@ csa2_status csa2_prefill(const csa2_dims* dims, const csa2_prefill_desc* desc, c
   const int64_t stride = (int64_t)score_stride_for(max_cand);
   float* scores = reinterpret_cast<float*>(ws);
   ws += align_up((size_t)T * stride * sizeof(float));
-  const int sp = attend_split_for(T);
+  const int sp = all_heads_splits(*dims, T);
   float* partial = sp > 1 ? reinterpret_cast<float*>(ws) : nullptr;
 
   hipLaunchKernelGGL(prefill_meta_kernel, dim3((T + 255) / 256), dim3(256), 0, stream, *desc, dims->window, m);

@@ -86,9 +86,12 @@ hipError_t launch_attend_hg(const csa2_dims& d, int32_t B, const csa2_batch& bt,
                             const void* win_kv, const uint8_t* win_scale, const void* comp_kv,
                             const uint8_t* comp_scale, const int32_t* topk_idx, const float* sink, float* out,
                             float* lse, hipStream_t s);
+// a query's entries go to at most this many (query, split) work items
+constexpr int kMaxSplit = 4;
 int attend_split_for(int32_t B);
-// bf16 KV, one workgroup of four waves per (query, entry split), rows
-// gathered into LDS by DMA; n_split > 1 needs `partial` (attend_partial_floats).
+// bf16 KV: resident workgroups of twelve waves (one per CU) taking (query,
+// entry split) items in turn, rows gathered into LDS by DMA; n_split > 1
+// needs `partial` (attend_partial_floats).
 hipError_t launch_attend_mq(const csa2_dims& d, int32_t B, const csa2_batch& bt, const void* q,
                             const void* win_kv, const void* comp_kv, const int32_t* topk_idx, const float* sink,
                             float* out, float* lse, int n_split, float* partial, hipStream_t s);

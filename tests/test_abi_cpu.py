@@ -103,8 +103,8 @@ def test_bad_arguments_rejected_before_launch():
         csa2.csa2_decode(d, 2, batch(), FAKE, FAKE, None, FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, None,
                          FAKE, 16, stream=0)
     assert e.value.status == csa2.CSA2_ERR_WORKSPACE
-    with pytest.raises(E) as e:  # attend: workspace given but too small
-        csa2.csa2_attend(d, 100, batch(), FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 16, stream=0)
+    with pytest.raises(E) as e:  # attend: workspace given but too small (40 bf16 queries split four ways)
+        csa2.csa2_attend(d, 40, batch(), FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 16, stream=0)
     assert e.value.status == csa2.CSA2_ERR_WORKSPACE
 
 

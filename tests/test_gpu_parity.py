@@ -234,10 +234,12 @@ def test_decode_small_topk_and_window(k, w):
 def test_attend_kernels_agree_with_oracle():
     # With fp8 KV a batch of at most 64 queries attends with four head-group
     # workgroups per query; bf16 batches of any size, and larger fp8 ones,
-    # with workgroups of all 64 heads over entry splits.  Three Full queries
-    # go through the head groups (fp8) and the all-heads kernel (bf16), then
-    # three more (with 63 window-only queries, 66 in all) through the
-    # all-heads kernel; all meet the bar.
+    # with workgroups of all 64 heads, over entry splits (a workspace then
+    # holds their partials) for bf16 batches below 64 queries and fp8 ones
+    # below 256.  Three Full queries go through the head groups (fp8) and the
+    # split all-heads kernel (bf16), then three more (with 63 window-only
+    # queries, 66 in all) through the all-heads kernels, unsplit (bf16) and
+    # split (fp8); all meet the bar.
     for kv in (synth.KV_FP8, synth.KV_BF16):
         few = synth.decode_batch(16, [20000] * 3, [0] * 3, [4] * 3, dims=small_dims(kv_dtype=kv))
         w = csa2.DecodeWorkload(few)
@@ -245,13 +247,14 @@ def test_attend_kernels_agree_with_oracle():
         torch.cuda.synchronize()
         assert (csa2.csa2_workspace_size(w.dims, w.B, 0) > 0) == (kv == synth.KV_BF16)
         compare(few, w.topk.cpu().numpy(), w.out.cpu().numpy(), w.lse.cpu().numpy())
-    many = synth.decode_batch(16, [20000] * 3 + [300] * 63, [0] * 3 + [3] * 63, [4] * 3 + [0] * 63,
-                              dims=small_dims())
-    v = csa2.DecodeWorkload(many)
-    v.decode()
-    torch.cuda.synchronize()
-    assert v.B > 64 and csa2.csa2_workspace_size(v.dims, v.B, 0) > 0
-    compare(many, v.topk.cpu().numpy(), v.out.cpu().numpy(), v.lse.cpu().numpy(), queries=[0, 1, 2, 5, 65])
+    for kv in (synth.KV_FP8, synth.KV_BF16):
+        many = synth.decode_batch(16, [20000] * 3 + [300] * 63, [0] * 3 + [3] * 63, [4] * 3 + [0] * 63,
+                                  dims=small_dims(kv_dtype=kv))
+        v = csa2.DecodeWorkload(many)
+        v.decode()
+        torch.cuda.synchronize()
+        assert v.B > 64 and (csa2.csa2_workspace_size(v.dims, v.B, 0) > 0) == (kv == synth.KV_FP8)
+        compare(many, v.topk.cpu().numpy(), v.out.cpu().numpy(), v.lse.cpu().numpy(), queries=[0, 1, 2, 5, 65])
 
 
 @pytest.mark.parametrize("kv", [synth.KV_BF16, synth.KV_FP8])
@@ -302,24 +305,25 @@ def test_attend_resident_many_items():
     compare(inp, sg, og, lg, queries=qs)
 
 
-def test_attend_entry_splits_with_empty_splits():
-    # 70 queries: each split over four items (280 items on 256 resident
-    # workgroups); queries with fewer chunks than splits leave whole items
-    # without entries, whose partials the merge must ignore
+@pytest.mark.parametrize("kv,B", [(synth.KV_BF16, 40), (synth.KV_FP8, 70)])
+def test_attend_entry_splits_with_empty_splits(kv, B):
+    # 40 bf16 queries (each split over four items of the resident all-heads
+    # kernel) or 70 fp8 ones (four workgroups each); queries with fewer chunks
+    # than splits leave whole splits without entries, whose partials the merge
+    # must ignore
     rng = np.random.default_rng(32)
-    B = 70
     ctx = rng.integers(1, 30000, size=B)
     ctx[:4] = [1, 2, 4 * 40, 4 * 100]  # 0, 0, 40, 100 selectable rows
     modes = np.zeros(B, np.int32)
     modes[4:10] = synth.MODE_WINDOW
     ratios = np.where(modes == 3, 0, 4).astype(np.int32)
-    inp = synth.decode_batch(32, list(ctx), list(modes), list(ratios), dims=small_dims())
+    inp = synth.decode_batch(32, list(ctx), list(modes), list(ratios), dims=small_dims(kv_dtype=kv))
     inp["win_len"][1] = 0
     inp["win_len"][4] = 17
-    say(f"decode B={B} all-heads kernel over entry splits")
+    say(f"decode B={B} kv {kv} all-heads kernel over entry splits")
     w, sg, og, lg = run_decode(inp)
     assert csa2.csa2_workspace_size(w.dims, w.B, 0) > 0
-    compare(inp, sg, og, lg, queries=[0, 1, 2, 3, 4, 5, 11, 35, 69])
+    compare(inp, sg, og, lg, queries=[0, 1, 2, 3, 4, 5, 11, 35, B - 1])
 
 
 def test_decode_is_deterministic():
