@@ -96,9 +96,10 @@ def summarize_traffic(fetch_csv, write_csv):
         idx = [x for k, xs in v.items() if "index_scores_decode" in k for x in xs]
         # the probe's streaming kernel for this counter: the sum reads, the fill writes
         probe = "reduce_kernel" if counter == "FETCH_SIZE" else "FillFunctor"
-        # (the cold-step flush is a 1 GiB fill: twice the probe, so it is not taken)
+        # (the cold-step flush is a 1 GiB fill: twice the probe, so it is not
+        # taken; FETCH_SIZE reports about half the bytes read on this part)
         cpy = [x for k, xs in v.items() if probe in k for x in xs
-               if 0.75 * COPY_PROBE_BYTES < x * 1024 < 1.5 * COPY_PROBE_BYTES]
+               if 0.3 * COPY_PROBE_BYTES < x * 1024 < 1.5 * COPY_PROBE_BYTES]
         if not idx or not cpy:
             raise SystemExit(f"{path}: no indexer or copy dispatches with {counter}")
         scale = COPY_PROBE_BYTES / (1024.0 * (sum(cpy) / len(cpy)))
