@@ -13,6 +13,8 @@ Prints ONE JSON line.  Besides the contract fields it carries
   cpu_baseline: the CPU oracle timed on a bounded sample of the same workload;
   step_us:      medians of per-step HIP-event times, warm (back to back) and
                 cold (a 1 GiB fill before each step evicts the last-level cache).
+The default warm-up (100 untimed steps) outlasts the clock ramp of the first
+~20 ms of sustained work, so the timed steps see the steady state.
 --config 2 times the 4,096-query prefill chunk instead (one csa2_prefill per
 step; the roofline is then the attention's against the bf16 MFMA peak).
 """
@@ -253,7 +255,11 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the clocks ramp for the first ~20 ms of sustained work (the prefill
+    # attention measured 499 us after 5 warm-up launches, 454 us after 100),
+    # so the default warm-up runs 100 untimed steps (and 100 launches before
+    # each stage's timing) to time the steady state
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", type=int, default=1,
                     help="workload index: decode 1, 3 or 4, or 2 (the 4,096-query prefill chunk)")
     ap.add_argument("--storage", choices=("native", "fp4"), default="native",

@@ -212,7 +212,8 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
   // the next): round r stages heads 32 r .. +31 as fp32 rows [32][512] (16-
   // byte unit u of row h at u ^ (h % 16), so neither the writes nor the
   // reads conflict), then value wave v stores rows 8 v .. +7 of it, each
-  // instruction 1 KiB at consecutive addresses.  Stored straight from the
+  // instruction 1 KiB at consecutive addresses (non-temporal: nothing here
+  // reads the output again).  Stored straight from the
   // accumulator layout, each instruction would cover sixteen 64-byte pieces
   // 2 KiB apart, which drain several times slower and hold up the next
   // item's loads behind them.  The lane index is re-derived opaquely, so no
@@ -249,7 +250,7 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
       const int h = 8 * hq + (i >> 1);  // staged row
       const int u = 64 * (i & 1) + lane_;
       const f32x4 v = *reinterpret_cast<const f32x4*>(st + (i >> 1) * (kDim * 4) + ((u ^ (h & 15)) << 4));
-      *reinterpret_cast<f32x4*>(obase + (i >> 1) * kDim + 256 * (i & 1)) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(obase + (i >> 1) * kDim + 256 * (i & 1)));
     }
   };
   // three barriers in every role: stage, store, stage, store
