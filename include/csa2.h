@@ -156,8 +156,10 @@ const char *csa2_status_str(csa2_status s);
 int32_t csa2_last_hip_error(void);
 
 /* Workspace bytes csa2_decode needs for B queries with at most max_candidates
- * candidates each (scores, plus attention split partials when B > 64).  With
- * max_candidates = 0 it is the workspace csa2_attend can use to split entries. */
+ * candidates each (scores, plus the partials of the attention's entry splits,
+ * which it takes for bf16 batches below 64 queries and fp8 / FP4 batches of
+ * 65 to 255).  With max_candidates = 0 it is the workspace csa2_attend can
+ * use to split entries. */
 csa2_status csa2_workspace_size(const csa2_dims *dims, int32_t B, int32_t max_candidates,
                                 size_t *bytes);
 

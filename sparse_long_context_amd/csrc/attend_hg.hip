@@ -1,5 +1,5 @@
-// Two-source single-softmax attention for decode batches, one workgroup per
-// (query, group of 16 heads) (Reading Notes of DeepSeek-V4.1-Flash, section
+// Two-source single-softmax attention for decode batches of fp8 / FP4 rows,
+// one workgroup per (query, group of 16 heads) (Reading Notes of DeepSeek-V4.1-Flash, section
 // 3f C2 Step 3; "DeepSeek-V4.1-Flash on WASTE", What is new, 1. CSA2): the
 // query's heads attend, in ONE softmax, over its window rows followed by its
 // selected compressed rows; every KV row is both key and value; an optional
@@ -23,8 +23,8 @@
 // end the four waves' (max, sum, O) are merged with log-sum-exp weights
 // through LDS and the workgroup writes its 16 heads of the final output.
 //
-// FP8 rows (E4M3 with one UE8M0 scale per 32 values) and FP4 rows (E2M1 with
-// one E4M3 scale per 16 values, Reading Notes 3f C4) are widened exactly to
+// The rows are FP8 (E4M3 with one UE8M0 scale per 32 values) or FP4 (E2M1
+// with one E4M3 scale per 16 values, Reading Notes 3f C4), widened exactly to
 // bf16 before the first product (at most 4 and 6 significant bits).  FP4 rows
 // are loaded 32 dims (16 bytes) per lane at a time, so k-step s = 4a + b of
 // lane group g covers dims 128a + 32g + 8b .. +7 instead of 32s + 8g .. +7;
@@ -98,10 +98,6 @@ __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 codes, uint32_t e) {
 // 32 s + 8 g .. +7 of row m of the tile: exactly the MFMA A-operand layout.
 template <int KV>
 struct Rows;
-template <>
-struct Rows<CSA2_KV_BF16> {
-  uint4 v[2][16];
-};
 template <>
 struct Rows<CSA2_KV_FP8_E4M3_UE8M0_32> {
   uint2 code[2][16];
@@ -187,11 +183,7 @@ __global__ __launch_bounds__(kThr) void attend_hg_kernel(HgArgs a) {
       const int64_t ev = (e < wl) ? w0 + e : ent_s[e];
       const bool pool = ev < 0;
       const int64_t row = pool ? (-ev - 1) : ev;
-      if constexpr (KV == CSA2_KV_BF16) {
-        const uint8_t* rp = (pool ? a.comp_kv : a.win_kv) + row * kRowB + 16 * g;
-#pragma unroll
-        for (int s = 0; s < 16; ++s) st.v[tl][s] = *reinterpret_cast<const uint4*>(rp + 64 * s);
-      } else if constexpr (KV == CSA2_KV_FP8_E4M3_UE8M0_32) {
+      if constexpr (KV == CSA2_KV_FP8_E4M3_UE8M0_32) {
         const uint8_t* rp = (pool ? a.comp_kv : a.win_kv) + row * kDim + 8 * g;
 #pragma unroll
         for (int s = 0; s < 16; ++s) st.code[tl][s] = *reinterpret_cast<const uint2*>(rp + 32 * s);
@@ -209,9 +201,7 @@ __global__ __launch_bounds__(kThr) void attend_hg_kernel(HgArgs a) {
     }
   };
   auto piece = [&](const Rows<KV>& st, int tl, int s) -> uint4 {
-    if constexpr (KV == CSA2_KV_BF16) {
-      return st.v[tl][s];
-    } else if constexpr (KV == CSA2_KV_FP8_E4M3_UE8M0_32) {
+    if constexpr (KV == CSA2_KV_FP8_E4M3_UE8M0_32) {
       const uint32_t w = (s < 4) ? st.sc[tl].x : (s < 8) ? st.sc[tl].y : (s < 12) ? st.sc[tl].z : st.sc[tl].w;
       return fp8x8_to_bf16x8(st.code[tl][s], (w >> (8 * (s & 3))) & 0xffu);
     } else {
@@ -407,6 +397,7 @@ hipError_t launch_attend_hg(const csa2_dims& d, int32_t B, const csa2_batch& bt,
                             const void* win_kv, const uint8_t* win_scale, const void* comp_kv,
                             const uint8_t* comp_scale, const int32_t* topk_idx, const float* sink, float* out,
                             float* lse, hipStream_t s) {
+  if (d.kv_dtype == CSA2_KV_BF16) return hipErrorInvalidValue;  // bf16 rows take the all-heads kernel
   if (B == 0) return hipSuccess;
   HgArgs a;
   a.mode = bt.mode;
@@ -429,9 +420,7 @@ hipError_t launch_attend_hg(const csa2_dims& d, int32_t B, const csa2_batch& bt,
   a.scale_log2 = d.softmax_scale * kLog2e;
   // 32 workgroups per 8 queries: slot i -> query 8 (i / 32) + i % 8, head group (i / 8) % 4
   const dim3 grid((unsigned)(32 * ((B + 7) / 8)));
-  if (d.kv_dtype == CSA2_KV_BF16)
-    hipLaunchKernelGGL((attend_hg_kernel<CSA2_KV_BF16>), grid, dim3(kThr), 0, s, a);
-  else if (d.kv_dtype == CSA2_KV_FP8_E4M3_UE8M0_32)
+  if (d.kv_dtype == CSA2_KV_FP8_E4M3_UE8M0_32)
     hipLaunchKernelGGL((attend_hg_kernel<CSA2_KV_FP8_E4M3_UE8M0_32>), grid, dim3(kThr), 0, s, a);
   else
     hipLaunchKernelGGL((attend_hg_kernel<CSA2_KV_FP4_E2M1_E4M3_16>), grid, dim3(kThr), 0, s, a);

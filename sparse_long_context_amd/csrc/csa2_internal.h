@@ -81,7 +81,8 @@ hipError_t launch_attend(const csa2_dims& d, int32_t B, const csa2_batch& bt, co
                          const uint8_t* comp_scale, const int32_t* topk_idx, const float* sink,
                          float* out, float* lse, int n_split, float* partial, hipStream_t s);
 size_t attend_partial_floats(int32_t B, int n_split);
-// Decode-shaped batches: four workgroups per query (16 heads each), no workspace.
+// Decode-shaped batches of fp8 / FP4 rows: four workgroups per query (16 heads
+// each), no workspace; bf16 rows are refused (they take the all-heads kernel).
 hipError_t launch_attend_hg(const csa2_dims& d, int32_t B, const csa2_batch& bt, const void* q,
                             const void* win_kv, const uint8_t* win_scale, const void* comp_kv,
                             const uint8_t* comp_scale, const int32_t* topk_idx, const float* sink, float* out,
