@@ -207,6 +207,7 @@ def bench_prefill(args):
     attn_flops = 4.0 * 64 * 512 * ent
     achieved = attn_flops / (attn_us * 1e-6) / 1e12
     d = pf["dims"]
+    gather_bytes = ent * d["head_dim"] * 2 + T * d["n_heads"] * d["head_dim"] * (2 + 4)
     line = {
         "metric": METRIC, "value": round(T * args.steps / wall, 1), "unit": "queries/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
@@ -221,6 +222,12 @@ def bench_prefill(args):
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                      "traffic": None, "algorithmic_flops_per_launch": attn_flops, "avg_launch_us": round(attn_us, 2)},
         "stages_us": {"attend": round(attn_us, 2)},
+        # the same launch against HBM bandwidth, every entry's row counted once
+        # per use (as if gathered from HBM) plus q and the fp32 output: most
+        # rows in fact come from the last-level cache (a 16 MiB pool)
+        "attend_gather": {"achieved": round(gather_bytes / (attn_us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": round(gather_bytes / (attn_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                          "bytes_per_launch": gather_bytes},
         "step_us": step_us,
         "gpu": torch.cuda.get_device_name(0),
     }
