@@ -146,8 +146,9 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
   const int k_first = (int)blockIdx.x >> 3;
   // One copy of the item loop per role (the role is a template constant in
   // each), so no role's registers stay live through another role's code;
-  // the copies pass the same barriers: per item one after the first rows
-  // have landed, one per chunk, one at the end.
+  // the copies pass the same barriers: per item three while the previous
+  // item's output leaves, one after the first rows have landed, one per
+  // chunk, one at the end.
   auto run = [&](auto role_c) __attribute__((always_inline)) {
   constexpr int R = decltype(role_c)::value;
   constexpr bool scorer = R == kScorer, gatherer = R == kGatherer, valuer = R == kValuer;
