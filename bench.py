@@ -37,6 +37,15 @@ INDEX_Q_BYTES = 128 * 4      # one fp32 indexer query per query
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILE_DIR, "index_scores_decode_64x16384_traffic.json")
 INDEX_SRC = os.path.join(ROOT, "sparse_long_context_amd", "csrc", "index_scores.hip")
+ATTN_TRAFFIC_FILE = os.path.join(PROFILE_DIR, "attend_mq_prefill_4096_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "sparse_long_context_amd", "csrc", "attend_mq.hip")
+# (kernel name fragment, record file, kernel source, workload, bench arguments of the counter runs)
+TRAFFIC_KERNELS = {
+    "index": ("index_scores_decode", TRAFFIC_FILE, INDEX_SRC, "decode, 64 queries x 16,384 candidates",
+              "--no-cpu-baseline --copy-probe --steps 3 --warmup 1"),
+    "attend": ("attend_mq_kernel", ATTN_TRAFFIC_FILE, ATTN_SRC, "prefill chunk, 4,096 queries x 640 entries",
+               "--config 2 --no-cpu-baseline --copy-probe --steps 3 --warmup 1"),
+}
 COPY_PROBE_BYTES = 512 << 20
 
 
@@ -62,21 +71,33 @@ def workload_desc(inp, storage="native"):
     }
 
 
-def traffic_from_profile():
-    """HBM bytes per launch of the indexer kernel from committed rocprofv3 PMC
-    counters, if they were taken on the current kernel source."""
+def traffic_from_profile(which="index"):
+    """HBM bytes per launch of a kernel (the decode indexer, or the prefill
+    attention) from committed rocprofv3 PMC counters, if they were taken on
+    the current kernel source."""
+    _, path, src, _, _ = TRAFFIC_KERNELS[which]
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256_16") != source_digest(INDEX_SRC):
+    if rec.get("kernel_source_sha256_16") != source_digest(src):
         return None
     return rec.get("hbm_bytes_per_launch")
 
 
-def summarize_traffic(fetch_csv, write_csv):
-    """Per-launch HBM bytes of the indexer from rocprofv3 counter CSVs.
+def copy_probe(torch):
+    """Plain streaming kernels of known size, for scaling the HBM byte
+    counters: a fill writes COPY_PROBE_BYTES, a sum reads them."""
+    src = torch.empty(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        src.fill_(1.0)
+        float(src.sum())
+    torch.cuda.synchronize()
+
+
+def summarize_traffic(fetch_csv, write_csv, which="index"):
+    """Per-launch HBM bytes of a kernel from rocprofv3 counter CSVs.
 
     FETCH_SIZE and WRITE_SIZE are in KiB per dispatch.  Each is scaled by what
     the counter reads for a plain streaming kernel of COPY_PROBE_BYTES (a sum
@@ -92,10 +113,11 @@ def summarize_traffic(fetch_csv, write_csv):
             vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
         return vals
 
+    kname, out_path, src, workload, run_args = TRAFFIC_KERNELS[which]
     out = {}
     for path, counter in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
         v = per_kernel(path, counter)
-        idx = [x for k, xs in v.items() if "index_scores_decode" in k for x in xs]
+        idx = [x for k, xs in v.items() if kname in k for x in xs]
         # the probe's streaming kernel for this counter: the sum reads, the fill writes
         probe = "reduce_kernel" if counter == "FETCH_SIZE" else "FillFunctor"
         # (the cold-step flush is a 1 GiB fill: twice the probe, so it is not
@@ -103,19 +125,17 @@ def summarize_traffic(fetch_csv, write_csv):
         cpy = [x for k, xs in v.items() if probe in k for x in xs
                if 0.3 * COPY_PROBE_BYTES < x * 1024 < 1.5 * COPY_PROBE_BYTES]
         if not idx or not cpy:
-            raise SystemExit(f"{path}: no indexer or copy dispatches with {counter}")
+            raise SystemExit(f"{path}: no {kname} or copy dispatches with {counter}")
         scale = COPY_PROBE_BYTES / (1024.0 * (sum(cpy) / len(cpy)))
         out[counter] = {"kib_per_launch": sum(idx) / len(idx), "copy_kib": sum(cpy) / len(cpy), "scale": scale,
                         "bytes_per_launch": scale * 1024.0 * sum(idx) / len(idx), "launches": len(idx)}
-    rec = {"kernel": "index_scores_decode", "workload": "decode, 64 queries x 16,384 candidates",
-           "kernel_source_sha256_16": source_digest(INDEX_SRC),
+    rec = {"kernel": kname, "workload": workload,
+           "kernel_source_sha256_16": source_digest(src),
            "hbm_bytes_per_launch": round(out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"]),
            "fetch": out["FETCH_SIZE"], "write": out["WRITE_SIZE"],
-           "commands": ["rocprofv3 --pmc FETCH_SIZE -d <dir> -o fetch --output-format csv -- python3 bench.py "
-                        "--no-cpu-baseline --copy-probe --steps 3 --warmup 1",
-                        "rocprofv3 --pmc WRITE_SIZE -d <dir> -o write --output-format csv -- python3 bench.py "
-                        "--no-cpu-baseline --copy-probe --steps 3 --warmup 1"]}
-    with open(TRAFFIC_FILE, "w") as f:
+           "commands": ["rocprofv3 --pmc FETCH_SIZE -d <dir> -o fetch --output-format csv -- python3 bench.py " + run_args,
+                        "rocprofv3 --pmc WRITE_SIZE -d <dir> -o write --output-format csv -- python3 bench.py " + run_args]}
+    with open(out_path, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec, indent=1))
 
@@ -203,6 +223,8 @@ def bench_prefill(args):
     torch.cuda.synchronize()
     attn_us = 1000.0 * e0.elapsed_time(e1) / args.steps
     step_us = step_medians(torch, w.prefill, min(args.steps, 20), stream)
+    if args.copy_probe:
+        copy_probe(torch)
     ent = int(inp["win_len"].sum()) + T * pf["dims"]["index_topk"]
     attn_flops = 4.0 * 64 * 512 * ent
     achieved = attn_flops / (attn_us * 1e-6) / 1e12
@@ -220,7 +242,8 @@ def bench_prefill(args):
                    "index_topk": d["index_topk"], "kv": "bf16", "index_keys": "fp32"},
         "roofline": {"bound": "mfma", "kernel": "attend_mq_kernel", "achieved": round(achieved, 1),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "algorithmic_flops_per_launch": attn_flops, "avg_launch_us": round(attn_us, 2)},
+                     "traffic": traffic_from_profile("attend"), "algorithmic_flops_per_launch": attn_flops,
+                     "avg_launch_us": round(attn_us, 2)},
         "stages_us": {"attend": round(attn_us, 2)},
         # the same launch against HBM bandwidth, every entry's row counted once
         # per use (as if gathered from HBM) plus q and the fp32 output: most
@@ -277,10 +300,12 @@ def main():
                     help="also run a plain %d MiB fill and sum (for scaling rocprofv3 byte counters)" % (COPY_PROBE_BYTES >> 20))
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of 'bench.py --copy-probe' "
-                         "into the indexer's HBM bytes per launch, and exit")
+                         "into a kernel's HBM bytes per launch, and exit")
+    ap.add_argument("--traffic-kernel", choices=sorted(TRAFFIC_KERNELS), default="index",
+                    help="with --traffic-from: the decode indexer (index) or the prefill attention (attend)")
     args = ap.parse_args()
     if args.traffic_from:
-        summarize_traffic(*args.traffic_from)
+        summarize_traffic(*args.traffic_from, which=args.traffic_kernel)
         return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); the decode batch "
@@ -373,13 +398,7 @@ def main():
         stage_us.append(1000.0 * e0.elapsed_time(e1) / args.steps)
     step_us = step_medians(torch, w.decode, args.steps, stream)
     if args.copy_probe:
-        # plain streaming kernels of known size, for scaling the HBM byte
-        # counters: a fill writes COPY_PROBE_BYTES, a sum reads them
-        src = torch.empty(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
-        for _ in range(3):
-            src.fill_(1.0)
-            float(src.sum())
-        torch.cuda.synchronize()
+        copy_probe(torch)
 
     n_cand = int(sum(min(int(p), (int(pos) + 1) // int(r)) for p, pos, r, m in
                      zip(inp["pool_len"], inp["pos"], inp["ratio"], inp["mode"]) if m == 0 and r > 0))
