@@ -354,6 +354,22 @@ def test_prefill_small_with_replay_cut(kv):
     compare(inp, w.topk.cpu().numpy(), w.out.cpu().numpy(), w.lse.cpu().numpy())
 
 
+@pytest.mark.parametrize("kv", [synth.KV_BF16, synth.KV_FP8])
+def test_prefill_short_chunk_entry_splits(kv):
+    # 40 queries: the chunk's attention splits each query's entries four ways
+    # (its workspace holds the partials), the window reaching back before the
+    # chunk for the first queries
+    pos0, T, m = 3000, 40, 4
+    pf = synth.prefill_chunk(23 + kv, T, pos0, m, (pos0 + T) // m, dims=small_dims(kv_dtype=kv),
+                             win_pos0=pos0 - 100)
+    say("prefill T=40 kv", kv)
+    w = csa2.PrefillWorkload(pf)
+    w.prefill()
+    torch.cuda.synchronize()
+    inp = synth.prefill_as_batch(pf)
+    compare(inp, w.topk.cpu().numpy(), w.out.cpu().numpy(), w.lse.cpu().numpy())
+
+
 @pytest.mark.parametrize("mode", [synth.MODE_REUSE, synth.MODE_WINDOW, synth.MODE_REINDEX])
 def test_prefill_other_modes(mode):
     pos0, T, m = 3000, 130, 4
