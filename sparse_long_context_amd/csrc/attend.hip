@@ -6,8 +6,9 @@
 // denominator; a query with no entry yields zeros (PocketLLM page, "The op
 // layer").
 //
-// This kernel serves batches of more than 64 queries whose rows are stored
-// narrower than bf16 (fp8, FP4); bf16 rows go to the DMA-ring kernel.
+// This kernel serves rows stored narrower than bf16 (fp8, FP4): decode
+// batches of more than 64 queries and prefill chunks of any length; bf16
+// rows go to the DMA-ring kernel.
 //
 // Workgroup = one (query, split) pair, 8 waves, two per SIMD so one wave's
 // latency (LDS, softmax, barriers) hides behind another's matrix work.  Wave w
