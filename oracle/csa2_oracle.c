@@ -808,3 +808,90 @@ int csa2o_decode_batch(int32_t nb, int32_t h, int32_t d, int32_t k, int32_t h_i,
   }
   return err;
 }
+
+/* ------------------------------------------------------------------------- */
+/* One prefill chunk: T queries of one sequence at consecutive positions       */
+/* pos0 .. pos0+T-1 ([RN] 3f C2 Steps 1-4), sharing the sequence's pool, index */
+/* keys and raw window rows.  Raw row r holds position win_pos0 + r; win_pos0  */
+/* is also the replay start, so the query at p reads the rows of positions     */
+/* window_range(p, w, win_pos0) ([RN] 3f C5: the window never reaches before   */
+/* the replay start).  The chunk has one mode; Reindex lists are per query     */
+/* (cand_idx[cand_off[t] .. cand_off[t+1]]).  Only the queries qs[0..nq-1] are */
+/* run; outputs are indexed by i < nq: sel_io [nq][k] (read for Reuse, written */
+/* for Full / Reindex), out [nq][h][d], lse [nq][h].  q, idx_q and idx_w are   */
+/* indexed by the query's t.  Index keys: fp32 [pool_len][d_i], or MXFP4       */
+/* decoded exactly to fp32 first (idx_kdtype as for the decode batch).         */
+/* ------------------------------------------------------------------------- */
+int csa2o_prefill_chunk(int32_t nq, const int32_t *qs, int64_t pos0, int32_t mode, int32_t m, int64_t pool_len,
+                        int64_t win_pos0, int64_t n_win_rows, int32_t w, int32_t h, int32_t d, int32_t k,
+                        int32_t h_i, int32_t d_i, int32_t relu, int32_t kv_dtype, double scale,
+                        const int64_t *cand_off, const int32_t *cand_idx, const uint16_t *q, const void *win_rows,
+                        const uint8_t *win_scales, const void *pool_rows, const uint8_t *pool_scales,
+                        const float *idx_q, const float *idx_w, int32_t idx_kdtype, const void *idx_k,
+                        const uint8_t *idx_k_scales, const float *sink, int32_t *sel_io, float *out, float *lse) {
+  size_t rb = (kv_dtype == ORC_KV_FP8) ? (size_t)d : (kv_dtype == ORC_KV_FP4) ? (size_t)d / 2 : 2 * (size_t)d;
+  size_t sb = (kv_dtype == ORC_KV_FP8) ? (size_t)d / 32 : (kv_dtype == ORC_KV_FP4) ? (size_t)d / 16 : 0;
+  const float *keys = NULL;
+  float *dec = NULL;
+  int32_t i;
+  int err = ORC_OK;
+  if (nq < 0 || !qs || pos0 < 0 || win_pos0 < 0 || win_pos0 > pos0 || n_win_rows < 0 || w < 0 || pool_len < 0)
+    return ORC_EBADARG;
+  if (mode < ORC_MODE_FULL || mode > ORC_MODE_WINDOW) return ORC_EBADARG;
+  if (mode == ORC_MODE_REINDEX && (!cand_off || !cand_idx)) return ORC_EBADARG;
+  if (idx_kdtype != ORC_IDXK_F32 && idx_kdtype != ORC_IDXK_MXFP4) return ORC_EBADARG;
+  if ((mode == ORC_MODE_FULL || mode == ORC_MODE_REINDEX) && pool_len > 0) {
+    if (!idx_k || !idx_q) return ORC_EBADARG;
+    if (idx_kdtype == ORC_IDXK_F32) {
+      keys = (const float *)idx_k;
+    } else {
+      int rc;
+      if ((d_i % 32) != 0 || !idx_k_scales) return ORC_EBADARG;
+      dec = (float *)malloc(sizeof(float) * (size_t)pool_len * (size_t)d_i);
+      if (!dec) return ORC_ENOMEM;
+      if ((rc = csa2o_dequant_mxfp4((const uint8_t *)idx_k, idx_k_scales, pool_len * d_i, dec)) != ORC_OK) {
+        free(dec);
+        return rc;
+      }
+      keys = dec;
+    }
+  }
+#pragma omp parallel for schedule(dynamic, 1)
+  for (i = 0; i < nq; ++i) {
+    const int64_t t = qs[i];
+    const int64_t p = pos0 + t;
+    int64_t lo = 0, cnt = 0;
+    int32_t *sel = sel_io + (size_t)i * (size_t)k;
+    int32_t nsel = k;
+    int rc = csa2o_window_range(p, w, win_pos0, &lo, &cnt);
+    if (rc == ORC_OK && (t < 0 || lo - win_pos0 + cnt > n_win_rows)) rc = ORC_EBADARG;
+    if (rc == ORC_OK && (mode == ORC_MODE_FULL || mode == ORC_MODE_REINDEX)) {
+      const int32_t *cl = (mode == ORC_MODE_REINDEX) ? cand_idx + cand_off[t] : NULL;
+      const int64_t nc = (mode == ORC_MODE_REINDEX) ? cand_off[t + 1] - cand_off[t] : 0;
+      int64_t r;
+      if (pool_len == 0) { /* nothing to score: every slot is -1 */
+        int32_t j;
+        for (j = 0; j < k; ++j) sel[j] = -1;
+        r = 0;
+      } else {
+        r = csa2o_select_query(mode, p, m, pool_len, h_i, d_i, idx_q + (size_t)t * (size_t)(h_i * d_i),
+                               idx_w ? idx_w + (size_t)t * (size_t)h_i : NULL, relu, keys, cl, nc, k, sel, NULL);
+      }
+      if (r < 0) rc = (int)r;
+    } else if (mode == ORC_MODE_WINDOW) {
+      nsel = 0;
+    }
+    if (rc == ORC_OK)
+      rc = csa2o_attend_query(h, d, kv_dtype, q + (size_t)t * (size_t)(h * d),
+                              win_rows ? (const uint8_t *)win_rows + (size_t)(lo - win_pos0) * rb : NULL,
+                              win_scales ? win_scales + (size_t)(lo - win_pos0) * sb : NULL, cnt, pool_rows,
+                              pool_scales, pool_len, sel, nsel, sink, scale, out + (size_t)i * (size_t)(h * d),
+                              lse ? lse + (size_t)i * (size_t)h : NULL);
+    if (rc != ORC_OK) {
+#pragma omp critical
+      err = rc;
+    }
+  }
+  free(dec);
+  return err;
+}

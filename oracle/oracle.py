@@ -4,10 +4,11 @@ TEST INFRASTRUCTURE ONLY: imported by tests/, ``__graft_entry__.smoke()`` and
 the ``cpu_baseline`` leg of ``bench.py``; never by the product path.
 
 Every function here is marshalling: the arithmetic lives in csa2_oracle.c,
-which follows the pages step by step (see the comments there).  The per-query
-composition (``decode_query`` / ``prefill_query``) strings the C steps together
-in the pages' order: reachability -> scores -> top-K -> one softmax over the
-window rows and the selected compressed rows.
+which follows the pages step by step (see the comments there), including the
+compositions over a decode batch (``decode_batch``) and over a prefill chunk
+(``prefill_chunk``, which derives each query's window itself) in the pages'
+order: reachability -> scores -> top-K -> one softmax over the window rows and
+the selected compressed rows.
 """
 import ctypes as C
 import os
@@ -73,6 +74,9 @@ def lib():
                                          P, P, P, P, P, P, P, P, P,
                                          P, P, P, P, P, P, P, i32, P, P, P, P, P, P]
         L.csa2o_decode_batch.restype = C.c_int
+        L.csa2o_prefill_chunk.argtypes = [i32, P, i64, i32, i32, i64, i64, i64, i32, i32, i32, i32, i32, i32,
+                                          i32, i32, dbl, P, P, P, P, P, P, P, P, P, i32, P, P, P, P, P, P]
+        L.csa2o_prefill_chunk.restype = C.c_int
         _lib = L
     return _lib
 
@@ -329,5 +333,36 @@ def decode_batch(inp, queries=None, sink=None, scale=1.0):
         _ptr(inp["comp_kv"]), _ptr(inp.get("comp_scale")), _ptr(idx_q), _ptr(idx_w),
         int(d.get("index_key_dtype", IDXK_F32)), _ptr(inp["idx_k"]), _ptr(inp.get("idx_k_scale")),
         _ptr(sink), _ptr(sel), _ptr(out), _ptr(lse))
+    _check(rc)
+    return sel, out, lse
+
+
+def prefill_chunk(pf, queries=None, sink=None, scale=1.0):
+    """Run the oracle over a prefill chunk (dict from ``synth.prefill_chunk``):
+    T queries of one sequence at pos0 .. pos0+T-1 sharing its raw window rows
+    (row r at position win_pos0 + r), pool and index keys.  Each query's window,
+    reachability, selection and attention are derived inside the oracle.
+    ``queries`` restricts the run to a subset of t.  Returns (sel int32 [n, K],
+    out f32 [n, H, D], lse f32 [n, H])."""
+    d = pf["dims"]
+    T = int(pf["T"])
+    qs = np.ascontiguousarray(np.arange(T) if queries is None else np.asarray(queries), np.int32)
+    n = len(qs)
+    H, D, K, HI, DI, W = d["n_heads"], d["head_dim"], d["index_topk"], d["index_heads"], d["index_dim"], d["window"]
+    kvd = d["kv_dtype"]
+    sel = np.full((n, K), -1, np.int32)
+    if pf.get("sel_in") is not None:
+        sel[:] = pf["sel_in"][qs]
+    win_kv = pf["win_kv"]
+    out = np.empty((n, H, D), np.float32)
+    lse = np.empty((n, H), np.float32)
+    rc = lib().csa2o_prefill_chunk(
+        n, _ptr(qs), int(pf["pos0"]), int(pf["mode"]), int(pf["ratio"]), int(pf["pool_len"]),
+        int(pf["win_pos0"]), int(win_kv.shape[0]), int(W), H, D, K, HI, DI, int(d["index_relu"]), kvd, float(scale),
+        _ptr(_c(pf.get("cand_off"), np.int64)), _ptr(_c(pf.get("cand_idx"), np.int32)), _ptr(pf["q"]),
+        _ptr(win_kv), _ptr(pf.get("win_scale")), _ptr(pf["comp_kv"]), _ptr(pf.get("comp_scale")),
+        _ptr(_c(pf["idx_q"], np.float32)), _ptr(_c(pf.get("idx_w"), np.float32)),
+        int(d.get("index_key_dtype", IDXK_F32)), _ptr(pf["idx_k"]), _ptr(pf.get("idx_k_scale")),
+        _ptr(_c(sink, np.float32)), _ptr(sel), _ptr(out), _ptr(lse))
     _check(rc)
     return sel, out, lse

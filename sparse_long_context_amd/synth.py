@@ -19,14 +19,15 @@ A decode batch is a dict:
   q           uint16 [B, H, D] (bf16 bits)
   win_kv      window rows [rows, D] (uint16 bf16, or uint8 e4m3) (+ win_scale [rows, D/32])
   comp_kv     compressed rows [rows, D] (same dtype)          (+ comp_scale)
-  idx_q       float32 [B, H_I, D_I];  idx_w None (unit weights)
+  idx_q       float32 [B, H_I, D_I];  idx_w float32 [B, H_I] (weights=True) or None (unit)
   idx_k       float32 [rows, D_I], same row numbering as comp_kv
   sel_in      int32 [B, K] supplied selections (Reuse rows), -1 elsewhere, or None
   cand_off, cand_idx   Reindex lists (or None)
   max_pool_len
 A prefill chunk is a dict with T, pos0, mode, ratio, win_pos0, pool_len, q, win_kv,
-comp_kv, idx_q, idx_k (one sequence); ``prefill_as_batch`` expands it into the
-per-query form above.
+comp_kv, idx_q, idx_w, idx_k (one sequence): raw window row r holds position
+win_pos0 + r.  Which rows each query reads is the method's business (the HIP
+library and the oracle each derive it), not this module's.
 """
 import ctypes as C
 import math
@@ -42,7 +43,7 @@ KV_BF16, KV_FP8, KV_FP4 = 0, 1, 2
 IDXK_F32, IDXK_MXFP4 = 0, 1
 
 # streams: one per tensor kind
-S_Q, S_WIN, S_POOL, S_IDXQ, S_IDXK, S_CTX, S_REUSE, S_CAND = 1, 2, 3, 4, 5, 6, 7, 8
+S_Q, S_WIN, S_POOL, S_IDXQ, S_IDXK, S_CTX, S_REUSE, S_CAND, S_IDXW = 1, 2, 3, 4, 5, 6, 7, 8, 9
 
 _lib = None
 
@@ -119,11 +120,13 @@ def _kv_rows(seed, stream, rows, d, kv_dtype):
     return normal_fp8(seed, stream, rows, d)
 
 
-def decode_batch(seed, contexts, modes, ratios, dims=None, pool_cap=None, reuse_k=None, win_len=None):
+def decode_batch(seed, contexts, modes, ratios, dims=None, pool_cap=None, reuse_k=None, win_len=None,
+                 weights=False):
     """General decode batch: query b sits at position contexts[b]-1 of its own
     sequence.  Full/Reuse queries get a pool of floor(context/ratio) rows (capped
     by pool_cap), window queries none.  Each query has min(window, context)
-    window rows of its own."""
+    window rows of its own.  weights=True draws per-head index weights
+    ~ N(0, 1) (the indexer's per-token weights); otherwise they are None."""
     dims = dict(dims or default_dims())
     B = len(contexts)
     H, D, K = dims["n_heads"], dims["head_dim"], dims["index_topk"]
@@ -152,7 +155,8 @@ def decode_batch(seed, contexts, modes, ratios, dims=None, pool_cap=None, reuse_
         win_row0=win_row0, win_len=wl, pool_row0=pool_row0, pool_len=pool_len,
         q=normal_bf16(seed, S_Q, (B, H, D), scale=1.0 / math.sqrt(512.0)),
         win_kv=win_kv, win_scale=win_scale, comp_kv=comp_kv, comp_scale=comp_scale,
-        idx_q=normal_f32(seed, S_IDXQ, (B, HI, DI)), idx_w=None,
+        idx_q=normal_f32(seed, S_IDXQ, (B, HI, DI)),
+        idx_w=normal_f32(seed, S_IDXW, (B, HI)) if weights else None,
         idx_k=normal_f32(seed, S_IDXK, (n_pool_rows, DI)),
         sel_in=None, cand_off=None, cand_idx=None,
         max_pool_len=int(pool_len.max()) if B else 0,
@@ -187,7 +191,7 @@ def add_reindex_lists(inp, seed, frac=0.25):
     return inp
 
 
-def prefill_chunk(seed, T, pos0, ratio, pool_len, dims=None, win_pos0=None, mode=MODE_FULL):
+def prefill_chunk(seed, T, pos0, ratio, pool_len, dims=None, win_pos0=None, mode=MODE_FULL, weights=False):
     """One sequence: T queries at positions pos0 .. pos0+T-1.  The raw window rows
     cover positions win_pos0 .. pos0+T-1 (default: the W-1 positions before pos0
     as well, so every query sees a full window)."""
@@ -204,35 +208,11 @@ def prefill_chunk(seed, T, pos0, ratio, pool_len, dims=None, win_pos0=None, mode
         pool_len=pool_len,
         q=normal_bf16(seed, S_Q, (T, H, D), scale=1.0 / math.sqrt(512.0)),
         win_kv=win_kv, win_scale=win_scale, comp_kv=comp_kv, comp_scale=comp_scale,
-        idx_q=normal_f32(seed, S_IDXQ, (T, HI, DI)), idx_w=None,
+        idx_q=normal_f32(seed, S_IDXQ, (T, HI, DI)),
+        idx_w=normal_f32(seed, S_IDXW, (T, HI)) if weights else None,
         idx_k=normal_f32(seed, S_IDXK, (pool_len, DI)),
         sel_in=None, cand_off=None, cand_idx=None,
     )
-
-
-def prefill_window(pos, w, replay_start):
-    """Window rows of the query at ``pos``: positions max(replay_start, pos-w+1) .. pos."""
-    lo = max(replay_start, pos - w + 1)
-    return lo, (pos - lo + 1) if w > 0 else 0
-
-
-def prefill_as_batch(pf, queries=None):
-    """Per-query metadata of a prefill chunk in decode-batch form (all queries
-    share the chunk's window rows, pool and index keys)."""
-    ts = np.arange(pf["T"]) if queries is None else np.asarray(queries)
-    n = len(ts)
-    W = pf["dims"]["window"]
-    pos = (pf["pos0"] + ts).astype(np.int64)
-    lo_cnt = [prefill_window(int(p), W, pf["win_pos0"]) for p in pos]
-    inp = dict(pf)
-    inp.update(
-        B=n, pos=pos, mode=np.full(n, pf["mode"], np.int32), ratio=np.full(n, pf["ratio"], np.int32),
-        win_row0=np.array([lo - pf["win_pos0"] for lo, _ in lo_cnt], np.int64),
-        win_len=np.array([c for _, c in lo_cnt], np.int32),
-        pool_row0=np.zeros(n, np.int64), pool_len=np.full(n, pf["pool_len"], np.int32),
-        q=pf["q"][ts], idx_q=pf["idx_q"][ts], max_pool_len=pf["pool_len"],
-    )
-    return inp
 
 
 # --- the five workloads -------------------------------------------------------

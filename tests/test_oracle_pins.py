@@ -679,3 +679,153 @@ def test_derotation_undoes_the_rotation():
     # a quarter turn maps (x, y) to (y, -x)
     q = O.derotate(o, 1, np.full(rd // 2, np.pi / 2), off, rd)
     assert np.allclose(q[:, off::2], o[:, off + 1::2], atol=1e-6) and np.allclose(q[:, off + 1::2], -o[:, off::2], atol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# Compositions: the decode batch and the prefill chunk against the per-query
+# steps (each pinned above) run on rows sliced by hand ([RN] 3f C2 Steps 1-4,
+# 3f C5).  A wrong row offset, bytes-per-row, mode dispatch, weight stride or
+# window rule in a composition makes these differ.
+# ---------------------------------------------------------------------------
+
+def _small_dims(**kw):
+    d = dict(n_heads=4, head_dim=64, window=6, index_topk=8, index_dim=32, index_heads=3, index_relu=1,
+             kv_dtype=O.KV_BF16, softmax_scale=1.0)
+    d.update(kw)
+    return d
+
+
+def _restore_fp4(inp):
+    """Re-store the bf16 KV rows of a batch / chunk as FP4 (oracle quantizer)."""
+    out = dict(inp, dims=dict(inp["dims"], kv_dtype=O.KV_FP4))
+    for src, sc in (("win_kv", "win_scale"), ("comp_kv", "comp_scale")):
+        out[src], out[sc] = O.quant_fp4kv(synth.bf16_bits_to_f32(inp[src]))
+    return out
+
+
+def _rows(inp, name, r0, n):
+    a = inp[name]
+    s = inp.get(name.replace("_kv", "_scale"))
+    return a[r0:r0 + n], (None if s is None else s[r0:r0 + n])
+
+
+@pytest.mark.parametrize("kv,idxk", [(O.KV_BF16, O.IDXK_F32), (O.KV_FP8, O.IDXK_MXFP4), (O.KV_FP4, O.IDXK_F32)])
+def test_decode_batch_equals_its_queries_run_one_by_one(kv, idxk):
+    # ragged contexts; modes Full, Reindex, Reuse, window-only, Full, Reindex;
+    # window lengths below the window size for some queries
+    ctx = [300, 257, 900, 40, 3, 1200]
+    modes = [O.MODE_FULL, O.MODE_REINDEX, O.MODE_REUSE, O.MODE_WINDOW, O.MODE_FULL, O.MODE_REINDEX]
+    ratios = [4, 4, 4, 0, 4, 8]
+    dims = _small_dims(kv_dtype=O.KV_FP8 if kv == O.KV_FP8 else O.KV_BF16)
+    inp = synth.decode_batch(51 + kv, ctx, modes, ratios, dims=dims, weights=True, reuse_k=5,
+                             win_len=[6, 2, 6, 5, 3, 0])
+    synth.add_reindex_lists(inp, 51, frac=0.5)
+    # a Reindex list naming rows the query cannot reach: the pool is larger
+    # than what pos lets it read
+    inp["pos"][1] = 100  # 25 reachable of 64 rows
+    if kv == O.KV_FP4:
+        inp = _restore_fp4(inp)
+    keys_f32 = inp["idx_k"]
+    if idxk == O.IDXK_MXFP4:
+        codes, scales = O.quant_mxfp4(keys_f32)
+        keys_f32 = O.dequant_mxfp4(codes, scales)
+        inp = dict(inp, idx_k=codes, idx_k_scale=scales, dims=dict(inp["dims"], index_key_dtype=O.IDXK_MXFP4))
+    sink = np.array([0.5, -1.0, 2.0, 0.0], np.float32)
+    scale = 0.37
+    sel_b, out_b, lse_b = O.decode_batch(inp, sink=sink, scale=scale)
+    K = dims["index_topk"]
+    assert (sel_b[1][sel_b[1] >= 0] < 25).all()
+    for b in range(inp["B"]):
+        w_rows, w_sc = _rows(inp, "win_kv", int(inp["win_row0"][b]), int(inp["win_len"][b]))
+        p0, pl = int(inp["pool_row0"][b]), int(inp["pool_len"][b])
+        p_rows, p_sc = _rows(inp, "comp_kv", p0, pl)
+        m = inp["mode"][b]
+        if m in (O.MODE_FULL, O.MODE_REINDEX):
+            cand = None
+            if m == O.MODE_REINDEX:
+                cand = inp["cand_idx"][inp["cand_off"][b]:inp["cand_off"][b + 1]]
+            sel = O.select_query(m, inp["pos"][b], inp["ratio"][b], pl, inp["idx_q"][b], keys_f32[p0:p0 + pl], K,
+                                 idx_w=inp["idx_w"][b], relu=True, cand=cand)
+        elif m == O.MODE_REUSE:
+            sel = inp["sel_in"][b]
+        else:
+            sel = np.zeros(0, np.int32)
+        out, lse = O.attend_query(inp["q"][b], w_rows, p_rows, sel, kv_dtype=inp["dims"]["kv_dtype"],
+                                  win_scales=w_sc, pool_scales=p_sc, sink=sink, scale=scale)
+        if m != O.MODE_WINDOW:
+            assert np.array_equal(sel_b[b], sel), f"query {b}"
+        assert np.array_equal(out_b[b], out) and np.array_equal(lse_b[b], lse), f"query {b}"
+
+
+def _brute_window(pos, w, start):
+    """Raw positions u with pos - w < u <= pos and u >= start, by enumeration."""
+    return [u for u in range(0, pos + 1) if pos - w < u and u >= start]
+
+
+@pytest.mark.parametrize("mode,kv", [(O.MODE_FULL, O.KV_BF16), (O.MODE_REINDEX, O.KV_FP8), (O.MODE_REUSE, O.KV_BF16),
+                                     (O.MODE_WINDOW, O.KV_FP4), (O.MODE_FULL, O.KV_FP8)])
+def test_prefill_chunk_equals_its_queries_run_one_by_one(mode, kv):
+    pos0, T, m, W = 50, 12, 4, 6
+    dims = _small_dims(kv_dtype=O.KV_FP8 if kv == O.KV_FP8 else O.KV_BF16, window=W)
+    pool = (pos0 + T) // m
+    # the raw rows start 3 positions before the chunk: that is also the replay
+    # start, so the first queries' windows are cut short ([RN] 3f C5)
+    pf = synth.prefill_chunk(61 + mode, T, pos0, m, pool, dims=dims, win_pos0=pos0 - 3, mode=mode, weights=True)
+    K = dims["index_topk"]
+    if mode == O.MODE_REUSE:
+        pf["sel_in"] = np.full((T, K), -1, np.int32)
+        for t in range(T):
+            s = synth.sample_distinct(61, 500 + t, (pos0 + t + 1) // m, 5)
+            pf["sel_in"][t, :len(s)] = s
+    if mode == O.MODE_REINDEX:
+        offs, parts = np.zeros(T + 1, np.int64), []
+        for t in range(T):
+            s = synth.sample_distinct(61, 700 + t, pool, 9)  # may name rows not yet reachable
+            parts.append(s)
+            offs[t + 1] = offs[t] + len(s)
+        pf["cand_off"], pf["cand_idx"] = offs, np.concatenate(parts).astype(np.int32)
+    if kv == O.KV_FP4:
+        pf = _restore_fp4(pf)
+    sel_c, out_c, lse_c = O.prefill_chunk(pf)
+    qs = [0, 2, 5, 11]
+    sel_s, out_s, lse_s = O.prefill_chunk(pf, qs)  # a subset gives the same rows
+    assert np.array_equal(sel_s, sel_c[qs]) and np.array_equal(out_s, out_c[qs])
+    for t in range(T):
+        p = pos0 + t
+        win = _brute_window(p, W, pf["win_pos0"])
+        assert len(win) == (min(W, 4 + t))
+        r0 = win[0] - pf["win_pos0"]
+        w_rows, w_sc = _rows(pf, "win_kv", r0, len(win))
+        p_rows, p_sc = _rows(pf, "comp_kv", 0, pool)
+        if mode in (O.MODE_FULL, O.MODE_REINDEX):
+            cand = None if mode == O.MODE_FULL else pf["cand_idx"][pf["cand_off"][t]:pf["cand_off"][t + 1]]
+            sel = O.select_query(mode, p, m, pool, pf["idx_q"][t], pf["idx_k"], K, idx_w=pf["idx_w"][t],
+                                 relu=True, cand=cand)
+            assert np.array_equal(sel_c[t], sel), f"query {t}"
+        elif mode == O.MODE_REUSE:
+            sel = pf["sel_in"][t]
+        else:
+            sel = np.zeros(0, np.int32)
+        out, lse = O.attend_query(pf["q"][t], w_rows, p_rows, sel, kv_dtype=pf["dims"]["kv_dtype"],
+                                  win_scales=w_sc, pool_scales=p_sc)
+        assert np.array_equal(out_c[t], out) and np.array_equal(lse_c[t], lse), f"query {t}"
+
+
+def test_prefill_chunk_window_example():
+    """[RN] 3f C5 worked example through the chunk: replay start s = 1000,
+    window 128, the query at i = 1050 reads the 51 raw positions 1000..1050.
+    Rows are built so that only the window matters: one pool-free chunk in
+    window-only mode whose attention output is the mean of the rows it reads
+    (q = 0 makes every score equal)."""
+    g = gold("replay_window_example.json")
+    s, i, w = g["replay_start"], g["query"], g["window"]
+    dims = _small_dims(window=w)
+    pf = synth.prefill_chunk(71, 1, i, 4, 0, dims=dims, win_pos0=s, mode=O.MODE_WINDOW)
+    pf["q"][:] = 0
+    _, out, lse = O.prefill_chunk(pf)
+    rows = synth.bf16_bits_to_f32(pf["win_kv"]).astype(np.float64)
+    n = g["count_with_cut"]
+    assert rows.shape[0] == n  # the chunk holds exactly the raw rows 1000..1050
+    # reading fewer rows changes the mean; reading more is refused (they do not exist)
+    assert np.allclose(out[0, 0], rows.mean(0), rtol=0, atol=1e-6)
+    assert np.allclose(lse[0], math.log(n), atol=1e-6)
