@@ -1,24 +1,34 @@
 """Throughput of the CSA2 attention step on one MI355X.
 
-One step = one csa2_decode call over the whole batch: indexer scores for every
-query over its reachable compressed entries, per-query top-512, and the
-64-head single-softmax attention over 128 window rows + 512 selected rows.
-Default workload: 64 independent decode queries at context 65,536 with
-compress ratio 4 (16,384 candidates each), bf16 KV, fp32 indexer keys; inputs
-are seeded synthetic N(0, 1) data, resident in HBM before timing starts.
+Headline workload (the default): the prefill chunk of 4,096 query tokens of one
+sequence at positions 126,976..131,071 of a 131,072-token context, compress
+ratio 8 (a pool of 16,384 compressed rows), each query with its own causal
+128-row window and its own top-512 from the indexer, 64 heads x 512 dims, bf16
+KV, fp32 index keys.  One step = one csa2_prefill call over the whole chunk:
+indexer scores, per-query top-512, and the 64-head single-softmax attention
+over 128 window rows + 512 selected rows.  Inputs are seeded synthetic N(0, 1)
+data, resident in HBM before timing starts.
 
 Prints ONE JSON line.  Besides the contract fields it carries
-  roofline:     the dominant kernel (the indexer scan) against HBM bandwidth,
-                its duration measured here with HIP events on the launch stream;
-  cpu_baseline: the CPU oracle timed on a bounded sample of the same workload;
+  roofline:     the dominant kernel (the prefill attention) against the bf16
+                MFMA peak, its duration measured here with HIP events on the
+                launch stream (a csa2_prefill call in Reuse mode over the same
+                selections: the attention and a 2-4 us descriptor kernel);
+  cpu_baseline: the CPU oracle timed on a bounded sample of the same workload
+                (all host threads), with the host's CPU model and a
+                single-thread rate;
   step_us:      medians of per-step HIP-event times, warm (back to back) and
-                cold (a 1 GiB fill before each step evicts the last-level cache).
-The default warm-up (100 untimed steps) outlasts the clock ramp of the first
-~20 ms of sustained work, so the timed steps see the steady state.
---config 2 times the 4,096-query prefill chunk instead (one csa2_prefill per
-step; the roofline is then the attention's against the bf16 MFMA peak).
+                cold (a 1 GiB fill before each step evicts the last-level cache);
+  workloads:    the decode batches (64 x 16,384 bf16; 256 x 16,384 fp8 at 1M
+                context; 128 mixed-mode ragged queries; the first re-stored as
+                FP4 KV + MXFP4 keys), each with its step time, queries/s, stage
+                times and its indexer against HBM bandwidth (--no-extras skips).
+Before the warm-up steps the GPU runs ~50 ms of plain fills, past the clock ramp
+of the first ~20 ms of sustained work, so the timed steps see the steady state.
+--config 1, 3 or 4 makes one decode batch the headline instead.
 """
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -42,11 +52,16 @@ ATTN_SRC = os.path.join(ROOT, "sparse_long_context_amd", "csrc", "attend_mq.hip"
 # (kernel name fragment, record file, kernel source, workload, bench arguments of the counter runs)
 TRAFFIC_KERNELS = {
     "index": ("index_scores_decode", TRAFFIC_FILE, INDEX_SRC, "decode, 64 queries x 16,384 candidates",
-              "--no-cpu-baseline --copy-probe --steps 3 --warmup 1"),
+              "--config 1 --no-cpu-baseline --copy-probe --steps 3 --warmup 1"),
     "attend": ("attend_mq_kernel", ATTN_TRAFFIC_FILE, ATTN_SRC, "prefill chunk, 4,096 queries x 640 entries",
-               "--config 2 --no-cpu-baseline --copy-probe --steps 3 --warmup 1"),
+               "--no-extras --no-cpu-baseline --copy-probe --steps 3 --warmup 1"),
 }
 COPY_PROBE_BYTES = 512 << 20
+KV_NAMES = {0: "bf16", 1: "fp8 e4m3 + ue8m0/32", 2: "fp4 e2m1 + e4m3/16"}
+
+
+def say(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
 
 
 def source_digest(path):
@@ -54,24 +69,7 @@ def source_digest(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def workload_desc(inp, storage="native"):
-    d = inp["dims"]
-    kv = "bf16" if d["kv_dtype"] == 0 else "fp8 e4m3 + ue8m0/32"
-    keys = "fp32"
-    if storage == "fp4":
-        kv, keys = "fp4 e2m1 + e4m3/16", "mxfp4 (e2m1 + e8m0/32)"
-    return {
-        "workload": (f"decode, {inp['B']} queries, context {int(inp['pos'][0]) + 1}, compress ratio "
-                     f"{int(inp['ratio'][0])} -> {int(inp['pool_len'][0])} candidates each, window "
-                     f"{d['window']}, top-{d['index_topk']}, {d['n_heads']} heads x {d['head_dim']}, {kv} KV, "
-                     f"{keys} indexer keys dim {d['index_dim']}"),
-        "queries_per_step": int(inp["B"]),
-        "candidates_per_query": int(inp["pool_len"][0]),
-        "window": d["window"], "index_topk": d["index_topk"], "kv": kv, "index_keys": keys,
-    }
-
-
-def traffic_from_profile(which="index"):
+def traffic_from_profile(which):
     """HBM bytes per launch of a kernel (the decode indexer, or the prefill
     attention) from committed rocprofv3 PMC counters, if they were taken on
     the current kernel source."""
@@ -140,23 +138,82 @@ def summarize_traffic(fetch_csv, write_csv, which="index"):
     print(json.dumps(rec, indent=1))
 
 
-def cpu_baseline(inp, min_seconds=10.0, max_seconds=30.0):
-    """Oracle over whole passes of the batch until at least min_seconds."""
-    from oracle import oracle as O
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    n = 0
-    passes = 0
+# ---- CPU baseline (the oracle, as it stands) ---------------------------------
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _omp_threads(n):
+    """Set the OpenMP thread count of the process (the oracle's libgomp)."""
+    try:
+        ctypes.CDLL("libgomp.so.1").omp_set_num_threads(int(n))
+        return True
+    except OSError:
+        return False
+
+
+def _timed_oracle(run, per_call, min_seconds, max_calls):
+    n = calls = 0
     t0 = time.perf_counter()
     while True:
-        O.decode_batch(inp)
-        n += inp["B"]
-        passes += 1
+        run(calls)
+        n += per_call
+        calls += 1
         el = time.perf_counter() - t0
-        if el >= min_seconds or el >= max_seconds:
-            break
-    return {"value": n / el, "unit": "queries/s", "cores": threads, "kind": "oracle",
-            "sample": f"{passes} passes over the {inp['B']}-query batch ({n} queries, {el:.1f} s, fp64 oracle, "
-                      f"OpenMP over queries)"}
+        if el >= min_seconds or calls >= max_calls:
+            return n, el
+
+
+def cpu_baseline(run, per_call, what, min_seconds=10.0, single_seconds=3.0):
+    """run(i) executes the oracle on the i-th group of per_call queries.  All
+    host threads first (at least min_seconds), then one thread."""
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    n, el = _timed_oracle(run, per_call, min_seconds, 10 ** 9)
+    rec = {"value": round(n / el, 1), "unit": "queries/s", "cores": threads, "kind": "oracle",
+           "cpu_model": cpu_model(),
+           "sample": f"{n} queries of {what} in groups of {per_call} ({el:.1f} s, fp64 oracle, OpenMP over "
+                     f"queries on {threads} threads)"}
+    if _omp_threads(1):
+        n1, el1 = _timed_oracle(run, per_call, single_seconds, 10 ** 9)
+        _omp_threads(threads)
+        rec["single_thread"] = {"value": round(n1 / el1, 2), "unit": "queries/s",
+                                "sample": f"{n1} queries ({el1:.1f} s, one thread)"}
+    return rec
+
+
+# ---- timing helpers -----------------------------------------------------------
+
+def ramp_clocks(torch, ms=50.0):
+    """About `ms` of plain fills, so the clocks leave their idle state before
+    the warm-up steps."""
+    buf = torch.empty(1 << 26, dtype=torch.float32, device="cuda")
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1000.0 < ms:
+        for _ in range(20):
+            buf.fill_(1.0)
+        torch.cuda.synchronize()
+    del buf
+
+
+def timed(torch, fn, n, stream):
+    """Average microseconds per call of fn over n calls back to back between
+    two HIP events on the launch stream."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(n):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return 1000.0 * e0.elapsed_time(e1) / n
 
 
 def step_medians(torch, fn, steps, stream):
@@ -182,69 +239,75 @@ def step_medians(torch, fn, steps, stream):
     return out
 
 
-def bench_prefill(args):
-    """The prefill chunk (4,096 queries of one sequence at positions
-    126,976..131,071, compress ratio 8): one step = one csa2_prefill call."""
-    import torch
-    from sparse_long_context_amd import csa2, synth
-    print("[bench] generating the prefill chunk", file=sys.stderr, flush=True)
-    pf = synth.config(2)
-    w = csa2.PrefillWorkload(pf)
-    stream = torch.cuda.current_stream()
-    T = w.T
-    for _ in range(args.warmup):
-        w.prefill()
+def headline_steps(torch, fn, n_queries, steps, warmup, stream):
+    """W untimed steps, then exactly K timed steps between a synchronize and
+    two HIP events; returns (queries/s over the wall clock, ms per step)."""
+    for _ in range(warmup):
+        fn()
     torch.cuda.synchronize()
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    say(f"timing {steps} steps")
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
-        w.prefill()
+    for _ in range(steps):
+        fn()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = ev0.elapsed_time(ev1) / args.steps
-    # the attention on its own (the dominant kernel): the same batch through
-    # csa2_attend, launched back to back between two HIP events
-    inp = synth.prefill_as_batch(pf)
-    dw = csa2.DecodeWorkload(inp)
-    dw.topk.copy_(w.topk)
-    attend = lambda: csa2.csa2_attend(dw.dims, T, dw.batch, dw.q, dw.win_kv, dw.win_scale, dw.comp_kv,  # noqa: E731
-                                      dw.comp_scale, dw.topk, None, dw.out, dw.lse, None, 0)
-    for _ in range(args.warmup):
-        attend()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
-        attend()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    attn_us = 1000.0 * e0.elapsed_time(e1) / args.steps
+    return n_queries * steps / wall, ev0.elapsed_time(ev1) / steps
+
+
+# ---- the prefill chunk ----------------------------------------------------------
+
+def prefill_desc(pf):
+    d = pf["dims"]
+    T = int(pf["T"])
+    return (f"prefill chunk, {T} queries at positions {int(pf['pos0'])}..{int(pf['pos0']) + T - 1}, compress "
+            f"ratio {int(pf['ratio'])} -> {int(pf['pool_len'])} pool rows, window {d['window']}, "
+            f"top-{d['index_topk']}, {d['n_heads']} heads x {d['head_dim']}, {KV_NAMES[d['kv_dtype']]} KV, "
+            f"fp32 indexer keys dim {d['index_dim']}")
+
+
+def bench_prefill(args, torch, stream):
+    import numpy as np
+    from sparse_long_context_amd import csa2, synth
+    say("generating the prefill chunk")
+    pf = synth.config(2)
+    w = csa2.PrefillWorkload(pf)
+    T = w.T
+    ramp_clocks(torch)
+    value, ms_step = headline_steps(torch, w.prefill, T, args.steps, args.warmup, stream)
+    # the attention on its own (the dominant kernel): the same chunk in Reuse
+    # mode over the selections just made, so each call is the descriptor
+    # kernel and the attention
+    reuse = dict(pf, mode=synth.MODE_REUSE, sel_in=w.topk.cpu().numpy())
+    rw = csa2.PrefillWorkload(reuse)
+    for _ in range(max(args.warmup, 20)):
+        rw.prefill()
+    attn_us = timed(torch, rw.prefill, max(args.steps, 20), stream)
     step_us = step_medians(torch, w.prefill, min(args.steps, 20), stream)
     if args.copy_probe:
         copy_probe(torch)
-    ent = int(inp["win_len"].sum()) + T * pf["dims"]["index_topk"]
-    attn_flops = 4.0 * 64 * 512 * ent
-    achieved = attn_flops / (attn_us * 1e-6) / 1e12
     d = pf["dims"]
+    # entries per query: its window rows (128 everywhere here: the raw rows
+    # reach 127 positions before the chunk) plus its 512 selected rows
+    sel = rw.topk.cpu().numpy()
+    win_rows = T * d["window"]
+    ent = win_rows + int((sel >= 0).sum())
+    attn_flops = 4.0 * d["n_heads"] * d["head_dim"] * ent
+    achieved = attn_flops / (attn_us * 1e-6) / 1e12
     gather_bytes = ent * d["head_dim"] * 2 + T * d["n_heads"] * d["head_dim"] * (2 + 4)
     line = {
-        "metric": METRIC, "value": round(T * args.steps / wall, 1), "unit": "queries/s", "n_gpus": 1,
+        "metric": METRIC, "value": round(value, 1), "unit": "queries/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": (f"prefill chunk, {T} queries at positions {int(pf['pos0'])}..{int(pf['pos0']) + T - 1}, "
-                                f"compress ratio {int(pf['ratio'])} -> {int(pf['pool_len'])} pool rows, window "
-                                f"{d['window']}, top-{d['index_topk']}, {d['n_heads']} heads x {d['head_dim']}, bf16 KV, "
-                                f"fp32 indexer keys dim {d['index_dim']}"),
-                   "queries_per_step": T, "pool_rows": int(pf["pool_len"]), "window": d["window"],
-                   "index_topk": d["index_topk"], "kv": "bf16", "index_keys": "fp32"},
+        "config": {"workload": prefill_desc(pf), "queries_per_step": T, "pool_rows": int(pf["pool_len"]),
+                   "window": d["window"], "index_topk": d["index_topk"], "kv": "bf16", "index_keys": "fp32"},
         "roofline": {"bound": "mfma", "kernel": "attend_mq_kernel", "achieved": round(achieved, 1),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                      "traffic": traffic_from_profile("attend"), "algorithmic_flops_per_launch": attn_flops,
                      "avg_launch_us": round(attn_us, 2)},
-        "stages_us": {"attend": round(attn_us, 2)},
+        "stages_us": {"attend": round(attn_us, 2), "select": round(1000.0 * ms_step - attn_us, 2)},
         # the same launch against HBM bandwidth, every entry's row counted once
         # per use (as if gathered from HBM) plus q and the fp32 output: most
         # rows in fact come from the last-level cache (a 16 MiB pool)
@@ -254,47 +317,140 @@ def bench_prefill(args):
         "step_us": step_us,
         "gpu": torch.cuda.get_device_name(0),
     }
+    del rw
+    cpu = None
     if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline_prefill(pf, inp)
-    print(json.dumps(line), flush=True)
+        from oracle import oracle as O
+        say("timing the CPU oracle")
+        per = 64
+        cpu = cpu_baseline(lambda i: O.prefill_chunk(pf, (np.arange(per) + per * i) % T), per,
+                           "the chunk (scores against the shared 16,384-row pool, top-512, attention)")
+    del w
+    torch.cuda.empty_cache()
+    return line, cpu
 
 
-def cpu_baseline_prefill(pf, inp, min_seconds=10.0):
-    """Oracle over groups of 64 consecutive prefill queries (scores against
-    the shared pool, top-512, attention) until at least min_seconds."""
-    import numpy as np
-    from oracle import oracle as O
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    n = 0
-    t0 = time.perf_counter()
-    start = 0
-    while True:
-        qs = np.arange(start, start + 64) % pf["T"]
-        O.decode_batch(inp, qs)
-        n += len(qs)
-        start += 64
-        el = time.perf_counter() - t0
-        if el >= min_seconds:
-            break
-    return {"value": n / el, "unit": "queries/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} of the chunk's queries in groups of 64 ({el:.1f} s, fp64 oracle, OpenMP over queries)"}
+# ---- decode batches ------------------------------------------------------------
+
+def decode_desc(inp, storage):
+    d = inp["dims"]
+    kv = KV_NAMES[d["kv_dtype"]] if storage == "native" else KV_NAMES[2]
+    keys = "fp32" if storage == "native" else "mxfp4 (e2m1 + e8m0/32)"
+    B = int(inp["B"])
+    modes = inp["mode"]
+    if len(set(int(m) for m in modes)) == 1 and len(set(int(p) for p in inp["pos"])) == 1:
+        what = (f"decode, {B} queries, context {int(inp['pos'][0]) + 1}, compress ratio {int(inp['ratio'][0])} -> "
+                f"{int(inp['pool_len'][0])} candidates each")
+    else:
+        ctx = inp["pos"] + 1
+        nf, nr, nw = (int((modes == m).sum()) for m in (0, 2, 3))
+        full = modes == 0
+        nv = [min(int(pl), (int(p) + 1) // int(r)) for pl, p, r in
+              zip(inp["pool_len"][full], inp["pos"][full], inp["ratio"][full])]
+        what = (f"decode, {B} mixed-mode queries ({nf} Full, {nr} Reuse, {nw} window-only), contexts "
+                f"{int(ctx.min())}..{int(ctx.max())}, compress ratio 4 -> {min(nv)}..{max(nv)} candidates per "
+                f"Full query")
+    return {"workload": f"{what}, window {d['window']}, top-{d['index_topk']}, {d['n_heads']} heads x "
+                        f"{d['head_dim']}, {kv} KV, {keys} indexer keys dim {d['index_dim']}",
+            "queries_per_step": B, "window": d["window"], "index_topk": d["index_topk"], "kv": kv,
+            "index_keys": keys}
+
+
+def restore_fp4(torch, csa2, w):
+    """Re-store a bf16 workload's KV rows as FP4 and its index keys as MXFP4
+    with the library's own quantizers (on the GPU, before timing)."""
+    for name, scname in (("win_kv", "win_scale"), ("comp_kv", "comp_scale")):
+        src = getattr(w, name).view(torch.bfloat16).float()
+        rows = src.shape[0]
+        codes = torch.empty((rows, 256), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((rows, 32), dtype=torch.uint8, device="cuda")
+        csa2.csa2_quantize_fp4_kv(rows, 512, src, codes, scales)
+        setattr(w, name, codes)
+        setattr(w, scname, scales)
+        del src
+    rows = w.idx_k.shape[0]
+    kc = torch.empty((rows, 64), dtype=torch.uint8, device="cuda")
+    ks = torch.empty((rows, 4), dtype=torch.uint8, device="cuda")
+    csa2.csa2_quantize_mxfp4(rows, 128, w.idx_k, kc, ks)
+    w.idx_k, w.idx_k_scale = kc, ks
+    w.dims.kv_dtype, w.dims.index_key_dtype = 2, 1
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def bench_decode(torch, stream, inp, storage, steps, warmup, copy_probe_run=False):
+    from sparse_long_context_amd import csa2
+    w = csa2.DecodeWorkload(inp)
+    B = w.B
+    if storage == "fp4":
+        restore_fp4(torch, csa2, w)
+    value, ms_step = headline_steps(torch, w.decode, B, steps, warmup, stream)
+    # per-kernel durations: each stage entry point launched back to back
+    # between two HIP events on the launch stream (the same kernels and
+    # launch shapes csa2_decode issues)
+    stride = (w.max_cand + 63) // 64 * 64  # the row stride csa2_decode uses for its own score buffer
+    scores = torch.empty((B, max(stride, 1)), dtype=torch.float32, device="cuda")
+    stages = {
+        "index_scores": lambda: csa2.csa2_index_scores(w.dims, B, w.batch, w.idx_q, w.idx_w, w.idx_k, scores,
+                                                       stride, idx_k_scale=w.idx_k_scale),
+        "topk": lambda: csa2.csa2_topk(w.dims, B, w.batch, scores, stride, w.topk),
+        "attend": lambda: csa2.csa2_attend(w.dims, B, w.batch, w.q, w.win_kv, w.win_scale, w.comp_kv, w.comp_scale,
+                                           w.topk, w.sink, w.out, w.lse, w.ws, w.ws_bytes),
+    }
+    stage_us = {}
+    for name, fn in stages.items():
+        for _ in range(max(warmup, 20)):
+            fn()
+        stage_us[name] = timed(torch, fn, max(steps, 20), stream)
+    step_us = step_medians(torch, w.decode, min(max(steps, 10), 20), stream)
+    if copy_probe_run:
+        copy_probe(torch)
+    full = inp["mode"] == 0
+    n_cand = int(sum(min(int(p), (int(pos) + 1) // int(r)) for p, pos, r in
+                     zip(inp["pool_len"][full], inp["pos"][full], inp["ratio"][full])))
+    key_bytes = MXFP4_KEY_BYTES if storage == "fp4" else INDEX_KEY_BYTES
+    idx_bytes = n_cand * key_bytes + int(full.sum()) * INDEX_Q_BYTES
+    achieved = idx_bytes / (stage_us["index_scores"] * 1e-6) / 1e9
+    ent = 0
+    for b in range(B):
+        nv = min(int(inp["pool_len"][b]), (int(inp["pos"][b]) + 1) // max(int(inp["ratio"][b]), 1))
+        m = int(inp["mode"][b])
+        sel = min(512, nv) if m in (0, 1) else (int((inp["sel_in"][b] >= 0).sum()) if m == 2 else 0)
+        ent += int(inp["win_len"][b]) + sel
+    attn_flops = 4.0 * 64 * 512 * ent
+    attend_tflops = attn_flops / (stage_us["attend"] * 1e-6) / 1e12
+    res = {
+        "value": round(value, 1), "unit": "queries/s", "ms_per_step": round(ms_step, 4),
+        "dtype": "bf16", "config": decode_desc(inp, storage),
+        "roofline": {"bound": "hbm", "kernel": "index_scores_decode" if storage == "native" else "index_scores_decode_mx",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": idx_bytes,
+                     "avg_launch_us": round(stage_us["index_scores"], 2)},
+        "stages_us": {k: round(v, 2) for k, v in stage_us.items()},
+        "attend_mfma": {"achieved": round(attend_tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(attend_tflops / BF16_PEAK_TFLOPS, 4)},
+        "step_us": step_us,
+    }
+    del w, scores
+    torch.cuda.empty_cache()
+    return res
+
+
+EXTRAS = [("decode_full_64x16384", 1, "native"), ("decode_fp8_256x16384_ctx1M", 3, "native"),
+          ("mixed_128_ragged", 4, "native"), ("decode_full_64x16384_fp4_storage", 1, "fp4")]
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    # the clocks ramp for the first ~20 ms of sustained work (the prefill
-    # attention measured 499 us after 5 warm-up launches, 454 us after 100),
-    # so the default warm-up runs 100 untimed steps (and 100 launches before
-    # each stage's timing) to time the steady state
-    ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--config", type=int, default=1,
-                    help="workload index: decode 1, 3 or 4, or 2 (the 4,096-query prefill chunk)")
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2,
+                    help="headline workload: 2 (the 4,096-query prefill chunk, default) or a decode batch 1, 3, 4")
     ap.add_argument("--storage", choices=("native", "fp4"), default="native",
-                    help="fp4: the same workload with its KV rows re-stored as FP4 (E4M3 scale per 16) and its index "
-                         "keys as MXFP4, quantized on the GPU by the library's own quantizers before timing")
+                    help="with --config 1 or 4: KV rows re-stored as FP4 (E4M3 scale per 16) and index keys as "
+                         "MXFP4, quantized on the GPU by the library's own quantizers before timing")
+    ap.add_argument("--no-extras", action="store_true", help="time the headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain %d MiB fill and sum (for scaling rocprofv3 byte counters)" % (COPY_PROBE_BYTES >> 20))
@@ -308,135 +464,64 @@ def main():
         summarize_traffic(*args.traffic_from, which=args.traffic_kernel)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); the decode batch "
-              "shards by sequence with no exchange, so N GPUs would each run this same step on their own "
-              "queries.", file=sys.stderr)
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); decode batches shard "
+              "by sequence with no exchange, and a long sequence by pool position with one all-gather of "
+              "(score, row) pairs and one merge of softmax partials, so each GPU would run this same step on "
+              "its own share.", file=sys.stderr)
+        sys.exit(2)
+    if args.config not in (1, 2, 3, 4):
+        print("bench.py times the workloads 1, 2, 3 or 4", file=sys.stderr)
+        sys.exit(2)
+    if args.storage == "fp4" and args.config not in (1, 4):
+        print("--storage fp4 re-stores the bf16 decode workloads (1 or 4)", file=sys.stderr)
         sys.exit(2)
 
+    import numpy as np
     import torch
-    from sparse_long_context_amd import csa2, synth
+    from sparse_long_context_amd import synth
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    if args.config not in (1, 2, 3, 4):
-        print("bench.py times the workloads 1, 2, 3 or 4", file=sys.stderr)
-        sys.exit(2)
-    if args.config == 2:
-        if args.storage != "native":
-            print("--storage fp4 re-stores decode workloads only", file=sys.stderr)
-            sys.exit(2)
-        bench_prefill(args)
-        return
-    print(f"[bench] generating workload {args.config}", file=sys.stderr, flush=True)
-    inp = synth.config(args.config)
-    w = csa2.DecodeWorkload(inp)
     stream = torch.cuda.current_stream()
-    B = w.B
-    if args.storage == "fp4":
-        if inp["dims"]["kv_dtype"] != 0:
-            print("--storage fp4 re-stores bf16 workloads (1 or 4)", file=sys.stderr)
-            sys.exit(2)
-        print("[bench] re-storing KV as FP4 and index keys as MXFP4 on the GPU", file=sys.stderr, flush=True)
-        for name, scname in (("win_kv", "win_scale"), ("comp_kv", "comp_scale")):
-            src = getattr(w, name).view(torch.bfloat16).float()
-            rows = src.shape[0]
-            codes = torch.empty((rows, 256), dtype=torch.uint8, device="cuda")
-            scales = torch.empty((rows, 32), dtype=torch.uint8, device="cuda")
-            csa2.csa2_quantize_fp4_kv(rows, 512, src, codes, scales)
-            setattr(w, name, codes)
-            setattr(w, scname, scales)
-            del src
-        rows = w.idx_k.shape[0]
-        kc = torch.empty((rows, 64), dtype=torch.uint8, device="cuda")
-        ks = torch.empty((rows, 4), dtype=torch.uint8, device="cuda")
-        csa2.csa2_quantize_mxfp4(rows, 128, w.idx_k, kc, ks)
-        w.idx_k, w.idx_k_scale = kc, ks
-        w.dims.kv_dtype, w.dims.index_key_dtype = 2, 1
-        torch.cuda.synchronize()
-        torch.cuda.empty_cache()
 
-    for _ in range(args.warmup):
-        w.decode()
-    torch.cuda.synchronize()
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        w.decode()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = ev0.elapsed_time(ev1) / args.steps
-    value = B * args.steps / wall
+    if args.config == 2:
+        line, cpu = bench_prefill(args, torch, stream)
+    else:
+        say(f"generating workload {args.config}")
+        inp = synth.config(args.config)
+        ramp_clocks(torch)
+        res = bench_decode(torch, stream, inp, args.storage, args.steps, args.warmup, args.copy_probe)
+        line = {"metric": METRIC, "value": res["value"], "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
+                "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True,
+                "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+                "config": res["config"], "roofline": dict(res["roofline"]), "stages_us": res["stages_us"],
+                "attend_mfma": res["attend_mfma"], "step_us": res["step_us"], "gpu": torch.cuda.get_device_name(0)}
+        line["roofline"]["traffic"] = (traffic_from_profile("index")
+                                       if (args.config == 1 and args.storage == "native") else None)
+        cpu = None
+        if not args.no_cpu_baseline:
+            from oracle import oracle as O
+            say("timing the CPU oracle")
+            per = min(64, int(inp["B"]))
+            cpu = cpu_baseline(lambda i: O.decode_batch(inp, (np.arange(per) + per * i) % inp["B"]), per,
+                               f"the {inp['B']}-query batch")
+        del inp
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
 
-    # per-kernel durations: each of the three stage entry points launched
-    # `steps` times back to back between two HIP events on the launch stream
-    # (the same kernels and launch shapes csa2_decode issues)
-    stride = (w.max_cand + 63) // 64 * 64  # the row stride csa2_decode uses for its own score buffer
-    scores = torch.empty((B, stride), dtype=torch.float32, device="cuda")
-    stages = [
-        lambda: csa2.csa2_index_scores(w.dims, B, w.batch, w.idx_q, w.idx_w, w.idx_k, scores, stride,
-                                       idx_k_scale=w.idx_k_scale),
-        lambda: csa2.csa2_topk(w.dims, B, w.batch, scores, stride, w.topk),
-        lambda: csa2.csa2_attend(w.dims, B, w.batch, w.q, w.win_kv, w.win_scale, w.comp_kv, w.comp_scale, w.topk,
-                                 w.sink, w.out, w.lse, w.ws, w.ws_bytes),
-    ]
-    stage_us = []
-    for fn in stages:
-        for _ in range(args.warmup):
-            fn()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(args.steps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        stage_us.append(1000.0 * e0.elapsed_time(e1) / args.steps)
-    step_us = step_medians(torch, w.decode, args.steps, stream)
-    if args.copy_probe:
-        copy_probe(torch)
-
-    n_cand = int(sum(min(int(p), (int(pos) + 1) // int(r)) for p, pos, r, m in
-                     zip(inp["pool_len"], inp["pos"], inp["ratio"], inp["mode"]) if m == 0 and r > 0))
-    n_full = int((inp["mode"] == 0).sum())
-    key_bytes = MXFP4_KEY_BYTES if args.storage == "fp4" else INDEX_KEY_BYTES
-    idx_bytes = n_cand * key_bytes + n_full * INDEX_Q_BYTES
-    achieved = idx_bytes / (stage_us[0] * 1e-6) / 1e9
-    traffic = traffic_from_profile() if (args.config == 1 and args.storage == "native") else None
-    roofline = {"bound": "hbm", "kernel": "index_scores_decode" if args.storage == "native" else "index_scores_decode_mx", "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic, "algorithmic_bytes_per_launch": idx_bytes,
-                "avg_launch_us": round(stage_us[0], 2)}
-    # the attention contraction on its own: 2 x (64 x entries x 512) MACs per query
-    ent = 0
-    for b in range(B):
-        nv = min(int(inp["pool_len"][b]), (int(inp["pos"][b]) + 1) // max(int(inp["ratio"][b]), 1))
-        sel = min(512, nv) if inp["mode"][b] in (0, 1) else (int((inp["sel_in"][b] >= 0).sum())
-                                                            if inp["mode"][b] == 2 else 0)
-        ent += int(inp["win_len"][b]) + sel
-    attn_flops = 4.0 * 64 * 512 * ent
-    attend_tflops = attn_flops / (stage_us[2] * 1e-6) / 1e12
-
-    line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": workload_desc(inp, args.storage),
-        "roofline": roofline,
-        "stages_us": {"index_scores": round(stage_us[0], 2), "topk": round(stage_us[1], 2),
-                      "attend": round(stage_us[2], 2)},
-        "attend_mfma": {"achieved": round(attend_tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                        "frac": round(attend_tflops / BF16_PEAK_TFLOPS, 4)},
-        "step_us": step_us,
-        "gpu": torch.cuda.get_device_name(0),
-    }
-    if not args.no_cpu_baseline and args.storage == "native":
-        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(inp)
+    if args.config == 2 and not args.no_extras:
+        extras = {}
+        for name, idx, storage in EXTRAS:
+            try:
+                say(f"extra workload {name}: generating")
+                inp = synth.config(idx)
+                extras[name] = bench_decode(torch, stream, inp, storage, max(args.steps, 20), max(args.warmup, 20))
+                del inp
+            except Exception as e:  # an extra never hides the headline
+                extras[name] = {"error": repr(e)}
+            say(f"extra workload {name}: {json.dumps(extras[name].get('value'))} queries/s")
+        line["workloads"] = extras
     print(json.dumps(line), flush=True)
 
 

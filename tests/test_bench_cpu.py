@@ -57,3 +57,17 @@ def test_traffic_summary_scales_by_the_copy_probe(tmp_path):
     rec["kernel_source_sha256_16"] = "0" * 16
     json.dump(rec, open(out, "w"))
     assert b.traffic_from_profile("attend") is None
+
+
+def test_cpu_baseline_reports_cores_model_and_one_thread():
+    b = _bench()
+    calls = []
+
+    def run(i):
+        calls.append(i)
+        sum(range(20000))
+
+    rec = b.cpu_baseline(run, 8, "a test sample", min_seconds=0.05, single_seconds=0.02)
+    assert rec["kind"] == "oracle" and rec["unit"] == "queries/s" and rec["value"] > 0
+    assert rec["cores"] >= 1 and rec["cpu_model"]
+    assert rec["single_thread"]["value"] > 0
