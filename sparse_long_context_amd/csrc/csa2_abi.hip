@@ -266,12 +266,14 @@ csa2_status csa2_decode(const csa2_dims* dims, int32_t B, const csa2_batch* batc
                                                      align_up((size_t)B * stride * sizeof(float)))
                           : nullptr;
 
-  if (batch->max_candidates > 0) {
-    if ((st = hip_status(launch_index_scores(*dims, B, *batch, idx_q, idx_w, idx_k, idx_k_scale, scores, stride,
-                                             stream))) != CSA2_OK)
-      return st;
-    if ((st = hip_status(launch_topk(*dims, B, *batch, scores, stride, topk_idx, stream))) != CSA2_OK) return st;
-  }
+  // scores only when some candidate can exist; the top-K always runs, so
+  // every FULL / REINDEX row of topk_idx is written (all -1 when nothing is
+  // scored)
+  if (batch->max_candidates > 0 &&
+      (st = hip_status(launch_index_scores(*dims, B, *batch, idx_q, idx_w, idx_k, idx_k_scale, scores, stride,
+                                           stream))) != CSA2_OK)
+    return st;
+  if ((st = hip_status(launch_topk(*dims, B, *batch, scores, stride, topk_idx, stream))) != CSA2_OK) return st;
   if (hg)
     return hip_status(launch_attend_hg(*dims, B, *batch, q, win_kv, win_scale, comp_kv, comp_scale, topk_idx, sink,
                                        out, lse, stream));
@@ -328,14 +330,17 @@ csa2_status csa2_prefill(const csa2_dims* dims, const csa2_prefill_desc* desc, c
   bt.cand_idx = desc->mode == CSA2_MODE_REINDEX ? desc->cand_idx : nullptr;
   bt.max_candidates = max_cand;
 
-  if (selects && max_cand > 0) {
-    if (desc->mode == CSA2_MODE_FULL && dims->index_heads == 1 && dims->index_key_dtype == CSA2_IDXK_F32)
-      st = hip_status(launch_index_scores_prefill(*dims, T, m.pos, desc->mode, desc->compress_ratio, desc->pool_len,
-                                                  idx_q, idx_w, static_cast<const float*>(idx_k), scores, stride,
-                                                  stream));
-    else
-      st = hip_status(launch_index_scores(*dims, T, bt, idx_q, idx_w, idx_k, idx_k_scale, scores, stride, stream));
-    if (st != CSA2_OK) return st;
+  if (selects) {
+    if (max_cand > 0) {
+      if (desc->mode == CSA2_MODE_FULL && dims->index_heads == 1 && dims->index_key_dtype == CSA2_IDXK_F32)
+        st = hip_status(launch_index_scores_prefill(*dims, T, m.pos, desc->mode, desc->compress_ratio,
+                                                    desc->pool_len, idx_q, idx_w, static_cast<const float*>(idx_k),
+                                                    scores, stride, stream));
+      else
+        st = hip_status(launch_index_scores(*dims, T, bt, idx_q, idx_w, idx_k, idx_k_scale, scores, stride, stream));
+      if (st != CSA2_OK) return st;
+    }
+    // always: with nothing scored every row becomes -1
     if ((st = hip_status(launch_topk(*dims, T, bt, scores, stride, topk_idx, stream))) != CSA2_OK) return st;
   }
   return attend_common(dims, T, &bt, q, win_kv, win_scale, comp_kv, comp_scale,

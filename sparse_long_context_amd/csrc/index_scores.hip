@@ -85,7 +85,8 @@ __global__ __launch_bounds__(kThreads, HP <= 4 ? 8 : 1) void index_scores_decode
   const int md = mode[b];
   if (md != CSA2_MODE_FULL && md != CSA2_MODE_REINDEX) return;
   const int64_t nv = n_valid_of(pos[b], ratio[b], md, pool_len[b]);
-  int64_t n = (md == CSA2_MODE_FULL) ? nv : (cand_off[b + 1] - cand_off[b]);
+  // a REINDEX query without lists (cand_off NULL) has an empty list
+  int64_t n = (md == CSA2_MODE_FULL) ? nv : (cand_off ? cand_off[b + 1] - cand_off[b] : 0);
   if (n > max_cand) n = max_cand;
   const int64_t j0 = (int64_t)blockIdx.x * kRows;
   if (j0 >= n) return;
@@ -175,7 +176,7 @@ __global__ __launch_bounds__(kMxThreads) void index_scores_decode_mx(
   if (md != CSA2_MODE_FULL && md != CSA2_MODE_REINDEX) return;
   if (ONE) hi = 1;
   const int64_t nv = n_valid_of(pos[b], ratio[b], md, pool_len[b]);
-  int64_t n = (md == CSA2_MODE_FULL) ? nv : (cand_off[b + 1] - cand_off[b]);
+  int64_t n = (md == CSA2_MODE_FULL) ? nv : (cand_off ? cand_off[b + 1] - cand_off[b] : 0);
   if (n > max_cand) n = max_cand;
   const int64_t j0 = (int64_t)blockIdx.x * kMxRows;
   if (j0 >= n) return;

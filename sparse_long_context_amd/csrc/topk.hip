@@ -178,10 +178,11 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
   const int md = mode[b];
   if (md != CSA2_MODE_FULL && md != CSA2_MODE_REINDEX) return;
   const int64_t nv = n_valid_of(pos[b], ratio[b], md, pool_len[b]);
-  int64_t n64 = (md == CSA2_MODE_FULL) ? nv : (cand_off[b + 1] - cand_off[b]);
+  // a REINDEX query without lists (cand_off NULL) has an empty list
+  int64_t n64 = (md == CSA2_MODE_FULL) ? nv : (cand_off ? cand_off[b + 1] - cand_off[b] : 0);
   if (n64 > max_cand) n64 = max_cand;
   const int n = (int)n64;
-  const int32_t* lst = (md == CSA2_MODE_REINDEX) ? cand_idx + cand_off[b] : nullptr;
+  const int32_t* lst = (md == CSA2_MODE_REINDEX && n64 > 0) ? cand_idx + cand_off[b] : nullptr;
   const float* sc = scores + (int64_t)b * stride;
   int32_t* out = topk_idx + (int64_t)b * K;
   const bool sc_aligned = (reinterpret_cast<uintptr_t>(sc) & 15u) == 0;
