@@ -58,7 +58,9 @@
  *            codes uint8 [rows][64] with idx_k_scale uint8 [rows][4]
  *            (E8M0, value = code * 2^(s-127), one scale per 32 values)
  *   win_kv / comp_kv: bf16 [rows][512], or fp8 codes uint8 [rows][512] with
- *            scales uint8 [rows][16] (UE8M0, value = code * 2^(s-127)), or FP4
+ *            scales uint8 [rows][16] (UE8M0, value = code * 2^(s-127), s = 0 .. 254;
+ *            255 is NaN and not allowed; decoded values below 2^-126 in magnitude
+ *            may be flushed to zero in the bf16 / fp32 arithmetic), or FP4
  *            codes uint8 [rows][256] with scales uint8 [rows][32] (E4M3,
  *            value = code * scale, one scale per 16 values)
  *   FP4 codes: E2M1 (0, +-0.5, +-1, +-1.5, +-2, +-3, +-4, +-6), two per byte,
@@ -77,15 +79,29 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 2
+#define CSA2_ABI_VERSION 3
 
 typedef enum {
   CSA2_OK = 0,
   CSA2_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad enum, ... */
   CSA2_ERR_UNSUPPORTED = 2, /* geometry this build does not implement */
   CSA2_ERR_WORKSPACE = 3,   /* workspace missing or too small */
-  CSA2_ERR_HIP = 4          /* a kernel launch failed; see csa2_last_hip_error */
+  CSA2_ERR_HIP = 4,         /* a kernel launch failed; see csa2_last_hip_error */
+  CSA2_ERR_PRECONDITION = 5 /* CSA2_DEBUG_CHECK=1 only: a device-side precondition does not
+                               hold; see csa2_last_precondition */
 } csa2_status;
+
+/* Bits of the device-side precondition word (csa2_last_precondition). */
+#define CSA2_PRE_MODE 1u      /* a mode outside FULL .. WINDOW */
+#define CSA2_PRE_DESC 2u      /* a negative position / ratio / row0 / length, win_len above the
+                                 window, or decreasing cand_off */
+#define CSA2_PRE_LIST 4u      /* a Reindex list that is not strictly ascending before its -1
+                                 padding, or holds an entry below -1 */
+#define CSA2_PRE_SEL 8u       /* an attended topk_idx entry outside [-1, pool_len) */
+#define CSA2_PRE_KV_SCALE 16u /* an fp8 / FP4 scale byte that decodes to NaN in a row the query
+                                 can attend */
+#define CSA2_PRE_INDEX 32u    /* a non-finite index query, weight or fp32 key, or an MXFP4 key
+                                 scale byte 255, in what the call scores */
 
 typedef enum {
   CSA2_KV_BF16 = 0,
@@ -154,6 +170,20 @@ int csa2_abi_version(void);
 const char *csa2_status_str(csa2_status s);
 /* hipError_t of the last CSA2_ERR_HIP returned on this thread (0 if none). */
 int32_t csa2_last_hip_error(void);
+/* Precondition word (CSA2_PRE_* bits) of the last call on this thread that
+ * ran the device-side check: 0 when it passed or no call ran it.
+ *
+ * Device-side check.  Release calls trust device arrays: positions, lengths,
+ * lists, selections and scale bytes are preconditions (see "Conventions").
+ * With CSA2_DEBUG_CHECK=1 in the environment (read at every call), each of
+ * csa2_index_scores, csa2_topk, csa2_attend, csa2_decode, csa2_prefill and
+ * csa2_candidate_pool first runs one kernel over what the call will read, then
+ * reads the word back and waits for it on `stream` (the only synchronizing
+ * path of the library, so it cannot run under graph capture: CSA2_ERR_HIP
+ * then).  If a bit is set the call returns CSA2_ERR_PRECONDITION and launches
+ * nothing else (csa2_prefill has by then written only its workspace).  Checks
+ * of concurrent calls in one process run one at a time. */
+uint32_t csa2_last_precondition(void);
 
 /* Workspace bytes csa2_decode needs for B queries with at most max_candidates
  * candidates each (scores, plus the partials of the attention's entry splits,

@@ -14,7 +14,9 @@ import numpy as np
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libcsa2.so")
 
-CSA2_OK, CSA2_ERR_INVALID_ARG, CSA2_ERR_UNSUPPORTED, CSA2_ERR_WORKSPACE, CSA2_ERR_HIP = range(5)
+CSA2_OK, CSA2_ERR_INVALID_ARG, CSA2_ERR_UNSUPPORTED, CSA2_ERR_WORKSPACE, CSA2_ERR_HIP, CSA2_ERR_PRECONDITION = range(6)
+# bits of the device-side precondition word (CSA2_DEBUG_CHECK=1)
+CSA2_PRE_MODE, CSA2_PRE_DESC, CSA2_PRE_LIST, CSA2_PRE_SEL, CSA2_PRE_KV_SCALE, CSA2_PRE_INDEX = 1, 2, 4, 8, 16, 32
 MODE_FULL, MODE_REINDEX, MODE_REUSE, MODE_WINDOW = range(4)
 KV_BF16, KV_FP8, KV_FP4 = 0, 1, 2
 IDXK_F32, IDXK_MXFP4 = 0, 1
@@ -51,7 +53,8 @@ class PrefillDesc(C.Structure):
 
 
 _lib = None
-EXPORTS = ["csa2_abi_version", "csa2_status_str", "csa2_last_hip_error", "csa2_workspace_size",
+EXPORTS = ["csa2_abi_version", "csa2_status_str", "csa2_last_hip_error", "csa2_last_precondition",
+           "csa2_workspace_size",
            "csa2_index_scores", "csa2_topk", "csa2_attend", "csa2_decode", "csa2_prefill_workspace_size",
            "csa2_prefill", "csa2_quantize_fp4_kv", "csa2_quantize_mxfp4", "csa2_candidate_pool_workspace_size",
            "csa2_candidate_pool", "csa2_compress", "csa2_derotate"]
@@ -68,6 +71,7 @@ def lib():
         L.csa2_status_str.argtypes = [C.c_int]
         L.csa2_status_str.restype = C.c_char_p
         L.csa2_last_hip_error.restype = i32
+        L.csa2_last_precondition.restype = C.c_uint32
         L.csa2_workspace_size.argtypes = [P, i32, i32, C.POINTER(sz)]
         L.csa2_index_scores.argtypes = [P, i32, P, P, P, P, P, P, i64, P]
         L.csa2_topk.argtypes = [P, i32, P, P, i64, P, P]
@@ -81,7 +85,7 @@ def lib():
         L.csa2_compress.argtypes = [i64, i32, i32, P, P, P, C.c_float, P, P]
         L.csa2_derotate.argtypes = [P, i32, P, i32, i32, P, P, P]
         L.csa2_quantize_mxfp4.argtypes = [i64, i32, P, P, P, P]
-        for name in EXPORTS[3:]:
+        for name in EXPORTS[4:]:
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -119,6 +123,10 @@ def csa2_abi_version():
 
 def csa2_last_hip_error():
     return lib().csa2_last_hip_error()
+
+
+def csa2_last_precondition():
+    return lib().csa2_last_precondition()
 
 
 def csa2_workspace_size(dims, B, max_candidates):

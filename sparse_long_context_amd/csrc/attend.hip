@@ -86,7 +86,10 @@ __device__ __forceinline__ int lds_off(int r, int byte) {
 // Widen 8 E4M3 codes (two dwords) times 2^(e - 127) to 8 bf16 with the gfx950
 // scaled conversion; exact, since each product has at most 4 significant bits.
 __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 codes, uint32_t e) {
-  const float scale = __uint_as_float(e << 23);  // 2^(e-127); e in 1..254 for the stored scales
+  // the conversion takes its scale operand's exponent field as the UE8M0
+  // byte, so e = 0 (the bit pattern of +0.0f) means 2^-127 like any other
+  // byte; e = 255 (NaN) is outside the format
+  const float scale = __uint_as_float(e << 23);
   const auto a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.x, scale, false);
   const auto a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.x, scale, true);
   const auto a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.y, scale, false);

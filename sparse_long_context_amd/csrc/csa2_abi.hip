@@ -12,11 +12,7 @@ namespace {
 
 thread_local int32_t g_last_hip = 0;
 
-csa2_status hip_status(hipError_t e) {
-  if (e == hipSuccess) return CSA2_OK;
-  g_last_hip = (int32_t)e;
-  return CSA2_ERR_HIP;
-}
+csa2_status hip_status(hipError_t e) { return e == hipSuccess ? CSA2_OK : csa2::set_hip_error(e); }
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
@@ -127,6 +123,13 @@ csa2_status check_prefill(const csa2_dims* d, const csa2_prefill_desc* p) {
 
 }  // namespace
 
+namespace csa2 {
+csa2_status set_hip_error(hipError_t e) {
+  g_last_hip = (int32_t)e;
+  return CSA2_ERR_HIP;
+}
+}  // namespace csa2
+
 // ---- prefill descriptors ----------------------------------------------------
 namespace csa2 {
 namespace {
@@ -158,11 +161,14 @@ const char* csa2_status_str(csa2_status s) {
     case CSA2_ERR_UNSUPPORTED: return "unsupported geometry";
     case CSA2_ERR_WORKSPACE: return "workspace missing or too small";
     case CSA2_ERR_HIP: return "HIP launch failed";
+    case CSA2_ERR_PRECONDITION: return "device-side precondition failed (see csa2_last_precondition)";
   }
   return "unknown status";
 }
 
 int32_t csa2_last_hip_error(void) { return g_last_hip; }
+
+uint32_t csa2_last_precondition(void) { return last_precondition_word(); }
 
 csa2_status csa2_workspace_size(const csa2_dims* dims, int32_t B, int32_t max_candidates, size_t* bytes) {
   csa2_status st = check_dims(dims);
@@ -181,6 +187,9 @@ csa2_status csa2_index_scores(const csa2_dims* dims, int32_t B, const csa2_batch
   if (B == 0 || batch->max_candidates == 0) return CSA2_OK;
   if (!idx_q || !index_keys_ok(dims, idx_k, idx_k_scale) || !scores || score_stride < batch->max_candidates)
     return CSA2_ERR_INVALID_ARG;
+  if (debug_check_enabled() && (st = debug_check(*dims, B, *batch, kCheckLists | kCheckIndex, nullptr, idx_q, idx_w,
+                                                 idx_k, idx_k_scale, nullptr, nullptr, stream)) != CSA2_OK)
+    return st;
   return hip_status(
       launch_index_scores(*dims, B, *batch, idx_q, idx_w, idx_k, idx_k_scale, scores, score_stride, stream));
 }
@@ -193,6 +202,9 @@ csa2_status csa2_topk(const csa2_dims* dims, int32_t B, const csa2_batch* batch,
   if (B == 0) return CSA2_OK;
   if (!topk_idx || (batch->max_candidates > 0 && !scores) || score_stride < batch->max_candidates)
     return CSA2_ERR_INVALID_ARG;
+  if (debug_check_enabled() && (st = debug_check(*dims, B, *batch, kCheckLists, nullptr, nullptr, nullptr, nullptr,
+                                                 nullptr, nullptr, nullptr, stream)) != CSA2_OK)
+    return st;
   return hip_status(launch_topk(*dims, B, *batch, scores, score_stride, topk_idx, stream));
 }
 
@@ -229,6 +241,10 @@ csa2_status csa2_attend(const csa2_dims* dims, int32_t B, const csa2_batch* batc
   if (st == CSA2_OK && B > 0) st = check_attend_ptrs(dims, q, win_kv, win_scale, comp_kv, comp_scale, out);
   if (st != CSA2_OK) return st;
   if (B == 0) return CSA2_OK;
+  if (debug_check_enabled() &&
+      (st = debug_check(*dims, B, *batch, kCheckSelections | kCheckScales, topk_idx, nullptr, nullptr, nullptr,
+                        nullptr, win_scale, comp_scale, stream)) != CSA2_OK)
+    return st;
   if (use_head_groups(*dims, B))
     return hip_status(launch_attend_hg(*dims, B, *batch, q, win_kv, win_scale, comp_kv, comp_scale, topk_idx, sink,
                                        out, lse, stream));
@@ -249,6 +265,18 @@ csa2_status csa2_decode(const csa2_dims* dims, int32_t B, const csa2_batch* batc
                         const uint8_t* win_scale, const void* comp_kv, const uint8_t* comp_scale,
                         int32_t* topk_idx, const float* sink, float* out, float* lse, void* workspace,
                         size_t workspace_bytes, hipStream_t stream) {
+  return csa2::decode_impl(dims, B, batch, q, idx_q, idx_w, idx_k, idx_k_scale, win_kv, win_scale, comp_kv,
+                           comp_scale, topk_idx, sink, out, lse, workspace, workspace_bytes, stream);
+}
+}  // extern "C"
+
+// The decode step on a given workspace; csa2_decode hands in the caller's,
+// csa2_decode_static the library's static scratch.
+csa2_status csa2::decode_impl(const csa2_dims* dims, int32_t B, const csa2_batch* batch, const void* q,
+                              const float* idx_q, const float* idx_w, const void* idx_k, const uint8_t* idx_k_scale,
+                              const void* win_kv, const uint8_t* win_scale, const void* comp_kv,
+                              const uint8_t* comp_scale, int32_t* topk_idx, const float* sink, float* out,
+                              float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   csa2_status st = check_dims(dims);
   if (st == CSA2_OK) st = check_batch(batch, B);
   if (st == CSA2_OK && B > 0) st = check_attend_ptrs(dims, q, win_kv, win_scale, comp_kv, comp_scale, out);
@@ -259,6 +287,12 @@ csa2_status csa2_decode(const csa2_dims* dims, int32_t B, const csa2_batch* batc
   const bool hg = use_head_groups(*dims, B);
   const size_t need = decode_ws_bytes(B, batch->max_candidates, attend_splits(*dims, B));
   if (need > 0 && (!workspace || workspace_bytes < need)) return CSA2_ERR_WORKSPACE;
+  if (debug_check_enabled() &&
+      (st = debug_check(*dims, B, *batch,
+                        kCheckLists | kCheckSelections | kCheckSelectsOwn | kCheckScales |
+                            (batch->max_candidates > 0 ? kCheckIndex : 0),
+                        topk_idx, idx_q, idx_w, idx_k, idx_k_scale, win_scale, comp_scale, stream)) != CSA2_OK)
+    return st;
   const int64_t stride = (int64_t)score_stride_for(batch->max_candidates);
   float* scores = static_cast<float*>(workspace);
   const int sp = attend_splits(*dims, B);
@@ -280,6 +314,8 @@ csa2_status csa2_decode(const csa2_dims* dims, int32_t B, const csa2_batch* batc
   return attend_common(dims, B, batch, q, win_kv, win_scale, comp_kv, comp_scale, topk_idx, sink, out, lse, partial, sp,
                        stream);
 }
+
+extern "C" {
 
 csa2_status csa2_prefill_workspace_size(const csa2_dims* dims, const csa2_prefill_desc* desc, size_t* bytes) {
   csa2_status st = check_prefill(dims, desc);
@@ -329,6 +365,13 @@ csa2_status csa2_prefill(const csa2_dims* dims, const csa2_prefill_desc* desc, c
   bt.cand_off = desc->mode == CSA2_MODE_REINDEX ? desc->cand_off : nullptr;
   bt.cand_idx = desc->mode == CSA2_MODE_REINDEX ? desc->cand_idx : nullptr;
   bt.max_candidates = max_cand;
+  if (debug_check_enabled() &&
+      (st = debug_check(*dims, T, bt,
+                        kCheckLists | kCheckSelections | kCheckSelectsOwn | kCheckScales |
+                            (selects && max_cand > 0 ? kCheckIndex : 0),
+                        desc->mode == CSA2_MODE_WINDOW ? nullptr : topk_idx, idx_q, idx_w, idx_k, idx_k_scale,
+                        win_scale, comp_scale, stream)) != CSA2_OK)
+    return st;
 
   if (selects) {
     if (max_cand > 0) {
@@ -373,6 +416,14 @@ csa2_status csa2_candidate_pool(int32_t B, const csa2_batch* batch, const float*
     return CSA2_ERR_INVALID_ARG;
   const size_t need = candidate_pool_ws_bytes(B, batch->max_candidates, block_size, top_blocks);
   if (!workspace || workspace_bytes < need) return CSA2_ERR_WORKSPACE;
+  if (debug_check_enabled()) {
+    csa2_dims d{};
+    d.window = kMaxWindow;
+    d.index_topk = 1;
+    if ((st = debug_check(d, B, *batch, 0, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, stream)) !=
+        CSA2_OK)
+      return st;
+  }
   return hip_status(launch_candidate_pool(B, *batch, scores, score_stride, block_size, top_blocks, cand_off, cand_idx,
                                           workspace, stream));
 }

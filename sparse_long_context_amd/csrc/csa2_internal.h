@@ -112,6 +112,30 @@ hipError_t launch_compress(int64_t n_groups, int32_t m, int32_t d, const float* 
 hipError_t launch_derotate(int32_t B, const int64_t* pos, int32_t rope_off, int32_t rope_dims,
                            const double* inv_freq, float* out, hipStream_t s);
 
+// ---- device-side precondition check (CSA2_DEBUG_CHECK=1) ------------------
+// parts of a call the check covers
+constexpr int kCheckLists = 1;        // Reindex lists
+constexpr int kCheckSelections = 2;   // topk_idx rows the call attends
+constexpr int kCheckSelectsOwn = 4;   // the call selects for Full / Reindex queries itself
+constexpr int kCheckScales = 8;       // KV scale bytes of the rows a query can attend
+constexpr int kCheckIndex = 16;       // index query, weights and keys of the scoring
+bool debug_check_enabled();
+// Runs the check on `s` and waits for it: CSA2_OK, CSA2_ERR_PRECONDITION (the
+// word is kept for csa2_last_precondition) or CSA2_ERR_HIP.
+csa2_status debug_check(const csa2_dims& d, int32_t B, const csa2_batch& bt, int parts, const int32_t* sel,
+                        const float* idx_q, const float* idx_w, const void* idx_k, const uint8_t* idx_k_scale,
+                        const uint8_t* win_scale, const uint8_t* comp_scale, hipStream_t s);
+uint32_t last_precondition_word();
+// records a failed HIP call for csa2_last_hip_error and returns CSA2_ERR_HIP
+csa2_status set_hip_error(hipError_t e);
+
+// csa2_decode on a given workspace (the caller's, or the static scratch)
+csa2_status decode_impl(const csa2_dims* dims, int32_t B, const csa2_batch* batch, const void* q, const float* idx_q,
+                        const float* idx_w, const void* idx_k, const uint8_t* idx_k_scale, const void* win_kv,
+                        const uint8_t* win_scale, const void* comp_kv, const uint8_t* comp_scale, int32_t* topk_idx,
+                        const float* sink, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
 // Per-query descriptors of a prefill chunk, written into workspace arrays.
 hipError_t launch_prefill_meta(const csa2_prefill_desc& p, int32_t window, int64_t* pos, int32_t* mode,
                                int32_t* ratio, int64_t* win_row0, int32_t* win_len, int64_t* pool_row0,

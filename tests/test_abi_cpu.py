@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     for n in declared_functions():
         assert hasattr(L, n), n
     assert set(declared_functions()) == set(csa2.EXPORTS)
-    assert csa2.csa2_abi_version() == 2
+    assert csa2.csa2_abi_version() == 3
     assert csa2.status_str(0) == "ok"
 
 
@@ -195,3 +195,32 @@ def test_compress_and_derotate_arguments_are_validated():
     with pytest.raises(E) as e:
         csa2.csa2_derotate(d, 2, None, 448, 64, FAKE, FAKE, stream=0)
     assert e.value.status == csa2.CSA2_ERR_INVALID_ARG
+
+
+def test_precondition_status_and_word():
+    """The debug-check status has its own message; the word starts at 0, and
+    host-invalid arguments are refused before any device check runs (no GPU is
+    touched here), whether or not CSA2_DEBUG_CHECK is set."""
+    assert "precondition" in csa2.status_str(csa2.CSA2_ERR_PRECONDITION)
+    assert csa2.csa2_last_precondition() == 0
+    L = csa2.lib()
+    old = os.environ.get("CSA2_DEBUG_CHECK")
+    os.environ["CSA2_DEBUG_CHECK"] = "1"
+    try:
+        d, b = dims(), batch()
+        assert L.csa2_topk(C.byref(d), 2, C.byref(b), None, 16, None, None) == csa2.CSA2_ERR_INVALID_ARG
+        assert L.csa2_attend(C.byref(dims(n_heads=8)), 2, C.byref(b), FAKE, None, None, None, None, FAKE, None,
+                             FAKE, None, None, 0, None) == csa2.CSA2_ERR_UNSUPPORTED
+        # an empty batch is a no-op: nothing to check, nothing launched
+        assert L.csa2_topk(C.byref(d), 0, C.byref(b), None, 0, None, None) == csa2.CSA2_OK
+        assert csa2.csa2_last_precondition() == 0
+    finally:
+        if old is None:
+            del os.environ["CSA2_DEBUG_CHECK"]
+        else:
+            os.environ["CSA2_DEBUG_CHECK"] = old
+    # the header's bits are the binding's
+    src = open(os.path.join(ROOT, "include", "csa2.h")).read()
+    for name in ("MODE", "DESC", "LIST", "SEL", "KV_SCALE", "INDEX"):
+        m = re.search(r"#define CSA2_PRE_%s (\d+)u" % name, src)
+        assert m and int(m.group(1)) == getattr(csa2, "CSA2_PRE_" + name), name
