@@ -244,6 +244,23 @@ csa2_status csa2_decode(const csa2_dims *dims, int32_t B, const csa2_batch *batc
                         float *out, float *lse, void *workspace, size_t workspace_bytes,
                         hipStream_t stream);
 
+/* csa2_decode for callers that cannot allocate device memory (work captured
+ * into a HIP graph, serving loops or harnesses that forbid allocation): the
+ * same step with the same arguments and results, but no workspace argument.
+ * Its scratch is a static device array of CSA2_STATIC_SCRATCH_BYTES held by
+ * every GPU the library runs on until the process ends; the call allocates
+ * and frees nothing.  It returns CSA2_ERR_WORKSPACE, launching nothing, when
+ * csa2_workspace_size(dims, B, batch->max_candidates) exceeds that size (e.g.
+ * 64 queries x 16,384 candidates need 4 MiB, 128 x 65,536 need 32 MiB).  Calls
+ * that overlap on one GPU (other streams or threads) share the array and
+ * race: serialize them. */
+#define CSA2_STATIC_SCRATCH_BYTES (64u << 20)
+csa2_status csa2_decode_static(const csa2_dims *dims, int32_t B, const csa2_batch *batch, const void *q,
+                               const float *idx_q, const float *idx_w, const void *idx_k,
+                               const uint8_t *idx_k_scale, const void *win_kv, const uint8_t *win_scale,
+                               const void *comp_kv, const uint8_t *comp_scale, int32_t *topk_idx,
+                               const float *sink, float *out, float *lse, hipStream_t stream);
+
 /* Workspace bytes for csa2_prefill on this chunk. */
 csa2_status csa2_prefill_workspace_size(const csa2_dims *dims, const csa2_prefill_desc *desc,
                                         size_t *bytes);

@@ -57,7 +57,8 @@ EXPORTS = ["csa2_abi_version", "csa2_status_str", "csa2_last_hip_error", "csa2_l
            "csa2_workspace_size",
            "csa2_index_scores", "csa2_topk", "csa2_attend", "csa2_decode", "csa2_prefill_workspace_size",
            "csa2_prefill", "csa2_quantize_fp4_kv", "csa2_quantize_mxfp4", "csa2_candidate_pool_workspace_size",
-           "csa2_candidate_pool", "csa2_compress", "csa2_derotate"]
+           "csa2_candidate_pool", "csa2_compress", "csa2_derotate", "csa2_decode_static"]
+CSA2_STATIC_SCRATCH_BYTES = 64 << 20
 
 
 def lib():
@@ -85,6 +86,7 @@ def lib():
         L.csa2_compress.argtypes = [i64, i32, i32, P, P, P, C.c_float, P, P]
         L.csa2_derotate.argtypes = [P, i32, P, i32, i32, P, P, P]
         L.csa2_quantize_mxfp4.argtypes = [i64, i32, P, P, P, P]
+        L.csa2_decode_static.argtypes = [P, i32, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
         for name in EXPORTS[4:]:
             getattr(L, name).restype = C.c_int
         _lib = L
@@ -158,6 +160,13 @@ def csa2_decode(dims, B, batch, q, idx_q, idx_w, idx_k, win_kv, win_scale, comp_
                           _p(idx_k_scale), _p(win_kv),
                           _p(win_scale), _p(comp_kv), _p(comp_scale), _p(topk_idx), _p(sink), _p(out), _p(lse),
                           _p(workspace), workspace_bytes, _stream(stream)), "csa2_decode")
+
+
+def csa2_decode_static(dims, B, batch, q, idx_q, idx_w, idx_k, win_kv, win_scale, comp_kv, comp_scale, topk_idx,
+                       sink, out, lse, stream=None, idx_k_scale=None):
+    _ok(lib().csa2_decode_static(C.byref(dims), B, C.byref(batch), _p(q), _p(idx_q), _p(idx_w), _p(idx_k),
+                                 _p(idx_k_scale), _p(win_kv), _p(win_scale), _p(comp_kv), _p(comp_scale),
+                                 _p(topk_idx), _p(sink), _p(out), _p(lse), _stream(stream)), "csa2_decode_static")
 
 
 def csa2_prefill_workspace_size(dims, desc):
