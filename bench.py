@@ -41,6 +41,7 @@ sys.path.insert(0, ROOT)
 METRIC = "CSA2 attended queries/sec (64h×512, 128+512 keys) + % of HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+FP32_MFMA_TFLOPS = 157.3     # MI355X fp32 matrix, published
 INDEX_KEY_BYTES = 128 * 4    # one fp32 index key row per scanned candidate
 MXFP4_KEY_BYTES = 64 + 4     # one MXFP4 index key row: 64 code bytes + 4 E8M0 scales
 INDEX_Q_BYTES = 128 * 4      # one fp32 indexer query per query
@@ -285,6 +286,13 @@ def bench_prefill(args, torch, stream):
     for _ in range(max(args.warmup, 20)):
         rw.prefill()
     attn_us = timed(torch, rw.prefill, max(args.steps, 20), stream)
+    # the indexer on its own: the chunk's scores into a buffer of the step's stride
+    stride = (int(pf["pool_len"]) + 63) // 64 * 64
+    scores = torch.empty((T, stride), dtype=torch.float32, device="cuda")
+    for _ in range(max(args.warmup, 20)):
+        w.index_scores(scores, stride)
+    scores_us = timed(torch, lambda: w.index_scores(scores, stride), max(args.steps, 20), stream)
+    del scores
     step_us = step_medians(torch, w.prefill, min(args.steps, 20), stream)
     if args.copy_probe:
         copy_probe(torch)
@@ -295,6 +303,9 @@ def bench_prefill(args, torch, stream):
     win_rows = T * d["window"]
     ent = win_rows + int((sel >= 0).sum())
     attn_flops = 4.0 * d["n_heads"] * d["head_dim"] * ent
+    # indexer: one 128-long fp32 FMA chain per (query, reachable candidate)
+    idx_flops = 2.0 * d["index_dim"] * sum(min(int(pf["pool_len"]), (int(pf["pos0"]) + t + 1) // int(pf["ratio"]))
+                                           for t in range(T))
     achieved = attn_flops / (attn_us * 1e-6) / 1e12
     gather_bytes = ent * d["head_dim"] * 2 + T * d["n_heads"] * d["head_dim"] * (2 + 4)
     line = {
@@ -307,7 +318,14 @@ def bench_prefill(args, torch, stream):
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                      "traffic": traffic_from_profile("attend"), "algorithmic_flops_per_launch": attn_flops,
                      "avg_launch_us": round(attn_us, 2)},
-        "stages_us": {"attend": round(attn_us, 2), "select": round(1000.0 * ms_step - attn_us, 2)},
+        # select = the step less the attention; index_scores = the chunk's
+        # scores alone (with the 2-4 us descriptor kernel); the top-K is the rest
+        "stages_us": {"attend": round(attn_us, 2), "select": round(1000.0 * ms_step - attn_us, 2),
+                      "index_scores": round(scores_us, 2),
+                      "topk": round(1000.0 * ms_step - attn_us - scores_us, 2)},
+        "index_scores_mfma": {"achieved": round(idx_flops / (scores_us * 1e-6) / 1e12, 1), "peak": FP32_MFMA_TFLOPS,
+                              "unit": "TFLOP/s",
+                              "frac": round(idx_flops / (scores_us * 1e-6) / 1e12 / FP32_MFMA_TFLOPS, 4)},
         # the same launch against HBM bandwidth, every entry's row counted once
         # per use (as if gathered from HBM) plus q and the fp32 output: most
         # rows in fact come from the last-level cache (a 16 MiB pool)

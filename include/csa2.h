@@ -265,6 +265,19 @@ csa2_status csa2_decode_static(const csa2_dims *dims, int32_t B, const csa2_batc
 csa2_status csa2_prefill_workspace_size(const csa2_dims *dims, const csa2_prefill_desc *desc,
                                         size_t *bytes);
 
+/* Steps 1-2 for a FULL / REINDEX prefill chunk: scores[t * score_stride + j]
+ * for query t and its candidate j, exactly as csa2_index_scores defines them
+ * for the query at pos0 + t (FULL: candidate j is pool row j, j < n_valid;
+ * REINDEX: the j-th row of its list, unreachable rows -inf); other slots are
+ * not written.  Requires score_stride >= the chunk's candidate cap (pool_len
+ * for FULL, max_candidates for REINDEX) and a multiple of 4 (scores are
+ * stored 16 bytes at a time; `scores` is 16-byte aligned like every base).  The workspace is that of
+ * csa2_prefill (csa2_prefill_workspace_size).  Other modes: nothing to do. */
+csa2_status csa2_prefill_index_scores(const csa2_dims *dims, const csa2_prefill_desc *desc, const float *idx_q,
+                                      const float *idx_w, const void *idx_k, const uint8_t *idx_k_scale,
+                                      float *scores, int64_t score_stride, void *workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
+
 /* The whole step for one prefill chunk (T queries of one sequence sharing its
  * window rows, pool and index keys).  Per query t at p = pos0 + t: window rows
  * as in csa2_prefill_desc; reachability, scores and top-K as for decode; q,

@@ -57,7 +57,8 @@ EXPORTS = ["csa2_abi_version", "csa2_status_str", "csa2_last_hip_error", "csa2_l
            "csa2_workspace_size",
            "csa2_index_scores", "csa2_topk", "csa2_attend", "csa2_decode", "csa2_prefill_workspace_size",
            "csa2_prefill", "csa2_quantize_fp4_kv", "csa2_quantize_mxfp4", "csa2_candidate_pool_workspace_size",
-           "csa2_candidate_pool", "csa2_compress", "csa2_derotate", "csa2_decode_static"]
+           "csa2_candidate_pool", "csa2_compress", "csa2_derotate", "csa2_decode_static",
+           "csa2_prefill_index_scores"]
 CSA2_STATIC_SCRATCH_BYTES = 64 << 20
 
 
@@ -87,6 +88,7 @@ def lib():
         L.csa2_derotate.argtypes = [P, i32, P, i32, i32, P, P, P]
         L.csa2_quantize_mxfp4.argtypes = [i64, i32, P, P, P, P]
         L.csa2_decode_static.argtypes = [P, i32, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
+        L.csa2_prefill_index_scores.argtypes = [P, P, P, P, P, P, P, i64, P, sz, P]
         for name in EXPORTS[4:]:
             getattr(L, name).restype = C.c_int
         _lib = L
@@ -174,6 +176,13 @@ def csa2_prefill_workspace_size(dims, desc):
     _ok(lib().csa2_prefill_workspace_size(C.byref(dims), C.byref(desc), C.byref(out)),
         "csa2_prefill_workspace_size")
     return out.value
+
+
+def csa2_prefill_index_scores(dims, desc, idx_q, idx_w, idx_k, scores, score_stride, workspace, workspace_bytes,
+                              stream=None, idx_k_scale=None):
+    _ok(lib().csa2_prefill_index_scores(C.byref(dims), C.byref(desc), _p(idx_q), _p(idx_w), _p(idx_k),
+                                        _p(idx_k_scale), _p(scores), score_stride, _p(workspace), workspace_bytes,
+                                        _stream(stream)), "csa2_prefill_index_scores")
 
 
 def csa2_prefill(dims, desc, q, idx_q, idx_w, idx_k, win_kv, win_scale, comp_kv, comp_scale, topk_idx, sink,
@@ -294,6 +303,10 @@ class PrefillWorkload:
         self.lse = torch.empty((self.T, H), dtype=torch.float32, device=device)
         self.ws_bytes = csa2_prefill_workspace_size(self.dims, self.desc)
         self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=device)
+
+    def index_scores(self, scores, stride, stream=None):
+        csa2_prefill_index_scores(self.dims, self.desc, self.idx_q, self.idx_w, self.idx_k, scores, stride, self.ws,
+                                  self.ws_bytes, stream, idx_k_scale=self.idx_k_scale)
 
     def prefill(self, stream=None):
         csa2_prefill(self.dims, self.desc, self.q, self.idx_q, self.idx_w, self.idx_k, self.win_kv, self.win_scale,

@@ -403,8 +403,9 @@ __global__ __launch_bounds__(128) void attend_combine(int32_t n_split, const flo
 }  // namespace
 
 int attend_split_for(int32_t B) {
-  // aim for >= 256 workgroups (one per CU) when the batch alone gives fewer
-  int s = (B > 0) ? (256 + B - 1) / B : 1;
+  // aim for at least one workgroup per CU when the batch alone gives fewer
+  const int n_cu = device_cu_count();
+  int s = (B > 0) ? (n_cu + B - 1) / B : 1;
   return s < 1 ? 1 : (s > kMaxSplit ? kMaxSplit : s);
 }
 

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "csa2_internal.h"
 
 using namespace csa2;
@@ -110,6 +112,22 @@ int32_t prefill_max_cand(const csa2_prefill_desc* p) {
   return 0;
 }
 
+// The per-query batch view of a prefill chunk over its descriptor arrays.
+csa2_batch prefill_batch(const csa2_prefill_desc* desc, const PrefillMeta& m, int32_t max_cand) {
+  csa2_batch bt;
+  bt.pos = m.pos;
+  bt.mode = m.mode;
+  bt.compress_ratio = m.ratio;
+  bt.win_row0 = m.win_row0;
+  bt.win_len = m.win_len;
+  bt.pool_row0 = m.pool_row0;
+  bt.pool_len = m.pool_len;
+  bt.cand_off = desc->mode == CSA2_MODE_REINDEX ? desc->cand_off : nullptr;
+  bt.cand_idx = desc->mode == CSA2_MODE_REINDEX ? desc->cand_idx : nullptr;
+  bt.max_candidates = max_cand;
+  return bt;
+}
+
 csa2_status check_prefill(const csa2_dims* d, const csa2_prefill_desc* p) {
   csa2_status st = check_dims(d);
   if (st != CSA2_OK) return st;
@@ -124,6 +142,18 @@ csa2_status check_prefill(const csa2_dims* d, const csa2_prefill_desc* p) {
 }  // namespace
 
 namespace csa2 {
+int device_cu_count() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cached[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+  cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 csa2_status set_hip_error(hipError_t e) {
   g_last_hip = (int32_t)e;
   return CSA2_ERR_HIP;
@@ -149,6 +179,25 @@ __global__ void prefill_meta_kernel(csa2_prefill_desc p, int32_t W, PrefillMeta 
 }
 }  // namespace
 }  // namespace csa2
+
+namespace {
+// Scores of a prefill chunk: FULL chunks with one fp32-key index head score
+// every query against the shared keys as one matrix product (whose tiles
+// address 128 rows of scores with 32-bit byte offsets); any other form runs
+// the decode-shaped kernels over the chunk's per-query view.
+constexpr int64_t kPrefillScoreMaxStride = ((int64_t)1 << 23) - 64;
+csa2_status prefill_scores(const csa2_dims* dims, const csa2_prefill_desc* desc, const csa2_batch& bt,
+                           const PrefillMeta& m, const float* idx_q, const float* idx_w, const void* idx_k,
+                           const uint8_t* idx_k_scale, float* scores, int64_t stride, hipStream_t stream) {
+  const int32_t T = desc->n_queries;
+  if (desc->mode == CSA2_MODE_FULL && dims->index_heads == 1 && dims->index_key_dtype == CSA2_IDXK_F32 &&
+      stride <= kPrefillScoreMaxStride)
+    return hip_status(launch_index_scores_prefill(*dims, T, m.pos, desc->mode, desc->compress_ratio, desc->pool_len,
+                                                  idx_q, idx_w, static_cast<const float*>(idx_k), scores, stride,
+                                                  stream));
+  return hip_status(launch_index_scores(*dims, T, bt, idx_q, idx_w, idx_k, idx_k_scale, scores, stride, stream));
+}
+}  // namespace
 
 extern "C" {
 
@@ -326,6 +375,29 @@ csa2_status csa2_prefill_workspace_size(const csa2_dims* dims, const csa2_prefil
   return CSA2_OK;
 }
 
+csa2_status csa2_prefill_index_scores(const csa2_dims* dims, const csa2_prefill_desc* desc, const float* idx_q,
+                                      const float* idx_w, const void* idx_k, const uint8_t* idx_k_scale, float* scores,
+                                      int64_t score_stride, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+  csa2_status st = check_prefill(dims, desc);
+  if (st != CSA2_OK) return st;
+  const int32_t T = desc->n_queries;
+  const int32_t max_cand = prefill_max_cand(desc);
+  if (T == 0 || max_cand == 0) return CSA2_OK;
+  if (!idx_q || !index_keys_ok(dims, idx_k, idx_k_scale) || !scores || score_stride < max_cand ||
+      (score_stride % 4) != 0)
+    return CSA2_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < prefill_meta_bytes(T)) return CSA2_ERR_WORKSPACE;
+  PrefillMeta m = carve_meta(static_cast<uint8_t*>(workspace), T);
+  hipLaunchKernelGGL(prefill_meta_kernel, dim3((T + 255) / 256), dim3(256), 0, stream, *desc, dims->window, m);
+  if ((st = hip_status(hipGetLastError())) != CSA2_OK) return st;
+  csa2_batch bt = prefill_batch(desc, m, max_cand);
+  if (debug_check_enabled() && (st = debug_check(*dims, T, bt, kCheckLists | kCheckIndex, nullptr, idx_q, idx_w,
+                                                 idx_k, idx_k_scale, nullptr, nullptr, stream)) != CSA2_OK)
+    return st;
+  return prefill_scores(dims, desc, bt, m, idx_q, idx_w, idx_k, idx_k_scale, scores, score_stride, stream);
+}
+
 csa2_status csa2_prefill(const csa2_dims* dims, const csa2_prefill_desc* desc, const void* q, const float* idx_q,
                          const float* idx_w, const void* idx_k, const uint8_t* idx_k_scale, const void* win_kv,
                          const uint8_t* win_scale,
@@ -354,17 +426,7 @@ csa2_status csa2_prefill(const csa2_dims* dims, const csa2_prefill_desc* desc, c
 
   hipLaunchKernelGGL(prefill_meta_kernel, dim3((T + 255) / 256), dim3(256), 0, stream, *desc, dims->window, m);
   if ((st = hip_status(hipGetLastError())) != CSA2_OK) return st;
-  csa2_batch bt;
-  bt.pos = m.pos;
-  bt.mode = m.mode;
-  bt.compress_ratio = m.ratio;
-  bt.win_row0 = m.win_row0;
-  bt.win_len = m.win_len;
-  bt.pool_row0 = m.pool_row0;
-  bt.pool_len = m.pool_len;
-  bt.cand_off = desc->mode == CSA2_MODE_REINDEX ? desc->cand_off : nullptr;
-  bt.cand_idx = desc->mode == CSA2_MODE_REINDEX ? desc->cand_idx : nullptr;
-  bt.max_candidates = max_cand;
+  csa2_batch bt = prefill_batch(desc, m, max_cand);
   if (debug_check_enabled() &&
       (st = debug_check(*dims, T, bt,
                         kCheckLists | kCheckSelections | kCheckSelectsOwn | kCheckScales |
@@ -374,15 +436,9 @@ csa2_status csa2_prefill(const csa2_dims* dims, const csa2_prefill_desc* desc, c
     return st;
 
   if (selects) {
-    if (max_cand > 0) {
-      if (desc->mode == CSA2_MODE_FULL && dims->index_heads == 1 && dims->index_key_dtype == CSA2_IDXK_F32)
-        st = hip_status(launch_index_scores_prefill(*dims, T, m.pos, desc->mode, desc->compress_ratio,
-                                                    desc->pool_len, idx_q, idx_w, static_cast<const float*>(idx_k),
-                                                    scores, stride, stream));
-      else
-        st = hip_status(launch_index_scores(*dims, T, bt, idx_q, idx_w, idx_k, idx_k_scale, scores, stride, stream));
-      if (st != CSA2_OK) return st;
-    }
+    if (max_cand > 0 &&
+        (st = prefill_scores(dims, desc, bt, m, idx_q, idx_w, idx_k, idx_k_scale, scores, stride, stream)) != CSA2_OK)
+      return st;
     // always: with nothing scored every row becomes -1
     if ((st = hip_status(launch_topk(*dims, T, bt, scores, stride, topk_idx, stream))) != CSA2_OK) return st;
   }

@@ -126,6 +126,10 @@ csa2_status debug_check(const csa2_dims& d, int32_t B, const csa2_batch& bt, int
                         const float* idx_q, const float* idx_w, const void* idx_k, const uint8_t* idx_k_scale,
                         const uint8_t* win_scale, const uint8_t* comp_scale, hipStream_t s);
 uint32_t last_precondition_word();
+// compute units of the current device (cached per device; 256 when it cannot
+// be queried, e.g. with no GPU, so workspace sizes stay defined)
+int device_cu_count();
+
 // records a failed HIP call for csa2_last_hip_error and returns CSA2_ERR_HIP
 csa2_status set_hip_error(hipError_t e);
 

@@ -19,9 +19,9 @@
 //    fp32 exactly and runs its FMA chain, so the score is the one fp32 keys
 //    holding the decoded values would give.
 //  * prefill: one sequence, many queries sharing the key rows, so the keys are
-//    reused across queries: a register-tiled product of 128 queries x 128
-//    candidates per workgroup (8 x 8 outputs per thread), each output's FMA
-//    chain still running over i in order.
+//    reused across queries: 128 queries x 256 candidates per workgroup on the
+//    matrix cores, whose single-rounding fp32 rank-1 updates run each output's
+//    FMA chain over i in order.
 #include "csa2_internal.h"
 
 namespace csa2 {
@@ -267,97 +267,232 @@ __global__ __launch_bounds__(kMxThreads) void index_scores_decode_mx(
   scores[(int64_t)b * stride + j] = sc;
 }
 
-// ---- prefill: queries x candidates, register tiled -------------------------
-constexpr int kPQ = 128;  // queries per workgroup
-constexpr int kPC = 128;  // candidates per workgroup
-constexpr int kPK = 16;   // k slab
+// ---- prefill: queries x candidates on the matrix cores ---------------------
+// v_mfma_f32_32x32x1_2b_f32 is a rank-1 update D += a b^T of two 32 x 32 fp32
+// blocks, each element one fused multiply-add with a single rounding: a chain
+// of them over i = 0 .. 127 performs, per output, exactly the fmaf chain that
+// defines the score (checked bit for bit on the GPU against the VALU chain,
+// denormal and cancelling inputs included), at 32 fused operations per clock
+// per SIMD against the VALU's 16.
+//
+// Tiles of 128 queries x 256 candidates; each of the four waves takes 64
+// queries (the two blocks: A is a query's value at dim i) x 128 candidates
+// (four accumulator sets: in set g, column n is candidate 4 n + g, so a lane
+// ends up holding four consecutive scores of a row and stores them with one
+// 16-byte store).  The operands stream through LDS in slabs of 16 dims.  Two
+// resident workgroups per CU walk the tiles, so one's waits hide behind the
+// other's products; every slab's global loads (the next tile's first slab
+// included) are issued before the current slab's products, the barriers order
+// LDS only, and a tile's scores are stored during the next tile's first slab.
+// (A wave that has stores in flight waits for all of them with any later
+// load: gfx9 counts loads and stores together and they may complete out of
+// order, so only the other workgroup's products cover that drain.)
+typedef float f32x32 __attribute__((ext_vector_type(32)));
+constexpr int kPQ = 128;            // queries per tile
+constexpr int kPC = 256;            // candidates per tile
+constexpr int kPS = 16;             // dims per slab
+constexpr int kPSlabs = kIndexDim / kPS;
+constexpr int kPU = kPS / 4;        // 16-byte units of a row per slab
+constexpr int kPRow = kPS + 4;      // LDS row stride in floats (an odd number of units)
+constexpr int kPQv = kPQ * kPS / 4 / 256;  // float4 of q per thread per slab (4)
+constexpr int kPKv = kPC * kPS / 4 / 256;  // float4 of keys per thread per slab (8)
 
-__global__ __launch_bounds__(256, 4) void index_scores_prefill(
+// Key rows keep their 16-byte unit u at u ^ ((r >> 4) & 3): with an odd row
+// stride in units, the sixteen lanes of a read phase (rows 4 l + g, l < 16,
+// one unit) then hit sixteen distinct bank groups; query rows are read sixteen
+// consecutive rows at a time, which the odd stride alone spreads.
+__device__ __forceinline__ int key_unit(int r, int u) { return u ^ ((r >> 4) & 3); }
+
+// LDS writes of every wave visible to every wave, without waiting for this
+// wave's outstanding global loads and stores
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// RELU: f = max(., 0); WEIGHTED: per-query weights (else w = 1, and
+// fmaf(1, f, +0) = f + 0, which only turns -0 into +0)
+template <bool RELU, bool WEIGHTED>
+__global__ __launch_bounds__(256, 2) void index_scores_prefill(
     int32_t T, const int64_t* __restrict__ pos, int32_t md, int32_t ratio, int32_t pool_len,
-    const float* __restrict__ idx_q, const float* __restrict__ idx_w, int32_t relu,
-    const float* __restrict__ idx_k, float* __restrict__ scores, int64_t stride) {
-  __shared__ __attribute__((aligned(16))) float qs[kPK][kPQ];
-  __shared__ __attribute__((aligned(16))) float ks[kPK][kPC];
-  const int t = threadIdx.x;
-  const int tq = t >> 4, tc = t & 15;
-  const int q0 = blockIdx.y * kPQ, c0 = blockIdx.x * kPC;
-  const int qlast = (q0 + kPQ < T ? q0 + kPQ : T) - 1;
-  // the chunk's largest reachable count bounds every query's candidates here
-  const int64_t nmax = n_valid_of(pos[qlast], ratio, md, pool_len);
-  if (c0 >= nmax) return;
+    const float* __restrict__ idx_q, const float* __restrict__ idx_w,
+    const float* __restrict__ idx_k, float* __restrict__ scores, int64_t stride, int32_t n_ct, int32_t n_tiles) {
+  __shared__ __attribute__((aligned(16))) float qs[kPQ * kPRow];
+  __shared__ __attribute__((aligned(16))) float ks[kPC * kPRow];
+  __shared__ int32_t nv_s[2][kPQ];  // per tile parity: reachable count of each query
+  __shared__ float w_s[2][kPQ];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int wq = (wv >> 1) * 64, wc = (wv & 1) * 128;
 
-  float acc[8][8];
-#pragma unroll
-  for (int a = 0; a < 8; ++a)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[a][c] = 0.0f;
+  // tile k of this workgroup: query tile (id / n_ct), candidate tile (id % n_ct);
+  // a tile whose first candidate no query of it reaches is skipped whole
+  auto tile_of = [&](int k) -> int { return (int)blockIdx.x + k * (int)gridDim.x; };
+  auto tile_live = [&](int id, int& q0, int& c0, int64_t& nmax) -> bool {
+    q0 = (id / n_ct) * kPQ;
+    c0 = (id % n_ct) * kPC;
+    const int qlast = (q0 + kPQ < T ? q0 + kPQ : T) - 1;
+    nmax = n_valid_of(pos[qlast], ratio, md, pool_len);  // the tile's last query reaches furthest
+    return c0 < nmax;
+  };
+  auto next_live = [&](int k, int& q0, int& c0, int64_t& nmax) -> int {
+    for (; tile_of(k) < n_tiles; ++k)
+      if (tile_live(tile_of(k), q0, c0, nmax)) return k;
+    return -1;
+  };
 
-  // loaders: 128 rows x 16 floats per slab = 512 float4, two per thread; the
-  // next slab's loads are issued before the current slab's products
-  float4 vq[2], vk[2];
-  auto load = [&](int s) __attribute__((always_inline)) {
+  float4 vq[kPQv], vk[kPKv];
+  auto load = [&](int q0, int c0, int64_t nmax, int sl) __attribute__((always_inline)) {
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int p = it * 256 + t;
-      const int r = p >> 2, part = p & 3;
-      const int qq = q0 + r, cc = c0 + r;
-      vq[it] = (qq < T) ? *reinterpret_cast<const float4*>(idx_q + (int64_t)qq * kIndexDim + s * kPK + part * 4)
+    for (int it = 0; it < kPQv; ++it) {
+      const int p = it * 256 + t, r = p / kPU, part = p % kPU, qq = q0 + r;
+      vq[it] = (qq < T) ? *reinterpret_cast<const float4*>(idx_q + (int64_t)qq * kIndexDim + sl * kPS + part * 4)
                         : make_float4(0.f, 0.f, 0.f, 0.f);
-      vk[it] = (cc < nmax) ? *reinterpret_cast<const float4*>(idx_k + (int64_t)cc * kIndexDim + s * kPK + part * 4)
+    }
+#pragma unroll
+    for (int it = 0; it < kPKv; ++it) {
+      const int p = it * 256 + t, r = p / kPU, part = p % kPU, cc = c0 + r;
+      vk[it] = (cc < nmax) ? *reinterpret_cast<const float4*>(idx_k + (int64_t)cc * kIndexDim + sl * kPS + part * 4)
                            : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
   auto stage = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
+    for (int it = 0; it < kPQv; ++it) {
       const int p = it * 256 + t;
-      const int r = p >> 2, part = p & 3;
-      qs[part * 4 + 0][r] = vq[it].x;
-      qs[part * 4 + 1][r] = vq[it].y;
-      qs[part * 4 + 2][r] = vq[it].z;
-      qs[part * 4 + 3][r] = vq[it].w;
-      ks[part * 4 + 0][r] = vk[it].x;
-      ks[part * 4 + 1][r] = vk[it].y;
-      ks[part * 4 + 2][r] = vk[it].z;
-      ks[part * 4 + 3][r] = vk[it].w;
+      *reinterpret_cast<float4*>(&qs[(p / kPU) * kPRow + (p % kPU) * 4]) = vq[it];
+    }
+#pragma unroll
+    for (int it = 0; it < kPKv; ++it) {
+      const int p = it * 256 + t, r = p / kPU;
+      *reinterpret_cast<float4*>(&ks[r * kPRow + key_unit(r, p % kPU) * 4]) = vk[it];
     }
   };
-  load(0);
-  for (int s = 0; s < kIndexDim / kPK; ++s) {
-    stage();
-    __syncthreads();
-    if (s + 1 < kIndexDim / kPK) load(s + 1);
-#pragma unroll
-    for (int k = 0; k < kPK; ++k) {
-      const float4 qa = *reinterpret_cast<const float4*>(&qs[k][tq * 8]);
-      const float4 qb = *reinterpret_cast<const float4*>(&qs[k][tq * 8 + 4]);
-      const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
-      float kv[8];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) kv[c] = ks[k][tc + 16 * c];
-#pragma unroll
-      for (int a = 0; a < 8; ++a)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) acc[a][c] = __builtin_fmaf(qv[a], kv[c], acc[a][c]);
-    }
-    __syncthreads();
-  }
 
+  // this lane's operand rows: query wq + lane; candidates wc + 4 (lane % 32) + g
+  const float* qa = &qs[(wq + lane) * kPRow];
+  const int kr = wc + 4 * (lane & 31);
+  const float* kb = &ks[kr * kPRow];
+  const int ksw = (kr >> 4) & 3;  // the same swizzle for the four rows kr .. kr + 3
+
+  f32x32 acc[4];
+  // Scores of a finished tile (accumulators of the tile at q0p / c0p, its
+  // counts and weights in slot pp).  Positions ascend with the query in a
+  // chunk, so the tile's first query reaches least: when it reaches all 256
+  // candidates (nearly every tile) no score is tested.  D of set g, register
+  // r: block r / 16 (queries wq + 32 (r / 16) ..), row 8 ((r % 16) / 4) +
+  // 4 (lane / 32) + r % 4, column lane % 32 (candidate wc + 4 (lane % 32) + g).
+  auto store_tile = [&](int q0p, int c0p, int pp) __attribute__((always_inline)) {
+    // buffer stores from one descriptor per tile, at 32-bit byte offsets
+    // within it (the lane's first row and its four candidates, plus the row);
+    // the descriptor spans the tile's rows (the launcher keeps 128 rows x
+    // stride x 4 B below 2^32)
+    const int rows = T - q0p < kPQ ? T - q0p : kPQ;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        scores + (int64_t)q0p * stride + c0p, (short)0, rows > 0 ? (int32_t)((uint32_t)rows * (uint32_t)stride * 4u) : 0,
+        0x00020000);
+    const int lane_off = (int)(((uint32_t)(wq + 4 * (lane >> 5)) * (uint32_t)stride + (uint32_t)kr) * 4u);
+    // the row stride in bytes, opaque here, so the 32 row offsets are formed
+    // per store instead of being hoisted out of the tile loop into 32 live
+    // registers
+    uint32_t rstride = (uint32_t)stride * 4u;
+    asm volatile("" : "+s"(rstride));
+    auto score_of = [&](float a, int qt) __attribute__((always_inline)) -> float {
+      if (RELU) a = fmaxf(a, 0.0f);
+      if (!WEIGHTED) return a + 0.0f;
+      const float sc = __builtin_fmaf(w_s[pp][qt], a, 0.0f);
+      return sc == 0.0f ? 0.0f : sc;
+    };
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    if (nv_s[pp][0] >= c0p + kPC && q0p + kPQ <= T) {
 #pragma unroll
-  for (int a = 0; a < 8; ++a) {
-    const int qq = q0 + tq * 8 + a;
-    if (qq >= T) continue;
-    const int64_t nq = n_valid_of(pos[qq], ratio, md, pool_len);
-    const float wq = idx_w ? idx_w[qq] : 1.0f;
+      for (int r = 0; r < 32; ++r) {
+        const int row = 32 * (r >> 4) + 8 * ((r & 15) >> 2) + (r & 3);
+        const int qt = wq + row + 4 * (lane >> 5);
+        const u32x4 v = {__float_as_uint(score_of(acc[0][r], qt)), __float_as_uint(score_of(acc[1][r], qt)),
+                         __float_as_uint(score_of(acc[2][r], qt)), __float_as_uint(score_of(acc[3][r], qt))};
+        // the row's offset goes into the VGPR offset, not the SGPR one: with a
+        // register soffset the compiler inserts no wait state between this
+        // 16-byte store and the next write of its data registers, and the
+        // store then picked up the next row's first value (seen on gfx950)
+        __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, lane_off + (int)((uint32_t)row * rstride), 0, 0);
+      }
+    } else {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int cc = c0 + tc + 16 * c;
-      if (cc >= nq) continue;
-      float f = acc[a][c];
-      if (relu) f = f > 0.0f ? f : 0.0f;
-      float s = __builtin_fmaf(wq, f, 0.0f);
-      scores[(int64_t)qq * stride + cc] = (s == 0.0f) ? 0.0f : s;
+      for (int r = 0; r < 32; ++r) {
+        const int row = 32 * (r >> 4) + 8 * ((r & 15) >> 2) + (r & 3);
+        const int qt = wq + row + 4 * (lane >> 5);
+        const int nvq = nv_s[pp][qt] - (c0p + kr);  // candidates of this lane's four the query reaches
+        const int roff = lane_off + (int)((uint32_t)row * rstride);
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          if (g < nvq)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(score_of(acc[g][r], qt)), rsrc, roff + 4 * g, 0, 0);
+      }
+      // up to 128 stores: more than the 6-bit store count of a later wait can
+      // leave in flight, so the rare edge tile drains its own (vmcnt(0) only)
+      __builtin_amdgcn_s_waitcnt(0x0F70);
     }
+  };
+
+  int q0, c0;
+  int64_t nmax;
+  int k = next_live(0, q0, c0, nmax);
+  if (k < 0) return;
+  load(q0, c0, nmax, 0);
+  // the tile whose scores are still in the accumulators; before the first
+  // tile a placeholder whose queries reach nothing (slot 1 counts all 0), so
+  // its store writes nothing and every tile's store runs the same code
+  int q0p = T, c0p = 0;
+  if (t < kPQ) nv_s[1][t] = 0;
+  for (int par = 0; k >= 0; par ^= 1) {
+    if (t < kPQ) {
+      const int qq = q0 + t;
+      nv_s[par][t] = qq < T ? (int32_t)n_valid_of(pos[qq], ratio, md, pool_len) : 0;
+      if (WEIGHTED) w_s[par][t] = qq < T ? idx_w[qq] : 1.0f;
+    }
+    int nq0 = 0, nc0 = 0;
+    int64_t nnmax = 0;
+    const int kn = next_live(k + 1, nq0, nc0, nnmax);
+    for (int sl = 0; sl < kPSlabs; ++sl) {
+      stage();
+      lds_barrier();
+      if (sl + 1 < kPSlabs)
+        load(q0, c0, nmax, sl + 1);
+      else if (kn >= 0)
+        load(nq0, nc0, nnmax, 0);
+      if (sl == 0) {
+        // the previous tile's stores go out after this tile's second-slab
+        // loads, so waiting for those loads never waits for the stores
+        store_tile(q0p, c0p, par ^ 1);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) acc[g] = f32x32{};
+      }
+#pragma unroll
+      for (int u = 0; u < kPS / 4; ++u) {
+        const float4 a4 = *reinterpret_cast<const float4*>(qa + 4 * u);
+        float4 b4[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) b4[g] = *reinterpret_cast<const float4*>(kb + g * kPRow + 4 * (u ^ ksw));
+        const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float bv = j == 0 ? b4[g].x : j == 1 ? b4[g].y : j == 2 ? b4[g].z : b4[g].w;
+            acc[g] = __builtin_amdgcn_mfma_f32_32x32x1f32(av[j], bv, acc[g], 0, 0, 0);
+          }
+        }
+      }
+      lds_barrier();
+    }
+    q0p = q0;
+    c0p = c0;
+    k = kn;
+    q0 = nq0;
+    c0 = nc0;
+    nmax = nnmax;
+    if (k < 0) store_tile(q0p, c0p, par);
   }
 }
 
@@ -403,9 +538,21 @@ hipError_t launch_index_scores_prefill(const csa2_dims& d, int32_t T, const int6
                                        const float* idx_w, const float* idx_k, float* scores,
                                        int64_t stride, hipStream_t s) {
   if (T == 0 || pool_len == 0) return hipSuccess;
-  dim3 grid((pool_len + kPC - 1) / kPC, (T + kPQ - 1) / kPQ);
-  hipLaunchKernelGGL(index_scores_prefill, grid, dim3(256), 0, s, T, pos, mode, ratio, pool_len, idx_q,
-                     idx_w, d.index_relu, idx_k, scores, stride);
+  const int32_t n_ct = (pool_len + kPC - 1) / kPC;
+  const int32_t n_tiles = n_ct * ((T + kPQ - 1) / kPQ);
+  const int n_cu = device_cu_count();
+  const int grid = n_tiles < 2 * n_cu ? n_tiles : 2 * n_cu;  // two resident workgroups per CU
+#define CSA2_PF_LAUNCH(R, W)                                                                                \
+  hipLaunchKernelGGL((index_scores_prefill<R, W>), dim3(grid), dim3(256), 0, s, T, pos, mode, ratio, pool_len, \
+                     idx_q, idx_w, idx_k, scores, stride, n_ct, n_tiles)
+  if (d.index_relu) {
+    if (idx_w) CSA2_PF_LAUNCH(true, true);
+    else CSA2_PF_LAUNCH(true, false);
+  } else {
+    if (idx_w) CSA2_PF_LAUNCH(false, true);
+    else CSA2_PF_LAUNCH(false, false);
+  }
+#undef CSA2_PF_LAUNCH
   return hipGetLastError();
 }
 

@@ -171,3 +171,46 @@ def test_indexer_heads_relu_weights_prefill(hi, mode):
     w.prefill()
     torch.cuda.synchronize()
     compare_prefill(pf, w.topk.cpu().numpy(), w.out.cpu().numpy(), w.lse.cpu().numpy())
+
+
+def _prefill_scores(pf):
+    w = csa2.PrefillWorkload(pf)
+    pool = int(pf["pool_len"])
+    stride = (pool + 3) // 4 * 4 + 4  # a multiple of 4 past the cap, so slots after it are checked
+    scores = torch.full((w.T, stride), float("nan"), device="cuda")
+    w.index_scores(scores, stride)
+    torch.cuda.synchronize()
+    return scores.cpu().numpy()
+
+
+@pytest.mark.parametrize("relu,weights,T", [(0, False, 300), (1, True, 300), (0, False, 129)])
+def test_prefill_index_scores_bit_exact(relu, weights, T):
+    """The chunk's matrix-core scores equal the oracle's fixed-order fp32
+    scores bit for bit, over ragged query and candidate tiles, with the causal
+    limit per query (slots past it untouched)."""
+    pos0, m = 6003, 8
+    pool = (pos0 + T) // m  # the last queries reach every row, the first ones fewer
+    pf = synth.prefill_chunk(120 + relu, T, pos0, m, pool, dims=dims(index_relu=relu), weights=weights)
+    say(f"prefill scores T={T} pool={pool} relu={relu} weights={weights}")
+    sg = _prefill_scores(pf)
+    for t in range(T):
+        nv = O.n_valid(pos0 + t, m, 0, pool)
+        ref, _, _ = O.index_scores(pf["idx_q"][t], pf["idx_k"], w=None if pf["idx_w"] is None else pf["idx_w"][t],
+                                   relu=bool(relu), n=nv)
+        assert sg[t, :nv].tobytes() == ref.tobytes(), f"query {t}"
+        assert np.isnan(sg[t, nv:]).all(), f"query {t}: slots past its reachable count were written"
+
+
+def test_prefill_index_scores_full_size_sampled():
+    """The 4,096-query chunk (several tiles per workgroup): the scores of two
+    whole 128-query bands and the first and last query of every other band
+    against the oracle's, bit for bit."""
+    pf = synth.config(2)
+    say("prefill scores, 4,096 x 16,384")
+    sg = _prefill_scores(pf)
+    qs = sorted({0, 1, 4095, 4094} | {128 * k for k in range(0, 32, 2)} | {128 * k + 127 for k in range(1, 32, 2)}
+                | set(range(1920, 2048)) | set(range(3968, 4096)))
+    for t in qs:
+        nv = O.n_valid(int(pf["pos0"]) + t, 8, 0, 16384)
+        ref, _, _ = O.index_scores(pf["idx_q"][t], pf["idx_k"], n=nv)
+        assert sg[t, :nv].tobytes() == ref.tobytes(), f"query {t}"
