@@ -368,8 +368,11 @@ def decode_desc(inp, storage):
         what = (f"decode, {B} mixed-mode queries ({nf} Full, {nr} Reuse, {nw} window-only), contexts "
                 f"{int(ctx.min())}..{int(ctx.max())}, compress ratio 4 -> {min(nv)}..{max(nv)} candidates per "
                 f"Full query")
+    idx = f"{keys} indexer keys dim {d['index_dim']}"
+    if d["index_heads"] > 1:
+        idx += f", {d['index_heads']} ReLU index heads with per-head weights"
     return {"workload": f"{what}, window {d['window']}, top-{d['index_topk']}, {d['n_heads']} heads x "
-                        f"{d['head_dim']}, {kv} KV, {keys} indexer keys dim {d['index_dim']}",
+                        f"{d['head_dim']}, {kv} KV, {idx}",
             "queries_per_step": B, "window": d["window"], "index_topk": d["index_topk"], "kv": kv,
             "index_keys": keys}
 
@@ -429,6 +432,8 @@ def bench_decode(torch, stream, inp, storage, steps, warmup, copy_probe_run=Fals
     key_bytes = MXFP4_KEY_BYTES if storage == "fp4" else INDEX_KEY_BYTES
     idx_bytes = n_cand * key_bytes + int(full.sum()) * INDEX_Q_BYTES
     achieved = idx_bytes / (stage_us["index_scores"] * 1e-6) / 1e9
+    hi = int(inp["dims"]["index_heads"])
+    idx_flops = 2.0 * 128 * hi * n_cand
     ent = 0
     for b in range(B):
         nv = min(int(inp["pool_len"][b]), (int(inp["pos"][b]) + 1) // max(int(inp["ratio"][b]), 1))
@@ -445,6 +450,12 @@ def bench_decode(torch, stream, inp, storage, steps, warmup, copy_probe_run=Fals
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": idx_bytes,
                      "avg_launch_us": round(stage_us["index_scores"], 2)},
         "stages_us": {k: round(v, 2) for k, v in stage_us.items()},
+        # the indexer's fixed-order fp32 chains (H_I x 128 FMAs per candidate)
+        # against the fp32 matrix peak (they run on the matrix cores for
+        # 17 to 32 heads, on the vector units otherwise)
+        "index_scores_fp32": {"index_heads": hi, "achieved": round(idx_flops / (stage_us["index_scores"] * 1e-6) / 1e12, 2),
+                              "peak": FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                              "frac": round(idx_flops / (stage_us["index_scores"] * 1e-6) / 1e12 / FP32_MFMA_TFLOPS, 4)},
         "attend_mfma": {"achieved": round(attend_tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(attend_tflops / BF16_PEAK_TFLOPS, 4)},
         "step_us": step_us,
@@ -468,6 +479,9 @@ def main():
     ap.add_argument("--storage", choices=("native", "fp4"), default="native",
                     help="with --config 1 or 4: KV rows re-stored as FP4 (E4M3 scale per 16) and index keys as "
                          "MXFP4, quantized on the GPU by the library's own quantizers before timing")
+    ap.add_argument("--index-heads", type=int, default=1,
+                    help="with --config 1, 3 or 4: the pages' indexer form (this many ReLU heads with drawn per-head "
+                         "weights) instead of the workloads' one plain-dot head")
     ap.add_argument("--no-extras", action="store_true", help="time the headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -490,6 +504,9 @@ def main():
     if args.config not in (1, 2, 3, 4):
         print("bench.py times the workloads 1, 2, 3 or 4", file=sys.stderr)
         sys.exit(2)
+    if args.index_heads != 1 and args.config == 2:
+        print("--index-heads applies to the decode workloads (1, 3, 4)", file=sys.stderr)
+        sys.exit(2)
     if args.storage == "fp4" and args.config not in (1, 4):
         print("--storage fp4 re-stores the bf16 decode workloads (1 or 4)", file=sys.stderr)
         sys.exit(2)
@@ -507,14 +524,15 @@ def main():
         line, cpu = bench_prefill(args, torch, stream)
     else:
         say(f"generating workload {args.config}")
-        inp = synth.config(args.config)
+        inp = synth.config(args.config, index_heads=args.index_heads)
         ramp_clocks(torch)
         res = bench_decode(torch, stream, inp, args.storage, args.steps, args.warmup, args.copy_probe)
         line = {"metric": METRIC, "value": res["value"], "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
                 "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True,
                 "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
                 "config": res["config"], "roofline": dict(res["roofline"]), "stages_us": res["stages_us"],
-                "attend_mfma": res["attend_mfma"], "step_us": res["step_us"], "gpu": torch.cuda.get_device_name(0)}
+                "attend_mfma": res["attend_mfma"], "index_scores_fp32": res["index_scores_fp32"],
+                "step_us": res["step_us"], "gpu": torch.cuda.get_device_name(0)}
         line["roofline"]["traffic"] = (traffic_from_profile("index")
                                        if (args.config == 1 and args.storage == "native") else None)
         cpu = None

@@ -267,6 +267,134 @@ __global__ __launch_bounds__(kMxThreads) void index_scores_decode_mx(
   scores[(int64_t)b * stride + j] = sc;
 }
 
+// ---- decode, 17 .. 32 index heads (the pages' 32-head indexer) ------------
+// One query's heads against 64 candidates per wave on the matrix cores: in
+// v_mfma_f32_32x32x1_2b_f32, A is head h's query value at dim i (h = lane % 32,
+// the same in both blocks) and B a candidate's key value at dim i (64
+// candidates, 32 per block), so each element runs the fixed-order fmaf chain
+// of its (head, candidate).  Heads past H_I are zero with zero weight.  A
+// workgroup of four waves takes 256 candidates; key rows come in with
+// coalesced 16-byte loads through LDS in slabs of 32 dims (whole 128-byte
+// lines of each row), two slabs in flight.  The per-candidate sum over heads,
+// in head order, needs the 32 heads of a candidate in one lane: lanes l and
+// l + 32 hold complementary halves of the heads of candidates l % 32 (block 0)
+// and 32 + l % 32 (block 1), and one permlane32 swap per register pair leaves
+// lane l < 32 with all of block 0's and lane l + 32 with all of block 1's.
+typedef float f32x32 __attribute__((ext_vector_type(32)));
+constexpr int kHC = 256;           // candidates per workgroup
+constexpr int kHS = 32;            // dims per slab
+constexpr int kHU = kHS / 4;       // 16-byte units of a row per slab
+constexpr int kHRow = kHS + 4;     // LDS row stride in floats (9 units: sixteen consecutive rows, one unit,
+                                   // cover sixteen bank groups)
+constexpr int kHKv = kHC * kHS / 4 / 256;  // float4 of keys per thread per slab (8)
+constexpr int kHQRow = kIndexDim + 4;      // query rows 33 units apart
+
+__global__ __launch_bounds__(256, 2) void index_scores_decode_h32(
+    int32_t hi, int32_t relu, int32_t max_cand, const int64_t* __restrict__ pos,
+    const int32_t* __restrict__ mode, const int32_t* __restrict__ ratio,
+    const int64_t* __restrict__ pool_row0, const int32_t* __restrict__ pool_len,
+    const int64_t* __restrict__ cand_off, const int32_t* __restrict__ cand_idx,
+    const float* __restrict__ idx_q, const float* __restrict__ idx_w, const float* __restrict__ idx_k,
+    float* __restrict__ scores, int64_t stride) {
+  __shared__ __attribute__((aligned(16))) float ks[kHC * kHRow];
+  __shared__ __attribute__((aligned(16))) float qs[32 * kHQRow];  // [head][i], zero past H_I
+  __shared__ float w_s[32];
+  __shared__ int64_t row_s[kHC];
+  const int b = blockIdx.y;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int md = mode[b];
+  if (md != CSA2_MODE_FULL && md != CSA2_MODE_REINDEX) return;
+  const int64_t nv = n_valid_of(pos[b], ratio[b], md, pool_len[b]);
+  int64_t n = (md == CSA2_MODE_FULL) ? nv : (cand_off ? cand_off[b + 1] - cand_off[b] : 0);
+  if (n > max_cand) n = max_cand;
+  const int64_t j0 = (int64_t)blockIdx.x * kHC;
+  if (j0 >= n) return;
+
+  {  // candidate rows (pool-relative), -1 when there is none
+    const int64_t j = j0 + t;
+    int64_t r = -1;
+    if (j < n) {
+      const int64_t rr = (md == CSA2_MODE_FULL) ? j : (int64_t)cand_idx[cand_off[b] + j];
+      if (rr >= 0 && rr < nv) r = rr;
+    }
+    row_s[t] = r;
+  }
+  for (int x = t; x < 32 * kIndexDim; x += 256) {
+    const int h = x / kIndexDim, i = x % kIndexDim;
+    qs[h * kHQRow + i] = h < hi ? idx_q[((int64_t)b * hi + h) * kIndexDim + i] : 0.0f;
+  }
+  if (t < 32) w_s[t] = t < hi ? (idx_w ? idx_w[(int64_t)b * hi + t] : 1.0f) : 0.0f;
+  __syncthreads();
+
+  const float* kbase = idx_k + pool_row0[b] * kIndexDim;
+  // two slabs in flight: slab s lands in vk[s % 2]
+  float4 vk[2][kHKv];
+  auto load = [&](int sl, float4* v) __attribute__((always_inline)) {
+#pragma unroll
+    for (int it = 0; it < kHKv; ++it) {
+      const int p = it * 256 + t, r = p / kHU, u = p % kHU;
+      const int64_t rr = row_s[r];
+      v[it] = rr >= 0 ? load_stream(kbase + rr * kIndexDim + sl * kHS + u * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto stage = [&](const float4* v) __attribute__((always_inline)) {
+#pragma unroll
+    for (int it = 0; it < kHKv; ++it) {
+      const int p = it * 256 + t;
+      *reinterpret_cast<float4*>(&ks[(p / kHU) * kHRow + 4 * (p % kHU)]) = v[it];
+    }
+  };
+  f32x32 acc = f32x32{};
+  const float* qa = &qs[(lane & 31) * kHQRow];
+  const float* kb = &ks[(64 * wv + lane) * kHRow];
+  load(0, vk[0]);
+  load(1, vk[1]);
+#pragma unroll
+  for (int sl = 0; sl < kIndexDim / kHS; ++sl) {
+    stage(vk[sl & 1]);
+    __syncthreads();
+    if (sl + 2 < kIndexDim / kHS) load(sl + 2, vk[sl & 1]);
+#pragma unroll
+    for (int u = 0; u < kHU; ++u) {
+      const float4 a4 = *reinterpret_cast<const float4*>(qa + sl * kHS + 4 * u);
+      const float4 b4 = *reinterpret_cast<const float4*>(kb + 4 * u);
+      acc = __builtin_amdgcn_mfma_f32_32x32x1f32(a4.x, b4.x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x1f32(a4.y, b4.y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x1f32(a4.z, b4.z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x1f32(a4.w, b4.w, acc, 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  // D register r: block r / 16 (candidate 32 (r / 16) + lane % 32 of the
+  // wave), head 8 ((r % 16) / 4) + 4 (lane / 32) + r % 4.  After the swaps,
+  // mine[q] (q < 16) is head 8 (q / 4) + 4 upper + q % 4 and got[q] head
+  // 8 (q / 4) + 4 (1 - upper) + q % 4 of this lane's candidate.
+  const bool upper = lane >= 32;
+  float mine[16], got[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[q]), __float_as_uint(acc[16 + q]), false,
+                                                     false);
+    // lanes < 32: sw[0] = own block-0 value, sw[1] = block-0 value of lane + 32;
+    // lanes >= 32: sw[0] = block-1 value of lane - 32, sw[1] = own block-1 value
+    mine[q] = __uint_as_float(upper ? sw[1] : sw[0]);
+    got[q] = __uint_as_float(upper ? sw[0] : sw[1]);
+  }
+  float sc = 0.0f;
+#pragma unroll
+  for (int h = 0; h < 32; ++h) {
+    const int q = 4 * (h / 8) + (h % 4);
+    const bool second = ((h / 4) & 1) != 0;  // head in the +4 half
+    float f = (second != upper) ? got[q] : mine[q];
+    if (relu) f = f > 0.0f ? f : 0.0f;
+    sc = __builtin_fmaf(w_s[h], f, sc);
+  }
+  sc = sc == 0.0f ? 0.0f : sc;
+  const int c = 64 * wv + 32 * (upper ? 1 : 0) + (lane & 31);
+  const int64_t j = j0 + c;
+  if (j < n) scores[(int64_t)b * stride + j] = row_s[c] >= 0 ? sc : -__builtin_inff();
+}
+
 // ---- prefill: queries x candidates on the matrix cores ---------------------
 // v_mfma_f32_32x32x1_2b_f32 is a rank-1 update D += a b^T of two 32 x 32 fp32
 // blocks, each element one fused multiply-add with a single rounding: a chain
@@ -287,7 +415,6 @@ __global__ __launch_bounds__(kMxThreads) void index_scores_decode_mx(
 // (A wave that has stores in flight waits for all of them with any later
 // load: gfx9 counts loads and stores together and they may complete out of
 // order, so only the other workgroup's products cover that drain.)
-typedef float f32x32 __attribute__((ext_vector_type(32)));
 constexpr int kPQ = 128;            // queries per tile
 constexpr int kPC = 256;            // candidates per tile
 constexpr int kPS = 16;             // dims per slab
@@ -527,6 +654,9 @@ hipError_t launch_index_scores(const csa2_dims& d, int32_t B, const csa2_batch& 
     hipLaunchKernelGGL(index_scores_decode<4>, grid, dim3(kThreads), 0, s, CSA2_IDX_ARGS);
   else if (hi <= 16)
     hipLaunchKernelGGL(index_scores_decode<16>, grid, dim3(kThreads), 0, s, CSA2_IDX_ARGS);
+  else if (hi <= 32)
+    hipLaunchKernelGGL(index_scores_decode_h32, dim3((bt.max_candidates + kHC - 1) / kHC, B), dim3(256), 0, s,
+                       CSA2_IDX_ARGS);
   else
     hipLaunchKernelGGL(index_scores_decode<64>, grid, dim3(kThreads), 0, s, CSA2_IDX_ARGS);
 #undef CSA2_IDX_ARGS

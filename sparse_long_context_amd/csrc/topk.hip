@@ -231,16 +231,42 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
   };
 
   // ---- pass 1: histogram of the top 12 key bits ----
-  for (int x = t; x < kBins; x += kThreads) hist_s[x] = 0u;
+  // A floor below which no chosen key lies: every thread's largest key is a
+  // distinct key, so at least kThreads >= K keys are >= the smallest of
+  // those maxima, and so is the K-th best.  Keys below it are set ineligible
+  // (0) before counting: for Gaussian scores about a sixth of the list stays,
+  // which spares the LDS histogram most of its same-bucket atomics.  Only
+  // for a list held in registers (one segment).  The waves' minima travel
+  // with the barrier that clears the histogram.
+  const bool floored = nseg == 1 && K <= kThreads;
+  for (int x = t; x < kBins / 4; x += kThreads) reinterpret_cast<uint4*>(hist_s)[x] = make_uint4(0u, 0u, 0u, 0u);
   if (t == 0) bcount_s = 0u;
+  if (floored) {
+    uint32_t m = 0u;
+#pragma unroll
+    for (int j = 0; j < kKpt; ++j) m = k[j] > m ? k[j] : m;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const uint32_t o = (uint32_t)__shfl_xor((int)m, off, 64);
+      m = o < m ? o : m;
+    }
+    if (lane == 0) red_s[wv] = m;
+  }
   __syncthreads();
+  if (floored) {
+    uint32_t floor = red_s[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) floor = red_s[w] < floor ? red_s[w] : floor;
+#pragma unroll
+    for (int j = 0; j < kKpt; ++j) k[j] = k[j] >= floor ? k[j] : 0u;
+  }
   for (int s = 0; s < nseg; ++s) {
     seg_keys(s);
 #pragma unroll
     for (int j = 0; j < kKpt; ++j)
       if (k[j] != 0u) atomicAdd(&hist_s[k[j] >> 20], 1u);
   }
-  __syncthreads();
+  __syncthreads();  // (also orders the floor's reads of red_s before find_bucket writes it)
   find_bucket<kThreads>(hist_s, kBins, (uint32_t)K, red_s, pick_s, t, lane, wv);  // pick_s[2]: eligible total
   __syncthreads();
   const uint32_t total = pick_s[2];
@@ -299,6 +325,24 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
         // sum the quad (DPP quad_perm [1,0,3,2] then [2,3,0,1])
         r += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)r, 0xB1, 0xf, 0xf, false);
         r += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)r, 0x4E, 0xf, 0xf, false);
+        if (key < m && part == 0u && r == quota - 1u) thr_s = me;
+      } else if (m <= (uint32_t)(kThreads / 2)) {
+        // two threads per key (the usual bucket of a 16,384-key list holds
+        // ~200), each comparing against every other key
+        const uint32_t key = (uint32_t)t >> 1, part = (uint32_t)t & 1u;
+        const uint64_t me = bk_s[key < m ? key : 0u];
+        uint32_t r = 0;
+        uint32_t q = part;
+        for (; q + 14 < m; q += 16) {
+          uint64_t o[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) o[u] = bk_s[q + 2 * u];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) r += (uint32_t)(o[u] > me);
+        }
+        for (; q < m; q += 2) r += (uint32_t)(bk_s[q] > me);
+        // sum the pair (DPP quad_perm [1,0,3,2])
+        r += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)r, 0xB1, 0xf, 0xf, false);
         if (key < m && part == 0u && r == quota - 1u) thr_s = me;
       } else {
         // one thread per key, several keys per thread past kThreads

@@ -220,20 +220,24 @@ def prefill_chunk(seed, T, pos0, ratio, pool_len, dims=None, win_pos0=None, mode
 CONFIG_NAMES = ["tiny", "decode_full", "prefill", "decode_fp8_long", "mixed"]
 
 
-def config(idx):
-    """Build workload ``idx`` (0..4) at its full size."""
+def config(idx, index_heads=1):
+    """Build workload ``idx`` (0..4) at its full size.  index_heads > 1 gives
+    the workload the pages' indexer form instead of one plain-dot head:
+    index_heads ReLU heads with per-head weights drawn N(0, 1)."""
+    pages = index_heads > 1
+    kw = dict(index_heads=index_heads, index_relu=1 if pages else 0)
     if idx == 0:  # one query, all 1,024 compressed rows reachable (pos 4095, ratio 4)
-        return decode_batch(0, [4096], [MODE_FULL], [4])
+        return decode_batch(0, [4096], [MODE_FULL], [4], dims=default_dims(**kw), weights=pages)
     if idx == 1:  # 64 sequences at context 65,536, ratio 4 -> 16,384 candidates each
-        return decode_batch(1, [65536] * 64, [MODE_FULL] * 64, [4] * 64)
+        return decode_batch(1, [65536] * 64, [MODE_FULL] * 64, [4] * 64, dims=default_dims(**kw), weights=pages)
     if idx == 2:  # 4,096 queries at 126,976 .. 131,071, ratio 8 -> pool of 16,384
-        return prefill_chunk(2, 4096, 126976, 8, 16384)
+        return prefill_chunk(2, 4096, 126976, 8, 16384, dims=default_dims(**kw), weights=pages)
     if idx == 3:  # 256 sequences at context 2^20, ratio 64, fp8 window and pool
         return decode_batch(3, [1 << 20] * 256, [MODE_FULL] * 256, [64] * 256,
-                            dims=default_dims(kv_dtype=KV_FP8))
+                            dims=default_dims(kv_dtype=KV_FP8, **kw), weights=pages)
     if idx == 4:  # 128 queries, contexts U{1024..262144}; Full / Reuse / window-only by i mod 3
         ctx = uniform_int(4, S_CTX, 128, 1024, 262144)
         modes = [(MODE_FULL, MODE_REUSE, MODE_WINDOW)[i % 3] for i in range(128)]
         ratios = [0 if m == MODE_WINDOW else 4 for m in modes]
-        return decode_batch(4, ctx, modes, ratios)
+        return decode_batch(4, ctx, modes, ratios, dims=default_dims(**kw), weights=pages)
     raise ValueError(idx)

@@ -214,3 +214,31 @@ def test_prefill_index_scores_full_size_sampled():
         nv = O.n_valid(int(pf["pos0"]) + t, 8, 0, 16384)
         ref, _, _ = O.index_scores(pf["idx_q"][t], pf["idx_k"], n=nv)
         assert sg[t, :nv].tobytes() == ref.tobytes(), f"query {t}"
+
+
+@pytest.mark.parametrize("kind", ["denormal_sums", "large", "cancelling", "small_integers"])
+def test_prefill_index_scores_adversarial_bit_exact(kind):
+    """The chunk's matrix-core chain against the oracle's fmaf chain where a
+    single rounding per step matters most: partial sums in the fp32 denormal
+    range, magnitudes near 2^110, pairs that cancel to the last bit, and small
+    integers whose sums are exact."""
+    pos0, T, m = 5000, 260, 4
+    pool = (pos0 + T) // m
+    pf = synth.prefill_chunk(130, T, pos0, m, pool, dims=dims())
+    q, k = pf["idx_q"].astype(np.float64), pf["idx_k"].astype(np.float64)
+    if kind == "denormal_sums":
+        q, k = q * 2.0 ** -64, k * 2.0 ** -66
+    elif kind == "large":
+        q, k = q * 2.0 ** 56, k * 2.0 ** 54
+    elif kind == "cancelling":
+        k[:, 1::2] = k[:, 0::2] * (1.0 + 2.0 ** -20)
+        q[:, 1::2] = -q[:, 0::2]
+    else:
+        q, k = np.trunc(q * 8), np.trunc(k * 8)
+    pf["idx_q"], pf["idx_k"] = q.astype(np.float32), k.astype(np.float32)
+    say(f"prefill scores, adversarial inputs: {kind}")
+    sg = _prefill_scores(pf)
+    for t in range(T):
+        nv = O.n_valid(pos0 + t, m, 0, pool)
+        ref, _, _ = O.index_scores(pf["idx_q"][t], pf["idx_k"], n=nv)
+        assert sg[t, :nv].tobytes() == ref.tobytes(), f"query {t}"
