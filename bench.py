@@ -286,6 +286,14 @@ def bench_prefill(args, torch, stream):
     for _ in range(max(args.warmup, 20)):
         rw.prefill()
     attn_us = timed(torch, rw.prefill, max(args.steps, 20), stream)
+    # the output de-rotation (64 rope dims at offset 448, theta 160,000):
+    # fused into the attention's writes, and as its own pass over the output
+    inv_t = torch.from_numpy(160000.0 ** (-np.arange(32, dtype=np.float64) / 32.0)).cuda()
+    rope = csa2.out_rope(448, 64, inv_t)
+    pos_t = torch.arange(int(pf["pos0"]), int(pf["pos0"]) + T, dtype=torch.int64, device="cuda")
+    attn_rope_us = timed(torch, lambda: rw.prefill(rope=rope), max(args.steps, 20), stream)
+    derot_us = timed(torch, lambda: csa2.csa2_derotate(rw.dims, T, pos_t, 448, 64, inv_t, rw.out),
+                     max(args.steps, 20), stream)
     # the indexer on its own: the chunk's scores into a buffer of the step's stride
     stride = (int(pf["pool_len"]) + 63) // 64 * 64
     scores = torch.empty((T, stride), dtype=torch.float32, device="cuda")
@@ -332,6 +340,8 @@ def bench_prefill(args, torch, stream):
         "attend_gather": {"achieved": round(gather_bytes / (attn_us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
                           "unit": "GB/s", "frac": round(gather_bytes / (attn_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                           "bytes_per_launch": gather_bytes},
+        "output_derotation_us": {"attend_fused": round(attn_rope_us, 2), "attend_plain": round(attn_us, 2),
+                                 "separate_pass": round(derot_us, 2)},
         "step_us": step_us,
         "gpu": torch.cuda.get_device_name(0),
     }

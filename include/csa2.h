@@ -79,7 +79,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 3
+#define CSA2_ABI_VERSION 4
 
 typedef enum {
   CSA2_OK = 0,
@@ -166,6 +166,24 @@ typedef struct csa2_prefill_desc {
   int32_t max_candidates;  /* REINDEX: cap on list length per query (host); ignored otherwise */
 } csa2_prefill_desc;
 
+/* Output de-rotation fused into the attention's output writes ("DeepSeek-V4.1-
+ * Flash on WASTE", What is new, 1. CSA2: the rope dims of the output turn back
+ * by the query's own rotation).  Passed as `rope` to csa2_attend, csa2_decode,
+ * csa2_decode_static and csa2_prefill (NULL: outputs left as attended): the
+ * output of query b is written already turned exactly as csa2_derotate would
+ * turn it with pos[b] (same bits), saving that pass's read and write of
+ * `out`.  rope_offset and rope_dims even, rope_dims <= 128, rope_offset +
+ * rope_dims <= 512; inv_freq: device f64 [rope_dims / 2]; rope_dims == 0
+ * turns nothing.  Invalid fields: CSA2_ERR_INVALID_ARG.  The call's cosines
+ * and sines go to a 512-byte row per query of its workspace (counted in
+ * csa2_workspace_size and csa2_prefill_workspace_size), so csa2_attend needs
+ * a workspace for it (none: CSA2_ERR_WORKSPACE). */
+typedef struct csa2_out_rope {
+  int32_t rope_offset;
+  int32_t rope_dims;
+  const double *inv_freq;
+} csa2_out_rope;
+
 int csa2_abi_version(void);
 const char *csa2_status_str(csa2_status s);
 /* hipError_t of the last CSA2_ERR_HIP returned on this thread (0 if none). */
@@ -188,8 +206,9 @@ uint32_t csa2_last_precondition(void);
 /* Workspace bytes csa2_decode needs for B queries with at most max_candidates
  * candidates each (scores, plus the partials of the attention's entry splits,
  * which it takes for bf16 batches below 64 queries and fp8 / FP4 batches of
- * 65 to 255).  With max_candidates = 0 it is the workspace csa2_attend can
- * use to split entries. */
+ * 65 to 255, plus 512 bytes per query for a fused output de-rotation).  With
+ * max_candidates = 0 it is the workspace csa2_attend can use to split entries
+ * and to de-rotate. */
 csa2_status csa2_workspace_size(const csa2_dims *dims, int32_t B, int32_t max_candidates,
                                 size_t *bytes);
 
@@ -227,12 +246,12 @@ csa2_status csa2_topk(const csa2_dims *dims, int32_t B, const csa2_batch *batch,
  * every B, run workgroups of all 64 heads; with a workspace of
  * csa2_workspace_size(dims, B, 0) bytes the entries of a query may be split
  * over several such workgroups and merged, with workspace == NULL and
- * workspace_bytes == 0 every query runs unsplit. */
+ * workspace_bytes == 0 every query runs unsplit (and `rope` must be NULL). */
 csa2_status csa2_attend(const csa2_dims *dims, int32_t B, const csa2_batch *batch, const void *q,
                         const void *win_kv, const uint8_t *win_scale, const void *comp_kv,
                         const uint8_t *comp_scale, const int32_t *topk_idx, const float *sink,
                         float *out, float *lse, void *workspace, size_t workspace_bytes,
-                        hipStream_t stream);
+                        const csa2_out_rope *rope, hipStream_t stream);
 
 /* The whole step for a decode batch of independent queries with per-query
  * modes: scores + top-K for FULL / REINDEX queries (their topk_idx rows are
@@ -242,7 +261,7 @@ csa2_status csa2_decode(const csa2_dims *dims, int32_t B, const csa2_batch *batc
                         const uint8_t *idx_k_scale, const void *win_kv, const uint8_t *win_scale, const void *comp_kv,
                         const uint8_t *comp_scale, int32_t *topk_idx, const float *sink,
                         float *out, float *lse, void *workspace, size_t workspace_bytes,
-                        hipStream_t stream);
+                        const csa2_out_rope *rope, hipStream_t stream);
 
 /* csa2_decode for callers that cannot allocate device memory (work captured
  * into a HIP graph, serving loops or harnesses that forbid allocation): the
@@ -259,7 +278,8 @@ csa2_status csa2_decode_static(const csa2_dims *dims, int32_t B, const csa2_batc
                                const float *idx_q, const float *idx_w, const void *idx_k,
                                const uint8_t *idx_k_scale, const void *win_kv, const uint8_t *win_scale,
                                const void *comp_kv, const uint8_t *comp_scale, int32_t *topk_idx,
-                               const float *sink, float *out, float *lse, hipStream_t stream);
+                               const float *sink, float *out, float *lse, const csa2_out_rope *rope,
+                               hipStream_t stream);
 
 /* Workspace bytes for csa2_prefill on this chunk. */
 csa2_status csa2_prefill_workspace_size(const csa2_dims *dims, const csa2_prefill_desc *desc,
@@ -287,7 +307,7 @@ csa2_status csa2_prefill(const csa2_dims *dims, const csa2_prefill_desc *desc, c
                          const uint8_t *idx_k_scale, const void *win_kv, const uint8_t *win_scale, const void *comp_kv,
                          const uint8_t *comp_scale, int32_t *topk_idx, const float *sink,
                          float *out, float *lse, void *workspace, size_t workspace_bytes,
-                         hipStream_t stream);
+                         const csa2_out_rope *rope, hipStream_t stream);
 
 /* Hierarchical candidate pool (Reading Notes, 3f C3; PocketLLM page, "The
  * CSA2 attention layers"): from the scores csa2_index_scores wrote for the
@@ -325,7 +345,9 @@ csa2_status csa2_compress(int64_t n_groups, int32_t m, int32_t d, const float *c
  * -pos[b] * inv_freq[i]:  (x, y) -> (x cos a + y sin a, -x sin a + y cos a).
  * inv_freq: f64 [rope_dims / 2] (device), the caller's frequency schedule
  * (plain RoPE theta^(-2i/rope_dims), or a YaRN-scaled one).  pos: device int64
- * [B].  Angles, sines and cosines in fp64.  rope_dims even, at most 128. */
+ * [B].  Angles, sines and cosines in fp64, rounded to fp32; each output is
+ * one fp32 product and one fused multiply-add (x' = fma(x, c, y s), y' =
+ * fma(-x, s, y c)).  rope_dims even, at most 128. */
 csa2_status csa2_derotate(const csa2_dims *dims, int32_t B, const int64_t *pos, int32_t rope_offset,
                           int32_t rope_dims, const double *inv_freq, float *out, hipStream_t stream);
 

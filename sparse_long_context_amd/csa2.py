@@ -52,6 +52,20 @@ class PrefillDesc(C.Structure):
                 ("cand_off", C.c_void_p), ("cand_idx", C.c_void_p), ("max_candidates", C.c_int32)]
 
 
+class OutRope(C.Structure):
+    """csa2_out_rope: the output de-rotation fused into the attention's writes."""
+    _fields_ = [("rope_offset", C.c_int32), ("rope_dims", C.c_int32), ("inv_freq", C.c_void_p)]
+
+
+def out_rope(rope_offset, rope_dims, inv_freq):
+    """An OutRope over a device f64 tensor of rope_dims / 2 inverse frequencies."""
+    return OutRope(int(rope_offset), int(rope_dims), _p(inv_freq))
+
+
+def _rope(r):
+    return None if r is None else C.byref(r)
+
+
 _lib = None
 EXPORTS = ["csa2_abi_version", "csa2_status_str", "csa2_last_hip_error", "csa2_last_precondition",
            "csa2_workspace_size",
@@ -77,17 +91,17 @@ def lib():
         L.csa2_workspace_size.argtypes = [P, i32, i32, C.POINTER(sz)]
         L.csa2_index_scores.argtypes = [P, i32, P, P, P, P, P, P, i64, P]
         L.csa2_topk.argtypes = [P, i32, P, P, i64, P, P]
-        L.csa2_attend.argtypes = [P, i32, P, P, P, P, P, P, P, P, P, P, P, sz, P]
-        L.csa2_decode.argtypes = [P, i32, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]
+        L.csa2_attend.argtypes = [P, i32, P, P, P, P, P, P, P, P, P, P, P, sz, P, P]
+        L.csa2_decode.argtypes = [P, i32, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P, P]
         L.csa2_prefill_workspace_size.argtypes = [P, P, C.POINTER(sz)]
-        L.csa2_prefill.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]
+        L.csa2_prefill.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P, P]
         L.csa2_quantize_fp4_kv.argtypes = [i64, i32, P, P, P, P]
         L.csa2_candidate_pool_workspace_size.argtypes = [i32, i32, i32, i32, C.POINTER(sz)]
         L.csa2_candidate_pool.argtypes = [i32, P, P, i64, i32, i32, P, P, P, sz, P]
         L.csa2_compress.argtypes = [i64, i32, i32, P, P, P, C.c_float, P, P]
         L.csa2_derotate.argtypes = [P, i32, P, i32, i32, P, P, P]
         L.csa2_quantize_mxfp4.argtypes = [i64, i32, P, P, P, P]
-        L.csa2_decode_static.argtypes = [P, i32, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
+        L.csa2_decode_static.argtypes = [P, i32, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
         L.csa2_prefill_index_scores.argtypes = [P, P, P, P, P, P, P, i64, P, sz, P]
         for name in EXPORTS[4:]:
             getattr(L, name).restype = C.c_int
@@ -150,25 +164,26 @@ def csa2_topk(dims, B, batch, scores, score_stride, topk_idx, stream=None):
 
 
 def csa2_attend(dims, B, batch, q, win_kv, win_scale, comp_kv, comp_scale, topk_idx, sink, out, lse,
-                workspace, workspace_bytes, stream=None):
+                workspace, workspace_bytes, stream=None, rope=None):
     _ok(lib().csa2_attend(C.byref(dims), B, C.byref(batch), _p(q), _p(win_kv), _p(win_scale), _p(comp_kv),
                           _p(comp_scale), _p(topk_idx), _p(sink), _p(out), _p(lse), _p(workspace),
-                          workspace_bytes, _stream(stream)), "csa2_attend")
+                          workspace_bytes, _rope(rope), _stream(stream)), "csa2_attend")
 
 
 def csa2_decode(dims, B, batch, q, idx_q, idx_w, idx_k, win_kv, win_scale, comp_kv, comp_scale, topk_idx, sink,
-                out, lse, workspace, workspace_bytes, stream=None, idx_k_scale=None):
+                out, lse, workspace, workspace_bytes, stream=None, idx_k_scale=None, rope=None):
     _ok(lib().csa2_decode(C.byref(dims), B, C.byref(batch), _p(q), _p(idx_q), _p(idx_w), _p(idx_k),
                           _p(idx_k_scale), _p(win_kv),
                           _p(win_scale), _p(comp_kv), _p(comp_scale), _p(topk_idx), _p(sink), _p(out), _p(lse),
-                          _p(workspace), workspace_bytes, _stream(stream)), "csa2_decode")
+                          _p(workspace), workspace_bytes, _rope(rope), _stream(stream)), "csa2_decode")
 
 
 def csa2_decode_static(dims, B, batch, q, idx_q, idx_w, idx_k, win_kv, win_scale, comp_kv, comp_scale, topk_idx,
-                       sink, out, lse, stream=None, idx_k_scale=None):
+                       sink, out, lse, stream=None, idx_k_scale=None, rope=None):
     _ok(lib().csa2_decode_static(C.byref(dims), B, C.byref(batch), _p(q), _p(idx_q), _p(idx_w), _p(idx_k),
                                  _p(idx_k_scale), _p(win_kv), _p(win_scale), _p(comp_kv), _p(comp_scale),
-                                 _p(topk_idx), _p(sink), _p(out), _p(lse), _stream(stream)), "csa2_decode_static")
+                                 _p(topk_idx), _p(sink), _p(out), _p(lse), _rope(rope), _stream(stream)),
+        "csa2_decode_static")
 
 
 def csa2_prefill_workspace_size(dims, desc):
@@ -186,11 +201,11 @@ def csa2_prefill_index_scores(dims, desc, idx_q, idx_w, idx_k, scores, score_str
 
 
 def csa2_prefill(dims, desc, q, idx_q, idx_w, idx_k, win_kv, win_scale, comp_kv, comp_scale, topk_idx, sink,
-                 out, lse, workspace, workspace_bytes, stream=None, idx_k_scale=None):
+                 out, lse, workspace, workspace_bytes, stream=None, idx_k_scale=None, rope=None):
     _ok(lib().csa2_prefill(C.byref(dims), C.byref(desc), _p(q), _p(idx_q), _p(idx_w), _p(idx_k),
                            _p(idx_k_scale), _p(win_kv),
                            _p(win_scale), _p(comp_kv), _p(comp_scale), _p(topk_idx), _p(sink), _p(out), _p(lse),
-                           _p(workspace), workspace_bytes, _stream(stream)), "csa2_prefill")
+                           _p(workspace), workspace_bytes, _rope(rope), _stream(stream)), "csa2_prefill")
 
 
 def csa2_quantize_fp4_kv(n_rows, d, src, codes, scales, stream=None):
@@ -271,10 +286,10 @@ class DecodeWorkload:
         self.ws_bytes = csa2_workspace_size(self.dims, self.B, self.max_cand)
         self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=device)
 
-    def decode(self, stream=None):
+    def decode(self, stream=None, rope=None):
         csa2_decode(self.dims, self.B, self.batch, self.q, self.idx_q, self.idx_w, self.idx_k, self.win_kv,
                     self.win_scale, self.comp_kv, self.comp_scale, self.topk, self.sink, self.out, self.lse,
-                    self.ws, self.ws_bytes, stream, idx_k_scale=self.idx_k_scale)
+                    self.ws, self.ws_bytes, stream, idx_k_scale=self.idx_k_scale, rope=rope)
 
 
 class PrefillWorkload:
@@ -308,7 +323,7 @@ class PrefillWorkload:
         csa2_prefill_index_scores(self.dims, self.desc, self.idx_q, self.idx_w, self.idx_k, scores, stride, self.ws,
                                   self.ws_bytes, stream, idx_k_scale=self.idx_k_scale)
 
-    def prefill(self, stream=None):
+    def prefill(self, stream=None, rope=None):
         csa2_prefill(self.dims, self.desc, self.q, self.idx_q, self.idx_w, self.idx_k, self.win_kv, self.win_scale,
                      self.comp_kv, self.comp_scale, self.topk, self.sink, self.out, self.lse, self.ws, self.ws_bytes,
-                     stream, idx_k_scale=self.idx_k_scale)
+                     stream, idx_k_scale=self.idx_k_scale, rope=rope)

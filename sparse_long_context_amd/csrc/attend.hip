@@ -70,6 +70,7 @@ struct AttendArgs {
   int32_t W;
   int32_t n_split;
   float scale_log2;  // softmax_scale * log2(e)
+  RopeOut rope;      // de-rotation of unsplit outputs (splits: the merge's)
 };
 
 // 16-byte unit u of LDS row r lives at unit u ^ f(r), where f swaps the two
@@ -102,7 +103,8 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kPieces = kBufBytes / 16 / kThreads;  // 16-byte LDS units per thread per chunk (4)
 
-template <int KV>
+// ROPE: unsplit outputs leave de-rotated (its own instantiation)
+template <int KV, bool ROPE>
 __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kBufBytes];  // double buffer
   __shared__ __attribute__((aligned(16))) float xs_s[kWaves][8][64];     // partial scores
@@ -330,10 +332,37 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
       f = (L > 0.f) ? 1.f / L : 0.f;
     }
     float* op = a.out + ((int64_t)b * kHeads + head) * kDim + dh * 256 + 4 * g;
+    // de-rotation: a lane's sixteen columns of four dims meet up to eight
+    // rope columns, so the query's cosines and sines are staged once per
+    // workgroup in the partial-score LDS (idle since the last barrier)
+    constexpr bool turn = ROPE;
+    float* cs_t = &xs_s[0][0][0];
+    float* sn_t = cs_t + kRopePairs;
+    static_assert(sizeof(xs_s) >= 2 * kRopePairs * sizeof(float), "the rope table fits the score buffer");
+    if (turn) {
+      if (2 * t < a.rope.dims) {
+        const float2 v = a.rope.table[(int64_t)b * kRopePairs + t];
+        cs_t[t] = v.x;
+        sn_t[t] = v.y;
+      }
+      __syncthreads();
+    }
 #pragma unroll
     for (int tt = 0; tt < 16; ++tt) {
       const f32x4 v = acc[tt] * f;
-      *reinterpret_cast<float4*>(op + tt * 16) = make_float4(v[0], v[1], v[2], v[3]);
+      float4 o = make_float4(v[0], v[1], v[2], v[3]);
+      const int d0 = 256 * dh + 16 * tt + 4 * g;
+      if (turn && d0 + 4 > a.rope.off && d0 < a.rope.off + a.rope.dims) {
+        if (d0 >= a.rope.off) {
+          const int i = (d0 - a.rope.off) >> 1;
+          rope_turn(o.x, o.y, cs_t[i], sn_t[i]);
+        }
+        if (d0 + 2 < a.rope.off + a.rope.dims) {
+          const int i = (d0 + 2 - a.rope.off) >> 1;
+          rope_turn(o.z, o.w, cs_t[i], sn_t[i]);
+        }
+      }
+      *reinterpret_cast<float4*>(op + tt * 16) = o;
     }
     if (a.lse && g == 0 && dh == 0)
       a.lse[(int64_t)b * kHeads + head] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -__builtin_inff();
@@ -356,9 +385,11 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
 __global__ __launch_bounds__(128) void attend_combine(int32_t n_split, const float* __restrict__ part_o,
                                                      const float* __restrict__ part_ml,
                                                      const float* __restrict__ sink, float* __restrict__ out,
-                                                     float* __restrict__ lse) {
+                                                     float* __restrict__ lse, RopeOut rope) {
   const int b = blockIdx.x / kHeads, h = blockIdx.x % kHeads;
   const int t = threadIdx.x;
+  Rope4 rq{1.f, 0.f, 1.f, 0.f, false, false};
+  if (rope.table != nullptr) rq = rope4_at(4 * t, rope.table + (int64_t)b * kRopePairs, rope);
   const int64_t slot0 = (int64_t)b * n_split * kHeads + h;
   float ms[kMaxSplit], ls[kMaxSplit];
   float4 v[kMaxSplit];
@@ -396,7 +427,7 @@ __global__ __launch_bounds__(128) void attend_combine(int32_t n_split, const flo
   }
   const float f = (L > 0.f) ? 1.f / L : 0.f;
   *reinterpret_cast<float4*>(out + ((int64_t)b * kHeads + h) * kDim + t * 4) =
-      make_float4(o.x * f, o.y * f, o.z * f, o.w * f);
+      rope4_apply(make_float4(o.x * f, o.y * f, o.z * f, o.w * f), rq);
   if (lse && t == 0) lse[(int64_t)b * kHeads + h] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -__builtin_inff();
 }
 
@@ -417,7 +448,7 @@ size_t attend_partial_floats(int32_t B, int n_split) {
 hipError_t launch_attend(const csa2_dims& d, int32_t B, const csa2_batch& bt, const void* q,
                          const void* win_kv, const uint8_t* win_scale, const void* comp_kv,
                          const uint8_t* comp_scale, const int32_t* topk_idx, const float* sink,
-                         float* out, float* lse, int n_split, float* partial, hipStream_t s) {
+                         float* out, float* lse, int n_split, float* partial, const RopeOut& rope, hipStream_t s) {
   if (n_split > kMaxSplit) return hipErrorInvalidValue;
   if (B == 0) return hipSuccess;
   if (n_split < 1) n_split = 1;
@@ -443,20 +474,26 @@ hipError_t launch_attend(const csa2_dims& d, int32_t B, const csa2_batch& bt, co
   a.W = d.window;
   a.n_split = n_split;
   a.scale_log2 = d.softmax_scale * kLog2e;
+  a.rope = rope;
   if (d.kv_dtype == CSA2_KV_BF16) return hipErrorInvalidValue;  // the DMA-ring kernel's
-  if (d.kv_dtype == CSA2_KV_FP8_E4M3_UE8M0_32)
-    hipLaunchKernelGGL((attend_kernel<CSA2_KV_FP8_E4M3_UE8M0_32>), dim3(B * n_split), dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((attend_kernel<CSA2_KV_FP4_E2M1_E4M3_16>), dim3(B * n_split), dim3(kThreads), 0, s, a);
+  const dim3 grid((unsigned)(B * n_split));
+  const bool turn = rope.table != nullptr;
+  if (d.kv_dtype == CSA2_KV_FP8_E4M3_UE8M0_32) {
+    if (turn) hipLaunchKernelGGL((attend_kernel<CSA2_KV_FP8_E4M3_UE8M0_32, true>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((attend_kernel<CSA2_KV_FP8_E4M3_UE8M0_32, false>), grid, dim3(kThreads), 0, s, a);
+  } else {
+    if (turn) hipLaunchKernelGGL((attend_kernel<CSA2_KV_FP4_E2M1_E4M3_16, true>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((attend_kernel<CSA2_KV_FP4_E2M1_E4M3_16, false>), grid, dim3(kThreads), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_split == 1) return e;
-  return launch_attend_combine(B, n_split, a.part_o, a.part_ml, sink, out, lse, s);
+  return launch_attend_combine(B, n_split, a.part_o, a.part_ml, sink, out, lse, rope, s);
 }
 
 hipError_t launch_attend_combine(int32_t B, int n_split, const float* part_o, const float* part_ml, const float* sink,
-                                 float* out, float* lse, hipStream_t s) {
+                                 float* out, float* lse, const RopeOut& rope, hipStream_t s) {
   if (n_split < 1 || n_split > kMaxSplit) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attend_combine, dim3(B * kHeads), dim3(128), 0, s, n_split, part_o, part_ml, sink, out, lse);
+  hipLaunchKernelGGL(attend_combine, dim3(B * kHeads), dim3(128), 0, s, n_split, part_o, part_ml, sink, out, lse, rope);
   return hipGetLastError();
 }
 

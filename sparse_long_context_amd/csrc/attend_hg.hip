@@ -75,6 +75,7 @@ struct HgArgs {
   int32_t K;
   int32_t W;
   float scale_log2;  // softmax_scale * log2(e)
+  RopeOut rope;      // de-rotation of the outputs
 };
 
 // 16-byte unit u of LDS row r sits at unit u ^ f(r), f swapping the two 2-bit
@@ -112,7 +113,8 @@ struct Rows<CSA2_KV_FP4_E2M1_E4M3_16> {
   uint32_t sw[2][4]; // [tile][a]: scale bytes 8a + 4(g/2) .. +3 (this lane's two are 8a + 2g, +1)
 };
 
-template <int KV>
+// ROPE: outputs leave de-rotated (its own instantiation)
+template <int KV, bool ROPE>
 __global__ __launch_bounds__(kThr) void attend_hg_kernel(HgArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kWv * kRegionB];
   __shared__ __attribute__((aligned(16))) uint8_t q_s[kGroupHeads * kRowB];  // this group's q, swizzled rows
@@ -361,6 +363,10 @@ __global__ __launch_bounds__(kThr) void attend_hg_kernel(HgArgs a) {
   }
   __syncthreads();
   const float* all = reinterpret_cast<const float*>(smem);
+  // a thread writes the same four dims of each of its heads: their turns once
+  static_assert(kThr % (kDim / 4) == 0, "a thread keeps its dims over the merge");
+  Rope4 rq{1.f, 0.f, 1.f, 0.f, false, false};
+  if constexpr (ROPE) rq = rope4_at(4 * (t & (kDim / 4 - 1)), a.rope.table + (int64_t)b * kRopePairs, a.rope);
 #pragma unroll
   for (int j = 0; j < (kGroupHeads * kDim / 4) / kThr; ++j) {
     const int id = t + kThr * j;
@@ -388,7 +394,7 @@ __global__ __launch_bounds__(kThr) void attend_hg_kernel(HgArgs a) {
     }
     const float inv = (L > 0.f) ? 1.f / L : 0.f;
     *reinterpret_cast<float4*>(a.out + ((int64_t)b * kHeads + hg * kGroupHeads + h) * kDim + 4 * d4) =
-        make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+        rope4_apply(make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv), rq);
     if (a.lse && d4 == 0)
       a.lse[(int64_t)b * kHeads + hg * kGroupHeads + h] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -__builtin_inff();
   }
@@ -399,7 +405,7 @@ __global__ __launch_bounds__(kThr) void attend_hg_kernel(HgArgs a) {
 hipError_t launch_attend_hg(const csa2_dims& d, int32_t B, const csa2_batch& bt, const void* q,
                             const void* win_kv, const uint8_t* win_scale, const void* comp_kv,
                             const uint8_t* comp_scale, const int32_t* topk_idx, const float* sink, float* out,
-                            float* lse, hipStream_t s) {
+                            float* lse, const RopeOut& rope, hipStream_t s) {
   if (d.kv_dtype == CSA2_KV_BF16) return hipErrorInvalidValue;  // bf16 rows take the all-heads kernel
   if (B == 0) return hipSuccess;
   HgArgs a;
@@ -421,12 +427,17 @@ hipError_t launch_attend_hg(const csa2_dims& d, int32_t B, const csa2_batch& bt,
   a.K = d.index_topk;
   a.W = d.window;
   a.scale_log2 = d.softmax_scale * kLog2e;
+  a.rope = rope;
   // 32 workgroups per 8 queries: slot i -> query 8 (i / 32) + i % 8, head group (i / 8) % 4
   const dim3 grid((unsigned)(32 * ((B + 7) / 8)));
-  if (d.kv_dtype == CSA2_KV_FP8_E4M3_UE8M0_32)
-    hipLaunchKernelGGL((attend_hg_kernel<CSA2_KV_FP8_E4M3_UE8M0_32>), grid, dim3(kThr), 0, s, a);
-  else
-    hipLaunchKernelGGL((attend_hg_kernel<CSA2_KV_FP4_E2M1_E4M3_16>), grid, dim3(kThr), 0, s, a);
+  const bool turn = rope.table != nullptr;
+  if (d.kv_dtype == CSA2_KV_FP8_E4M3_UE8M0_32) {
+    if (turn) hipLaunchKernelGGL((attend_hg_kernel<CSA2_KV_FP8_E4M3_UE8M0_32, true>), grid, dim3(kThr), 0, s, a);
+    else hipLaunchKernelGGL((attend_hg_kernel<CSA2_KV_FP8_E4M3_UE8M0_32, false>), grid, dim3(kThr), 0, s, a);
+  } else {
+    if (turn) hipLaunchKernelGGL((attend_hg_kernel<CSA2_KV_FP4_E2M1_E4M3_16, true>), grid, dim3(kThr), 0, s, a);
+    else hipLaunchKernelGGL((attend_hg_kernel<CSA2_KV_FP4_E2M1_E4M3_16, false>), grid, dim3(kThr), 0, s, a);
+  }
   return hipGetLastError();
 }
 

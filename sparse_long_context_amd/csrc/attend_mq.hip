@@ -83,6 +83,7 @@ struct MqArgs {
   int32_t K;
   int32_t W;
   float scale_log2;  // softmax_scale * log2(e)
+  RopeOut rope;      // de-rotation of unsplit outputs (splits: the merge's)
 };
 
 // 16-byte unit u of slot row r sits at unit u ^ f(r), with f(r) =
@@ -120,6 +121,9 @@ __device__ __forceinline__ void dma_row16(const void* src, uint32_t lds) {
 // at their maxima): vmcnt in bits 3:0 and 15:14.
 #define CSA2_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x0F70)
 
+// ROPE: unsplit outputs leave de-rotated (a separate instantiation, so the
+// plain kernel carries none of its code or registers)
+template <bool ROPE>
 __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[kSlots * kSlotB];
   __shared__ __attribute__((aligned(16))) uint8_t pbuf[2][kPBufB];  // P of chunk c in pbuf[c % 2]
@@ -128,6 +132,7 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
   __shared__ float fin_s[kHeads];       // output factor of each head
   __shared__ int64_t ent_s[kMaxEntries];  // >= 0: window row; < 0: -(pool row) - 1
   __shared__ int32_t item_e_s[2];       // entry count of the item, by item parity
+  __shared__ float rope_s[2][kMaxRopeDims / 2];  // cos, sin of the rope pairs of the output leaving next
 
   const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // wave-uniform role
   const int role = wv >= 8 ? kGatherer : ((wv & 2) == 0 ? kScorer : kValuer);
@@ -161,6 +166,7 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
   struct Pf {
     int32_t wl, md, plen;
     int64_t w0, p0;
+    float2 cs;  // (cos, sin) of the lane's rope pair (ROPE)
     int32_t idx[8];
   };
   auto prefetch = [&](int item_, int lane_) __attribute__((always_inline)) -> Pf {
@@ -171,6 +177,9 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
     p.md = a.mode[bb];
     p.plen = a.pool_len[bb];
     p.p0 = a.pool_row0[bb];
+    p.cs = make_float2(1.f, 0.f);
+    if constexpr (ROPE)
+      if (a.n_split == 1 && 2 * lane_ < a.rope.dims) p.cs = a.rope.table[(int64_t)bb * kRopePairs + lane_];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int k = 64 * r + lane_;
@@ -246,12 +255,45 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
                                   : a.out + (int64_t)b_ * kHeads * kDim) +
                    (32 * r + 8 * hq) * kDim + 4 * lane_;
     const uint8_t* st = ring + 2 * kSlotB + 8 * hq * (kDim * 4);
+    // A finished output turns its rope pairs back.  The lane's two columns of
+    // four dims lie 256 apart and the rope dims span at most 128, so at most
+    // one column (half rh) meets them; a gather wave left the pairs'
+    // cosines and sines in rope_s, and the column's two serve every row.
+    // Every lane turns and then selects (no branch between the staged loads
+    // and the stores, which would serialize them).
+    auto rows = [&](auto turn_c) __attribute__((always_inline)) {
+      constexpr bool turn = decltype(turn_c)::value;
+      bool e0 = false, e1 = false, o0 = false, o1 = false;  // pair 0 / 1 turns in the even / odd half
+      float c0 = 1.f, s0 = 0.f, c1 = 1.f, s1 = 0.f;
+      if constexpr (turn) {
+        const int lo = a.rope.off, hi = a.rope.off + a.rope.dims;
+        const int rh = (4 * lane_ + 4 > lo && 4 * lane_ < hi) ? 0 : (4 * lane_ + 260 > lo && 4 * lane_ + 256 < hi) ? 1 : -1;
+        const int d0 = 4 * lane_ + 256 * (rh > 0 ? 1 : 0);
+        const bool t0 = rh >= 0 && d0 >= lo, t1 = rh >= 0 && d0 + 2 < hi;
+        e0 = t0 && rh == 0, e1 = t1 && rh == 0, o0 = t0 && rh == 1, o1 = t1 && rh == 1;
+        const int p0 = t0 ? (d0 - lo) >> 1 : 0, p1 = t1 ? (d0 + 2 - lo) >> 1 : 0;
+        c0 = rope_s[0][p0], s0 = rope_s[1][p0], c1 = rope_s[0][p1], s1 = rope_s[1][p1];
+      }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int h = 8 * hq + (i >> 1);  // staged row
-      const int u = 64 * (i & 1) + lane_;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(st + (i >> 1) * (kDim * 4) + ((u ^ (h & 15)) << 4));
-      __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(obase + (i >> 1) * kDim + 256 * (i & 1)));
+      for (int i = 0; i < 16; ++i) {
+        const int h = 8 * hq + (i >> 1);  // staged row
+        const int u = 64 * (i & 1) + lane_;
+        f32x4 v = *reinterpret_cast<const f32x4*>(st + (i >> 1) * (kDim * 4) + ((u ^ (h & 15)) << 4));
+        if constexpr (turn) {
+          const bool u0 = (i & 1) ? o0 : e0, u1 = (i & 1) ? o1 : e1;
+          float x = v[0], y = v[1], z = v[2], w = v[3];
+          rope_turn(x, y, c0, s0);
+          rope_turn(z, w, c1, s1);
+          v = f32x4{u0 ? x : v[0], u0 ? y : v[1], u1 ? z : v[2], u1 ? w : v[3]};
+        }
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(obase + (i >> 1) * kDim + 256 * (i & 1)));
+      }
+    };
+    if constexpr (ROPE) {
+      if (a.n_split == 1) rows(std::true_type{});
+      else rows(std::false_type{});
+    } else {
+      rows(std::false_type{});
     }
   };
   // three barriers in every role: stage, store, stage, store
@@ -534,6 +576,14 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
     if (nch > 1) CSA2_WAIT_VMCNT(kRowsPerValuer);
     else CSA2_WAIT_VMCNT(0);
     __syncthreads();
+    // The cosines and sines of this item's rope pairs (loaded with its
+    // list), for its output, which leaves in the next item's first rounds:
+    // the previous item's output was read from rope_s before the barrier
+    // just passed.
+    if (ROPE && a.n_split == 1 && hq == 0 && 2 * lane < a.rope.dims) {
+      rope_s[0][lane] = cur.cs.x;
+      rope_s[1][lane] = cur.cs.y;
+    }
 #pragma clang loop unroll(disable)
     for (int c = 0; c < nch; ++c) {
       if (c + 2 < nch) {
@@ -585,7 +635,8 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
 
 hipError_t launch_attend_mq(const csa2_dims& d, int32_t B, const csa2_batch& bt, const void* q,
                             const void* win_kv, const void* comp_kv, const int32_t* topk_idx, const float* sink,
-                            float* out, float* lse, int n_split, float* partial, hipStream_t s) {
+                            float* out, float* lse, int n_split, float* partial, const RopeOut& rope,
+                            hipStream_t s) {
   if (B == 0) return hipSuccess;
   if (n_split > kMaxSplit) return hipErrorInvalidValue;
   MqArgs a;
@@ -609,6 +660,7 @@ hipError_t launch_attend_mq(const csa2_dims& d, int32_t B, const csa2_batch& bt,
   a.K = d.index_topk;
   a.W = d.window;
   a.scale_log2 = d.softmax_scale * kLog2e;
+  a.rope = rope;
   // one resident workgroup per CU (its LDS rules out a second), each taking
   // items in turn
   int dev = 0, n_cu = 0;
@@ -617,10 +669,13 @@ hipError_t launch_attend_mq(const csa2_dims& d, int32_t B, const csa2_batch& bt,
   if (e0 != hipSuccess) return e0;
   const int64_t n_items = (int64_t)B * n_split;
   const int grid = (int)(n_items < n_cu ? n_items : (n_cu > 0 ? n_cu : 1));
-  hipLaunchKernelGGL(attend_mq_kernel, dim3((unsigned)grid), dim3(kThr), 0, s, a);
+  if (rope.table != nullptr)
+    hipLaunchKernelGGL(attend_mq_kernel<true>, dim3((unsigned)grid), dim3(kThr), 0, s, a);
+  else
+    hipLaunchKernelGGL(attend_mq_kernel<false>, dim3((unsigned)grid), dim3(kThr), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_split == 1) return e;
-  return launch_attend_combine(B, n_split, a.part_o, a.part_ml, sink, out, lse, s);
+  return launch_attend_combine(B, n_split, a.part_o, a.part_ml, sink, out, lse, rope, s);
 }
 
 }  // namespace csa2

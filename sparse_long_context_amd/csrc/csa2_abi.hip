@@ -76,10 +76,12 @@ int all_heads_splits(const csa2_dims& d, int32_t B) {
 // FP4 batches to the head groups (never split)
 int attend_splits(const csa2_dims& d, int32_t B) { return use_head_groups(d, B) ? 1 : all_heads_splits(d, B); }
 
-// Scores, then the split partials of the attention when its kernel uses them.
+// Scores, then the split partials of the attention when its kernel uses them,
+// then the rope table of a fused output de-rotation.
 size_t decode_ws_bytes(int32_t B, int32_t max_cand, int n_split) {
   size_t s = align_up((size_t)B * score_stride_for(max_cand) * sizeof(float));
   s += align_up(attend_partial_floats(B, n_split) * sizeof(float));
+  s += align_up(rope_table_bytes(B));
   return s;
 }
 
@@ -264,12 +266,13 @@ csa2_status csa2_topk(const csa2_dims* dims, int32_t B, const csa2_batch* batch,
 static csa2_status attend_common(const csa2_dims* dims, int32_t B, const csa2_batch* batch, const void* q,
                                  const void* win_kv, const uint8_t* win_scale, const void* comp_kv,
                                  const uint8_t* comp_scale, const int32_t* topk_idx, const float* sink,
-                                 float* out, float* lse, float* partial, int n_split, hipStream_t stream) {
+                                 float* out, float* lse, float* partial, int n_split, const RopeOut& rope,
+                                 hipStream_t stream) {
   if (dims->kv_dtype == CSA2_KV_BF16)
-    return hip_status(
-        launch_attend_mq(*dims, B, *batch, q, win_kv, comp_kv, topk_idx, sink, out, lse, n_split, partial, stream));
+    return hip_status(launch_attend_mq(*dims, B, *batch, q, win_kv, comp_kv, topk_idx, sink, out, lse, n_split,
+                                       partial, rope, stream));
   return hip_status(launch_attend(*dims, B, *batch, q, win_kv, win_scale, comp_kv, comp_scale, topk_idx, sink,
-                                  out, lse, n_split, partial, stream));
+                                  out, lse, n_split, partial, rope, stream));
 }
 
 static csa2_status check_attend_ptrs(const csa2_dims* dims, const void* q, const void* win_kv,
@@ -281,31 +284,62 @@ static csa2_status check_attend_ptrs(const csa2_dims* dims, const void* q, const
   return CSA2_OK;
 }
 
+// The fused de-rotation's descriptor (NULL or rope_dims == 0: none).  Pairs
+// must not straddle the four-dim columns the kernels store, hence the even
+// offset.
+static csa2_status rope_arg(const csa2_out_rope* r, RopeOut* out) {
+  *out = RopeOut{nullptr, nullptr, 0, 0};
+  if (!r) return CSA2_OK;
+  if (r->rope_offset < 0 || (r->rope_offset % 2) != 0 || r->rope_dims < 0 || (r->rope_dims % 2) != 0 ||
+      r->rope_dims > kMaxRopeDims || r->rope_offset + r->rope_dims > kDim)
+    return CSA2_ERR_INVALID_ARG;
+  if (r->rope_dims == 0) return CSA2_OK;
+  if (!r->inv_freq) return CSA2_ERR_INVALID_ARG;
+  *out = RopeOut{r->inv_freq, nullptr, r->rope_offset, r->rope_dims};
+  return CSA2_OK;
+}
+
+// A fused de-rotation's table: its rows go to `table` (rope_table_bytes(B) of
+// the workspace), filled for the call's queries before the attention runs.
+static csa2_status rope_prepare(RopeOut& rope, int32_t B, const int64_t* pos, void* table, hipStream_t stream) {
+  if (!rope.inv_freq) return CSA2_OK;
+  rope.table = static_cast<const float2*>(table);
+  return hip_status(launch_rope_table(B, pos, rope, stream));
+}
+
 csa2_status csa2_attend(const csa2_dims* dims, int32_t B, const csa2_batch* batch, const void* q,
                         const void* win_kv, const uint8_t* win_scale, const void* comp_kv,
                         const uint8_t* comp_scale, const int32_t* topk_idx, const float* sink, float* out,
-                        float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                        float* lse, void* workspace, size_t workspace_bytes, const csa2_out_rope* rope_desc,
+                        hipStream_t stream) {
+  RopeOut rope;
   csa2_status st = check_dims(dims);
   if (st == CSA2_OK) st = check_batch(batch, B);
   if (st == CSA2_OK && B > 0) st = check_attend_ptrs(dims, q, win_kv, win_scale, comp_kv, comp_scale, out);
+  if (st == CSA2_OK) st = rope_arg(rope_desc, &rope);
   if (st != CSA2_OK) return st;
   if (B == 0) return CSA2_OK;
   if (debug_check_enabled() &&
       (st = debug_check(*dims, B, *batch, kCheckSelections | kCheckScales, topk_idx, nullptr, nullptr, nullptr,
                         nullptr, win_scale, comp_scale, stream)) != CSA2_OK)
     return st;
+  // workspace: the split partials (when the kernel splits), then the rope
+  // table (when the output is de-rotated); none at all runs every query
+  // unsplit, without de-rotation
+  const bool no_ws = workspace == nullptr && workspace_bytes == 0;
+  if (no_ws && rope.inv_freq) return CSA2_ERR_WORKSPACE;
+  const int n_split = no_ws ? 1 : attend_splits(*dims, B);
+  const size_t part_bytes = align_up(attend_partial_floats(B, n_split) * sizeof(float));
+  const size_t need = part_bytes + (rope.inv_freq ? align_up(rope_table_bytes(B)) : 0);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return CSA2_ERR_WORKSPACE;
+  if ((st = rope_prepare(rope, B, batch->pos, static_cast<uint8_t*>(workspace) + part_bytes, stream)) != CSA2_OK)
+    return st;
   if (use_head_groups(*dims, B))
     return hip_status(launch_attend_hg(*dims, B, *batch, q, win_kv, win_scale, comp_kv, comp_scale, topk_idx, sink,
-                                       out, lse, stream));
-  if (workspace == nullptr && workspace_bytes == 0)
-    return attend_common(dims, B, batch, q, win_kv, win_scale, comp_kv, comp_scale, topk_idx, sink, out, lse, nullptr,
-                         1, stream);
-  const int n_split = attend_splits(*dims, B);
-  const size_t need = align_up(attend_partial_floats(B, n_split) * sizeof(float));
-  if (!workspace || workspace_bytes < need) return CSA2_ERR_WORKSPACE;
+                                       out, lse, rope, stream));
   float* partial = n_split > 1 ? static_cast<float*>(workspace) : nullptr;
   return attend_common(dims, B, batch, q, win_kv, win_scale, comp_kv, comp_scale, topk_idx, sink, out, lse, partial,
-                       n_split, stream);
+                       n_split, rope, stream);
 }
 
 csa2_status csa2_decode(const csa2_dims* dims, int32_t B, const csa2_batch* batch, const void* q,
@@ -313,9 +347,9 @@ csa2_status csa2_decode(const csa2_dims* dims, int32_t B, const csa2_batch* batc
                         const void* win_kv,
                         const uint8_t* win_scale, const void* comp_kv, const uint8_t* comp_scale,
                         int32_t* topk_idx, const float* sink, float* out, float* lse, void* workspace,
-                        size_t workspace_bytes, hipStream_t stream) {
+                        size_t workspace_bytes, const csa2_out_rope* rope, hipStream_t stream) {
   return csa2::decode_impl(dims, B, batch, q, idx_q, idx_w, idx_k, idx_k_scale, win_kv, win_scale, comp_kv,
-                           comp_scale, topk_idx, sink, out, lse, workspace, workspace_bytes, stream);
+                           comp_scale, topk_idx, sink, out, lse, workspace, workspace_bytes, rope, stream);
 }
 }  // extern "C"
 
@@ -325,10 +359,13 @@ csa2_status csa2::decode_impl(const csa2_dims* dims, int32_t B, const csa2_batch
                               const float* idx_q, const float* idx_w, const void* idx_k, const uint8_t* idx_k_scale,
                               const void* win_kv, const uint8_t* win_scale, const void* comp_kv,
                               const uint8_t* comp_scale, int32_t* topk_idx, const float* sink, float* out,
-                              float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                              float* lse, void* workspace, size_t workspace_bytes, const csa2_out_rope* rope_desc,
+                              hipStream_t stream) {
+  RopeOut rope;
   csa2_status st = check_dims(dims);
   if (st == CSA2_OK) st = check_batch(batch, B);
   if (st == CSA2_OK && B > 0) st = check_attend_ptrs(dims, q, win_kv, win_scale, comp_kv, comp_scale, out);
+  if (st == CSA2_OK) st = rope_arg(rope_desc, &rope);
   if (st != CSA2_OK) return st;
   if (B == 0) return CSA2_OK;
   if (!topk_idx || (batch->max_candidates > 0 && (!idx_q || !index_keys_ok(dims, idx_k, idx_k_scale))))
@@ -345,9 +382,11 @@ csa2_status csa2::decode_impl(const csa2_dims* dims, int32_t B, const csa2_batch
   const int64_t stride = (int64_t)score_stride_for(batch->max_candidates);
   float* scores = static_cast<float*>(workspace);
   const int sp = attend_splits(*dims, B);
-  float* partial = sp > 1 ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
-                                                     align_up((size_t)B * stride * sizeof(float)))
-                          : nullptr;
+  uint8_t* after_scores = static_cast<uint8_t*>(workspace) + align_up((size_t)B * stride * sizeof(float));
+  float* partial = sp > 1 ? reinterpret_cast<float*>(after_scores) : nullptr;
+  if ((st = rope_prepare(rope, B, batch->pos, after_scores + align_up(attend_partial_floats(B, sp) * sizeof(float)),
+                         stream)) != CSA2_OK)
+    return st;
 
   // scores only when some candidate can exist; the top-K always runs, so
   // every FULL / REINDEX row of topk_idx is written (all -1 when nothing is
@@ -359,9 +398,9 @@ csa2_status csa2::decode_impl(const csa2_dims* dims, int32_t B, const csa2_batch
   if ((st = hip_status(launch_topk(*dims, B, *batch, scores, stride, topk_idx, stream))) != CSA2_OK) return st;
   if (hg)
     return hip_status(launch_attend_hg(*dims, B, *batch, q, win_kv, win_scale, comp_kv, comp_scale, topk_idx, sink,
-                                       out, lse, stream));
+                                       out, lse, rope, stream));
   return attend_common(dims, B, batch, q, win_kv, win_scale, comp_kv, comp_scale, topk_idx, sink, out, lse, partial, sp,
-                       stream);
+                       rope, stream);
 }
 
 extern "C" {
@@ -402,8 +441,11 @@ csa2_status csa2_prefill(const csa2_dims* dims, const csa2_prefill_desc* desc, c
                          const float* idx_w, const void* idx_k, const uint8_t* idx_k_scale, const void* win_kv,
                          const uint8_t* win_scale,
                          const void* comp_kv, const uint8_t* comp_scale, int32_t* topk_idx, const float* sink,
-                         float* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                         float* out, float* lse, void* workspace, size_t workspace_bytes,
+                         const csa2_out_rope* rope_desc, hipStream_t stream) {
+  RopeOut rope;
   csa2_status st = check_prefill(dims, desc);
+  if (st == CSA2_OK) st = rope_arg(rope_desc, &rope);
   if (st != CSA2_OK) return st;
   const int32_t T = desc->n_queries;
   if (T == 0) return CSA2_OK;
@@ -423,9 +465,11 @@ csa2_status csa2_prefill(const csa2_dims* dims, const csa2_prefill_desc* desc, c
   ws += align_up((size_t)T * stride * sizeof(float));
   const int sp = all_heads_splits(*dims, T);
   float* partial = sp > 1 ? reinterpret_cast<float*>(ws) : nullptr;
+  ws += align_up(attend_partial_floats(T, sp) * sizeof(float));
 
   hipLaunchKernelGGL(prefill_meta_kernel, dim3((T + 255) / 256), dim3(256), 0, stream, *desc, dims->window, m);
   if ((st = hip_status(hipGetLastError())) != CSA2_OK) return st;
+  if ((st = rope_prepare(rope, T, m.pos, ws, stream)) != CSA2_OK) return st;
   csa2_batch bt = prefill_batch(desc, m, max_cand);
   if (debug_check_enabled() &&
       (st = debug_check(*dims, T, bt,
@@ -443,7 +487,7 @@ csa2_status csa2_prefill(const csa2_dims* dims, const csa2_prefill_desc* desc, c
     if ((st = hip_status(launch_topk(*dims, T, bt, scores, stride, topk_idx, stream))) != CSA2_OK) return st;
   }
   return attend_common(dims, T, &bt, q, win_kv, win_scale, comp_kv, comp_scale,
-                       desc->mode == CSA2_MODE_WINDOW ? nullptr : topk_idx, sink, out, lse, partial, sp, stream);
+                       desc->mode == CSA2_MODE_WINDOW ? nullptr : topk_idx, sink, out, lse, partial, sp, rope, stream);
 }
 
 static csa2_status check_pool_args(int32_t B, int32_t max_cand, int32_t bs, int32_t top_blocks) {

@@ -53,6 +53,57 @@ __device__ __forceinline__ uint4 fp4x8_e4m3_to_bf16x8(uint32_t w, uint32_t scale
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
+// Output de-rotation ("DeepSeek-V4.1-Flash on WASTE", What is new, 1. CSA2:
+// the rope dims of the attention output turn back by the query's rotation):
+// the pair (off + 2i, off + 2i + 1) of every head turns by -pos * inv_freq[i],
+// (x, y) -> (x cos a + y sin a, -x sin a + y cos a).  The angle, its cosine
+// and sine are fp64, rounded to fp32; the turn is fp32 with one fused
+// multiply-add per output, like the rest of the output arithmetic.  The fused
+// epilogues and the standalone pass share these helpers, so both give the
+// same bits.
+constexpr int kRopePairs = kMaxRopeDims / 2;  // row width of a call's rope table
+struct RopeOut {
+  const double* inv_freq;  // nullptr: no de-rotation
+  const float2* table;     // [B][kRopePairs] (cos, sin) per query, filled by launch_rope_table
+  int32_t off, dims;       // even offset and dims, off + dims <= 512
+};
+__device__ __forceinline__ void rope_angle(int64_t pos, double f, float& cs, float& sn) {
+  const double a = (double)pos * f;
+  cs = (float)cos(a);
+  sn = (float)sin(a);
+}
+__device__ __forceinline__ void rope_turn(float& x, float& y, float cs, float sn) {
+  const float u = x, v = y;
+  x = __builtin_fmaf(u, cs, v * sn);
+  y = __builtin_fmaf(-u, sn, v * cs);
+}
+// The turns of one head's four output dims d0 .. d0 + 3 (d0 a multiple of 4,
+// the offset even, so each pair lies inside): which of the two pairs are rope
+// pairs, and their cosines and sines from the query's table row.
+struct Rope4 {
+  float c0, s0, c1, s1;
+  bool t0, t1;
+};
+__device__ __forceinline__ Rope4 rope4_at(int d0, const float2* row, const RopeOut& r) {
+  Rope4 q{1.f, 0.f, 1.f, 0.f, false, false};
+  q.t0 = d0 >= r.off && d0 < r.off + r.dims;
+  q.t1 = d0 + 2 >= r.off && d0 + 2 < r.off + r.dims;
+  if (q.t0) {
+    const float2 v = row[(d0 - r.off) >> 1];
+    q.c0 = v.x, q.s0 = v.y;
+  }
+  if (q.t1) {
+    const float2 v = row[(d0 + 2 - r.off) >> 1];
+    q.c1 = v.x, q.s1 = v.y;
+  }
+  return q;
+}
+__device__ __forceinline__ float4 rope4_apply(float4 o, const Rope4& q) {
+  if (q.t0) rope_turn(o.x, o.y, q.c0, q.s0);
+  if (q.t1) rope_turn(o.z, o.w, q.c1, q.s1);
+  return o;
+}
+
 // ---- launchers (each returns the launch's hipError_t) ----------------------
 
 // Decode-shaped scores: one workgroup per (query, tile of candidates).
@@ -79,14 +130,14 @@ hipError_t launch_candidate_pool(int32_t B, const csa2_batch& bt, const float* s
 hipError_t launch_attend(const csa2_dims& d, int32_t B, const csa2_batch& bt, const void* q,
                          const void* win_kv, const uint8_t* win_scale, const void* comp_kv,
                          const uint8_t* comp_scale, const int32_t* topk_idx, const float* sink,
-                         float* out, float* lse, int n_split, float* partial, hipStream_t s);
+                         float* out, float* lse, int n_split, float* partial, const RopeOut& rope, hipStream_t s);
 size_t attend_partial_floats(int32_t B, int n_split);
 // Decode-shaped batches of fp8 / FP4 rows: four workgroups per query (16 heads
 // each), no workspace; bf16 rows are refused (they take the all-heads kernel).
 hipError_t launch_attend_hg(const csa2_dims& d, int32_t B, const csa2_batch& bt, const void* q,
                             const void* win_kv, const uint8_t* win_scale, const void* comp_kv,
                             const uint8_t* comp_scale, const int32_t* topk_idx, const float* sink, float* out,
-                            float* lse, hipStream_t s);
+                            float* lse, const RopeOut& rope, hipStream_t s);
 // a query's entries go to at most this many (query, split) work items
 constexpr int kMaxSplit = 4;
 int attend_split_for(int32_t B);
@@ -95,10 +146,11 @@ int attend_split_for(int32_t B);
 // needs `partial` (attend_partial_floats).
 hipError_t launch_attend_mq(const csa2_dims& d, int32_t B, const csa2_batch& bt, const void* q,
                             const void* win_kv, const void* comp_kv, const int32_t* topk_idx, const float* sink,
-                            float* out, float* lse, int n_split, float* partial, hipStream_t s);
+                            float* out, float* lse, int n_split, float* partial, const RopeOut& rope,
+                            hipStream_t s);
 // Log-sum-exp merge of split partials into out / lse.
 hipError_t launch_attend_combine(int32_t B, int n_split, const float* part_o, const float* part_ml, const float* sink,
-                                 float* out, float* lse, hipStream_t s);
+                                 float* out, float* lse, const RopeOut& rope, hipStream_t s);
 
 // The cache writer's quantizers (one thread per scale block).
 hipError_t launch_quantize_fp4_kv(int64_t n_rows, int32_t d, const float* src, uint8_t* codes, uint8_t* scales,
@@ -111,6 +163,10 @@ hipError_t launch_compress(int64_t n_groups, int32_t m, int32_t d, const float* 
                            float eps, float* out, hipStream_t s);
 hipError_t launch_derotate(int32_t B, const int64_t* pos, int32_t rope_off, int32_t rope_dims,
                            const double* inv_freq, float* out, hipStream_t s);
+// The (cos, sin) rows of a call's queries into r.table (rope_table_bytes(B)),
+// for the attention kernels' fused de-rotation.
+size_t rope_table_bytes(int32_t B);
+hipError_t launch_rope_table(int32_t B, const int64_t* pos, const RopeOut& r, hipStream_t s);
 
 // ---- device-side precondition check (CSA2_DEBUG_CHECK=1) ------------------
 // parts of a call the check covers
@@ -138,7 +194,7 @@ csa2_status decode_impl(const csa2_dims* dims, int32_t B, const csa2_batch* batc
                         const float* idx_w, const void* idx_k, const uint8_t* idx_k_scale, const void* win_kv,
                         const uint8_t* win_scale, const void* comp_kv, const uint8_t* comp_scale, int32_t* topk_idx,
                         const float* sink, float* out, float* lse, void* workspace, size_t workspace_bytes,
-                        hipStream_t stream);
+                        const csa2_out_rope* rope, hipStream_t stream);
 
 // Per-query descriptors of a prefill chunk, written into workspace arrays.
 hipError_t launch_prefill_meta(const csa2_prefill_desc& p, int32_t window, int64_t* pos, int32_t* mode,

@@ -30,7 +30,8 @@ extern "C" csa2_status csa2_decode_static(const csa2_dims* dims, int32_t B, cons
                                           const float* idx_q, const float* idx_w, const void* idx_k,
                                           const uint8_t* idx_k_scale, const void* win_kv, const uint8_t* win_scale,
                                           const void* comp_kv, const uint8_t* comp_scale, int32_t* topk_idx,
-                                          const float* sink, float* out, float* lse, hipStream_t stream) {
+                                          const float* sink, float* out, float* lse, const csa2_out_rope* rope,
+                                          hipStream_t stream) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return csa2::set_hip_error(e);
@@ -49,5 +50,5 @@ extern "C" csa2_status csa2_decode_static(const csa2_dims* dims, int32_t B, cons
   // a batch whose workspace would exceed the scratch is refused by the size
   // check of the shared implementation (CSA2_ERR_WORKSPACE) before any launch
   return csa2::decode_impl(dims, B, batch, q, idx_q, idx_w, idx_k, idx_k_scale, win_kv, win_scale, comp_kv,
-                           comp_scale, topk_idx, sink, out, lse, ptr, CSA2_STATIC_SCRATCH_BYTES, stream);
+                           comp_scale, topk_idx, sink, out, lse, ptr, CSA2_STATIC_SCRATCH_BYTES, rope, stream);
 }

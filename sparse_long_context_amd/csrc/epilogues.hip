@@ -72,26 +72,42 @@ __global__ __launch_bounds__(kCThreads) void compress_kernel(int32_t m, int32_t 
 __global__ __launch_bounds__(256) void derotate_kernel(const int64_t* __restrict__ pos, int32_t rope_off,
                                                        int32_t rope_dims, const double* __restrict__ inv_freq,
                                                        float* __restrict__ out) {
-  __shared__ double cs_s[kMaxRopeDims / 2], sn_s[kMaxRopeDims / 2];
+  __shared__ float cs_s[kMaxRopeDims / 2], sn_s[kMaxRopeDims / 2];
   const int b = blockIdx.x, t = threadIdx.x;
   const int np = rope_dims / 2;
-  if (t < np) {
-    const double a = (double)pos[b] * inv_freq[t];
-    cs_s[t] = cos(a);
-    sn_s[t] = sin(a);
-  }
+  if (t < np) rope_angle(pos[b], inv_freq[t], cs_s[t], sn_s[t]);
   __syncthreads();
   float* ob = out + (int64_t)b * kHeads * kDim;
   for (int x = t; x < kHeads * np; x += 256) {
     const int h = x / np, i = x % np;
     float* p = ob + (int64_t)h * kDim + rope_off + 2 * i;
-    const double u = p[0], v = p[1], cs = cs_s[i], sn = sn_s[i];
-    p[0] = (float)(u * cs + v * sn);
-    p[1] = (float)(-u * sn + v * cs);
+    rope_turn(p[0], p[1], cs_s[i], sn_s[i]);
   }
 }
 
+// one thread per (query, pair): the cosine and sine the fused epilogues turn by
+__global__ __launch_bounds__(256) void rope_table_kernel(int32_t B, const int64_t* __restrict__ pos, RopeOut r,
+                                                         float2* __restrict__ table) {
+  const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t b = x / kRopePairs;
+  const int i = (int)(x % kRopePairs);
+  if (b >= B || 2 * i >= r.dims) return;
+  float c, s;
+  rope_angle(pos[b], r.inv_freq[i], c, s);
+  table[x] = make_float2(c, s);
+}
+
 }  // namespace
+
+size_t rope_table_bytes(int32_t B) { return (size_t)(B > 0 ? B : 0) * kRopePairs * sizeof(float2); }
+
+hipError_t launch_rope_table(int32_t B, const int64_t* pos, const RopeOut& r, hipStream_t s) {
+  if (B <= 0 || r.inv_freq == nullptr || r.table == nullptr) return hipSuccess;
+  const int64_t n = (int64_t)B * kRopePairs;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, B, pos, r,
+                     const_cast<float2*>(r.table));
+  return hipGetLastError();
+}
 
 hipError_t launch_compress(int64_t n_groups, int32_t m, int32_t d, const float* c, const float* g, const float* w,
                            float eps, float* out, hipStream_t s) {

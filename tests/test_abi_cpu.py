@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     for n in declared_functions():
         assert hasattr(L, n), n
     assert set(declared_functions()) == set(csa2.EXPORTS)
-    assert csa2.csa2_abi_version() == 3
+    assert csa2.csa2_abi_version() == 4
     assert csa2.status_str(0) == "ok"
 
 
@@ -106,6 +106,31 @@ def test_bad_arguments_rejected_before_launch():
     with pytest.raises(E) as e:  # attend: workspace given but too small (40 bf16 queries split four ways)
         csa2.csa2_attend(d, 40, batch(), FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, None, FAKE, 16, stream=0)
     assert e.value.status == csa2.CSA2_ERR_WORKSPACE
+
+
+def test_fused_derotation_descriptor_is_validated():
+    # odd offset, odd or too many dims, past the head, no frequencies: refused
+    # before anything is launched
+    d = dims()
+    for off, rd, f in [(447, 64, FAKE), (448, 63, FAKE), (256, 130, FAKE), (480, 64, FAKE), (448, 64, None),
+                       (-2, 4, FAKE)]:
+        r = csa2.OutRope(off, rd, f)
+        with pytest.raises(csa2.Csa2Error) as e:
+            csa2.csa2_attend(d, 2, batch(), FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, None, None, 0,
+                             stream=0, rope=r)
+        assert e.value.status == csa2.CSA2_ERR_INVALID_ARG
+        with pytest.raises(csa2.Csa2Error) as e:
+            csa2.csa2_decode(d, 2, batch(), FAKE, FAKE, None, FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, None,
+                             FAKE, 1 << 30, stream=0, rope=r)
+        assert e.value.status == csa2.CSA2_ERR_INVALID_ARG
+        desc = csa2.PrefillDesc(1000, 10, csa2.MODE_FULL, 4, 250, 900, None, None, 0)
+        with pytest.raises(csa2.Csa2Error) as e:
+            csa2.csa2_prefill(d, desc, FAKE, FAKE, None, FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, None,
+                              FAKE, 1 << 30, stream=0, rope=r)
+        assert e.value.status == csa2.CSA2_ERR_INVALID_ARG
+    # zero rope dims turn nothing: a valid descriptor (an empty batch is a no-op)
+    csa2.csa2_attend(d, 0, batch(), None, None, None, None, None, None, None, None, None, None, 0, stream=0,
+                     rope=csa2.OutRope(448, 0, None))
 
 
 def test_prefill_descriptor_validation():
@@ -210,7 +235,7 @@ def test_precondition_status_and_word():
         d, b = dims(), batch()
         assert L.csa2_topk(C.byref(d), 2, C.byref(b), None, 16, None, None) == csa2.CSA2_ERR_INVALID_ARG
         assert L.csa2_attend(C.byref(dims(n_heads=8)), 2, C.byref(b), FAKE, None, None, None, None, FAKE, None,
-                             FAKE, None, None, 0, None) == csa2.CSA2_ERR_UNSUPPORTED
+                             FAKE, None, None, 0, None, None) == csa2.CSA2_ERR_UNSUPPORTED
         # an empty batch is a no-op: nothing to check, nothing launched
         assert L.csa2_topk(C.byref(d), 0, C.byref(b), None, 0, None, None) == csa2.CSA2_OK
         assert csa2.csa2_last_precondition() == 0

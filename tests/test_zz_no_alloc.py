@@ -74,5 +74,5 @@ def test_static_scratch_refuses_a_batch_past_its_size():
     B = 1100  # 1,100 x 16,384 fp32 scores = 72 MB > 64 MiB
     assert csa2.csa2_workspace_size(d, B, 16384) > csa2.CSA2_STATIC_SCRATCH_BYTES
     st = csa2.lib().csa2_decode_static(csa2.C.byref(d), B, csa2.C.byref(b), fake, fake, None, fake, None, fake, None,
-                                       fake, None, fake, None, fake, None, None)
+                                       fake, None, fake, None, fake, None, None, None)
     assert st == csa2.CSA2_ERR_WORKSPACE
