@@ -527,6 +527,50 @@ int csa2o_compress(int64_t n_groups, int32_t m, int32_t d, const float *c, const
 }
 
 /* ------------------------------------------------------------------------- */
+/* Compressor decode step ([RN] 3f C2 Step 1: entry j is the block of tokens   */
+/* jm .. jm + m - 1, so it exists once its last token is in; [PLLM] "The CSA2  */
+/* attention layers": the trailing partial group waits in state between      */
+/* calls, and a step at a position that does not close a group emits nothing). */
+/* One new token per sequence b at pos[b]: c_new[b], g_new[b] ([B][d]) become */
+/* row u = pos[b] mod m of its state kv_state[b] / score_state[b] ([B][m][d]). */
+/* When u == m - 1 the state holds the whole group: out[b] is the compressor  */
+/* above over those m rows and emit_idx[b] = (pos[b] + 1) / m - 1; otherwise   */
+/* out[b] is left as it was and emit_idx[b] = -1.  At m == 1 every token is   */
+/* its own group (no gate, no state).                                          */
+/* ------------------------------------------------------------------------- */
+int csa2o_compress_step(int32_t B, int32_t m, int32_t d, const int64_t *pos, const float *c_new,
+                        const float *g_new, float *kv_state, float *score_state, const float *w, double eps,
+                        float *out, int32_t *emit_idx) {
+  int32_t b;
+  if (B < 0 || m < 1 || d < 1 || eps < 0.0) return ORC_EBADARG;
+  if (B > 0 && (!pos || !c_new || !w || !out || !emit_idx || (m > 1 && (!g_new || !kv_state || !score_state))))
+    return ORC_EBADARG;
+  for (b = 0; b < B; ++b) {
+    const int64_t p = pos[b];
+    int64_t u;
+    int rc;
+    if (p < 0) return ORC_EBADARG;
+    u = p % m;
+    if (m == 1) {
+      rc = csa2o_compress(1, 1, d, c_new + (size_t)b * (size_t)d, NULL, w, eps, out + (size_t)b * (size_t)d);
+    } else {
+      float *cs = kv_state + (size_t)b * (size_t)m * (size_t)d;
+      float *gs = score_state + (size_t)b * (size_t)m * (size_t)d;
+      memcpy(cs + (size_t)u * (size_t)d, c_new + (size_t)b * (size_t)d, sizeof(float) * (size_t)d);
+      memcpy(gs + (size_t)u * (size_t)d, g_new + (size_t)b * (size_t)d, sizeof(float) * (size_t)d);
+      if (u != m - 1) {
+        emit_idx[b] = -1;
+        continue;
+      }
+      rc = csa2o_compress(1, m, d, cs, gs, w, eps, out + (size_t)b * (size_t)d);
+    }
+    if (rc != ORC_OK) return rc;
+    emit_idx[b] = (int32_t)((p + 1) / m - 1);
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------- */
 /* Output de-rotation ([WASTE] "What is new", 1. CSA2: the rope dims of the    */
 /* attention output are rotated by the conjugate of the query's rotation).     */
 /* Each head's dims rope_off + 2i, rope_off + 2i + 1 (i < rope_dims / 2) form  */

@@ -52,6 +52,8 @@ def lib():
         L.csa2o_dequant_mxfp4.restype = C.c_int
         L.csa2o_compress.argtypes = [i64, i32, i32, P, P, P, dbl, P]
         L.csa2o_compress.restype = C.c_int
+        L.csa2o_compress_step.argtypes = [i32, i32, i32, P, P, P, P, P, P, dbl, P, P]
+        L.csa2o_compress_step.restype = C.c_int
         L.csa2o_derotate.argtypes = [i32, i32, i32, i32, P, i64, P]
         L.csa2o_derotate.restype = C.c_int
         L.csa2o_candidate_pool.argtypes = [P, i64, i32, i32, P]
@@ -277,6 +279,24 @@ def compress(c, g, w, m, eps=1e-20):
     out = np.empty((n, d), np.float32)
     _check(lib().csa2o_compress(n, int(m), d, _ptr(c), _ptr(g), _ptr(w), float(eps), _ptr(out)))
     return out
+
+
+def compress_step(pos, c_new, g_new, kv_state, score_state, w, m, out, eps=1e-20):
+    """One decode step of the compressor for B sequences: pos int64 [B], c_new,
+    g_new f32 [B, d] (g_new None for m == 1); kv_state, score_state f32
+    [B, m, d] and out f32 [B, d] are updated in place.  Returns emit_idx int32
+    [B] (-1 where the step closes no group)."""
+    pos = _c(pos, np.int64)
+    c_new = _c(c_new, np.float32)
+    g_new = _c(g_new, np.float32)
+    w = _c(w, np.float32)
+    for a in (kv_state, score_state, out):
+        assert a is None or (a.dtype == np.float32 and a.flags.c_contiguous)
+    B, d = c_new.shape
+    emit = np.empty(B, np.int32)
+    _check(lib().csa2o_compress_step(B, int(m), d, _ptr(pos), _ptr(c_new), _ptr(g_new), _ptr(kv_state),
+                                     _ptr(score_state), _ptr(w), float(eps), _ptr(out), _ptr(emit)))
+    return emit
 
 
 def derotate(out_h_d, pos, inv_freq, rope_off=448, rope_dims=64):

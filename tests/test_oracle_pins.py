@@ -660,6 +660,49 @@ def test_compressor_closed_forms():
     assert np.allclose(O.compress(c, gg, w, m), O.compress(c[perm], gg[perm], w, m), rtol=1e-6, atol=1e-7)
 
 
+@pytest.mark.parametrize("m", [1, 4, 8])
+def test_compressor_decode_step_emits_each_group_once_it_is_whole(m):
+    # [RN] 3f C2 Step 1 (entry j = tokens jm .. jm + m - 1) and [PLLM] "The
+    # CSA2 attention layers" (the partial group waits in state; a step that
+    # closes no group emits nothing): three sequences, two of them starting
+    # mid-group with their prefix's partial group already in state, step
+    # together; every emission must be the batch compressor over that group,
+    # at exactly the steps whose token closes it, and nothing else is written.
+    rng = np.random.default_rng(40 + m)
+    d, T = 48, 3 * m + 5
+    starts = np.array([0, 3 * m + 1, 5 * m + m - 1], np.int64) if m > 1 else np.array([0, 7, 12], np.int64)
+    B = len(starts)
+    n_tok = int(starts.max()) + T
+    c = rng.standard_normal((B, n_tok, d)).astype(np.float32)
+    g = rng.standard_normal((B, n_tok, d)).astype(np.float32) * 2
+    w = rng.uniform(0.5, 2, d).astype(np.float32)
+    kv = np.full((B, m, d), np.nan, np.float32) if m > 1 else None
+    sc = np.full((B, m, d), np.nan, np.float32) if m > 1 else None
+    for b, s0 in enumerate(starts):  # the prefix's trailing partial group
+        for p in range(int(s0) // m * m, int(s0)):
+            kv[b, p % m], sc[b, p % m] = c[b, p], g[b, p]
+    seen = {b: [] for b in range(B)}
+    for t in range(T):
+        pos = starts + t
+        out = np.full((B, d), np.nan, np.float32)
+        emit = O.compress_step(pos, c[np.arange(B), pos], g[np.arange(B), pos] if m > 1 else None, kv, sc, w, m, out)
+        for b in range(B):
+            p = int(pos[b])
+            if (p + 1) % m == 0:
+                j = (p + 1) // m - 1
+                assert emit[b] == j
+                want = O.compress(c[b, j * m:(j + 1) * m], g[b, j * m:(j + 1) * m] if m > 1 else None, w, m)[0]
+                assert np.array_equal(out[b], want)
+                seen[b].append(j)
+            else:
+                assert emit[b] == -1 and np.isnan(out[b]).all()
+            if m > 1:  # the token sits in its slot of the state
+                assert np.array_equal(kv[b, p % m], c[b, p]) and np.array_equal(sc[b, p % m], g[b, p])
+    for b, s0 in enumerate(starts):  # every group closed inside the steps, once, in order
+        first = (int(s0) + m) // m - 1  # the first group whose last token comes at or after the start
+        assert seen[b] == list(range(first, (int(s0) + T) // m))
+
+
 def test_derotation_undoes_the_rotation():
     rng = np.random.default_rng(12)
     H, D, off, rd = 4, 512, 448, 64
