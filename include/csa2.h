@@ -339,6 +339,25 @@ csa2_status csa2_candidate_pool(int32_t B, const csa2_batch *batch, const float 
 csa2_status csa2_compress(int64_t n_groups, int32_t m, int32_t d, const float *c, const float *g,
                           const float *norm_w, float eps, float *out, hipStream_t stream);
 
+/* Compressor decode step (Reading Notes, 3f C2 Step 1: entry j is the block
+ * of tokens jm .. jm + m - 1, so it exists once its last token is in;
+ * PocketLLM page, "The CSA2 attention layers": the trailing partial group
+ * waits in state between calls, and a step that closes no group emits
+ * nothing).  One new token per sequence b at pos[b] (device int64 [B], >= 0;
+ * a negative position writes and emits nothing): its latent c_new[b] and gate
+ * logits g_new[b] (f32 [B][d], device) go to row u = pos[b] mod m of the
+ * sequence's state kv_state[b] / score_state[b] (f32 [B][m][d], device, the
+ * caller's, kept between calls; a prefill's trailing partial group is put
+ * there by the caller, token p in row p mod m).  When u == m - 1 the group is
+ * whole: out[b] (f32 [B][d]) becomes csa2_compress of its m rows (the same
+ * bits) and emit_idx[b] (int32 [B]) = (pos[b] + 1) / m - 1, the entry's index
+ * in the sequence's pool; otherwise out[b] is not written and emit_idx[b] =
+ * -1.  m == 1: every step emits RMSNorm(c_new[b]) (g_new and the states are
+ * not used and may be NULL).  1 <= d <= 1024. */
+csa2_status csa2_compress_step(int32_t B, int32_t m, int32_t d, const int64_t *pos, const float *c_new,
+                               const float *g_new, float *kv_state, float *score_state, const float *norm_w,
+                               float eps, float *out, int32_t *emit_idx, hipStream_t stream);
+
 /* Output de-rotation ("DeepSeek-V4.1-Flash on WASTE", What is new, 1. CSA2):
  * for each query b and head, the pairs of dims (rope_offset + 2i, +2i+1),
  * i < rope_dims / 2, of out [B][64][512] are rotated in place by

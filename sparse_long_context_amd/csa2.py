@@ -72,7 +72,7 @@ EXPORTS = ["csa2_abi_version", "csa2_status_str", "csa2_last_hip_error", "csa2_l
            "csa2_index_scores", "csa2_topk", "csa2_attend", "csa2_decode", "csa2_prefill_workspace_size",
            "csa2_prefill", "csa2_quantize_fp4_kv", "csa2_quantize_mxfp4", "csa2_candidate_pool_workspace_size",
            "csa2_candidate_pool", "csa2_compress", "csa2_derotate", "csa2_decode_static",
-           "csa2_prefill_index_scores"]
+           "csa2_prefill_index_scores", "csa2_compress_step"]
 CSA2_STATIC_SCRATCH_BYTES = 64 << 20
 
 
@@ -103,6 +103,7 @@ def lib():
         L.csa2_quantize_mxfp4.argtypes = [i64, i32, P, P, P, P]
         L.csa2_decode_static.argtypes = [P, i32, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
         L.csa2_prefill_index_scores.argtypes = [P, P, P, P, P, P, P, i64, P, sz, P]
+        L.csa2_compress_step.argtypes = [i32, i32, i32, P, P, P, P, P, P, C.c_float, P, P, P]
         for name in EXPORTS[4:]:
             getattr(L, name).restype = C.c_int
         _lib = L
@@ -234,6 +235,11 @@ def csa2_candidate_pool(B, batch, scores, score_stride, block_size, top_blocks, 
 def csa2_compress(n_groups, m, d, c, g, norm_w, eps, out, stream=None):
     _ok(lib().csa2_compress(n_groups, m, d, _p(c), _p(g), _p(norm_w), float(eps), _p(out), _stream(stream)),
         "csa2_compress")
+
+
+def csa2_compress_step(B, m, d, pos, c_new, g_new, kv_state, score_state, norm_w, eps, out, emit_idx, stream=None):
+    _ok(lib().csa2_compress_step(B, m, d, _p(pos), _p(c_new), _p(g_new), _p(kv_state), _p(score_state), _p(norm_w),
+                                 float(eps), _p(out), _p(emit_idx), _stream(stream)), "csa2_compress_step")
 
 
 def csa2_derotate(dims, B, pos, rope_offset, rope_dims, inv_freq, out, stream=None):

@@ -537,6 +537,18 @@ csa2_status csa2_compress(int64_t n_groups, int32_t m, int32_t d, const float* c
   return hip_status(launch_compress(n_groups, m, d, c, g, norm_w, eps, out, stream));
 }
 
+csa2_status csa2_compress_step(int32_t B, int32_t m, int32_t d, const int64_t* pos, const float* c_new,
+                               const float* g_new, float* kv_state, float* score_state, const float* norm_w, float eps,
+                               float* out, int32_t* emit_idx, hipStream_t stream) {
+  if (B < 0 || m < 1 || d < 1 || d > kMaxCompressDim || !(eps >= 0.0f) || !isfinite(eps))
+    return CSA2_ERR_INVALID_ARG;
+  if (B == 0) return CSA2_OK;
+  if (!pos || !c_new || !norm_w || !out || !emit_idx || (m > 1 && (!g_new || !kv_state || !score_state)))
+    return CSA2_ERR_INVALID_ARG;
+  return hip_status(
+      launch_compress_step(B, m, d, pos, c_new, g_new, kv_state, score_state, norm_w, eps, out, emit_idx, stream));
+}
+
 csa2_status csa2_derotate(const csa2_dims* dims, int32_t B, const int64_t* pos, int32_t rope_offset,
                           int32_t rope_dims, const double* inv_freq, float* out, hipStream_t stream) {
   csa2_status st = check_dims(dims);

@@ -161,6 +161,9 @@ hipError_t launch_quantize_mxfp4(int64_t n_rows, int32_t d, const float* src, ui
 // Compressor (one workgroup per group) and output de-rotation (one per query).
 hipError_t launch_compress(int64_t n_groups, int32_t m, int32_t d, const float* c, const float* g, const float* w,
                            float eps, float* out, hipStream_t s);
+hipError_t launch_compress_step(int32_t B, int32_t m, int32_t d, const int64_t* pos, const float* c_new,
+                                const float* g_new, float* kv_state, float* score_state, const float* w, float eps,
+                                float* out, int32_t* emit_idx, hipStream_t s);
 hipError_t launch_derotate(int32_t B, const int64_t* pos, int32_t rope_off, int32_t rope_dims,
                            const double* inv_freq, float* out, hipStream_t s);
 // The (cos, sin) rows of a call's queries into r.table (rope_table_bytes(B)),

@@ -212,6 +212,22 @@ def test_compress_and_derotate_arguments_are_validated():
         csa2.csa2_compress(4, 2, 512, FAKE, FAKE, FAKE, -1.0, FAKE, stream=0)
     assert e.value.status == csa2.CSA2_ERR_INVALID_ARG
     csa2.csa2_compress(0, 2, 512, None, None, None, 1e-6, None, stream=0)
+    # the decode step: sizes, eps, and every array it needs (states and gate
+    # logits only above ratio 1)
+    for args in ((4, 0, 512), (4, 2, 0), (4, 2, 1025), (-1, 2, 512)):
+        with pytest.raises(E) as e:
+            csa2.csa2_compress_step(*args, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1e-6, FAKE, FAKE, stream=0)
+        assert e.value.status == csa2.CSA2_ERR_INVALID_ARG, args
+    for k in range(8):
+        ptrs = [FAKE] * 8
+        ptrs[k] = None
+        with pytest.raises(E) as e:
+            csa2.csa2_compress_step(4, 2, 512, *ptrs[:6], 1e-6, *ptrs[6:], stream=0)
+        assert e.value.status == csa2.CSA2_ERR_INVALID_ARG, k
+    with pytest.raises(E) as e:
+        csa2.csa2_compress_step(4, 2, 512, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, float("nan"), FAKE, FAKE, stream=0)
+    assert e.value.status == csa2.CSA2_ERR_INVALID_ARG
+    csa2.csa2_compress_step(0, 2, 512, None, None, None, None, None, None, 1e-6, None, None, stream=0)
     d = dims()
     for args in ((2, 448, 63), (2, 449, 64), (2, 0, 130), (2, -1, 64), (-1, 448, 64)):
         with pytest.raises(E) as e:

@@ -5,8 +5,11 @@ CSA2) against the oracle.
 Compressor: fp32 on the GPU against fp64 in the oracle; per group the
 normwise error max|o - o_ref| / max|o_ref| must stay below 1e-5 (a fast exp
 with a few ulps of error, sums of at most m terms and one reciprocal square
-root, all well below that).  De-rotation: fp64 angles and rotation on both
-sides, so the outputs agree to within one fp32 rounding (2e-7 relative).
+root, all well below that).  Its decode step (the partial group waits in
+state, PocketLLM "DeepSeek-V4.1-Flash", "The CSA2 attention layers") must emit
+exactly where the oracle emits, with the batch compressor's bits for the same
+group.  De-rotation: fp64 angles on both sides, the GPU's turn in fp32 (the
+bound is derived at the test).
 """
 import sys
 
@@ -74,3 +77,56 @@ def test_derotation_matches_oracle():
             err = np.abs(got[b][:, 448 + k::2].astype(np.float64) - want[:, 448 + k::2])
             assert (err <= 2.0 ** -21 * n).all(), (b, k, float((err / np.maximum(n, 1e-30)).max()))
         assert np.array_equal(got[b][:, :448], out[b][:, :448])
+
+
+@pytest.mark.parametrize("m,d", [(1, 512), (4, 512), (8, 1024), (5, 130)])
+def test_compressor_decode_step(m, d):
+    # five sequences step together, two of them starting mid-group with the
+    # prefix's partial group already in state; each emission must equal the
+    # batch compressor over that group bit for bit (GPU) and the oracle's step
+    # within the compressor's bound; a step that closes no group leaves its
+    # output row untouched
+    say(f"compress step m={m} d={d}")
+    starts = np.array([0, m + 1, 3 * m - 1, 7, 2 * m], np.int64)
+    B, T = len(starts), 2 * m + 3
+    n_tok = int(starts.max()) + T
+    c = synth.normal_f32(53, 1, (B, n_tok, d))
+    g = synth.normal_f32(53, 2, (B, n_tok, d), scale=2.0)
+    w = synth.normal_f32(53, 3, (d,))
+    kv = np.zeros((B, m, d), np.float32)
+    sc = np.zeros((B, m, d), np.float32)
+    for b, s0 in enumerate(starts):
+        for p in range(int(s0) // m * m, int(s0)):
+            kv[b, p % m], sc[b, p % m] = c[b, p], g[b, p]
+    kv_t, sc_t = torch.from_numpy(kv.copy()).cuda(), torch.from_numpy(sc.copy()).cuda()
+    w_t = torch.from_numpy(w).cuda()
+    out_t = torch.empty((B, d), dtype=torch.float32, device="cuda")
+    emit_t = torch.empty(B, dtype=torch.int32, device="cuda")
+    for t in range(T):
+        pos = starts + t
+        cn, gn = c[np.arange(B), pos], g[np.arange(B), pos]
+        out_t.fill_(float("nan"))
+        csa2.csa2_compress_step(B, m, d, torch.from_numpy(pos).cuda(), torch.from_numpy(cn).cuda(),
+                                torch.from_numpy(gn).cuda() if m > 1 else None, kv_t if m > 1 else None,
+                                sc_t if m > 1 else None, w_t, 1e-20, out_t, emit_t)
+        out_o = np.full((B, d), np.nan, np.float32)
+        emit_o = O.compress_step(pos, cn, gn if m > 1 else None, kv if m > 1 else None, sc if m > 1 else None, w, m,
+                                 out_o)
+        torch.cuda.synchronize()
+        got, emit = out_t.cpu().numpy(), emit_t.cpu().numpy()
+        assert np.array_equal(emit, emit_o), (t, emit, emit_o)
+        for b in range(B):
+            if emit[b] < 0:
+                assert np.isnan(got[b]).all()
+                continue
+            j = int(emit[b])
+            grp_c = torch.from_numpy(np.ascontiguousarray(c[b, j * m:(j + 1) * m])).cuda()
+            grp_g = torch.from_numpy(np.ascontiguousarray(g[b, j * m:(j + 1) * m])).cuda()
+            ref = torch.empty((1, d), dtype=torch.float32, device="cuda")
+            csa2.csa2_compress(1, m, d, grp_c, grp_g if m > 1 else None, w_t, 1e-20, ref)
+            torch.cuda.synchronize()
+            assert np.array_equal(got[b].view(np.uint32), ref.cpu().numpy()[0].view(np.uint32)), (t, b)
+            err = np.abs(got[b] - out_o[b]).max() / np.abs(out_o[b]).max()
+            assert err <= 1e-5, (t, b, err)
+    if m > 1:  # the states hold the same tokens in the same slots
+        assert np.array_equal(kv_t.cpu().numpy(), kv) and np.array_equal(sc_t.cpu().numpy(), sc)
