@@ -16,7 +16,8 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "liboracle.so")
+# CSA2_ORACLE_LIB names another build of the same source (the sanitizer test's)
+LIB_PATH = os.environ.get("CSA2_ORACLE_LIB") or os.path.join(HERE, "liboracle.so")
 
 MODE_FULL, MODE_REINDEX, MODE_REUSE, MODE_WINDOW = 0, 1, 2, 3
 KV_BF16, KV_FP8, KV_FP4 = 0, 1, 2

@@ -36,7 +36,8 @@ import os
 import numpy as np
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-SYNTH_LIB = os.path.join(PKG, "libcsa2_synth.so")
+# CSA2_SYNTH_LIB names another build of the same source (the sanitizer test's)
+SYNTH_LIB = os.environ.get("CSA2_SYNTH_LIB") or os.path.join(PKG, "libcsa2_synth.so")
 
 MODE_FULL, MODE_REINDEX, MODE_REUSE, MODE_WINDOW = 0, 1, 2, 3
 KV_BF16, KV_FP8, KV_FP4 = 0, 1, 2
