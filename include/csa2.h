@@ -203,6 +203,19 @@ int32_t csa2_last_hip_error(void);
  * of concurrent calls in one process run one at a time. */
 uint32_t csa2_last_precondition(void);
 
+/* Trace.  With CSA2_TRACE=1 in the environment (read at every call),
+ * csa2_decode, csa2_decode_static and csa2_prefill print one checksum line per
+ * stage on stderr, in the format of the oracle's trace for the same results:
+ *   csa2-trace <call> scores finite=<n> sum=<s>   (fp64 sum of the finite
+ *       scores of the Full / Reindex queries, query by query in candidate
+ *       order: equal to the oracle's, digit for digit)
+ *   csa2-trace <call> topk rows=<r> chosen=<c> fnv1a=<h>   (the top-K rows
+ *       written: entries >= 0, and the 64-bit FNV-1a hash of their int32
+ *       values, little-endian, row by row)
+ *   csa2-trace <call> attend out_sum=<s> out_abs=<a> lse_sum=<l> lse_ninf=<k>
+ * Each line waits for its stage on `stream` and copies its output to the
+ * host: a debugging aid that cannot run under graph capture. */
+
 /* Workspace bytes csa2_decode needs for B queries with at most max_candidates
  * candidates each (scores, plus the partials of the attention's entry splits,
  * which it takes for bf16 batches below 64 queries and fp8 / FP4 batches of

@@ -255,18 +255,22 @@ def attend_query(q_bf16, win_rows, pool_rows, sel, kv_dtype=KV_BF16, win_scales=
     return out, lse
 
 
-def select_query(mode, pos, ratio, pool_len, idx_q, idx_k, k, idx_w=None, relu=False, cand=None):
-    """Reachability + scores + top-K for one Full/Reindex query.  Returns int32 [k]."""
+def select_query(mode, pos, ratio, pool_len, idx_q, idx_k, k, idx_w=None, relu=False, cand=None, scores=False):
+    """Reachability + scores + top-K for one Full/Reindex query.  Returns int32
+    [k], or (int32 [k], f32 scores of the scored candidates in candidate
+    order: the reachable pool rows, or the reachable listed rows) with
+    scores=True."""
     idx_q = _c(idx_q, np.float32)
     h_i, d_i = idx_q.shape
     idx_k = _c(idx_k, np.float32)
     idx_w = _c(idx_w, np.float32)
     cand = _c(cand, np.int32)
     out = np.empty(k, np.int32)
-    _check(lib().csa2o_select_query(int(mode), int(pos), int(ratio), int(pool_len), h_i, d_i,
-                                    _ptr(idx_q), _ptr(idx_w), int(bool(relu)), _ptr(idx_k), _ptr(cand),
-                                    0 if cand is None else cand.shape[0], int(k), _ptr(out), None))
-    return out
+    sc = np.empty(max(int(pool_len), 0 if cand is None else cand.shape[0], 1), np.float32) if scores else None
+    n = _check(lib().csa2o_select_query(int(mode), int(pos), int(ratio), int(pool_len), h_i, d_i,
+                                        _ptr(idx_q), _ptr(idx_w), int(bool(relu)), _ptr(idx_k), _ptr(cand),
+                                        0 if cand is None else cand.shape[0], int(k), _ptr(out), _ptr(sc)))
+    return (out, sc[:n]) if scores else out
 
 
 def compress(c, g, w, m, eps=1e-20):
@@ -356,6 +360,83 @@ def decode_batch(inp, queries=None, sink=None, scale=1.0):
         _ptr(sink), _ptr(sel), _ptr(out), _ptr(lse))
     _check(rc)
     return sel, out, lse
+
+
+# --- trace (the CSA2_TRACE=1 line format of the HIP library) -------------------
+
+def fnv1a64(data):
+    """64-bit FNV-1a of a bytes object."""
+    h = 0xcbf29ce484222325
+    for byte in data:
+        h = ((h ^ byte) * 0x100000001b3) & 0xFFFFFFFFFFFFFFFF
+    return h
+
+
+def trace_lines(call, score_rows, sel_rows, out, lse):
+    """The checksum lines of one call: score_rows, the scores of each Full /
+    Reindex query in candidate order; sel_rows [r, K] int32, the top-K rows the
+    call writes; out [n, H, D] and lse [n, H] of all its queries."""
+    vals = [np.asarray(r, np.float32) for r in score_rows]
+    vals = np.concatenate(vals) if vals else np.zeros(0, np.float32)
+    vals = vals[np.isfinite(vals)].astype(np.float64)
+    finite = len(vals)
+    total = float(np.cumsum(vals)[-1]) if finite else 0.0  # one addition after another, in order
+    sel_rows = np.ascontiguousarray(sel_rows, np.int32).reshape(-1, np.shape(sel_rows)[-1] if len(sel_rows) else 1)
+    chosen = int((sel_rows >= 0).sum())
+    h = fnv1a64(sel_rows.astype("<i4").tobytes())
+    o = np.asarray(out, np.float32).ravel().astype(np.float64)
+    lv = np.asarray(lse, np.float32).ravel()
+    fin = np.isfinite(lv)
+    return [f"csa2-trace {call} scores finite={finite} sum={total:.17g}",
+            f"csa2-trace {call} topk rows={len(sel_rows)} chosen={chosen} fnv1a={h:016x}",
+            f"csa2-trace {call} attend out_sum={o.sum():.6e} out_abs={np.abs(o).sum():.6e} "
+            f"lse_sum={lv[fin].astype(np.float64).sum():.6e} lse_ninf={int((~fin).sum())}"]
+
+
+def decode_trace(inp, sink=None, scale=1.0):
+    """The oracle's trace lines for a whole decode batch (fp32 index keys)."""
+    d = inp["dims"]
+    sel, out, lse = decode_batch(inp, sink=sink, scale=scale)
+    rows, sels = [], []
+    for b in range(inp["B"]):
+        md = int(inp["mode"][b])
+        if md not in (MODE_FULL, MODE_REINDEX):
+            continue
+        p0, pl = int(inp["pool_row0"][b]), int(inp["pool_len"][b])
+        cand = None
+        if md == MODE_REINDEX:
+            offs = inp.get("cand_off")
+            cand = np.zeros(0, np.int32) if offs is None else inp["cand_idx"][offs[b]:offs[b + 1]]
+        hi = d["index_heads"]
+        _, sc = select_query(md, int(inp["pos"][b]), int(inp["ratio"][b]), pl, inp["idx_q"][b].reshape(hi, -1),
+                             inp["idx_k"][p0:p0 + pl], d["index_topk"],
+                             idx_w=None if inp.get("idx_w") is None else inp["idx_w"][b], relu=d["index_relu"],
+                             cand=cand, scores=True)
+        rows.append(sc)
+        sels.append(sel[b])
+    return trace_lines("decode", rows, np.array(sels, np.int32).reshape(len(sels), -1), out, lse)
+
+
+def prefill_trace(pf, sink=None, scale=1.0):
+    """The oracle's trace lines for a whole prefill chunk (fp32 index keys)."""
+    d = pf["dims"]
+    sel, out, lse = prefill_chunk(pf, sink=sink, scale=scale)
+    md = int(pf["mode"])
+    rows = []
+    if md in (MODE_FULL, MODE_REINDEX):
+        hi = d["index_heads"]
+        for t in range(int(pf["T"])):
+            cand = None
+            if md == MODE_REINDEX:
+                offs = pf.get("cand_off")
+                cand = np.zeros(0, np.int32) if offs is None else pf["cand_idx"][offs[t]:offs[t + 1]]
+            _, sc = select_query(md, int(pf["pos0"]) + t, int(pf["ratio"]), int(pf["pool_len"]),
+                                 pf["idx_q"][t].reshape(hi, -1), pf["idx_k"], d["index_topk"],
+                                 idx_w=None if pf.get("idx_w") is None else pf["idx_w"][t], relu=d["index_relu"],
+                                 cand=cand, scores=True)
+            rows.append(sc)
+    sels = sel if md in (MODE_FULL, MODE_REINDEX) else sel[:0]
+    return trace_lines("prefill", rows, sels, out, lse)
 
 
 def prefill_chunk(pf, queries=None, sink=None, scale=1.0):

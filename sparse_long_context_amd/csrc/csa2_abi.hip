@@ -391,16 +391,22 @@ csa2_status csa2::decode_impl(const csa2_dims* dims, int32_t B, const csa2_batch
   // scores only when some candidate can exist; the top-K always runs, so
   // every FULL / REINDEX row of topk_idx is written (all -1 when nothing is
   // scored)
+  const bool trace = trace_enabled();
   if (batch->max_candidates > 0 &&
       (st = hip_status(launch_index_scores(*dims, B, *batch, idx_q, idx_w, idx_k, idx_k_scale, scores, stride,
                                            stream))) != CSA2_OK)
     return st;
+  if (trace) trace_scores("decode", B, *batch, scores, batch->max_candidates > 0 ? stride : 0, stream);
   if ((st = hip_status(launch_topk(*dims, B, *batch, scores, stride, topk_idx, stream))) != CSA2_OK) return st;
+  if (trace) trace_topk("decode", B, *batch, dims->index_topk, topk_idx, stream);
   if (hg)
-    return hip_status(launch_attend_hg(*dims, B, *batch, q, win_kv, win_scale, comp_kv, comp_scale, topk_idx, sink,
-                                       out, lse, rope, stream));
-  return attend_common(dims, B, batch, q, win_kv, win_scale, comp_kv, comp_scale, topk_idx, sink, out, lse, partial, sp,
-                       rope, stream);
+    st = hip_status(launch_attend_hg(*dims, B, *batch, q, win_kv, win_scale, comp_kv, comp_scale, topk_idx, sink,
+                                     out, lse, rope, stream));
+  else
+    st = attend_common(dims, B, batch, q, win_kv, win_scale, comp_kv, comp_scale, topk_idx, sink, out, lse, partial,
+                       sp, rope, stream);
+  if (st == CSA2_OK && trace) trace_attend("decode", B, out, lse, stream);
+  return st;
 }
 
 extern "C" {
@@ -479,15 +485,20 @@ csa2_status csa2_prefill(const csa2_dims* dims, const csa2_prefill_desc* desc, c
                         win_scale, comp_scale, stream)) != CSA2_OK)
     return st;
 
+  const bool trace = trace_enabled();
   if (selects) {
     if (max_cand > 0 &&
         (st = prefill_scores(dims, desc, bt, m, idx_q, idx_w, idx_k, idx_k_scale, scores, stride, stream)) != CSA2_OK)
       return st;
+    if (trace) trace_scores("prefill", T, bt, scores, max_cand > 0 ? stride : 0, stream);
     // always: with nothing scored every row becomes -1
     if ((st = hip_status(launch_topk(*dims, T, bt, scores, stride, topk_idx, stream))) != CSA2_OK) return st;
+    if (trace) trace_topk("prefill", T, bt, dims->index_topk, topk_idx, stream);
   }
-  return attend_common(dims, T, &bt, q, win_kv, win_scale, comp_kv, comp_scale,
-                       desc->mode == CSA2_MODE_WINDOW ? nullptr : topk_idx, sink, out, lse, partial, sp, rope, stream);
+  st = attend_common(dims, T, &bt, q, win_kv, win_scale, comp_kv, comp_scale,
+                     desc->mode == CSA2_MODE_WINDOW ? nullptr : topk_idx, sink, out, lse, partial, sp, rope, stream);
+  if (st == CSA2_OK && trace) trace_attend("prefill", T, out, lse, stream);
+  return st;
 }
 
 static csa2_status check_pool_args(int32_t B, int32_t max_cand, int32_t bs, int32_t top_blocks) {

@@ -189,6 +189,13 @@ uint32_t last_precondition_word();
 // be queried, e.g. with no GPU, so workspace sizes stay defined)
 int device_cu_count();
 
+// CSA2_TRACE=1: per-stage checksum lines on stderr (each waits for its stage)
+bool trace_enabled();
+void trace_scores(const char* call, int32_t B, const csa2_batch& bt, const float* scores, int64_t stride,
+                  hipStream_t s);
+void trace_topk(const char* call, int32_t B, const csa2_batch& bt, int32_t K, const int32_t* topk, hipStream_t s);
+void trace_attend(const char* call, int32_t B, const float* out, const float* lse, hipStream_t s);
+
 // records a failed HIP call for csa2_last_hip_error and returns CSA2_ERR_HIP
 csa2_status set_hip_error(hipError_t e);
 

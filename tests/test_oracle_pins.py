@@ -872,3 +872,24 @@ def test_prefill_chunk_window_example():
     # reading fewer rows changes the mean; reading more is refused (they do not exist)
     assert np.allclose(out[0, 0], rows.mean(0), rtol=0, atol=1e-6)
     assert np.allclose(lse[0], math.log(n), atol=1e-6)
+
+
+def test_trace_hash_is_fnv1a_64():
+    # the FNV-1a 64-bit reference values (offset basis 0xcbf29ce484222325,
+    # prime 0x100000001b3)
+    assert O.fnv1a64(b"") == 0xCBF29CE484222325
+    assert O.fnv1a64(b"a") == 0xAF63DC4C8601EC8C
+    assert O.fnv1a64(b"foobar") == 0x85944171F73967E8
+
+
+def test_trace_lines_format():
+    # two scoring queries (one score -inf), one top-K row pair, a small output
+    lines = O.trace_lines("decode", [np.array([1.5, -np.inf, 2.25], np.float32), np.array([0.125], np.float32)],
+                          np.array([[3, -1], [0, 7]], np.int32),
+                          np.array([[[1.0, -2.0]], [[0.5, 0.5]]], np.float32),
+                          np.array([[0.75], [-np.inf]], np.float32))
+    h = O.fnv1a64(np.array([3, -1, 0, 7], "<i4").tobytes())
+    assert lines == ["csa2-trace decode scores finite=3 sum=3.875",
+                     f"csa2-trace decode topk rows=2 chosen=3 fnv1a={h:016x}",
+                     "csa2-trace decode attend out_sum=0.000000e+00 out_abs=4.000000e+00 lse_sum=7.500000e-01 "
+                     "lse_ninf=1"]
