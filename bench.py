@@ -54,7 +54,7 @@ ATTN_SRC = os.path.join(ROOT, "sparse_long_context_amd", "csrc", "attend_mq.hip"
 TRAFFIC_KERNELS = {
     "index": ("index_scores_decode", TRAFFIC_FILE, INDEX_SRC, "decode, 64 queries x 16,384 candidates",
               "--config 1 --no-cpu-baseline --copy-probe --steps 3 --warmup 1"),
-    "attend": ("attend_mq_kernel", ATTN_TRAFFIC_FILE, ATTN_SRC, "prefill chunk, 4,096 queries x 640 entries",
+    "attend": ("attend_mq_kernel<false>", ATTN_TRAFFIC_FILE, ATTN_SRC, "prefill chunk, 4,096 queries x 640 entries",
                "--no-extras --no-cpu-baseline --copy-probe --steps 3 --warmup 1"),
 }
 COPY_PROBE_BYTES = 512 << 20
@@ -112,17 +112,28 @@ def summarize_traffic(fetch_csv, write_csv, which="index"):
             vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
         return vals
 
+    def probe_of(counter):
+        return "reduce_kernel" if counter == "FETCH_SIZE" else "FillFunctor"
+
     kname, out_path, src, workload, run_args = TRAFFIC_KERNELS[which]
     out = {}
     for path, counter in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
         v = per_kernel(path, counter)
         idx = [x for k, xs in v.items() if kname in k for x in xs]
-        # the probe's streaming kernel for this counter: the sum reads, the fill writes
-        probe = "reduce_kernel" if counter == "FETCH_SIZE" else "FillFunctor"
-        # (the cold-step flush is a 1 GiB fill: twice the probe, so it is not
-        # taken; FETCH_SIZE reports about half the bytes read on this part)
-        cpy = [x for k, xs in v.items() if probe in k for x in xs
-               if 0.3 * COPY_PROBE_BYTES < x * 1024 < 1.5 * COPY_PROBE_BYTES]
+        # the probe's streaming kernel for this counter: the sum reads, the fill
+        # writes.  A counter reports either the true bytes or half of them on
+        # this part (FETCH_SIZE: half), so the probe dispatches are those within
+        # 10% of the probe's size or of half of it, the full-size ones when both
+        # occur; the other fills (the clock ramp's 192 MiB, the cold-step flush's
+        # 1 GiB) fall in neither window.
+        near = {1.0: [], 0.5: []}
+        for k, xs in v.items():
+            if probe_of(counter) in k:
+                for x in xs:
+                    for f in near:
+                        if abs(x * 1024 - f * COPY_PROBE_BYTES) < 0.1 * f * COPY_PROBE_BYTES:
+                            near[f].append(x)
+        cpy = near[1.0] or near[0.5]
         if not idx or not cpy:
             raise SystemExit(f"{path}: no {kname} or copy dispatches with {counter}")
         scale = COPY_PROBE_BYTES / (1024.0 * (sum(cpy) / len(cpy)))
@@ -195,7 +206,8 @@ def cpu_baseline(run, per_call, what, min_seconds=10.0, single_seconds=3.0):
 def ramp_clocks(torch, ms=50.0):
     """About `ms` of plain fills, so the clocks leave their idle state before
     the warm-up steps."""
-    buf = torch.empty(1 << 26, dtype=torch.float32, device="cuda")
+    # 192 MiB: a size the traffic counters' probe windows never take
+    buf = torch.empty(48 << 20, dtype=torch.float32, device="cuda")
     t0 = time.perf_counter()
     while (time.perf_counter() - t0) * 1000.0 < ms:
         for _ in range(20):
@@ -278,21 +290,40 @@ def bench_prefill(args, torch, stream):
     T = w.T
     ramp_clocks(torch)
     value, ms_step = headline_steps(torch, w.prefill, T, args.steps, args.warmup, stream)
-    # the attention on its own (the dominant kernel): the same chunk in Reuse
-    # mode over the selections just made, so each call is the descriptor
-    # kernel and the attention
-    reuse = dict(pf, mode=synth.MODE_REUSE, sel_in=w.topk.cpu().numpy())
-    rw = csa2.PrefillWorkload(reuse)
+    # the attention on its own (the dominant kernel), one launch per call:
+    # csa2_attend over the chunk as a batch of Reuse queries, each with the
+    # window rows and the selection the step gave it (query t at p = pos0 + t
+    # reads raw rows max(win_pos0, p - W + 1) .. p, as the chunk's descriptor
+    # kernel derives them), unsplit as in the step
+    d = pf["dims"]
+    pos = int(pf["pos0"]) + np.arange(T, dtype=np.int64)
+    lo = np.maximum(int(pf["win_pos0"]), pos - d["window"] + 1)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    rb = {"pos": dev(pos), "mode": dev(np.full(T, synth.MODE_REUSE, np.int32)),
+          "ratio": dev(np.full(T, int(pf["ratio"]), np.int32)), "win_row0": dev(lo - int(pf["win_pos0"])),
+          "win_len": dev((pos - lo + 1).astype(np.int32)), "pool_row0": dev(np.zeros(T, np.int64)),
+          "pool_len": dev(np.full(T, int(pf["pool_len"]), np.int32))}
+    batch = csa2.Batch(csa2._p(rb["pos"]), csa2._p(rb["mode"]), csa2._p(rb["ratio"]), csa2._p(rb["win_row0"]),
+                       csa2._p(rb["win_len"]), csa2._p(rb["pool_row0"]), csa2._p(rb["pool_len"]), None, None, 0)
+    out = torch.empty_like(w.out)
+    lse = torch.empty_like(w.lse)
+    ws_bytes = csa2.csa2_workspace_size(w.dims, T, 0)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+
+    def attend(rope=None, ws_=None, ws_bytes_=0):
+        csa2.csa2_attend(w.dims, T, batch, w.q, w.win_kv, None, w.comp_kv, None, w.topk, None, out, lse, ws_,
+                         ws_bytes_, stream=stream, rope=rope)
+
     for _ in range(max(args.warmup, 20)):
-        rw.prefill()
-    attn_us = timed(torch, rw.prefill, max(args.steps, 20), stream)
+        attend()
+    attn_us = timed(torch, attend, max(args.steps, 20), stream)
     # the output de-rotation (64 rope dims at offset 448, theta 160,000):
-    # fused into the attention's writes, and as its own pass over the output
+    # fused into the attention's writes (its cos / sin rows need the
+    # workspace), and as its own pass over the output
     inv_t = torch.from_numpy(160000.0 ** (-np.arange(32, dtype=np.float64) / 32.0)).cuda()
     rope = csa2.out_rope(448, 64, inv_t)
-    pos_t = torch.arange(int(pf["pos0"]), int(pf["pos0"]) + T, dtype=torch.int64, device="cuda")
-    attn_rope_us = timed(torch, lambda: rw.prefill(rope=rope), max(args.steps, 20), stream)
-    derot_us = timed(torch, lambda: csa2.csa2_derotate(rw.dims, T, pos_t, 448, 64, inv_t, rw.out),
+    attn_rope_us = timed(torch, lambda: attend(rope, ws, ws_bytes), max(args.steps, 20), stream)
+    derot_us = timed(torch, lambda: csa2.csa2_derotate(w.dims, T, rb["pos"], 448, 64, inv_t, out),
                      max(args.steps, 20), stream)
     # the indexer on its own: the chunk's scores into a buffer of the step's stride
     stride = (int(pf["pool_len"]) + 63) // 64 * 64
@@ -300,14 +331,22 @@ def bench_prefill(args, torch, stream):
     for _ in range(max(args.warmup, 20)):
         w.index_scores(scores, stride)
     scores_us = timed(torch, lambda: w.index_scores(scores, stride), max(args.steps, 20), stream)
-    del scores
+    # the top-K on its own, over those scores (the same descriptors as Full queries)
+    full = csa2.Batch(csa2._p(rb["pos"]), csa2._p(dev(np.full(T, synth.MODE_FULL, np.int32))), csa2._p(rb["ratio"]),
+                      csa2._p(rb["win_row0"]), csa2._p(rb["win_len"]), csa2._p(rb["pool_row0"]),
+                      csa2._p(rb["pool_len"]), None, None, int(pf["pool_len"]))
+    sel_t = torch.empty_like(w.topk)
+    topk = lambda: csa2.csa2_topk(w.dims, T, full, scores, stride, sel_t, stream=stream)  # noqa: E731
+    for _ in range(max(args.warmup, 20)):
+        topk()
+    topk_us = timed(torch, topk, max(args.steps, 20), stream)
+    del scores, sel_t
     step_us = step_medians(torch, w.prefill, min(args.steps, 20), stream)
     if args.copy_probe:
         copy_probe(torch)
-    d = pf["dims"]
     # entries per query: its window rows (128 everywhere here: the raw rows
     # reach 127 positions before the chunk) plus its 512 selected rows
-    sel = rw.topk.cpu().numpy()
+    sel = w.topk.cpu().numpy()
     win_rows = T * d["window"]
     ent = win_rows + int((sel >= 0).sum())
     attn_flops = 4.0 * d["n_heads"] * d["head_dim"] * ent
@@ -326,11 +365,12 @@ def bench_prefill(args, torch, stream):
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                      "traffic": traffic_from_profile("attend"), "algorithmic_flops_per_launch": attn_flops,
                      "avg_launch_us": round(attn_us, 2)},
-        # select = the step less the attention; index_scores = the chunk's
-        # scores alone (with the 2-4 us descriptor kernel); the top-K is the rest
+        # each stage timed alone: the attention (csa2_attend), the chunk's
+        # scores (csa2_prefill_index_scores, with the 2-5 us descriptor
+        # kernel), the top-K over them (csa2_topk); select = the step less the
+        # attention
         "stages_us": {"attend": round(attn_us, 2), "select": round(1000.0 * ms_step - attn_us, 2),
-                      "index_scores": round(scores_us, 2),
-                      "topk": round(1000.0 * ms_step - attn_us - scores_us, 2)},
+                      "index_scores": round(scores_us, 2), "topk": round(topk_us, 2)},
         "index_scores_mfma": {"achieved": round(idx_flops / (scores_us * 1e-6) / 1e12, 1), "peak": FP32_MFMA_TFLOPS,
                               "unit": "TFLOP/s",
                               "frac": round(idx_flops / (scores_us * 1e-6) / 1e12 / FP32_MFMA_TFLOPS, 4)},
@@ -345,7 +385,7 @@ def bench_prefill(args, torch, stream):
         "step_us": step_us,
         "gpu": torch.cuda.get_device_name(0),
     }
-    del rw
+    del out, lse, ws
     cpu = None
     if not args.no_cpu_baseline:
         from oracle import oracle as O

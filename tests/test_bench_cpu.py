@@ -27,28 +27,34 @@ def test_traffic_summary_scales_by_the_copy_probe(tmp_path):
     b = _bench()
     kib = b.COPY_PROBE_BYTES / 1024.0
     # the fetch counter reads half the bytes on this part: the probe's sum shows
-    # kib / 2, a kernel that truly reads 3 x 1 GiB shows 1.5 GiB; the 1 GiB
-    # cache flush (twice the probe) must not be taken as the probe
+    # kib / 2, a kernel that truly reads 3 x 1 GiB shows 1.5 GiB; the write
+    # counter reads true bytes: the probe's fill shows kib, and neither the
+    # 1 GiB cache flush (twice the probe) nor the clock-ramp fills (192 MiB)
+    # nor a half-size fill next to the full-size probe may be taken as it;
+    # the rope instantiation of the kernel is not the one summarized
     fetch = tmp_path / "fetch.csv"
     _counters(fetch, "FETCH_SIZE", [
         ("void at::native::reduce_kernel<512, 1>", kib / 2),
-        ("csa2::attend_mq_kernel(MqArgs)", 1.5 * 1024 * 1024),
-        ("csa2::attend_mq_kernel(MqArgs)", 1.5 * 1024 * 1024),
+        ("csa2::attend_mq_kernel<false>(MqArgs)", 1.5 * 1024 * 1024),
+        ("csa2::attend_mq_kernel<false>(MqArgs)", 1.5 * 1024 * 1024),
+        ("csa2::attend_mq_kernel<true>(MqArgs)", 9.0 * 1024 * 1024),
         ("void at::native::vectorized_elementwise_kernel<FillFunctor>", 10.0),
     ])
     write = tmp_path / "write.csv"
     _counters(write, "WRITE_SIZE", [
         ("void at::native::vectorized_elementwise_kernel<FillFunctor>", kib),
+        ("void at::native::vectorized_elementwise_kernel<FillFunctor>", kib / 2),
+        ("void at::native::vectorized_elementwise_kernel<FillFunctor>", 192.0 * 1024),
         ("void at::native::vectorized_elementwise_kernel<FillFunctor>", 2 * kib),
-        ("csa2::attend_mq_kernel(MqArgs)", 512.0 * 1024),
-        ("csa2::attend_mq_kernel(MqArgs)", 512.0 * 1024),
+        ("csa2::attend_mq_kernel<false>(MqArgs)", 512.0 * 1024),
+        ("csa2::attend_mq_kernel<false>(MqArgs)", 512.0 * 1024),
     ])
     out = tmp_path / "rec.json"
     name, _, src, workload, args = b.TRAFFIC_KERNELS["attend"]
     b.TRAFFIC_KERNELS["attend"] = (name, str(out), src, workload, args)
     b.summarize_traffic(str(fetch), str(write), which="attend")
     rec = json.load(open(out))
-    assert rec["kernel"] == "attend_mq_kernel"
+    assert rec["kernel"] == "attend_mq_kernel<false>"
     assert abs(rec["fetch"]["scale"] - 2.0) < 1e-12 and rec["write"]["scale"] == 1.0
     assert rec["hbm_bytes_per_launch"] == 3 * (1 << 30) + (512 << 20)
     assert rec["kernel_source_sha256_16"] == b.source_digest(src)
