@@ -494,7 +494,9 @@ def bench_decode(torch, stream, inp, storage, steps, warmup, copy_probe_run=Fals
     attend_tflops = attn_flops / (stage_us["attend"] * 1e-6) / 1e12
     res = {
         "value": round(value, 1), "unit": "queries/s", "ms_per_step": round(ms_step, 4),
-        "dtype": "bf16", "config": decode_desc(inp, storage),
+        # the arithmetic: fp32 index scores (FP4 keys widened exactly), bf16
+        # matrix products in the attention (fp8 / FP4 rows widened exactly)
+        "dtype": "fp32+bf16", "config": decode_desc(inp, storage),
         "roofline": {"bound": "hbm", "kernel": "index_scores_decode" if storage == "native" else "index_scores_decode_mx",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": idx_bytes,
@@ -579,12 +581,13 @@ def main():
         res = bench_decode(torch, stream, inp, args.storage, args.steps, args.warmup, args.copy_probe)
         line = {"metric": METRIC, "value": res["value"], "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
                 "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True,
-                "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+                "scaling": "weak", "vs_baseline": None, "dtype": res["dtype"], "data": "synthetic",
                 "config": res["config"], "roofline": dict(res["roofline"]), "stages_us": res["stages_us"],
                 "attend_mfma": res["attend_mfma"], "index_scores_fp32": res["index_scores_fp32"],
                 "step_us": res["step_us"], "gpu": torch.cuda.get_device_name(0)}
         line["roofline"]["traffic"] = (traffic_from_profile("index")
-                                       if (args.config == 1 and args.storage == "native") else None)
+                                       if (args.config == 1 and args.storage == "native" and args.index_heads == 1)
+                                       else None)
         cpu = None
         if not args.no_cpu_baseline:
             from oracle import oracle as O
@@ -603,6 +606,9 @@ def main():
                 say(f"extra workload {name}: generating")
                 inp = synth.config(idx)
                 extras[name] = bench_decode(torch, stream, inp, storage, max(args.steps, 20), max(args.warmup, 20))
+                # the counters were taken on workload 1's indexer (fp32 keys)
+                extras[name]["roofline"]["traffic"] = (traffic_from_profile("index")
+                                                       if (idx == 1 and storage == "native") else None)
                 del inp
             except Exception as e:  # an extra never hides the headline
                 extras[name] = {"error": repr(e)}
