@@ -156,8 +156,11 @@ __device__ __forceinline__ void radix_finish(int d0, uint32_t prefix, uint32_t p
   take_eq = krem;
 }
 
-template <int kThreads, int kKpt>
-__global__ __launch_bounds__(kThreads) void topk_kernel(
+// kOneSeg: every list fits one segment and none is a Reindex list (the
+// launcher's choice), so the keys are loaded once and never re-read, and the
+// re-reading paths drop out of the kernel with their registers.
+template <int kThreads, int kKpt, bool kOneSeg>
+__global__ __launch_bounds__(kThreads, kThreads == 512 ? 4 : 1) void topk_kernel(
     int32_t K, int32_t max_cand, const int64_t* __restrict__ pos, const int32_t* __restrict__ mode,
     const int32_t* __restrict__ ratio, const int32_t* __restrict__ pool_len,
     const int64_t* __restrict__ cand_off, const int32_t* __restrict__ cand_idx,
@@ -165,6 +168,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
   constexpr int kWaves = kThreads / 64;
   constexpr int kSeg = kThreads * kKpt;  // keys per segment (one key register set)
   static_assert(kKpt % 4 == 0, "keys are loaded four at a time");
+  // A thread's per-key decisions are kept as bits of one 32-bit mask (one
+  // register) between counting and placing, rather than as kKpt condition
+  // masks held across the block-wide scan in between.
+  static_assert(kKpt <= 32, "a thread's keys fit one bit mask");
   __shared__ __attribute__((aligned(16))) uint32_t hist_s[kBins];
   __shared__ uint32_t red_s[2 * kWaves];
   __shared__ uint32_t pick_s[4];
@@ -182,7 +189,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
   int64_t n64 = (md == CSA2_MODE_FULL) ? nv : (cand_off ? cand_off[b + 1] - cand_off[b] : 0);
   if (n64 > max_cand) n64 = max_cand;
   const int n = (int)n64;
-  const int32_t* lst = (md == CSA2_MODE_REINDEX && n64 > 0) ? cand_idx + cand_off[b] : nullptr;
+  const int32_t* lst = (!kOneSeg && md == CSA2_MODE_REINDEX && n64 > 0) ? cand_idx + cand_off[b] : nullptr;
   const float* sc = scores + (int64_t)b * stride;
   int32_t* out = topk_idx + (int64_t)b * K;
   const bool sc_aligned = (reinterpret_cast<uintptr_t>(sc) & 15u) == 0;
@@ -193,7 +200,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
 
   // Thread t holds keys s*kSeg + t*kKpt + j, j < kKpt, of segment s.  Bounds
   // are tested as j < nrem with j a constant, so no per-key index stays live.
-  const int nseg = (n + kSeg - 1) / kSeg;
+  const int nseg = kOneSeg ? 1 : (n + kSeg - 1) / kSeg;
   uint32_t k[kKpt];
   auto load_seg = [&](int s) __attribute__((always_inline)) {
     const int base = s * kSeg + t * kKpt;
@@ -213,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
 #pragma unroll
       for (int j = 0; j < kKpt; ++j) k[j] = (j < nrem) ? order_key(sp[j]) : 0u;
     }
-    if (lst) {  // REINDEX rows outside the reachable range are ineligible
+    if (!kOneSeg && lst) {  // REINDEX rows outside the reachable range are ineligible
       const int32_t* lp = lst + base;
 #pragma unroll
       for (int j = 0; j < kKpt; ++j) {
@@ -227,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
   // one segment: its keys stay in registers through every pass
   if (nseg == 1) load_seg(0);
   auto seg_keys = [&](int s) __attribute__((always_inline)) {
-    if (nseg > 1) load_seg(s);
+    if (!kOneSeg && nseg > 1) load_seg(s);
   };
 
   // ---- pass 1: histogram of the top 12 key bits ----
@@ -285,9 +292,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
     // per-thread counts and one LDS atomic per wave place every key) ----
     for (int s = 0; s < nseg; ++s) {
       seg_keys(s);
-      uint32_t nb = 0;
+      uint32_t bm = 0;  // keys of the boundary bucket
 #pragma unroll
-      for (int j = 0; j < kKpt; ++j) nb += (k[j] != 0u) & ((k[j] - lo) < (1u << 20));
+      for (int j = 0; j < kKpt; ++j) bm |= (uint32_t)((k[j] != 0u) & ((k[j] - lo) < (1u << 20))) << j;
+      const uint32_t nb = (uint32_t)__popc(bm);
       const uint32_t nb_incl = wave_incl_scan(nb);
       uint32_t wbase = 0;
       if (lane == 63 && nb_incl != 0u) wbase = atomicAdd(&bcount_s, nb_incl);
@@ -296,7 +304,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
       if (nb != 0u) {
 #pragma unroll
         for (int j = 0; j < kKpt; ++j) {
-          if (k[j] != 0u && (k[j] - lo) < (1u << 20)) {
+          if ((bm >> j) & 1u) {
             if (slot < (uint32_t)kRankCap) bk_s[slot] = ((uint64_t)k[j] << 32) | (uint32_t)~(gbase + j);
             ++slot;
           }
@@ -372,7 +380,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
       radix_finish<kThreads>(1, lo, 0xFFF00000u, quota, hist_s, red_s, pick_s, t, lane, wv,
                              [&](int shift, uint32_t dm, uint32_t prefix, uint32_t pmask) __attribute__((always_inline)) {
                                for (int s = 0; s < nseg; ++s) {
-                                 load_seg(s);
+                                 if (!kOneSeg) load_seg(s);
 #pragma unroll
                                  for (int j = 0; j < kKpt; ++j)
                                    if (k[j] != 0u && (k[j] & pmask) == prefix)
@@ -382,10 +390,11 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
                              thr, take_eq);
       uint32_t carry = 0;
       for (int s = 0; s < nseg; ++s) {
-        load_seg(s);
-        uint32_t ce = 0;
+        if (!kOneSeg) load_seg(s);
+        uint32_t em = 0;  // keys equal to the K-th value
 #pragma unroll
-        for (int j = 0; j < kKpt; ++j) ce += (k[j] == thr);
+        for (int j = 0; j < kKpt; ++j) em |= (uint32_t)(k[j] == thr) << j;
+        const uint32_t ce = (uint32_t)__popc(em);
         uint32_t before, unused, tot_eq, unused2;
         block_prefix2<kWaves>(ce, 0u, red_s, lane, wv, before, unused, tot_eq, unused2);
         before += carry;
@@ -393,7 +402,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
           const uint32_t gbase = (uint32_t)(s * kSeg + t * kKpt);
 #pragma unroll
           for (int j = 0; j < kKpt; ++j) {
-            if (k[j] == thr) {
+            if ((em >> j) & 1u) {
               if (++before == take_eq) thr_s = ((uint64_t)thr << 32) | (uint32_t)~(gbase + j);
             }
           }
@@ -418,18 +427,18 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
     seg_keys(s);
     const int base = s * kSeg + t * kKpt;
     const int jl = idx_lim - base;  // key j of this thread may equal th iff j <= jl
-    auto chosen = [&](int j) __attribute__((always_inline)) -> bool { return (k[j] > th) | ((k[j] == th) & (j <= jl)); };
-    uint32_t cnt = 0;
+    uint32_t cm = 0;  // chosen keys
 #pragma unroll
-    for (int j = 0; j < kKpt; ++j) cnt += chosen(j);
+    for (int j = 0; j < kKpt; ++j) cm |= (uint32_t)((k[j] > th) | ((k[j] == th) & (j <= jl))) << j;
+    const uint32_t cnt = (uint32_t)__popc(cm);
     uint32_t before, unused, tot_sel, unused2;
     block_prefix2<kWaves>(cnt, 0u, red_s, lane, wv, before, unused, tot_sel, unused2);
     before += carry;
     if (cnt != 0u) {
-      const int32_t* lp = lst ? lst + base : nullptr;
+      const int32_t* lp = (!kOneSeg && lst) ? lst + base : nullptr;
 #pragma unroll
       for (int j = 0; j < kKpt; ++j) {
-        if (chosen(j)) {
+        if ((cm >> j) & 1u) {
           if (before < (uint32_t)K) {
             const int32_t row = lp ? lp[j] : base + j;
             if (staged) hist_s[before] = (uint32_t)row;
@@ -458,12 +467,18 @@ constexpr int32_t kManyQueries = 512;
 hipError_t launch_topk_k(int32_t K, int32_t B, const csa2_batch& bt, const float* scores, int64_t stride,
                          int32_t* topk_idx, hipStream_t s) {
   if (B == 0) return hipSuccess;
-  if (B >= kManyQueries)
-    hipLaunchKernelGGL((topk_kernel<512, 32>), dim3(B), dim3(512), 0, s, K, bt.max_candidates, bt.pos, bt.mode,
-                       bt.compress_ratio, bt.pool_len, bt.cand_off, bt.cand_idx, scores, stride, topk_idx);
-  else
-    hipLaunchKernelGGL((topk_kernel<1024, 16>), dim3(B), dim3(1024), 0, s, K, bt.max_candidates, bt.pos, bt.mode,
-                       bt.compress_ratio, bt.pool_len, bt.cand_off, bt.cand_idx, scores, stride, topk_idx);
+#define CSA2_TOPK_ARGS \
+  K, bt.max_candidates, bt.pos, bt.mode, bt.compress_ratio, bt.pool_len, bt.cand_off, bt.cand_idx, scores, stride, topk_idx
+  if (B >= kManyQueries) {
+    // lists of at most one 512 x 32 segment and no Reindex lists: the lean form
+    if (bt.max_candidates <= 512 * 32 && bt.cand_off == nullptr)
+      hipLaunchKernelGGL((topk_kernel<512, 32, true>), dim3(B), dim3(512), 0, s, CSA2_TOPK_ARGS);
+    else
+      hipLaunchKernelGGL((topk_kernel<512, 32, false>), dim3(B), dim3(512), 0, s, CSA2_TOPK_ARGS);
+  } else {
+    hipLaunchKernelGGL((topk_kernel<1024, 16, false>), dim3(B), dim3(1024), 0, s, CSA2_TOPK_ARGS);
+  }
+#undef CSA2_TOPK_ARGS
   return hipGetLastError();
 }
 
