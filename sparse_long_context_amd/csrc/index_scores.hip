@@ -64,85 +64,132 @@ __device__ __forceinline__ uint4 load_stream(const uint8_t* p) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-// With one or a few index heads: eight waves per SIMD (at most 64 VGPRs), so
-// eight workgroups per CU keep 128 KiB of key rows in flight, where the
-// register use the compiler picks by itself (80) allows six.
-template <int HP>
-__global__ __launch_bounds__(kThreads, HP <= 4 ? 8 : 1) void index_scores_decode(
-    int32_t hi, int32_t relu, int32_t max_cand, const int64_t* __restrict__ pos,
-    const int32_t* __restrict__ mode, const int32_t* __restrict__ ratio,
-    const int64_t* __restrict__ pool_row0, const int32_t* __restrict__ pool_len,
-    const int64_t* __restrict__ cand_off, const int32_t* __restrict__ cand_idx,
-    const float* __restrict__ idx_q, const float* __restrict__ idx_w, const float* __restrict__ idx_k,
-    float* __restrict__ scores, int64_t stride) {
-  __shared__ __attribute__((aligned(16))) float k_s[kRows * kIndexDim];
-  __shared__ __attribute__((aligned(16))) float q_s[HP][kIndexDim];
-  __shared__ float w_s[HP];
-  __shared__ int64_t row_s[kRows];
+struct DecodeIdxArgs {
+  int32_t hi, relu, max_cand, B;
+  const int64_t* pos;
+  const int32_t* mode;
+  const int32_t* ratio;
+  const int64_t* pool_row0;
+  const int32_t* pool_len;
+  const int64_t* cand_off;
+  const int32_t* cand_idx;
+  const float* idx_q;
+  const float* idx_w;
+  const float* idx_k;
+  float* scores;
+  int64_t stride;
+};
 
-  const int b = blockIdx.y;
-  const int t = threadIdx.x;
-  const int md = mode[b];
-  if (md != CSA2_MODE_FULL && md != CSA2_MODE_REINDEX) return;
-  const int64_t nv = n_valid_of(pos[b], ratio[b], md, pool_len[b]);
+// Candidates a query scores (0 for Reuse / Window queries), and its reachable
+// count.
+__device__ __forceinline__ int64_t decode_cands(const DecodeIdxArgs& a, int b, int& md, int64_t& nv) {
+  md = a.mode[b];
+  nv = 0;
+  if (md != CSA2_MODE_FULL && md != CSA2_MODE_REINDEX) return 0;
+  nv = n_valid_of(a.pos[b], a.ratio[b], md, a.pool_len[b]);
   // a REINDEX query without lists (cand_off NULL) has an empty list
-  int64_t n = (md == CSA2_MODE_FULL) ? nv : (cand_off ? cand_off[b + 1] - cand_off[b] : 0);
-  if (n > max_cand) n = max_cand;
-  const int64_t j0 = (int64_t)blockIdx.x * kRows;
-  if (j0 >= n) return;
+  int64_t n = (md == CSA2_MODE_FULL) ? nv : (a.cand_off ? a.cand_off[b + 1] - a.cand_off[b] : 0);
+  return n > a.max_cand ? a.max_cand : n;
+}
 
+template <int HP>
+struct DecodeTileLds {
+  float k_s[kRows * kIndexDim];
+  float q_s[HP][kIndexDim];
+  float w_s[HP];
+  int64_t row_s[kRows];
+};
+
+// Candidates j0 .. j0 + 31 of query b (the whole workgroup; two barriers): rows
+// and the query into LDS, the 16 KiB of key rows through registers into the
+// swizzled tile, then 32 lanes run one candidate's FMA chain each.
+template <int HP>
+__device__ __forceinline__ void decode_tile(const DecodeIdxArgs& a, DecodeTileLds<HP>& L, int b, int md,
+                                            int64_t nv, int64_t n, int64_t j0) {
+  const int t = threadIdx.x;
   if (t < kRows) {  // candidate rows (pool-relative), -1 when there is none
     const int64_t j = j0 + t;
     int64_t r = -1;
     if (j < n) {
-      const int64_t rr = (md == CSA2_MODE_FULL) ? j : (int64_t)cand_idx[cand_off[b] + j];
+      const int64_t rr = (md == CSA2_MODE_FULL) ? j : (int64_t)a.cand_idx[a.cand_off[b] + j];
       if (rr >= 0 && rr < nv) r = rr;
     }
-    row_s[t] = r;
+    L.row_s[t] = r;
   }
   for (int x = t; x < HP * kIndexDim; x += kThreads) {
     const int h = x / kIndexDim, i = x % kIndexDim;
-    q_s[h][i] = (h < hi) ? idx_q[((int64_t)b * hi + h) * kIndexDim + i] : 0.0f;
+    L.q_s[h][i] = (h < a.hi) ? a.idx_q[((int64_t)b * a.hi + h) * kIndexDim + i] : 0.0f;
   }
-  if (t < HP) w_s[t] = (t < hi) ? (idx_w ? idx_w[(int64_t)b * hi + t] : 1.0f) : 0.0f;
+  if (t < HP) L.w_s[t] = (t < a.hi) ? (a.idx_w ? a.idx_w[(int64_t)b * a.hi + t] : 1.0f) : 0.0f;
   __syncthreads();
 
-  const float* kbase = idx_k + pool_row0[b] * kIndexDim;
+  const float* kbase = a.idx_k + a.pool_row0[b] * kIndexDim;
   float4 v[kPieces];
 #pragma unroll
   for (int it = 0; it < kPieces; ++it) {
     const int p = it * kThreads + t, r = p / kUnits, u = p % kUnits;
-    const int64_t rr = row_s[r];
+    const int64_t rr = L.row_s[r];
     v[it] = (rr >= 0) ? load_stream(kbase + rr * kIndexDim + u * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 #pragma unroll
   for (int it = 0; it < kPieces; ++it) {
     const int p = it * kThreads + t, r = p / kUnits, u = p % kUnits;
-    *reinterpret_cast<float4*>(&k_s[r * kIndexDim + key_unit_swz(r, u) * 4]) = v[it];
+    *reinterpret_cast<float4*>(&L.k_s[r * kIndexDim + key_unit_swz(r, u) * 4]) = v[it];
   }
   __syncthreads();
-  if (t >= kRows) return;
   const int64_t j = j0 + t;
-  if (j >= n) return;
+  if (t >= kRows || j >= n) return;
   float sc = -__builtin_inff();
-  if (row_s[t] >= 0) {
+  if (L.row_s[t] >= 0) {
     float acc[HP];
 #pragma unroll
     for (int h = 0; h < HP; ++h) acc[h] = 0.0f;
 #pragma unroll
     for (int u = 0; u < kUnits; ++u) {
-      const float4 k4 = *reinterpret_cast<const float4*>(&k_s[t * kIndexDim + key_unit_swz(t, u) * 4]);
+      const float4 k4 = *reinterpret_cast<const float4*>(&L.k_s[t * kIndexDim + key_unit_swz(t, u) * 4]);
       const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = u * 4 + e;
 #pragma unroll
-        for (int h = 0; h < HP; ++h) acc[h] = __builtin_fmaf(q_s[h][i], kv[e], acc[h]);
+        for (int h = 0; h < HP; ++h) acc[h] = __builtin_fmaf(L.q_s[h][i], kv[e], acc[h]);
       }
     }
-    sc = finish_score(acc, w_s, HP, relu);
+    sc = finish_score(acc, L.w_s, HP, a.relu);
   }
-  scores[(int64_t)b * stride + j] = sc;
+  a.scores[(int64_t)b * a.stride + j] = sc;
+}
+
+// With one or a few index heads: eight waves per SIMD (at most 64 VGPRs), so
+// eight workgroups per CU keep 128 KiB of key rows in flight, where the
+// register use the compiler picks by itself (80) allows six.
+//
+// Grid (X, B): workgroup (x, b) scores tiles x, x + X, x + 2X, .. of query b.
+// X covers every tile of lists up to kGridTiles tiles, so dense batches run
+// one tile per workgroup; past that, a long list's workgroups loop, which
+// keeps the grid (and the idle workgroups of the queries with short lists or
+// none) from growing with the longest list of a ragged batch.
+constexpr int kGridTiles = 512;  // 16,384 candidates
+template <int HP, bool LOOP>  // LOOP: the grid is narrower than the longest list
+__global__ __launch_bounds__(kThreads, (HP == 1 || (HP <= 4 && !LOOP)) ? 8 : 1) void index_scores_decode(
+    DecodeIdxArgs a) {
+  __shared__ __attribute__((aligned(16))) DecodeTileLds<HP> L;
+  const int b = blockIdx.y;
+  int md;
+  int64_t nv;
+  const int64_t n = decode_cands(a, b, md, nv);
+  if constexpr (!LOOP) {
+    const int64_t j0 = (int64_t)blockIdx.x * kRows;
+    if (j0 >= n) return;  // whole workgroup, before any barrier
+    decode_tile<HP>(a, L, b, md, nv, n, j0);
+  } else {
+    const int64_t step = (int64_t)gridDim.x * kRows;
+#pragma clang loop unroll(disable)
+    for (int64_t j0 = (int64_t)blockIdx.x * kRows; j0 < n; j0 += step) {  // uniform
+      decode_tile<HP>(a, L, b, md, nv, n, j0);
+      if (j0 + step < n) __syncthreads();  // this tile's LDS is read before the next one is written
+    }
+  }
 }
 
 // ---- decode, MXFP4 keys ------------------------------------------------------
@@ -644,22 +691,27 @@ hipError_t launch_index_scores(const csa2_dims& d, int32_t B, const csa2_batch& 
     return hipGetLastError();
   }
   const float* idx_k = static_cast<const float*>(idx_k_v);
-  dim3 grid((bt.max_candidates + kRows - 1) / kRows, B);
-#define CSA2_IDX_ARGS                                                                                 \
-  hi, d.index_relu, bt.max_candidates, bt.pos, bt.mode, bt.compress_ratio, bt.pool_row0, bt.pool_len, \
-      bt.cand_off, bt.cand_idx, idx_q, idx_w, idx_k, scores, stride
-  if (hi <= 1)
-    hipLaunchKernelGGL(index_scores_decode<1>, grid, dim3(kThreads), 0, s, CSA2_IDX_ARGS);
-  else if (hi <= 4)
-    hipLaunchKernelGGL(index_scores_decode<4>, grid, dim3(kThreads), 0, s, CSA2_IDX_ARGS);
-  else if (hi <= 16)
-    hipLaunchKernelGGL(index_scores_decode<16>, grid, dim3(kThreads), 0, s, CSA2_IDX_ARGS);
-  else if (hi <= 32)
-    hipLaunchKernelGGL(index_scores_decode_h32, dim3((bt.max_candidates + kHC - 1) / kHC, B), dim3(256), 0, s,
-                       CSA2_IDX_ARGS);
-  else
-    hipLaunchKernelGGL(index_scores_decode<64>, grid, dim3(kThreads), 0, s, CSA2_IDX_ARGS);
-#undef CSA2_IDX_ARGS
+  if (hi > 16 && hi <= 32) {
+    hipLaunchKernelGGL(index_scores_decode_h32, dim3((bt.max_candidates + kHC - 1) / kHC, B), dim3(256), 0, s, hi,
+                       d.index_relu, bt.max_candidates, bt.pos, bt.mode, bt.compress_ratio, bt.pool_row0,
+                       bt.pool_len, bt.cand_off, bt.cand_idx, idx_q, idx_w, idx_k, scores, stride);
+    return hipGetLastError();
+  }
+  DecodeIdxArgs a{hi, d.index_relu, bt.max_candidates, B, bt.pos, bt.mode, bt.compress_ratio, bt.pool_row0,
+                  bt.pool_len, bt.cand_off, bt.cand_idx, idx_q, idx_w, idx_k, scores, stride};
+  const int32_t tiles = (bt.max_candidates + kRows - 1) / kRows;
+  const bool loop = tiles > kGridTiles;
+  const dim3 grid((unsigned)(loop ? kGridTiles : tiles), (unsigned)B);
+#define CSA2_IDX_LAUNCH(H)                                                                  \
+  do {                                                                                       \
+    if (loop) hipLaunchKernelGGL((index_scores_decode<H, true>), grid, dim3(kThreads), 0, s, a); \
+    else hipLaunchKernelGGL((index_scores_decode<H, false>), grid, dim3(kThreads), 0, s, a);     \
+  } while (0)
+  if (hi <= 1) CSA2_IDX_LAUNCH(1);
+  else if (hi <= 4) CSA2_IDX_LAUNCH(4);
+  else if (hi <= 16) CSA2_IDX_LAUNCH(16);
+  else CSA2_IDX_LAUNCH(64);
+#undef CSA2_IDX_LAUNCH
   return hipGetLastError();
 }
 

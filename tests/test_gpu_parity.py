@@ -49,9 +49,11 @@ def small_dims(**kw):
 # ---------------------------------------------------------------------------
 
 def test_index_scores_bit_exact_full_and_reindex():
-    ctx = [4096 + 4 * 37, 999, 64 * 1024 + 4, 3, 20000]
-    modes = [0, 1, 0, 0, 1]
-    inp = synth.decode_batch(11, ctx, modes, [4] * 5, dims=small_dims())
+    # pools of 16,385 and 50,000 rows and a 20,000-row list run past the
+    # indexer grid's 512 tiles, so their workgroups score several tiles each
+    ctx = [4096 + 4 * 37, 999, 64 * 1024 + 4, 3, 20000, 200000, 200004]
+    modes = [0, 1, 0, 0, 1, 0, 1]
+    inp = synth.decode_batch(11, ctx, modes, [4] * len(ctx), dims=small_dims())
     synth.add_reindex_lists(inp, 11, frac=0.4)
     say("index scores: B=5 ragged pools", list(inp["pool_len"]))
     w = csa2.DecodeWorkload(inp)
