@@ -464,7 +464,8 @@ def bench_decode(torch, stream, inp, storage, steps, warmup, copy_probe_run=Fals
     stages = {
         "index_scores": lambda: csa2.csa2_index_scores(w.dims, B, w.batch, w.idx_q, w.idx_w, w.idx_k, scores,
                                                        stride, idx_k_scale=w.idx_k_scale),
-        "topk": lambda: csa2.csa2_topk(w.dims, B, w.batch, scores, stride, w.topk),
+        "topk": lambda: csa2.csa2_topk(w.dims, B, w.batch, scores, stride, w.topk, workspace=w.ws,
+                                       workspace_bytes=w.ws_bytes),
         "attend": lambda: csa2.csa2_attend(w.dims, B, w.batch, w.q, w.win_kv, w.win_scale, w.comp_kv, w.comp_scale,
                                            w.topk, w.sink, w.out, w.lse, w.ws, w.ws_bytes),
     }

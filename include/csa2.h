@@ -242,9 +242,15 @@ csa2_status csa2_index_scores(const csa2_dims *dims, int32_t B, const csa2_batch
  * write the first min(K, eligible) candidates under (score descending, row
  * ascending) to topk_idx[b][*] in ascending row order, padded with -1.
  * Eligible: candidate row in [0, n_valid).  Scores must be finite or -inf; +0
- * and -0 tie.  Rows of REUSE / WINDOW queries are not written. */
+ * and -0 tie.  Rows of REUSE / WINDOW queries are not written.
+ * workspace: NULL (workspace_bytes 0), or at least
+ * csa2_workspace_size(dims, B, batch->max_candidates) bytes, with which a
+ * batch of under 512 queries whose lists exceed 16,384 candidates spreads
+ * each list over several workgroups (each keeps its segment's K best, then
+ * the K best of those are taken: the same result). */
 csa2_status csa2_topk(const csa2_dims *dims, int32_t B, const csa2_batch *batch, const float *scores,
-                      int64_t score_stride, int32_t *topk_idx, hipStream_t stream);
+                      int64_t score_stride, int32_t *topk_idx, void *workspace, size_t workspace_bytes,
+                      hipStream_t stream);
 
 /* Step 4 for every query: FULL / REINDEX / REUSE queries attend their window
  * rows plus the pool rows named in topk_idx[b] (-1 skipped; duplicates count

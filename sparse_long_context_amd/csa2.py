@@ -90,7 +90,7 @@ def lib():
         L.csa2_last_precondition.restype = C.c_uint32
         L.csa2_workspace_size.argtypes = [P, i32, i32, C.POINTER(sz)]
         L.csa2_index_scores.argtypes = [P, i32, P, P, P, P, P, P, i64, P]
-        L.csa2_topk.argtypes = [P, i32, P, P, i64, P, P]
+        L.csa2_topk.argtypes = [P, i32, P, P, i64, P, P, sz, P]
         L.csa2_attend.argtypes = [P, i32, P, P, P, P, P, P, P, P, P, P, P, sz, P, P]
         L.csa2_decode.argtypes = [P, i32, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P, P]
         L.csa2_prefill_workspace_size.argtypes = [P, P, C.POINTER(sz)]
@@ -159,9 +159,9 @@ def csa2_index_scores(dims, B, batch, idx_q, idx_w, idx_k, scores, score_stride,
                                 _p(idx_k_scale), _p(scores), score_stride, _stream(stream)), "csa2_index_scores")
 
 
-def csa2_topk(dims, B, batch, scores, score_stride, topk_idx, stream=None):
-    _ok(lib().csa2_topk(C.byref(dims), B, C.byref(batch), _p(scores), score_stride, _p(topk_idx),
-                        _stream(stream)), "csa2_topk")
+def csa2_topk(dims, B, batch, scores, score_stride, topk_idx, stream=None, workspace=None, workspace_bytes=0):
+    _ok(lib().csa2_topk(C.byref(dims), B, C.byref(batch), _p(scores), score_stride, _p(topk_idx), _p(workspace),
+                        workspace_bytes, _stream(stream)), "csa2_topk")
 
 
 def csa2_attend(dims, B, batch, q, win_kv, win_scale, comp_kv, comp_scale, topk_idx, sink, out, lse,

@@ -77,12 +77,19 @@ int all_heads_splits(const csa2_dims& d, int32_t B) {
 int attend_splits(const csa2_dims& d, int32_t B) { return use_head_groups(d, B) ? 1 : all_heads_splits(d, B); }
 
 // Scores, then the split partials of the attention when its kernel uses them,
-// then the rope table of a fused output de-rotation.
+// then the rope table of a fused output de-rotation, then the top-K's split
+// buffers (small batches with long lists).
 size_t decode_ws_bytes(int32_t B, int32_t max_cand, int n_split) {
   size_t s = align_up((size_t)B * score_stride_for(max_cand) * sizeof(float));
   s += align_up(attend_partial_floats(B, n_split) * sizeof(float));
   s += align_up(rope_table_bytes(B));
+  s += align_up(topk_split_bytes(B, max_cand));
   return s;
+}
+// where the top-K's split buffers start in that layout
+size_t decode_ws_topk_offset(int32_t B, int32_t max_cand, int n_split) {
+  return align_up((size_t)B * score_stride_for(max_cand) * sizeof(float)) +
+         align_up(attend_partial_floats(B, n_split) * sizeof(float)) + align_up(rope_table_bytes(B));
 }
 
 // Per-query prefill descriptors live at the front of the prefill workspace.
@@ -246,17 +253,21 @@ csa2_status csa2_index_scores(const csa2_dims* dims, int32_t B, const csa2_batch
 }
 
 csa2_status csa2_topk(const csa2_dims* dims, int32_t B, const csa2_batch* batch, const float* scores,
-                      int64_t score_stride, int32_t* topk_idx, hipStream_t stream) {
+                      int64_t score_stride, int32_t* topk_idx, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
   csa2_status st = check_dims(dims);
   if (st == CSA2_OK) st = check_batch(batch, B);
   if (st != CSA2_OK) return st;
   if (B == 0) return CSA2_OK;
   if (!topk_idx || (batch->max_candidates > 0 && !scores) || score_stride < batch->max_candidates)
     return CSA2_ERR_INVALID_ARG;
+  // the split buffers sit at the front of a workspace that is given
+  if ((workspace == nullptr) != (workspace_bytes == 0)) return CSA2_ERR_INVALID_ARG;
+  if (workspace && workspace_bytes < topk_split_bytes(B, batch->max_candidates)) return CSA2_ERR_WORKSPACE;
   if (debug_check_enabled() && (st = debug_check(*dims, B, *batch, kCheckLists, nullptr, nullptr, nullptr, nullptr,
                                                  nullptr, nullptr, nullptr, stream)) != CSA2_OK)
     return st;
-  return hip_status(launch_topk(*dims, B, *batch, scores, score_stride, topk_idx, stream));
+  return hip_status(launch_topk(*dims, B, *batch, scores, score_stride, topk_idx, workspace, stream));
 }
 
 // Batches past the head-group size: with bf16 KV the all-heads kernel whose
@@ -397,7 +408,9 @@ csa2_status csa2::decode_impl(const csa2_dims* dims, int32_t B, const csa2_batch
                                            stream))) != CSA2_OK)
     return st;
   if (trace) trace_scores("decode", B, *batch, scores, batch->max_candidates > 0 ? stride : 0, stream);
-  if ((st = hip_status(launch_topk(*dims, B, *batch, scores, stride, topk_idx, stream))) != CSA2_OK) return st;
+  void* split_ws = static_cast<uint8_t*>(workspace) + decode_ws_topk_offset(B, batch->max_candidates, sp);
+  if ((st = hip_status(launch_topk(*dims, B, *batch, scores, stride, topk_idx, split_ws, stream))) != CSA2_OK)
+    return st;
   if (trace) trace_topk("decode", B, *batch, dims->index_topk, topk_idx, stream);
   if (hg)
     st = hip_status(launch_attend_hg(*dims, B, *batch, q, win_kv, win_scale, comp_kv, comp_scale, topk_idx, sink,
@@ -492,7 +505,8 @@ csa2_status csa2_prefill(const csa2_dims* dims, const csa2_prefill_desc* desc, c
       return st;
     if (trace) trace_scores("prefill", T, bt, scores, max_cand > 0 ? stride : 0, stream);
     // always: with nothing scored every row becomes -1
-    if ((st = hip_status(launch_topk(*dims, T, bt, scores, stride, topk_idx, stream))) != CSA2_OK) return st;
+    void* split_ws = static_cast<uint8_t*>(workspace) + prefill_meta_bytes(T) + decode_ws_topk_offset(T, max_cand, sp);
+    if ((st = hip_status(launch_topk(*dims, T, bt, scores, stride, topk_idx, split_ws, stream))) != CSA2_OK) return st;
     if (trace) trace_topk("prefill", T, bt, dims->index_topk, topk_idx, stream);
   }
   st = attend_common(dims, T, &bt, q, win_kv, win_scale, comp_kv, comp_scale,

@@ -116,8 +116,11 @@ hipError_t launch_index_scores_prefill(const csa2_dims& d, int32_t T, const int6
                                        int32_t ratio, int32_t pool_len, const float* idx_q,
                                        const float* idx_w, const float* idx_k, float* scores,
                                        int64_t stride, hipStream_t s);
+// split_ws (topk_split_bytes, or NULL): lets a small batch with long lists
+// spread each list over several workgroups
 hipError_t launch_topk(const csa2_dims& d, int32_t B, const csa2_batch& bt, const float* scores,
-                       int64_t stride, int32_t* topk_idx, hipStream_t s);
+                       int64_t stride, int32_t* topk_idx, void* split_ws, hipStream_t s);
+size_t topk_split_bytes(int32_t B, int32_t max_cand);
 // The same selection with an explicit K (any K >= 1).
 hipError_t launch_topk_k(int32_t K, int32_t B, const csa2_batch& bt, const float* scores, int64_t stride,
                          int32_t* topk_idx, hipStream_t s);

@@ -156,15 +156,34 @@ __device__ __forceinline__ void radix_finish(int d0, uint32_t prefix, uint32_t p
   take_eq = krem;
 }
 
-// kOneSeg: every list fits one segment and none is a Reindex list (the
-// launcher's choice), so the keys are loaded once and never re-read, and the
-// re-reading paths drop out of the kernel with their registers.
-template <int kThreads, int kKpt, bool kOneSeg>
+// Forms of the kernel:
+//   kGeneral  any list, re-read in segments when it outgrows the registers;
+//   kOneSeg   every list fits one segment and none is a Reindex list (the
+//             launcher's choice): keys loaded once, the re-reading paths gone
+//             with their registers;
+//   kSegment  workgroup (b, s) takes segment s of query b's list as its list
+//             (one register segment, Reindex lists included) and writes its
+//             own top-K, rows and scores, to the split buffers, padded with
+//             -1; a second pass (kGeneral over those as Reindex lists) picks
+//             the query's top-K from them.  Exact: under the strict
+//             (score, row) order the K best of a list are among the K best of
+//             the segments holding them.
+constexpr int kGeneral = 0, kOneSeg = 1, kSegment = 2;
+struct TopkSplit {
+  int32_t nseg;        // segments per query (kSegment)
+  int32_t* rows;       // [B][nseg][K]: each segment's chosen rows, ascending, -1 padded
+  float* scores;       // [B][nseg][K]: their scores
+  int32_t* mode2;      // [B]: Reindex for a query that selects, else its own mode
+  int64_t* off2;       // [B + 1]: b * nseg * K
+};
+
+template <int kThreads, int kKpt, int kForm>
 __global__ __launch_bounds__(kThreads, kThreads == 512 ? 4 : 1) void topk_kernel(
     int32_t K, int32_t max_cand, const int64_t* __restrict__ pos, const int32_t* __restrict__ mode,
     const int32_t* __restrict__ ratio, const int32_t* __restrict__ pool_len,
     const int64_t* __restrict__ cand_off, const int32_t* __restrict__ cand_idx,
-    const float* __restrict__ scores, int64_t stride, int32_t* __restrict__ topk_idx) {
+    const float* __restrict__ scores, int64_t stride, int32_t* __restrict__ topk_idx, TopkSplit split) {
+  constexpr bool kOne = kForm != kGeneral;  // the list is one register segment
   constexpr int kWaves = kThreads / 64;
   constexpr int kSeg = kThreads * kKpt;  // keys per segment (one key register set)
   static_assert(kKpt % 4 == 0, "keys are loaded four at a time");
@@ -183,15 +202,27 @@ __global__ __launch_bounds__(kThreads, kThreads == 512 ? 4 : 1) void topk_kernel
   const int t = threadIdx.x;
   const int lane = t & 63, wv = t >> 6;
   const int md = mode[b];
+  if constexpr (kForm == kSegment) {
+    if (blockIdx.y == 0 && t == 0) {
+      split.mode2[b] = (md == CSA2_MODE_FULL || md == CSA2_MODE_REINDEX) ? CSA2_MODE_REINDEX : md;
+      split.off2[b] = (int64_t)b * split.nseg * K;
+      if (b == (int)gridDim.x - 1) split.off2[b + 1] = (int64_t)(b + 1) * split.nseg * K;
+    }
+  }
   if (md != CSA2_MODE_FULL && md != CSA2_MODE_REINDEX) return;
   const int64_t nv = n_valid_of(pos[b], ratio[b], md, pool_len[b]);
   // a REINDEX query without lists (cand_off NULL) has an empty list
   int64_t n64 = (md == CSA2_MODE_FULL) ? nv : (cand_off ? cand_off[b + 1] - cand_off[b] : 0);
   if (n64 > max_cand) n64 = max_cand;
+  // kSegment: this workgroup's part of the list, positions first .. first + n - 1
+  const int64_t first = kForm == kSegment ? (int64_t)blockIdx.y * (kThreads * kKpt) : 0;
+  if (kForm == kSegment) n64 = n64 > first ? (n64 - first < kThreads * kKpt ? n64 - first : kThreads * kKpt) : 0;
   const int n = (int)n64;
-  const int32_t* lst = (!kOneSeg && md == CSA2_MODE_REINDEX && n64 > 0) ? cand_idx + cand_off[b] : nullptr;
-  const float* sc = scores + (int64_t)b * stride;
-  int32_t* out = topk_idx + (int64_t)b * K;
+  const int32_t* lst =
+      (kForm != kOneSeg && md == CSA2_MODE_REINDEX && n64 > 0) ? cand_idx + cand_off[b] + first : nullptr;
+  const float* sc = scores + (int64_t)b * stride + first;
+  int32_t* out = kForm == kSegment ? split.rows + ((int64_t)b * split.nseg + blockIdx.y) * K
+                                   : topk_idx + (int64_t)b * K;
   const bool sc_aligned = (reinterpret_cast<uintptr_t>(sc) & 15u) == 0;
   auto pad = [&](uint32_t chosen) {
     if (chosen > (uint32_t)K) chosen = K;
@@ -200,7 +231,7 @@ __global__ __launch_bounds__(kThreads, kThreads == 512 ? 4 : 1) void topk_kernel
 
   // Thread t holds keys s*kSeg + t*kKpt + j, j < kKpt, of segment s.  Bounds
   // are tested as j < nrem with j a constant, so no per-key index stays live.
-  const int nseg = kOneSeg ? 1 : (n + kSeg - 1) / kSeg;
+  const int nseg = kOne ? 1 : (n + kSeg - 1) / kSeg;
   uint32_t k[kKpt];
   auto load_seg = [&](int s) __attribute__((always_inline)) {
     const int base = s * kSeg + t * kKpt;
@@ -220,7 +251,7 @@ __global__ __launch_bounds__(kThreads, kThreads == 512 ? 4 : 1) void topk_kernel
 #pragma unroll
       for (int j = 0; j < kKpt; ++j) k[j] = (j < nrem) ? order_key(sp[j]) : 0u;
     }
-    if (!kOneSeg && lst) {  // REINDEX rows outside the reachable range are ineligible
+    if (kForm != kOneSeg && lst) {  // REINDEX rows outside the reachable range are ineligible
       const int32_t* lp = lst + base;
 #pragma unroll
       for (int j = 0; j < kKpt; ++j) {
@@ -234,7 +265,7 @@ __global__ __launch_bounds__(kThreads, kThreads == 512 ? 4 : 1) void topk_kernel
   // one segment: its keys stay in registers through every pass
   if (nseg == 1) load_seg(0);
   auto seg_keys = [&](int s) __attribute__((always_inline)) {
-    if (!kOneSeg && nseg > 1) load_seg(s);
+    if (!kOne && nseg > 1) load_seg(s);
   };
 
   // ---- pass 1: histogram of the top 12 key bits ----
@@ -380,7 +411,7 @@ __global__ __launch_bounds__(kThreads, kThreads == 512 ? 4 : 1) void topk_kernel
       radix_finish<kThreads>(1, lo, 0xFFF00000u, quota, hist_s, red_s, pick_s, t, lane, wv,
                              [&](int shift, uint32_t dm, uint32_t prefix, uint32_t pmask) __attribute__((always_inline)) {
                                for (int s = 0; s < nseg; ++s) {
-                                 if (!kOneSeg) load_seg(s);
+                                 if (!kOne) load_seg(s);
 #pragma unroll
                                  for (int j = 0; j < kKpt; ++j)
                                    if (k[j] != 0u && (k[j] & pmask) == prefix)
@@ -390,7 +421,7 @@ __global__ __launch_bounds__(kThreads, kThreads == 512 ? 4 : 1) void topk_kernel
                              thr, take_eq);
       uint32_t carry = 0;
       for (int s = 0; s < nseg; ++s) {
-        if (!kOneSeg) load_seg(s);
+        if (!kOne) load_seg(s);
         uint32_t em = 0;  // keys equal to the K-th value
 #pragma unroll
         for (int j = 0; j < kKpt; ++j) em |= (uint32_t)(k[j] == thr) << j;
@@ -435,12 +466,13 @@ __global__ __launch_bounds__(kThreads, kThreads == 512 ? 4 : 1) void topk_kernel
     block_prefix2<kWaves>(cnt, 0u, red_s, lane, wv, before, unused, tot_sel, unused2);
     before += carry;
     if (cnt != 0u) {
-      const int32_t* lp = (!kOneSeg && lst) ? lst + base : nullptr;
+      const int32_t* lp = (kForm != kOneSeg && lst) ? lst + base : nullptr;
 #pragma unroll
       for (int j = 0; j < kKpt; ++j) {
         if ((cm >> j) & 1u) {
           if (before < (uint32_t)K) {
-            const int32_t row = lp ? lp[j] : base + j;
+            // kSegment stages the list position (its row and score are both read out below)
+            const int32_t row = kForm == kSegment ? base + j : (lp ? lp[j] : base + j);
             if (staged) hist_s[before] = (uint32_t)row;
             else out[before] = row;
           }
@@ -451,7 +483,16 @@ __global__ __launch_bounds__(kThreads, kThreads == 512 ? 4 : 1) void topk_kernel
     carry += tot_sel;
     __syncthreads();
   }
-  if (staged) {
+  if constexpr (kForm == kSegment) {  // K <= kBins here (the launcher's choice)
+    const uint32_t n_out = carry < (uint32_t)K ? carry : (uint32_t)K;
+    float* so = split.scores + ((int64_t)b * split.nseg + blockIdx.y) * K;
+    for (int x = t; x < K; x += kThreads) {
+      const bool has = (uint32_t)x < n_out;
+      const int32_t p = has ? (int32_t)hist_s[x] : 0;
+      out[x] = has ? (lst ? lst[p] : (int32_t)(first + p)) : -1;
+      so[x] = has ? sc[p] : -__builtin_inff();
+    }
+  } else if (staged) {
     const uint32_t n_out = carry < (uint32_t)K ? carry : (uint32_t)K;
     for (int x = t; x < K; x += kThreads) out[x] = (uint32_t)x < n_out ? (int32_t)hist_s[x] : -1;
   } else {
@@ -463,28 +504,81 @@ __global__ __launch_bounds__(kThreads, kThreads == 512 ? 4 : 1) void topk_kernel
 
 // Batches of at least this many queries take the 512-thread shape.
 constexpr int32_t kManyQueries = 512;
+// Smaller batches with lists past one 1,024 x 16 segment split them over
+// workgroups (kSegment) when given the buffers; the largest batches have
+// workgroups enough without.
+constexpr int32_t kSplitSeg = 1024 * 16;
+
+static void launch_forms(int32_t K, int32_t B, const csa2_batch& bt, const float* scores, int64_t stride,
+                         int32_t* topk_idx, hipStream_t s) {
+  const TopkSplit none{0, nullptr, nullptr, nullptr, nullptr};
+#define CSA2_TOPK_ARGS                                                                                    \
+  K, bt.max_candidates, bt.pos, bt.mode, bt.compress_ratio, bt.pool_len, bt.cand_off, bt.cand_idx, scores, \
+      stride, topk_idx, none
+  if (B >= kManyQueries) {
+    // lists of at most one 512 x 32 segment and no Reindex lists: the lean form
+    if (bt.max_candidates <= 512 * 32 && bt.cand_off == nullptr)
+      hipLaunchKernelGGL((topk_kernel<512, 32, kOneSeg>), dim3(B), dim3(512), 0, s, CSA2_TOPK_ARGS);
+    else
+      hipLaunchKernelGGL((topk_kernel<512, 32, kGeneral>), dim3(B), dim3(512), 0, s, CSA2_TOPK_ARGS);
+  } else {
+    hipLaunchKernelGGL((topk_kernel<1024, 16, kGeneral>), dim3(B), dim3(1024), 0, s, CSA2_TOPK_ARGS);
+  }
+#undef CSA2_TOPK_ARGS
+}
 
 hipError_t launch_topk_k(int32_t K, int32_t B, const csa2_batch& bt, const float* scores, int64_t stride,
                          int32_t* topk_idx, hipStream_t s) {
   if (B == 0) return hipSuccess;
-#define CSA2_TOPK_ARGS \
-  K, bt.max_candidates, bt.pos, bt.mode, bt.compress_ratio, bt.pool_len, bt.cand_off, bt.cand_idx, scores, stride, topk_idx
-  if (B >= kManyQueries) {
-    // lists of at most one 512 x 32 segment and no Reindex lists: the lean form
-    if (bt.max_candidates <= 512 * 32 && bt.cand_off == nullptr)
-      hipLaunchKernelGGL((topk_kernel<512, 32, true>), dim3(B), dim3(512), 0, s, CSA2_TOPK_ARGS);
-    else
-      hipLaunchKernelGGL((topk_kernel<512, 32, false>), dim3(B), dim3(512), 0, s, CSA2_TOPK_ARGS);
-  } else {
-    hipLaunchKernelGGL((topk_kernel<1024, 16, false>), dim3(B), dim3(1024), 0, s, CSA2_TOPK_ARGS);
-  }
-#undef CSA2_TOPK_ARGS
+  launch_forms(K, B, bt, scores, stride, topk_idx, s);
   return hipGetLastError();
 }
 
+static int32_t split_segments(int32_t B, int32_t max_cand) {
+  if (B <= 0 || B >= kManyQueries || max_cand <= kSplitSeg) return 0;
+  return (max_cand + kSplitSeg - 1) / kSplitSeg;
+}
+
+size_t topk_split_bytes(int32_t B, int32_t max_cand) {
+  const int32_t S = split_segments(B, max_cand);
+  if (S == 0) return 0;
+  const size_t a = 256;
+  auto up = [&](size_t x) { return (x + a - 1) / a * a; };
+  const size_t per = (size_t)B * S * kMaxTopK;
+  return up(per * 4) + up(per * 4) + up((size_t)B * 4) + up(((size_t)B + 1) * 8);
+}
+
 hipError_t launch_topk(const csa2_dims& d, int32_t B, const csa2_batch& bt, const float* scores,
-                       int64_t stride, int32_t* topk_idx, hipStream_t s) {
-  return launch_topk_k(d.index_topk, B, bt, scores, stride, topk_idx, s);
+                       int64_t stride, int32_t* topk_idx, void* split_ws, hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  const int32_t K = d.index_topk;
+  const int32_t S = split_segments(B, bt.max_candidates);
+  if (split_ws == nullptr || S == 0 || K > kBins) {
+    launch_forms(K, B, bt, scores, stride, topk_idx, s);
+    return hipGetLastError();
+  }
+  const size_t a = 256;
+  auto up = [&](size_t x) { return (x + a - 1) / a * a; };
+  const size_t per = (size_t)B * S * kMaxTopK;
+  uint8_t* p = static_cast<uint8_t*>(split_ws);
+  TopkSplit sp;
+  sp.nseg = S;
+  sp.rows = reinterpret_cast<int32_t*>(p);
+  sp.scores = reinterpret_cast<float*>(p + up(per * 4));
+  sp.mode2 = reinterpret_cast<int32_t*>(p + 2 * up(per * 4));
+  sp.off2 = reinterpret_cast<int64_t*>(p + 2 * up(per * 4) + up((size_t)B * 4));
+  // each segment's top-K, then the top-K of those
+  hipLaunchKernelGGL((topk_kernel<1024, 16, kSegment>), dim3(B, S), dim3(1024), 0, s, K, bt.max_candidates, bt.pos,
+                     bt.mode, bt.compress_ratio, bt.pool_len, bt.cand_off, bt.cand_idx, scores, stride, topk_idx, sp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  csa2_batch b2 = bt;
+  b2.mode = sp.mode2;
+  b2.cand_off = sp.off2;
+  b2.cand_idx = sp.rows;
+  b2.max_candidates = S * K;
+  launch_forms(K, B, b2, sp.scores, (int64_t)S * K, topk_idx, s);
+  return hipGetLastError();
 }
 
 }  // namespace csa2

@@ -249,11 +249,11 @@ def test_precondition_status_and_word():
     os.environ["CSA2_DEBUG_CHECK"] = "1"
     try:
         d, b = dims(), batch()
-        assert L.csa2_topk(C.byref(d), 2, C.byref(b), None, 16, None, None) == csa2.CSA2_ERR_INVALID_ARG
+        assert L.csa2_topk(C.byref(d), 2, C.byref(b), None, 16, None, None, 0, None) == csa2.CSA2_ERR_INVALID_ARG
         assert L.csa2_attend(C.byref(dims(n_heads=8)), 2, C.byref(b), FAKE, None, None, None, None, FAKE, None,
                              FAKE, None, None, 0, None, None) == csa2.CSA2_ERR_UNSUPPORTED
         # an empty batch is a no-op: nothing to check, nothing launched
-        assert L.csa2_topk(C.byref(d), 0, C.byref(b), None, 0, None, None) == csa2.CSA2_OK
+        assert L.csa2_topk(C.byref(d), 0, C.byref(b), None, 0, None, None, 0, None) == csa2.CSA2_OK
         assert csa2.csa2_last_precondition() == 0
     finally:
         if old is None:

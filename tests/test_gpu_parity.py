@@ -106,6 +106,67 @@ def test_topk_from_oracle_scores_with_ties(n, k):
         assert np.array_equal(got[b], O.topk(s[b], k)), f"row {b}"
 
 
+@pytest.mark.parametrize("k", [512, 37, 1])
+def test_topk_split_over_workgroups(k):
+    # with a workspace, a small batch whose lists exceed 16,384 candidates
+    # spreads each list over workgroups (segment top-Ks, then the top-K of
+    # those): Full lists of 70,000 (Gaussian), 40,000 (heavy ties), 100,003
+    # (all equal: the lowest rows win) and 16,385 (+0 / -0 mixed), one short
+    # list, and Reindex lists of 30,000 and 20,000 rows with unreachable rows
+    # and -1 padding
+    rng = np.random.default_rng(900 + k)
+    ns = [70000, 40000, 100003, 16385, 300, 30000, 20000]
+    modes = [0, 0, 0, 0, 0, 1, 1]
+    B, n = len(ns), max(ns)
+    s = np.full((B, n), np.nan, np.float32)
+    s[0, :ns[0]] = rng.standard_normal(ns[0])
+    s[1, :ns[1]] = rng.integers(-64, 64, size=ns[1]) / 8
+    s[2, :ns[2]] = 1.5
+    s[3, :ns[3]] = np.where(rng.random(ns[3]) < 0.5, -0.0, 0.0)
+    s[3, rng.integers(0, ns[3], 400)] = rng.standard_normal(400)
+    s[4, :ns[4]] = rng.standard_normal(ns[4])
+    pool = 150000  # rows of the Reindex queries' pools; n_valid 120,000
+    lists, offs = [], [0]
+    for b in range(B):
+        if modes[b] == 1:
+            lst = np.sort(rng.choice(pool, size=ns[b] - 50, replace=False)).astype(np.int32)
+            lst = np.concatenate([lst, np.full(50, -1, np.int32)])
+            s[b, :ns[b]] = rng.standard_normal(ns[b])
+        else:
+            lst = np.zeros(0, np.int32)
+        lists.append(lst)
+        offs.append(offs[-1] + len(lst))
+    pos = np.array([x - 1 if m == 0 else 4 * 120000 - 1 for x, m in zip(ns, modes)], np.int64)
+    ratio = np.array([1 if m == 0 else 4 for m in modes], np.int32)
+    pool_len = np.array([x if m == 0 else pool for x, m in zip(ns, modes)], np.int32)
+    dims = synth.default_dims(index_topk=k)
+    arrs = dict(pos=pos, mode=np.array(modes, np.int32), ratio=ratio, win_row0=np.zeros(B, np.int64),
+                win_len=np.zeros(B, np.int32), pool_row0=np.zeros(B, np.int64), pool_len=pool_len,
+                cand_off=np.array(offs, np.int64), cand_idx=np.concatenate(lists))
+    dev = {kk: torch.from_numpy(np.ascontiguousarray(v)).cuda() for kk, v in arrs.items()}
+    bt = csa2.Batch(*(dev[x].data_ptr() for x in ["pos", "mode", "ratio", "win_row0", "win_len", "pool_row0",
+                                                   "pool_len", "cand_off", "cand_idx"]), n)
+    d = csa2.Dims.from_dict(dims)
+    sc = torch.from_numpy(np.nan_to_num(s, nan=-np.inf)).cuda()
+    ws_bytes = csa2.csa2_workspace_size(d, B, n)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    out = torch.full((B, k), -7, dtype=torch.int32, device="cuda")
+    out1 = torch.full((B, k), -7, dtype=torch.int32, device="cuda")
+    say(f"topk split over workgroups k={k}")
+    csa2.csa2_topk(d, B, bt, sc, n, out, workspace=ws, workspace_bytes=ws_bytes)
+    csa2.csa2_topk(d, B, bt, sc, n, out1)  # one workgroup per query
+    torch.cuda.synchronize()
+    got, one = out.cpu().numpy(), out1.cpu().numpy()
+    assert np.array_equal(got, one)
+    for b in range(B):
+        if modes[b] == 0:
+            want = O.topk(s[b, :ns[b]], k)
+        else:
+            nv = 120000
+            want = O.topk(s[b, :ns[b]], k, nv, pos_of=lists[b])
+        assert np.array_equal(got[b], want), f"row {b}"
+
+
 @pytest.mark.parametrize("B,n,k", [(520, 20000, 512), (512, 16384, 512), (600, 700, 512), (530, 40000, 100)])
 def test_topk_many_queries_with_ties(B, n, k):
     # a batch of many queries takes the top-K kernel's many-queries shape;
