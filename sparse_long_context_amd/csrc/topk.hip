@@ -577,7 +577,20 @@ hipError_t launch_topk(const csa2_dims& d, int32_t B, const csa2_batch& bt, cons
   b2.cand_off = sp.off2;
   b2.cand_idx = sp.rows;
   b2.max_candidates = S * K;
-  launch_forms(K, B, b2, sp.scores, (int64_t)S * K, topk_idx, s);
+  // the merge's lists are short (S x K): a workgroup of 512 threads holding
+  // four or eight keys each takes a query's list in one register segment,
+  // at a fraction of the 1,024 x 16 form's latency
+  const TopkSplit none{0, nullptr, nullptr, nullptr, nullptr};
+#define CSA2_MERGE_ARGS                                                                                   \
+  K, b2.max_candidates, b2.pos, b2.mode, b2.compress_ratio, b2.pool_len, b2.cand_off, b2.cand_idx, sp.scores, \
+      (int64_t)S * K, topk_idx, none
+  if (S * K <= 512 * 4)
+    hipLaunchKernelGGL((topk_kernel<512, 4, kGeneral>), dim3(B), dim3(512), 0, s, CSA2_MERGE_ARGS);
+  else if (S * K <= 512 * 8)
+    hipLaunchKernelGGL((topk_kernel<512, 8, kGeneral>), dim3(B), dim3(512), 0, s, CSA2_MERGE_ARGS);
+  else
+    launch_forms(K, B, b2, sp.scores, (int64_t)S * K, topk_idx, s);
+#undef CSA2_MERGE_ARGS
   return hipGetLastError();
 }
 
