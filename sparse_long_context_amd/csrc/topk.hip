@@ -248,8 +248,23 @@ __global__ __launch_bounds__(kThreads, kThreads == 512 ? 4 : 1) void topk_kernel
         k[4 * j4 + 3] = order_key(s4.w);
       }
     } else {
+      // the thread that straddles the list's end (or an unaligned row):
+      // whole float4s while they lie inside the list, single keys after
+      // (32 single loads in one lane would hold its wave, and the
+      // workgroup's next barrier, for thousands of cycles)
 #pragma unroll
-      for (int j = 0; j < kKpt; ++j) k[j] = (j < nrem) ? order_key(sp[j]) : 0u;
+      for (int j4 = 0; j4 < kKpt / 4; ++j4) {
+        if (sc_aligned && 4 * j4 + 4 <= nrem) {
+          const float4 s4 = reinterpret_cast<const float4*>(sp)[j4];
+          k[4 * j4 + 0] = order_key(s4.x);
+          k[4 * j4 + 1] = order_key(s4.y);
+          k[4 * j4 + 2] = order_key(s4.z);
+          k[4 * j4 + 3] = order_key(s4.w);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) k[4 * j4 + q] = (4 * j4 + q < nrem) ? order_key(sp[4 * j4 + q]) : 0u;
+        }
+      }
     }
     if (kForm != kOneSeg && lst) {  // REINDEX rows outside the reachable range are ineligible
       const int32_t* lp = lst + base;
@@ -268,41 +283,69 @@ __global__ __launch_bounds__(kThreads, kThreads == 512 ? 4 : 1) void topk_kernel
     if (!kOne && nseg > 1) load_seg(s);
   };
 
-  // ---- pass 1: histogram of the top 12 key bits ----
-  // A floor below which no chosen key lies: every thread's largest key is a
-  // distinct key, so at least kThreads >= K keys are >= the smallest of
-  // those maxima, and so is the K-th best.  Keys below it are set ineligible
-  // (0) before counting: for Gaussian scores about a sixth of the list stays,
-  // which spares the LDS histogram most of its same-bucket atomics.  Only
-  // for a list held in registers (one segment).  The waves' minima travel
-  // with the barrier that clears the histogram.
+  // ---- pass 1: histogram of the eligible keys ----
+  // A floor below which no chosen key lies: the largest keys of the P
+  // threads that hold keys are P distinct keys, and the second largest of
+  // the first K - P of them (when P < K; a list a little short of the
+  // segment leaves its last threads empty) K - P more, so at least K keys
+  // are >= the smallest of those, and so is the K-th best.  Keys below it
+  // are set ineligible (0) before counting: for Gaussian scores about a
+  // sixth of the list stays.
+  // The histogram then spans the survivors' own range, [floor, largest key]
+  // in 4,096 bins of 2^shift keys, so the boundary bin of a 16,384-key list
+  // holds a key or two rather than the ~200 that bins of the top 12 key bits
+  // hold there (the ranking and the gather that follow scale with it), and
+  // the counting atomics rarely meet on one bin.  Only for a list held in
+  // registers (one segment); otherwise the bins are the top 12 key bits.  The
+  // waves' minima and maxima travel with the barrier that clears the
+  // histogram.
   const bool floored = nseg == 1 && K <= kThreads;
   for (int x = t; x < kBins / 4; x += kThreads) reinterpret_cast<uint4*>(hist_s)[x] = make_uint4(0u, 0u, 0u, 0u);
   if (t == 0) bcount_s = 0u;
   if (floored) {
-    uint32_t m = 0u;
+    uint32_t m = 0u, m2 = 0u;  // the thread's largest and second largest keys
 #pragma unroll
-    for (int j = 0; j < kKpt; ++j) m = k[j] > m ? k[j] : m;
+    for (int j = 0; j < kKpt; ++j) {
+      const uint32_t lo2 = k[j] < m ? k[j] : m;
+      m2 = lo2 > m2 ? lo2 : m2;
+      m = k[j] > m ? k[j] : m;
+    }
+    uint32_t mx = m;
+    const int P = (n + kKpt - 1) / kKpt < kThreads ? (n + kKpt - 1) / kKpt : kThreads;  // threads holding keys
+    const int D = K > P ? K - P : 0;
+    // D > P: too short a list for a floor (0 keeps every key)
+    m = D > P ? 0u : (t < D ? m2 : (t < P ? m : 0xFFFFFFFFu));
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
       const uint32_t o = (uint32_t)__shfl_xor((int)m, off, 64);
+      const uint32_t ox = (uint32_t)__shfl_xor((int)mx, off, 64);
       m = o < m ? o : m;
+      mx = ox > mx ? ox : mx;
     }
-    if (lane == 0) red_s[wv] = m;
+    if (lane == 0) red_s[wv] = m, red_s[kWaves + wv] = mx;
   }
   __syncthreads();
+  uint32_t kbase = 0u;  // bin of an eligible key: (key - kbase) >> kshift
+  int kshift = 20;
   if (floored) {
-    uint32_t floor = red_s[0];
+    uint32_t floor = red_s[0], top = red_s[kWaves];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) floor = red_s[w] < floor ? red_s[w] : floor;
+    for (int w = 1; w < kWaves; ++w) {
+      floor = red_s[w] < floor ? red_s[w] : floor;
+      top = red_s[kWaves + w] > top ? red_s[kWaves + w] : top;
+    }
 #pragma unroll
     for (int j = 0; j < kKpt; ++j) k[j] = k[j] >= floor ? k[j] : 0u;
+    kbase = floor > 1u ? floor : 1u;  // eligible keys are >= 1
+    const uint32_t range = top > kbase ? top - kbase : 0u;
+    const int bits = range ? 32 - __clz((int)range) : 0;
+    kshift = bits > 12 ? bits - 12 : 0;  // range >> kshift < 4,096
   }
   for (int s = 0; s < nseg; ++s) {
     seg_keys(s);
 #pragma unroll
     for (int j = 0; j < kKpt; ++j)
-      if (k[j] != 0u) atomicAdd(&hist_s[k[j] >> 20], 1u);
+      if (k[j] != 0u) atomicAdd(&hist_s[(k[j] - kbase) >> kshift], 1u);
   }
   __syncthreads();  // (also orders the floor's reads of red_s before find_bucket writes it)
   find_bucket<kThreads>(hist_s, kBins, (uint32_t)K, red_s, pick_s, t, lane, wv);  // pick_s[2]: eligible total
@@ -318,28 +361,31 @@ __global__ __launch_bounds__(kThreads, kThreads == 512 ? 4 : 1) void topk_kernel
   if (!take_all) {
     const uint32_t bucket = pick_s[0];
     const uint32_t quota = (uint32_t)K - pick_s[1];  // 1 .. keys in the bucket
-    const uint32_t lo = bucket << 20;
+    const uint32_t lo = kbase + (bucket << kshift), width = 1u << kshift;  // the bucket: keys lo .. lo + width - 1
     // ---- pass 2: gather the boundary bucket (a wave-wide prefix of the
     // per-thread counts and one LDS atomic per wave place every key) ----
     for (int s = 0; s < nseg; ++s) {
       seg_keys(s);
       uint32_t bm = 0;  // keys of the boundary bucket
 #pragma unroll
-      for (int j = 0; j < kKpt; ++j) bm |= (uint32_t)((k[j] != 0u) & ((k[j] - lo) < (1u << 20))) << j;
+      for (int j = 0; j < kKpt; ++j) bm |= (uint32_t)((k[j] != 0u) & ((k[j] - lo) < width)) << j;
       const uint32_t nb = (uint32_t)__popc(bm);
       const uint32_t nb_incl = wave_incl_scan(nb);
       uint32_t wbase = 0;
       if (lane == 63 && nb_incl != 0u) wbase = atomicAdd(&bcount_s, nb_incl);
       uint32_t slot = (uint32_t)__builtin_amdgcn_readlane((int)wbase, 63) + nb_incl - nb;
       const uint32_t gbase = (uint32_t)(s * kSeg + t * kKpt);
-      if (nb != 0u) {
+      // over the set bits only (a thread holds a key or two of the bucket;
+      // a branch per key position would cost every wave all kKpt of them);
+      // the key at a dynamic position comes from its register by a select
+      // chain, kept off the common path
+      for (uint32_t rest = bm; rest != 0u; rest &= rest - 1u) {
+        const int j = __builtin_ctz(rest);
+        uint32_t kj = 0u;
 #pragma unroll
-        for (int j = 0; j < kKpt; ++j) {
-          if ((bm >> j) & 1u) {
-            if (slot < (uint32_t)kRankCap) bk_s[slot] = ((uint64_t)k[j] << 32) | (uint32_t)~(gbase + j);
-            ++slot;
-          }
-        }
+        for (int q = 0; q < kKpt; ++q) kj = q == j ? k[q] : kj;
+        if (slot < (uint32_t)kRankCap) bk_s[slot] = ((uint64_t)kj << 32) | (uint32_t)~(gbase + (uint32_t)j);
+        ++slot;
       }
     }
     __syncthreads();
@@ -402,19 +448,19 @@ __global__ __launch_bounds__(kThreads, kThreads == 512 ? 4 : 1) void topk_kernel
         }
       }
     } else {
-      // heavy ties: radix select gives the K-th key value and how many keys
-      // equal to it are taken (lowest indices first); the last of those,
-      // found by a prefix over the keys in index order, is the K-th key.
-      // This rare path re-reads the keys, so the register copy need not
-      // stay live through it.
+      // heavy ties: radix select over the bucket's keys gives the K-th key
+      // value and how many keys equal to it are taken (lowest indices
+      // first); the last of those, found by a prefix over the keys in index
+      // order, is the K-th key.  This rare path re-reads the keys, so the
+      // register copy need not stay live through it.
       uint32_t thr = 0, take_eq = 0;
-      radix_finish<kThreads>(1, lo, 0xFFF00000u, quota, hist_s, red_s, pick_s, t, lane, wv,
+      radix_finish<kThreads>(0, 0u, 0u, quota, hist_s, red_s, pick_s, t, lane, wv,
                              [&](int shift, uint32_t dm, uint32_t prefix, uint32_t pmask) __attribute__((always_inline)) {
                                for (int s = 0; s < nseg; ++s) {
                                  if (!kOne) load_seg(s);
 #pragma unroll
                                  for (int j = 0; j < kKpt; ++j)
-                                   if (k[j] != 0u && (k[j] & pmask) == prefix)
+                                   if (k[j] != 0u && (k[j] - lo) < width && (k[j] & pmask) == prefix)
                                      atomicAdd(&hist_s[(k[j] >> shift) & dm], 1u);
                                }
                              },
@@ -465,19 +511,20 @@ __global__ __launch_bounds__(kThreads, kThreads == 512 ? 4 : 1) void topk_kernel
     uint32_t before, unused, tot_sel, unused2;
     block_prefix2<kWaves>(cnt, 0u, red_s, lane, wv, before, unused, tot_sel, unused2);
     before += carry;
-    if (cnt != 0u) {
+    {
+      // over the set bits only (about one chosen key per thread)
       const int32_t* lp = (kForm != kOneSeg && lst) ? lst + base : nullptr;
-#pragma unroll
-      for (int j = 0; j < kKpt; ++j) {
-        if ((cm >> j) & 1u) {
-          if (before < (uint32_t)K) {
-            // kSegment stages the list position (its row and score are both read out below)
-            const int32_t row = kForm == kSegment ? base + j : (lp ? lp[j] : base + j);
-            if (staged) hist_s[before] = (uint32_t)row;
-            else out[before] = row;
-          }
-          ++before;
-        }
+      const uint32_t lim = before < (uint32_t)K ? (uint32_t)K - before : 0u;  // places left
+      uint32_t rest = cnt > lim ? 0u : cm;
+      if (cnt > lim)  // the last places: the chosen keys of lowest position
+        for (uint32_t r = cm, c = 0; c < lim; ++c, r &= r - 1u) rest |= r & (0u - r);
+      for (; rest != 0u; rest &= rest - 1u) {
+        const int j = __builtin_ctz(rest);
+        // kSegment stages the list position (its row and score are both read out below)
+        const int32_t row = kForm == kSegment ? base + j : (lp ? lp[j] : base + j);
+        if (staged) hist_s[before] = (uint32_t)row;
+        else out[before] = row;
+        ++before;
       }
     }
     carry += tot_sel;

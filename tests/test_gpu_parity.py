@@ -194,6 +194,56 @@ def test_topk_many_queries_with_ties(B, n, k):
         assert np.array_equal(got[b], O.topk(s[b, :lens[b]], k)), f"row {b} (n={lens[b]})"
 
 
+def narrow_scores(rng, kind, n):
+    """Score rows whose eligible keys span few order keys (the top-K bins
+    them over their own range): ulp-spaced clusters, two values only, a
+    crowd of ties under a few outliers, negatives, and Gaussian."""
+    one = np.float32(1.0)
+    if kind == 0:    # 1 + u ulp, u < 3,000: bins of one key each
+        return (one.view(np.int32) + rng.integers(0, 3000, n)).astype(np.int32).view(np.float32)
+    if kind == 1:    # u < 5,000: bins of two keys
+        return (one.view(np.int32) + rng.integers(0, 5000, n)).astype(np.int32).view(np.float32)
+    if kind == 2:    # two adjacent values: the boundary bin holds thousands of ties
+        return (one.view(np.int32) + rng.integers(0, 2, n)).astype(np.int32).view(np.float32)
+    if kind == 3:    # a crowd at 2.0 and a few hundred spread above it
+        s = np.full(n, 2.0, np.float32)
+        s[rng.integers(0, n, 300)] = rng.uniform(10, 1000, 300).astype(np.float32)
+        return s
+    if kind == 4:    # negative and narrow
+        return -(one.view(np.int32) + rng.integers(0, 100, n)).astype(np.int32).view(np.float32)
+    return (rng.standard_normal(n) * 11.0).astype(np.float32)
+
+
+@pytest.mark.parametrize("B", [3, 512])
+def test_topk_narrow_key_ranges(B):
+    # both register-segment shapes (a few queries: 1,024 x 16; many: 512 x 32)
+    # over lists of 16,384, 16,001, 15,873 and 5,000 whose keys crowd into
+    # narrow ranges
+    k = 512
+    rng = np.random.default_rng(4200 + B)
+    n = 16384
+    s = np.stack([narrow_scores(rng, b % 6, n) for b in range(B)])
+    lens = np.full(B, n, np.int32)
+    lens[1::4] = 5000
+    lens[2::8] = 15873  # a little short of the register segment: its last threads hold no keys
+    lens[3::8] = 16001
+    dims = synth.default_dims(index_topk=k)
+    inp = dict(pos=lens.astype(np.int64) - 1, mode=np.zeros(B, np.int32), ratio=np.ones(B, np.int32),
+               win_row0=np.zeros(B, np.int64), win_len=np.zeros(B, np.int32), pool_row0=np.zeros(B, np.int64),
+               pool_len=np.full(B, n, np.int32))
+    dev = {kk: torch.from_numpy(v).cuda() for kk, v in inp.items()}
+    bt = csa2.Batch(*(dev[x].data_ptr() for x in ["pos", "mode", "ratio", "win_row0", "win_len", "pool_row0",
+                                                   "pool_len"]), None, None, n)
+    sc = torch.from_numpy(s).cuda()
+    out = torch.full((B, k), -7, dtype=torch.int32, device="cuda")
+    say(f"topk narrow key ranges B={B}")
+    csa2.csa2_topk(csa2.Dims.from_dict(dims), B, bt, sc, n, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for b in range(B):
+        assert np.array_equal(got[b], O.topk(s[b, :lens[b]], k)), f"row {b} (kind {b % 6}, n={lens[b]})"
+
+
 def test_attend_reuse_lists_with_padding_and_duplicates():
     ctx = [30000, 2000, 500, 128 * 4 + 8]
     inp = synth.decode_batch(12, ctx, [synth.MODE_REUSE] * 4, [4] * 4, dims=small_dims())
