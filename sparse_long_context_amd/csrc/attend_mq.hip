@@ -135,8 +135,13 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
   __shared__ float rope_s[2][kMaxRopeDims / 2];  // cos, sin of the rope pairs of the output leaving next
 
   const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // wave-uniform role
-  const int role = wv >= 8 ? kGatherer : ((wv & 2) == 0 ? kScorer : kValuer);
-  const int hq = role == kGatherer ? wv - 8 : (wv & 1) + 2 * (wv >> 2);  // scorer: head tile; value wave: dim quarter; gatherer: row group
+  // A workgroup's waves go to the SIMDs in turn (wave w to SIMD w % 4), so
+  // every SIMD holds one score wave, one value wave and one gather wave: the
+  // same matrix work on each, and a score wave's softmax runs beside the
+  // value wave's products (two score waves on one SIMD reach their products,
+  // and their softmax, together)
+  const int role = wv >= 8 ? kGatherer : (wv < 4 ? kScorer : kValuer);
+  const int hq = wv & 3;  // scorer: head tile; value wave: dim quarter; gatherer: row group
 
   // The workgroups stay resident and take (query, split) items in turn: the
   // items form contiguous runs per XCD (workgroup i runs on XCD i % 8), and
