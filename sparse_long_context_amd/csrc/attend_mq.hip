@@ -631,9 +631,16 @@ __global__ __launch_bounds__(kThr) void attend_mq_kernel(MqArgs a) {
   }  // items
   flush_out();  // the last item's output
   };
-  if (role == kScorer) run(std::integral_constant<int, kScorer>{});
-  else if (role == kGatherer) run(std::integral_constant<int, kGatherer>{});
-  else run(std::integral_constant<int, kValuer>{});
+  // the gather waves' DMAs go out ahead of the other waves' work on their
+  // SIMD (a wave's issue priority, not a stream's)
+  if (role == kScorer) {
+    run(std::integral_constant<int, kScorer>{});
+  } else if (role == kGatherer) {
+    __builtin_amdgcn_s_setprio(3);
+    run(std::integral_constant<int, kGatherer>{});
+  } else {
+    run(std::integral_constant<int, kValuer>{});
+  }
 }
 
 }  // namespace
