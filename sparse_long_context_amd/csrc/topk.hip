@@ -198,7 +198,10 @@ __global__ __launch_bounds__(kThreads, kThreads == 512 ? 4 : 1) void topk_kernel
   __shared__ uint64_t thr_s;
   __shared__ uint32_t bcount_s;
 
-  const int b = blockIdx.x;
+  // queries in reverse: a batch's scores are written in query order just
+  // before, so the last rows written, the likeliest to be in the last-level
+  // cache, are read first (forward, the first misses evict them)
+  const int b = kForm == kSegment ? (int)blockIdx.x : (int)gridDim.x - 1 - (int)blockIdx.x;
   const int t = threadIdx.x;
   const int lane = t & 63, wv = t >> 6;
   const int md = mode[b];
