@@ -85,6 +85,56 @@ def traffic_from_profile(which):
     return rec.get("hbm_bytes_per_launch")
 
 
+def gather_probe(torch):
+    """Rate of random 1 KiB row gathers per CU and over the chip (the bf16
+    attention's access pattern), by LDS DMA and by loads into registers, from
+    regions of 2 MiB (L2-resident), 16 MiB (the prefill pool) and 512 MiB,
+    with libcsa2_probe.so; one JSON line."""
+    import ctypes
+    import numpy as np
+    from sparse_long_context_amd import build as B
+    if not os.path.exists(B.PROBE_LIB):
+        raise RuntimeError(f"{B.PROBE_LIB} is not built; run __graft_entry__.build() first")
+    L = ctypes.CDLL(B.PROBE_LIB)
+    L.csa2_probe_gather.restype = ctypes.c_int
+    L.csa2_probe_gather.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    nrows, per_wave, reps = 1 << 19, 1024, 5
+    rows = torch.zeros(nrows * 256, dtype=torch.int32, device="cuda")  # 512 MiB of 1 KiB rows
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    rng = np.random.default_rng(1)
+    out = {"probe": "random 1 KiB row gathers, one workgroup per CU, each wave two batches of 8 rows in flight",
+           "cus": n_cu, "rows_per_wave": per_wave, "results": []}
+    for region, span in (("2 MiB", 2048), ("16 MiB", 16384), ("512 MiB", nrows)):
+        idx_np = rng.integers(0, span, size=n_cu * 8 * per_wave).astype(np.int32)
+        assert idx_np.min() >= 0 and idx_np.max() < nrows
+        idx = torch.from_numpy(idx_np).cuda()
+        for mode, name in ((0, "lds_dma"), (1, "registers")):
+            for waves in (4, 8):
+                def go():
+                    rc = L.csa2_probe_gather(mode, waves, n_cu, rows.data_ptr(), idx.data_ptr(), per_wave,
+                                             sink.data_ptr(), ctypes.c_void_p(stream.cuda_stream))
+                    if rc != 0:
+                        raise RuntimeError(f"csa2_probe_gather: hipError {rc}")
+                go()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(reps):
+                    go()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1000.0 / reps
+                gbs = n_cu * waves * per_wave * 1024.0 / (us * 1e-6) / 1e9
+                out["results"].append({"region": region, "path": name, "waves_per_cu": waves,
+                                       "us_per_launch": round(us, 1), "gb_s": round(gbs, 1),
+                                       "gb_s_per_cu": round(gbs / n_cu, 1)})
+        del idx
+    print(json.dumps(out), flush=True)
+
+
 def copy_probe(torch):
     """Plain streaming kernels of known size, for scaling the HBM byte
     counters: a fill writes COPY_PROBE_BYTES, a sum reads them."""
@@ -539,6 +589,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain %d MiB fill and sum (for scaling rocprofv3 byte counters)" % (COPY_PROBE_BYTES >> 20))
+    ap.add_argument("--gather-probe", action="store_true",
+                    help="only measure the rate of random 1 KiB row gathers (libcsa2_probe.so) and print it")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of 'bench.py --copy-probe' "
                          "into a kernel's HBM bytes per launch, and exit")
@@ -571,6 +623,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.gather_probe:
+        gather_probe(torch)
+        return
     stream = torch.cuda.current_stream()
 
     if args.config == 2:

@@ -2,6 +2,8 @@
 
 * ``libcsa2.so``        -- the HIP library behind include/csa2.h (hipcc, gfx950).
 * ``libcsa2_synth.so``  -- the seeded synthetic-input generator (gcc).
+* ``libcsa2_probe.so``  -- the row-gather rate probe behind ``bench.py
+  --gather-probe`` (a measurement aid, not part of the ABI).
 """
 import concurrent.futures as cf
 import glob
@@ -16,6 +18,7 @@ ARCH = "gfx950"
 
 HIP_LIB = os.path.join(PKG, "libcsa2.so")
 SYNTH_LIB = os.path.join(PKG, "libcsa2_synth.so")
+PROBE_LIB = os.path.join(PKG, "libcsa2_probe.so")
 
 def _run(cmd, verbose):
     if verbose:
@@ -58,8 +61,15 @@ def build_hip(verbose: bool = False) -> str:
     return HIP_LIB
 
 
+def build_probe(verbose: bool = False) -> str:
+    src = os.path.join(PKG, "probe", "gather_rate.hip")
+    _run([HIPCC] + _hip_flags(src) + ["-shared", "-o", PROBE_LIB + ".tmp", src], verbose)
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
+    return PROBE_LIB
+
+
 def build_all(verbose: bool = False):
-    return build_synth(verbose), build_hip(verbose)
+    return build_synth(verbose), build_hip(verbose), build_probe(verbose)
 
 
 if __name__ == "__main__":

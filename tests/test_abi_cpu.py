@@ -265,3 +265,20 @@ def test_precondition_status_and_word():
     for name in ("MODE", "DESC", "LIST", "SEL", "KV_SCALE", "INDEX"):
         m = re.search(r"#define CSA2_PRE_%s (\d+)u" % name, src)
         assert m and int(m.group(1)) == getattr(csa2, "CSA2_PRE_" + name), name
+
+
+def test_gather_probe_library_validates_before_launching():
+    # the measurement aid behind bench.py --gather-probe (not part of the ABI):
+    # built beside libcsa2.so, it refuses a bad mode, wave count or row count
+    # (hipErrorInvalidValue = 1) before any launch
+    from sparse_long_context_amd import build as B
+    if not os.path.exists(B.PROBE_LIB):
+        pytest.skip("libcsa2_probe.so is built by __graft_entry__.build()")
+    L = C.CDLL(B.PROBE_LIB)
+    f = L.csa2_probe_gather
+    f.restype = C.c_int
+    f.argtypes = [C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_int, C.c_void_p, C.c_void_p]
+    assert f(2, 4, 1, FAKE, FAKE, 8, FAKE, None) == 1      # mode
+    assert f(0, 6, 1, FAKE, FAKE, 8, FAKE, None) == 1      # waves
+    assert f(0, 4, 0, FAKE, FAKE, 8, FAKE, None) == 1      # workgroups
+    assert f(1, 8, 1, FAKE, FAKE, 12, FAKE, None) == 1     # rows per wave, a multiple of 8
