@@ -322,7 +322,9 @@ __global__ __launch_bounds__(kMxThreads) void index_scores_decode_mx(
 // of its (head, candidate).  Heads past H_I are zero with zero weight.  A
 // workgroup of four waves takes 256 candidates; key rows come in with
 // coalesced 16-byte loads through LDS in slabs of 32 dims (whole 128-byte
-// lines of each row), two slabs in flight.  The per-candidate sum over heads,
+// lines of each row), two slabs in flight, each with its 32 dims of the 32
+// heads' queries (so LDS holds one slab of each, 42 KiB, and three
+// workgroups share a CU).  The per-candidate sum over heads,
 // in head order, needs the 32 heads of a candidate in one lane: lanes l and
 // l + 32 hold complementary halves of the heads of candidates l % 32 (block 0)
 // and 32 + l % 32 (block 1), and one permlane32 swap per register pair leaves
@@ -334,9 +336,8 @@ constexpr int kHU = kHS / 4;       // 16-byte units of a row per slab
 constexpr int kHRow = kHS + 4;     // LDS row stride in floats (9 units: sixteen consecutive rows, one unit,
                                    // cover sixteen bank groups)
 constexpr int kHKv = kHC * kHS / 4 / 256;  // float4 of keys per thread per slab (8)
-constexpr int kHQRow = kIndexDim + 4;      // query rows 33 units apart
 
-__global__ __launch_bounds__(256, 2) void index_scores_decode_h32(
+__global__ __launch_bounds__(256, 3) void index_scores_decode_h32(
     int32_t hi, int32_t relu, int32_t max_cand, const int64_t* __restrict__ pos,
     const int32_t* __restrict__ mode, const int32_t* __restrict__ ratio,
     const int64_t* __restrict__ pool_row0, const int32_t* __restrict__ pool_len,
@@ -344,9 +345,9 @@ __global__ __launch_bounds__(256, 2) void index_scores_decode_h32(
     const float* __restrict__ idx_q, const float* __restrict__ idx_w, const float* __restrict__ idx_k,
     float* __restrict__ scores, int64_t stride) {
   __shared__ __attribute__((aligned(16))) float ks[kHC * kHRow];
-  __shared__ __attribute__((aligned(16))) float qs[32 * kHQRow];  // [head][i], zero past H_I
+  __shared__ __attribute__((aligned(16))) float qs[32 * kHRow];  // this slab's [head][i], zero past H_I
   __shared__ float w_s[32];
-  __shared__ int64_t row_s[kHC];
+  __shared__ int32_t row_s[kHC];
   const int b = blockIdx.y;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int md = mode[b];
@@ -359,51 +360,53 @@ __global__ __launch_bounds__(256, 2) void index_scores_decode_h32(
 
   {  // candidate rows (pool-relative), -1 when there is none
     const int64_t j = j0 + t;
-    int64_t r = -1;
+    int32_t r = -1;
     if (j < n) {
       const int64_t rr = (md == CSA2_MODE_FULL) ? j : (int64_t)cand_idx[cand_off[b] + j];
-      if (rr >= 0 && rr < nv) r = rr;
+      if (rr >= 0 && rr < nv) r = (int32_t)rr;  // pool rows fit 32 bits (pool_len is int32)
     }
     row_s[t] = r;
-  }
-  for (int x = t; x < 32 * kIndexDim; x += 256) {
-    const int h = x / kIndexDim, i = x % kIndexDim;
-    qs[h * kHQRow + i] = h < hi ? idx_q[((int64_t)b * hi + h) * kIndexDim + i] : 0.0f;
   }
   if (t < 32) w_s[t] = t < hi ? (idx_w ? idx_w[(int64_t)b * hi + t] : 1.0f) : 0.0f;
   __syncthreads();
 
   const float* kbase = idx_k + pool_row0[b] * kIndexDim;
-  // two slabs in flight: slab s lands in vk[s % 2]
-  float4 vk[2][kHKv];
-  auto load = [&](int sl, float4* v) __attribute__((always_inline)) {
+  // two slabs in flight: slab s lands in vk[s % 2], its 32 dims of q (head
+  // t / 8, dims 4 (t % 8) ..) in vq[s % 2]; the q slab is staged beside the
+  // key slab, so LDS holds one slab of each (three workgroups per CU)
+  float4 vk[2][kHKv], vq[2];
+  auto load = [&](int sl, float4* v, float4& q) __attribute__((always_inline)) {
 #pragma unroll
     for (int it = 0; it < kHKv; ++it) {
       const int p = it * 256 + t, r = p / kHU, u = p % kHU;
       const int64_t rr = row_s[r];
       v[it] = rr >= 0 ? load_stream(kbase + rr * kIndexDim + sl * kHS + u * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    const int h = t / kHU, u = t % kHU;
+    q = h < hi ? *reinterpret_cast<const float4*>(idx_q + ((int64_t)b * hi + h) * kIndexDim + sl * kHS + 4 * u)
+               : make_float4(0.f, 0.f, 0.f, 0.f);
   };
-  auto stage = [&](const float4* v) __attribute__((always_inline)) {
+  auto stage = [&](const float4* v, const float4& q) __attribute__((always_inline)) {
 #pragma unroll
     for (int it = 0; it < kHKv; ++it) {
       const int p = it * 256 + t;
       *reinterpret_cast<float4*>(&ks[(p / kHU) * kHRow + 4 * (p % kHU)]) = v[it];
     }
+    *reinterpret_cast<float4*>(&qs[(t / kHU) * kHRow + 4 * (t % kHU)]) = q;
   };
   f32x32 acc = f32x32{};
-  const float* qa = &qs[(lane & 31) * kHQRow];
+  const float* qa = &qs[(lane & 31) * kHRow];
   const float* kb = &ks[(64 * wv + lane) * kHRow];
-  load(0, vk[0]);
-  load(1, vk[1]);
+  load(0, vk[0], vq[0]);
+  load(1, vk[1], vq[1]);
 #pragma unroll
   for (int sl = 0; sl < kIndexDim / kHS; ++sl) {
-    stage(vk[sl & 1]);
+    stage(vk[sl & 1], vq[sl & 1]);
     __syncthreads();
-    if (sl + 2 < kIndexDim / kHS) load(sl + 2, vk[sl & 1]);
+    if (sl + 2 < kIndexDim / kHS) load(sl + 2, vk[sl & 1], vq[sl & 1]);
 #pragma unroll
     for (int u = 0; u < kHU; ++u) {
-      const float4 a4 = *reinterpret_cast<const float4*>(qa + sl * kHS + 4 * u);
+      const float4 a4 = *reinterpret_cast<const float4*>(qa + 4 * u);
       const float4 b4 = *reinterpret_cast<const float4*>(kb + 4 * u);
       acc = __builtin_amdgcn_mfma_f32_32x32x1f32(a4.x, b4.x, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x1f32(a4.y, b4.y, acc, 0, 0, 0);
