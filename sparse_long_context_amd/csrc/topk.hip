@@ -552,7 +552,8 @@ __global__ __launch_bounds__(kThreads, kThreads == 512 ? 4 : 1) void topk_kernel
 
 }  // namespace
 
-// Batches of at least this many queries take the 512-thread shape.
+// Batches of at least this many queries take the 512-thread shape for lists
+// past one register segment or with Reindex lists.
 constexpr int32_t kManyQueries = 512;
 // Smaller batches with lists past one 1,024 x 16 segment split them over
 // workgroups (kSegment) when given the buffers; the largest batches have
@@ -565,15 +566,14 @@ static void launch_forms(int32_t K, int32_t B, const csa2_batch& bt, const float
 #define CSA2_TOPK_ARGS                                                                                    \
   K, bt.max_candidates, bt.pos, bt.mode, bt.compress_ratio, bt.pool_len, bt.cand_off, bt.cand_idx, scores, \
       stride, topk_idx, none
-  if (B >= kManyQueries) {
-    // lists of at most one 512 x 32 segment and no Reindex lists: the lean form
-    if (bt.max_candidates <= 512 * 32 && bt.cand_off == nullptr)
-      hipLaunchKernelGGL((topk_kernel<512, 32, kOneSeg>), dim3(B), dim3(512), 0, s, CSA2_TOPK_ARGS);
-    else
-      hipLaunchKernelGGL((topk_kernel<512, 32, kGeneral>), dim3(B), dim3(512), 0, s, CSA2_TOPK_ARGS);
-  } else {
+  // lists of at most one 512 x 32 segment and no Reindex lists: the lean
+  // form, at any batch size (its latency per query is also the lowest)
+  if (bt.max_candidates <= 512 * 32 && bt.cand_off == nullptr)
+    hipLaunchKernelGGL((topk_kernel<512, 32, kOneSeg>), dim3(B), dim3(512), 0, s, CSA2_TOPK_ARGS);
+  else if (B >= kManyQueries)
+    hipLaunchKernelGGL((topk_kernel<512, 32, kGeneral>), dim3(B), dim3(512), 0, s, CSA2_TOPK_ARGS);
+  else
     hipLaunchKernelGGL((topk_kernel<1024, 16, kGeneral>), dim3(B), dim3(1024), 0, s, CSA2_TOPK_ARGS);
-  }
 #undef CSA2_TOPK_ARGS
 }
 
