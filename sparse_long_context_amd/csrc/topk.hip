@@ -156,6 +156,71 @@ __device__ __forceinline__ void radix_finish(int d0, uint32_t prefix, uint32_t p
   take_eq = krem;
 }
 
+// Rank the m (<= kRankCap) keys gathered in bk_s against each other under the
+// unsigned order of (key << 32 | ~index); the one ranked quota - 1 (0-based)
+// is written to *thr_s.  Keys are distinct (their indices differ), so exactly
+// one thread writes.
+template <int kThreads>
+__device__ __forceinline__ void rank_bucket(const uint64_t* bk_s, uint32_t m, uint32_t quota, uint64_t* thr_s,
+                                            int t) {
+  // rank the bucket's keys against each other; the one ranked quota-1
+  // is the K-th key overall
+  if (m <= (uint32_t)(kThreads / 4)) {
+    // four threads per key, each comparing against every fourth key
+    const uint32_t key = (uint32_t)t >> 2, part = (uint32_t)t & 3u;
+    const uint64_t me = bk_s[key < m ? key : 0u];
+    uint32_t r = 0;
+    uint32_t q = part;
+    for (; q + 28 < m; q += 32) {
+      uint64_t o[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) o[u] = bk_s[q + 4 * u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) r += (uint32_t)(o[u] > me);
+    }
+    for (; q < m; q += 4) r += (uint32_t)(bk_s[q] > me);
+    // sum the quad (DPP quad_perm [1,0,3,2] then [2,3,0,1])
+    r += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)r, 0xB1, 0xf, 0xf, false);
+    r += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)r, 0x4E, 0xf, 0xf, false);
+    if (key < m && part == 0u && r == quota - 1u) *thr_s = me;
+  } else if (m <= (uint32_t)(kThreads / 2)) {
+    // two threads per key (the usual bucket of a 16,384-key list holds
+    // ~200), each comparing against every other key
+    const uint32_t key = (uint32_t)t >> 1, part = (uint32_t)t & 1u;
+    const uint64_t me = bk_s[key < m ? key : 0u];
+    uint32_t r = 0;
+    uint32_t q = part;
+    for (; q + 14 < m; q += 16) {
+      uint64_t o[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) o[u] = bk_s[q + 2 * u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) r += (uint32_t)(o[u] > me);
+    }
+    for (; q < m; q += 2) r += (uint32_t)(bk_s[q] > me);
+    // sum the pair (DPP quad_perm [1,0,3,2])
+    r += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)r, 0xB1, 0xf, 0xf, false);
+    if (key < m && part == 0u && r == quota - 1u) *thr_s = me;
+  } else {
+    // one thread per key, several keys per thread past kThreads
+    for (uint32_t key = (uint32_t)t; key < m; key += kThreads) {
+      // (key desc, index asc) is the unsigned order of key << 32 | ~index
+      const uint64_t me = bk_s[key];
+      uint32_t r = 0;
+      uint32_t q = 0;
+      for (; q + 8 <= m; q += 8) {  // eight independent LDS reads in flight
+        uint64_t o[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) o[u] = bk_s[q + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) r += (uint32_t)(o[u] > me);
+      }
+      for (; q < m; ++q) r += (uint32_t)(bk_s[q] > me);
+      if (r == quota - 1u) *thr_s = me;
+    }
+  }
+}
+
 // Forms of the kernel:
 //   kGeneral  any list, re-read in segments when it outgrows the registers;
 //   kOneSeg   every list fits one segment and none is a Reindex list (the
@@ -177,12 +242,24 @@ struct TopkSplit {
   int64_t* off2;       // [B + 1]: b * nseg * K
 };
 
+// The LDS a workgroup of topk_run works in (the caller owns it, so another
+// kernel can run topk_run over storage it also uses for other purposes).
+struct TopkLds {
+  uint32_t* hist;    // [kBins], 16-byte aligned
+  uint32_t* red;     // [2 * waves]
+  uint32_t* pick;    // [4]
+  uint64_t* bk;      // [kRankCap]: boundary-bucket (key << 32 | ~index)
+  uint64_t* thr;     // the K-th key, (key << 32 | ~index)
+  uint32_t* bcount;  // boundary keys gathered
+};
+
 template <int kThreads, int kKpt, int kForm>
-__global__ __launch_bounds__(kThreads, kThreads == 512 ? 4 : 1) void topk_kernel(
-    int32_t K, int32_t max_cand, const int64_t* __restrict__ pos, const int32_t* __restrict__ mode,
-    const int32_t* __restrict__ ratio, const int32_t* __restrict__ pool_len,
-    const int64_t* __restrict__ cand_off, const int32_t* __restrict__ cand_idx,
-    const float* __restrict__ scores, int64_t stride, int32_t* __restrict__ topk_idx, TopkSplit split) {
+__device__ __forceinline__ void topk_run(int32_t K, int32_t max_cand, const int64_t* __restrict__ pos,
+                                         const int32_t* __restrict__ mode, const int32_t* __restrict__ ratio,
+                                         const int32_t* __restrict__ pool_len, const int64_t* __restrict__ cand_off,
+                                         const int32_t* __restrict__ cand_idx, const float* __restrict__ scores,
+                                         int64_t stride, int32_t* __restrict__ topk_idx, TopkSplit split,
+                                         const TopkLds& L) {
   constexpr bool kOne = kForm != kGeneral;  // the list is one register segment
   constexpr int kWaves = kThreads / 64;
   constexpr int kSeg = kThreads * kKpt;  // keys per segment (one key register set)
@@ -191,12 +268,12 @@ __global__ __launch_bounds__(kThreads, kThreads == 512 ? 4 : 1) void topk_kernel
   // register) between counting and placing, rather than as kKpt condition
   // masks held across the block-wide scan in between.
   static_assert(kKpt <= 32, "a thread's keys fit one bit mask");
-  __shared__ __attribute__((aligned(16))) uint32_t hist_s[kBins];
-  __shared__ uint32_t red_s[2 * kWaves];
-  __shared__ uint32_t pick_s[4];
-  __shared__ uint64_t bk_s[kRankCap];  // boundary-bucket (key << 32 | ~index)
-  __shared__ uint64_t thr_s;
-  __shared__ uint32_t bcount_s;
+  uint32_t* const hist_s = L.hist;
+  uint32_t* const red_s = L.red;
+  uint32_t* const pick_s = L.pick;
+  uint64_t* const bk_s = L.bk;
+  uint64_t& thr_s = *L.thr;
+  uint32_t& bcount_s = *L.bcount;
 
   // queries in reverse: a batch's scores are written in query order just
   // before, so the last rows written, the likeliest to be in the last-level
@@ -394,62 +471,7 @@ __global__ __launch_bounds__(kThreads, kThreads == 512 ? 4 : 1) void topk_kernel
     __syncthreads();
     const uint32_t m = bcount_s;
     if (m <= (uint32_t)kRankCap) {
-      // rank the bucket's keys against each other; the one ranked quota-1
-      // is the K-th key overall
-      if (m <= (uint32_t)(kThreads / 4)) {
-        // four threads per key, each comparing against every fourth key
-        const uint32_t key = (uint32_t)t >> 2, part = (uint32_t)t & 3u;
-        const uint64_t me = bk_s[key < m ? key : 0u];
-        uint32_t r = 0;
-        uint32_t q = part;
-        for (; q + 28 < m; q += 32) {
-          uint64_t o[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) o[u] = bk_s[q + 4 * u];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) r += (uint32_t)(o[u] > me);
-        }
-        for (; q < m; q += 4) r += (uint32_t)(bk_s[q] > me);
-        // sum the quad (DPP quad_perm [1,0,3,2] then [2,3,0,1])
-        r += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)r, 0xB1, 0xf, 0xf, false);
-        r += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)r, 0x4E, 0xf, 0xf, false);
-        if (key < m && part == 0u && r == quota - 1u) thr_s = me;
-      } else if (m <= (uint32_t)(kThreads / 2)) {
-        // two threads per key (the usual bucket of a 16,384-key list holds
-        // ~200), each comparing against every other key
-        const uint32_t key = (uint32_t)t >> 1, part = (uint32_t)t & 1u;
-        const uint64_t me = bk_s[key < m ? key : 0u];
-        uint32_t r = 0;
-        uint32_t q = part;
-        for (; q + 14 < m; q += 16) {
-          uint64_t o[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) o[u] = bk_s[q + 2 * u];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) r += (uint32_t)(o[u] > me);
-        }
-        for (; q < m; q += 2) r += (uint32_t)(bk_s[q] > me);
-        // sum the pair (DPP quad_perm [1,0,3,2])
-        r += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)r, 0xB1, 0xf, 0xf, false);
-        if (key < m && part == 0u && r == quota - 1u) thr_s = me;
-      } else {
-        // one thread per key, several keys per thread past kThreads
-        for (uint32_t key = (uint32_t)t; key < m; key += kThreads) {
-          // (key desc, index asc) is the unsigned order of key << 32 | ~index
-          const uint64_t me = bk_s[key];
-          uint32_t r = 0;
-          uint32_t q = 0;
-          for (; q + 8 <= m; q += 8) {  // eight independent LDS reads in flight
-            uint64_t o[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) o[u] = bk_s[q + u];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) r += (uint32_t)(o[u] > me);
-          }
-          for (; q < m; ++q) r += (uint32_t)(bk_s[q] > me);
-          if (r == quota - 1u) thr_s = me;
-        }
-      }
+      rank_bucket<kThreads>(bk_s, m, quota, &thr_s, t);
     } else {
       // heavy ties: radix select over the bucket's keys gives the K-th key
       // value and how many keys equal to it are taken (lowest indices
@@ -550,6 +572,235 @@ __global__ __launch_bounds__(kThreads, kThreads == 512 ? 4 : 1) void topk_kernel
   }
 }
 
+template <int kThreads, int kKpt, int kForm>
+__global__ __launch_bounds__(kThreads, kThreads == 512 ? 4 : 1) void topk_kernel(
+    int32_t K, int32_t max_cand, const int64_t* __restrict__ pos, const int32_t* __restrict__ mode,
+    const int32_t* __restrict__ ratio, const int32_t* __restrict__ pool_len,
+    const int64_t* __restrict__ cand_off, const int32_t* __restrict__ cand_idx,
+    const float* __restrict__ scores, int64_t stride, int32_t* __restrict__ topk_idx, TopkSplit split) {
+  __shared__ __attribute__((aligned(16))) uint32_t hist_s[kBins];
+  __shared__ uint32_t red_s[2 * (kThreads / 64)];
+  __shared__ uint32_t pick_s[4];
+  __shared__ uint64_t bk_s[kRankCap];
+  __shared__ uint64_t thr_s;
+  __shared__ uint32_t bcount_s;
+  const TopkLds L{hist_s, red_s, pick_s, bk_s, &thr_s, &bcount_s};
+  topk_run<kThreads, kKpt, kForm>(K, max_cand, pos, mode, ratio, pool_len, cand_off, cand_idx, scores, stride,
+                                  topk_idx, split, L);
+}
+
+// ---------------------------------------------------------------------------
+// The survivor form: one workgroup of 512 threads per query for lists of
+// 2,048 .. 16,384 candidates (no Reindex lists, K <= 512).
+//
+// The list is read as 8 chunks of 2,048 keys, thread t holding keys
+// 2048c + 4t .. 2048c + 4t + 3 of chunk c (one 16-byte load per chunk, so
+// each load instruction of a wave reads 1 KiB of consecutive scores).  Every
+// thread holds at least one key of the first chunk, so the 512 threads'
+// largest keys are 512 >= K distinct keys, and the smallest of them is a
+// floor: no key below it can be among the K best.
+//
+// With a positive floor, the order of keys at or above it is the order of
+// the scores' bit patterns read as signed integers (non-negative patterns are
+// the positive scores, +inf and +NaN patterns above them in the same order the
+// key map gives them; every pattern with the sign bit set, -0 included, maps
+// below +0 and so below the floor).  The floor test is one integer compare
+// per key, with no key map at all.  Keys at or above the floor (for Gaussian
+// scores about 18 % of the list: the floor is the smallest of 512 maxima of
+// 32) are appended to their wave's survivor list in LDS, (~position, score
+// bits), by a wave-wide ballot and prefix.  Every later pass runs over the
+// survivors only, a few per lane instead of 32 keys per thread:
+//  1. a 4,096-bin histogram over [floor, largest key] finds the bucket that
+//     holds the K-th best survivor and how many lie above it;
+//  2. that bucket's survivors (typically one or two) are ranked exactly
+//     under (score desc, position asc): the K-th key (th, index limit);
+//  3. each chosen survivor sets its position's bit in a 16,384-bit LDS map;
+//     thread t owns word t (positions 32t .. 32t + 31), so a block-wide
+//     prefix over the words' popcounts writes the chosen rows in ascending
+//     order.
+// Whatever this form does not cover goes through the register-segment form
+// (topk_run, kOneSeg) on the same LDS: a short or unaligned list, a floor at
+// or below +0 (some thread holds no positive score), a wave with more than
+// kLCap survivors, or a boundary bucket of more than kRankCap keys (heavy
+// ties).  The results are the same either way.
+constexpr int kLThreads = 512, kLWaves = kLThreads / 64;
+constexpr int kLChunks = 8, kLSpan = kLThreads * 4;  // 2,048 keys per chunk
+constexpr int kLMax = kLChunks * kLSpan;               // 16,384
+constexpr uint32_t kLCap = 512;                        // survivors a wave's list holds
+
+__global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(6))) void topk_lean_kernel(
+    int32_t K, int32_t max_cand, const int64_t* __restrict__ pos, const int32_t* __restrict__ mode,
+    const int32_t* __restrict__ ratio, const int32_t* __restrict__ pool_len,
+    const int64_t* __restrict__ cand_off, const int32_t* __restrict__ cand_idx,
+    const float* __restrict__ scores, int64_t stride, int32_t* __restrict__ topk_idx, TopkSplit split) {
+  __shared__ __attribute__((aligned(16))) uint32_t hist_s[kBins];
+  // per wave kLCap pairs (~position, score bits); the fallback's bk list
+  __shared__ __attribute__((aligned(16))) uint32_t surv_s[2 * kLWaves * kLCap];
+  __shared__ uint32_t map_s[kLThreads];  // chosen positions, one bit each
+  __shared__ uint32_t red_s[2 * kLWaves];
+  __shared__ uint32_t pick_s[4];
+  __shared__ uint32_t cnt_s[kLWaves];
+  __shared__ uint64_t thr_s;
+  __shared__ uint32_t bcount_s;
+  static_assert(2 * kLWaves * kLCap * 4 >= kRankCap * 8, "the fallback's bk list fits the survivor lists");
+  const TopkLds L{hist_s, red_s, pick_s, reinterpret_cast<uint64_t*>(surv_s), &thr_s, &bcount_s};
+  // the survivor path; false: the query goes through topk_run instead (a
+  // uniform decision, taken before or after a barrier; one call site keeps
+  // one inlined copy of topk_run)
+  auto survivors = [&]() __attribute__((always_inline)) -> bool {
+  const int b = (int)gridDim.x - 1 - (int)blockIdx.x;  // queries in reverse, as in topk_run
+  const int t = threadIdx.x;
+  const int lane = t & 63, wv = t >> 6;
+  const int md = mode[b];
+  if (md != CSA2_MODE_FULL && md != CSA2_MODE_REINDEX) return true;
+  int64_t n64 = md == CSA2_MODE_FULL ? n_valid_of(pos[b], ratio[b], md, pool_len[b]) : 0;
+  if (n64 > max_cand) n64 = max_cand;
+  const float* sc = scores + (int64_t)b * stride;
+  if (cand_off != nullptr || K < 1 || K > kLThreads || n64 < kLSpan || n64 > kLMax ||
+      (reinterpret_cast<uintptr_t>(sc) & 15u) != 0)
+    return false;
+  const int n = (int)n64;
+  int32_t* out = topk_idx + (int64_t)b * K;
+
+  // ---- the keys (score bits as signed integers), the thread's largest ----
+  int v[kLChunks * 4];
+#pragma unroll
+  for (int c = 0; c < kLChunks; ++c) {
+    // positions past the list's end are INT32_MIN, below any positive floor;
+    // only the thread that straddles the end loads single scores
+    const int off = c * kLSpan + 4 * t;
+    int4 x = make_int4(INT32_MIN, INT32_MIN, INT32_MIN, INT32_MIN);
+    if (off + 4 <= n) {
+      x = reinterpret_cast<const int4*>(sc + off)[0];
+    } else if (off < n) {
+      x.x = __float_as_int(sc[off]);
+      if (off + 1 < n) x.y = __float_as_int(sc[off + 1]);
+      if (off + 2 < n) x.z = __float_as_int(sc[off + 2]);
+    }
+    v[4 * c + 0] = x.x, v[4 * c + 1] = x.y, v[4 * c + 2] = x.z, v[4 * c + 3] = x.w;
+  }
+  int mx = v[0];
+#pragma unroll
+  for (int j = 1; j < kLChunks * 4; ++j) mx = v[j] > mx ? v[j] : mx;
+  int lo_m = mx, hi_m = mx;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const int a = __shfl_xor(lo_m, off, 64), c = __shfl_xor(hi_m, off, 64);
+    lo_m = a < lo_m ? a : lo_m;
+    hi_m = c > hi_m ? c : hi_m;
+  }
+  for (int x = t; x < kBins / 4; x += kLThreads) reinterpret_cast<uint4*>(hist_s)[x] = make_uint4(0u, 0u, 0u, 0u);
+  map_s[t] = 0u;
+  if (t == 0) bcount_s = 0u;
+  if (lane == 0) red_s[wv] = (uint32_t)lo_m, red_s[kLWaves + wv] = (uint32_t)hi_m;
+  __syncthreads();
+  // the block's floor and largest key, reduced over eight lanes and kept
+  // wave-uniform (scalar registers)
+  int fl = lane < kLWaves ? (int)red_s[lane] : INT32_MAX;
+  int tp = lane < kLWaves ? (int)red_s[kLWaves + lane] : INT32_MIN;
+#pragma unroll
+  for (int off = 4; off >= 1; off >>= 1) {
+    const int a = __shfl_xor(fl, off, 64), c = __shfl_xor(tp, off, 64);
+    fl = a < fl ? a : fl;
+    tp = c > tp ? c : tp;
+  }
+  const int floor = __builtin_amdgcn_readfirstlane(fl), top = __builtin_amdgcn_readfirstlane(tp);
+  if (floor < 1) return false;  // a thread without a positive score: no integer floor
+  const uint32_t range = (uint32_t)(top - floor);
+  const int rbits = range ? 32 - __clz((int)range) : 0;
+  const int kshift = rbits > 12 ? rbits - 12 : 0;  // range >> kshift < 4,096
+
+  // ---- survivors: keys >= floor, appended to the wave's list ----
+  uint32_t* const mine = surv_s + 2u * kLCap * (uint32_t)wv;
+  const uint32_t npos = ~(uint32_t)(4 * t);  // ~position of the thread's first key of chunk 0
+  uint32_t wcnt = 0;                          // the wave's survivors so far (wave-uniform)
+#pragma unroll
+  for (int j = 0; j < kLChunks * 4; ++j) {
+    const bool e = v[j] >= floor;
+    const uint64_t bal = __ballot(e);
+    const uint32_t nb = (uint32_t)__popcll(bal);
+    if (wcnt + nb <= kLCap && e) {
+      const uint32_t slot =
+          __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, wcnt));
+      mine[2 * slot] = npos ^ (uint32_t)((j >> 2) * kLSpan + (j & 3));  // ~position (the bits are disjoint)
+      mine[2 * slot + 1] = (uint32_t)v[j];
+    }
+    wcnt += nb;
+  }
+  // this wave's histogram (its own list: no barrier, only the wave's own
+  // LDS writes to see)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const uint32_t nsurv = wcnt < kLCap ? wcnt : kLCap;
+  for (uint32_t i = (uint32_t)lane; i < nsurv; i += 64)
+    atomicAdd(&hist_s[(mine[2 * i + 1] - (uint32_t)floor) >> kshift], 1u);
+  if (lane == 0) cnt_s[wv] = wcnt;
+  __syncthreads();
+  bool ovf = false;
+#pragma unroll
+  for (int w = 0; w < kLWaves; ++w) ovf |= cnt_s[w] > kLCap;
+  if (ovf) return false;
+  find_bucket<kLThreads>(hist_s, kBins, (uint32_t)K, red_s, pick_s, t, lane, wv);  // pick_s[2]: survivors
+  __syncthreads();
+  const uint32_t total = pick_s[2];
+
+  // a survivor is chosen iff bits > th, or bits == th and position <= plim
+  uint32_t th = 0u, plim = 0xFFFFFFFFu;  // every survivor (its bits are >= floor >= 1)
+  if (total > (uint32_t)K) {
+    const uint32_t bucket = pick_s[0];
+    const uint32_t quota = (uint32_t)K - pick_s[1];  // 1 .. survivors in the bucket
+    const uint32_t lo = (uint32_t)floor + (bucket << kshift), width = 1u << kshift;
+    // the bucket's survivors into bk (the histogram's storage, read for the
+    // last time by find_bucket before the barrier above)
+    uint64_t* const bk = reinterpret_cast<uint64_t*>(hist_s);
+    for (uint32_t i0 = 0; i0 < nsurv; i0 += 64) {
+      const uint32_t i = i0 + (uint32_t)lane;
+      const bool in = i < nsurv;
+      const uint32_t kb = in ? mine[2 * i + 1] : 0u;
+      const bool isb = in && (kb - lo) < width;
+      const uint64_t bal = __ballot(isb);
+      if (bal != 0u) {
+        uint32_t base = 0u;
+        if (lane == 0) base = atomicAdd(&bcount_s, (uint32_t)__popcll(bal));
+        base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+        const uint32_t slot =
+            __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, base));
+        if (isb && slot < (uint32_t)kRankCap) bk[slot] = ((uint64_t)kb << 32) | mine[2 * i];
+      }
+    }
+    __syncthreads();
+    const uint32_t m = bcount_s;
+    if (m > (uint32_t)kRankCap) return false;  // heavy ties
+    rank_bucket<kLThreads>(bk, m, quota, &thr_s, t);
+    __syncthreads();
+    const uint64_t kth = thr_s;
+    th = (uint32_t)(kth >> 32);
+    plim = ~(uint32_t)kth;
+  }
+
+  // ---- the chosen survivors' bits, then rows in ascending order ----
+  for (uint32_t i = (uint32_t)lane; i < nsurv; i += 64) {
+    const uint32_t kb = mine[2 * i + 1], p = ~mine[2 * i];
+    if (kb > th || (kb == th && p <= plim)) atomicOr(&map_s[p >> 5], 1u << (p & 31u));
+  }
+  __syncthreads();
+  const uint32_t word = map_s[t];
+  uint32_t before, unused, n_out, unused2;
+  block_prefix2<kLWaves>((uint32_t)__popc(word), 0u, red_s, lane, wv, before, unused, n_out, unused2);
+  // stage the rows (hist_s is free again: bk's last reads were before the
+  // barrier above) and write them out in one coalesced pass, -1 padded
+  for (uint32_t rest = word; rest != 0u; rest &= rest - 1u) hist_s[before++] = 32u * (uint32_t)t + __builtin_ctz(rest);
+  __syncthreads();
+  for (int x = t; x < K; x += kLThreads) out[x] = (uint32_t)x < n_out ? (int32_t)hist_s[x] : -1;
+  return true;
+  };
+  if (survivors()) return;
+  __syncthreads();  // the survivor path's LDS reads are done before topk_run writes it
+  topk_run<kLThreads, 32, kOneSeg>(K, max_cand, pos, mode, ratio, pool_len, cand_off, cand_idx, scores, stride,
+                                   topk_idx, split, L);
+}
+
 }  // namespace
 
 // Batches of at least this many queries take the 512-thread shape for lists
@@ -568,7 +819,9 @@ static void launch_forms(int32_t K, int32_t B, const csa2_batch& bt, const float
       stride, topk_idx, none
   // lists of at most one 512 x 32 segment and no Reindex lists: the lean
   // form, at any batch size (its latency per query is also the lowest)
-  if (bt.max_candidates <= 512 * 32 && bt.cand_off == nullptr)
+  if (bt.max_candidates <= kLMax && bt.cand_off == nullptr && K <= kLThreads)
+    hipLaunchKernelGGL(topk_lean_kernel, dim3(B), dim3(kLThreads), 0, s, CSA2_TOPK_ARGS);
+  else if (bt.max_candidates <= 512 * 32 && bt.cand_off == nullptr)
     hipLaunchKernelGGL((topk_kernel<512, 32, kOneSeg>), dim3(B), dim3(512), 0, s, CSA2_TOPK_ARGS);
   else if (B >= kManyQueries)
     hipLaunchKernelGGL((topk_kernel<512, 32, kGeneral>), dim3(B), dim3(512), 0, s, CSA2_TOPK_ARGS);
@@ -645,3 +898,4 @@ hipError_t launch_topk(const csa2_dims& d, int32_t B, const csa2_batch& bt, cons
 }
 
 }  // namespace csa2
+

@@ -244,6 +244,57 @@ def test_topk_narrow_key_ranges(B):
         assert np.array_equal(got[b], O.topk(s[b, :lens[b]], k)), f"row {b} (kind {b % 6}, n={lens[b]})"
 
 
+def survivor_rows(rng, n):
+    """Score rows aimed at the top-K's survivor form (lists of 2,048 ..
+    16,384 held as 8 chunks of 2,048, thread t holding 4 scores of each chunk
+    at 4t, wave w the chunk positions 256w .. 256w + 255): Gaussian; one
+    wave's positions far above the rest (its survivor list overflows); only
+    the first score of each thread positive (exactly 512 survivors, all
+    taken); a gap-free run of ties at the floor; Gaussian shifted negative
+    (no positive floor)."""
+    rows = []
+    rows.append(rng.standard_normal(n).astype(np.float32))
+    s = rng.standard_normal(n).astype(np.float32)
+    s[(np.arange(n) % 2048) < 256] += 100.0
+    rows.append(s)
+    s = -np.abs(rng.standard_normal(n)).astype(np.float32) - 1.0
+    first = np.arange(0, 2048, 4)
+    s[first] = rng.permutation(np.arange(1, 513)).astype(np.float32) / 4
+    rows.append(s)
+    rows.append((np.round(rng.standard_normal(n) * 4) / 4 + 3.0).astype(np.float32))
+    rows.append((rng.standard_normal(n) - 6.0).astype(np.float32))
+    return rows
+
+
+@pytest.mark.parametrize("n,k,pad", [(16384, 512, 0), (2048, 512, 0), (2047, 512, 0), (2049, 300, 0),
+                                     (15873, 512, 0), (16384, 512, 1), (9000, 1, 0), (4096, 512, 0)])
+def test_topk_survivor_form(n, k, pad):
+    # a row stride of n + 1 leaves odd rows unaligned (those go through the
+    # register-segment form); every row must match the oracle bit for bit
+    rng = np.random.default_rng(n * 3 + k + pad)
+    rows = survivor_rows(rng, n)
+    B = len(rows)
+    stride = n + pad
+    s = np.full((B, stride), -np.inf, np.float32)
+    for b, r in enumerate(rows):
+        s[b, :n] = r
+    dims = synth.default_dims(index_topk=k)
+    inp = dict(pos=np.full(B, n - 1, np.int64), mode=np.zeros(B, np.int32), ratio=np.ones(B, np.int32),
+               win_row0=np.zeros(B, np.int64), win_len=np.zeros(B, np.int32), pool_row0=np.zeros(B, np.int64),
+               pool_len=np.full(B, n, np.int32))
+    dev = {kk: torch.from_numpy(v).cuda() for kk, v in inp.items()}
+    bt = csa2.Batch(*(dev[x].data_ptr() for x in ["pos", "mode", "ratio", "win_row0", "win_len", "pool_row0",
+                                                   "pool_len"]), None, None, n)
+    sc = torch.from_numpy(s).cuda()
+    out = torch.full((B, k), -7, dtype=torch.int32, device="cuda")
+    say(f"topk survivor form n={n} k={k} stride={stride}")
+    csa2.csa2_topk(csa2.Dims.from_dict(dims), B, bt, sc, stride, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for b in range(B):
+        assert np.array_equal(got[b], O.topk(s[b, :n], k)), f"row {b} (n={n}, k={k}, stride={stride})"
+
+
 def test_attend_reuse_lists_with_padding_and_duplicates():
     ctx = [30000, 2000, 500, 128 * 4 + 8]
     inp = synth.decode_batch(12, ctx, [synth.MODE_REUSE] * 4, [4] * 4, dims=small_dims())
