@@ -100,7 +100,8 @@ constexpr int kRankCap = 1024;  // boundary-bucket keys ranked directly
 // Find the bucket of an nb-bucket histogram that holds the krem-th largest
 // key: each thread owns a run of consecutive buckets, a block-wide suffix scan
 // gives the count above each run.  pick_s[0] = bucket, pick_s[1] = keys above
-// it, pick_s[2] = all keys counted.  Contains barriers; call uniformly.
+// it, pick_s[2] = all keys counted, pick_s[3] = keys in the bucket.  Contains
+// barriers; call uniformly.
 template <int kThreads>
 __device__ __forceinline__ void find_bucket(const uint32_t* hist_s, int nb, uint32_t krem, uint32_t* red_s,
                                             uint32_t* pick_s, int t, int lane, int wv) {
@@ -121,6 +122,7 @@ __device__ __forceinline__ void find_bucket(const uint32_t* hist_s, int nb, uint
       if (above < krem && krem <= above + c[u]) {
         pick_s[0] = t * bpt + u;
         pick_s[1] = above;
+        pick_s[3] = c[u];
       }
       above += c[u];
     }
@@ -627,6 +629,7 @@ constexpr int kLThreads = 512, kLWaves = kLThreads / 64;
 constexpr int kLChunks = 8, kLSpan = kLThreads * 4;  // 2,048 keys per chunk
 constexpr int kLMax = kLChunks * kLSpan;               // 16,384
 constexpr uint32_t kLCap = 512;                        // survivors a wave's list holds
+constexpr uint32_t kLPos = kLWaves * kLCap;            // from a survivor's bits to its ~position
 
 __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(6))) void topk_lean_kernel(
     int32_t K, int32_t max_cand, const int64_t* __restrict__ pos, const int32_t* __restrict__ mode,
@@ -634,7 +637,8 @@ __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(6))) 
     const int64_t* __restrict__ cand_off, const int32_t* __restrict__ cand_idx,
     const float* __restrict__ scores, int64_t stride, int32_t* __restrict__ topk_idx, TopkSplit split) {
   __shared__ __attribute__((aligned(16))) uint32_t hist_s[kBins];
-  // per wave kLCap pairs (~position, score bits); the fallback's bk list
+  // survivors: wave w's score bits at [w kLCap, ..), their ~positions kLPos
+  // words further on; the fallback's bk list
   __shared__ __attribute__((aligned(16))) uint32_t surv_s[2 * kLWaves * kLCap];
   __shared__ uint32_t map_s[kLThreads];  // chosen positions, one bit each
   __shared__ uint32_t red_s[2 * kLWaves];
@@ -711,7 +715,10 @@ __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(6))) 
   const int kshift = rbits > 12 ? rbits - 12 : 0;  // range >> kshift < 4,096
 
   // ---- survivors: keys >= floor, appended to the wave's list ----
-  uint32_t* const mine = surv_s + 2u * kLCap * (uint32_t)wv;
+  // (the list's base and count are wave-uniform scalars, so a survivor's
+  // address is one shift-add of its lane's ballot prefix, and its bits and
+  // ~position go out as two 4-byte writes at a constant distance)
+  uint32_t* const mine = surv_s + kLCap * (uint32_t)__builtin_amdgcn_readfirstlane(wv);
   const uint32_t npos = ~(uint32_t)(4 * t);  // ~position of the thread's first key of chunk 0
   uint32_t wcnt = 0;                          // the wave's survivors so far (wave-uniform)
 #pragma unroll
@@ -720,10 +727,10 @@ __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(6))) 
     const uint64_t bal = __ballot(e);
     const uint32_t nb = (uint32_t)__popcll(bal);
     if (wcnt + nb <= kLCap && e) {
-      const uint32_t slot =
-          __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, wcnt));
-      mine[2 * slot] = npos ^ (uint32_t)((j >> 2) * kLSpan + (j & 3));  // ~position (the bits are disjoint)
-      mine[2 * slot + 1] = (uint32_t)v[j];
+      const uint32_t pre = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+      uint32_t* const at = mine + wcnt + pre;
+      at[0] = (uint32_t)v[j];
+      at[kLPos] = npos ^ (uint32_t)((j >> 2) * kLSpan + (j & 3));  // ~position (the bits are disjoint)
     }
     wcnt += nb;
   }
@@ -734,7 +741,7 @@ __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(6))) 
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   const uint32_t nsurv = wcnt < kLCap ? wcnt : kLCap;
   for (uint32_t i = (uint32_t)lane; i < nsurv; i += 64)
-    atomicAdd(&hist_s[(mine[2 * i + 1] - (uint32_t)floor) >> kshift], 1u);
+    atomicAdd(&hist_s[(mine[i] - (uint32_t)floor) >> kshift], 1u);
   if (lane == 0) cnt_s[wv] = wcnt;
   __syncthreads();
   bool ovf = false;
@@ -747,17 +754,22 @@ __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(6))) 
 
   // a survivor is chosen iff bits > th, or bits == th and position <= plim
   uint32_t th = 0u, plim = 0xFFFFFFFFu;  // every survivor (its bits are >= floor >= 1)
-  if (total > (uint32_t)K) {
-    const uint32_t bucket = pick_s[0];
-    const uint32_t quota = (uint32_t)K - pick_s[1];  // 1 .. survivors in the bucket
-    const uint32_t lo = (uint32_t)floor + (bucket << kshift), width = 1u << kshift;
+  const uint32_t bucket = pick_s[0];
+  const uint32_t quota = (uint32_t)K - pick_s[1];  // 1 .. survivors in the bucket
+  const uint32_t lo = (uint32_t)floor + (bucket << kshift), width = 1u << kshift;
+  if (total > (uint32_t)K && pick_s[3] == quota) {
+    // the bucket's survivors are all chosen (usually the bucket holds just
+    // the one survivor still needed): the chosen ones are those >= lo, and
+    // there is nothing to rank
+    th = lo;
+  } else if (total > (uint32_t)K) {
     // the bucket's survivors into bk (the histogram's storage, read for the
     // last time by find_bucket before the barrier above)
     uint64_t* const bk = reinterpret_cast<uint64_t*>(hist_s);
     for (uint32_t i0 = 0; i0 < nsurv; i0 += 64) {
       const uint32_t i = i0 + (uint32_t)lane;
       const bool in = i < nsurv;
-      const uint32_t kb = in ? mine[2 * i + 1] : 0u;
+      const uint32_t kb = in ? mine[i] : 0u;
       const bool isb = in && (kb - lo) < width;
       const uint64_t bal = __ballot(isb);
       if (bal != 0u) {
@@ -766,7 +778,7 @@ __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(6))) 
         base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
         const uint32_t slot =
             __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, base));
-        if (isb && slot < (uint32_t)kRankCap) bk[slot] = ((uint64_t)kb << 32) | mine[2 * i];
+        if (isb && slot < (uint32_t)kRankCap) bk[slot] = ((uint64_t)kb << 32) | mine[i + kLPos];
       }
     }
     __syncthreads();
@@ -781,7 +793,7 @@ __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(6))) 
 
   // ---- the chosen survivors' bits, then rows in ascending order ----
   for (uint32_t i = (uint32_t)lane; i < nsurv; i += 64) {
-    const uint32_t kb = mine[2 * i + 1], p = ~mine[2 * i];
+    const uint32_t kb = mine[i], p = ~mine[i + kLPos];
     if (kb > th || (kb == th && p <= plim)) atomicOr(&map_s[p >> 5], 1u << (p & 31u));
   }
   __syncthreads();
