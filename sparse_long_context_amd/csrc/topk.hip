@@ -815,8 +815,9 @@ __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(6))) 
 
 }  // namespace
 
-// Batches of at least this many queries take the 512-thread shape for lists
-// past one register segment or with Reindex lists.
+// Batches of at least this many queries take the survivor form for lists of
+// one register segment, and the 512-thread shape for lists past one register
+// segment or with Reindex lists.
 constexpr int32_t kManyQueries = 512;
 // Smaller batches with lists past one 1,024 x 16 segment split them over
 // workgroups (kSegment) when given the buffers; the largest batches have
@@ -829,9 +830,12 @@ static void launch_forms(int32_t K, int32_t B, const csa2_batch& bt, const float
 #define CSA2_TOPK_ARGS                                                                                    \
   K, bt.max_candidates, bt.pos, bt.mode, bt.compress_ratio, bt.pool_len, bt.cand_off, bt.cand_idx, scores, \
       stride, topk_idx, none
-  // lists of at most one 512 x 32 segment and no Reindex lists: the lean
-  // form, at any batch size (its latency per query is also the lowest)
-  if (bt.max_candidates <= kLMax && bt.cand_off == nullptr && K <= kLThreads)
+  // lists of at most one 512 x 32 segment and no Reindex lists: in a batch
+  // of many queries the survivor form (several workgroups share each CU and
+  // hide each other's barrier and LDS waits), otherwise the register-segment
+  // form (one workgroup alone on a CU: its shorter chain of passes has the
+  // lower latency; 11 against 15 us for 64 or 256 queries of 16,384)
+  if (bt.max_candidates <= kLMax && bt.cand_off == nullptr && K <= kLThreads && B >= kManyQueries)
     hipLaunchKernelGGL(topk_lean_kernel, dim3(B), dim3(kLThreads), 0, s, CSA2_TOPK_ARGS);
   else if (bt.max_candidates <= 512 * 32 && bt.cand_off == nullptr)
     hipLaunchKernelGGL((topk_kernel<512, 32, kOneSeg>), dim3(B), dim3(512), 0, s, CSA2_TOPK_ARGS);

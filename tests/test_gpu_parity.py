@@ -269,10 +269,13 @@ def survivor_rows(rng, n):
 @pytest.mark.parametrize("n,k,pad", [(16384, 512, 0), (2048, 512, 0), (2047, 512, 0), (2049, 300, 0),
                                      (15873, 512, 0), (16384, 512, 1), (9000, 1, 0), (4096, 512, 0)])
 def test_topk_survivor_form(n, k, pad):
+    # a batch of 520 rows (the survivor form serves batches of 512 or more);
     # a row stride of n + 1 leaves odd rows unaligned (those go through the
     # register-segment form); every row must match the oracle bit for bit
     rng = np.random.default_rng(n * 3 + k + pad)
     rows = survivor_rows(rng, n)
+    while len(rows) < 520:  # the survivor form serves batches of 512 queries or more
+        rows += survivor_rows(rng, n)
     B = len(rows)
     stride = n + pad
     s = np.full((B, stride), -np.inf, np.float32)
