@@ -25,10 +25,19 @@
 // over the two remaining digits (bits 19-8, 7-0) finds the K-th key value and
 // a prefix over the keys equal to it finds its index.
 //
-// Two shapes are built: 1,024 threads x 16 keys (few queries: the lowest
-// latency per query) and 512 x 32 for batches of many queries (a prefill
-// chunk): two independent workgroups per CU, so one workgroup's barriers and
-// LDS round trips hide behind the other's.
+// The forms (launch_forms picks one per batch):
+//  - the survivor form (topk_lean_kernel, below) for batches of 512 queries
+//    or more whose lists fit one 512 x 32 segment and carry no Reindex list:
+//    a floor from the threads' largest keys leaves ~18 % of the keys, and
+//    every pass after the first runs over those survivors only; three
+//    workgroups per CU hide each other's barrier and LDS waits;
+//  - the register-segment form above (topk_run), 512 threads x 32 keys, for
+//    the same lists in smaller batches (one workgroup alone on a CU: its
+//    shorter chain of passes has the lower latency);
+//  - 1,024 x 16 (few queries) and 512 x 32 (many queries) general shapes for
+//    longer lists and Reindex lists, segments re-read per pass; with a
+//    workspace, a few long lists split over workgroups (kSegment) and merge
+//    in a 512 x 4 / 512 x 8 shape.
 #include "csa2_internal.h"
 
 namespace csa2 {
