@@ -38,6 +38,19 @@ __device__ __forceinline__ void fp4x8_to_f32x8(uint32_t w, float* out) {
   out[4] = a2[0], out[5] = a2[1], out[6] = a3[0], out[7] = a3[1];
 }
 
+// Eight E2M1 codes times a power of two 2^k (the float `scale`), each the
+// exact product: the conversion takes only the exponent of its scale
+// operand, which for a power of two is the whole scale.  The caller keeps
+// every product a finite normal float (-125 <= k <= 125: magnitudes 0.5 .. 6).
+__device__ __forceinline__ void fp4x8_pow2_to_f32x8(uint32_t w, float scale, float* out) {
+  const auto a0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 0);
+  const auto a1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 1);
+  const auto a2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 2);
+  const auto a3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 3);
+  out[0] = a0[0], out[1] = a0[1], out[2] = a1[0], out[3] = a1[1];
+  out[4] = a2[0], out[5] = a2[1], out[6] = a3[0], out[7] = a3[1];
+}
+
 // Eight E2M1 codes times one E4M3 scale byte -> eight bf16 (a uint4), exact:
 // each product has at most 6 significant bits.
 __device__ __forceinline__ uint4 fp4x8_e4m3_to_bf16x8(uint32_t w, uint32_t scale_byte) {

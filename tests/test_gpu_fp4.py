@@ -163,3 +163,51 @@ def test_full_size_decode_fp4():
         v = sg[b][sg[b] >= 0]
         assert len(v) == 512 and (np.diff(v) > 0).all()
     assert np.isfinite(og).all()
+
+
+def test_mxfp4_scores_at_extreme_scale_bytes():
+    """MXFP4 index scores bit for bit against the oracle's fmaf chain over the
+    decoded keys, with E8M0 scale bytes at both ends: 0 and 1 (products down to
+    2^-128, subnormal), 2 and 252 (the first and last bytes whose products are
+    all normal), 253 and 254 (codes kept at most 3 and 1.5, so the keys stay
+    finite), among ordinary bytes near 127.  The query's last 32 dims (the
+    block that carries the largest scales) are tiny, so no score overflows."""
+    rng = np.random.default_rng(4711)
+    ctx = [4 * 3000, 4 * 1500 + 3, 4 * 777]
+    inp = synth.decode_batch(77, ctx, [synth.MODE_FULL] * 3, [4] * 3, dims=small_dims())
+    rows = inp["idx_k"].shape[0]
+    codes = rng.integers(0, 256, size=(rows, 64), dtype=np.uint8)
+    scales = rng.integers(118, 136, size=(rows, 4), dtype=np.uint8)
+    lowb = np.array([0, 1, 2], np.uint8)
+    scales[:, :3] = np.where(rng.random((rows, 3)) < 0.4, rng.choice(lowb, size=(rows, 3)), scales[:, :3])
+    top = rng.choice(np.array([252, 253, 254, 127], np.uint8), size=rows)
+    scales[:, 3] = top
+    # block 3 (bytes 48..63 of a row's codes): magnitude codes 0..5 (|v| <= 3)
+    # under byte 253, 0..3 (|v| <= 1.5) under byte 254, so 6 * 2^126 and
+    # 2 * 2^127 never occur
+    blk3 = codes[:, 48:].copy()
+    lo, hi = blk3 & 0xF, blk3 >> 4
+    for lim, byte in ((5, 253), (3, 254)):
+        sel = top == byte
+        lo[sel] = (lo[sel] & 8) | np.minimum(lo[sel] & 7, lim)
+        hi[sel] = (hi[sel] & 8) | np.minimum(hi[sel] & 7, lim)
+    codes[:, 48:] = (hi << 4) | lo
+    q = inp["idx_q"].copy()
+    q[..., 96:] *= np.float32(2.0 ** -100)
+    inp = dict(inp, idx_q=q, idx_k=codes, idx_k_scale=scales,
+               dims=dict(inp["dims"], index_key_dtype=synth.IDXK_MXFP4))
+    keys = O.dequant_mxfp4(codes, scales)
+    assert np.isfinite(keys).all()
+    w = csa2.DecodeWorkload(inp)
+    stride = w.max_cand + 4
+    sc = torch.full((w.B, stride), float("nan"), device="cuda")
+    say("MXFP4 scores at scale bytes 0..2 and 252..254")
+    csa2.csa2_index_scores(w.dims, w.B, w.batch, w.idx_q, w.idx_w, w.idx_k, sc, stride, idx_k_scale=w.idx_k_scale)
+    torch.cuda.synchronize()
+    got = sc.cpu().numpy()
+    for b in range(w.B):
+        p0, pl = int(inp["pool_row0"][b]), int(inp["pool_len"][b])
+        nv = O.n_valid(inp["pos"][b], 4, synth.MODE_FULL, pl)
+        ref, _, _ = O.index_scores(q[b].reshape(1, -1), keys[p0:p0 + pl], n=nv)
+        assert np.isfinite(ref).all()
+        assert got[b, :nv].tobytes() == ref.tobytes(), f"query {b}"
