@@ -602,7 +602,8 @@ __global__ __launch_bounds__(kThreads, kThreads == 512 ? 4 : 1) void topk_kernel
 
 // ---------------------------------------------------------------------------
 // The survivor form: one workgroup of 512 threads per query for lists of
-// 2,048 .. 16,384 candidates (no Reindex lists, K <= 512).
+// 2,048 .. 16,384 candidates (no Reindex lists, K <= 512), launched for
+// batches of 512 queries or more.
 //
 // The list is read as 8 chunks of 2,048 keys, thread t holding keys
 // 2048c + 4t .. 2048c + 4t + 3 of chunk c (one 16-byte load per chunk, so
@@ -618,12 +619,13 @@ __global__ __launch_bounds__(kThreads, kThreads == 512 ? 4 : 1) void topk_kernel
 // below +0 and so below the floor).  The floor test is one integer compare
 // per key, with no key map at all.  Keys at or above the floor (for Gaussian
 // scores about 18 % of the list: the floor is the smallest of 512 maxima of
-// 32) are appended to their wave's survivor list in LDS, (~position, score
-// bits), by a wave-wide ballot and prefix.  Every later pass runs over the
-// survivors only, a few per lane instead of 32 keys per thread:
+// 32) are appended to their wave's survivor list in LDS (score bits and
+// ~position) by a wave-wide ballot and prefix.  Every later pass runs over
+// the survivors only, a few per lane instead of 32 keys per thread:
 //  1. a 4,096-bin histogram over [floor, largest key] finds the bucket that
 //     holds the K-th best survivor and how many lie above it;
-//  2. that bucket's survivors (typically one or two) are ranked exactly
+//  2. when that bucket holds exactly the survivors still needed (usually
+//     one), all of it is chosen; otherwise its survivors are ranked exactly
 //     under (score desc, position asc): the K-th key (th, index limit);
 //  3. each chosen survivor sets its position's bit in a 16,384-bit LDS map;
 //     thread t owns word t (positions 32t .. 32t + 31), so a block-wide
