@@ -298,6 +298,50 @@ def test_topk_survivor_form(n, k, pad):
         assert np.array_equal(got[b], O.topk(s[b, :n], k)), f"row {b} (n={n}, k={k}, stride={stride})"
 
 
+def test_topk_minus_inf_scores():
+    # the interface allows -inf scores (unreachable Reindex rows get them),
+    # which the oracle's top-K does not take: the reference here is the
+    # definition itself, a lexicographic sort by (score descending, row
+    # ascending), -inf last and its ties by row.  A batch of 520 rows of
+    # 16,384 (the survivor form's shape): Gaussian with 30 % -inf, only 300
+    # finite scores (the K-th is a -inf, taken by lowest row), all -inf, and
+    # Gaussian with a few -inf
+    rng = np.random.default_rng(31337)
+    B, n, k = 520, 16384, 512
+    s = rng.standard_normal((B, n)).astype(np.float32)
+    for b in range(B):
+        kind = b % 4
+        if kind == 0:
+            s[b, rng.random(n) < 0.3] = -np.inf
+        elif kind == 1:
+            keep = rng.choice(n, 300, replace=False)
+            row = np.full(n, -np.inf, np.float32)
+            row[keep] = s[b, keep]
+            s[b] = row
+        elif kind == 2:
+            s[b] = -np.inf
+        else:
+            s[b, rng.integers(0, n, 20)] = -np.inf
+    dims = synth.default_dims(index_topk=k)
+    inp = dict(pos=np.full(B, n - 1, np.int64), mode=np.zeros(B, np.int32), ratio=np.ones(B, np.int32),
+               win_row0=np.zeros(B, np.int64), win_len=np.zeros(B, np.int32), pool_row0=np.zeros(B, np.int64),
+               pool_len=np.full(B, n, np.int32))
+    dev = {kk: torch.from_numpy(v).cuda() for kk, v in inp.items()}
+    bt = csa2.Batch(*(dev[x].data_ptr() for x in ["pos", "mode", "ratio", "win_row0", "win_len", "pool_row0",
+                                                   "pool_len"]), None, None, n)
+    sc = torch.from_numpy(s).cuda()
+    out = torch.full((B, k), -7, dtype=torch.int32, device="cuda")
+    say("topk with -inf scores, B=520")
+    csa2.csa2_topk(csa2.Dims.from_dict(dims), B, bt, sc, n, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    rows = np.arange(n)
+    for b in range(B):
+        order = np.lexsort((rows, -s[b].astype(np.float64)))
+        want = np.sort(order[:k]).astype(np.int32)
+        assert np.array_equal(got[b], want), f"row {b} (kind {b % 4})"
+
+
 def test_attend_reuse_lists_with_padding_and_duplicates():
     ctx = [30000, 2000, 500, 128 * 4 + 8]
     inp = synth.decode_batch(12, ctx, [synth.MODE_REUSE] * 4, [4] * 4, dims=small_dims())
